@@ -1,0 +1,371 @@
+"""Benchmark: batched chain verification on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu-baseline] [--probe]
+
+One step = one spec_verify_chain call over a batch of B=64 sequences, K=5 drafts,
+V=128256 bf16 logits (high-acceptance recipe, T=0.8): the row statistics, accept
+tests, first-reject scan, residual/bonus draw and compaction of every sequence.
+Inputs are resident in HBM before timing; consecutive steps rotate over several
+distinct input sets whose total exceeds twice the 256 MB last-level cache, so
+every step streams its logits from HBM.
+
+Prints ONE JSON line (rank 0).  `value` is verified draft positions per second
+(B*K per step); `roofline` reports the dominant kernel (chain_stats, which reads
+every logit once) against the MI355X HBM peak, with its duration measured by HIP
+events recorded around its launches on its stream; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.  Secondary workloads (greedy
+tree verify, low-acceptance chain, n-gram propose + one-hot verify, the small
+fp32 chain) are reported under "other_workloads" unless --quick is given.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+LLC_BYTES = 256 * 1024 * 1024
+
+
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken on
+    the current kernel source (same digest); otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def sets_needed(bytes_per_set: int) -> int:
+    return max(2, -(-2 * LLC_BYTES // bytes_per_set) + 1)
+
+
+def to_dev(x, dtype, dev):
+    import numpy as np
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def chain_device_sets(make, n_sets, dev):
+    import numpy as np
+    import torch
+
+    sets = []
+    host0 = None
+    for s in range(n_sets):
+        inp = make(s)
+        if s == 0:
+            host0 = inp
+        sets.append(dict(
+            t=to_dev(inp.target, inp.dtype, dev),
+            d=None if inp.draft is None else to_dev(inp.draft, inp.dtype, dev),
+            tok=torch.from_numpy(np.ascontiguousarray(inp.tokens, dtype=np.int32)).to(dev),
+            T=torch.from_numpy(inp.temperature).to(dev),
+            ua=torch.from_numpy(inp.u_accept).to(dev),
+            uf=torch.from_numpy(inp.u_final).to(dev),
+            dl=None if inp.draft_len is None else torch.from_numpy(inp.draft_len).to(dev),
+        ))
+    return sets, host0
+
+
+def chain_bytes(inp) -> int:
+    """Algorithmic bytes of one call: every logit row the method uses read once, plus tokens,
+    uniforms, temperatures, draft lengths and the outputs written."""
+    import numpy as np
+
+    B, K, V = inp.B, inp.K, inp.V
+    es = 2 if inp.dtype == "bf16" else 4
+    kb = np.full(B, K) if inp.draft_len is None else np.asarray(inp.draft_len)
+    rows = int(np.sum(kb + 1) + (np.sum(kb) if inp.draft is not None else 0))
+    small = B * K * 4 * 2 + B * 4 * 2 + (B * 4 if inp.draft_len is not None else 0)
+    outs = B * (K + 1) * 4 + B * 4 + B * K * 12
+    return rows * V * es + small + outs
+
+
+def time_calls(call, n_sets, warmup, steps, kernel_timing):
+    """Run warmup, then `steps` timed calls rotating over the input sets.  Returns
+    (ms per call from events around the whole region, {kernel: (launches, total_ms)})."""
+    import torch
+
+    import draft_token_verification_09_amd as sv
+
+    for i in range(warmup):
+        call(i % n_sets)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    if kernel_timing:
+        sv.spec_timing_reset()
+        sv.spec_timing_enable(True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        call((warmup + i) % n_sets)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    kernels = {}
+    if kernel_timing:
+        sv.spec_timing_enable(False)
+        for name, launches, ms in sv.spec_timing_collect():
+            kernels[name] = (launches, ms)
+        sv.spec_timing_reset()
+    return start.elapsed_time(stop) / steps, kernels
+
+
+def bench_chain_workload(make, name, warmup, steps, dev, kernel_timing=True):
+    import draft_token_verification_09_amd as sv
+
+    probe = make(0)
+    per_set = chain_bytes(probe)
+    n_sets = sets_needed(per_set)
+    progress(f"{name}: generating {n_sets} input sets of {per_set / 1e6:.1f} MB")
+    sets, host0 = chain_device_sets(make, n_sets, dev)
+
+    def call(i):
+        s = sets[i]
+        sv.spec_verify_chain(s["t"], s["d"], s["tok"], s["T"], s["ua"], s["uf"], s["dl"])
+
+    progress(f"{name}: timing {steps} calls")
+    ms, _ = time_calls(call, n_sets, warmup, steps, kernel_timing=False)
+    kms = {}
+    if kernel_timing:
+        _, kms = time_calls(call, n_sets, 2, steps, kernel_timing=True)
+    del sets
+    return dict(ms=ms, bytes=per_set, kernels=kms, host=host0, positions=probe.B * probe.K)
+
+
+def cpu_baseline(host_inp, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample of sequences of the same workload."""
+    import oracle
+
+    t0 = time.perf_counter()
+    done = 0
+    while done < host_inp.B and time.perf_counter() - t0 < budget_s:
+        oracle.verify_chain(host_inp.target, host_inp.draft, host_inp.dtype, host_inp.tokens, host_inp.temperature,
+                            host_inp.u_accept, host_inp.u_final, draft_len=host_inp.draft_len, seqs=[done])
+        done += 1
+    dt = time.perf_counter() - t0
+    return dict(value=done * host_inp.K / dt, unit="positions/s", cores=1, kind="oracle",
+                sample=f"{done} of {host_inp.B} sequences (K={host_inp.K}, V={host_inp.V}, {host_inp.dtype}) "
+                       f"of input set 0, verified one after another in {dt:.1f} s; float64 NumPy, one thread")
+
+
+def other_workloads(warmup, steps, dev):
+    import numpy as np
+    import torch
+
+    import draft_token_verification_09_amd as sv
+    import synth
+
+    out = []
+    # chain, low acceptance, B=256 K=8 V=152064 bf16
+    r = bench_chain_workload(lambda s: synth.chain_config_low_accept_bf16(s), "chain_B256_K8_V152064_bf16",
+                             warmup, steps, dev)
+    out.append(_entry("chain_verify_B256_K8_V152064_bf16_low_accept", r, r["positions"]))
+    # small fp32 chain: latency
+    r = bench_chain_workload(lambda s: synth.chain_config_small_f32(s), "chain_B1_K5_V32000_f32", warmup, steps, dev)
+    out.append(_entry("chain_verify_B1_K5_V32000_f32", r, r["positions"]))
+
+    # greedy tree, B=32 N=60 V=128256 bf16
+    tr0 = synth.tree_config_eagle_bf16(0)
+    per = tr0.target.nbytes + tr0.parent.nbytes * 2
+    n_sets = sets_needed(per)
+    progress(f"tree: generating {n_sets} input sets")
+    sets = []
+    for s in range(n_sets):
+        tr = tr0 if s == 0 else synth.tree_config_eagle_bf16(s)
+        sets.append((to_dev(tr.target, "bf16", dev), torch.from_numpy(tr.parent).to(dev),
+                     torch.from_numpy(tr.node_token).to(dev)))
+
+    def tcall(i):
+        t, p, k = sets[i]
+        sv.spec_verify_tree_greedy(t, p, k, 6)
+
+    ms, _ = time_calls(tcall, n_sets, warmup, steps, False)
+    _, kms = time_calls(tcall, n_sets, 2, steps, True)
+    del sets
+    tb = per + tr0.B * (7 * 3 + 1 + tr0.N1) * 4
+    out.append(_entry("tree_greedy_B32_N60_V128256_bf16", dict(ms=ms, bytes=tb, kernels=kms), tr0.B * (tr0.N1 - 1)))
+
+    # n-gram propose + one-hot verify, B=128 L=4096 K=5 V=32000 bf16
+    progress("ngram: generating inputs")
+    n_sets = 11
+    sets = []
+    for s in range(n_sets):
+        pr = synth.ngram_config_prompts(s)
+        ctx = torch.from_numpy(pr.context).to(dev)
+        cl = torch.from_numpy(pr.context_len).to(dev)
+        g = sv.ngram_propose(ctx, cl, 1, 4, 5)
+        torch.cuda.synchronize()
+        inp = synth.ngram_target_inputs(s, g.draft_tokens.cpu().numpy(), g.draft_len.cpu().numpy(), V=32000)
+        sets.append(dict(ctx=ctx, cl=cl, t=to_dev(inp.target, "bf16", dev), T=torch.from_numpy(inp.temperature).to(dev),
+                         ua=torch.from_numpy(inp.u_accept).to(dev), uf=torch.from_numpy(inp.u_final).to(dev),
+                         bytes=chain_bytes(inp) + pr.context.nbytes + pr.context_len.nbytes))
+
+    def ncall(i):
+        s = sets[i]
+        g = sv.ngram_propose(s["ctx"], s["cl"], 1, 4, 5)
+        sv.spec_verify_chain(s["t"], None, g.draft_tokens, s["T"], s["ua"], s["uf"], g.draft_len)
+
+    ms, _ = time_calls(ncall, n_sets, warmup, steps, False)
+    _, kms = time_calls(ncall, n_sets, 2, steps, True)
+    nb = int(np.mean([s["bytes"] for s in sets]))
+    del sets
+    out.append(_entry("ngram_propose_verify_B128_L4096_K5_V32000_bf16", dict(ms=ms, bytes=nb, kernels=kms), 128 * 5))
+    return out
+
+
+def _entry(workload, r, positions):
+    ms = r["ms"]
+    return dict(workload=workload, ms_per_call=round(ms, 5), positions_per_s=round(positions / (ms * 1e-3), 1),
+                algorithmic_GBps=round(r["bytes"] / (ms * 1e-3) / 1e9, 1),
+                frac_of_hbm_peak=round(r["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                kernels_us={k: round(v[1] / v[0] * 1e3, 2) for k, v in r["kernels"].items()})
+
+
+def probe(dev, nbytes=1 << 30):
+    """Streaming read and copy probes over `nbytes` (calibration for counters and roofline)."""
+    import torch
+
+    import draft_token_verification_09_amd as sv
+
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {}
+    for name, fn in (("probe_read", lambda: sv.spec_probe_read(src, out)),
+                     ("probe_copy", lambda: sv.spec_probe_copy(src, dst))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 10
+        moved = nbytes * (2 if name == "probe_copy" else 1)
+        res[name] = dict(bytes_per_launch=moved, ms=round(ms, 4), GBps=round(moved / (ms * 1e-3) / 1e9, 1))
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", action="store_true", help="also run the streaming read/copy probes")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the verification path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}); sequences shard across GPUs "
+              f"without communication, so run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import draft_token_verification_09_amd as sv
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sv.lib()  # fails loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    progress(f"device {torch.cuda.get_device_name(dev)}")
+
+    workload = "chain_verify_B64_K5_V128256_bf16_high_accept"
+    head = bench_chain_workload(lambda s: synth.chain_config_high_accept_bf16(s), workload,
+                                args.warmup, args.steps, dev)
+    ms = head["ms"]
+    B, K, V = 64, 5, 128256
+    positions = B * K
+    logits_bytes = B * (2 * K + 1) * V * 2
+    stats_launches, stats_ms = head["kernels"].get("chain_stats", (1, float("nan")))
+    stats_avg_s = stats_ms / stats_launches * 1e-3
+    achieved = logits_bytes / stats_avg_s / 1e9
+    digest = source_digest(["draft_token_verification_09_amd/csrc/chain.hip",
+                            "draft_token_verification_09_amd/csrc/device_common.h"])
+    traffic = read_traffic("chain_stats", "B64_K5_V128256_bf16", digest)
+
+    result = {
+        "metric": "verified draft positions/sec and achieved HBM GB/s (% of peak), 1 MI355X",
+        "value": round(positions / (ms * 1e-3), 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Philox): target N(0,3^2) + 20 peaks at +8 per row, draft = target + N(0,0.7^2), "
+                "drafts sampled from q, T=0.8",
+        "config": {"workload": workload, "B": B, "K": K, "V": V, "temperature": 0.8,
+                   "input_sets_rotated": sets_needed(head["bytes"]), "parallelism": "single GPU"},
+        "achieved_GBps_step": round(head["bytes"] / (ms * 1e-3) / 1e9, 1),
+        "kernels_us": {k: round(v[1] / v[0] * 1e3, 3) for k, v in head["kernels"].items()},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "chain_stats",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": logits_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        progress("cpu baseline (oracle on a bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(head["host"])
+    if not args.quick:
+        result["other_workloads"] = other_workloads(args.warmup, max(20, args.steps // 2), dev)
+    if args.probe:
+        result["probes"] = probe(dev)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,24 @@
+"""Batched speculative-decoding draft verification on AMD Instinct MI355X (gfx950).
+
+The work runs in libspecverify.so (HIP kernels behind a C ABI, include/spec_verify.h);
+this package holds the kernel sources (csrc/), the build step (build.py) and a thin
+ctypes binding (binding.py) whose functions carry the C entry points' names.
+"""
+
+from .binding import (  # noqa: F401
+    ChainResult,
+    NgramResult,
+    SpecError,
+    TreeResult,
+    lib,
+    loaded_library_path,
+    ngram_propose,
+    spec_probe_copy,
+    spec_probe_read,
+    spec_timing_collect,
+    spec_timing_enable,
+    spec_timing_reset,
+    spec_verify_chain,
+    spec_verify_chain_workspace_size,
+    spec_verify_tree_greedy,
+)

@@ -1,0 +1,316 @@
+"""ctypes binding of libspecverify.so (include/spec_verify.h, include/spec_measure.h).
+
+Argument marshalling only: every step of verification runs in the library's HIP
+kernels.  PyTorch supplies device memory (inputs, outputs, a cached scratch
+workspace) and the current HIP stream.  If the library is not built, every call
+raises -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Tuple
+
+import torch
+
+from .build import library_path
+
+SPEC_F32 = 0
+SPEC_BF16 = 1
+SPEC_MAX_K = 64
+SPEC_MAX_TREE_NODES = 1024
+SPEC_MAX_NGRAM_N = 16
+
+
+class SpecError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, func: str, status: int, name: str, detail: str):
+        super().__init__(f"{func} failed: {name}: {detail}")
+        self.status = status
+        self.status_name = name
+        self.detail = detail
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "spec_status_string": (ctypes.c_char_p, [_i32]),
+    "spec_last_error": (ctypes.c_char_p, []),
+    "spec_verify_chain_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "spec_verify_chain": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_tree_greedy_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "spec_verify_tree_greedy": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                       _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ngram_propose": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "spec_timing_enable": (_i32, [_i32]),
+    "spec_timing_reset": (_i32, []),
+    "spec_timing_collect": (_i32, []),
+    "spec_timing_entry": (_i32, [_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_longlong),
+                                 ctypes.POINTER(ctypes.c_double)]),
+    "spec_probe_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "spec_probe_copy": (_i32, [_vp, _vp, _sz, _vp]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lib_lock:
+            if _lib is None:
+                path = library_path()
+                if not os.path.exists(path):
+                    raise RuntimeError(
+                        f"{path} is missing: build it with `python -m draft_token_verification_09_amd.build` "
+                        "(or __graft_entry__.build()); there is no CPU fallback")
+                handle = ctypes.CDLL(path)
+                for name, (res, args) in _SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = handle
+    return _lib
+
+
+def loaded_library_path() -> Optional[str]:
+    return library_path() if _lib is not None else None
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        L = lib()
+        name = L.spec_status_string(status).decode()
+        detail = L.spec_last_error().decode()
+        raise SpecError(func, status, name, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape: Tuple[int, ...], device) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# -------------------------------------------------------------------- workspaces
+
+_ws_cache: Dict[Tuple[int, int, str], torch.Tensor] = {}
+
+
+def workspace(nbytes: int, device: torch.device, stream_handle: int, tag: str) -> torch.Tensor:
+    """A device scratch buffer cached per (device, stream, tag), grown when a call needs more.
+    The library needs no particular contents in it."""
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle, tag)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _aligned_ptr(buf: torch.Tensor) -> Tuple[int, int]:
+    p = buf.data_ptr()
+    off = (-p) % 256
+    return p + off, buf.numel() - off
+
+
+# -------------------------------------------------------------------- entry points
+
+
+@dataclass
+class ChainResult:
+    tokens: torch.Tensor         # [B, K+1] int32, -1 padded
+    num_accepted: torch.Tensor   # [B] int32 (-1 = invalid input)
+    probs: Optional[torch.Tensor]    # [B, K, 3] float32
+    packed: Optional[torch.Tensor]   # [B*(K+1)] int32
+    offsets: Optional[torch.Tensor]  # [B+1] int32
+
+
+def spec_verify_chain_workspace_size(B: int, K: int, V: int, dtype_code: int) -> int:
+    return int(lib().spec_verify_chain_workspace_size(B, K, V, dtype_code))
+
+
+def spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                      draft_tokens: torch.Tensor, temperature: torch.Tensor, u_accept: torch.Tensor,
+                      u_final: torch.Tensor, draft_len: Optional[torch.Tensor] = None, *,
+                      want_probs: bool = True, want_packed: bool = False,
+                      out: Optional[ChainResult] = None, workspace_buf: Optional[torch.Tensor] = None,
+                      stream=None) -> ChainResult:
+    """Batched chain verification (spec_verify_chain).  Shapes: target [B, K+1, V],
+    draft [B, K, V] or None (one-hot draft), draft_tokens [B, K] int32, temperature [B]
+    float32, u_accept [B, K] float32, u_final [B] float32, draft_len [B] int32 or None."""
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    code = _dtype_code(target_logits)
+    if not target_logits.is_contiguous():
+        raise ValueError("target_logits must be contiguous")
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", target_logits.dtype, (B, K, V), dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, K), dev)
+    _need(u_final, "u_final", torch.float32, (B,), dev)
+    if draft_len is not None:
+        _need(draft_len, "draft_len", torch.int32, (B,), dev)
+    if out is None:
+        out = ChainResult(
+            tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+            num_accepted=torch.empty((B,), dtype=torch.int32, device=dev),
+            probs=torch.empty((B, K, 3), dtype=torch.float32, device=dev) if want_probs else None,
+            packed=torch.empty((max(1, B * (K + 1)),), dtype=torch.int32, device=dev) if want_packed else None,
+            offsets=torch.empty((B + 1,), dtype=torch.int32, device=dev) if want_packed else None,
+        )
+    s = _stream(stream, dev)
+    L = lib()
+    need = int(L.spec_verify_chain_workspace_size(B, K, V, code)) if B > 0 else 0
+    buf = workspace_buf if workspace_buf is not None else workspace(need, dev, s, "chain")
+    wp, wbytes = _aligned_ptr(buf)
+    st = L.spec_verify_chain(_ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(draft_len),
+                             _ptr(temperature), _ptr(u_accept), _ptr(u_final), B, K, V,
+                             _ptr(out.tokens), _ptr(out.num_accepted), _ptr(out.probs),
+                             _ptr(out.packed), _ptr(out.offsets), wp, wbytes, s)
+    _check("spec_verify_chain", st)
+    return out
+
+
+@dataclass
+class TreeResult:
+    accept_len: torch.Tensor   # [B] int32 (-1 = invalid input)
+    tokens: torch.Tensor       # [B, max_depth+1] int32
+    path_nodes: torch.Tensor   # [B, max_depth+1] int32
+    argmax: Optional[torch.Tensor]  # [B, N1] int32
+
+
+def spec_verify_tree_greedy(target_logits: torch.Tensor, parent: torch.Tensor, node_token: torch.Tensor,
+                            max_depth: int, *, want_argmax: bool = True, out: Optional[TreeResult] = None,
+                            workspace_buf: Optional[torch.Tensor] = None, stream=None) -> TreeResult:
+    """Batched greedy tree verification (spec_verify_tree_greedy).  target [B, N1, V],
+    parent [B, N1] int32, node_token [B, N1] int32."""
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, N1, V]")
+    B, N1, V = target_logits.shape
+    dev = target_logits.device
+    code = _dtype_code(target_logits)
+    if not target_logits.is_contiguous():
+        raise ValueError("target_logits must be contiguous")
+    _need(parent, "parent", torch.int32, (B, N1), dev)
+    _need(node_token, "node_token", torch.int32, (B, N1), dev)
+    D1 = max_depth + 1
+    if out is None:
+        out = TreeResult(
+            accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+            tokens=torch.empty((B, D1), dtype=torch.int32, device=dev),
+            path_nodes=torch.empty((B, D1), dtype=torch.int32, device=dev),
+            argmax=torch.empty((B, N1), dtype=torch.int32, device=dev) if want_argmax else None,
+        )
+    s = _stream(stream, dev)
+    L = lib()
+    need = int(L.spec_verify_tree_greedy_workspace_size(B, N1, V, code)) if B > 0 else 0
+    buf = workspace_buf if workspace_buf is not None else workspace(need, dev, s, "tree")
+    wp, wbytes = _aligned_ptr(buf)
+    st = L.spec_verify_tree_greedy(_ptr(target_logits), code, _ptr(parent), _ptr(node_token), B, N1, V, max_depth,
+                                   _ptr(out.accept_len), _ptr(out.tokens), _ptr(out.path_nodes), _ptr(out.argmax),
+                                   wp, wbytes, s)
+    _check("spec_verify_tree_greedy", st)
+    return out
+
+
+@dataclass
+class NgramResult:
+    draft_tokens: torch.Tensor  # [B, K] int32, -1 padded
+    draft_len: torch.Tensor     # [B] int32
+    match_n: Optional[torch.Tensor]  # [B] int32
+
+
+def ngram_propose(context: torch.Tensor, context_len: torch.Tensor, n_min: int, n_max: int, K: int, *,
+                  want_match_n: bool = True, out: Optional[NgramResult] = None, stream=None) -> NgramResult:
+    """Batched prompt n-gram lookup (ngram_propose).  context [B, L_max] int32, context_len [B] int32."""
+    if context.dim() != 2:
+        raise ValueError("context must be [B, L_max]")
+    B, L_max = context.shape
+    dev = context.device
+    _need(context, "context", torch.int32, (B, L_max), dev)
+    _need(context_len, "context_len", torch.int32, (B,), dev)
+    if out is None:
+        out = NgramResult(
+            draft_tokens=torch.empty((B, K), dtype=torch.int32, device=dev),
+            draft_len=torch.empty((B,), dtype=torch.int32, device=dev),
+            match_n=torch.empty((B,), dtype=torch.int32, device=dev) if want_match_n else None,
+        )
+    s = _stream(stream, dev)
+    st = lib().ngram_propose(_ptr(context), _ptr(context_len), B, L_max, n_min, n_max, K,
+                             _ptr(out.draft_tokens), _ptr(out.draft_len), _ptr(out.match_n), s)
+    _check("ngram_propose", st)
+    return out
+
+
+# -------------------------------------------------------------------- measurement hooks
+
+
+def spec_timing_enable(enable: bool) -> None:
+    _check("spec_timing_enable", lib().spec_timing_enable(1 if enable else 0))
+
+
+def spec_timing_reset() -> None:
+    _check("spec_timing_reset", lib().spec_timing_reset())
+
+
+def spec_timing_collect() -> List[Tuple[str, int, float]]:
+    """[(kernel name, launches, total milliseconds)] since the last reset."""
+    L = lib()
+    n = int(L.spec_timing_collect())
+    out = []
+    for i in range(n):
+        name = ctypes.c_char_p()
+        launches = ctypes.c_longlong()
+        ms = ctypes.c_double()
+        _check("spec_timing_entry", L.spec_timing_entry(i, ctypes.byref(name), ctypes.byref(launches), ctypes.byref(ms)))
+        out.append((name.value.decode(), int(launches.value), float(ms.value)))
+    return out
+
+
+def spec_probe_read(src: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    s = _stream(stream, src.device)
+    _check("spec_probe_read", lib().spec_probe_read(src.data_ptr(), src.numel() * src.element_size(), out.data_ptr(), s))
+
+
+def spec_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    s = _stream(stream, src.device)
+    _check("spec_probe_copy", lib().spec_probe_copy(src.data_ptr(), dst.data_ptr(),
+                                                    src.numel() * src.element_size(), s))

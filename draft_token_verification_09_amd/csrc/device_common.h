@@ -1,0 +1,208 @@
+// Device-side building blocks shared by the verification kernels (gfx950, wave64).
+//
+// * Vocabulary streaming: a workgroup of 256 lanes covers one "chunk" of a row as
+//   NV segments; in segment j lane t holds one 16-byte vector (4 fp32 or 8 bf16
+//   logits) at element (j*256 + t)*E, so each wave instruction reads 1 KiB of
+//   contiguous memory and, inside a segment, vocabulary order is lane order.
+// * Reductions use cross-lane shuffles within a wave and a small LDS array across
+//   the 4 waves of a workgroup.
+// * Partial results pass from one kernel to the next through the workspace; the
+//   kernel boundary orders them, so no inter-workgroup synchronisation is used.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specv {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<kF32> {
+  static constexpr int kPerVec = 4;
+  static constexpr int kBytes = 4;
+  static constexpr uint32_t kNegInfBits = 0xff800000u;
+  __device__ static inline float get(const u32x4& v, int i) { return __uint_as_float(v[i]); }
+  __device__ static inline uint32_t bits(const void* base, size_t idx) {
+    return reinterpret_cast<const uint32_t*>(base)[idx];
+  }
+  __device__ static inline float value(const void* base, size_t idx) {
+    return reinterpret_cast<const float*>(base)[idx];
+  }
+  // pack E element bit patterns (already in the low bits) into a vector
+  __device__ static inline void put(u32x4& v, int i, uint32_t b) { v[i] = b; }
+};
+
+template <>
+struct Elem<kBF16> {
+  static constexpr int kPerVec = 8;
+  static constexpr int kBytes = 2;
+  static constexpr uint32_t kNegInfBits = 0xff80u;
+  __device__ static inline float get(const u32x4& v, int i) {
+    const uint32_t w = v[i >> 1];
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  __device__ static inline uint32_t bits(const void* base, size_t idx) {
+    return reinterpret_cast<const uint16_t*>(base)[idx];
+  }
+  __device__ static inline float value(const void* base, size_t idx) {
+    return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(base)[idx]) << 16);
+  }
+  __device__ static inline void put(u32x4& v, int i, uint32_t b) {
+    uint32_t w = v[i >> 1];
+    w = (i & 1) ? ((w & 0x0000ffffu) | (b << 16)) : ((w & 0xffff0000u) | b);
+    v[i >> 1] = w;
+  }
+};
+
+template <int DT, int NV>
+struct ChunkShape {
+  static constexpr int E = Elem<DT>::kPerVec;
+  static constexpr int kSegment = kThreads * E;  // elements per segment
+  static constexpr int kChunk = NV * kSegment;   // elements per chunk
+};
+
+// Load chunk `c` of a row of V logits into registers.  Elements past V read as -inf.
+// VEC: the row starts 16-byte aligned, so whole vectors can be loaded.
+template <int DT, int NV, bool VEC>
+__device__ inline void load_chunk(u32x4 (&raw)[NV], const void* row, int V, int c) {
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  const int base = c * ChunkShape<DT, NV>::kChunk;
+  const int lane = threadIdx.x;
+  if (VEC && base + ChunkShape<DT, NV>::kChunk <= V) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
+                                                    static_cast<size_t>(base) * EL::kBytes);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) raw[j] = p[j * kThreads + lane];
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int e0 = base + (j * kThreads + lane) * E;
+    if (VEC && e0 + E <= V) {
+      raw[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + static_cast<size_t>(e0) * EL::kBytes);
+    } else {
+      u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int e = e0 + i;
+        EL::put(v, i, e < V ? EL::bits(row, e) : EL::kNegInfBits);
+      }
+      raw[j] = v;
+    }
+  }
+}
+
+// Load the one vector of a row that starts at element e0 (a multiple of E); elements
+// past V read as -inf.
+template <int DT, bool VEC>
+__device__ inline u32x4 load_vector(const void* row, int V, int e0) {
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  if (VEC && e0 + E <= V)
+    return *reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + static_cast<size_t>(e0) * EL::kBytes);
+  u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < E; ++i) EL::put(v, i, e0 + i < V ? EL::bits(row, e0 + i) : EL::kNegInfBits);
+  return v;
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ inline int wave_min_int(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ inline int wave_max_int(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Inclusive scan over the lanes of a wave (lane order).
+__device__ inline double wave_inclusive_scan(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Workgroup-wide reductions (every lane receives the result).  Contain __syncthreads.
+__device__ inline float block_max(float v, float* lds4) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds4[w] = v;
+  __syncthreads();
+  float r = lds4[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, lds4[i]);
+  return r;
+}
+
+__device__ inline double block_sum(double v, double* lds4) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds4[w] = v;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) r += lds4[i];
+  return r;
+}
+
+__device__ inline int block_min_int(int v, int* lds4) {
+  v = wave_min_int(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds4[w] = v;
+  __syncthreads();
+  int r = lds4[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = min(r, lds4[i]);
+  return r;
+}
+
+__device__ inline int block_max_int(int v, int* lds4) {
+  v = wave_max_int(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds4[w] = v;
+  __syncthreads();
+  int r = lds4[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = max(r, lds4[i]);
+  return r;
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace specv

@@ -1,0 +1,44 @@
+// Host-side runtime shared by the entry points: error reporting, launch checks,
+// optional per-kernel event timing, workspace carving and tuning knobs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+namespace specv {
+
+// Record a thread-local detail message and return `status`.
+spec_status_t fail(spec_status_t status, const char* fmt, ...);
+
+// Brackets one kernel launch: when timing is enabled it records a HIP event pair on
+// `stream` around the launch under `name`; on destruction it checks the launch.
+class LaunchScope {
+ public:
+  LaunchScope(const char* name, hipStream_t stream);
+  ~LaunchScope();
+  // Status of the launch (checks hipGetLastError); call after the kernel launch.
+  spec_status_t finish();
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  int slot_;
+  bool finished_;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Integer tuning knob from the environment (read on every call; absent -> dflt).
+int env_int(const char* name, int dflt);
+
+// Vectors (16 B each) per lane in one chunk: the largest of 8, 4, 2, 1 that still
+// gives at least `min_groups` workgroups over `rows` rows of V elements, else 1.
+// SPEC_NV in the environment forces a value (1, 2, 4 or 8).
+int choose_nv(long long rows, int V, int elems_per_vec, long long min_groups);
+
+}  // namespace specv

@@ -1,0 +1,91 @@
+// Prompt n-gram lookup drafting, batched over sequences.
+//
+// "Accelerating Autoregressive LLM Inference 3x with Lossless Speculative Decoding
+// and EAGLE Heads" (x078.com): prompt n-gram lookup as a zero-VRAM draft
+// mechanism proposing K candidates, with the lookup's maximum n set to 4 in its
+// deployment snippet (section 1).  Reading: for n = n_max down to n_min, the
+// earliest j with c[j:j+n] == c[L-n:L] and j + n <= L - 1 wins; the draft is
+// c[j+n : min(j+n+K, L)].
+//
+// One workgroup per sequence.  Instead of testing every (n, j) pair, each lane
+// takes candidate end positions e = j + n - 1 in [0, L-2] and measures how many
+// tokens ending at e match the suffix ending at L-1 (at most n_max); a match of
+// length >= n at end e is an occurrence for n starting at j = e - n + 1, so the
+// earliest occurrence for n is the smallest such e.  A shared-memory atomic min per
+// n combines the lanes; the largest n with an occurrence wins.
+#include "device_common.h"
+#include "host_runtime.h"
+#include "spec_verify.h"
+
+namespace specv {
+
+__global__ __launch_bounds__(kThreads) void ngram_propose_kernel(const int32_t* context, const int32_t* context_len,
+                                                                 int L_max, int n_min, int n_max, int K,
+                                                                 int32_t* out_draft, int32_t* out_len,
+                                                                 int32_t* out_match_n) {
+  __shared__ int s_suffix[SPEC_MAX_NGRAM_N];
+  __shared__ int s_first[SPEC_MAX_NGRAM_N + 1];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t* c = context + static_cast<size_t>(b) * L_max;
+  int32_t* od = out_draft + static_cast<size_t>(b) * K;
+  const int L = context_len[b];
+  if (L < 1 || L > L_max) {
+    for (int k = tid; k < K; k += kThreads) od[k] = -1;
+    if (tid == 0) {
+      out_len[b] = 0;
+      if (out_match_n) out_match_n[b] = -1;
+    }
+    return;
+  }
+  if (tid < n_max) s_suffix[tid] = tid < L ? c[L - 1 - tid] : 0;
+  if (tid <= n_max) s_first[tid] = INT_MAX;
+  __syncthreads();
+  for (int e = tid; e <= L - 2; e += kThreads) {
+    int ml = 0;
+    while (ml < n_max && ml <= e && c[e - ml] == s_suffix[ml]) ++ml;
+    for (int n = n_min; n <= ml; ++n) atomicMin(&s_first[n], e);
+  }
+  __syncthreads();
+  int best_n = 0, best_e = -1;
+  for (int n = n_max; n >= n_min; --n) {
+    if (s_first[n] != INT_MAX) {
+      best_n = n;
+      best_e = s_first[n];
+      break;
+    }
+  }
+  const int start = best_e + 1;  // first continuation token
+  const int len = best_n ? min(K, L - start) : 0;
+  for (int k = tid; k < K; k += kThreads) od[k] = k < len ? c[start + k] : -1;
+  if (tid == 0) {
+    out_len[b] = len;
+    if (out_match_n) out_match_n[b] = best_n;
+  }
+}
+
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" {
+
+spec_status_t ngram_propose(const int32_t* context, const int32_t* context_len,
+                            int B, int L_max, int n_min, int n_max, int K,
+                            int32_t* out_draft_tokens, int32_t* out_draft_len, int32_t* out_match_n,
+                            spec_stream_t stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B < 0 || L_max < 1 || K < 1 || n_min < 1 || n_max < n_min)
+    return fail(SPEC_ERR_INVALID_ARG, "need B >= 0, L_max >= 1, K >= 1, 1 <= n_min <= n_max");
+  if (n_max > SPEC_MAX_NGRAM_N) return fail(SPEC_ERR_UNSUPPORTED, "n_max = %d exceeds SPEC_MAX_NGRAM_N", n_max);
+  if (K > SPEC_MAX_K) return fail(SPEC_ERR_UNSUPPORTED, "K = %d exceeds SPEC_MAX_K", K);
+  if (B == 0) return SPEC_OK;
+  if (!context || !context_len || !out_draft_tokens || !out_draft_len)
+    return fail(SPEC_ERR_INVALID_ARG, "a required pointer is NULL");
+  LaunchScope scope("ngram_propose", s);
+  hipLaunchKernelGGL(ngram_propose_kernel, dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, s, context, context_len,
+                     L_max, n_min, n_max, K, out_draft_tokens, out_draft_len, out_match_n);
+  return scope.finish();
+}
+
+}  // extern "C"

@@ -1,0 +1,200 @@
+/*
+ * spec_verify.h -- C ABI of the gfx950 (AMD Instinct MI355X) draft-token
+ * verification library, libspecverify.so.
+ *
+ * Three operations of speculative decoding's verification step, batched over
+ * sequences and streamed over the full vocabulary:
+ *
+ *   spec_verify_chain        modified rejection sampling of a chain of drafts
+ *   spec_verify_tree_greedy  greedy acceptance of the longest matching tree path
+ *   ngram_propose            prompt n-gram lookup drafting (one-hot draft q)
+ *
+ * Pages that define the operations (cited by title):
+ *   [Production]  "Speculative Decoding in Production: From Draft Models to
+ *                 EAGLE-3 Dynamic Trees for 3x-5x Lossless Acceleration"
+ *                 (blog.llmgo.top)
+ *   [Accelerating] "Accelerating Autoregressive LLM Inference 3x with Lossless
+ *                 Speculative Decoding and EAGLE Heads" (x078.com)
+ *   [Medusa]      "Speculative decoding: Medusa, EAGLE, vLLM"
+ *                 (vikram-blog.pages.dev)
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer to caller-owned memory; the
+ *     library never allocates, frees or retains it.  Arrays are dense,
+ *     row-major, with the shapes given below.  Outputs must not alias inputs.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise.  Results are valid once the stream has
+ *     completed the call.
+ *   - Errors that the host can see (sizes, NULL pointers, dtype, workspace
+ *     size, alignment of the workspace) return a status synchronously and
+ *     launch nothing.  SPEC_ERR_HIP reports a failed launch.
+ *   - Errors in device data (an out-of-range token, a non-positive
+ *     temperature, a uniform outside (0, 1], a bad tree topology) cannot be
+ *     seen without a synchronisation: they mark the affected sequence in its
+ *     outputs instead (documented per call), and other sequences are unaffected.
+ *   - Results are deterministic: no floating-point atomics feed any result.
+ *   - A workspace is scratch for one call at a time: its contents need no
+ *     initialisation and are meaningless after the call (every byte a kernel
+ *     reads was written earlier in the same call).  Calls that overlap in time
+ *     (different streams) need different workspaces.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spec_status {
+  SPEC_OK = 0,
+  SPEC_ERR_INVALID_ARG = 1, /* a size, pointer or parameter the host can check is wrong */
+  SPEC_ERR_UNSUPPORTED = 2, /* beyond a documented limit (SPEC_MAX_*) */
+  SPEC_ERR_WORKSPACE = 3,   /* workspace NULL, too small or not 256-byte aligned */
+  SPEC_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} spec_status_t;
+
+typedef enum spec_dtype {
+  SPEC_F32 = 0,  /* IEEE float32 logits */
+  SPEC_BF16 = 1  /* bfloat16 logits (upper 16 bits of a float32) */
+} spec_dtype_t;
+
+typedef void* spec_stream_t; /* hipStream_t */
+
+#define SPEC_MAX_K 64            /* drafted positions per sequence (chain) */
+#define SPEC_MAX_TREE_NODES 1024 /* nodes per tree, root included */
+#define SPEC_MAX_NGRAM_N 16      /* longest n-gram the lookup matches */
+
+/* Human-readable name of a status code (static storage). */
+const char* spec_status_string(spec_status_t status);
+
+/* Detail message of the last non-OK status returned on the calling thread. */
+const char* spec_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Chain verification by modified rejection sampling.
+ *
+ * [Production] section I.1 "Verification via Modified Rejection Sampling":
+ * for drafted token x_k, alpha_k = min(1, p_k(x_k) / q_k(x_k)) (step 1); with
+ * r_k uniform, accept while r_k <= alpha_k and stop at the first rejection
+ * (step 2); on a rejection at position n draw the replacement from
+ * max(0, p_n - q_n) normalised (step 3).  The invariance theorem of the same
+ * section is why this reproduces the target distribution.
+ *
+ * Readings where the page is silent: p_k = softmax(target_k / T_b) and
+ * q_k = softmax(draft_k / T_b); when all k_b drafts are accepted a bonus token
+ * is drawn from p_{k_b} (target row k_b); every draw from a weight vector w
+ * uses inverse-CDF sampling in vocabulary order: the smallest index i whose
+ * inclusive prefix sum reaches u * sum(w).
+ *
+ * target_logits [B, K+1, V] dtype.  Row k scores draft k; row k_b gives the bonus.
+ * draft_logits  [B, K, V] dtype, or NULL: then q_k is one-hot at x_k (prompt
+ *               lookup drafting), alpha_k = p_k(x_k), and the residual is p_n
+ *               without x_n.  Draft rows are then never read.
+ * draft_tokens  [B, K] int32 in [0, V) for k < k_b (entries k >= k_b are ignored).
+ * draft_len     [B] int32 k_b in [0, K], or NULL meaning k_b = K for every b.
+ *               Rows beyond k_b are never read.
+ * temperature   [B] float32, > 0 and finite.
+ * u_accept      [B, K] float32 in (0, 1]: r_k of the accept test of draft k.
+ * u_final       [B] float32 in (0, 1]: the one uniform of the replacement or
+ *               bonus draw.
+ * out_tokens    [B, K+1] int32: x_0..x_{n-1}, then the drawn token, then -1.
+ * out_num_accepted [B] int32: n, the number of accepted drafts (0..k_b).
+ * out_probs     [B, K, 3] float32 (p_k(x_k), q_k(x_k), alpha_k) for k < k_b,
+ *               zeros for k >= k_b; or NULL.
+ * out_packed    [B*(K+1)] int32 or NULL: the emitted tokens of all sequences
+ *               back to back (sequence b's n_b+1 tokens at out_offsets[b]).
+ * out_offsets   [B+1] int32 or NULL (both or neither of packed/offsets):
+ *               exclusive prefix sums of the per-sequence token counts.
+ * workspace     device scratch of at least spec_verify_chain_workspace_size()
+ *               bytes, 256-byte aligned.
+ *
+ * Invalid device data for sequence b (token out of range, k_b outside [0, K],
+ * T not > 0 or not finite, a uniform outside (0, 1]) sets out_num_accepted[b]
+ * = -1, out_tokens[b, :] = -1, out_probs[b] = 0 and gives it no packed tokens.
+ * Limits: 1 <= K <= SPEC_MAX_K, V >= 1, B >= 0, B*(K+1)*V < 2^47.
+ * Logits may be -inf (probability 0); +inf and NaN are not supported; each
+ * used row needs at least one finite logit.
+ * ------------------------------------------------------------------------- */
+size_t spec_verify_chain_workspace_size(int B, int K, int V, spec_dtype_t dtype);
+
+spec_status_t spec_verify_chain(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                const int32_t* draft_tokens, const int32_t* draft_len,
+                                const float* temperature, const float* u_accept, const float* u_final,
+                                int B, int K, int V,
+                                int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                int32_t* out_packed, int32_t* out_offsets,
+                                void* workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Greedy tree verification.
+ *
+ * [Production] section III.2 "The Tree Attention Verification Mechanism": all
+ * branches of the flattened draft tree are scored in one target pass, and a
+ * matching branch is accepted even when a sibling is rejected.  [Medusa],
+ * "System Topology & Data Flow" figure (branch [t1,t2,t3] accepted, sibling
+ * [t1,t2',t4] rejected) and its temperature-0 usage example.
+ *
+ * Readings: node i (i >= 1) is accepted iff its parent is accepted and its token
+ * equals the argmax of its parent's row (smallest vocabulary index on ties; raw
+ * logits, so temperature plays no part); the accepted path ends at the deepest
+ * accepted node, smallest node index on ties; the bonus token is the argmax of
+ * that node's row.
+ *
+ * target_logits [B, N1, V] dtype: row i = next-token logits after node i; row 0 = root.
+ * parent        [B, N1] int32: parent[b,0] = -1, 0 <= parent[b,i] < i.
+ * node_token    [B, N1] int32 in [0, V) for i >= 1 (entry 0 is ignored).
+ * max_depth     capacity of the path outputs; must be >= the accepted depth.
+ * out_accept_len [B] int32: accepted draft nodes on the path (root excluded).
+ * out_tokens    [B, max_depth+1] int32: path tokens root-first, then the bonus, then -1.
+ * out_path_nodes [B, max_depth+1] int32: path node indices root-first, then -1.
+ * out_argmax    [B, N1] int32 row argmaxes, or NULL.
+ * workspace     >= spec_verify_tree_greedy_workspace_size() bytes, as for the chain.
+ *
+ * Invalid device data for sequence b (bad parent, token out of range, accepted
+ * depth > max_depth) sets out_accept_len[b] = -1 and its path outputs to -1.
+ * Limits: 1 <= N1 <= SPEC_MAX_TREE_NODES, V >= 1, 0 <= max_depth < N1 + 1.
+ * ------------------------------------------------------------------------- */
+size_t spec_verify_tree_greedy_workspace_size(int B, int N1, int V, spec_dtype_t dtype);
+
+spec_status_t spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dtype,
+                                      const int32_t* parent, const int32_t* node_token,
+                                      int B, int N1, int V, int max_depth,
+                                      int32_t* out_accept_len, int32_t* out_tokens, int32_t* out_path_nodes,
+                                      int32_t* out_argmax,
+                                      void* workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Prompt n-gram lookup drafting.
+ *
+ * [Accelerating]: a zero-VRAM prompt n-gram lookup as the draft mechanism,
+ * proposing K candidates; its deployment snippet (section 1) caps n at 4.
+ *
+ * Reading: for n = n_max down to n_min, find the earliest j with
+ * context[j : j+n] == context[L-n : L] and j + n <= L - 1 (overlap allowed);
+ * the first n that matches wins and the draft is context[j+n : min(j+n+K, L)].
+ * Verify the result with spec_verify_chain(draft_logits = NULL,
+ * draft_len = out_draft_len).
+ *
+ * context      [B, L_max] int32 token ids (any values; only equality is used).
+ * context_len  [B] int32 L in [1, L_max].
+ * out_draft_tokens [B, K] int32: the draft, then -1.
+ * out_draft_len [B] int32 in [0, K] (0 = no match).
+ * out_match_n  [B] int32 matched n (0 = none), or NULL.
+ *
+ * Invalid device data (L outside [1, L_max]) gives draft_len 0, match_n -1.
+ * Limits: 1 <= n_min <= n_max <= SPEC_MAX_NGRAM_N, 1 <= K <= SPEC_MAX_K, L_max >= 1.
+ * No workspace is needed.
+ * ------------------------------------------------------------------------- */
+spec_status_t ngram_propose(const int32_t* context, const int32_t* context_len,
+                            int B, int L_max, int n_min, int n_max, int K,
+                            int32_t* out_draft_tokens, int32_t* out_draft_len, int32_t* out_match_n,
+                            spec_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,108 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the headers declare,
+and rejects bad host-side arguments before touching the GPU."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECL = re.compile(r"^(?:const\s+)?(?:spec_status_t|size_t|int|char|void)\s*\*?\s*(\w+)\s*\(", re.M)
+
+
+def declared_functions():
+    names = []
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        with open(h) as f:
+            names += DECL.findall(f.read())
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from draft_token_verification_09_amd.build import library_path
+
+    path = library_path()
+    if not os.path.exists(path):
+        pytest.fail(f"{path} not built: run python -m draft_token_verification_09_amd.build")
+    from draft_token_verification_09_amd import binding
+
+    return binding.lib()
+
+
+def test_headers_declare_the_three_operations():
+    names = declared_functions()
+    for n in ("spec_verify_chain", "spec_verify_tree_greedy", "ngram_propose", "spec_verify_chain_workspace_size",
+              "spec_verify_tree_greedy_workspace_size", "spec_status_string", "spec_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.spec_status_string(0) == b"SPEC_OK"
+    assert lib.spec_status_string(3) == b"SPEC_ERR_WORKSPACE"
+
+
+def test_workspace_sizes_are_host_only(lib):
+    assert lib.spec_verify_chain_workspace_size(64, 5, 128256, 1) > 0
+    assert lib.spec_verify_chain_workspace_size(0, 5, 128256, 1) == 0
+    assert lib.spec_verify_chain_workspace_size(4, 65, 100, 1) == 0
+    assert lib.spec_verify_tree_greedy_workspace_size(32, 61, 128256, 1) > 0
+    assert lib.spec_verify_tree_greedy_workspace_size(1, 2000, 100, 1) == 0
+
+
+def test_host_argument_errors_return_before_any_launch(lib):
+    null = None
+    # K = 0
+    st = lib.spec_verify_chain(null, null, 1, null, null, null, null, null, 2, 0, 10,
+                               null, null, null, null, null, null, 0, null)
+    assert st == 1 and b"K >= 1" in lib.spec_last_error()
+    # K too large
+    st = lib.spec_verify_chain(null, null, 1, null, null, null, null, null, 2, 65, 10,
+                               null, null, null, null, null, null, 0, null)
+    assert st == 2
+    # unknown dtype
+    st = lib.spec_verify_chain(null, null, 7, null, null, null, null, null, 2, 5, 10,
+                               null, null, null, null, null, null, 0, null)
+    assert st == 1
+    # required pointers missing
+    st = lib.spec_verify_chain(null, null, 1, null, null, null, null, null, 2, 5, 10,
+                               null, null, null, null, null, null, 0, null)
+    assert st == 1
+    # packed without offsets
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.spec_verify_chain(fake, null, 1, fake, null, fake, fake, fake, 2, 5, 10,
+                               fake, fake, null, fake, null, null, 0, null)
+    assert st == 1
+    # workspace missing / too small / misaligned
+    st = lib.spec_verify_chain(fake, null, 1, fake, null, fake, fake, fake, 2, 5, 10,
+                               fake, fake, null, null, null, null, 0, null)
+    assert st == 3
+    st = lib.spec_verify_chain(fake, null, 1, fake, null, fake, fake, fake, 2, 5, 10,
+                               fake, fake, null, null, null, ctypes.c_void_p(1 << 20), 16, null)
+    assert st == 3
+    st = lib.spec_verify_chain(fake, null, 1, fake, null, fake, fake, fake, 2, 5, 10,
+                               fake, fake, null, null, null, ctypes.c_void_p((1 << 20) + 8), 1 << 20, null)
+    assert st == 3
+    # tree: too many nodes; max_depth beyond N1
+    st = lib.spec_verify_tree_greedy(null, 1, null, null, 1, 2000, 10, 3, null, null, null, null, null, 0, null)
+    assert st == 2
+    st = lib.spec_verify_tree_greedy(null, 1, null, null, 1, 4, 10, 9, null, null, null, null, null, 0, null)
+    assert st == 1
+    # n-gram: n_min > n_max, n_max too large
+    assert lib.ngram_propose(null, null, 1, 10, 3, 2, 5, null, null, null, null) == 1
+    assert lib.ngram_propose(null, null, 1, 10, 1, 17, 5, null, null, null, null) == 2
+
+
+def test_empty_batches_need_no_gpu_work(lib):
+    null = None
+    assert lib.spec_verify_tree_greedy(null, 1, null, null, 0, 4, 10, 3, null, null, null, null, null, 0, null) == 0
+    assert lib.ngram_propose(null, null, 0, 10, 1, 4, 5, null, null, null, null) == 0
