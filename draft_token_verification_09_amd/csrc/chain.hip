@@ -8,30 +8,35 @@
 // target row after the last accepted draft; draws are inverse-CDF in vocabulary
 // order (smallest index whose inclusive prefix reaches u * total).
 //
-// Three kernels, streaming the vocabulary in 16-byte vectors.  No state survives a
-// call: every workspace byte a kernel reads was written earlier in the same call.
+// Three kernels (four with packed output), ordered by the stream:
 //
-//  chain_stats    grid = B x R x C workgroups, R = K+1 target rows (+ K draft rows),
-//                 C chunks per row.  Each workgroup reduces one chunk to
-//                 (o, s) = (max(l) * log2(e)/T, sum exp2(l * log2(e)/T - o)).
-//  chain_decide   grid = B x C (draft logits) or B x 1 (one-hot draft).  Every
-//                 workgroup of a sequence combines the chunk partials into per-row
-//                 (O, S), evaluates p(x_k), q(x_k), alpha_k and the accept tests of
-//                 all drafted positions at once (one lane per position) and takes
-//                 the first rejection n with a wave ballot; the workgroup of chunk 0
-//                 stores the decision, the accepted prefix and the probabilities.
-//                 After a rejection with a draft distribution, workgroup c computes
-//                 the residual mass max(0, p_n - q_n) of chunk c of row n.
-//  chain_draw     grid = B.  Selects the chunk holding u * W from the chunk prefix
-//                 sums (residual masses, or, for a bonus draw from p and for a
-//                 one-hot draft whose residual is p without x_n, masses that follow
-//                 from chain_stats' partials), re-reads that one chunk, finds the
-//                 token in vocabulary order and writes the outputs.
+//  chain_stats   grid = B x R x C workgroups: R = K+1 target rows (+ K draft rows), C
+//                chunks per row.  Each workgroup reduces one chunk (non-temporal 16-byte
+//                loads) to (o, s) = (max(l) * log2(e)/T, sum exp2(l * log2(e)/T - o))
+//                and, if the chunk holds the row's drafted token x_k, copies l(x_k) out
+//                of its registers.  This is the pass that reads every logit.
+//  chain_decide  grid = B x C (draft logits) or B x 1 (one-hot draft).  Every workgroup
+//                of a sequence combines its chunk partials into per-row (O, S) and
+//                evaluates p(x_k), q(x_k), alpha_k and the accept tests of all drafted
+//                positions at once (one lane per position), taking the first rejection
+//                n with a wave ballot -- the same decision in each, from the same data
+//                by the same arithmetic; workgroup 0 stores it with the accepted prefix,
+//                the probabilities and the count.  After a rejection with a draft
+//                distribution, workgroup c computes the residual masses
+//                max(0, p_n - q_n) of the segments of chunk c of row n.
+//  chain_draw    grid = B.  Narrows u * W down to a segment, a lane and an element (see
+//                chain_draw) and writes the drawn token.  For a bonus draw from p, or a
+//                one-hot draft whose residual is p without x_n, the chunk masses follow
+//                from chain_stats' partials.
+//  chain_pack    grid = 1, only for packed output: offsets and packed tokens.
+//
+// No workgroup waits for another and no state outlives a call: each kernel reads only
+// what an earlier kernel of the same call wrote.
 //
 // Softmax is evaluated in the exp2 domain: with scale = log2(e)/T,
-// p_i = exp2(l_i * scale - O) / S, where O is the float max(l) * scale used by
-// every term and S = sum_chunks s_c * exp2(o_c - O).  Per-element work is fp32;
-// cross-lane, cross-chunk and prefix sums are fp64.
+// p_i = exp2(l_i * scale - O) / S, where O is the float max(l) * scale used by every
+// term and S = sum_chunks s_c * exp2(o_c - O).  Per-element work is fp32; cross-lane,
+// cross-chunk and prefix sums are fp64.
 #include <math.h>
 
 #include "device_common.h"
@@ -43,9 +48,9 @@ namespace specv {
 enum ChainMode : int { kModeInvalid = 0, kModeResidual = 1, kModeBonus = 2, kModeOneHot = 3, kModeFallbackP = 4 };
 
 struct RowStat {
-  float o;     // offset in the log2 domain: max(l) * scale over the chunk (-inf if empty)
+  float o;  // log2-domain offset: max(l) * scale over the chunk (-inf if every logit is -inf)
   float pad;
-  double s;    // sum over the chunk of exp2(l * scale - o)
+  double s;  // sum over the chunk of exp2(l * scale - o)
 };
 
 struct ChainDecision {
@@ -53,12 +58,11 @@ struct ChainDecision {
   int n;         // accepted drafts
   int kb;        // draft length
   int excl_tok;  // one-hot mode: token removed from the residual
-  int row;       // row (position) of the final draw
+  int row;       // position whose row(s) the final draw samples
   float scale;   // log2(e) / T
   float Ot, Od;  // row offsets (target, draft)
   float invSt, invSd;
   float p_excl;  // one-hot mode: p_n(x_n)
-  float pad;
   double St, Sd;
 };
 
@@ -76,25 +80,26 @@ struct ChainArgs {
   float* out_probs;
   int32_t* out_packed;
   int32_t* out_offsets;
-  RowStat* part;
-  ChainDecision* dec;
-  double* wmass;
+  RowStat* part;        // [B, R, C]
+  float* gath;          // [B, R] logit of the drafted token in each scoring row
+  ChainDecision* dec;   // [B]
+  double* wseg;         // [B, C, NV] residual mass per segment
 };
 
 template <int DT>
-__device__ inline const void* target_row(const ChainArgs& a, int b, int k) {
+__device__ __forceinline__ const void* target_row(const ChainArgs& a, int b, int k) {
   return static_cast<const char*>(a.target) +
          (static_cast<size_t>(b) * (a.K + 1) + k) * static_cast<size_t>(a.V) * Elem<DT>::kBytes;
 }
 
 template <int DT>
-__device__ inline const void* draft_row(const ChainArgs& a, int b, int k) {
+__device__ __forceinline__ const void* draft_row(const ChainArgs& a, int b, int k) {
   return static_cast<const char*>(a.draft) +
          (static_cast<size_t>(b) * a.K + k) * static_cast<size_t>(a.V) * Elem<DT>::kBytes;
 }
 
 // Draft length of sequence b clamped to [0, K] (an out-of-range value is flagged later).
-__device__ inline int clamped_len(const ChainArgs& a, int b) {
+__device__ __forceinline__ int clamped_len(const ChainArgs& a, int b) {
   if (!a.draft_len) return a.K;
   const int v = a.draft_len[b];
   return v < 0 ? 0 : (v > a.K ? a.K : v);
@@ -102,137 +107,158 @@ __device__ inline int clamped_len(const ChainArgs& a, int b) {
 
 // Row rr of the stats grid: rr <= K is target row rr, otherwise draft row rr-K-1
 // (draft rows exist only when draft logits are given; then R = 2K+1, else R = K+1).
-__device__ inline bool row_needed(const ChainArgs& a, int rr, int kb) {
+__device__ __forceinline__ bool row_needed(const ChainArgs& a, int rr, int kb) {
   return rr <= a.K ? (rr <= kb) : (a.draft != nullptr && rr - (a.K + 1) < kb);
+}
+
+// Drafted position whose token row rr scores (target row k or draft row k, k < kb), else -1.
+__device__ __forceinline__ int row_position(const ChainArgs& a, int rr, int kb) {
+  const int k = rr <= a.K ? rr : rr - (a.K + 1);
+  return k < kb ? k : -1;
 }
 
 // ---------------------------------------------------------------- decision
 
-template <int DT>
-__device__ void chain_decide_positions(const ChainArgs& a, int b, int kb, bool write_outputs, ChainDecision* out,
-                                       const float* sO, const double* sS);
+constexpr int kStage = 1024;  // chunk partials staged in shared memory per batch of rows
 
-// Every workgroup of sequence b calls this with all lanes; the decision lands in *out
-// (shared memory) in all of them, identically (same inputs, same arithmetic, same order).
-// Only the workgroup with write_outputs stores it and the decision-level outputs.
+// Called by every lane of every chain_decide workgroup of sequence b.  The decision lands
+// in *out (shared memory) identically in all of them: same data, same arithmetic, same
+// order.  Only the workgroup with write_outputs stores the decision-level outputs.  The
+// loads of a batch of rows are all issued before any is used: one memory round trip.
 template <int DT>
-__device__ void chain_decide(const ChainArgs& a, int b, int kb, bool write_outputs, ChainDecision* out) {
+__device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, bool write_outputs, ChainDecision* out) {
   __shared__ float sO[2 * SPEC_MAX_K + 1];
   __shared__ double sS[2 * SPEC_MAX_K + 1];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  __shared__ float st_o[kStage];
+  __shared__ double st_s[kStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int R = a.R, C = a.C;
 
-  // Per-row statistics from the chunk partials.
-  for (int rr = w; rr < a.R; rr += kWaves) {
-    if (!row_needed(a, rr, kb)) continue;
-    const RowStat* ps = a.part + (static_cast<size_t>(b) * a.R + rr) * a.C;
-    float om = -INFINITY;
-    for (int c = lane; c < a.C; c += 64) om = fmaxf(om, ps[c].o);
-    om = wave_max(om);
-    double sum = 0.0;
-    for (int c = lane; c < a.C; c += 64) {
-      const RowStat st = ps[c];
-      if (st.o != -INFINITY) sum += st.s * static_cast<double>(exp2_fast(st.o - om));
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      sO[rr] = om;
-      sS[rr] = sum;
-    }
-  }
-  __syncthreads();
-  if (w == 0) chain_decide_positions<DT>(a, b, kb, write_outputs, out, sO, sS);
-  __syncthreads();
-}
-
-template <int DT>
-__device__ void chain_decide_positions(const ChainArgs& a, int b, int kb, bool write_outputs, ChainDecision* out,
-                                       const float* sO, const double* sS) {
-  const int lane = threadIdx.x & 63;
-  // One lane per drafted position: p(x_k), q(x_k), alpha_k and the accept test.
-  const float T = a.temperature[b];
-  const float scale = kLog2e / T;
+  // Wave 0, lane k: the inputs of drafted position k (issued before the partials arrive).
   const int k = lane;
-  const bool active = k < kb;
-  bool bad = false, accepted = true;
-  float P = 0.f, Q = 0.f, alpha = 0.f;
+  const bool active = w == 0 && k < kb;
   int x = 0;
+  float u = 1.f, gt = 0.f, gd = 0.f;
   if (active) {
     x = a.tokens[static_cast<size_t>(b) * a.K + k];
-    const float u = a.u_accept[static_cast<size_t>(b) * a.K + k];
-    if (x < 0 || x >= a.V || !(u > 0.f && u <= 1.f)) {
-      bad = true;
-    } else {
-      const float lt = Elem<DT>::value(target_row<DT>(a, b, k), x);
-      P = static_cast<float>(static_cast<double>(exp2_fast(fmaf(lt, scale, -sO[k]))) / sS[k]);
-      if (a.draft) {
-        const int rd = a.K + 1 + k;
-        const float ld = Elem<DT>::value(draft_row<DT>(a, b, k), x);
-        Q = static_cast<float>(static_cast<double>(exp2_fast(fmaf(ld, scale, -sO[rd]))) / sS[rd]);
-      } else {
-        Q = 1.f;
-      }
-      alpha = Q > 0.f ? fminf(1.f, P / Q) : (P > 0.f ? 1.f : 0.f);
-      accepted = u <= alpha;
-    }
+    u = a.u_accept[static_cast<size_t>(b) * a.K + k];
+    const float* g = a.gath + static_cast<size_t>(b) * R;
+    gt = g[k];
+    if (a.draft) gd = g[a.K + 1 + k];
   }
-  const unsigned long long rej = __ballot(active && !accepted);
-  const unsigned long long badm = __ballot(active && bad);
-  const int n = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : kb;
-  const int kb_raw = a.draft_len ? a.draft_len[b] : a.K;
+  const float T = a.temperature[b];
   const float uf = a.u_final[b];
-  const bool invalid = badm != 0ull || !(T > 0.f) || !(T <= 3.4e38f) || kb_raw < 0 || kb_raw > a.K ||
-                       !(uf > 0.f && uf <= 1.f);
-  const float Pn = __shfl(P, n < 64 ? n : 0, 64);
-  const int xn = __shfl(x, n < 64 ? n : 0, 64);
+  const int kb_raw = a.draft_len ? a.draft_len[b] : a.K;
 
-  if (write_outputs && a.out_probs && k < a.K) {
-    float* pr = a.out_probs + (static_cast<size_t>(b) * a.K + k) * 3;
-    const bool keep = active && !invalid;
-    pr[0] = keep ? P : 0.f;
-    pr[1] = keep ? Q : 0.f;
-    pr[2] = keep ? alpha : 0.f;
+  // Per-row (O, S) from the chunk partials.
+  const int rows_per_batch = max(1, kStage / C);
+  for (int r0 = 0; r0 < R; r0 += rows_per_batch) {
+    const int r1 = min(R, r0 + rows_per_batch);
+    const int items = (r1 - r0) * C;
+    const RowStat* ps = a.part + (static_cast<size_t>(b) * R + r0) * C;
+    for (int i = tid; i < items; i += kThreads) {
+      const RowStat st = ps[i];
+      st_o[i] = st.o;
+      st_s[i] = st.s;
+    }
+    __syncthreads();
+    for (int rr = r0 + w; rr < r1; rr += kWaves) {
+      if (!row_needed(a, rr, kb)) continue;
+      const int base = (rr - r0) * C;
+      float om = -INFINITY;
+      for (int c = lane; c < C; c += 64) om = fmaxf(om, st_o[base + c]);
+      om = wave_max(om);
+      double sum = 0.0;
+      for (int c = lane; c < C; c += 64) {
+        const float o = st_o[base + c];
+        if (o != -INFINITY) sum += st_s[base + c] * static_cast<double>(exp2_fast(o - om));
+      }
+      sum = wave_sum(sum);
+      if (lane == 0) {
+        sO[rr] = om;
+        sS[rr] = sum;
+      }
+    }
+    __syncthreads();
   }
-  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-  if (write_outputs) {
-    if (invalid) {
-      for (int kk = lane; kk <= a.K; kk += 64) ot[kk] = -1;
-    } else if (k < n) {
-      ot[k] = x;
+
+  if (w == 0) {
+    // One lane per drafted position: p(x_k), q(x_k), alpha_k and the accept test.
+    const float scale = kLog2e / T;
+    bool bad = false, accepted = true;
+    float P = 0.f, Q = 0.f, alpha = 0.f;
+    if (active) {
+      if (x < 0 || x >= a.V || !(u > 0.f && u <= 1.f)) {
+        bad = true;
+      } else {
+        P = static_cast<float>(static_cast<double>(exp2_fast(fmaf(gt, scale, -sO[k]))) / sS[k]);
+        if (a.draft) {
+          const int rd = a.K + 1 + k;
+          Q = static_cast<float>(static_cast<double>(exp2_fast(fmaf(gd, scale, -sO[rd]))) / sS[rd]);
+        } else {
+          Q = 1.f;
+        }
+        alpha = Q > 0.f ? fminf(1.f, P / Q) : (P > 0.f ? 1.f : 0.f);
+        accepted = u <= alpha;
+      }
+    }
+    const unsigned long long rej = __ballot(active && !accepted);
+    const unsigned long long badm = __ballot(active && bad);
+    const int n = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : kb;
+    const bool invalid = badm != 0ull || !(T > 0.f) || !(T <= 3.4e38f) || kb_raw < 0 || kb_raw > a.K ||
+                         !(uf > 0.f && uf <= 1.f);
+    const float Pn = __shfl(P, n < 64 ? n : 0, 64);
+    const int xn = __shfl(x, n < 64 ? n : 0, 64);
+    if (write_outputs) {
+      if (a.out_probs && k < a.K) {
+        float* pr = a.out_probs + (static_cast<size_t>(b) * a.K + k) * 3;
+        const bool keep = active && !invalid;
+        pr[0] = keep ? P : 0.f;
+        pr[1] = keep ? Q : 0.f;
+        pr[2] = keep ? alpha : 0.f;
+      }
+      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+      if (invalid) {
+        for (int kk = lane; kk <= a.K; kk += 64) ot[kk] = -1;
+      } else if (k < n) {
+        ot[k] = x;
+      }
+      if (lane == 0) a.out_num[b] = invalid ? -1 : n;
+    }
+    if (lane == 0) {
+      ChainDecision d{};
+      d.n = n;
+      d.kb = kb;
+      d.scale = scale;
+      d.excl_tok = -1;
+      if (invalid) {
+        d.mode = kModeInvalid;
+      } else if (n == kb) {
+        d.mode = kModeBonus;
+        d.row = kb;
+      } else if (a.draft) {
+        d.mode = kModeResidual;
+        d.row = n;
+        d.Od = sO[a.K + 1 + n];
+        d.Sd = sS[a.K + 1 + n];
+        d.invSd = static_cast<float>(1.0 / d.Sd);
+      } else {
+        d.mode = kModeOneHot;
+        d.row = n;
+        d.excl_tok = xn;
+        d.p_excl = Pn;
+      }
+      if (!invalid) {
+        d.Ot = sO[d.row];
+        d.St = sS[d.row];
+        d.invSt = static_cast<float>(1.0 / d.St);
+      }
+      *out = d;
     }
   }
-  if (lane == 0) {
-    if (write_outputs) a.out_num[b] = invalid ? -1 : n;
-    ChainDecision d{};
-    d.n = n;
-    d.kb = kb;
-    d.scale = scale;
-    d.excl_tok = -1;
-    if (invalid) {
-      d.mode = kModeInvalid;
-    } else if (n == kb) {
-      d.mode = kModeBonus;
-      d.row = kb;
-    } else if (a.draft) {
-      d.mode = kModeResidual;
-      d.row = n;
-      d.Od = sO[a.K + 1 + n];
-      d.Sd = sS[a.K + 1 + n];
-      d.invSd = static_cast<float>(1.0 / d.Sd);
-    } else {
-      d.mode = kModeOneHot;
-      d.row = n;
-      d.excl_tok = xn;
-      d.p_excl = Pn;
-    }
-    if (!invalid) {
-      d.Ot = sO[d.row];
-      d.St = sS[d.row];
-      d.invSt = static_cast<float>(1.0 / d.St);
-    }
-    *out = d;
-    if (write_outputs) a.dec[b] = d;
-  }
+  __syncthreads();
 }
 
 template <int DT, int NV, bool VEC>
@@ -241,6 +267,8 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   __shared__ double s_d[kWaves];
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
+  constexpr int kSeg = ChunkShape<DT, NV>::kSegment;
+  constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
   const int g = blockIdx.x;
   const int c = g % a.C;
   const int rr = (g / a.C) % a.R;
@@ -249,9 +277,25 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   if (!row_needed(a, rr, kb)) return;
   const void* row = rr <= a.K ? target_row<DT>(a, b, rr) : draft_row<DT>(a, b, rr - (a.K + 1));
   const float scale = kLog2e / a.temperature[b];
+  const int pos = row_position(a, rr, kb);
+  const int x = pos >= 0 ? a.tokens[static_cast<size_t>(b) * a.K + pos] : -1;
 
   u32x4 raw[NV];
-  load_chunk<DT, NV, VEC>(raw, row, a.V, c);
+  load_chunk<DT, NV, VEC, true>(raw, row, a.V, c);
+
+  // The lane holding the drafted token's logit copies it out (bit-exact).
+  if (x >= 0 && x < a.V && x / kChunk == c) {
+    const int local = x - c * kChunk;
+    if (threadIdx.x == (local / E) % kThreads) {
+      const int j = local / kSeg;
+      u32x4 v = raw[0];
+#pragma unroll
+      for (int jj = 1; jj < NV; ++jj)
+        if (jj == j) v = raw[jj];
+      a.gath[static_cast<size_t>(b) * a.R + rr] = EL::get(v, local % E);
+    }
+  }
+
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < NV; ++j)
@@ -279,11 +323,11 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   if (threadIdx.x == 0) a.part[(static_cast<size_t>(b) * a.R + rr) * a.C + c] = RowStat{ob, 0.f, sb};
 }
 
-// ---------------------------------------------------------------- final draw (one workgroup per sequence)
+// ---------------------------------------------------------------- final draw
 
-// Weight of element e of the final draw's row(s) for a chunk already in registers.
+// Weight of element e of the final draw's row(s).
 template <int DT>
-__device__ inline float draw_weight(int mode, const ChainDecision& d, float lt, float ld, int e) {
+__device__ __forceinline__ float draw_weight(int mode, const ChainDecision& d, float lt, float ld, int e) {
   const float p = exp2_fast(fmaf(lt, d.scale, -d.Ot)) * d.invSt;
   if (mode == kModeResidual) {
     const float q = exp2_fast(fmaf(ld, d.scale, -d.Od)) * d.invSd;
@@ -293,204 +337,236 @@ __device__ inline float draw_weight(int mode, const ChainDecision& d, float lt, 
   return p;
 }
 
+// The last sequence to finish packs the emitted tokens of the batch back to back.
+__device__ __forceinline__ void chain_pack(const ChainArgs& a) {
+  __shared__ int s_i[kWaves];
+  const int tid = threadIdx.x;
+  const int per = (a.B + kThreads - 1) / kThreads;
+  const int b0 = min(a.B, tid * per);
+  const int b1 = min(a.B, b0 + per);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int n = a.out_num[b];
+    local += n >= 0 ? n + 1 : 0;
+  }
+  int total = 0;
+  int run = block_exclusive_scan_int(local, s_i, &total);
+  for (int b = b0; b < b1; ++b) {
+    const int n = a.out_num[b];
+    const int cnt = n >= 0 ? n + 1 : 0;
+    a.out_offsets[b] = run;
+    const int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+    for (int i = 0; i < cnt; ++i) a.out_packed[run + i] = ot[i];
+    run += cnt;
+  }
+  if (tid == 0) a.out_offsets[a.B] = total;
+}
+
+// One workgroup draws the final token of sequence b and writes it.
+//
+// Vocabulary order inside a chunk is segment-major (a segment = one 16-byte vector per
+// lane), then lane, then element.  The draw narrows u * W down in three levels:
+//  1. units: segments for a residual draw (masses from chain_decide's residual pass),
+//     chunks otherwise (masses from chain_stats' partials); block prefix scan;
+//  2. for a chunk: the lanes load that chunk of the one row, and per-segment totals
+//     pick the segment;
+//  3. the lanes load one vector each of the selected segment, a block scan of their
+//     sums picks the lane, and that lane scans its elements.
 template <int DT, int NV, bool VEC>
-__device__ void chain_finalize(const ChainArgs& a, int b, ChainDecision d) {
+__device__ __forceinline__ void chain_draw(const ChainArgs& a, int b, const ChainDecision& d) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
+  constexpr int kSeg = ChunkShape<DT, NV>::kSegment;
   constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
   __shared__ double s_d[kWaves];
   __shared__ int s_i[kWaves];
   __shared__ double s_seg[NV][kWaves];
   __shared__ double s_base;
-  __shared__ int s_c;
+  __shared__ int s_y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int C = a.C;
+  int mode = d.mode;
+  const float uf = a.u_final[b];
 
-  if (d.mode != kModeInvalid) {
-    int mode = d.mode;
-    const float uf = a.u_final[b];
-    const int per = (C + kThreads - 1) / kThreads;
-    const int c0 = tid * per;
-    const int c1 = min(C, c0 + per);
-
-    auto chunk_mass = [&](int c) -> double {
-      if (mode == kModeResidual) return a.wmass[static_cast<size_t>(b) * C + c];
-      const RowStat st = a.part[(static_cast<size_t>(b) * a.R + d.row) * C + c];
-      double mc = st.o == -INFINITY ? 0.0 : st.s * static_cast<double>(exp2_fast(st.o - d.Ot)) / d.St;
-      if (mode == kModeOneHot && c == d.excl_tok / kChunk) mc = fmax(0.0, mc - static_cast<double>(d.p_excl));
-      return mc;
-    };
-
-    // Chunk prefix sums (fp64, chunk order); W = their total.
-    double local = 0.0;
-    for (int c = c0; c < c1; ++c) local += chunk_mass(c);
-    double W = block_sum(local, s_d);
-    if (!(W > 0.0) && mode == kModeResidual) {
-      mode = kModeFallbackP;  // residual lost to rounding: draw from p_n itself
-      local = 0.0;
-      for (int c = c0; c < c1; ++c) local += chunk_mass(c);
-      W = block_sum(local, s_d);
-    }
-    const double t = static_cast<double>(uf) * W;
-    // exclusive prefix of this lane's chunk range
-    const double incl = wave_inclusive_scan(local);
-    __syncthreads();
-    if (lane == 63) s_d[w] = incl;
-    __syncthreads();
-    double before = incl - local;
-    for (int i = 0; i < w; ++i) before += s_d[i];
-    int cand = INT_MAX;
-    {
-      double run = before;
-      for (int c = c0; c < c1; ++c) {
-        const double mc = chunk_mass(c);
-        run += mc;
-        if (run >= t && mc > 0.0) {
-          cand = c;
-          break;
+  // ---- level 1: unit masses, this lane's share (at most 4) in registers
+  int units = mode == kModeResidual ? C * NV : C;
+  int per = (units + kThreads - 1) / kThreads;
+  int u0 = tid * per;
+  double mass[4];
+  auto load_masses = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int u = u0 + q;
+      double m = 0.0;
+      if (q < per && u < units) {
+        if (mode == kModeResidual) {
+          m = a.wseg[static_cast<size_t>(b) * C * NV + u];
+        } else {
+          const RowStat st = a.part[(static_cast<size_t>(b) * a.R + d.row) * C + u];
+          m = st.o == -INFINITY ? 0.0 : st.s * static_cast<double>(exp2_fast(st.o - d.Ot)) / d.St;
+          if (mode == kModeOneHot && u == d.excl_tok / kChunk) m = fmax(0.0, m - static_cast<double>(d.p_excl));
         }
       }
+      mass[q] = m;
     }
-    int csel = block_min_int(cand, s_i);
-    if (csel == INT_MAX) {  // rounding left t above every prefix: last chunk with mass
-      int lastc = -1;
-      for (int c = c0; c < c1; ++c)
-        if (chunk_mass(c) > 0.0) lastc = c;
-      csel = block_max_int(lastc, s_i);
-      if (csel < 0) csel = 0;
+  };
+  load_masses();
+  double local = mass[0] + mass[1] + mass[2] + mass[3];
+  double W = block_sum(local, s_d);
+  if (!(W > 0.0) && mode == kModeResidual) {
+    mode = kModeFallbackP;  // residual lost to rounding: draw from p_n itself
+    units = C;
+    per = (units + kThreads - 1) / kThreads;
+    u0 = tid * per;
+    load_masses();
+    local = mass[0] + mass[1] + mass[2] + mass[3];
+    W = block_sum(local, s_d);
+  }
+  const double t = static_cast<double>(uf) * W;
+  const double incl = wave_inclusive_scan(local);
+  __syncthreads();
+  if (lane == 63) s_d[w] = incl;
+  __syncthreads();
+  double before = incl - local;
+  for (int i = 0; i < w; ++i) before += s_d[i];
+  int cand = INT_MAX, lastu = -1;
+  {
+    double run = before;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      run += mass[q];
+      if (mass[q] > 0.0) {
+        lastu = u0 + q;
+        if (cand == INT_MAX && run >= t) cand = u0 + q;
+      }
     }
-    if (c0 <= csel && csel < c1) {
-      double run = before;
-      for (int c = c0; c < csel; ++c) run += chunk_mass(c);
-      s_base = run;
-    }
-    __syncthreads();
-    const double t_loc = t - s_base;
+  }
+  int usel = block_min_int(cand, s_i);
+  if (usel == INT_MAX) {  // rounding left t above every prefix: last unit with mass
+    usel = block_max_int(lastu, s_i);
+    if (usel < 0) usel = 0;
+  }
+  if (u0 <= usel && usel < u0 + per) {
+    double run = before;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (u0 + q < usel) run += mass[q];
+    s_base = run;
+  }
+  __syncthreads();
+  double t_loc = t - s_base;
 
-    // Re-read the selected chunk.  Vocabulary order inside a chunk is segment-major,
-    // then lane, then element: each lane sums its vector of every segment, a block
-    // scan of those sums finds the (segment, lane) whose range reaches t_loc, and
-    // that one lane scans its own vector element by element.
-    const int base = csel * kChunk;
-    const void* row_t = target_row<DT>(a, b, d.row);
-    const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : nullptr;
-    float seg_local[NV];
-    int last_pos = -1;
+  const void* row_t = target_row<DT>(a, b, d.row);
+  const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : nullptr;
+  int seg_start;
+  if (mode == kModeResidual) {
+    seg_start = (usel / NV) * kChunk + (usel % NV) * kSeg;
+  } else {
+    // ---- level 2: segment totals of chunk usel of the one row
+    const int c = usel;
+    float sl[NV];
     {
-      u32x4 rt[NV], rd[NV];
-      load_chunk<DT, NV, VEC>(rt, row_t, a.V, csel);
-      if (mode == kModeResidual) load_chunk<DT, NV, VEC>(rd, row_d, a.V, csel);
+      u32x4 raw[NV];
+      load_chunk<DT, NV, VEC>(raw, row_t, a.V, c);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         float sj = 0.f;
 #pragma unroll
         for (int i = 0; i < E; ++i) {
-          const int e = base + (j * kThreads + tid) * E + i;
-          const float ld = mode == kModeResidual ? EL::get(rd[j], i) : 0.f;
-          const float wv = e < a.V ? draw_weight<DT>(mode, d, EL::get(rt[j], i), ld, e) : 0.f;
-          sj += wv;
-          if (wv > 0.f) last_pos = e;
+          const int e = c * kChunk + (j * kThreads + tid) * E + i;
+          sj += e < a.V ? draw_weight<DT>(mode, d, EL::get(raw[j], i), 0.f, e) : 0.f;
         }
-        seg_local[j] = sj;
+        sl[j] = sj;
       }
     }
-    double seg_incl[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      seg_incl[j] = wave_inclusive_scan(static_cast<double>(seg_local[j]));
-      if (lane == 63) s_seg[j][w] = seg_incl[j];
+      const double ws = wave_sum(static_cast<double>(sl[j]));
+      if (lane == 0) s_seg[j][w] = ws;
     }
     __syncthreads();
-    int key = INT_MAX;
-    double key_before = 0.0;
-    double seg_base = 0.0;
+    int js = -1, jlast = 0;
+    double run = 0.0, run_last = 0.0;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      double before = seg_base + seg_incl[j] - static_cast<double>(seg_local[j]);
-      for (int i = 0; i < w; ++i) before += s_seg[j][i];
-      if (key == INT_MAX && seg_local[j] > 0.f && before + static_cast<double>(seg_local[j]) >= t_loc) {
-        key = j * kThreads + tid;
-        key_before = before;
-      }
-      for (int i = 0; i < kWaves; ++i) seg_base += s_seg[j][i];
-    }
-    const int kmin = block_min_int(key, s_i);
-    int y;
-    if (kmin == INT_MAX) {  // rounding left t_loc above the chunk total: last positive weight
-      y = block_max_int(last_pos, s_i);
-      if (y < 0) y = base;    // unreachable: the selected chunk has positive mass
-    } else {
-      if (key == kmin) {
-        const int e0 = base + kmin * E;
-        const u32x4 vt = load_vector<DT, VEC>(row_t, a.V, e0);
-        u32x4 vd = vt;
-        if (mode == kModeResidual) vd = load_vector<DT, VEC>(row_d, a.V, e0);
-        double run = key_before;
-        int pick = -1, lastp = -1;
+      double tot = 0.0;
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-          const int e = e0 + i;
-          const float ld = mode == kModeResidual ? EL::get(vd, i) : 0.f;
-          const float wv = e < a.V ? draw_weight<DT>(mode, d, EL::get(vt, i), ld, e) : 0.f;
-          run += wv;
-          if (wv > 0.f) {
-            lastp = e;
-            if (pick < 0 && run >= t_loc) pick = e;
-          }
+      for (int i = 0; i < kWaves; ++i) tot += s_seg[j][i];
+      if (js < 0) {
+        if (tot > 0.0) {
+          jlast = j;
+          run_last = run;
         }
-        s_c = pick >= 0 ? pick : lastp;
-      }
-      __syncthreads();
-      y = s_c;
-    }
-
-    const int n = d.n;
-    int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-    for (int kk = n + tid; kk <= a.K; kk += kThreads) ot[kk] = (kk == n) ? y : -1;
-
-    if (a.out_packed) {
-      double cnt = 0.0;
-      for (int bb = tid; bb < b; bb += kThreads) {
-        const ChainDecision e = a.dec[bb];
-        cnt += e.mode == kModeInvalid ? 0.0 : static_cast<double>(e.n + 1);
-      }
-      const int off = static_cast<int>(block_sum(cnt, s_d));
-      for (int i = tid; i <= n; i += kThreads)
-        a.out_packed[off + i] = i < n ? a.tokens[static_cast<size_t>(b) * a.K + i] : y;
-      if (tid == 0) {
-        a.out_offsets[b] = off;
-        if (b == a.B - 1) a.out_offsets[a.B] = off + n + 1;
+        if (tot > 0.0 && run + tot >= t_loc) {
+          js = j;
+        } else {
+          run += tot;
+        }
       }
     }
-    return;
+    if (js < 0) {  // rounding: take the last segment with mass
+      js = jlast;
+      run = run_last;
+    }
+    t_loc -= run;
+    seg_start = c * kChunk + js * kSeg;
   }
 
-  // Invalid sequence: no tokens, only its packed offset.
-  if (a.out_packed) {
-    double cnt = 0.0;
-    for (int bb = tid; bb < b; bb += kThreads) {
-      const ChainDecision e = a.dec[bb];
-      cnt += e.mode == kModeInvalid ? 0.0 : static_cast<double>(e.n + 1);
-    }
-    const int off = static_cast<int>(block_sum(cnt, s_d));
-    if (tid == 0) {
-      a.out_offsets[b] = off;
-      if (b == a.B - 1) a.out_offsets[a.B] = off;
-    }
+  // ---- level 3: one vector per lane of the selected segment
+  const int e0 = seg_start + tid * E;
+  const u32x4 vt = load_vector<DT, VEC>(row_t, a.V, e0);
+  u32x4 vd = vt;
+  if (mode == kModeResidual) vd = load_vector<DT, VEC>(row_d, a.V, e0);
+  float wl[E];
+  float lsum = 0.f;
+  int last_pos = -1;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int e = e0 + i;
+    const float ld = mode == kModeResidual ? EL::get(vd, i) : 0.f;
+    wl[i] = e < a.V ? draw_weight<DT>(mode, d, EL::get(vt, i), ld, e) : 0.f;
+    lsum += wl[i];
+    if (wl[i] > 0.f) last_pos = e;
   }
+  const double lincl = wave_inclusive_scan(static_cast<double>(lsum));
+  __syncthreads();
+  if (lane == 63) s_d[w] = lincl;
+  __syncthreads();
+  double lbefore = lincl - static_cast<double>(lsum);
+  for (int i = 0; i < w; ++i) lbefore += s_d[i];
+  const int key = (lsum > 0.f && lbefore + static_cast<double>(lsum) >= t_loc) ? tid : INT_MAX;
+  const int kmin = block_min_int(key, s_i);
+  int y;
+  if (kmin == INT_MAX) {  // rounding left t_loc above the segment total: last positive weight
+    y = block_max_int(last_pos, s_i);
+    if (y < 0) y = seg_start;  // unreachable: the selected segment has positive mass
+  } else {
+    if (tid == kmin) {
+      double run = lbefore;
+      int pick = -1;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        run += wl[i];
+        if (pick < 0 && wl[i] > 0.f && run >= t_loc) pick = e0 + i;
+      }
+      s_y = pick >= 0 ? pick : last_pos;
+    }
+    __syncthreads();
+    y = s_y;
+  }
+  const int n = d.n;
+  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+  for (int kk = n + tid; kk <= a.K; kk += kThreads) ot[kk] = (kk == n) ? y : -1;
 }
 
-// Residual mass max(0, p_n - q_n) of one chunk of a rejected sequence's row pair.
-// grid = B x C2 (C2 = C with draft logits, else 1).  Every workgroup of sequence b
-// evaluates the sequence's decision from chain_stats' partials; the one with c == 0
-// stores it with the accepted prefix, the probabilities and the count.  With a
-// rejection and a draft distribution, workgroup c then computes the residual mass
-// max(0, p_n - q_n) of chunk c of row n.
+// grid = B x C2: the decision of sequence b in every workgroup, stored by workgroup 0;
+// after a rejection with draft logits, workgroup c computes the residual masses
+// max(0, p_n - q_n) of the segments of chunk c of row n.
 template <int DT, int NV, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainArgs a, int C2) {
-  __shared__ double s_d[kWaves];
+  __shared__ double s_seg[NV][kWaves];
   __shared__ ChainDecision s_dec;
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
@@ -499,6 +575,7 @@ __global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainArgs a, int
   const int b = g / C2;
   chain_decide<DT>(a, b, clamped_len(a, b), c == 0, &s_dec);
   const ChainDecision d = s_dec;
+  if (c == 0 && threadIdx.x == 0) a.dec[b] = d;
   if (d.mode != kModeResidual) return;
   u32x4 rt[NV], rd[NV];
   load_chunk<DT, NV, VEC>(rt, target_row<DT>(a, b, d.row), a.V, c);
@@ -514,20 +591,33 @@ __global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainArgs a, int
       acc[j] += fmaxf(0.f, p - q);
     }
   }
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
 #pragma unroll
-  for (int h = NV / 2; h >= 1; h >>= 1)
+  for (int j = 0; j < NV; ++j) {
+    const double ws = wave_sum(static_cast<double>(acc[j]));
+    if (lane == 0) s_seg[j][w] = ws;
+  }
+  __syncthreads();
+  if (threadIdx.x < NV) {
+    double tot = 0.0;
 #pragma unroll
-    for (int j = 0; j < h; ++j) acc[j] += acc[j + h];
-  const double sb = block_sum(static_cast<double>(acc[0]), s_d);
-  if (threadIdx.x == 0) a.wmass[static_cast<size_t>(b) * a.C + c] = sb;
+    for (int i = 0; i < kWaves; ++i) tot += s_seg[threadIdx.x][i];
+    a.wseg[(static_cast<size_t>(b) * a.C + c) * NV + threadIdx.x] = tot;
+  }
 }
 
-// The final draw of each sequence (one workgroup per sequence).
+// grid = B: the final draw of every valid sequence.
 template <int DT, int NV, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_draw_kernel(ChainArgs a) {
   const int b = blockIdx.x;
-  chain_finalize<DT, NV, VEC>(a, b, a.dec[b]);
+  const ChainDecision d = a.dec[b];
+  if (d.mode == kModeInvalid) return;
+  chain_draw<DT, NV, VEC>(a, b, d);
 }
+
+// grid = 1: offsets and packed tokens of the batch (only when packed output is asked for).
+__global__ __launch_bounds__(kThreads) void chain_pack_kernel(ChainArgs a) { chain_pack(a); }
 
 __global__ void write_zero_offset_kernel(int32_t* offsets) {
   if (threadIdx.x == 0) offsets[0] = 0;
@@ -537,7 +627,7 @@ __global__ void write_zero_offset_kernel(int32_t* offsets) {
 
 struct ChainLayout {
   int nv, C, R;
-  size_t off_part, off_dec, off_wmass, bytes;
+  size_t off_gath, off_part, off_dec, off_wseg, bytes;
 };
 
 static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
@@ -548,12 +638,14 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
   const long long chunk = static_cast<long long>(L.nv) * kThreads * epv;
   L.C = static_cast<int>((V + chunk - 1) / chunk);
   size_t off = 0;
+  L.off_gath = off;
+  off = align_up(off + sizeof(float) * static_cast<size_t>(B) * L.R, 256);
   L.off_part = off;
   off = align_up(off + sizeof(RowStat) * static_cast<size_t>(B) * L.R * L.C, 256);
   L.off_dec = off;
   off = align_up(off + sizeof(ChainDecision) * static_cast<size_t>(B), 256);
-  L.off_wmass = off;
-  off = align_up(off + sizeof(double) * static_cast<size_t>(B) * L.C, 256);
+  L.off_wseg = off;
+  off = align_up(off + sizeof(double) * static_cast<size_t>(B) * L.C * L.nv, 256);
   L.bytes = off;
   return L;
 }
@@ -576,8 +668,15 @@ static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
     const spec_status_t st = scope.finish();
     if (st != SPEC_OK) return st;
   }
-  LaunchScope scope("chain_draw", stream);
-  hipLaunchKernelGGL((chain_draw_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, stream, a);
+  {
+    LaunchScope scope("chain_draw", stream);
+    hipLaunchKernelGGL((chain_draw_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, stream, a);
+    const spec_status_t st = scope.finish();
+    if (st != SPEC_OK) return st;
+  }
+  if (!a.out_packed) return SPEC_OK;
+  LaunchScope scope("chain_pack", stream);
+  hipLaunchKernelGGL(chain_pack_kernel, dim3(1), dim3(kThreads), 0, stream, a);
   return scope.finish();
 }
 
@@ -631,6 +730,8 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   const ChainLayout L = chain_layout(B, K, V, dtype);
   const double groups = static_cast<double>(B) * L.R * L.C;
   if (groups > 2147483647.0) return fail(SPEC_ERR_UNSUPPORTED, "grid of %.0f workgroups too large", groups);
+  if (L.C * L.nv > 4 * kThreads)
+    return fail(SPEC_ERR_UNSUPPORTED, "V = %d needs more than %d segments", V, 4 * kThreads);
   if (!workspace) return fail(SPEC_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(SPEC_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < L.bytes)
@@ -655,9 +756,10 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   a.out_packed = out_packed;
   a.out_offsets = out_offsets;
   char* ws = static_cast<char*>(workspace);
+  a.gath = reinterpret_cast<float*>(ws + L.off_gath);
   a.part = reinterpret_cast<RowStat*>(ws + L.off_part);
   a.dec = reinterpret_cast<ChainDecision*>(ws + L.off_dec);
-  a.wmass = reinterpret_cast<double*>(ws + L.off_wmass);
+  a.wseg = reinterpret_cast<double*>(ws + L.off_wseg);
 
   const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits) &&
                    (draft_logits == nullptr || aligned16(draft_logits));

@@ -6,8 +6,8 @@
 //   contiguous memory and, inside a segment, vocabulary order is lane order.
 // * Reductions use cross-lane shuffles within a wave and a small LDS array across
 //   the 4 waves of a workgroup.
-// * Partial results pass from one kernel to the next through the workspace; the
-//   kernel boundary orders them, so no inter-workgroup synchronisation is used.
+// * Partial results pass between kernels through the workspace; the stream orders the
+//   kernels, so no workgroup waits for another.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,15 +31,15 @@ struct Elem<kF32> {
   static constexpr int kPerVec = 4;
   static constexpr int kBytes = 4;
   static constexpr uint32_t kNegInfBits = 0xff800000u;
-  __device__ static inline float get(const u32x4& v, int i) { return __uint_as_float(v[i]); }
-  __device__ static inline uint32_t bits(const void* base, size_t idx) {
+  __device__ static __forceinline__ float get(const u32x4& v, int i) { return __uint_as_float(v[i]); }
+  __device__ static __forceinline__ uint32_t bits(const void* base, size_t idx) {
     return reinterpret_cast<const uint32_t*>(base)[idx];
   }
-  __device__ static inline float value(const void* base, size_t idx) {
+  __device__ static __forceinline__ float value(const void* base, size_t idx) {
     return reinterpret_cast<const float*>(base)[idx];
   }
   // pack E element bit patterns (already in the low bits) into a vector
-  __device__ static inline void put(u32x4& v, int i, uint32_t b) { v[i] = b; }
+  __device__ static __forceinline__ void put(u32x4& v, int i, uint32_t b) { v[i] = b; }
 };
 
 template <>
@@ -47,17 +47,17 @@ struct Elem<kBF16> {
   static constexpr int kPerVec = 8;
   static constexpr int kBytes = 2;
   static constexpr uint32_t kNegInfBits = 0xff80u;
-  __device__ static inline float get(const u32x4& v, int i) {
+  __device__ static __forceinline__ float get(const u32x4& v, int i) {
     const uint32_t w = v[i >> 1];
     return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
   }
-  __device__ static inline uint32_t bits(const void* base, size_t idx) {
+  __device__ static __forceinline__ uint32_t bits(const void* base, size_t idx) {
     return reinterpret_cast<const uint16_t*>(base)[idx];
   }
-  __device__ static inline float value(const void* base, size_t idx) {
+  __device__ static __forceinline__ float value(const void* base, size_t idx) {
     return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(base)[idx]) << 16);
   }
-  __device__ static inline void put(u32x4& v, int i, uint32_t b) {
+  __device__ static __forceinline__ void put(u32x4& v, int i, uint32_t b) {
     uint32_t w = v[i >> 1];
     w = (i & 1) ? ((w & 0x0000ffffu) | (b << 16)) : ((w & 0xffff0000u) | b);
     v[i >> 1] = w;
@@ -71,10 +71,17 @@ struct ChunkShape {
   static constexpr int kChunk = NV * kSegment;   // elements per chunk
 };
 
+// 16-byte vector load; NT marks it non-temporal (streamed once: no reuse expected).
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
 // Load chunk `c` of a row of V logits into registers.  Elements past V read as -inf.
 // VEC: the row starts 16-byte aligned, so whole vectors can be loaded.
-template <int DT, int NV, bool VEC>
-__device__ inline void load_chunk(u32x4 (&raw)[NV], const void* row, int V, int c) {
+template <int DT, int NV, bool VEC, bool NT = false>
+__device__ __forceinline__ void load_chunk(u32x4 (&raw)[NV], const void* row, int V, int c) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   const int base = c * ChunkShape<DT, NV>::kChunk;
@@ -83,14 +90,15 @@ __device__ inline void load_chunk(u32x4 (&raw)[NV], const void* row, int V, int 
     const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
                                                     static_cast<size_t>(base) * EL::kBytes);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) raw[j] = p[j * kThreads + lane];
+    for (int j = 0; j < NV; ++j) raw[j] = load16<NT>(p + j * kThreads + lane);
     return;
   }
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int e0 = base + (j * kThreads + lane) * E;
     if (VEC && e0 + E <= V) {
-      raw[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + static_cast<size_t>(e0) * EL::kBytes);
+      raw[j] = load16<NT>(reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
+                                                       static_cast<size_t>(e0) * EL::kBytes));
     } else {
       u32x4 v = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -106,7 +114,7 @@ __device__ inline void load_chunk(u32x4 (&raw)[NV], const void* row, int V, int 
 // Load the one vector of a row that starts at element e0 (a multiple of E); elements
 // past V read as -inf.
 template <int DT, bool VEC>
-__device__ inline u32x4 load_vector(const void* row, int V, int e0) {
+__device__ __forceinline__ u32x4 load_vector(const void* row, int V, int e0) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   if (VEC && e0 + E <= V)
@@ -119,32 +127,32 @@ __device__ inline u32x4 load_vector(const void* row, int V, int e0) {
 
 // ---------------------------------------------------------------- reductions
 
-__device__ inline float wave_max(float v) {
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
 }
 
-__device__ inline double wave_sum(double v) {
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
-__device__ inline int wave_min_int(int v) {
+__device__ __forceinline__ int wave_min_int(int v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
   return v;
 }
 
-__device__ inline int wave_max_int(int v) {
+__device__ __forceinline__ int wave_max_int(int v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
   return v;
 }
 
 // Inclusive scan over the lanes of a wave (lane order).
-__device__ inline double wave_inclusive_scan(double v) {
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -154,8 +162,31 @@ __device__ inline double wave_inclusive_scan(double v) {
   return v;
 }
 
+// Exclusive scan of one int per lane over the workgroup (lane order); *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan_int(int v, int* lds4, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  __syncthreads();
+  if (lane == 63) lds4[w] = incl;
+  __syncthreads();
+  int before = incl - v, sum = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) before += lds4[i];
+    sum += lds4[i];
+  }
+  *total = sum;
+  return before;
+}
+
 // Workgroup-wide reductions (every lane receives the result).  Contain __syncthreads.
-__device__ inline float block_max(float v, float* lds4) {
+__device__ __forceinline__ float block_max(float v, float* lds4) {
   v = wave_max(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
@@ -167,7 +198,7 @@ __device__ inline float block_max(float v, float* lds4) {
   return r;
 }
 
-__device__ inline double block_sum(double v, double* lds4) {
+__device__ __forceinline__ double block_sum(double v, double* lds4) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
@@ -179,7 +210,7 @@ __device__ inline double block_sum(double v, double* lds4) {
   return r;
 }
 
-__device__ inline int block_min_int(int v, int* lds4) {
+__device__ __forceinline__ int block_min_int(int v, int* lds4) {
   v = wave_min_int(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
@@ -191,7 +222,7 @@ __device__ inline int block_min_int(int v, int* lds4) {
   return r;
 }
 
-__device__ inline int block_max_int(int v, int* lds4) {
+__device__ __forceinline__ int block_max_int(int v, int* lds4) {
   v = wave_max_int(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
@@ -203,6 +234,6 @@ __device__ inline int block_max_int(int v, int* lds4) {
   return r;
 }
 
-__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace specv

@@ -10,11 +10,11 @@
 // the deepest accepted node (smallest node index on ties); the bonus is that node's
 // row argmax.
 //
-// Two kernels.  tree_argmax (grid = B x N1 x C): each workgroup finds (max, first
-// index) over one chunk of one node row.  tree_select (grid = B): combines the chunks
-// into per-node argmaxes, validates the topology, walks each node's path to the root
-// in parallel (one lane per node), picks the deepest accepted node and writes the
-// compacted path.  No state survives a call.
+// Two kernels.  tree_argmax (grid = B x N1 x C): each workgroup finds (max, first index)
+// over one chunk of one node row (non-temporal loads).  tree_select (grid = B) combines
+// the chunks into per-node argmaxes, validates the topology, walks each node's path to
+// the root in parallel (one lane per node), picks the deepest accepted node and writes
+// the compacted path.  Nothing in the workspace outlives a call.
 #include <math.h>
 
 #include "device_common.h"
@@ -37,13 +37,13 @@ struct TreeArgs {
   int32_t* out_tokens;
   int32_t* out_nodes;
   int32_t* out_argmax;
-  ArgMax* part;
+  ArgMax* part;  // [B, N1, C]
 };
 
 // (v, i) beats (w, j) if v > w, or v == w and i < j.
-__device__ inline bool better(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
+__device__ __forceinline__ bool better(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
 
-__device__ inline void wave_argmax(float& v, int& i) {
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const float ov = __shfl_xor(v, off, 64);
@@ -55,39 +55,64 @@ __device__ inline void wave_argmax(float& v, int& i) {
   }
 }
 
+constexpr int kStageT = 2048;  // chunk partials staged in shared memory per batch of rows
+
+// grid = B.  Topology and partials are staged in shared memory first, so the path walks
+// below touch no global memory.
 __global__ __launch_bounds__(kThreads) void tree_select_kernel(TreeArgs a) {
   const int b = blockIdx.x;
   __shared__ int s_amax[SPEC_MAX_TREE_NODES];
+  __shared__ int s_par[SPEC_MAX_TREE_NODES];
+  __shared__ int s_tok[SPEC_MAX_TREE_NODES];
+  __shared__ float st_v[kStageT];
+  __shared__ int st_i[kStageT];
   __shared__ int s_key[kWaves];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int N1 = a.N1;
+  const int C = a.C;
   const int32_t* par = a.parent + static_cast<size_t>(b) * N1;
   const int32_t* tok = a.token + static_cast<size_t>(b) * N1;
+  for (int i = tid; i < N1; i += kThreads) {
+    s_par[i] = par[i];
+    s_tok[i] = tok[i];
+  }
+  if (tid == 0) s_bad = 0;
 
   // Row argmax per node from the chunk partials (one wave per row).
-  for (int r = w; r < N1; r += kWaves) {
-    const ArgMax* ps = a.part + (static_cast<size_t>(b) * N1 + r) * a.C;
-    float v = -INFINITY;
-    int i = INT_MAX;
-    for (int c = lane; c < a.C; c += 64) {
-      const ArgMax p = ps[c];
-      if (better(p.v, p.i, v, i)) {
-        v = p.v;
-        i = p.i;
-      }
+  const int rows_per_batch = max(1, kStageT / C);
+  for (int r0 = 0; r0 < N1; r0 += rows_per_batch) {
+    const int r1 = min(N1, r0 + rows_per_batch);
+    const int items = (r1 - r0) * C;
+    const ArgMax* ps = a.part + (static_cast<size_t>(b) * N1 + r0) * C;
+    for (int i = tid; i < items; i += kThreads) {
+      const ArgMax p = ps[i];
+      st_v[i] = p.v;
+      st_i[i] = p.i;
     }
-    wave_argmax(v, i);
-    if (lane == 0) s_amax[r] = i;
+    __syncthreads();
+    for (int r = r0 + w; r < r1; r += kWaves) {
+      const int base = (r - r0) * C;
+      float v = -INFINITY;
+      int i = INT_MAX;
+      for (int c = lane; c < C; c += 64) {
+        if (better(st_v[base + c], st_i[base + c], v, i)) {
+          v = st_v[base + c];
+          i = st_i[base + c];
+        }
+      }
+      wave_argmax(v, i);
+      if (lane == 0) s_amax[r] = i;
+    }
+    __syncthreads();
   }
-  if (tid == 0) s_bad = (par[0] != -1) ? 1 : 0;
-  __syncthreads();
   // Topology and token checks.
+  if (tid == 0 && s_par[0] != -1) s_bad = 1;
   for (int i = 1 + tid; i < N1; i += kThreads) {
-    const int p = par[i];
-    const int t = tok[i];
+    const int p = s_par[i];
+    const int t = s_tok[i];
     if (p < 0 || p >= i || t < 0 || t >= a.V) atomicOr(&s_bad, 1);
   }
   __syncthreads();
@@ -101,8 +126,8 @@ __global__ __launch_bounds__(kThreads) void tree_select_kernel(TreeArgs a) {
       int v = i, depth = 0;
       bool ok = true;
       while (v != 0) {
-        const int p = par[v];
-        ok = ok && (tok[v] == s_amax[p]);
+        const int p = s_par[v];
+        ok = ok && (s_tok[v] == s_amax[p]);
         v = p;
         ++depth;
       }
@@ -129,9 +154,9 @@ __global__ __launch_bounds__(kThreads) void tree_select_kernel(TreeArgs a) {
     for (int k = tid; k < D1; k += kThreads) {
       if (k < depth) {
         int v = best;
-        for (int s = 0; s < depth - 1 - k; ++s) v = par[v];
+        for (int s = 0; s < depth - 1 - k; ++s) v = s_par[v];
         on[k] = v;
-        ot[k] = tok[v];
+        ot[k] = s_tok[v];
       } else {
         on[k] = -1;
         ot[k] = (k == depth) ? s_amax[best] : -1;
@@ -157,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void tree_argmax_kernel(TreeArgs a) {
   const void* row = static_cast<const char*>(a.target) +
                     (static_cast<size_t>(b) * a.N1 + r) * static_cast<size_t>(a.V) * EL::kBytes;
   u32x4 raw[NV];
-  load_chunk<DT, NV, VEC>(raw, row, a.V, c);
+  load_chunk<DT, NV, VEC, true>(raw, row, a.V, c);
   // Lane-local scan in increasing vocabulary order; strict '>' keeps the first maximum.
   const int first = c * kChunk + threadIdx.x * E;
   float bv = -INFINITY;
@@ -262,6 +287,7 @@ spec_status_t spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dt
   if (static_cast<double>(B) * N1 * V >= 140737488355328.0) return fail(SPEC_ERR_UNSUPPORTED, "B*N1*V too large");
   const TreeLayout L = tree_layout(B, N1, V, dtype);
   if (static_cast<double>(B) * N1 * L.C > 2147483647.0) return fail(SPEC_ERR_UNSUPPORTED, "grid too large");
+  if (L.C > kStageT) return fail(SPEC_ERR_UNSUPPORTED, "V = %d needs more than %d chunks", V, kStageT);
   if (!workspace) return fail(SPEC_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(SPEC_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < L.bytes)
