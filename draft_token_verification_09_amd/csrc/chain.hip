@@ -209,8 +209,8 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
     const int n = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : kb;
     const bool invalid = badm != 0ull || !(T > 0.f) || !(T <= 3.4e38f) || kb_raw < 0 || kb_raw > a.K ||
                          !(uf > 0.f && uf <= 1.f);
-    const float Pn = __shfl(P, n < 64 ? n : 0, 64);
-    const int xn = __shfl(x, n < 64 ? n : 0, 64);
+    const float Pn = lane_broadcast(P, n < 64 ? n : 0);
+    const int xn = lane_broadcast(x, n < 64 ? n : 0);
     if (write_outputs) {
       if (a.out_probs && k < a.K) {
         float* pr = a.out_probs + (static_cast<size_t>(b) * a.K + k) * 3;

@@ -11,6 +11,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace specv {
@@ -125,112 +127,163 @@ __device__ __forceinline__ u32x4 load_vector(const void* row, int V, int e0) {
   return v;
 }
 
-// ---------------------------------------------------------------- reductions
+// ---------------------------------------------------------------- wave64 scans and reductions
+//
+// Cross-lane steps use DPP (data-parallel primitives: operands read from another lane
+// inside the VALU, no LDS round trip): row_shr:1,2,4,8 scan each 16-lane row, then
+// row_bcast:15 (rows 1, 3) and row_bcast:31 (rows 2, 3) carry the row totals across, which
+// yields an inclusive scan over the wave; lane 63 then holds the total and
+// v_readlane broadcasts it.  Every lane of the wave must be active.
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+namespace dppc {
+constexpr int kRowShr1 = 0x111;
+constexpr int kRowShr2 = 0x112;
+constexpr int kRowShr4 = 0x114;
+constexpr int kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+}  // namespace dppc
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_int(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_float(float old, float v) {
+  return __int_as_float(dpp_int<CTRL, ROW_MASK>(__float_as_int(old), __float_as_int(v)));
 }
 
-__device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
-  return v;
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_double(double old, double v) {
+  const long long o = __double_as_longlong(old), x = __double_as_longlong(v);
+  const int lo = dpp_int<CTRL, ROW_MASK>(static_cast<int>(o), static_cast<int>(x));
+  const int hi = dpp_int<CTRL, ROW_MASK>(static_cast<int>(o >> 32), static_cast<int>(x >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
 }
 
-__device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-  return v;
+__device__ __forceinline__ float lane_broadcast(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ int lane_broadcast(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ double lane_broadcast(double v, int lane) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(x), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(x >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
 }
 
-// Inclusive scan over the lanes of a wave (lane order).
+#define SPECV_WAVE_SCAN(T, DPP, OP, ID, x)              \
+  do {                                                  \
+    x = OP(x, DPP<dppc::kRowShr1>(ID, x));              \
+    x = OP(x, DPP<dppc::kRowShr2>(ID, x));              \
+    x = OP(x, DPP<dppc::kRowShr4>(ID, x));              \
+    x = OP(x, DPP<dppc::kRowShr8>(ID, x));              \
+    x = OP(x, (DPP<dppc::kRowBcast15, 0xa>(ID, x)));    \
+    x = OP(x, (DPP<dppc::kRowBcast31, 0xc>(ID, x)));    \
+  } while (0)
+
+__device__ __forceinline__ double add_d(double a, double b) { return a + b; }
+__device__ __forceinline__ int add_i(int a, int b) { return a + b; }
+__device__ __forceinline__ int min_i(int a, int b) { return min(a, b); }
+__device__ __forceinline__ int max_i(int a, int b) { return max(a, b); }
+__device__ __forceinline__ float max_f(float a, float b) { return fmaxf(a, b); }
+
+// Inclusive scans over the lanes of a wave (lane order).
 __device__ __forceinline__ double wave_inclusive_scan(double v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+  SPECV_WAVE_SCAN(double, dpp_double, add_d, 0.0, v);
   return v;
+}
+__device__ __forceinline__ int wave_inclusive_scan_int(int v) {
+  SPECV_WAVE_SCAN(int, dpp_int, add_i, 0, v);
+  return v;
+}
+
+// Reductions: every lane receives the result.
+__device__ __forceinline__ float wave_max(float v) {
+  SPECV_WAVE_SCAN(float, dpp_float, max_f, -INFINITY, v);
+  return lane_broadcast(v, 63);
+}
+__device__ __forceinline__ double wave_sum(double v) { return lane_broadcast(wave_inclusive_scan(v), 63); }
+__device__ __forceinline__ int wave_min_int(int v) {
+  SPECV_WAVE_SCAN(int, dpp_int, min_i, INT_MAX, v);
+  return lane_broadcast(v, 63);
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+  SPECV_WAVE_SCAN(int, dpp_int, max_i, INT_MIN, v);
+  return lane_broadcast(v, 63);
 }
 
 // Exclusive scan of one int per lane over the workgroup (lane order); *total gets the sum.
-__device__ __forceinline__ int block_exclusive_scan_int(int v, int* lds4, int* total) {
+// NW = waves in the workgroup; lds holds NW ints.
+template <int NW = kWaves>
+__device__ __forceinline__ int block_exclusive_scan_int(int v, int* lds, int* total) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_inclusive_scan_int(v);
   __syncthreads();
-  if (lane == 63) lds4[w] = incl;
+  if (lane == 63) lds[w] = incl;
   __syncthreads();
   int before = incl - v, sum = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    if (i < w) before += lds4[i];
-    sum += lds4[i];
+  for (int i = 0; i < NW; ++i) {
+    if (i < w) before += lds[i];
+    sum += lds[i];
   }
   *total = sum;
   return before;
 }
 
 // Workgroup-wide reductions (every lane receives the result).  Contain __syncthreads.
-__device__ __forceinline__ float block_max(float v, float* lds4) {
+template <int NW = kWaves>
+__device__ __forceinline__ float block_max(float v, float* lds) {
   v = wave_max(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds4[w] = v;
+  if ((threadIdx.x & 63) == 0) lds[w] = v;
   __syncthreads();
-  float r = lds4[0];
+  float r = lds[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, lds4[i]);
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, lds[i]);
   return r;
 }
 
-__device__ __forceinline__ double block_sum(double v, double* lds4) {
+template <int NW = kWaves>
+__device__ __forceinline__ double block_sum(double v, double* lds) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds4[w] = v;
+  if ((threadIdx.x & 63) == 0) lds[w] = v;
   __syncthreads();
   double r = 0.0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) r += lds4[i];
+  for (int i = 0; i < NW; ++i) r += lds[i];
   return r;
 }
 
-__device__ __forceinline__ int block_min_int(int v, int* lds4) {
+template <int NW = kWaves>
+__device__ __forceinline__ int block_min_int(int v, int* lds) {
   v = wave_min_int(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds4[w] = v;
+  if ((threadIdx.x & 63) == 0) lds[w] = v;
   __syncthreads();
-  int r = lds4[0];
+  int r = lds[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = min(r, lds4[i]);
+  for (int i = 1; i < NW; ++i) r = min(r, lds[i]);
   return r;
 }
 
-__device__ __forceinline__ int block_max_int(int v, int* lds4) {
+template <int NW = kWaves>
+__device__ __forceinline__ int block_max_int(int v, int* lds) {
   v = wave_max_int(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds4[w] = v;
+  if ((threadIdx.x & 63) == 0) lds[w] = v;
   __syncthreads();
-  int r = lds4[0];
+  int r = lds[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = max(r, lds4[i]);
+  for (int i = 1; i < NW; ++i) r = max(r, lds[i]);
   return r;
 }
 
