@@ -39,11 +39,18 @@ def progress(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+HOST_SIDE_MARKER = "// ---------------------------------------------------------------- host side"
+
+
 def source_digest(paths) -> str:
+    """Digest of the device code in `paths`: each file up to its host-side marker line (launch
+    and argument checking code after it does not change what the kernels read or write)."""
     h = hashlib.sha256()
     for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+            text = f.read()
+        cut = text.find(HOST_SIDE_MARKER.encode())
+        h.update(text if cut < 0 else text[:cut])
     return h.hexdigest()[:16]
 
 

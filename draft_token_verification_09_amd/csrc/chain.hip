@@ -655,7 +655,7 @@ static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
   {
     const long long g1 = static_cast<long long>(a.B) * a.R * a.C;
     LaunchScope scope("chain_stats", stream);
-    hipLaunchKernelGGL((chain_stats_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0, stream, a);
+    hipExtLaunchKernelGGL((chain_stats_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0, stream, scope.start(), scope.stop(), 0, a);
     const spec_status_t st = scope.finish();
     if (st != SPEC_OK) return st;
   }
@@ -663,20 +663,20 @@ static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
     const int C2 = a.draft ? a.C : 1;  // a one-hot draft never takes the residual path
     const long long g2 = static_cast<long long>(a.B) * C2;
     LaunchScope scope("chain_decide", stream);
-    hipLaunchKernelGGL((chain_decide_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, stream,
+    hipExtLaunchKernelGGL((chain_decide_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, stream, scope.start(), scope.stop(), 0,
                        a, C2);
     const spec_status_t st = scope.finish();
     if (st != SPEC_OK) return st;
   }
   {
     LaunchScope scope("chain_draw", stream);
-    hipLaunchKernelGGL((chain_draw_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, stream, a);
+    hipExtLaunchKernelGGL((chain_draw_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, stream, scope.start(), scope.stop(), 0, a);
     const spec_status_t st = scope.finish();
     if (st != SPEC_OK) return st;
   }
   if (!a.out_packed) return SPEC_OK;
   LaunchScope scope("chain_pack", stream);
-  hipLaunchKernelGGL(chain_pack_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+  hipExtLaunchKernelGGL(chain_pack_kernel, dim3(1), dim3(kThreads), 0, stream, scope.start(), scope.stop(), 0, a);
   return scope.finish();
 }
 
@@ -717,7 +717,7 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   if (B == 0) {
     if (out_offsets) {
       LaunchScope scope("chain_empty", s);
-      hipLaunchKernelGGL(write_zero_offset_kernel, dim3(1), dim3(64), 0, s, out_offsets);
+      hipExtLaunchKernelGGL(write_zero_offset_kernel, dim3(1), dim3(64), 0, s, scope.start(), scope.stop(), 0, out_offsets);
       return scope.finish();
     }
     return SPEC_OK;

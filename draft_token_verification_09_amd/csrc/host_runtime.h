@@ -2,6 +2,7 @@
 // optional per-kernel event timing, workspace carving and tuning knobs.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -13,19 +14,23 @@ namespace specv {
 // Record a thread-local detail message and return `status`.
 spec_status_t fail(spec_status_t status, const char* fmt, ...);
 
-// Brackets one kernel launch: when timing is enabled it records a HIP event pair on
-// `stream` around the launch under `name`; on destruction it checks the launch.
+// One kernel launch under `name`.  When timing is enabled, start() and stop() are a HIP
+// event pair for hipExtLaunchKernelGGL, which stamps them at the kernel's own dispatch
+// and completion on `stream` (otherwise both are null and nothing is recorded); on
+// destruction the launch is checked.
 class LaunchScope {
  public:
   LaunchScope(const char* name, hipStream_t stream);
   ~LaunchScope();
+  hipEvent_t start() const { return start_; }
+  hipEvent_t stop() const { return stop_; }
   // Status of the launch (checks hipGetLastError); call after the kernel launch.
   spec_status_t finish();
 
  private:
   const char* name_;
-  hipStream_t stream_;
-  int slot_;
+  hipEvent_t start_;
+  hipEvent_t stop_;
   bool finished_;
 };
 

@@ -85,26 +85,21 @@ hipEvent_t take_event(TimingState& t) {
 
 }  // namespace
 
-LaunchScope::LaunchScope(const char* name, hipStream_t stream)
-    : name_(name), stream_(stream), slot_(-1), finished_(false) {
+LaunchScope::LaunchScope(const char* name, hipStream_t)
+    : name_(name), start_(nullptr), stop_(nullptr), finished_(false) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> lock(t.mu);
   if (!t.enabled) return;
   TimedRecord r{name, take_event(t), take_event(t)};
   if (!r.start || !r.stop) return;
-  if (hipEventRecord(r.start, stream) != hipSuccess) return;
   t.records.push_back(r);
-  slot_ = static_cast<int>(t.records.size()) - 1;
+  start_ = r.start;
+  stop_ = r.stop;
 }
 
 spec_status_t LaunchScope::finish() {
   finished_ = true;
   const hipError_t e = hipGetLastError();
-  if (slot_ >= 0) {
-    TimingState& t = timing();
-    std::lock_guard<std::mutex> lock(t.mu);
-    if (slot_ < static_cast<int>(t.records.size())) hipEventRecord(t.records[slot_].stop, stream_);
-  }
   if (e != hipSuccess) return fail(SPEC_ERR_HIP, "launch of %s failed: %s", name_, hipGetErrorString(e));
   return SPEC_OK;
 }
@@ -223,7 +218,7 @@ spec_status_t spec_probe_read(const void* src, size_t bytes, uint32_t* out, spec
     return fail(SPEC_ERR_INVALID_ARG, "probe_read needs a 16-byte aligned source and size");
   const unsigned grid = static_cast<unsigned>(device_cu_count() * 8);
   LaunchScope scope("probe_read", static_cast<hipStream_t>(stream));
-  hipLaunchKernelGGL(probe_read_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+  hipExtLaunchKernelGGL(probe_read_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), scope.start(), scope.stop(), 0,
                      static_cast<const u32x4*>(src), bytes / 16, out);
   return scope.finish();
 }
@@ -233,7 +228,7 @@ spec_status_t spec_probe_copy(const void* src, void* dst, size_t bytes, spec_str
     return fail(SPEC_ERR_INVALID_ARG, "probe_copy needs 16-byte aligned buffers and size");
   const unsigned grid = static_cast<unsigned>(device_cu_count() * 8);
   LaunchScope scope("probe_copy", static_cast<hipStream_t>(stream));
-  hipLaunchKernelGGL(probe_copy_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+  hipExtLaunchKernelGGL(probe_copy_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), scope.start(), scope.stop(), 0,
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
   return scope.finish();
 }
