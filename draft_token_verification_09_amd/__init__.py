@@ -8,11 +8,13 @@ ctypes binding (binding.py) whose functions carry the C entry points' names.
 from .binding import (  # noqa: F401
     ChainResult,
     NgramResult,
+    PreparedCall,
     SpecError,
     TreeResult,
     lib,
     loaded_library_path,
     ngram_propose,
+    prepare_spec_verify_chain,
     spec_probe_copy,
     spec_probe_read,
     spec_timing_collect,

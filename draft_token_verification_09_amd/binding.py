@@ -163,15 +163,12 @@ def spec_verify_chain_workspace_size(B: int, K: int, V: int, dtype_code: int) ->
     return int(lib().spec_verify_chain_workspace_size(B, K, V, dtype_code))
 
 
-def spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
-                      draft_tokens: torch.Tensor, temperature: torch.Tensor, u_accept: torch.Tensor,
-                      u_final: torch.Tensor, draft_len: Optional[torch.Tensor] = None, *,
-                      want_probs: bool = True, want_packed: bool = False,
-                      out: Optional[ChainResult] = None, workspace_buf: Optional[torch.Tensor] = None,
-                      stream=None) -> ChainResult:
-    """Batched chain verification (spec_verify_chain).  Shapes: target [B, K+1, V],
-    draft [B, K, V] or None (one-hot draft), draft_tokens [B, K] int32, temperature [B]
-    float32, u_accept [B, K] float32, u_final [B] float32, draft_len [B] int32 or None."""
+def _chain_call(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor], draft_tokens: torch.Tensor,
+                temperature: torch.Tensor, u_accept: torch.Tensor, u_final: torch.Tensor,
+                draft_len: Optional[torch.Tensor], want_probs: bool, want_packed: bool,
+                out: Optional[ChainResult], workspace_buf: Optional[torch.Tensor], stream):
+    """Checks the tensors and returns (argument tuple of spec_verify_chain, result, buffers
+    the call uses)."""
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [B, K+1, V]")
     B, K1, V = target_logits.shape
@@ -197,16 +194,64 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.
             offsets=torch.empty((B + 1,), dtype=torch.int32, device=dev) if want_packed else None,
         )
     s = _stream(stream, dev)
-    L = lib()
-    need = int(L.spec_verify_chain_workspace_size(B, K, V, code)) if B > 0 else 0
+    need = int(lib().spec_verify_chain_workspace_size(B, K, V, code)) if B > 0 else 0
     buf = workspace_buf if workspace_buf is not None else workspace(need, dev, s, "chain")
     wp, wbytes = _aligned_ptr(buf)
-    st = L.spec_verify_chain(_ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(draft_len),
-                             _ptr(temperature), _ptr(u_accept), _ptr(u_final), B, K, V,
-                             _ptr(out.tokens), _ptr(out.num_accepted), _ptr(out.probs),
-                             _ptr(out.packed), _ptr(out.offsets), wp, wbytes, s)
-    _check("spec_verify_chain", st)
+    args = (_ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(draft_len),
+            _ptr(temperature), _ptr(u_accept), _ptr(u_final), B, K, V,
+            _ptr(out.tokens), _ptr(out.num_accepted), _ptr(out.probs),
+            _ptr(out.packed), _ptr(out.offsets), wp, wbytes, s)
+    keep = (target_logits, draft_logits, draft_tokens, temperature, u_accept, u_final, draft_len, buf)
+    return args, out, keep
+
+
+def spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                      draft_tokens: torch.Tensor, temperature: torch.Tensor, u_accept: torch.Tensor,
+                      u_final: torch.Tensor, draft_len: Optional[torch.Tensor] = None, *,
+                      want_probs: bool = True, want_packed: bool = False,
+                      out: Optional[ChainResult] = None, workspace_buf: Optional[torch.Tensor] = None,
+                      stream=None) -> ChainResult:
+    """Batched chain verification (spec_verify_chain).  Shapes: target [B, K+1, V],
+    draft [B, K, V] or None (one-hot draft), draft_tokens [B, K] int32, temperature [B]
+    float32, u_accept [B, K] float32, u_final [B] float32, draft_len [B] int32 or None."""
+    args, out, _ = _chain_call(target_logits, draft_logits, draft_tokens, temperature, u_accept, u_final,
+                               draft_len, want_probs, want_packed, out, workspace_buf, stream)
+    _check("spec_verify_chain", lib().spec_verify_chain(*args))
     return out
+
+
+class PreparedCall:
+    """An entry point with its arguments checked and marshalled once.  Calling the object
+    issues the same call again (same buffers, same stream) for the cost of one foreign
+    call, for loops that refill fixed buffers between calls.  It keeps references to
+    every buffer it names; their shapes and addresses must not change."""
+
+    def __init__(self, name: str, fn, argtypes, args, result, keep):
+        self._name = name
+        self._fn = fn
+        self._args = tuple(t(v) if v is not None else t() for t, v in zip(argtypes, args))
+        self.result = result
+        self._keep = keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            _check(self._name, st)
+        return self.result
+
+
+def prepare_spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                              draft_tokens: torch.Tensor, temperature: torch.Tensor, u_accept: torch.Tensor,
+                              u_final: torch.Tensor, draft_len: Optional[torch.Tensor] = None, *,
+                              want_probs: bool = True, want_packed: bool = False,
+                              out: Optional[ChainResult] = None, workspace_buf: Optional[torch.Tensor] = None,
+                              stream=None) -> PreparedCall:
+    """spec_verify_chain with every argument fixed: returns a PreparedCall whose result is
+    the ChainResult that each call overwrites."""
+    args, out, keep = _chain_call(target_logits, draft_logits, draft_tokens, temperature, u_accept, u_final,
+                                  draft_len, want_probs, want_packed, out, workspace_buf, stream)
+    return PreparedCall("spec_verify_chain", lib().spec_verify_chain, _SIGNATURES["spec_verify_chain"][1],
+                        args, out, keep)
 
 
 @dataclass

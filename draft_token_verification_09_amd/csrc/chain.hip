@@ -8,36 +8,31 @@
 // target row after the last accepted draft; draws are inverse-CDF in vocabulary
 // order (smallest index whose inclusive prefix reaches u * total).
 //
-// Three kernels (four with packed output), ordered by the stream:
+// Two kernels (three with packed output), ordered by the stream:
 //
-//  chain_stats   grid = B x R x C workgroups: R = K+1 target rows (+ K draft rows), C
-//                chunks per row.  Each workgroup reduces one chunk (non-temporal 16-byte
-//                loads) to (o, s) = (max(l) * log2(e)/T, sum exp2(l * log2(e)/T - o))
-//                and, if the chunk holds the row's drafted token x_k, copies l(x_k) out
-//                of its registers.  This is the pass that reads every logit.
-//  chain_decide  grid = B x C (draft logits) or B x 1 (one-hot draft).  Every workgroup
-//                of a sequence combines its chunk partials into per-row (O, S) and
-//                evaluates p(x_k), q(x_k), alpha_k and the accept tests of all drafted
-//                positions at once (one lane per position), taking the first rejection
-//                n with a wave ballot -- the same decision in each, from the same data
-//                by the same arithmetic; workgroup 0 stores it with the accepted prefix,
-//                the probabilities and the count.  After a rejection with a draft
-//                distribution, workgroup c computes the residual masses
-//                max(0, p_n - q_n) of the segments of chunk c of row n.
-//  chain_draw    grid = B.  Narrows u * W down to a segment, a lane and an element (see
-//                chain_draw) and writes the drawn token.  For a bonus draw from p, or a
-//                one-hot draft whose residual is p without x_n, the chunk masses follow
-//                from chain_stats' partials.
-//  chain_pack    grid = 1, only for packed output: offsets and packed tokens.
-//
-// No workgroup waits for another and no state outlives a call: each kernel reads only
-// what an earlier kernel of the same call wrote.
+//  chain_stats  grid = B x R x C: R = K+1 target rows (+ K draft rows when draft logits
+//               are given), C chunks per row.  Each workgroup reduces one chunk
+//               (non-temporal 16-byte loads) to (o, s) = (max(l) * log2(e)/T,
+//               sum exp2(l * log2(e)/T - o)) and, if the chunk holds the row's drafted
+//               token x_k, copies l(x_k) out of its registers.  This is the pass that
+//               reads every logit, once.
+//  chain_pool   grid = B x C tasks (see chain_pool_kernel): every task of a sequence
+//               combines the partials into per-row (O, S) and evaluates p(x_k), q(x_k),
+//               alpha_k and the accept tests of all drafted positions at once (one lane
+//               per position), taking the first rejection n with a wave ballot; task c
+//               then sums the final draw's weights over the segments of chunk c, and the
+//               sequence's last task draws the token from those masses.
+//  chain_pack   grid = 1, only for packed output: offsets and packed tokens.
 //
 // Softmax is evaluated in the exp2 domain: with scale = log2(e)/T,
 // p_i = exp2(l_i * scale - O) / S, where O is the float max(l) * scale used by every
 // term and S = sum_chunks s_c * exp2(o_c - O).  Per-element work is fp32; cross-lane,
 // cross-chunk and prefix sums are fp64.
 #include <math.h>
+
+#include <atomic>
+#include <chrono>
+#include <random>
 
 #include "device_common.h"
 #include "host_runtime.h"
@@ -53,6 +48,39 @@ struct RowStat {
   double s;  // sum over the chunk of exp2(l * scale - o)
 };
 
+// Segment masses pass between the tasks of one pool launch through slots of two 64-bit
+// words, each carrying 32 bits of the double in its low half and the call's generation
+// number in its high half, written by one atomic store.  A reader knows that a slot was
+// written during this call when both high halves equal the generation, so no clearing
+// pass is needed: whatever a slot held before (an earlier call's words, or anything else)
+// reads as "not written yet" unless 64 bits match by chance.  Generations come from a
+// process-wide counter with a random start and are never 0.
+struct SlotDouble {
+  uint64_t lo, hi;
+};
+
+__device__ __forceinline__ uint64_t tagged(uint32_t payload, uint32_t gen) {
+  return static_cast<uint64_t>(payload) | (static_cast<uint64_t>(gen) << 32);
+}
+
+__device__ __forceinline__ void put_slot(SlotDouble* p, double v, uint32_t gen) {
+  const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(v));
+  store_agent(&p->lo, tagged(static_cast<uint32_t>(bits), gen));
+  store_agent(&p->hi, tagged(static_cast<uint32_t>(bits >> 32), gen));
+}
+
+// Reads a slot; false if it has not been written during this call.
+__device__ __forceinline__ bool get_slot(const SlotDouble* p, uint32_t gen, double* v) {
+  const uint64_t lo = load_agent(&p->lo), hi = load_agent(&p->hi);
+  *v = __longlong_as_double(static_cast<long long>((hi << 32) | (lo & 0xffffffffull)));
+  return static_cast<uint32_t>(lo >> 32) == gen && static_cast<uint32_t>(hi >> 32) == gen;
+}
+
+// Polls of a slot that has not been written yet before a wait gives up (each poll takes
+// a memory round trip plus a pause of about a microsecond: a quarter of a second or more).
+constexpr int kPollLimit = 1 << 18;
+__device__ __forceinline__ void poll_pause() { __builtin_amdgcn_s_sleep(31); }
+
 struct ChainDecision {
   int mode;
   int n;         // accepted drafts
@@ -65,6 +93,26 @@ struct ChainDecision {
   float p_excl;  // one-hot mode: p_n(x_n)
   double St, Sd;
 };
+
+// A decision read from shared memory, held in scalar registers.
+__device__ __forceinline__ ChainDecision uniform_decision(const ChainDecision& s) {
+  ChainDecision d;
+  d.mode = uniform(s.mode);
+  d.n = uniform(s.n);
+  d.kb = uniform(s.kb);
+  d.excl_tok = uniform(s.excl_tok);
+  d.row = uniform(s.row);
+  d.scale = uniform(s.scale);
+  d.Ot = uniform(s.Ot);
+  d.Od = uniform(s.Od);
+  d.invSt = uniform(s.invSt);
+  d.invSd = uniform(s.invSd);
+  d.p_excl = uniform(s.p_excl);
+  d.St = uniform(s.St);
+  d.Sd = uniform(s.Sd);
+  return d;
+}
+
 
 struct ChainArgs {
   const void* target;
@@ -80,10 +128,11 @@ struct ChainArgs {
   float* out_probs;
   int32_t* out_packed;
   int32_t* out_offsets;
-  RowStat* part;        // [B, R, C]
+  uint32_t gen;         // generation of this call's slot words
+  RowStat* part;        // [B, R, C] chunk partials
   float* gath;          // [B, R] logit of the drafted token in each scoring row
-  ChainDecision* dec;   // [B]
-  double* wseg;         // [B, C, NV] residual mass per segment
+  SlotDouble* wseg;     // [B, C, NV] slots: mass of the final draw's weights per segment
+  SlotDouble* wsegp;    // [B, C, NV] slots: mass of p of the same row per segment (fallback)
 };
 
 template <int DT>
@@ -120,23 +169,27 @@ __device__ __forceinline__ int row_position(const ChainArgs& a, int rr, int kb) 
 // ---------------------------------------------------------------- decision
 
 constexpr int kStage = 1024;  // chunk partials staged in shared memory per batch of rows
+constexpr int kStageBytes = kStage * (sizeof(double) + sizeof(float));
 
-// Called by every lane of every chain_decide workgroup of sequence b.  The decision lands
-// in *out (shared memory) identically in all of them: same data, same arithmetic, same
-// order.  Only the workgroup with write_outputs stores the decision-level outputs.  The
-// loads of a batch of rows are all issued before any is used: one memory round trip.
+// Called by every lane of every pool task of sequence b: combines the sequence's chunk
+// partials, decides and leaves the decision in *out (shared memory) -- identically in
+// every task: same data, same arithmetic, same order.  With write_outputs it also writes
+// the count and the probabilities (and a -1 row for invalid input).  `stage` is shared
+// memory of at least kStageBytes (reused by the caller afterwards).  The loads of a batch
+// of rows are all issued before any is used.
 template <int DT>
-__device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, bool write_outputs, ChainDecision* out) {
+__device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, bool write_outputs,
+                                             ChainDecision* out, unsigned char* stage) {
   __shared__ float sO[2 * SPEC_MAX_K + 1];
   __shared__ double sS[2 * SPEC_MAX_K + 1];
-  __shared__ float st_o[kStage];
-  __shared__ double st_s[kStage];
+  double* st_s = reinterpret_cast<double*>(stage);
+  float* st_o = reinterpret_cast<float*>(stage + kStage * sizeof(double));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int R = a.R, C = a.C;
 
-  // Wave 0, lane k: the inputs of drafted position k (issued before the partials arrive).
+  // Wave 0, lane k: the inputs of drafted position k.
   const int k = lane;
   const bool active = w == 0 && k < kb;
   int x = 0;
@@ -219,11 +272,9 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
         pr[1] = keep ? Q : 0.f;
         pr[2] = keep ? alpha : 0.f;
       }
-      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-      if (invalid) {
+      if (invalid) {  // a valid sequence's row is written by its final draw
+        int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
         for (int kk = lane; kk <= a.K; kk += 64) ot[kk] = -1;
-      } else if (k < n) {
-        ot[k] = x;
       }
       if (lane == 0) a.out_num[b] = invalid ? -1 : n;
     }
@@ -261,6 +312,7 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   __syncthreads();
 }
 
+// grid = B x R x C: workgroup g reduces one chunk of one row.
 template <int DT, int NV, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   __shared__ float s_f[kWaves];
@@ -325,19 +377,18 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
 
 // ---------------------------------------------------------------- final draw
 
-// Weight of element e of the final draw's row(s).
-template <int DT>
-__device__ __forceinline__ float draw_weight(int mode, const ChainDecision& d, float lt, float ld, int e) {
+// Weight of one element in the final draw: max(0, p - q) after a rejection (residual),
+// else p; zero for the excluded token (one-hot residual; excl = -1 excludes nothing).
+// Logits past V read as -inf and weigh 0 in every mode.
+__device__ __forceinline__ float draw_weight(bool residual, const ChainDecision& d, float lt, float ld, int e,
+                                             int excl) {
   const float p = exp2_fast(fmaf(lt, d.scale, -d.Ot)) * d.invSt;
-  if (mode == kModeResidual) {
-    const float q = exp2_fast(fmaf(ld, d.scale, -d.Od)) * d.invSd;
-    return fmaxf(0.f, p - q);
-  }
-  if (mode == kModeOneHot && e == d.excl_tok) return 0.f;
-  return p;
+  float w = p;
+  if (residual) w = fmaxf(0.f, p - exp2_fast(fmaf(ld, d.scale, -d.Od)) * d.invSd);
+  return e == excl ? 0.f : w;
 }
 
-// The last sequence to finish packs the emitted tokens of the batch back to back.
+// Offsets and packed tokens of the whole batch (one workgroup, after the pass).
 __device__ __forceinline__ void chain_pack(const ChainArgs& a) {
   __shared__ int s_i[kWaves];
   const int tid = threadIdx.x;
@@ -362,69 +413,150 @@ __device__ __forceinline__ void chain_pack(const ChainArgs& a) {
   if (tid == 0) a.out_offsets[a.B] = total;
 }
 
-// One workgroup draws the final token of sequence b and writes it.
+// grid = Bs x C pool tasks for the sequences b0 .. b0+Bs-1: task t = (sequence b, chunk c).
+//  1. Decides for b (identically in each of the sequence's C tasks), then loads chunk c of
+//     the final draw's row(s) (two rows after a rejection) and sums, for each of its NV
+//     segments, the draw weights and p: per lane in fp32, across lanes in fp64.
+//  2. Hands the segment masses over.  Every task but the sequence's last (chunk C-1)
+//     ends here.
+//  3. The last task waits for the masses of chunks 0 .. C-2, scans the C*NV segment
+//     masses in vocabulary order, takes the first segment whose inclusive prefix reaches
+//     u * W (W = the total), narrows it to a lane and an element, and writes the emitted
+//     row (x_0 .. x_{n-1}, the drawn token, then -1).  If rounding leaves no residual mass
+//     (W = 0 after a rejection) it draws from the masses of p instead.
+// Only last tasks wait, and only for tasks of this launch; the host keeps Bs at most half
+// of the workgroups the device holds at once, so the tasks they wait for always find
+// room and every wait ends (each is also bounded; on timeout the sequence is flagged).
 //
 // Vocabulary order inside a chunk is segment-major (a segment = one 16-byte vector per
-// lane), then lane, then element.  The draw narrows u * W down in three levels:
-//  1. units: segments for a residual draw (masses from chain_decide's residual pass),
-//     chunks otherwise (masses from chain_stats' partials); block prefix scan;
-//  2. for a chunk: the lanes load that chunk of the one row, and per-segment totals
-//     pick the segment;
-//  3. the lanes load one vector each of the selected segment, a block scan of their
-//     sums picks the lane, and that lane scans its elements.
+// lane), then lane, then element.
 template <int DT, int NV, bool VEC>
-__device__ __forceinline__ void chain_draw(const ChainArgs& a, int b, const ChainDecision& d) {
+__global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0) {
+  constexpr int kRedBytes = 2 * NV * kThreads * static_cast<int>(sizeof(float));
+  __shared__ __align__(16) unsigned char s_buf[kRedBytes > kStageBytes ? kRedBytes : kStageBytes];
+  __shared__ ChainDecision s_dec;
+  __shared__ double s_d[kWaves];
+  __shared__ int s_i[kWaves];
+  __shared__ double s_base;
+  __shared__ int s_budget, s_y;
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSeg = ChunkShape<DT, NV>::kSegment;
   constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
-  __shared__ double s_d[kWaves];
-  __shared__ int s_i[kWaves];
-  __shared__ double s_seg[NV][kWaves];
-  __shared__ double s_base;
-  __shared__ int s_y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int C = a.C;
-  int mode = d.mode;
-  const float uf = a.u_final[b];
+  const int b = b0 + static_cast<int>(blockIdx.x) / C;
+  const int c = static_cast<int>(blockIdx.x) % C;
+  const bool last = c == C - 1;
+  float* red = reinterpret_cast<float*>(s_buf);  // [2][NV][kThreads] per-lane masses
 
-  // ---- level 1: unit masses, this lane's share (at most 4) in registers
-  int units = mode == kModeResidual ? C * NV : C;
-  int per = (units + kThreads - 1) / kThreads;
-  int u0 = tid * per;
-  double mass[4];
-  auto load_masses = [&]() {
+  chain_decide<DT>(a, b, clamped_len(a, b), last, &s_dec, s_buf);
+  const ChainDecision d = uniform_decision(s_dec);
+  if (d.mode == kModeInvalid) return;  // the decision already wrote the -1 row
+  int mode = d.mode;
+  const void* row_t = target_row<DT>(a, b, d.row);
+  const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : row_t;
+
+  // ---- 1. per-lane masses of this chunk's segments: the draw weights, and p.  The
+  // chunk is read in two halves to bound the registers held.
+  {
+    constexpr int H = NV > 1 ? NV / 2 : 1;
+    const bool residual = mode == kModeResidual;
+    const int excl = mode == kModeOneHot ? d.excl_tok : -1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int u = u0 + q;
-      double m = 0.0;
-      if (q < per && u < units) {
-        if (mode == kModeResidual) {
-          m = a.wseg[static_cast<size_t>(b) * C * NV + u];
-        } else {
-          const RowStat st = a.part[(static_cast<size_t>(b) * a.R + d.row) * C + u];
-          m = st.o == -INFINITY ? 0.0 : st.s * static_cast<double>(exp2_fast(st.o - d.Ot)) / d.St;
-          if (mode == kModeOneHot && u == d.excl_tok / kChunk) m = fmax(0.0, m - static_cast<double>(d.p_excl));
-        }
+    for (int h = 0; h < NV; h += H) {
+      u32x4 rt[H], rd[H];
+      const int sbase = c * kChunk + h * kSeg;  // first element of this half
+#pragma unroll
+      for (int j = 0; j < H; ++j) rt[j] = load_vector<DT, VEC>(row_t, a.V, sbase + (j * kThreads + tid) * E);
+      if (residual) {
+#pragma unroll
+        for (int j = 0; j < H; ++j) rd[j] = load_vector<DT, VEC>(row_d, a.V, sbase + (j * kThreads + tid) * E);
+      } else {
+#pragma unroll
+        for (int j = 0; j < H; ++j) rd[j] = rt[j];
       }
-      mass[q] = m;
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const int e0 = sbase + (j * kThreads + tid) * E;
+        float aw = 0.f, ap = 0.f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const float pv = exp2_fast(fmaf(EL::get(rt[j], i), d.scale, -d.Ot)) * d.invSt;
+          float wv = pv;
+          if (residual) wv = fmaxf(0.f, pv - exp2_fast(fmaf(EL::get(rd[j], i), d.scale, -d.Od)) * d.invSd);
+          aw += e0 + i == excl ? 0.f : wv;
+          ap += pv;
+        }
+        red[(h + j) * kThreads + tid] = aw;
+        red[(NV + h + j) * kThreads + tid] = ap;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  load_masses();
-  double local = mass[0] + mass[1] + mass[2] + mass[3];
-  double W = block_sum(local, s_d);
-  if (!(W > 0.0) && mode == kModeResidual) {
-    mode = kModeFallbackP;  // residual lost to rounding: draw from p_n itself
-    units = C;
-    per = (units + kThreads - 1) / kThreads;
-    u0 = tid * per;
-    load_masses();
-    local = mass[0] + mass[1] + mass[2] + mass[3];
-    W = block_sum(local, s_d);
   }
-  const double t = static_cast<double>(uf) * W;
+  __syncthreads();
+  // ---- 2. segment totals in fp64 (one 16-lane row sums one segment's 256 lane values)
+  const int units = C * NV;
+  SlotDouble* mw = a.wseg + static_cast<size_t>(b) * units;
+  SlotDouble* mp = a.wsegp + static_cast<size_t>(b) * units;
+  {
+    const int q = tid >> 4;  // q < NV: draw-weight mass of segment q; NV <= q < 2NV: p mass
+    const int r = tid & 15;
+    double v = 0.0;
+    if (q < 2 * NV) {
+      const float* src = red + q * kThreads + r * 16;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v += static_cast<double>(src[i]);
+    }
+    v = row16_inclusive_sum(v);
+    if (q < 2 * NV && r == 15) put_slot((q < NV ? mw : mp) + c * NV + (q % NV), v, a.gen);
+  }
+  if (!last) return;
+
+  // ---- 3. the last task: every chunk's masses (this lane's share of the units)
+  const int per = (units + kThreads - 1) / kThreads;  // <= 4
+  const int u0 = tid * per;
+  double mass[4];
+  double W = 0.0;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const SlotDouble* slots = attempt == 0 ? mw : mp;
+    if (tid == 0) s_budget = kPollLimit;
+    bool arrived = true;
+    for (;;) {
+      int missing = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = u0 + q;
+        mass[q] = 0.0;
+        if (q < per && u < units && !get_slot(slots + u, a.gen, &mass[q])) missing = 1;
+      }
+      if (!__syncthreads_or(missing)) break;
+      if (tid == 0) {
+        poll_pause();
+        --s_budget;
+      }
+      __syncthreads();
+      if (s_budget <= 0) {
+        arrived = false;
+        break;
+      }
+    }
+    if (!arrived) {  // flag the sequence rather than wait on
+      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+      for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
+      if (tid == 0) a.out_num[b] = -1;
+      return;
+    }
+    W = block_sum(mass[0] + mass[1] + mass[2] + mass[3], s_d);
+    if (W > 0.0 || !(mode == kModeResidual || mode == kModeOneHot)) break;
+    mode = kModeFallbackP;  // no residual mass left after rounding: draw from p_n itself
+  }
+
+  // ---- the segment holding u * W
+  const double local = mass[0] + mass[1] + mass[2] + mass[3];
+  const double tt = static_cast<double>(a.u_final[b]) * W;
   const double incl = wave_inclusive_scan(local);
   __syncthreads();
   if (lane == 63) s_d[w] = incl;
@@ -439,12 +571,12 @@ __device__ __forceinline__ void chain_draw(const ChainArgs& a, int b, const Chai
       run += mass[q];
       if (mass[q] > 0.0) {
         lastu = u0 + q;
-        if (cand == INT_MAX && run >= t) cand = u0 + q;
+        if (cand == INT_MAX && run >= tt) cand = u0 + q;
       }
     }
   }
   int usel = block_min_int(cand, s_i);
-  if (usel == INT_MAX) {  // rounding left t above every prefix: last unit with mass
+  if (usel == INT_MAX) {  // rounding left u * W above every prefix: last segment with mass
     usel = block_max_int(lastu, s_i);
     if (usel < 0) usel = 0;
   }
@@ -456,79 +588,25 @@ __device__ __forceinline__ void chain_draw(const ChainArgs& a, int b, const Chai
     s_base = run;
   }
   __syncthreads();
-  double t_loc = t - s_base;
+  const double t_loc = tt - s_base;
+  const int seg_start = (usel / NV) * kChunk + (usel % NV) * kSeg;
 
-  const void* row_t = target_row<DT>(a, b, d.row);
-  const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : nullptr;
-  int seg_start;
-  if (mode == kModeResidual) {
-    seg_start = (usel / NV) * kChunk + (usel % NV) * kSeg;
-  } else {
-    // ---- level 2: segment totals of chunk usel of the one row
-    const int c = usel;
-    float sl[NV];
-    {
-      u32x4 raw[NV];
-      load_chunk<DT, NV, VEC>(raw, row_t, a.V, c);
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        float sj = 0.f;
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-          const int e = c * kChunk + (j * kThreads + tid) * E + i;
-          sj += e < a.V ? draw_weight<DT>(mode, d, EL::get(raw[j], i), 0.f, e) : 0.f;
-        }
-        sl[j] = sj;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const double ws = wave_sum(static_cast<double>(sl[j]));
-      if (lane == 0) s_seg[j][w] = ws;
-    }
-    __syncthreads();
-    int js = -1, jlast = 0;
-    double run = 0.0, run_last = 0.0;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      double tot = 0.0;
-#pragma unroll
-      for (int i = 0; i < kWaves; ++i) tot += s_seg[j][i];
-      if (js < 0) {
-        if (tot > 0.0) {
-          jlast = j;
-          run_last = run;
-        }
-        if (tot > 0.0 && run + tot >= t_loc) {
-          js = j;
-        } else {
-          run += tot;
-        }
-      }
-    }
-    if (js < 0) {  // rounding: take the last segment with mass
-      js = jlast;
-      run = run_last;
-    }
-    t_loc -= run;
-    seg_start = c * kChunk + js * kSeg;
-  }
-
-  // ---- level 3: one vector per lane of the selected segment
+  // ---- the lane and the element inside that segment
   const int e0 = seg_start + tid * E;
   const u32x4 vt = load_vector<DT, VEC>(row_t, a.V, e0);
-  u32x4 vd = vt;
-  if (mode == kModeResidual) vd = load_vector<DT, VEC>(row_d, a.V, e0);
+  const u32x4 vd = mode == kModeResidual ? load_vector<DT, VEC>(row_d, a.V, e0) : vt;
   float wl[E];
   float lsum = 0.f;
   int last_pos = -1;
+  {
+    const bool residual = mode == kModeResidual;
+    const int excl = mode == kModeOneHot ? d.excl_tok : -1;
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const int e = e0 + i;
-    const float ld = mode == kModeResidual ? EL::get(vd, i) : 0.f;
-    wl[i] = e < a.V ? draw_weight<DT>(mode, d, EL::get(vt, i), ld, e) : 0.f;
-    lsum += wl[i];
-    if (wl[i] > 0.f) last_pos = e;
+    for (int i = 0; i < E; ++i) {
+      wl[i] = draw_weight(residual, d, EL::get(vt, i), EL::get(vd, i), e0 + i, excl);
+      lsum += wl[i];
+      last_pos = wl[i] > 0.f ? e0 + i : last_pos;
+    }
   }
   const double lincl = wave_inclusive_scan(static_cast<double>(lsum));
   __syncthreads();
@@ -557,63 +635,9 @@ __device__ __forceinline__ void chain_draw(const ChainArgs& a, int b, const Chai
     y = s_y;
   }
   const int n = d.n;
+  const int32_t* xs = a.tokens + static_cast<size_t>(b) * a.K;
   int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-  for (int kk = n + tid; kk <= a.K; kk += kThreads) ot[kk] = (kk == n) ? y : -1;
-}
-
-// grid = B x C2: the decision of sequence b in every workgroup, stored by workgroup 0;
-// after a rejection with draft logits, workgroup c computes the residual masses
-// max(0, p_n - q_n) of the segments of chunk c of row n.
-template <int DT, int NV, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainArgs a, int C2) {
-  __shared__ double s_seg[NV][kWaves];
-  __shared__ ChainDecision s_dec;
-  using EL = Elem<DT>;
-  constexpr int E = EL::kPerVec;
-  const int g = blockIdx.x;
-  const int c = g % C2;
-  const int b = g / C2;
-  chain_decide<DT>(a, b, clamped_len(a, b), c == 0, &s_dec);
-  const ChainDecision d = s_dec;
-  if (c == 0 && threadIdx.x == 0) a.dec[b] = d;
-  if (d.mode != kModeResidual) return;
-  u32x4 rt[NV], rd[NV];
-  load_chunk<DT, NV, VEC>(rt, target_row<DT>(a, b, d.row), a.V, c);
-  load_chunk<DT, NV, VEC>(rd, draft_row<DT>(a, b, d.row), a.V, c);
-  float acc[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    acc[j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const float p = exp2_fast(fmaf(EL::get(rt[j], i), d.scale, -d.Ot)) * d.invSt;
-      const float q = exp2_fast(fmaf(EL::get(rd[j], i), d.scale, -d.Od)) * d.invSd;
-      acc[j] += fmaxf(0.f, p - q);
-    }
-  }
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const double ws = wave_sum(static_cast<double>(acc[j]));
-    if (lane == 0) s_seg[j][w] = ws;
-  }
-  __syncthreads();
-  if (threadIdx.x < NV) {
-    double tot = 0.0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) tot += s_seg[threadIdx.x][i];
-    a.wseg[(static_cast<size_t>(b) * a.C + c) * NV + threadIdx.x] = tot;
-  }
-}
-
-// grid = B: the final draw of every valid sequence.
-template <int DT, int NV, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_draw_kernel(ChainArgs a) {
-  const int b = blockIdx.x;
-  const ChainDecision d = a.dec[b];
-  if (d.mode == kModeInvalid) return;
-  chain_draw<DT, NV, VEC>(a, b, d);
+  for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = kk < n ? xs[kk] : (kk == n ? y : -1);
 }
 
 // grid = 1: offsets and packed tokens of the batch (only when packed output is asked for).
@@ -627,7 +651,7 @@ __global__ void write_zero_offset_kernel(int32_t* offsets) {
 
 struct ChainLayout {
   int nv, C, R;
-  size_t off_gath, off_part, off_dec, off_wseg, bytes;
+  size_t off_gath, off_part, off_wseg, off_wsegp, bytes;
 };
 
 static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
@@ -637,42 +661,72 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
   L.nv = choose_nv(static_cast<long long>(B) * L.R, V, epv, 1024);
   const long long chunk = static_cast<long long>(L.nv) * kThreads * epv;
   L.C = static_cast<int>((V + chunk - 1) / chunk);
+  const size_t segs = static_cast<size_t>(B) * L.C * L.nv;
   size_t off = 0;
   L.off_gath = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(B) * L.R, 256);
   L.off_part = off;
   off = align_up(off + sizeof(RowStat) * static_cast<size_t>(B) * L.R * L.C, 256);
-  L.off_dec = off;
-  off = align_up(off + sizeof(ChainDecision) * static_cast<size_t>(B), 256);
   L.off_wseg = off;
-  off = align_up(off + sizeof(double) * static_cast<size_t>(B) * L.C * L.nv, 256);
+  off = align_up(off + sizeof(SlotDouble) * segs, 256);
+  L.off_wsegp = off;
+  off = align_up(off + sizeof(SlotDouble) * segs, 256);
   L.bytes = off;
   return L;
 }
 
+// Sequences per pool launch: at most half of the pool workgroups the current device
+// holds at once (cached per device), so that the tasks a last task waits for always
+// find room.
+static int pool_sequences(const void* kernel, std::atomic<int>* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int slots = dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (slots <= 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
+    slots = max(1, per_cu) * max(1, cus);
+    if (dev < kMaxDevices) cache[dev].store(slots, std::memory_order_relaxed);
+  }
+  return max(1, slots / 2);
+}
+
+// Generation of the next call's slot words: a process-wide counter with a random start,
+// skipping 0.
+static uint32_t next_generation() {
+  static std::atomic<uint32_t> counter{[] {
+    std::random_device rd;
+    return static_cast<uint32_t>(rd()) ^
+           static_cast<uint32_t>(std::chrono::steady_clock::now().time_since_epoch().count());
+  }()};
+  uint32_t g = counter.fetch_add(1u, std::memory_order_relaxed);
+  if (g == 0u) g = counter.fetch_add(1u, std::memory_order_relaxed);
+  return g;
+}
+
 template <int DT, int NV, bool VEC>
 static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
+  static std::atomic<int> slots_cache[kMaxDevices];
   {
     const long long g1 = static_cast<long long>(a.B) * a.R * a.C;
     LaunchScope scope("chain_stats", stream);
-    hipExtLaunchKernelGGL((chain_stats_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0, stream, scope.start(), scope.stop(), 0, a);
+    hipExtLaunchKernelGGL((chain_stats_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0,
+                          stream, scope.start(), scope.stop(), 0, a);
     const spec_status_t st = scope.finish();
     if (st != SPEC_OK) return st;
   }
   {
-    const int C2 = a.draft ? a.C : 1;  // a one-hot draft never takes the residual path
-    const long long g2 = static_cast<long long>(a.B) * C2;
-    LaunchScope scope("chain_decide", stream);
-    hipExtLaunchKernelGGL((chain_decide_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, stream, scope.start(), scope.stop(), 0,
-                       a, C2);
-    const spec_status_t st = scope.finish();
-    if (st != SPEC_OK) return st;
-  }
-  {
-    LaunchScope scope("chain_draw", stream);
-    hipExtLaunchKernelGGL((chain_draw_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, stream, scope.start(), scope.stop(), 0, a);
-    const spec_status_t st = scope.finish();
-    if (st != SPEC_OK) return st;
+    const auto kernel = chain_pool_kernel<DT, NV, VEC>;
+    const int per_launch = pool_sequences(reinterpret_cast<const void*>(kernel), slots_cache);
+    for (int b0 = 0; b0 < a.B; b0 += per_launch) {
+      const int bs = min(per_launch, a.B - b0);
+      LaunchScope scope("chain_pool", stream);
+      hipExtLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(static_cast<long long>(bs) * a.C)), dim3(kThreads), 0,
+                            stream, scope.start(), scope.stop(), 0, a, b0);
+      const spec_status_t st = scope.finish();
+      if (st != SPEC_OK) return st;
+    }
   }
   if (!a.out_packed) return SPEC_OK;
   LaunchScope scope("chain_pack", stream);
@@ -756,10 +810,11 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   a.out_packed = out_packed;
   a.out_offsets = out_offsets;
   char* ws = static_cast<char*>(workspace);
+  a.gen = next_generation();
   a.gath = reinterpret_cast<float*>(ws + L.off_gath);
   a.part = reinterpret_cast<RowStat*>(ws + L.off_part);
-  a.dec = reinterpret_cast<ChainDecision*>(ws + L.off_dec);
-  a.wseg = reinterpret_cast<double*>(ws + L.off_wseg);
+  a.wseg = reinterpret_cast<SlotDouble*>(ws + L.off_wseg);
+  a.wsegp = reinterpret_cast<SlotDouble*>(ws + L.off_wsegp);
 
   const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits) &&
                    (draft_logits == nullptr || aligned16(draft_logits));

@@ -4,10 +4,11 @@
 //   NV segments; in segment j lane t holds one 16-byte vector (4 fp32 or 8 bf16
 //   logits) at element (j*256 + t)*E, so each wave instruction reads 1 KiB of
 //   contiguous memory and, inside a segment, vocabulary order is lane order.
-// * Reductions use cross-lane shuffles within a wave and a small LDS array across
-//   the 4 waves of a workgroup.
-// * Partial results pass between kernels through the workspace; the stream orders the
-//   kernels, so no workgroup waits for another.
+// * Reductions use cross-lane DPP within a wave and a small LDS array across the 4
+//   waves of a workgroup.
+// * Partial results pass between kernels through the workspace (the stream orders the
+//   kernels); inside a kernel, workgroups hand values over through agent-scope atomic
+//   stores and loads (see "cross-workgroup hand-off" below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -81,35 +82,39 @@ __device__ __forceinline__ u32x4 load16(const u32x4* p) {
 }
 
 // Load chunk `c` of a row of V logits into registers.  Elements past V read as -inf.
-// VEC: the row starts 16-byte aligned, so whole vectors can be loaded.
+// VEC: the row starts 16-byte aligned and holds a whole number of 16-byte vectors, so
+// every vector lies either wholly inside the row or wholly past its end.
 template <int DT, int NV, bool VEC, bool NT = false>
 __device__ __forceinline__ void load_chunk(u32x4 (&raw)[NV], const void* row, int V, int c) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
+  constexpr uint32_t kNegInf2 = EL::kNegInfBits | (E == 8 ? (EL::kNegInfBits << 16) : 0u);
   const int base = c * ChunkShape<DT, NV>::kChunk;
   const int lane = threadIdx.x;
-  if (VEC && base + ChunkShape<DT, NV>::kChunk <= V) {
+  if (VEC) {
     const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
                                                     static_cast<size_t>(base) * EL::kBytes);
+    if (base + ChunkShape<DT, NV>::kChunk <= V) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) raw[j] = load16<NT>(p + j * kThreads + lane);
+      for (int j = 0; j < NV; ++j) raw[j] = load16<NT>(p + j * kThreads + lane);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        raw[j] = base + (j * kThreads + lane) * E < V ? load16<NT>(p + j * kThreads + lane)
+                                                       : u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
+    }
     return;
   }
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int e0 = base + (j * kThreads + lane) * E;
-    if (VEC && e0 + E <= V) {
-      raw[j] = load16<NT>(reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
-                                                       static_cast<size_t>(e0) * EL::kBytes));
-    } else {
-      u32x4 v = {0u, 0u, 0u, 0u};
+    u32x4 v = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const int e = e0 + i;
-        EL::put(v, i, e < V ? EL::bits(row, e) : EL::kNegInfBits);
-      }
-      raw[j] = v;
+    for (int i = 0; i < E; ++i) {
+      const int e = e0 + i;
+      EL::put(v, i, e < V ? EL::bits(row, e) : EL::kNegInfBits);
     }
+    raw[j] = v;
   }
 }
 
@@ -119,8 +124,12 @@ template <int DT, bool VEC>
 __device__ __forceinline__ u32x4 load_vector(const void* row, int V, int e0) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
-  if (VEC && e0 + E <= V)
-    return *reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + static_cast<size_t>(e0) * EL::kBytes);
+  if (VEC) {
+    constexpr uint32_t kNegInf2 = EL::kNegInfBits | (E == 8 ? (EL::kNegInfBits << 16) : 0u);
+    if (e0 < V)
+      return *reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + static_cast<size_t>(e0) * EL::kBytes);
+    return u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
+  }
   u32x4 v = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < E; ++i) EL::put(v, i, e0 + i < V ? EL::bits(row, e0 + i) : EL::kNegInfBits);
@@ -162,6 +171,17 @@ __device__ __forceinline__ double dpp_double(double old, double v) {
   return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
 }
 
+// A value known to be the same in every lane, moved to a scalar register so that the
+// compiler treats it as uniform (scalar branches, no per-lane copies).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniform(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
+__device__ __forceinline__ double uniform(double v) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(x));
+  const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(x >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
 __device__ __forceinline__ float lane_broadcast(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
@@ -196,6 +216,15 @@ __device__ __forceinline__ double wave_inclusive_scan(double v) {
 }
 __device__ __forceinline__ int wave_inclusive_scan_int(int v) {
   SPECV_WAVE_SCAN(int, dpp_int, add_i, 0, v);
+  return v;
+}
+
+// Inclusive scan within each 16-lane row of the wave (lane 15 of a row holds its total).
+__device__ __forceinline__ double row16_inclusive_sum(double v) {
+  v += dpp_double<dppc::kRowShr1>(0.0, v);
+  v += dpp_double<dppc::kRowShr2>(0.0, v);
+  v += dpp_double<dppc::kRowShr4>(0.0, v);
+  v += dpp_double<dppc::kRowShr8>(0.0, v);
   return v;
 }
 
@@ -288,5 +317,24 @@ __device__ __forceinline__ int block_max_int(int v, int* lds) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- cross-workgroup hand-off
+//
+// The 8 XCDs of the chip each have their own L2, which is not coherent with the others
+// for plain loads and stores.  A value one workgroup hands to another inside a kernel is
+// therefore written with an agent-scope atomic store and read with an agent-scope atomic
+// load (both coherent across XCDs).  Nothing handed over goes through a plain store, so
+// no L2 write-back fence is needed (such a fence costs tens of microseconds per kernel on
+// this part).  Between kernels of one stream, plain stores and loads suffice.
+
+template <class T>
+__device__ __forceinline__ void store_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class T>
+__device__ __forceinline__ T load_agent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 }  // namespace specv

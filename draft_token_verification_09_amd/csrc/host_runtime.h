@@ -34,6 +34,8 @@ class LaunchScope {
   bool finished_;
 };
 
+constexpr int kMaxDevices = 64;  // per-device caches in the host code
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -4,9 +4,10 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 import synth
-from gpu_helpers import chain_on_gpu, chain_oracle, check_packed, compare_chain, log
+from gpu_helpers import chain_on_gpu, chain_oracle, check_packed, compare_chain, f32, i32, log, logits_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -74,3 +75,46 @@ def test_repeat_calls_are_bit_identical():
     total = int(a.offsets.cpu()[-1])
     assert int(b.offsets.cpu()[-1]) == total
     assert np.array_equal(a.packed.cpu().numpy()[:total], b.packed.cpu().numpy()[:total])
+
+
+def _device_args(inp):
+    return (logits_to_device(inp.target, inp.dtype), None if inp.draft is None else logits_to_device(inp.draft, inp.dtype),
+            i32(inp.tokens), f32(inp.temperature), f32(inp.u_accept), f32(inp.u_final),
+            None if inp.draft_len is None else i32(inp.draft_len))
+
+
+def test_prepared_call_matches_plain_call():
+    import draft_token_verification_09_amd as sv
+
+    inp = synth.chain_config_high_accept_bf16(3, B=8, V=30000)
+    args = _device_args(inp)
+    plain = sv.spec_verify_chain(*args, want_packed=True)
+    prep = sv.prepare_spec_verify_chain(*args, want_packed=True)
+    for _ in range(3):
+        res = prep()
+    torch.cuda.synchronize()
+    for name in ("tokens", "num_accepted", "probs", "offsets"):
+        assert torch.equal(getattr(plain, name), getattr(res, name)), name
+    rep = compare_chain(res, chain_oracle(inp), inp)
+    assert rep.ok(), rep.failures[:5]
+
+
+def test_dirty_workspace_reused_across_shapes():
+    # the workspace needs no initialisation and may hold anything, including the state a
+    # call of another shape left behind: fill it with junk, then alternate shapes on it
+    import draft_token_verification_09_amd as sv
+
+    shapes = [synth.chain_config_high_accept_bf16(4, B=12, K=5, V=40000),
+              synth.chain_config_low_accept_bf16(4, B=5, K=8, V=40000),
+              synth.chain_config_high_accept_bf16(5, B=3, K=2, V=40000)]
+    need = max(sv.spec_verify_chain_workspace_size(i.B, i.K, i.V, 1) for i in shapes)
+    ws = torch.full((need + 256,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    for rnd in range(2):
+        for inp in shapes:
+            log(f"[chain] dirty workspace round {rnd}: B={inp.B} K={inp.K} V={inp.V}")
+            res = sv.spec_verify_chain(*_device_args(inp), workspace_buf=ws, want_packed=True)
+            torch.cuda.synchronize()
+            rep = compare_chain(res, chain_oracle(inp), inp)
+            assert rep.ok(), rep.failures[:5]
+            check_packed(res, inp.B)
+        ws.fill_(0xFF if rnd == 0 else 0x00)
