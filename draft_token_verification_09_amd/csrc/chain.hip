@@ -77,9 +77,9 @@ __device__ __forceinline__ bool get_slot(const SlotDouble* p, uint32_t gen, doub
 }
 
 // Polls of a slot that has not been written yet before a wait gives up (each poll takes
-// a memory round trip plus a pause of about a microsecond: a quarter of a second or more).
+// at least a memory round trip, about a microsecond: a quarter of a second or more).
 constexpr int kPollLimit = 1 << 18;
-__device__ __forceinline__ void poll_pause() { __builtin_amdgcn_s_sleep(31); }
+__device__ __forceinline__ void short_pause() { __builtin_amdgcn_s_sleep(2); }
 
 struct ChainDecision {
   int mode;
@@ -129,7 +129,7 @@ struct ChainArgs {
   int32_t* out_packed;
   int32_t* out_offsets;
   uint32_t gen;         // generation of this call's slot words
-  RowStat* part;        // [B, R, C] chunk partials
+  RowStat* part;        // [B, R, C, 4] partials, one per wave of each chunk
   float* gath;          // [B, R] logit of the drafted token in each scoring row
   SlotDouble* wseg;     // [B, C, NV] slots: mass of the final draw's weights per segment
   SlotDouble* wsegp;    // [B, C, NV] slots: mass of p of the same row per segment (fallback)
@@ -187,7 +187,7 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int R = a.R, C = a.C;
+  const int R = a.R, C = a.C * kWaves;  // C = partials per row (one per wave of a chunk)
 
   // Wave 0, lane k: the inputs of drafted position k.
   const int k = lane;
@@ -205,7 +205,11 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   const float uf = a.u_final[b];
   const int kb_raw = a.draft_len ? a.draft_len[b] : a.K;
 
-  // Per-row (O, S) from the chunk partials.
+  // Per-row (O, S) from the partials: each 16-lane row of the workgroup combines one row
+  // of logits (16 at a time), lane r taking partials r, r+16, ...
+  __shared__ float s_om[kThreads / 16];
+  const int grp = tid >> 4;  // 16-lane group
+  const int r = tid & 15;
   const int rows_per_batch = max(1, kStage / C);
   for (int r0 = 0; r0 < R; r0 += rows_per_batch) {
     const int r1 = min(R, r0 + rows_per_batch);
@@ -217,24 +221,30 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
       st_s[i] = st.s;
     }
     __syncthreads();
-    for (int rr = r0 + w; rr < r1; rr += kWaves) {
-      if (!row_needed(a, rr, kb)) continue;
+    for (int g0 = r0; g0 < r1; g0 += kThreads / 16) {
+      const int rr = g0 + grp;
+      const bool live = rr < r1 && row_needed(a, rr, kb);
       const int base = (rr - r0) * C;
       float om = -INFINITY;
-      for (int c = lane; c < C; c += 64) om = fmaxf(om, st_o[base + c]);
-      om = wave_max(om);
+      if (live)
+        for (int c = r; c < C; c += 16) om = fmaxf(om, st_o[base + c]);
+      om = row16_inclusive_max(om);
+      if (r == 15) s_om[grp] = om;
+      __syncthreads();
+      om = s_om[grp];
       double sum = 0.0;
-      for (int c = lane; c < C; c += 64) {
-        const float o = st_o[base + c];
-        if (o != -INFINITY) sum += st_s[base + c] * static_cast<double>(exp2_fast(o - om));
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) {
+      if (live)
+        for (int c = r; c < C; c += 16) {
+          const float o = st_o[base + c];
+          if (o != -INFINITY) sum += st_s[base + c] * static_cast<double>(exp2_fast(o - om));
+        }
+      sum = row16_inclusive_sum(sum);
+      if (live && r == 15) {
         sO[rr] = om;
         sS[rr] = sum;
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   if (w == 0) {
@@ -312,11 +322,10 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   __syncthreads();
 }
 
-// grid = B x R x C: workgroup g reduces one chunk of one row.
+// grid = B x R x C: workgroup g reduces one chunk of one row, each of its waves to one
+// partial (the wave's lanes hold every 4th group of 64 vectors of the chunk).
 template <int DT, int NV, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
-  __shared__ float s_f[kWaves];
-  __shared__ double s_d[kWaves];
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSeg = ChunkShape<DT, NV>::kSegment;
@@ -369,10 +378,12 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
       for (int j = 0; j < h; ++j) acc[j] += acc[j + h];
     s = acc[0];
   }
-  const float ob = block_max(o, s_f);
-  const double contrib = (o == -INFINITY) ? 0.0 : static_cast<double>(s) * static_cast<double>(exp2_fast(o - ob));
-  const double sb = block_sum(contrib, s_d);
-  if (threadIdx.x == 0) a.part[(static_cast<size_t>(b) * a.R + rr) * a.C + c] = RowStat{ob, 0.f, sb};
+  // One partial per wave: no workgroup barrier in this kernel.
+  const float ow = wave_max(o);
+  const double contrib = (o == -INFINITY) ? 0.0 : static_cast<double>(s) * static_cast<double>(exp2_fast(o - ow));
+  const double sw = wave_sum(contrib);
+  if ((threadIdx.x & 63) == 0)
+    a.part[((static_cast<size_t>(b) * a.R + rr) * a.C + c) * kWaves + (threadIdx.x >> 6)] = RowStat{ow, 0.f, sw};
 }
 
 // ---------------------------------------------------------------- final draw
@@ -414,19 +425,20 @@ __device__ __forceinline__ void chain_pack(const ChainArgs& a) {
 }
 
 // grid = Bs x C pool tasks for the sequences b0 .. b0+Bs-1: task t = (sequence b, chunk c).
-//  1. Decides for b (identically in each of the sequence's C tasks), then loads chunk c of
-//     the final draw's row(s) (two rows after a rejection) and sums, for each of its NV
-//     segments, the draw weights and p: per lane in fp32, across lanes in fp64.
-//  2. Hands the segment masses over.  Every task but the sequence's last (chunk C-1)
-//     ends here.
-//  3. The last task waits for the masses of chunks 0 .. C-2, scans the C*NV segment
-//     masses in vocabulary order, takes the first segment whose inclusive prefix reaches
-//     u * W (W = the total), narrows it to a lane and an element, and writes the emitted
+//  1. Decides for b (identically in each of the sequence's C tasks; the last task, chunk
+//     C-1, writes the count and probabilities), then loads chunk c of the final draw's
+//     row(s) (two rows after a rejection) and sums, for each of its NV segments, the draw
+//     weights and p: per lane in fp32, across lanes in fp64.
+//  2. Hands the segment masses over and waits for those of the sequence's other tasks.
+//  3. Scans the C*NV segment masses in vocabulary order -- the same way in every task of
+//     the sequence -- and takes the first segment whose inclusive prefix reaches u * W
+//     (W = the total).  The task whose chunk holds that segment narrows it to a lane and
+//     an element (its loads of the chunk are still in the cache) and writes the emitted
 //     row (x_0 .. x_{n-1}, the drawn token, then -1).  If rounding leaves no residual mass
-//     (W = 0 after a rejection) it draws from the masses of p instead.
-// Only last tasks wait, and only for tasks of this launch; the host keeps Bs at most half
-// of the workgroups the device holds at once, so the tasks they wait for always find
-// room and every wait ends (each is also bounded; on timeout the sequence is flagged).
+//     (W = 0 after a rejection) the draw uses the masses of p instead.
+// Tasks wait only for tasks of the same launch, and the host keeps a launch to at most
+// the workgroups the device holds at once, so all of them become resident and every wait
+// ends (each is also bounded; on timeout the sequence is flagged invalid).
 //
 // Vocabulary order inside a chunk is segment-major (a segment = one 16-byte vector per
 // lane), then lane, then element.
@@ -460,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : row_t;
 
   // ---- 1. per-lane masses of this chunk's segments: the draw weights, and p.  The
-  // chunk is read in two halves to bound the registers held.
+  // chunk is read in two halves (fewer requests in flight at once measured faster).
   {
     constexpr int H = NV > 1 ? NV / 2 : 1;
     const bool residual = mode == kModeResidual;
@@ -513,9 +525,8 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
     v = row16_inclusive_sum(v);
     if (q < 2 * NV && r == 15) put_slot((q < NV ? mw : mp) + c * NV + (q % NV), v, a.gen);
   }
-  if (!last) return;
 
-  // ---- 3. the last task: every chunk's masses (this lane's share of the units)
+  // ---- 3. every chunk's masses (this lane's share of the units)
   const int per = (units + kThreads - 1) / kThreads;  // <= 4
   const int u0 = tid * per;
   double mass[4];
@@ -534,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
       }
       if (!__syncthreads_or(missing)) break;
       if (tid == 0) {
-        poll_pause();
+        short_pause();
         --s_budget;
       }
       __syncthreads();
@@ -544,9 +555,11 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
       }
     }
     if (!arrived) {  // flag the sequence rather than wait on
-      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-      for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
-      if (tid == 0) a.out_num[b] = -1;
+      if (last) {
+        int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+        for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
+        if (tid == 0) a.out_num[b] = -1;
+      }
       return;
     }
     W = block_sum(mass[0] + mass[1] + mass[2] + mass[3], s_d);
@@ -580,6 +593,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
     usel = block_max_int(lastu, s_i);
     if (usel < 0) usel = 0;
   }
+  if (usel / NV != c) return;  // another task of the sequence holds the segment
   if (u0 <= usel && usel < u0 + per) {
     double run = before;
 #pragma unroll
@@ -589,9 +603,10 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   }
   __syncthreads();
   const double t_loc = tt - s_base;
-  const int seg_start = (usel / NV) * kChunk + (usel % NV) * kSeg;
+  const int seg_start = c * kChunk + (usel % NV) * kSeg;
 
-  // ---- the lane and the element inside that segment
+  // ---- the lane and the element inside that segment (this task read the chunk moments
+  // ago, so these loads are served from the cache)
   const int e0 = seg_start + tid * E;
   const u32x4 vt = load_vector<DT, VEC>(row_t, a.V, e0);
   const u32x4 vd = mode == kModeResidual ? load_vector<DT, VEC>(row_d, a.V, e0) : vt;
@@ -659,6 +674,9 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
   const int epv = dtype == SPEC_BF16 ? 8 : 4;
   L.R = 2 * K + 1;
   L.nv = choose_nv(static_cast<long long>(B) * L.R, V, epv, 1024);
+  // the partials of one row (4 per chunk) must fit the decision's staging
+  while (L.nv < 8 && (V + static_cast<long long>(L.nv) * kThreads * epv - 1) / (static_cast<long long>(L.nv) * kThreads * epv) * kWaves > kStage)
+    L.nv *= 2;
   const long long chunk = static_cast<long long>(L.nv) * kThreads * epv;
   L.C = static_cast<int>((V + chunk - 1) / chunk);
   const size_t segs = static_cast<size_t>(B) * L.C * L.nv;
@@ -666,7 +684,7 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
   L.off_gath = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(B) * L.R, 256);
   L.off_part = off;
-  off = align_up(off + sizeof(RowStat) * static_cast<size_t>(B) * L.R * L.C, 256);
+  off = align_up(off + sizeof(RowStat) * static_cast<size_t>(B) * L.R * L.C * kWaves, 256);
   L.off_wseg = off;
   off = align_up(off + sizeof(SlotDouble) * segs, 256);
   L.off_wsegp = off;
@@ -675,10 +693,9 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
   return L;
 }
 
-// Sequences per pool launch: at most half of the pool workgroups the current device
-// holds at once (cached per device), so that the tasks a last task waits for always
-// find room.
-static int pool_sequences(const void* kernel, std::atomic<int>* cache) {
+// Sequences per pool launch: C tasks each, at most as many tasks as the current device
+// holds at once (cached per device), so that all tasks of a launch become resident.
+static int pool_sequences(const void* kernel, int C, std::atomic<int>* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   int slots = dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
@@ -689,7 +706,7 @@ static int pool_sequences(const void* kernel, std::atomic<int>* cache) {
     slots = max(1, per_cu) * max(1, cus);
     if (dev < kMaxDevices) cache[dev].store(slots, std::memory_order_relaxed);
   }
-  return max(1, slots / 2);
+  return max(1, slots / max(1, C));
 }
 
 // Generation of the next call's slot words: a process-wide counter with a random start,
@@ -718,7 +735,7 @@ static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
   }
   {
     const auto kernel = chain_pool_kernel<DT, NV, VEC>;
-    const int per_launch = pool_sequences(reinterpret_cast<const void*>(kernel), slots_cache);
+    const int per_launch = pool_sequences(reinterpret_cast<const void*>(kernel), a.C, slots_cache);
     for (int b0 = 0; b0 < a.B; b0 += per_launch) {
       const int bs = min(per_launch, a.B - b0);
       LaunchScope scope("chain_pool", stream);
@@ -784,8 +801,9 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   const ChainLayout L = chain_layout(B, K, V, dtype);
   const double groups = static_cast<double>(B) * L.R * L.C;
   if (groups > 2147483647.0) return fail(SPEC_ERR_UNSUPPORTED, "grid of %.0f workgroups too large", groups);
-  if (L.C * L.nv > 4 * kThreads)
-    return fail(SPEC_ERR_UNSUPPORTED, "V = %d needs more than %d segments", V, 4 * kThreads);
+  if (L.C * L.nv > 4 * kThreads || L.C * kWaves > kStage)
+    return fail(SPEC_ERR_UNSUPPORTED, "V = %d is too large (more than %d chunks of %d elements)", V, kStage / kWaves,
+                L.nv * kThreads * (dtype == SPEC_BF16 ? 8 : 4));
   if (!workspace) return fail(SPEC_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(SPEC_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < L.bytes)

@@ -219,6 +219,15 @@ __device__ __forceinline__ int wave_inclusive_scan_int(int v) {
   return v;
 }
 
+// Inclusive max-scan within each 16-lane row of the wave (lane 15 of a row holds the max).
+__device__ __forceinline__ float row16_inclusive_max(float v) {
+  v = fmaxf(v, dpp_float<dppc::kRowShr1>(-INFINITY, v));
+  v = fmaxf(v, dpp_float<dppc::kRowShr2>(-INFINITY, v));
+  v = fmaxf(v, dpp_float<dppc::kRowShr4>(-INFINITY, v));
+  v = fmaxf(v, dpp_float<dppc::kRowShr8>(-INFINITY, v));
+  return v;
+}
+
 // Inclusive scan within each 16-lane row of the wave (lane 15 of a row holds its total).
 __device__ __forceinline__ double row16_inclusive_sum(double v) {
   v += dpp_double<dppc::kRowShr1>(0.0, v);
