@@ -41,19 +41,24 @@ def progress(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-HOST_SIDE_MARKER = "// ---------------------------------------------------------------- host side"
+STATS_END_MARKER = "// ---------------------------------------------------------------- final draw"
 
 
-def source_digest(paths) -> str:
-    """Digest of the device code in `paths`: each file up to its host-side marker line (launch
-    and argument checking code after it does not change what the kernels read or write)."""
+def source_digest(parts) -> str:
+    """Digest of the device code a kernel is built from: for each (path, end_marker), the
+    file up to the marker line (the whole file when the marker is None)."""
     h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
+    for path, marker in parts:
+        with open(os.path.join(ROOT, path), "rb") as f:
             text = f.read()
-        cut = text.find(HOST_SIDE_MARKER.encode())
+        cut = text.find(marker.encode()) if marker else -1
         h.update(text if cut < 0 else text[:cut])
     return h.hexdigest()[:16]
+
+
+# the chain_stats kernel: chain.hip up to its draw section, and the shared device helpers
+STATS_SOURCES = (("draft_token_verification_09_amd/csrc/chain.hip", STATS_END_MARKER),
+                 ("draft_token_verification_09_amd/csrc/device_common.h", None))
 
 
 def read_traffic(kernel: str, workload: str, digest: str):
@@ -191,7 +196,8 @@ def bench_chain_workload(make, name, warmup, steps, dev, kernel_timing=True):
     if kernel_timing:
         _, kms = time_calls(call, n_sets, 2, steps, kernel_timing=True)
     del sets
-    return dict(ms=ms, bytes=per_set, kernels=kms, host=host0, positions=probe.B * probe.K, host_us=host_us)
+    return dict(ms=ms, bytes=per_set, kernels=kms, host=host0, positions=probe.B * probe.K, host_us=host_us,
+                steps=steps)
 
 
 def cpu_baseline(host_inp, budget_s=15.0):
@@ -239,15 +245,17 @@ def other_workloads(warmup, steps, dev):
         sets.append((to_dev(tr.target, "bf16", dev), torch.from_numpy(tr.parent).to(dev),
                      torch.from_numpy(tr.node_token).to(dev)))
 
+    prepared = [sv.prepare_spec_verify_tree_greedy(t, p, k, 6) for t, p, k in sets]
+
     def tcall(i):
-        t, p, k = sets[i]
-        sv.spec_verify_tree_greedy(t, p, k, 6)
+        prepared[i]()
 
     ms, _ = time_calls(tcall, n_sets, warmup, steps, False)
     _, kms = time_calls(tcall, n_sets, 2, steps, True)
     del sets
     tb = per + tr0.B * (7 * 3 + 1 + tr0.N1) * 4
-    out.append(_entry("tree_greedy_B32_N60_V128256_bf16", dict(ms=ms, bytes=tb, kernels=kms), tr0.B * (tr0.N1 - 1)))
+    out.append(_entry("tree_greedy_B32_N60_V128256_bf16", dict(ms=ms, bytes=tb, kernels=kms, steps=steps),
+                      tr0.B * (tr0.N1 - 1)))
 
     # n-gram propose + one-hot verify, B=128 L=4096 K=5 V=32000 bf16
     progress("ngram: generating inputs")
@@ -264,16 +272,25 @@ def other_workloads(warmup, steps, dev):
                          ua=torch.from_numpy(inp.u_accept).to(dev), uf=torch.from_numpy(inp.u_final).to(dev),
                          bytes=chain_bytes(inp) + pr.context.nbytes + pr.context_len.nbytes))
 
+    # propose, then verify the proposals in place (the verify reads the propose's outputs)
+    pairs = []
+    for s in sets:
+        pp = sv.prepare_ngram_propose(s["ctx"], s["cl"], 1, 4, 5)
+        pv = sv.prepare_spec_verify_chain(s["t"], None, pp.result.draft_tokens, s["T"], s["ua"], s["uf"],
+                                          pp.result.draft_len)
+        pairs.append((pp, pv))
+
     def ncall(i):
-        s = sets[i]
-        g = sv.ngram_propose(s["ctx"], s["cl"], 1, 4, 5)
-        sv.spec_verify_chain(s["t"], None, g.draft_tokens, s["T"], s["ua"], s["uf"], g.draft_len)
+        pp, pv = pairs[i]
+        pp()
+        pv()
 
     ms, _ = time_calls(ncall, n_sets, warmup, steps, False)
     _, kms = time_calls(ncall, n_sets, 2, steps, True)
     nb = int(np.mean([s["bytes"] for s in sets]))
     del sets
-    out.append(_entry("ngram_propose_verify_B128_L4096_K5_V32000_bf16", dict(ms=ms, bytes=nb, kernels=kms), 128 * 5))
+    out.append(_entry("ngram_propose_verify_B128_L4096_K5_V32000_bf16", dict(ms=ms, bytes=nb, kernels=kms, steps=steps),
+                      128 * 5))
     return out
 
 
@@ -282,7 +299,14 @@ def _entry(workload, r, positions):
     return dict(workload=workload, ms_per_call=round(ms, 5), positions_per_s=round(positions / (ms * 1e-3), 1),
                 algorithmic_GBps=round(r["bytes"] / (ms * 1e-3) / 1e9, 1),
                 frac_of_hbm_peak=round(r["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                kernels_us={k: round(v[1] / v[0] * 1e3, 2) for k, v in r["kernels"].items()})
+                kernels_us_per_call=kernels_per_call(r["kernels"], r.get("steps")))
+
+
+def kernels_per_call(kernels, steps):
+    """{kernel: microseconds per call} (summed over the call's launches of that kernel)."""
+    if not steps:
+        return {k: round(v[1] / v[0] * 1e3, 2) for k, v in kernels.items()}
+    return {k: round(v[1] / steps * 1e3, 3) for k, v in kernels.items()}
 
 
 def probe(dev, nbytes=1 << 30):
@@ -351,8 +375,7 @@ def main():
     stats_launches, stats_ms = head["kernels"].get(ROOF_KERNEL, (1, float("nan")))
     stats_avg_s = stats_ms / stats_launches * 1e-3
     achieved = logits_bytes / stats_avg_s / 1e9
-    digest = source_digest(["draft_token_verification_09_amd/csrc/chain.hip",
-                            "draft_token_verification_09_amd/csrc/device_common.h"])
+    digest = source_digest(STATS_SOURCES)
     traffic = read_traffic(ROOF_KERNEL, "B64_K5_V128256_bf16", digest)
 
     result = {
@@ -372,7 +395,7 @@ def main():
         "config": {"workload": workload, "B": B, "K": K, "V": V, "temperature": 0.8,
                    "input_sets_rotated": sets_needed(head["bytes"]), "parallelism": "single GPU"},
         "achieved_GBps_step": round(head["bytes"] / (ms * 1e-3) / 1e9, 1),
-        "kernels_us": {k: round(v[1] / v[0] * 1e3, 3) for k, v in head["kernels"].items()},
+        "kernels_us_per_call": kernels_per_call(head["kernels"], args.steps),
         "host_issue_us_per_step": round(head["host_us"], 2),
         "roofline": {
             "bound": "hbm",

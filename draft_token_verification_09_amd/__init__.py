@@ -14,7 +14,9 @@ from .binding import (  # noqa: F401
     lib,
     loaded_library_path,
     ngram_propose,
+    prepare_ngram_propose,
     prepare_spec_verify_chain,
+    prepare_spec_verify_tree_greedy,
     spec_probe_copy,
     spec_probe_read,
     spec_timing_collect,

@@ -262,11 +262,9 @@ class TreeResult:
     argmax: Optional[torch.Tensor]  # [B, N1] int32
 
 
-def spec_verify_tree_greedy(target_logits: torch.Tensor, parent: torch.Tensor, node_token: torch.Tensor,
-                            max_depth: int, *, want_argmax: bool = True, out: Optional[TreeResult] = None,
-                            workspace_buf: Optional[torch.Tensor] = None, stream=None) -> TreeResult:
-    """Batched greedy tree verification (spec_verify_tree_greedy).  target [B, N1, V],
-    parent [B, N1] int32, node_token [B, N1] int32."""
+def _tree_call(target_logits, parent, node_token, max_depth, want_argmax, out, workspace_buf, stream):
+    """Checks the tensors and returns (argument tuple of spec_verify_tree_greedy, result,
+    buffers the call uses)."""
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [B, N1, V]")
     B, N1, V = target_logits.shape
@@ -285,15 +283,32 @@ def spec_verify_tree_greedy(target_logits: torch.Tensor, parent: torch.Tensor, n
             argmax=torch.empty((B, N1), dtype=torch.int32, device=dev) if want_argmax else None,
         )
     s = _stream(stream, dev)
-    L = lib()
-    need = int(L.spec_verify_tree_greedy_workspace_size(B, N1, V, code)) if B > 0 else 0
+    need = int(lib().spec_verify_tree_greedy_workspace_size(B, N1, V, code)) if B > 0 else 0
     buf = workspace_buf if workspace_buf is not None else workspace(need, dev, s, "tree")
     wp, wbytes = _aligned_ptr(buf)
-    st = L.spec_verify_tree_greedy(_ptr(target_logits), code, _ptr(parent), _ptr(node_token), B, N1, V, max_depth,
-                                   _ptr(out.accept_len), _ptr(out.tokens), _ptr(out.path_nodes), _ptr(out.argmax),
-                                   wp, wbytes, s)
-    _check("spec_verify_tree_greedy", st)
+    args = (_ptr(target_logits), code, _ptr(parent), _ptr(node_token), B, N1, V, max_depth,
+            _ptr(out.accept_len), _ptr(out.tokens), _ptr(out.path_nodes), _ptr(out.argmax), wp, wbytes, s)
+    return args, out, (target_logits, parent, node_token, buf)
+
+
+def spec_verify_tree_greedy(target_logits: torch.Tensor, parent: torch.Tensor, node_token: torch.Tensor,
+                            max_depth: int, *, want_argmax: bool = True, out: Optional[TreeResult] = None,
+                            workspace_buf: Optional[torch.Tensor] = None, stream=None) -> TreeResult:
+    """Batched greedy tree verification (spec_verify_tree_greedy).  target [B, N1, V],
+    parent [B, N1] int32, node_token [B, N1] int32."""
+    args, out, _ = _tree_call(target_logits, parent, node_token, max_depth, want_argmax, out, workspace_buf, stream)
+    _check("spec_verify_tree_greedy", lib().spec_verify_tree_greedy(*args))
     return out
+
+
+def prepare_spec_verify_tree_greedy(target_logits: torch.Tensor, parent: torch.Tensor, node_token: torch.Tensor,
+                                    max_depth: int, *, want_argmax: bool = True, out: Optional[TreeResult] = None,
+                                    workspace_buf: Optional[torch.Tensor] = None, stream=None) -> PreparedCall:
+    """spec_verify_tree_greedy with every argument fixed (see PreparedCall)."""
+    args, out, keep = _tree_call(target_logits, parent, node_token, max_depth, want_argmax, out, workspace_buf,
+                                 stream)
+    return PreparedCall("spec_verify_tree_greedy", lib().spec_verify_tree_greedy,
+                        _SIGNATURES["spec_verify_tree_greedy"][1], args, out, keep)
 
 
 @dataclass
@@ -303,9 +318,7 @@ class NgramResult:
     match_n: Optional[torch.Tensor]  # [B] int32
 
 
-def ngram_propose(context: torch.Tensor, context_len: torch.Tensor, n_min: int, n_max: int, K: int, *,
-                  want_match_n: bool = True, out: Optional[NgramResult] = None, stream=None) -> NgramResult:
-    """Batched prompt n-gram lookup (ngram_propose).  context [B, L_max] int32, context_len [B] int32."""
+def _ngram_call(context, context_len, n_min, n_max, K, want_match_n, out, stream):
     if context.dim() != 2:
         raise ValueError("context must be [B, L_max]")
     B, L_max = context.shape
@@ -319,10 +332,24 @@ def ngram_propose(context: torch.Tensor, context_len: torch.Tensor, n_min: int, 
             match_n=torch.empty((B,), dtype=torch.int32, device=dev) if want_match_n else None,
         )
     s = _stream(stream, dev)
-    st = lib().ngram_propose(_ptr(context), _ptr(context_len), B, L_max, n_min, n_max, K,
-                             _ptr(out.draft_tokens), _ptr(out.draft_len), _ptr(out.match_n), s)
-    _check("ngram_propose", st)
+    args = (_ptr(context), _ptr(context_len), B, L_max, n_min, n_max, K,
+            _ptr(out.draft_tokens), _ptr(out.draft_len), _ptr(out.match_n), s)
+    return args, out, (context, context_len)
+
+
+def ngram_propose(context: torch.Tensor, context_len: torch.Tensor, n_min: int, n_max: int, K: int, *,
+                  want_match_n: bool = True, out: Optional[NgramResult] = None, stream=None) -> NgramResult:
+    """Batched prompt n-gram lookup (ngram_propose).  context [B, L_max] int32, context_len [B] int32."""
+    args, out, _ = _ngram_call(context, context_len, n_min, n_max, K, want_match_n, out, stream)
+    _check("ngram_propose", lib().ngram_propose(*args))
     return out
+
+
+def prepare_ngram_propose(context: torch.Tensor, context_len: torch.Tensor, n_min: int, n_max: int, K: int, *,
+                          want_match_n: bool = True, out: Optional[NgramResult] = None, stream=None) -> PreparedCall:
+    """ngram_propose with every argument fixed (see PreparedCall)."""
+    args, out, keep = _ngram_call(context, context_len, n_min, n_max, K, want_match_n, out, stream)
+    return PreparedCall("ngram_propose", lib().ngram_propose, _SIGNATURES["ngram_propose"][1], args, out, keep)
 
 
 # -------------------------------------------------------------------- measurement hooks

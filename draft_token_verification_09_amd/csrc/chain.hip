@@ -429,21 +429,25 @@ __device__ __forceinline__ void chain_pack(const ChainArgs& a) {
 //     C-1, writes the count and probabilities), then loads chunk c of the final draw's
 //     row(s) (two rows after a rejection) and sums, for each of its NV segments, the draw
 //     weights and p: per lane in fp32, across lanes in fp64.
-//  2. Hands the segment masses over and waits for those of the sequence's other tasks.
-//  3. Scans the C*NV segment masses in vocabulary order -- the same way in every task of
-//     the sequence -- and takes the first segment whose inclusive prefix reaches u * W
-//     (W = the total).  The task whose chunk holds that segment narrows it to a lane and
-//     an element (its loads of the chunk are still in the cache) and writes the emitted
-//     row (x_0 .. x_{n-1}, the drawn token, then -1).  If rounding leaves no residual mass
-//     (W = 0 after a rejection) the draw uses the masses of p instead.
-// Tasks wait only for tasks of the same launch, and the host keeps a launch to at most
-// the workgroups the device holds at once, so all of them become resident and every wait
-// ends (each is also bounded; on timeout the sequence is flagged invalid).
+//  2. Hands the segment masses over and waits for those of the sequence's other tasks --
+//     every task when all_wait is set, else only the sequence's last task.
+//  3. Scans the C*NV segment masses in vocabulary order -- the same way in every waiting
+//     task -- and takes the first segment whose inclusive prefix reaches u * W (W = the
+//     total).  With all_wait the task whose chunk holds that segment (whose loads of it are
+//     still in the cache) finishes, else the last task: it narrows the segment to a lane
+//     and an element and writes the emitted row (x_0 .. x_{n-1}, the drawn token, then
+//     -1).  If rounding leaves no residual mass (W = 0 after a rejection) the draw uses
+//     the masses of p instead.
+// Tasks wait only for tasks of the same launch.  The host sets all_wait only when every
+// task of the launch fits on the device at once, and otherwise keeps the number of
+// sequences (hence of waiting tasks) to at most half of what fits, so the tasks waited
+// for always find room.  Every wait therefore ends (each is also bounded; on timeout the
+// sequence is flagged invalid).
 //
 // Vocabulary order inside a chunk is segment-major (a segment = one 16-byte vector per
 // lane), then lane, then element.
 template <int DT, int NV, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0) {
+__global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0, int all_wait) {
   constexpr int kRedBytes = 2 * NV * kThreads * static_cast<int>(sizeof(float));
   __shared__ __align__(16) unsigned char s_buf[kRedBytes > kStageBytes ? kRedBytes : kStageBytes];
   __shared__ ChainDecision s_dec;
@@ -525,6 +529,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
     v = row16_inclusive_sum(v);
     if (q < 2 * NV && r == 15) put_slot((q < NV ? mw : mp) + c * NV + (q % NV), v, a.gen);
   }
+  if (!all_wait && !last) return;
 
   // ---- 3. every chunk's masses (this lane's share of the units)
   const int per = (units + kThreads - 1) / kThreads;  // <= 4
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
     usel = block_max_int(lastu, s_i);
     if (usel < 0) usel = 0;
   }
-  if (usel / NV != c) return;  // another task of the sequence holds the segment
+  if (all_wait && usel / NV != c) return;  // another task of the sequence holds the segment
   if (u0 <= usel && usel < u0 + per) {
     double run = before;
 #pragma unroll
@@ -603,10 +608,9 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   }
   __syncthreads();
   const double t_loc = tt - s_base;
-  const int seg_start = c * kChunk + (usel % NV) * kSeg;
+  const int seg_start = (usel / NV) * kChunk + (usel % NV) * kSeg;
 
-  // ---- the lane and the element inside that segment (this task read the chunk moments
-  // ago, so these loads are served from the cache)
+  // ---- the lane and the element inside that segment
   const int e0 = seg_start + tid * E;
   const u32x4 vt = load_vector<DT, VEC>(row_t, a.V, e0);
   const u32x4 vd = mode == kModeResidual ? load_vector<DT, VEC>(row_d, a.V, e0) : vt;
@@ -693,9 +697,8 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
   return L;
 }
 
-// Sequences per pool launch: C tasks each, at most as many tasks as the current device
-// holds at once (cached per device), so that all tasks of a launch become resident.
-static int pool_sequences(const void* kernel, int C, std::atomic<int>* cache) {
+// Pool workgroups the current device holds at once (cached per device).
+static int pool_slots(const void* kernel, std::atomic<int>* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   int slots = dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
@@ -706,7 +709,7 @@ static int pool_sequences(const void* kernel, int C, std::atomic<int>* cache) {
     slots = max(1, per_cu) * max(1, cus);
     if (dev < kMaxDevices) cache[dev].store(slots, std::memory_order_relaxed);
   }
-  return max(1, slots / max(1, C));
+  return slots;
 }
 
 // Generation of the next call's slot words: a process-wide counter with a random start,
@@ -735,12 +738,16 @@ static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
   }
   {
     const auto kernel = chain_pool_kernel<DT, NV, VEC>;
-    const int per_launch = pool_sequences(reinterpret_cast<const void*>(kernel), a.C, slots_cache);
+    const int slots = pool_slots(reinterpret_cast<const void*>(kernel), slots_cache);
+    // every task waits when the whole launch fits at once; else only last tasks wait,
+    // at most half of what fits per launch
+    const int all_wait = static_cast<long long>(a.B) * a.C <= slots && env_int("SPEC_POOL_ALL_WAIT", 1) != 0 ? 1 : 0;
+    const int per_launch = all_wait ? a.B : max(1, slots / 2);
     for (int b0 = 0; b0 < a.B; b0 += per_launch) {
       const int bs = min(per_launch, a.B - b0);
       LaunchScope scope("chain_pool", stream);
       hipExtLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(static_cast<long long>(bs) * a.C)), dim3(kThreads), 0,
-                            stream, scope.start(), scope.stop(), 0, a, b0);
+                            stream, scope.start(), scope.stop(), 0, a, b0, all_wait);
       const spec_status_t st = scope.finish();
       if (st != SPEC_OK) return st;
     }

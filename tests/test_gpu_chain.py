@@ -118,3 +118,24 @@ def test_dirty_workspace_reused_across_shapes():
             assert rep.ok(), rep.failures[:5]
             check_packed(res, inp.B)
         ws.fill_(0xFF if rnd == 0 else 0x00)
+
+
+@pytest.mark.parametrize("recipe", ["high", "low"])
+def test_pool_wait_modes_agree(recipe, monkeypatch):
+    # the pool kernel finishes the draw either in the task owning the chosen segment (every
+    # task waits) or in each sequence's last task (only last tasks wait); same results
+    import draft_token_verification_09_amd as sv
+
+    inp = (synth.chain_config_high_accept_bf16(6, B=20, V=70000) if recipe == "high"
+           else synth.chain_config_low_accept_bf16(6, B=20, K=8, V=70000))
+    args = _device_args(inp)
+    monkeypatch.setenv("SPEC_POOL_ALL_WAIT", "1")
+    a = sv.spec_verify_chain(*args)
+    monkeypatch.setenv("SPEC_POOL_ALL_WAIT", "0")
+    b = sv.spec_verify_chain(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(a.tokens, b.tokens)
+    assert torch.equal(a.num_accepted, b.num_accepted)
+    assert torch.equal(a.probs, b.probs)
+    rep = compare_chain(b, chain_oracle(inp), inp)
+    assert rep.ok(), rep.failures[:5]

@@ -138,3 +138,24 @@ def test_ngram_device_outputs_feed_verify_directly():
     torch.cuda.synchronize()
     rep = compare_chain(res, ref, inp)
     assert rep.ok(), rep.failures[:5]
+
+
+def test_prepared_tree_and_ngram_match_plain_calls():
+    import draft_token_verification_09_amd as sv
+
+    tr = synth.tree_inputs(12, B=8, n_nodes=30, depth=5, V=5000, dtype="bf16")
+    t, p, k = logits_to_device(tr.target, "bf16"), i32(tr.parent), i32(tr.node_token)
+    plain = sv.spec_verify_tree_greedy(t, p, k, tr.max_depth)
+    prep = sv.prepare_spec_verify_tree_greedy(t, p, k, tr.max_depth)
+    res = prep()
+    res = prep()
+    torch.cuda.synchronize()
+    for name in ("accept_len", "tokens", "path_nodes", "argmax"):
+        assert torch.equal(getattr(plain, name), getattr(res, name)), name
+    pr = synth.ngram_config_prompts(5, B=16)
+    ctx, cl = i32(pr.context), i32(pr.context_len)
+    plain = sv.ngram_propose(ctx, cl, 1, 4, 5)
+    res = sv.prepare_ngram_propose(ctx, cl, 1, 4, 5)()
+    torch.cuda.synchronize()
+    for name in ("draft_tokens", "draft_len", "match_n"):
+        assert torch.equal(getattr(plain, name), getattr(res, name)), name
