@@ -34,9 +34,11 @@
  *     outputs instead (documented per call), and other sequences are unaffected.
  *   - Results are deterministic: no floating-point atomics feed any result.
  *   - A workspace is scratch for one call at a time: its contents need no
- *     initialisation and are meaningless after the call (every byte a kernel
- *     reads was written earlier in the same call).  Calls that overlap in time
- *     (different streams) need different workspaces.
+ *     initialisation and are meaningless after the call.  A kernel uses only
+ *     values written earlier in the same call (values that workgroups hand to
+ *     each other carry the call's generation number, so whatever the
+ *     workspace held before is recognised and ignored).  Calls that overlap
+ *     in time (different streams) need different workspaces.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
