@@ -16,12 +16,13 @@
 //               sum exp2(l * log2(e)/T - o)) and, if the chunk holds the row's drafted
 //               token x_k, copies l(x_k) out of its registers.  This is the pass that
 //               reads every logit, once.
-//  chain_pool   grid = B x C tasks (see chain_pool_kernel): every task of a sequence
+//  chain_pool   grid = B x S/4 tasks (see chain_pool_kernel): every task of a sequence
 //               combines the partials into per-row (O, S) and evaluates p(x_k), q(x_k),
 //               alpha_k and the accept tests of all drafted positions at once (one lane
-//               per position), taking the first rejection n with a wave ballot; task c
-//               then sums the final draw's weights over the segments of chunk c, and the
-//               sequence's last task draws the token from those masses.
+//               per position), taking the first rejection n with a wave ballot; each task
+//               then sums the final draw's weights over its 4 segments of the row (a
+//               segment = one 16-byte vector per lane), and the token is drawn from those
+//               masses.
 //  chain_pack   grid = 1, only for packed output: offsets and packed tokens.
 //
 // Softmax is evaluated in the exp2 domain: with scale = log2(e)/T,
@@ -123,6 +124,7 @@ struct ChainArgs {
   const float* u_accept;
   const float* u_final;
   int B, K, V, C, R;
+  int S;                // pool segment slots per row: ceil(V / segment) rounded up to whole tasks
   int32_t* out_tokens;
   int32_t* out_num;
   float* out_probs;
@@ -131,8 +133,8 @@ struct ChainArgs {
   uint32_t gen;         // generation of this call's slot words
   RowStat* part;        // [B, R, C, 4] partials, one per wave of each chunk
   float* gath;          // [B, R] logit of the drafted token in each scoring row
-  SlotDouble* wseg;     // [B, C, NV] slots: mass of the final draw's weights per segment
-  SlotDouble* wsegp;    // [B, C, NV] slots: mass of p of the same row per segment (fallback)
+  SlotDouble* wseg;     // [B, S] slots: mass of the final draw's weights per segment
+  SlotDouble* wsegp;    // [B, S] slots: mass of p of the same row per segment (fallback)
 };
 
 template <int DT>
@@ -424,17 +426,19 @@ __device__ __forceinline__ void chain_pack(const ChainArgs& a) {
   if (tid == 0) a.out_offsets[a.B] = total;
 }
 
-// grid = Bs x C pool tasks for the sequences b0 .. b0+Bs-1: task t = (sequence b, chunk c).
-//  1. Decides for b (identically in each of the sequence's C tasks; the last task, chunk
-//     C-1, writes the count and probabilities), then loads chunk c of the final draw's
-//     row(s) (two rows after a rejection) and sums, for each of its NV segments, the draw
-//     weights and p: per lane in fp32, across lanes in fp64.
+// grid = Bs x CP pool tasks for the sequences b0 .. b0+Bs-1, CP = S/SPT per sequence:
+// task t = (sequence b, group c of SPT consecutive segments; a segment is one 16-byte vector
+// per lane, 256*E elements, and a row has S segment slots, the last ones past V weighing 0).
+//  1. Decides for b (identically in each of the sequence's tasks; the last task writes the
+//     count and probabilities), then loads its segments of the final draw's row(s) (two
+//     rows after a rejection) and sums, for each segment, the draw weights and p: per lane
+//     in fp32, across lanes in fp64.
 //  2. Hands the segment masses over and waits for those of the sequence's other tasks --
 //     every task when all_wait is set, else only the sequence's last task.
-//  3. Scans the C*NV segment masses in vocabulary order -- the same way in every waiting
+//  3. Scans the S segment masses in vocabulary order -- the same way in every waiting
 //     task -- and takes the first segment whose inclusive prefix reaches u * W (W = the
-//     total).  With all_wait the task whose chunk holds that segment (whose loads of it are
-//     still in the cache) finishes, else the last task: it narrows the segment to a lane
+//     total).  With all_wait the task holding that segment (whose loads of it are still in
+//     the cache) finishes, else the last task: it narrows the segment to a lane
 //     and an element and writes the emitted row (x_0 .. x_{n-1}, the drawn token, then
 //     -1).  If rounding leaves no residual mass (W = 0 after a rejection) the draw uses
 //     the masses of p instead.
@@ -446,9 +450,9 @@ __device__ __forceinline__ void chain_pack(const ChainArgs& a) {
 //
 // Vocabulary order inside a chunk is segment-major (a segment = one 16-byte vector per
 // lane), then lane, then element.
-template <int DT, int NV, bool VEC>
+template <int DT, int SPT, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0, int all_wait) {
-  constexpr int kRedBytes = 2 * NV * kThreads * static_cast<int>(sizeof(float));
+  constexpr int kRedBytes = 2 * SPT * kThreads * static_cast<int>(sizeof(float));
   __shared__ __align__(16) unsigned char s_buf[kRedBytes > kStageBytes ? kRedBytes : kStageBytes];
   __shared__ ChainDecision s_dec;
   __shared__ double s_d[kWaves];
@@ -457,16 +461,15 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   __shared__ int s_budget, s_y;
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
-  constexpr int kSeg = ChunkShape<DT, NV>::kSegment;
-  constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
+  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;  // elements per segment
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int C = a.C;
-  const int b = b0 + static_cast<int>(blockIdx.x) / C;
-  const int c = static_cast<int>(blockIdx.x) % C;
-  const bool last = c == C - 1;
-  float* red = reinterpret_cast<float*>(s_buf);  // [2][NV][kThreads] per-lane masses
+  const int CP = a.S / SPT;  // tasks per sequence
+  const int b = b0 + static_cast<int>(blockIdx.x) / CP;
+  const int c = static_cast<int>(blockIdx.x) % CP;  // this task's group of SPT segments
+  const bool last = c == CP - 1;
+  float* red = reinterpret_cast<float*>(s_buf);  // [2][SPT][kThreads] per-lane masses
 
   chain_decide<DT>(a, b, clamped_len(a, b), last, &s_dec, s_buf);
   const ChainDecision d = uniform_decision(s_dec);
@@ -475,59 +478,53 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   const void* row_t = target_row<DT>(a, b, d.row);
   const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : row_t;
 
-  // ---- 1. per-lane masses of this chunk's segments: the draw weights, and p.  The
-  // chunk is read in two halves (fewer requests in flight at once measured faster).
+  // ---- 1. per-lane masses of this task's segments: the draw weights, and p
   {
-    constexpr int H = NV > 1 ? NV / 2 : 1;
     const bool residual = mode == kModeResidual;
     const int excl = mode == kModeOneHot ? d.excl_tok : -1;
+    const int sbase = c * SPT * kSeg;  // first element of this task's segments
+    u32x4 rt[SPT], rd[SPT];
 #pragma unroll
-    for (int h = 0; h < NV; h += H) {
-      u32x4 rt[H], rd[H];
-      const int sbase = c * kChunk + h * kSeg;  // first element of this half
+    for (int j = 0; j < SPT; ++j) rt[j] = load_vector<DT, VEC>(row_t, a.V, sbase + (j * kThreads + tid) * E);
+    if (residual) {
 #pragma unroll
-      for (int j = 0; j < H; ++j) rt[j] = load_vector<DT, VEC>(row_t, a.V, sbase + (j * kThreads + tid) * E);
-      if (residual) {
+      for (int j = 0; j < SPT; ++j) rd[j] = load_vector<DT, VEC>(row_d, a.V, sbase + (j * kThreads + tid) * E);
+    } else {
 #pragma unroll
-        for (int j = 0; j < H; ++j) rd[j] = load_vector<DT, VEC>(row_d, a.V, sbase + (j * kThreads + tid) * E);
-      } else {
+      for (int j = 0; j < SPT; ++j) rd[j] = rt[j];
+    }
 #pragma unroll
-        for (int j = 0; j < H; ++j) rd[j] = rt[j];
+    for (int j = 0; j < SPT; ++j) {
+      const int e0 = sbase + (j * kThreads + tid) * E;
+      float aw = 0.f, ap = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const float pv = exp2_fast(fmaf(EL::get(rt[j], i), d.scale, -d.Ot)) * d.invSt;
+        float wv = pv;
+        if (residual) wv = fmaxf(0.f, pv - exp2_fast(fmaf(EL::get(rd[j], i), d.scale, -d.Od)) * d.invSd);
+        aw += e0 + i == excl ? 0.f : wv;
+        ap += pv;
       }
-#pragma unroll
-      for (int j = 0; j < H; ++j) {
-        const int e0 = sbase + (j * kThreads + tid) * E;
-        float aw = 0.f, ap = 0.f;
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-          const float pv = exp2_fast(fmaf(EL::get(rt[j], i), d.scale, -d.Ot)) * d.invSt;
-          float wv = pv;
-          if (residual) wv = fmaxf(0.f, pv - exp2_fast(fmaf(EL::get(rd[j], i), d.scale, -d.Od)) * d.invSd);
-          aw += e0 + i == excl ? 0.f : wv;
-          ap += pv;
-        }
-        red[(h + j) * kThreads + tid] = aw;
-        red[(NV + h + j) * kThreads + tid] = ap;
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      red[j * kThreads + tid] = aw;
+      red[(SPT + j) * kThreads + tid] = ap;
     }
   }
   __syncthreads();
   // ---- 2. segment totals in fp64 (one 16-lane row sums one segment's 256 lane values)
-  const int units = C * NV;
+  const int units = a.S;  // segment slots per row
   SlotDouble* mw = a.wseg + static_cast<size_t>(b) * units;
   SlotDouble* mp = a.wsegp + static_cast<size_t>(b) * units;
   {
-    const int q = tid >> 4;  // q < NV: draw-weight mass of segment q; NV <= q < 2NV: p mass
+    const int q = tid >> 4;  // q < SPT: draw-weight mass of segment q; SPT <= q < 2 SPT: p mass
     const int r = tid & 15;
     double v = 0.0;
-    if (q < 2 * NV) {
+    if (q < 2 * SPT) {
       const float* src = red + q * kThreads + r * 16;
 #pragma unroll
       for (int i = 0; i < 16; ++i) v += static_cast<double>(src[i]);
     }
     v = row16_inclusive_sum(v);
-    if (q < 2 * NV && r == 15) put_slot((q < NV ? mw : mp) + c * NV + (q % NV), v, a.gen);
+    if (q < 2 * SPT && r == 15) put_slot((q < SPT ? mw : mp) + c * SPT + (q % SPT), v, a.gen);
   }
   if (!all_wait && !last) return;
 
@@ -598,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
     usel = block_max_int(lastu, s_i);
     if (usel < 0) usel = 0;
   }
-  if (all_wait && usel / NV != c) return;  // another task of the sequence holds the segment
+  if (all_wait && usel / SPT != c) return;  // another task of the sequence holds the segment
   if (u0 <= usel && usel < u0 + per) {
     double run = before;
 #pragma unroll
@@ -608,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   }
   __syncthreads();
   const double t_loc = tt - s_base;
-  const int seg_start = (usel / NV) * kChunk + (usel % NV) * kSeg;
+  const int seg_start = usel * kSeg;  // segment u starts at element u * kSeg
 
   // ---- the lane and the element inside that segment
   const int e0 = seg_start + tid * E;
@@ -668,22 +665,36 @@ __global__ void write_zero_offset_kernel(int32_t* offsets) {
 
 // ---------------------------------------------------------------- host side
 
+constexpr int kPoolSegments = 4;  // segments per pool task
+
 struct ChainLayout {
-  int nv, C, R;
+  int nv, C, R, S;
   size_t off_gath, off_part, off_wseg, off_wsegp, bytes;
 };
+
+// Vectors per lane in one stats chunk: the largest of 8, 4, 2, 1 that gives at least 1024
+// workgroups (else 1), raised if needed until a row's partials fit the decision's staging.
+// (Smaller chunks shorten the stats pass's tail but lengthen the time between calls:
+// measured at B=64, K=5, V=128256, 8 is faster per call than 4.)  SPEC_NV in the
+// environment forces 1, 2, 4 or 8.
+static int chain_nv(long long rows, int V, int epv) {
+  int nv = choose_nv(rows, V, epv, 1024);
+  while (nv < 8 && (V + static_cast<long long>(nv) * kThreads * epv - 1) / (static_cast<long long>(nv) * kThreads * epv) * kWaves > kStage)
+    nv *= 2;
+  return nv;
+}
 
 static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
   ChainLayout L{};
   const int epv = dtype == SPEC_BF16 ? 8 : 4;
   L.R = 2 * K + 1;
-  L.nv = choose_nv(static_cast<long long>(B) * L.R, V, epv, 1024);
-  // the partials of one row (4 per chunk) must fit the decision's staging
-  while (L.nv < 8 && (V + static_cast<long long>(L.nv) * kThreads * epv - 1) / (static_cast<long long>(L.nv) * kThreads * epv) * kWaves > kStage)
-    L.nv *= 2;
+  L.nv = chain_nv(static_cast<long long>(B) * L.R, V, epv);
   const long long chunk = static_cast<long long>(L.nv) * kThreads * epv;
   L.C = static_cast<int>((V + chunk - 1) / chunk);
-  const size_t segs = static_cast<size_t>(B) * L.C * L.nv;
+  const long long seg = static_cast<long long>(kThreads) * epv;
+  const long long used = (V + seg - 1) / seg;
+  L.S = static_cast<int>((used + kPoolSegments - 1) / kPoolSegments * kPoolSegments);
+  const size_t segs = static_cast<size_t>(B) * L.S;
   size_t off = 0;
   L.off_gath = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(B) * L.R, 256);
@@ -737,16 +748,17 @@ static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
     if (st != SPEC_OK) return st;
   }
   {
-    const auto kernel = chain_pool_kernel<DT, NV, VEC>;
+    const auto kernel = chain_pool_kernel<DT, kPoolSegments, VEC>;
+    const int CP = a.S / kPoolSegments;
     const int slots = pool_slots(reinterpret_cast<const void*>(kernel), slots_cache);
     // every task waits when the whole launch fits at once; else only last tasks wait,
     // at most half of what fits per launch
-    const int all_wait = static_cast<long long>(a.B) * a.C <= slots && env_int("SPEC_POOL_ALL_WAIT", 1) != 0 ? 1 : 0;
+    const int all_wait = static_cast<long long>(a.B) * CP <= slots && env_int("SPEC_POOL_ALL_WAIT", 1) != 0 ? 1 : 0;
     const int per_launch = all_wait ? a.B : max(1, slots / 2);
     for (int b0 = 0; b0 < a.B; b0 += per_launch) {
       const int bs = min(per_launch, a.B - b0);
       LaunchScope scope("chain_pool", stream);
-      hipExtLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(static_cast<long long>(bs) * a.C)), dim3(kThreads), 0,
+      hipExtLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(static_cast<long long>(bs) * CP)), dim3(kThreads), 0,
                             stream, scope.start(), scope.stop(), 0, a, b0, all_wait);
       const spec_status_t st = scope.finish();
       if (st != SPEC_OK) return st;
@@ -808,9 +820,9 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   const ChainLayout L = chain_layout(B, K, V, dtype);
   const double groups = static_cast<double>(B) * L.R * L.C;
   if (groups > 2147483647.0) return fail(SPEC_ERR_UNSUPPORTED, "grid of %.0f workgroups too large", groups);
-  if (L.C * L.nv > 4 * kThreads || L.C * kWaves > kStage)
-    return fail(SPEC_ERR_UNSUPPORTED, "V = %d is too large (more than %d chunks of %d elements)", V, kStage / kWaves,
-                L.nv * kThreads * (dtype == SPEC_BF16 ? 8 : 4));
+  if (L.S > 4 * kThreads || L.C * kWaves > kStage)
+    return fail(SPEC_ERR_UNSUPPORTED, "V = %d is too large (at most %d segments of %d elements)", V, 4 * kThreads,
+                kThreads * (dtype == SPEC_BF16 ? 8 : 4));
   if (!workspace) return fail(SPEC_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(SPEC_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < L.bytes)
@@ -828,6 +840,7 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   a.K = K;
   a.V = V;
   a.C = L.C;
+  a.S = L.S;
   a.R = draft_logits ? L.R : K + 1;  // the workspace is laid out for 2K+1 rows; fewer fit
   a.out_tokens = out_tokens;
   a.out_num = out_num_accepted;
