@@ -54,8 +54,10 @@ struct RowStat {
 // number in its high half, written by one atomic store.  A reader knows that a slot was
 // written during this call when both high halves equal the generation, so no clearing
 // pass is needed: whatever a slot held before (an earlier call's words, or anything else)
-// reads as "not written yet" unless 64 bits match by chance.  Generations come from a
-// process-wide counter with a random start and are never 0.
+// reads as "not written yet" unless 64 bits match by chance.  The generation mixes a
+// number the host draws for each call (a process-wide counter with a random start) with
+// a counter in the workspace that the stats kernel advances on every run, so that it
+// changes even when a captured graph replays the same launch arguments; it is never 0.
 struct SlotDouble {
   uint64_t lo, hi;
 };
@@ -130,12 +132,20 @@ struct ChainArgs {
   float* out_probs;
   int32_t* out_packed;
   int32_t* out_offsets;
-  uint32_t gen;         // generation of this call's slot words
+  uint32_t gen;         // the host's number for this call (see pool_generation)
+  uint32_t* runs;       // workspace counter advanced by every stats kernel run
   RowStat* part;        // [B, R, C, 4] partials, one per wave of each chunk
   float* gath;          // [B, R] logit of the drafted token in each scoring row
   SlotDouble* wseg;     // [B, S] slots: mass of the final draw's weights per segment
   SlotDouble* wsegp;    // [B, S] slots: mass of p of the same row per segment (fallback)
 };
+
+// Generation of the slot words of this pool launch (see SlotDouble): the host's number
+// mixed with the workspace counter as the stats kernel of this call left it.
+__device__ __forceinline__ uint32_t pool_generation(const ChainArgs& a) {
+  const uint32_t g = a.gen ^ (load_agent(a.runs) * 0x9e3779b1u);
+  return g != 0u ? g : 0x2545f491u;
+}
 
 template <int DT>
 __device__ __forceinline__ const void* target_row(const ChainArgs& a, int b, int k) {
@@ -328,6 +338,7 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
 // partial (the wave's lanes hold every 4th group of 64 vectors of the chunk).
 template <int DT, int NV, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_fetch_add(a.runs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSeg = ChunkShape<DT, NV>::kSegment;
@@ -470,6 +481,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   const int c = static_cast<int>(blockIdx.x) % CP;  // this task's group of SPT segments
   const bool last = c == CP - 1;
   float* red = reinterpret_cast<float*>(s_buf);  // [2][SPT][kThreads] per-lane masses
+  const uint32_t gen = pool_generation(a);
 
   chain_decide<DT>(a, b, clamped_len(a, b), last, &s_dec, s_buf);
   const ChainDecision d = uniform_decision(s_dec);
@@ -524,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
       for (int i = 0; i < 16; ++i) v += static_cast<double>(src[i]);
     }
     v = row16_inclusive_sum(v);
-    if (q < 2 * SPT && r == 15) put_slot((q < SPT ? mw : mp) + c * SPT + (q % SPT), v, a.gen);
+    if (q < 2 * SPT && r == 15) put_slot((q < SPT ? mw : mp) + c * SPT + (q % SPT), v, gen);
   }
   if (!all_wait && !last) return;
 
@@ -543,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
       for (int q = 0; q < 4; ++q) {
         const int u = u0 + q;
         mass[q] = 0.0;
-        if (q < per && u < units && !get_slot(slots + u, a.gen, &mass[q])) missing = 1;
+        if (q < per && u < units && !get_slot(slots + u, gen, &mass[q])) missing = 1;
       }
       if (!__syncthreads_or(missing)) break;
       if (tid == 0) {
@@ -695,7 +707,7 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
   const long long used = (V + seg - 1) / seg;
   L.S = static_cast<int>((used + kPoolSegments - 1) / kPoolSegments * kPoolSegments);
   const size_t segs = static_cast<size_t>(B) * L.S;
-  size_t off = 0;
+  size_t off = 256;  // bytes 0..3: the run counter
   L.off_gath = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(B) * L.R, 256);
   L.off_part = off;
@@ -742,8 +754,7 @@ static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
   {
     const long long g1 = static_cast<long long>(a.B) * a.R * a.C;
     LaunchScope scope("chain_stats", stream);
-    hipExtLaunchKernelGGL((chain_stats_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0,
-                          stream, scope.start(), scope.stop(), 0, a);
+    scope.launch((chain_stats_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), stream, a);
     const spec_status_t st = scope.finish();
     if (st != SPEC_OK) return st;
   }
@@ -758,15 +769,14 @@ static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
     for (int b0 = 0; b0 < a.B; b0 += per_launch) {
       const int bs = min(per_launch, a.B - b0);
       LaunchScope scope("chain_pool", stream);
-      hipExtLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(static_cast<long long>(bs) * CP)), dim3(kThreads), 0,
-                            stream, scope.start(), scope.stop(), 0, a, b0, all_wait);
+      scope.launch(kernel, dim3(static_cast<unsigned>(static_cast<long long>(bs) * CP)), dim3(kThreads), stream, a, b0, all_wait);
       const spec_status_t st = scope.finish();
       if (st != SPEC_OK) return st;
     }
   }
   if (!a.out_packed) return SPEC_OK;
   LaunchScope scope("chain_pack", stream);
-  hipExtLaunchKernelGGL(chain_pack_kernel, dim3(1), dim3(kThreads), 0, stream, scope.start(), scope.stop(), 0, a);
+  scope.launch(chain_pack_kernel, dim3(1), dim3(kThreads), stream, a);
   return scope.finish();
 }
 
@@ -807,7 +817,7 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   if (B == 0) {
     if (out_offsets) {
       LaunchScope scope("chain_empty", s);
-      hipExtLaunchKernelGGL(write_zero_offset_kernel, dim3(1), dim3(64), 0, s, scope.start(), scope.stop(), 0, out_offsets);
+      scope.launch(write_zero_offset_kernel, dim3(1), dim3(64), s, out_offsets);
       return scope.finish();
     }
     return SPEC_OK;
@@ -849,6 +859,7 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   a.out_offsets = out_offsets;
   char* ws = static_cast<char*>(workspace);
   a.gen = next_generation();
+  a.runs = static_cast<uint32_t*>(workspace);
   a.gath = reinterpret_cast<float*>(ws + L.off_gath);
   a.part = reinterpret_cast<RowStat*>(ws + L.off_part);
   a.wseg = reinterpret_cast<SlotDouble*>(ws + L.off_wseg);

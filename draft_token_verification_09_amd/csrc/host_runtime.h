@@ -24,6 +24,16 @@ class LaunchScope {
   ~LaunchScope();
   hipEvent_t start() const { return start_; }
   hipEvent_t stop() const { return stop_; }
+  // Launches `kernel` on `stream`: with the timing events when timing is on, else as a
+  // plain launch (which stream capture records like any other).
+  template <typename F, typename... Args>
+  void launch(F kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+    if (start_ && stop_) {
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start_, stop_, 0, args...);
+    } else {
+      hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+    }
+  }
   // Status of the launch (checks hipGetLastError); call after the kernel launch.
   spec_status_t finish();
 

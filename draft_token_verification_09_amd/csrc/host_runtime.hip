@@ -218,8 +218,7 @@ spec_status_t spec_probe_read(const void* src, size_t bytes, uint32_t* out, spec
     return fail(SPEC_ERR_INVALID_ARG, "probe_read needs a 16-byte aligned source and size");
   const unsigned grid = static_cast<unsigned>(device_cu_count() * 8);
   LaunchScope scope("probe_read", static_cast<hipStream_t>(stream));
-  hipExtLaunchKernelGGL(probe_read_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), scope.start(), scope.stop(), 0,
-                     static_cast<const u32x4*>(src), bytes / 16, out);
+  scope.launch(probe_read_kernel, dim3(grid), dim3(kThreads), static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), bytes / 16, out);
   return scope.finish();
 }
 
@@ -228,8 +227,7 @@ spec_status_t spec_probe_copy(const void* src, void* dst, size_t bytes, spec_str
     return fail(SPEC_ERR_INVALID_ARG, "probe_copy needs 16-byte aligned buffers and size");
   const unsigned grid = static_cast<unsigned>(device_cu_count() * 8);
   LaunchScope scope("probe_copy", static_cast<hipStream_t>(stream));
-  hipExtLaunchKernelGGL(probe_copy_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), scope.start(), scope.stop(), 0,
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  scope.launch(probe_copy_kernel, dim3(grid), dim3(kThreads), static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
   return scope.finish();
 }
 

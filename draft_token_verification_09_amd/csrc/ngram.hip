@@ -83,8 +83,7 @@ spec_status_t ngram_propose(const int32_t* context, const int32_t* context_len,
   if (!context || !context_len || !out_draft_tokens || !out_draft_len)
     return fail(SPEC_ERR_INVALID_ARG, "a required pointer is NULL");
   LaunchScope scope("ngram_propose", s);
-  hipExtLaunchKernelGGL(ngram_propose_kernel, dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, s, scope.start(), scope.stop(), 0, context, context_len,
-                     L_max, n_min, n_max, K, out_draft_tokens, out_draft_len, out_match_n);
+  scope.launch(ngram_propose_kernel, dim3(static_cast<unsigned>(B)), dim3(kThreads), s, context, context_len, L_max, n_min, n_max, K, out_draft_tokens, out_draft_len, out_match_n);
   return scope.finish();
 }
 

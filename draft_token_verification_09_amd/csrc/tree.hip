@@ -249,12 +249,12 @@ static spec_status_t launch_tree(const TreeArgs& a, hipStream_t s) {
   {
     const long long g = static_cast<long long>(a.B) * a.N1 * a.C;
     LaunchScope scope("tree_argmax", s);
-    hipExtLaunchKernelGGL((tree_argmax_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s, scope.start(), scope.stop(), 0, a);
+    scope.launch((tree_argmax_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g)), dim3(kThreads), s, a);
     const spec_status_t st = scope.finish();
     if (st != SPEC_OK) return st;
   }
   LaunchScope scope("tree_select", s);
-  hipExtLaunchKernelGGL(tree_select_kernel, dim3(static_cast<unsigned>(a.B)), dim3(kThreads), 0, s, scope.start(), scope.stop(), 0, a);
+  scope.launch(tree_select_kernel, dim3(static_cast<unsigned>(a.B)), dim3(kThreads), s, a);
   return scope.finish();
 }
 

@@ -139,3 +139,44 @@ def test_pool_wait_modes_agree(recipe, monkeypatch):
     assert torch.equal(a.probs, b.probs)
     rep = compare_chain(b, chain_oracle(inp), inp)
     assert rep.ok(), rep.failures[:5]
+
+
+def test_graph_replays_match_eager_calls():
+    # a captured call replays correctly with new inputs each time: the hand-over slots'
+    # generation changes on every run even though the captured launch arguments do not
+    import draft_token_verification_09_amd as sv
+
+    inps = [synth.chain_config_high_accept_bf16(20 + s, B=12, V=40000) for s in range(3)]
+    dev_args = [_device_args(inp) for inp in inps]
+    static = [x.clone() for x in dev_args[0][:1]] + [dev_args[0][1].clone()] + [x.clone() for x in dev_args[0][2:6]]
+    B, K1, V = static[0].shape
+    out = sv.ChainResult(tokens=torch.empty((B, K1), dtype=torch.int32, device="cuda:0"),
+                         num_accepted=torch.empty((B,), dtype=torch.int32, device="cuda:0"),
+                         probs=torch.empty((B, K1 - 1, 3), dtype=torch.float32, device="cuda:0"),
+                         packed=None, offsets=None)
+    ws = torch.empty(sv.spec_verify_chain_workspace_size(B, K1 - 1, V, 1) + 256, dtype=torch.uint8, device="cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sv.spec_verify_chain(*static, out=out, workspace_buf=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.spec_verify_chain(*static, out=out, workspace_buf=ws)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        k = (rep + 1) % 3
+        for dst, src in zip(static, dev_args[k][:6]):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = sv.spec_verify_chain(*dev_args[k][:6])
+        torch.cuda.synchronize()
+        log(f"[chain] graph replay {rep}: input set {k}")
+        assert torch.equal(out.tokens, eager.tokens)
+        assert torch.equal(out.num_accepted, eager.num_accepted)
+        assert torch.equal(out.probs, eager.probs)
+        rep_ = compare_chain(out, chain_oracle(inps[k]), inps[k])
+        assert rep_.ok(), rep_.failures[:5]
