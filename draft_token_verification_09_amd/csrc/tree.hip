@@ -53,6 +53,14 @@ __device__ __forceinline__ void argmax_step(float& v, int& i) {
   }
 }
 
+// (max, first index) over each 16-lane row of the wave; lane 15 of a row holds the result.
+__device__ __forceinline__ void row16_argmax(float& v, int& i) {
+  argmax_step<dppc::kRowShr1>(v, i);
+  argmax_step<dppc::kRowShr2>(v, i);
+  argmax_step<dppc::kRowShr4>(v, i);
+  argmax_step<dppc::kRowShr8>(v, i);
+}
+
 // Wave-wide (max, first index) with DPP steps (see device_common.h); every lane gets it.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   argmax_step<dppc::kRowShr1>(v, i);
@@ -79,8 +87,6 @@ __global__ __launch_bounds__(kThreads) void tree_select_kernel(TreeArgs a) {
   __shared__ int s_key[kWaves];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
   const int N1 = a.N1;
   const int C = a.C;
   const int32_t* par = a.parent + static_cast<size_t>(b) * N1;
@@ -91,7 +97,8 @@ __global__ __launch_bounds__(kThreads) void tree_select_kernel(TreeArgs a) {
   }
   if (tid == 0) s_bad = 0;
 
-  // Row argmax per node from the chunk partials (one wave per row).
+  // Row argmax per node from the chunk partials: each 16-lane row of the workgroup
+  // combines one node row (16 at a time), lane r taking partials r, r+16, ...
   const int rows_per_batch = max(1, kStageT / C);
   for (int r0 = 0; r0 < N1; r0 += rows_per_batch) {
     const int r1 = min(N1, r0 + rows_per_batch);
@@ -103,18 +110,22 @@ __global__ __launch_bounds__(kThreads) void tree_select_kernel(TreeArgs a) {
       st_i[i] = p.i;
     }
     __syncthreads();
-    for (int r = r0 + w; r < r1; r += kWaves) {
-      const int base = (r - r0) * C;
+    for (int g0 = r0; g0 < r1; g0 += kThreads / 16) {
+      const int r = g0 + (tid >> 4);
+      const int q = tid & 15;
       float v = -INFINITY;
       int i = INT_MAX;
-      for (int c = lane; c < C; c += 64) {
-        if (better(st_v[base + c], st_i[base + c], v, i)) {
-          v = st_v[base + c];
-          i = st_i[base + c];
+      if (r < r1) {
+        const int base = (r - r0) * C;
+        for (int c = q; c < C; c += 16) {
+          if (better(st_v[base + c], st_i[base + c], v, i)) {
+            v = st_v[base + c];
+            i = st_i[base + c];
+          }
         }
       }
-      wave_argmax(v, i);
-      if (lane == 0) s_amax[r] = i;
+      row16_argmax(v, i);
+      if (r < r1 && q == 15) s_amax[r] = i;
     }
     __syncthreads();
   }
