@@ -41,12 +41,22 @@
 
 namespace specv {
 
-enum ChainMode : int { kModeInvalid = 0, kModeResidual = 1, kModeBonus = 2, kModeOneHot = 3, kModeFallbackP = 4 };
+enum ChainMode : int {
+  kModeInvalid = 0,
+  kModeResidual = 1,
+  kModeBonus = 2,
+  kModeOneHot = 3,
+  kModeFallbackP = 4,
+  kModeGreedy = 5,  // temperature 0: the emitted row is complete after the decision
+};
 
+// Partial of one wave's share of a chunk.  Sampled rows: o = max(l) * scale (-inf if every
+// logit is -inf) and s = sum exp2(l * scale - o).  Greedy rows (temperature 0): o = the
+// largest logit and s = its smallest vocabulary index.
 struct RowStat {
-  float o;  // log2-domain offset: max(l) * scale over the chunk (-inf if every logit is -inf)
+  float o;
   float pad;
-  double s;  // sum over the chunk of exp2(l * scale - o)
+  double s;
 };
 
 // Segment masses pass between the tasks of one pool launch through slots of two 64-bit
@@ -166,10 +176,14 @@ __device__ __forceinline__ int clamped_len(const ChainArgs& a, int b) {
   return v < 0 ? 0 : (v > a.K ? a.K : v);
 }
 
+// Temperature 0 selects greedy verification for a sequence.
+__device__ __forceinline__ bool is_greedy(const ChainArgs& a, int b) { return a.temperature[b] == 0.f; }
+
 // Row rr of the stats grid: rr <= K is target row rr, otherwise draft row rr-K-1
-// (draft rows exist only when draft logits are given; then R = 2K+1, else R = K+1).
-__device__ __forceinline__ bool row_needed(const ChainArgs& a, int rr, int kb) {
-  return rr <= a.K ? (rr <= kb) : (a.draft != nullptr && rr - (a.K + 1) < kb);
+// (draft rows exist only when draft logits are given; then R = 2K+1, else R = K+1; a
+// greedy sequence reads no draft row).
+__device__ __forceinline__ bool row_needed(const ChainArgs& a, int rr, int kb, bool greedy) {
+  return rr <= a.K ? (rr <= kb) : (!greedy && a.draft != nullptr && rr - (a.K + 1) < kb);
 }
 
 // Drafted position whose token row rr scores (target row k or draft row k, k < kb), else -1.
@@ -216,10 +230,13 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   const float T = a.temperature[b];
   const float uf = a.u_final[b];
   const int kb_raw = a.draft_len ? a.draft_len[b] : a.K;
+  const bool greedy = T == 0.f;
 
-  // Per-row (O, S) from the partials: each 16-lane row of the workgroup combines one row
-  // of logits (16 at a time), lane r taking partials r, r+16, ...
+  // Per-row (O, S) from the partials -- for a greedy sequence the row argmax instead:
+  // each 16-lane row of the workgroup combines one row of logits (16 at a time), lane r
+  // taking partials r, r+16, ...
   __shared__ float s_om[kThreads / 16];
+  __shared__ int sA[2 * SPEC_MAX_K + 1];  // greedy: argmax of each target row
   const int grp = tid >> 4;  // 16-lane group
   const int r = tid & 15;
   const int rows_per_batch = max(1, kStage / C);
@@ -233,9 +250,27 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
       st_s[i] = st.s;
     }
     __syncthreads();
-    for (int g0 = r0; g0 < r1; g0 += kThreads / 16) {
+    for (int g0 = r0; g0 < r1 && greedy; g0 += kThreads / 16) {
       const int rr = g0 + grp;
-      const bool live = rr < r1 && row_needed(a, rr, kb);
+      const bool live = rr < r1 && row_needed(a, rr, kb, true);
+      const int base = (rr - r0) * C;
+      float v = -INFINITY;
+      int idx = INT_MAX;
+      if (live)
+        for (int c = r; c < C; c += 16) {
+          const int ci = static_cast<int>(st_s[base + c]);
+          if (better(st_o[base + c], ci, v, idx)) {
+            v = st_o[base + c];
+            idx = ci;
+          }
+        }
+      row16_argmax(v, idx);
+      if (live && r == 15) sA[rr] = idx;
+    }
+    __syncthreads();
+    for (int g0 = r0; g0 < r1 && !greedy; g0 += kThreads / 16) {
+      const int rr = g0 + grp;
+      const bool live = rr < r1 && row_needed(a, rr, kb, false);
       const int base = (rr - r0) * C;
       float om = -INFINITY;
       if (live)
@@ -259,7 +294,36 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
     }
   }
 
-  if (w == 0) {
+  if (w == 0 && greedy) {
+    // One lane per drafted position: accepted iff the draft is its target row's argmax;
+    // the emitted row ends with the argmax of the row after the last accepted draft.
+    bool bad = false, accepted = true;
+    if (active) {
+      bad = x < 0 || x >= a.V;
+      accepted = x == sA[k];
+    }
+    const unsigned long long rej = __ballot(active && !accepted);
+    const unsigned long long badm = __ballot(active && bad);
+    const int n = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : kb;
+    const bool invalid = badm != 0ull || kb_raw < 0 || kb_raw > a.K;
+    if (write_outputs) {
+      if (a.out_probs && k < a.K) {  // p, q and alpha are not defined at temperature 0
+        float* pr = a.out_probs + (static_cast<size_t>(b) * a.K + k) * 3;
+        pr[0] = pr[1] = pr[2] = 0.f;
+      }
+      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+      for (int kk = lane; kk <= a.K; kk += 64) ot[kk] = invalid ? -1 : (kk < n ? x : (kk == n ? sA[n] : -1));
+      if (lane == 0) a.out_num[b] = invalid ? -1 : n;
+    }
+    if (lane == 0) {
+      ChainDecision d{};
+      d.mode = invalid ? kModeInvalid : kModeGreedy;
+      d.n = n;
+      d.kb = kb;
+      *out = d;
+    }
+  }
+  if (w == 0 && !greedy) {
     // One lane per drafted position: p(x_k), q(x_k), alpha_k and the accept test.
     const float scale = kLog2e / T;
     bool bad = false, accepted = true;
@@ -348,14 +412,35 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   const int rr = (g / a.C) % a.R;
   const int b = g / (a.C * a.R);
   const int kb = clamped_len(a, b);
-  if (!row_needed(a, rr, kb)) return;
+  const bool greedy = is_greedy(a, b);
+  if (!row_needed(a, rr, kb, greedy)) return;
   const void* row = rr <= a.K ? target_row<DT>(a, b, rr) : draft_row<DT>(a, b, rr - (a.K + 1));
-  const float scale = kLog2e / a.temperature[b];
-  const int pos = row_position(a, rr, kb);
-  const int x = pos >= 0 ? a.tokens[static_cast<size_t>(b) * a.K + pos] : -1;
+  RowStat* out = a.part + ((static_cast<size_t>(b) * a.R + rr) * a.C + c) * kWaves + (threadIdx.x >> 6);
 
   u32x4 raw[NV];
   load_chunk<DT, NV, VEC, true>(raw, row, a.V, c);
+
+  if (greedy) {  // (largest logit, smallest index) of the wave's share
+    float v = -INFINITY;
+    int idx = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int e = c * kChunk + (j * kThreads + static_cast<int>(threadIdx.x)) * E + i;
+        const float l = EL::get(raw[j], i);
+        if (e < a.V && better(l, e, v, idx)) {
+          v = l;
+          idx = e;
+        }
+      }
+    wave_argmax(v, idx);
+    if ((threadIdx.x & 63) == 0) *out = RowStat{v, 0.f, static_cast<double>(idx)};
+    return;
+  }
+  const float scale = kLog2e / a.temperature[b];
+  const int pos = row_position(a, rr, kb);
+  const int x = pos >= 0 ? a.tokens[static_cast<size_t>(b) * a.K + pos] : -1;
 
   // The lane holding the drafted token's logit copies it out (bit-exact).
   if (x >= 0 && x < a.V && x / kChunk == c) {
@@ -395,8 +480,7 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   const float ow = wave_max(o);
   const double contrib = (o == -INFINITY) ? 0.0 : static_cast<double>(s) * static_cast<double>(exp2_fast(o - ow));
   const double sw = wave_sum(contrib);
-  if ((threadIdx.x & 63) == 0)
-    a.part[((static_cast<size_t>(b) * a.R + rr) * a.C + c) * kWaves + (threadIdx.x >> 6)] = RowStat{ow, 0.f, sw};
+  if ((threadIdx.x & 63) == 0) *out = RowStat{ow, 0.f, sw};
 }
 
 // ---------------------------------------------------------------- final draw
@@ -485,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
 
   chain_decide<DT>(a, b, clamped_len(a, b), last, &s_dec, s_buf);
   const ChainDecision d = uniform_decision(s_dec);
-  if (d.mode == kModeInvalid) return;  // the decision already wrote the -1 row
+  if (d.mode == kModeInvalid || d.mode == kModeGreedy) return;  // the decision wrote the row
   int mode = d.mode;
   const void* row_t = target_row<DT>(a, b, d.row);
   const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : row_t;

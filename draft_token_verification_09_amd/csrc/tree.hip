@@ -40,39 +40,6 @@ struct TreeArgs {
   ArgMax* part;  // [B, N1, C]
 };
 
-// (v, i) beats (w, j) if v > w, or v == w and i < j.
-__device__ __forceinline__ bool better(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
-
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  const float ov = dpp_float<CTRL, ROW_MASK>(-INFINITY, v);
-  const int oi = dpp_int<CTRL, ROW_MASK>(INT_MAX, i);
-  if (better(ov, oi, v, i)) {
-    v = ov;
-    i = oi;
-  }
-}
-
-// (max, first index) over each 16-lane row of the wave; lane 15 of a row holds the result.
-__device__ __forceinline__ void row16_argmax(float& v, int& i) {
-  argmax_step<dppc::kRowShr1>(v, i);
-  argmax_step<dppc::kRowShr2>(v, i);
-  argmax_step<dppc::kRowShr4>(v, i);
-  argmax_step<dppc::kRowShr8>(v, i);
-}
-
-// Wave-wide (max, first index) with DPP steps (see device_common.h); every lane gets it.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_step<dppc::kRowShr1>(v, i);
-  argmax_step<dppc::kRowShr2>(v, i);
-  argmax_step<dppc::kRowShr4>(v, i);
-  argmax_step<dppc::kRowShr8>(v, i);
-  argmax_step<dppc::kRowBcast15, 0xa>(v, i);
-  argmax_step<dppc::kRowBcast31, 0xc>(v, i);
-  v = lane_broadcast(v, 63);
-  i = lane_broadcast(i, 63);
-}
-
 constexpr int kStageT = 2048;  // chunk partials staged in shared memory per batch of rows
 
 // grid = B.  Topology and partials are staged in shared memory first, so the path walks

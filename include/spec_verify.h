@@ -98,10 +98,19 @@ const char* spec_last_error(void);
  * draft_tokens  [B, K] int32 in [0, V) for k < k_b (entries k >= k_b are ignored).
  * draft_len     [B] int32 k_b in [0, K], or NULL meaning k_b = K for every b.
  *               Rows beyond k_b are never read.
- * temperature   [B] float32, > 0 and finite.
- * u_accept      [B, K] float32 in (0, 1]: r_k of the accept test of draft k.
+ * temperature   [B] float32, finite and >= 0.  T_b = 0 selects greedy
+ *               verification for sequence b (the invariance theorem of
+ *               section I.1 covers greedy decoding; "Speculative decoding:
+ *               Medusa, EAGLE, vLLM" runs its example at temperature 0): draft
+ *               k is accepted iff it is the argmax of target row k (raw logits,
+ *               smallest index on ties), the emitted row ends with the argmax
+ *               of target row n, no draft row and no uniform is read, and
+ *               out_probs[b] is 0.  Greedy and sampled sequences may share a
+ *               batch.
+ * u_accept      [B, K] float32 in (0, 1]: r_k of the accept test of draft k
+ *               (ignored when T_b = 0).
  * u_final       [B] float32 in (0, 1]: the one uniform of the replacement or
- *               bonus draw.
+ *               bonus draw (ignored when T_b = 0).
  * out_tokens    [B, K+1] int32: x_0..x_{n-1}, then the drawn token, then -1.
  * out_num_accepted [B] int32: n, the number of accepted drafts (0..k_b).
  * out_probs     [B, K, 3] float32 (p_k(x_k), q_k(x_k), alpha_k) for k < k_b,
@@ -114,7 +123,7 @@ const char* spec_last_error(void);
  *               bytes, 256-byte aligned.
  *
  * Invalid device data for sequence b (token out of range, k_b outside [0, K],
- * T not > 0 or not finite, a uniform outside (0, 1]) sets out_num_accepted[b]
+ * T negative or not finite, a uniform outside (0, 1] when T > 0) sets out_num_accepted[b]
  * = -1, out_tokens[b, :] = -1, out_probs[b] = 0 and gives it no packed tokens.
  * Limits: 1 <= K <= SPEC_MAX_K, V >= 1, B >= 0, B*(K+1)*V < 2^47.
  * Logits may be -inf (probability 0); +inf and NaN are not supported; each

@@ -23,7 +23,8 @@ Pages cited (by title; section, step or figure given at each use):
 Where the pages are silent the oracle takes one stated reading (temperature
 divides the logits; a bonus token is drawn from the target row after the last
 draft when every draft is accepted; inverse-CDF sampling in vocabulary order with
-the smallest index whose inclusive prefix reaches u*W; greedy tree acceptance by
+the smallest index whose inclusive prefix reaches u*W; temperature 0 as greedy chain
+verification; greedy tree acceptance by
 argmax with smallest-index ties; n-gram lookup by the longest suffix and its
 earliest occurrence).  Each function names the reading it takes.
 
@@ -41,6 +42,7 @@ from .chain import (  # noqa: F401
     residual_weights,
     softmax_at_temperature,
     verify_chain,
+    verify_chain_greedy_sequence,
     verify_chain_sequence,
 )
 from .tree import TreeBatchResult, argmax_first, verify_tree_greedy, verify_tree_greedy_sequence  # noqa: F401

@@ -20,6 +20,12 @@ Readings taken where that page is silent (each also named at its use):
     order, t = u * C[V-1]; the result is the smallest i with C[i] >= t.
   * q(x) = 0 gives alpha = 1 if p(x) > 0 else 0; an all-zero residual falls back
     to sampling p itself (both unreachable in exact arithmetic when x ~ q).
+  * Temperature 0 means greedy verification (the invariance theorem of section I.1
+    covers greedy decoding; the "Speculative decoding: Medusa, EAGLE, vLLM" usage
+    example runs at temperature 0): draft k is accepted iff it equals the argmax of
+    target row k (raw logits, smallest index on ties), and the token emitted after
+    the last accepted draft is the argmax of the next target row.  No uniform and
+    no draft logit is used.
 
 Everything is float64; each sequence is verified by a plain sequential loop.
 """
@@ -32,6 +38,7 @@ from typing import List, Optional
 import numpy as np
 
 from .common import widen_logits
+from .tree import argmax_first
 
 
 def softmax_at_temperature(logits: np.ndarray, temperature: float) -> np.ndarray:
@@ -180,6 +187,30 @@ def verify_chain_sequence(
     )
 
 
+def verify_chain_greedy_sequence(target_rows: np.ndarray, tokens: np.ndarray, draft_len: int) -> ChainSequenceResult:
+    """Greedy (temperature 0) verification of one sequence's chain: accept draft k while it
+    equals argmax_first(target row k); emit the argmax of the row after the last accepted
+    draft.  p_x, q_x and alpha are not defined at temperature 0 and are reported as 0."""
+    K1, V = target_rows.shape
+    K = K1 - 1
+    kb = int(draft_len)
+    if not 0 <= kb <= K:
+        raise ValueError("draft_len out of range")
+    for k in range(kb):
+        if not 0 <= int(tokens[k]) < V:
+            raise ValueError("draft token out of range")
+    n = kb
+    for k in range(kb):
+        if int(tokens[k]) != argmax_first(target_rows[k]):
+            n = k
+            break
+    out = [int(tokens[k]) for k in range(n)] + [argmax_first(target_rows[n])]
+    return ChainSequenceResult(
+        num_accepted=n, tokens=out, p_x=[0.0] * kb, q_x=[0.0] * kb, alpha=[0.0] * kb, accept_margins=[],
+        cdf_gap=float("inf"), mode="greedy", final_mass=0.0,
+    )
+
+
 @dataclass
 class ChainBatchResult:
     tokens: np.ndarray        # [B, K+1] int32, -1 padded
@@ -190,7 +221,8 @@ class ChainBatchResult:
 
 def verify_chain(target, draft, dtype: str, tokens, temperature, u_accept, u_final,
                  draft_len=None, seqs=None) -> ChainBatchResult:
-    """Batched chain verification: a loop over sequences of verify_chain_sequence.
+    """Batched chain verification: a loop over sequences of verify_chain_sequence, or of
+    verify_chain_greedy_sequence for a sequence whose temperature is 0.
 
     target: [B, K+1, V] and draft: [B, K, V] (or None) as float32 or bf16 uint16 bits;
     tokens [B, K] int; temperature [B]; u_accept [B, K]; u_final [B]; draft_len [B] or None.
@@ -205,9 +237,12 @@ def verify_chain(target, draft, dtype: str, tokens, temperature, u_accept, u_fin
     for b in (range(B) if seqs is None else seqs):
         kb = K if draft_len is None else int(draft_len[b])
         t_rows = widen_logits(target[b], dtype)
-        d_rows = None if draft is None else widen_logits(np.asarray(draft)[b], dtype)
-        r = verify_chain_sequence(t_rows, d_rows, np.asarray(tokens)[b], kb, float(temperature[b]),
-                                  np.asarray(u_accept)[b], float(u_final[b]))
+        if float(temperature[b]) == 0.0:
+            r = verify_chain_greedy_sequence(t_rows, np.asarray(tokens)[b], kb)
+        else:
+            d_rows = None if draft is None else widen_logits(np.asarray(draft)[b], dtype)
+            r = verify_chain_sequence(t_rows, d_rows, np.asarray(tokens)[b], kb, float(temperature[b]),
+                                      np.asarray(u_accept)[b], float(u_final[b]))
         results[b] = r
         out_tok[b, : len(r.tokens)] = r.tokens
         out_n[b] = r.num_accepted

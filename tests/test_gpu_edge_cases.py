@@ -160,7 +160,7 @@ def test_invalid_device_inputs_are_flagged_per_sequence():
     inp.draft_len = np.full(8, 4, np.int32)
     inp.tokens[1, 2] = 5000            # token out of range
     inp.tokens[2, 0] = -1
-    inp.temperature[3] = 0.0           # T must be > 0
+    inp.temperature[3] = -1.0          # T must be >= 0 (0 is greedy)
     inp.temperature[4] = np.nan
     inp.u_accept[5, 1] = 0.0           # u outside (0, 1]
     inp.u_final[6] = 1.5
