@@ -47,3 +47,4 @@ from .chain import (  # noqa: F401
 )
 from .tree import TreeBatchResult, argmax_first, verify_tree_greedy, verify_tree_greedy_sequence  # noqa: F401
 from .ngram import NgramResult, ngram_propose, ngram_propose_sequence  # noqa: F401
+from .tree_io import commit_path, tree_attention_mask  # noqa: F401
