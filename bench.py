@@ -230,6 +230,15 @@ def other_workloads(warmup, steps, dev):
     r = bench_chain_workload(lambda s: synth.chain_config_low_accept_bf16(s), "chain_B256_K8_V152064_bf16",
                              warmup, steps, dev)
     out.append(_entry("chain_verify_B256_K8_V152064_bf16_low_accept", r, r["positions"]))
+    # greedy chain (temperature 0): B=64 K=5 V=128256 bf16, target rows only
+    def greedy(s):
+        inp = synth.chain_config_high_accept_bf16(s)
+        inp.draft = None  # a greedy sequence reads no draft row
+        inp.temperature = np.zeros_like(inp.temperature)
+        return inp
+
+    r = bench_chain_workload(greedy, "chain_greedy_B64_K5_V128256_bf16", warmup, steps, dev)
+    out.append(_entry("chain_greedy_B64_K5_V128256_bf16", r, r["positions"]))
     # small fp32 chain: latency
     r = bench_chain_workload(lambda s: synth.chain_config_small_f32(s), "chain_B1_K5_V32000_f32", warmup, steps, dev)
     out.append(_entry("chain_verify_B1_K5_V32000_f32", r, r["positions"]))
@@ -252,10 +261,16 @@ def other_workloads(warmup, steps, dev):
 
     ms, _ = time_calls(tcall, n_sets, warmup, steps, False)
     _, kms = time_calls(tcall, n_sets, 2, steps, True)
-    del sets
+    torch.cuda.synchronize()
+    tree_parents = [p for _, p, _ in sets]
+    tree_paths = [(c.result.path_nodes.clone(), c.result.accept_len.clone()) for c in prepared]
+    del sets, prepared
     tb = per + tr0.B * (7 * 3 + 1 + tr0.N1) * 4
     out.append(_entry("tree_greedy_B32_N60_V128256_bf16", dict(ms=ms, bytes=tb, kernels=kms, steps=steps),
                       tr0.B * (tr0.N1 - 1)))
+
+    # the steps on either side of tree verification, on the same workload's trees
+    out += tree_io_workloads(warmup, steps, dev, tree_parents, tree_paths)
 
     # n-gram propose + one-hot verify, B=128 L=4096 K=5 V=32000 bf16
     progress("ngram: generating inputs")
@@ -291,6 +306,59 @@ def other_workloads(warmup, steps, dev):
     del sets
     out.append(_entry("ngram_propose_verify_B128_L4096_K5_V32000_bf16", dict(ms=ms, bytes=nb, kernels=kms, steps=steps),
                       128 * 5))
+    return out
+
+
+def tree_io_workloads(warmup, steps, dev, parents, paths):
+    """Tree-attention mask of the B=32 (60 nodes + root) trees, and the commit of each
+    verified path's cache entries (`paths`: (path_nodes, accept_len) from verification):
+    a 70B-class entry per token, 160 planes (80 layers x K, V) of 8 heads x 128 x bf16 =
+    2 KiB, i.e. 320 KiB per token."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_09_amd as sv
+
+    out = []
+    B, N1 = parents[0].shape
+    pm = [sv.prepare_spec_tree_mask(p) for p in parents]
+
+    def mcall(i):
+        pm[i]()
+
+    ms, _ = time_calls(mcall, len(pm), warmup, steps, False)
+    _, kms = time_calls(mcall, len(pm), 2, steps, True)
+    mb = B * N1 * 4 * 2 + B * N1 * N1
+    out.append(_entry(f"tree_mask_B{B}_N{N1 - 1}", dict(ms=ms, bytes=mb, kernels=kms, steps=steps), B * (N1 - 1)))
+
+    planes, W, L_cap = 160, 1024, 16
+    entry = planes * W * 2
+    per_set = int(np.mean([int((a + 1).sum().item()) for _, a in paths])) * entry * 2
+    n_sets = sets_needed(per_set)
+    progress(f"commit: {n_sets} node buffers of {planes * B * N1 * W * 2 / 1e6:.0f} MB")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    prepared, moved = [], []
+    clen = (torch.arange(B, dtype=torch.int32, device=dev) * 3) % (L_cap - 7)
+    for s in range(n_sets):
+        kv = torch.randint(-32768, 32767, (planes, B, N1, W), dtype=torch.int16, device=dev, generator=gen)
+        cache = torch.zeros((planes, B, L_cap, W), dtype=torch.int16, device=dev)
+        path, acc = paths[s % len(paths)]
+        prepared.append(sv.prepare_spec_commit_path(kv, path, acc, clen, cache))
+        moved.append(int((acc + 1).sum().item()) * entry * 2 + B * (path.shape[1] + 3) * 4)
+
+    def ccall(i):
+        prepared[i]()
+
+    ms, _ = time_calls(ccall, n_sets, warmup, steps, False)
+    _, kms = time_calls(ccall, n_sets, 2, steps, True)
+    committed = int(np.mean([int((a + 1).sum().item()) for _, a in paths]))
+    r = _entry(f"tree_commit_B{B}_N{N1 - 1}_planes{planes}_entry{entry}",
+               dict(ms=ms, bytes=int(np.mean(moved)), kernels=kms, steps=steps), committed)
+    r["entries_per_call"] = committed
+    out.append(r)
+    del prepared
+    torch.cuda.empty_cache()
     return out
 
 

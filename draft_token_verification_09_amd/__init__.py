@@ -10,18 +10,23 @@ from .binding import (  # noqa: F401
     NgramResult,
     PreparedCall,
     SpecError,
+    TreeMaskResult,
     TreeResult,
     lib,
     loaded_library_path,
     ngram_propose,
     prepare_ngram_propose,
+    prepare_spec_commit_path,
     prepare_spec_verify_chain,
+    prepare_spec_tree_mask,
     prepare_spec_verify_tree_greedy,
+    spec_commit_path,
     spec_probe_copy,
     spec_probe_read,
     spec_timing_collect,
     spec_timing_enable,
     spec_timing_reset,
+    spec_tree_mask,
     spec_verify_chain,
     spec_verify_chain_workspace_size,
     spec_verify_tree_greedy,

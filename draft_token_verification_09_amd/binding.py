@@ -52,6 +52,9 @@ _SIGNATURES = {
     "spec_verify_tree_greedy": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                        _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ngram_propose": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "spec_tree_mask": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
+    "spec_commit_path": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _sz, _sz, _sz,
+                                _vp, _vp, _vp]),
     "spec_timing_enable": (_i32, [_i32]),
     "spec_timing_reset": (_i32, []),
     "spec_timing_collect": (_i32, []),
@@ -350,6 +353,109 @@ def prepare_ngram_propose(context: torch.Tensor, context_len: torch.Tensor, n_mi
     """ngram_propose with every argument fixed (see PreparedCall)."""
     args, out, keep = _ngram_call(context, context_len, n_min, n_max, K, want_match_n, out, stream)
     return PreparedCall("ngram_propose", lib().ngram_propose, _SIGNATURES["ngram_propose"][1], args, out, keep)
+
+
+@dataclass
+class TreeMaskResult:
+    mask: Optional[torch.Tensor]   # [B, N1, N1] uint8
+    depth: Optional[torch.Tensor]  # [B, N1] int32
+
+
+def _tree_mask_call(parent, want_mask, want_depth, out, stream):
+    if parent.dim() != 2:
+        raise ValueError("parent must be [B, N1]")
+    B, N1 = parent.shape
+    dev = parent.device
+    _need(parent, "parent", torch.int32, (B, N1), dev)
+    if out is None:
+        out = TreeMaskResult(
+            mask=torch.empty((B, N1, N1), dtype=torch.uint8, device=dev) if want_mask else None,
+            depth=torch.empty((B, N1), dtype=torch.int32, device=dev) if want_depth else None,
+        )
+    if out.mask is not None:
+        _need(out.mask, "mask", torch.uint8, (B, N1, N1), dev)
+    if out.depth is not None:
+        _need(out.depth, "depth", torch.int32, (B, N1), dev)
+    s = _stream(stream, dev)
+    args = (_ptr(parent), B, N1, _ptr(out.mask), _ptr(out.depth), s)
+    return args, out, (parent,)
+
+
+def spec_tree_mask(parent: torch.Tensor, *, want_mask: bool = True, want_depth: bool = True,
+                   out: Optional[TreeMaskResult] = None, stream=None) -> TreeMaskResult:
+    """Tree-attention mask and node depths (spec_tree_mask).  parent [B, N1] int32."""
+    args, out, _ = _tree_mask_call(parent, want_mask, want_depth, out, stream)
+    _check("spec_tree_mask", lib().spec_tree_mask(*args))
+    return out
+
+
+def prepare_spec_tree_mask(parent: torch.Tensor, *, want_mask: bool = True, want_depth: bool = True,
+                           out: Optional[TreeMaskResult] = None, stream=None) -> PreparedCall:
+    """spec_tree_mask with every argument fixed (see PreparedCall)."""
+    args, out, keep = _tree_mask_call(parent, want_mask, want_depth, out, stream)
+    return PreparedCall("spec_tree_mask", lib().spec_tree_mask, _SIGNATURES["spec_tree_mask"][1], args, out, keep)
+
+
+def _plane_view(t: torch.Tensor, name: str, B: int, rows: int):
+    """(planes, entry_bytes, plane_stride_bytes) of a [planes, B, rows, W] tensor whose
+    last three dimensions are dense (the plane dimension may be strided)."""
+    if t.dim() != 4 or t.shape[1] != B or t.shape[2] != rows:
+        raise ValueError(f"{name} must be [planes, {B}, {rows}, W], got {tuple(t.shape)}")
+    P_, _, _, W = t.shape
+    es = t.element_size()
+    if t.stride(3) != 1 or t.stride(2) != W or t.stride(1) != rows * W:
+        raise ValueError(f"{name} must be dense in its last three dimensions")
+    return P_, W * es, t.stride(0) * es
+
+
+def _commit_call(kv_nodes, path_nodes, accept_len, cache_len, kv_cache, out_cache_len, stream):
+    if kv_nodes.dim() != 4:
+        raise ValueError("kv_nodes must be [planes, B, N1, W]")
+    planes, B, N1, W = kv_nodes.shape
+    dev = kv_nodes.device
+    if kv_cache.device != dev or kv_cache.dtype != kv_nodes.dtype:
+        raise ValueError("kv_cache must match kv_nodes in device and dtype")
+    L_cap = kv_cache.shape[2] if kv_cache.dim() == 4 else -1
+    p1, eb, sstride = _plane_view(kv_nodes, "kv_nodes", B, N1)
+    p2, eb2, dstride = _plane_view(kv_cache, "kv_cache", B, L_cap)
+    if p1 != p2 or eb != eb2:
+        raise ValueError("kv_nodes and kv_cache must have the same planes and entry width")
+    _need(accept_len, "accept_len", torch.int32, (B,), dev)
+    _need(cache_len, "cache_len", torch.int32, (B,), dev)
+    P = 0
+    if path_nodes is not None:
+        if path_nodes.dim() != 2 or path_nodes.shape[0] != B:
+            raise ValueError("path_nodes must be [B, P]")
+        P = path_nodes.shape[1]
+        _need(path_nodes, "path_nodes", torch.int32, (B, P), dev)
+    if out_cache_len is None:
+        out_cache_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(out_cache_len, "out_cache_len", torch.int32, (B,), dev)
+    s = _stream(stream, dev)
+    args = (_ptr(kv_nodes), _ptr(path_nodes), P, _ptr(accept_len), _ptr(cache_len), B, N1, L_cap, planes, eb,
+            sstride, dstride, _ptr(kv_cache), _ptr(out_cache_len), s)
+    return args, out_cache_len, (kv_nodes, path_nodes, accept_len, cache_len, kv_cache)
+
+
+def spec_commit_path(kv_nodes: torch.Tensor, path_nodes: Optional[torch.Tensor], accept_len: torch.Tensor,
+                     cache_len: torch.Tensor, kv_cache: torch.Tensor, *,
+                     out_cache_len: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Copy the root's and the accepted nodes' entries into the cache (spec_commit_path).
+    kv_nodes [planes, B, N1, W], kv_cache [planes, B, L_cap, W] (same dtype; the plane
+    dimension may be strided), path_nodes [B, P] int32 or None (chain), accept_len and
+    cache_len [B] int32.  Returns the new cache lengths [B] int32 (-1 = invalid)."""
+    args, out, _ = _commit_call(kv_nodes, path_nodes, accept_len, cache_len, kv_cache, out_cache_len, stream)
+    _check("spec_commit_path", lib().spec_commit_path(*args))
+    return out
+
+
+def prepare_spec_commit_path(kv_nodes: torch.Tensor, path_nodes: Optional[torch.Tensor], accept_len: torch.Tensor,
+                             cache_len: torch.Tensor, kv_cache: torch.Tensor, *,
+                             out_cache_len: Optional[torch.Tensor] = None, stream=None) -> PreparedCall:
+    """spec_commit_path with every argument fixed (see PreparedCall)."""
+    args, out, keep = _commit_call(kv_nodes, path_nodes, accept_len, cache_len, kv_cache, out_cache_len, stream)
+    return PreparedCall("spec_commit_path", lib().spec_commit_path, _SIGNATURES["spec_commit_path"][1],
+                        args, out, keep)
 
 
 # -------------------------------------------------------------------- measurement hooks

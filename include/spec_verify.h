@@ -3,11 +3,14 @@
  * verification library, libspecverify.so.
  *
  * Three operations of speculative decoding's verification step, batched over
- * sequences and streamed over the full vocabulary:
+ * sequences and streamed over the full vocabulary, and the two steps on either
+ * side of tree verification:
  *
  *   spec_verify_chain        modified rejection sampling of a chain of drafts
  *   spec_verify_tree_greedy  greedy acceptance of the longest matching tree path
  *   ngram_propose            prompt n-gram lookup drafting (one-hot draft q)
+ *   spec_tree_mask           2-D tree-attention mask and node depths of a draft tree
+ *   spec_commit_path         copy the accepted path's cache entries into the KV cache
  *
  * Pages that define the operations (cited by title):
  *   [Production]  "Speculative Decoding in Production: From Draft Models to
@@ -203,6 +206,72 @@ spec_status_t ngram_propose(const int32_t* context, const int32_t* context_len,
                             int B, int L_max, int n_min, int n_max, int K,
                             int32_t* out_draft_tokens, int32_t* out_draft_len, int32_t* out_match_n,
                             spec_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Tree-attention mask.
+ *
+ * [Production] section III.2 "The Tree Attention Verification Mechanism": the
+ * candidate tree is flattened into one sequence (node order) and verified in one
+ * target pass under a 2-D mask, so that each branch is scored on its own path.
+ *
+ * Reading: out_mask[b, i, j] = 1 iff node j lies on the path from the root to node
+ * i, node i included (so row 0 is the root alone, column 0 is all ones, and the
+ * mask is lower triangular); out_depth[b, i] = edges from the root to node i.  The
+ * flattened sequence is the node order itself: node_token needs no reordering.
+ *
+ * parent    [B, N1] int32: parent[b,0] = -1, 0 <= parent[b,i] < i.
+ * out_mask  [B, N1, N1] uint8 (0 or 1), or NULL; any alignment.
+ * out_depth [B, N1] int32, or NULL (not both NULL).
+ *
+ * Invalid device data (a parent array that breaks the order) gives tree b an
+ * all-zero mask and depth -1 for every node.
+ * Limits: 1 <= N1 <= SPEC_MAX_TREE_NODES.  No workspace is needed.
+ * ------------------------------------------------------------------------- */
+spec_status_t spec_tree_mask(const int32_t* parent, int B, int N1, uint8_t* out_mask, int32_t* out_depth,
+                             spec_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Commit of the accepted path's cache entries.
+ *
+ * [Medusa], "System Topology & Data Flow" figure: after tree verification the
+ * tokens of the accepted branch are committed to the KV cache.
+ *
+ * Reading: the pass that scored the flattened tree produced one cache entry per
+ * node, the root (the token emitted by the previous step) included.  For sequence
+ * b with n = accept_len[b] and c = cache_len[b], the root's entry goes to cache
+ * position c and the entry of the k-th accepted node to position c + k
+ * (k = 1..n); out_cache_len[b] = c + n + 1.  The token emitted after the path has
+ * no entry yet.  Without path_nodes the accepted nodes are 1..n (a chain).
+ *
+ * An entry is `planes` pieces of entry_bytes each (e.g. one per layer and K/V):
+ * kv_nodes  piece p of node i of sequence b at byte
+ *           p * node_plane_stride + (b * N1 + i) * entry_bytes;
+ *           holds (planes - 1) * node_plane_stride + B * N1 * entry_bytes bytes.
+ * kv_cache  piece p of position t of sequence b at byte
+ *           p * cache_plane_stride + (b * L_cap + t) * entry_bytes;
+ *           holds (planes - 1) * cache_plane_stride + B * L_cap * entry_bytes bytes.
+ *           Only the committed positions are written.
+ * path_nodes [B, path_stride] int32: accepted nodes from the root side, root
+ *           excluded (out_path_nodes of spec_verify_tree_greedy, path_stride =
+ *           max_depth + 1), or NULL for a chain.
+ * accept_len [B] int32 (out_accept_len of verification; -1 = flagged invalid).
+ * cache_len [B] int32 committed length before the call.
+ * out_cache_len [B] int32 length after the call, or NULL; must not alias cache_len.
+ * kv_nodes and kv_cache must not overlap; both 16-byte aligned; entry_bytes and
+ * (with planes > 1) the plane strides are multiples of 16, each stride at least
+ * one plane.
+ *
+ * Invalid device data for sequence b (accept_len < 0, n > path_stride or, without
+ * path_nodes, n > N1 - 1, a path node outside [0, N1), c < 0 or c + n + 1 > L_cap)
+ * writes nothing for b and sets out_cache_len[b] = -1.
+ * Limits: planes * entry_bytes / 16 < 2^31, 1 <= path_stride <= SPEC_MAX_TREE_NODES + 1.
+ * No workspace is needed.
+ * ------------------------------------------------------------------------- */
+spec_status_t spec_commit_path(const void* kv_nodes, const int32_t* path_nodes, int path_stride,
+                               const int32_t* accept_len, const int32_t* cache_len,
+                               int B, int N1, int L_cap, int planes, size_t entry_bytes,
+                               size_t node_plane_stride, size_t cache_plane_stride,
+                               void* kv_cache, int32_t* out_cache_len, spec_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,10 @@ from .workloads import (  # noqa: F401
     chain_config_low_accept_bf16,
     tree_inputs,
     tree_config_eagle_bf16,
+    tree_parents,
+    random_parents,
+    kv_entries,
+    commit_requests,
     ngram_prompts,
     ngram_config_prompts,
     ngram_target_inputs,

@@ -41,6 +41,9 @@ _ROLES = {
     "prompt": 10,
     "ngram_target": 11,
     "draft_len": 12,
+    "kv": 13,
+    "commit": 14,
+    "parents": 15,
 }
 
 
@@ -349,6 +352,61 @@ def tree_config_eagle_bf16(seed: int = 0, B: int = 32, n_nodes: int = 60, depth:
     matching child token +10 with probability 0.7 per node."""
     return tree_inputs(seed, B=B, n_nodes=n_nodes, depth=depth, V=V, dtype="bf16", sigma=2.0,
                        boost=10.0, p_boost=0.7, **kw)
+
+
+def tree_parents(seed: int = 0, *, B: int = 32, n_nodes: int = 60, depth: int = 6, max_branch: int = 4) -> np.ndarray:
+    """The topologies of tree_inputs(seed, ...) alone: parent [B, n_nodes + 1] int32."""
+    return np.stack([_tree_shape(philox(seed, "tree_shape", b), n_nodes, depth, max_branch) for b in range(B)])
+
+
+def random_parents(seed: int, *, B: int, N1: int, kind: str = "mixed", window: int = 8) -> np.ndarray:
+    """Parents-first trees of N1 nodes: "random" (parent of i uniform over the `window`
+    nodes before it), "chain" (parent i - 1), "star" (every parent the root), or "mixed"
+    (one of the three per sequence).  Returns parent [B, N1] int32."""
+    out = np.empty((B, N1), dtype=np.int32)
+    for b in range(B):
+        rng = philox(seed, "parents", b)
+        k = kind if kind != "mixed" else ("random", "chain", "star")[int(rng.integers(0, 3))]
+        par = np.empty(N1, dtype=np.int64)
+        par[0] = -1
+        idx = np.arange(1, N1)
+        if k == "chain":
+            par[1:] = idx - 1
+        elif k == "star":
+            par[1:] = 0
+        else:
+            lo = np.maximum(0, idx - window)
+            par[1:] = lo + (rng.random(N1 - 1) * (idx - lo)).astype(np.int64)
+        out[b] = par
+    return out
+
+
+def kv_entries(seed: int, *, planes: int, B: int, rows: int, W: int) -> np.ndarray:
+    """Random 16-bit cache entries [planes, B, rows, W] (uint16 bit patterns)."""
+    out = np.empty((planes, B, rows, W), dtype=np.uint16)
+
+    def one(b: int) -> None:
+        out[:, b] = philox(seed, "kv", b).integers(0, 1 << 16, size=(planes, rows, W), dtype=np.uint16)
+
+    _parallel(one, B, None)
+    return out
+
+
+def commit_requests(seed: int, *, B: int, N1: int, P: int, L_cap: int):
+    """Random commit inputs: accept_len [B] in [0, min(P, N1 - 1)], path [B, P] of that
+    many distinct nodes in [1, N1) in increasing order (-1 padded), cache_len [B] with
+    room for the commit.  Returns (accept_len, path, cache_len) as int32 arrays."""
+    acc = np.zeros(B, dtype=np.int32)
+    path = np.full((B, P), -1, dtype=np.int32)
+    clen = np.zeros(B, dtype=np.int32)
+    top = min(P, N1 - 1)
+    for b in range(B):
+        rng = philox(seed, "commit", b)
+        n = int(rng.integers(0, top + 1))
+        acc[b] = n
+        path[b, :n] = np.sort(rng.choice(np.arange(1, N1), size=n, replace=False))
+        clen[b] = int(rng.integers(0, L_cap - n))
+    return acc, path, clen
 
 
 # --------------------------------------------------------------------------------------

@@ -106,3 +106,32 @@ def test_empty_batches_need_no_gpu_work(lib):
     null = None
     assert lib.spec_verify_tree_greedy(null, 1, null, null, 0, 4, 10, 3, null, null, null, null, null, 0, null) == 0
     assert lib.ngram_propose(null, null, 0, 10, 1, 4, 5, null, null, null, null) == 0
+
+
+def test_mask_and_commit_host_errors(lib):
+    null = None
+    fake = ctypes.c_void_p(1 << 20)
+    # mask: too many nodes, no outputs, N1 = 0
+    assert lib.spec_tree_mask(fake, 1, 2000, fake, null, null) == 2
+    assert lib.spec_tree_mask(fake, 1, 5, null, null, null) == 1
+    assert lib.spec_tree_mask(fake, 1, 0, fake, null, null) == 1
+    assert lib.spec_tree_mask(null, 0, 5, null, null, null) == 0
+    # commit: entry not a multiple of 16 bytes, bad path stride, plane stride too small,
+    # misaligned buffers, NULL lengths
+    args = dict(kv=fake, path=fake, P=7, acc=fake, clen=fake, B=4, N1=61, L=32, planes=2, eb=2048,
+                sp=4 * 61 * 2048, dp=4 * 32 * 2048, cache=ctypes.c_void_p(1 << 21), out=null)
+
+    def commit(**kw):
+        a = dict(args, **kw)
+        return lib.spec_commit_path(a["kv"], a["path"], a["P"], a["acc"], a["clen"], a["B"], a["N1"], a["L"],
+                                    a["planes"], a["eb"], a["sp"], a["dp"], a["cache"], a["out"], null)
+
+    assert commit(eb=24) == 1
+    assert commit(P=0) == 1
+    assert commit(P=2000) == 1
+    assert commit(sp=100) == 1
+    assert b"plane stride" in lib.spec_last_error()
+    assert commit(dp=4 * 32 * 2048 - 16) == 1
+    assert commit(kv=ctypes.c_void_p((1 << 20) + 8)) == 1
+    assert commit(clen=null) == 1
+    assert commit(B=0) == 0
