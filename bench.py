@@ -356,8 +356,19 @@ def tree_io_workloads(warmup, steps, dev, parents, paths):
     r = _entry(f"tree_commit_B{B}_N{N1 - 1}_planes{planes}_entry{entry}",
                dict(ms=ms, bytes=int(np.mean(moved)), kernels=kms, steps=steps), committed)
     r["entries_per_call"] = committed
-    out.append(r)
     del prepared
+    # context: a plain contiguous copy of the same bytes, rotating over as many buffer pairs
+    half = int(np.mean(moved)) // 2 // 16 * 16
+    pairs = [(torch.empty(half, dtype=torch.uint8, device=dev), torch.empty(half, dtype=torch.uint8, device=dev))
+             for _ in range(n_sets)]
+
+    def pcall(i):
+        sv.spec_probe_copy(*pairs[i])
+
+    pms, _ = time_calls(pcall, n_sets, warmup, steps, False)
+    r["plain_copy_same_bytes_us"] = round(pms * 1e3, 3)
+    out.append(r)
+    del pairs
     torch.cuda.empty_cache()
     return out
 

@@ -15,8 +15,11 @@
 // shared memory; each row's ancestor set is a bitset there, built by one lane walking
 // up to the root; the rows' bytes are then written as 16-byte vectors (the block's
 // rows are one contiguous byte range of the output).
-// commit_path: a pure copy, bound by HBM.  One workgroup moves 16 KB of one entry with
-// 16-byte non-temporal loads and stores; entries past the accepted length exit at once.
+// commit_path: a pure copy, bound by HBM.  One workgroup moves one 4 KB chunk of every
+// committed entry of one sequence: 16-byte loads, the loads of four entries in flight
+// together, then 16-byte non-temporal stores (measured: plain loads beat non-temporal
+// ones here, non-temporal stores beat plain ones; 4 KB chunks with 4 entries in flight
+// beat 8 and 16 KB chunks, and 8 entries in flight).
 #include "device_common.h"
 #include "host_runtime.h"
 #include "spec_verify.h"
@@ -93,8 +96,9 @@ __global__ __launch_bounds__(kMaskThreads) void tree_mask_kernel(const int32_t* 
 }
 
 constexpr int kCommitThreads = 256;
-constexpr int kCommitUnroll = 4;                                 // vectors per lane
-constexpr int kCommitVecs = kCommitThreads * kCommitUnroll;      // 16-byte vectors per workgroup
+constexpr int kCommitUnroll = 1;                              // vectors per lane per entry
+constexpr int kCommitBatch = 4;                               // entries whose loads are in flight together
+constexpr int kCommitVecs = kCommitThreads * kCommitUnroll;   // 16-byte vectors per workgroup and entry
 
 struct CommitArgs {
   const char* src;
@@ -103,61 +107,80 @@ struct CommitArgs {
   const int32_t* acc;
   const int32_t* clen;
   int32_t* out_len;
-  int B, N1, P, L_cap, E_max, chunks;
+  int B, N1, P, L_cap, chunks;
   uint32_t vpp;  // 16-byte vectors per plane of one entry
   uint32_t vpe;  // 16-byte vectors per entry (all planes)
   size_t entry_bytes, src_plane, dst_plane;
 };
 
+// Node of the k-th committed entry (k >= 1): the path row is held one node per lane
+// (`pv`, lanes 0..63) when it fits in a wave, else read from memory.
+__device__ __forceinline__ int committed_node(const CommitArgs& a, const int32_t* prow, int pv, int k) {
+  if (!a.path) return k;
+  if (k - 1 < 64) return __builtin_amdgcn_readlane(pv, k - 1);
+  return prow[k - 1];
+}
+
+// One workgroup per (sequence, 4 KB chunk of an entry), for every committed entry of
+// that sequence: each wave reads the sequence's lengths and path row itself and checks
+// them with a ballot, so the kernel has no barrier and three memory round trips (the
+// row, the entries' chunks, the stores) however many entries are committed.
 __global__ __launch_bounds__(kCommitThreads) void commit_path_kernel(CommitArgs a) {
   const int tid = threadIdx.x;
-  const int chunk = blockIdx.x % a.chunks;
-  const int rest = blockIdx.x / a.chunks;
-  const int k = rest % a.E_max;
-  const int b = rest / a.E_max;
-  const bool reporter = chunk == 0 && k == 0;  // writes the sequence's new length
+  const int lane = tid & 63;
+  const int b = blockIdx.x / a.chunks;
+  const int chunk = blockIdx.x - b * a.chunks;
+  const int32_t* prow = a.path ? a.path + static_cast<size_t>(b) * a.P : nullptr;
+  // the path row's first 64 nodes, the lengths: loads with no dependence on each other
+  const int pv = prow && lane < a.P ? prow[lane] : 0;
   const int n = a.acc[b];
   const int c0 = a.clen[b];
-  const bool ok = n >= 0 && c0 >= 0 && static_cast<long long>(c0) + n + 1 <= a.L_cap &&
-                  (a.path ? n <= a.P : n <= a.N1 - 1);
-  if (!ok) {
-    if (reporter && tid == 0 && a.out_len) a.out_len[b] = -1;
-    return;
-  }
-  if (k > n) return;
-  if (a.path) {
-    int bad = 0;
-    for (int t = tid; t < n; t += kCommitThreads) {
-      const int v = a.path[static_cast<size_t>(b) * a.P + t];
+  bool bad = !(n >= 0 && c0 >= 0 && static_cast<long long>(c0) + n + 1 <= a.L_cap &&
+               (prow ? n <= a.P : n <= a.N1 - 1));
+  if (prow) {
+    bad |= lane < n && (pv < 0 || pv >= a.N1);
+    for (int t = lane + 64; t < n; t += 64) {
+      const int v = prow[t];
       bad |= v < 0 || v >= a.N1;
     }
-    if (__syncthreads_or(bad)) {
-      if (reporter && tid == 0 && a.out_len) a.out_len[b] = -1;
-      return;
-    }
   }
-  if (reporter && tid == 0 && a.out_len) a.out_len[b] = c0 + n + 1;
-  const int node = k == 0 ? 0 : (a.path ? a.path[static_cast<size_t>(b) * a.P + k - 1] : k);
-  const char* src = a.src + (static_cast<size_t>(b) * a.N1 + node) * a.entry_bytes;
-  char* dst = a.dst + (static_cast<size_t>(b) * a.L_cap + c0 + k) * a.entry_bytes;
-  const uint32_t v0 = static_cast<uint32_t>(chunk) * kCommitVecs + tid;
-  u32x4 r[kCommitUnroll];
+  bad = __any(bad);
+  if (chunk == 0 && tid == 0 && a.out_len) a.out_len[b] = bad ? -1 : c0 + n + 1;
+  if (bad) return;
+  // this lane's vectors: plane and offset do not depend on the entry
+  size_t so[kCommitUnroll], dof[kCommitUnroll];
+  bool live[kCommitUnroll];
 #pragma unroll
   for (int j = 0; j < kCommitUnroll; ++j) {
-    const uint32_t v = v0 + j * kCommitThreads;
-    if (v < a.vpe) {
-      const uint32_t plane = v / a.vpp;
-      const uint32_t off = v - plane * a.vpp;
-      r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + plane * a.src_plane) + off);
-    }
+    const uint32_t v = static_cast<uint32_t>(chunk) * kCommitVecs + j * kCommitThreads + tid;
+    live[j] = v < a.vpe;
+    const uint32_t plane = live[j] ? v / a.vpp : 0u;
+    const uint32_t off = live[j] ? v - plane * a.vpp : 0u;
+    so[j] = plane * a.src_plane + static_cast<size_t>(off) * 16;
+    dof[j] = plane * a.dst_plane + static_cast<size_t>(off) * 16;
   }
+  const char* sseq = a.src + static_cast<size_t>(b) * a.N1 * a.entry_bytes;
+  char* dseq = a.dst + (static_cast<size_t>(b) * a.L_cap + c0) * a.entry_bytes;
+  for (int k0 = 0; k0 <= n; k0 += kCommitBatch) {
+    u32x4 r[kCommitBatch][kCommitUnroll];
 #pragma unroll
-  for (int j = 0; j < kCommitUnroll; ++j) {
-    const uint32_t v = v0 + j * kCommitThreads;
-    if (v < a.vpe) {
-      const uint32_t plane = v / a.vpp;
-      const uint32_t off = v - plane * a.vpp;
-      __builtin_nontemporal_store(r[j], reinterpret_cast<u32x4*>(dst + plane * a.dst_plane) + off);
+    for (int e = 0; e < kCommitBatch; ++e) {
+      const int k = k0 + e;
+      if (k > n) break;
+      const int node = k == 0 ? 0 : committed_node(a, prow, pv, k);
+      const char* src = sseq + static_cast<size_t>(node) * a.entry_bytes;
+#pragma unroll
+      for (int j = 0; j < kCommitUnroll; ++j)
+        if (live[j]) r[e][j] = *reinterpret_cast<const u32x4*>(src + so[j]);
+    }
+#pragma unroll
+    for (int e = 0; e < kCommitBatch; ++e) {
+      const int k = k0 + e;
+      if (k > n) break;
+      char* dst = dseq + static_cast<size_t>(k) * a.entry_bytes;
+#pragma unroll
+      for (int j = 0; j < kCommitUnroll; ++j)
+        if (live[j]) __builtin_nontemporal_store(r[e][j], reinterpret_cast<u32x4*>(dst + dof[j]));
     }
   }
 }
@@ -220,14 +243,13 @@ spec_status_t spec_commit_path(const void* kv_nodes, const int32_t* path_nodes, 
   a.N1 = N1;
   a.P = path_nodes ? path_stride : 0;
   a.L_cap = L_cap;
-  a.E_max = path_nodes ? path_stride + 1 : N1;
   a.chunks = static_cast<int>((vpe + kCommitVecs - 1) / kCommitVecs);
   a.vpp = static_cast<uint32_t>(entry_bytes / 16);
   a.vpe = static_cast<uint32_t>(vpe);
   a.entry_bytes = entry_bytes;
   a.src_plane = node_plane_stride;
   a.dst_plane = cache_plane_stride;
-  const long long grid = static_cast<long long>(B) * a.E_max * a.chunks;
+  const long long grid = static_cast<long long>(B) * a.chunks;
   if (grid > 2147483647LL) return fail(SPEC_ERR_UNSUPPORTED, "grid too large");
   LaunchScope scope("commit_path", s);
   scope.launch(commit_path_kernel, dim3(static_cast<unsigned>(grid)), dim3(kCommitThreads), s, a);
