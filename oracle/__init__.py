@@ -18,7 +18,10 @@ Pages cited (by title; section, step or figure given at each use):
     Speculative Decoding" (acefleet.dev) -- "Technical Foundations" (draft, then
     one verification pass; acceptance restated).
   * "Speculative decoding: Medusa, EAGLE, vLLM" (vikram-blog.pages.dev) -- the
-    "System Topology & Data Flow" tree figure and the greedy (temperature 0) usage.
+    "System Topology & Data Flow" tree figure (and the commit of the accepted branch)
+    and the greedy (temperature 0) usage.
+  * "Breaking the Memory Bandwidth Wall ..." (acefleet.dev), "Closed-Loop Real-Time
+    Adaptive Gating" -- the temperature gate and the per-tenant acceptance breaker.
 
 Where the pages are silent the oracle takes one stated reading (temperature
 divides the logits; a bonus token is drawn from the target row after the last
@@ -48,3 +51,4 @@ from .chain import (  # noqa: F401
 from .tree import TreeBatchResult, argmax_first, verify_tree_greedy, verify_tree_greedy_sequence  # noqa: F401
 from .ngram import NgramResult, ngram_propose, ngram_propose_sequence  # noqa: F401
 from .tree_io import commit_path, tree_attention_mask  # noqa: F401
+from .gate import Gate  # noqa: F401
