@@ -272,6 +272,9 @@ def other_workloads(warmup, steps, dev):
     # the steps on either side of tree verification, on the same workload's trees
     out += tree_io_workloads(warmup, steps, dev, tree_parents, tree_paths)
 
+    # adaptive gate (host code): decide + observe for a batch of 64 requests over 16 tenants
+    out.append(gate_workload())
+
     # n-gram propose + one-hot verify, B=128 L=4096 K=5 V=32000 bf16
     progress("ngram: generating inputs")
     n_sets = 11
@@ -371,6 +374,27 @@ def tree_io_workloads(warmup, steps, dev, parents, paths):
     del pairs
     torch.cuda.empty_cache()
     return out
+
+
+def gate_workload(B=64, tenants=16, iters=2000):
+    """Host time of one gate decision batch plus one outcome batch (no GPU work)."""
+    import numpy as np
+
+    import draft_token_verification_09_amd as sv
+
+    rng = np.random.default_rng(0)
+    g = sv.SpecGate()
+    keys = rng.integers(0, tenants, size=(iters, B)).astype(np.uint64)
+    temps = rng.choice([0.0, 0.5, 0.8], size=(iters, B)).astype(np.float32)
+    acc = rng.binomial(5, 0.7, size=(iters, B)).astype(np.int32)
+    dl = np.full(B, 5, dtype=np.int32)
+    t0 = time.perf_counter()
+    for i in range(iters):
+        g.decide(keys[i], temps[i])
+        g.observe(keys[i], acc[i], dl)
+    us = (time.perf_counter() - t0) / iters * 1e6
+    return dict(workload=f"gate_decide_observe_B{B}_tenants{tenants}_host", us_per_batch=round(us, 2),
+                note="host code through the Python binding; no GPU work")
 
 
 def _entry(workload, r, positions):

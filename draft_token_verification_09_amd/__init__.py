@@ -7,9 +7,13 @@ ctypes binding (binding.py) whose functions carry the C entry points' names.
 
 from .binding import (  # noqa: F401
     ChainResult,
+    GATE_CLOSED,
+    GATE_HALF_OPEN,
+    GATE_OPEN,
     NgramResult,
     PreparedCall,
     SpecError,
+    SpecGate,
     TreeMaskResult,
     TreeResult,
     lib,

@@ -55,6 +55,13 @@ _SIGNATURES = {
     "spec_tree_mask": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "spec_commit_path": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _sz, _sz, _sz,
                                 _vp, _vp, _vp]),
+    "spec_gate_default_config": (None, [_vp]),
+    "spec_gate_create": (_i32, [_vp, _vp]),
+    "spec_gate_destroy": (None, [_vp]),
+    "spec_gate_decide": (_i32, [_vp, _vp, _vp, _i32, _vp]),
+    "spec_gate_observe": (_i32, [_vp, _vp, _vp, _vp, _i32]),
+    "spec_gate_tenant": (_i32, [_vp, ctypes.c_uint64, _vp]),
+    "spec_gate_tenant_count": (ctypes.c_int64, [_vp]),
     "spec_timing_enable": (_i32, [_i32]),
     "spec_timing_reset": (_i32, []),
     "spec_timing_collect": (_i32, []),
@@ -456,6 +463,100 @@ def prepare_spec_commit_path(kv_nodes: torch.Tensor, path_nodes: Optional[torch.
     args, out, keep = _commit_call(kv_nodes, path_nodes, accept_len, cache_len, kv_cache, out_cache_len, stream)
     return PreparedCall("spec_commit_path", lib().spec_commit_path, _SIGNATURES["spec_commit_path"][1],
                         args, out, keep)
+
+
+# -------------------------------------------------------------------- adaptive gate
+
+
+class GateConfig(ctypes.Structure):
+    _fields_ = [("temperature_limit", ctypes.c_double), ("acceptance_floor", ctypes.c_double),
+                ("ema_weight", ctypes.c_double), ("cooldown", ctypes.c_int32)]
+
+
+class GateTenantStats(ctypes.Structure):
+    _fields_ = [("ema", ctypes.c_double), ("state", ctypes.c_int32), ("cooldown", ctypes.c_int32),
+                ("observations", ctypes.c_int64), ("accepted", ctypes.c_int64), ("drafted", ctypes.c_int64),
+                ("trips", ctypes.c_int64)]
+
+
+GATE_CLOSED, GATE_OPEN, GATE_HALF_OPEN = 0, 1, 2
+
+
+class SpecGate:
+    """The library's adaptive speculation gate (include/spec_gate.h): host-side state,
+    host arrays.  decide() says per request whether to speculate; observe() feeds
+    verification outcomes (num_accepted, draft_len) back per tenant."""
+
+    def __init__(self, temperature_limit: Optional[float] = None, acceptance_floor: Optional[float] = None,
+                 ema_weight: Optional[float] = None, cooldown: Optional[int] = None):
+        L = lib()
+        cfg = GateConfig()
+        L.spec_gate_default_config(ctypes.byref(cfg))
+        if temperature_limit is not None:
+            cfg.temperature_limit = temperature_limit
+        if acceptance_floor is not None:
+            cfg.acceptance_floor = acceptance_floor
+        if ema_weight is not None:
+            cfg.ema_weight = ema_weight
+        if cooldown is not None:
+            cfg.cooldown = cooldown
+        handle = ctypes.c_void_p()
+        _check("spec_gate_create", L.spec_gate_create(ctypes.byref(cfg), ctypes.byref(handle)))
+        self._h = handle
+        self.config = cfg
+
+    def close(self) -> None:
+        if self._h:
+            lib().spec_gate_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _host(x, dtype):
+        import numpy as np
+
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().numpy()
+        return np.ascontiguousarray(np.asarray(x), dtype=dtype)
+
+    def decide(self, tenant, temperature):
+        """Per request: True to speculate.  tenant [B] (uint64 keys), temperature [B]."""
+        import numpy as np
+
+        t = self._host(tenant, np.uint64)
+        T = self._host(temperature, np.float32)
+        if t.shape != T.shape or t.ndim != 1:
+            raise ValueError("tenant and temperature must be 1-D of one length")
+        out = np.empty(t.shape, dtype=np.int32)
+        _check("spec_gate_decide", lib().spec_gate_decide(self._h, t.ctypes.data, T.ctypes.data, t.size,
+                                                           out.ctypes.data))
+        return out.astype(bool)
+
+    def observe(self, tenant, num_accepted, draft_len) -> None:
+        """Feed verification outcomes: tenant [B], num_accepted [B], draft_len [B] (tensors
+        on any device or arrays; device tensors are copied to the host)."""
+        import numpy as np
+
+        t = self._host(tenant, np.uint64)
+        a = self._host(num_accepted, np.int32)
+        d = self._host(draft_len, np.int32)
+        if not (t.shape == a.shape == d.shape) or t.ndim != 1:
+            raise ValueError("tenant, num_accepted and draft_len must be 1-D of one length")
+        _check("spec_gate_observe", lib().spec_gate_observe(self._h, t.ctypes.data, a.ctypes.data, d.ctypes.data,
+                                                             t.size))
+
+    def tenant(self, key: int) -> GateTenantStats:
+        st = GateTenantStats()
+        _check("spec_gate_tenant", lib().spec_gate_tenant(self._h, key, ctypes.byref(st)))
+        return st
+
+    def tenant_count(self) -> int:
+        return int(lib().spec_gate_tenant_count(self._h))
 
 
 # -------------------------------------------------------------------- measurement hooks

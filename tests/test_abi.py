@@ -9,7 +9,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-DECL = re.compile(r"^(?:const\s+)?(?:spec_status_t|size_t|int|char|void)\s*\*?\s*(\w+)\s*\(", re.M)
+DECL = re.compile(r"^(?:const\s+)?(?:spec_status_t|size_t|int|int64_t|char|void)\s*\*?\s*(\w+)\s*\(", re.M)
 
 
 def declared_functions():
