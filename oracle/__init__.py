@@ -52,3 +52,4 @@ from .tree import TreeBatchResult, argmax_first, verify_tree_greedy, verify_tree
 from .ngram import NgramResult, ngram_propose, ngram_propose_sequence  # noqa: F401
 from .tree_io import commit_path, tree_attention_mask  # noqa: F401
 from .gate import Gate  # noqa: F401
+from .tree_sampled import verify_tree_sampled, verify_tree_sampled_sequence  # noqa: F401
