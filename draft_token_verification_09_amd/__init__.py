@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     prepare_spec_commit_path,
     prepare_spec_verify_chain,
     prepare_spec_tree_mask,
+    prepare_spec_verify_tree,
     prepare_spec_verify_tree_greedy,
     spec_commit_path,
     spec_probe_copy,
@@ -33,5 +34,6 @@ from .binding import (  # noqa: F401
     spec_tree_mask,
     spec_verify_chain,
     spec_verify_chain_workspace_size,
+    spec_verify_tree,
     spec_verify_tree_greedy,
 )

@@ -52,6 +52,9 @@ _SIGNATURES = {
     "spec_verify_tree_greedy": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                        _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ngram_propose": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "spec_verify_tree_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "spec_verify_tree": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_tree_mask": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "spec_commit_path": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _sz, _sz, _sz,
                                 _vp, _vp, _vp]),
@@ -319,6 +322,64 @@ def prepare_spec_verify_tree_greedy(target_logits: torch.Tensor, parent: torch.T
                                  stream)
     return PreparedCall("spec_verify_tree_greedy", lib().spec_verify_tree_greedy,
                         _SIGNATURES["spec_verify_tree_greedy"][1], args, out, keep)
+
+
+def _tree_sampled_call(target_logits, draft_logits, parent, node_token, temperature, u_accept, u_final,
+                       max_depth, out, workspace_buf, stream):
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, N1, V]")
+    B, N1, V = target_logits.shape
+    dev = target_logits.device
+    code = _dtype_code(target_logits)
+    for t, name in ((target_logits, "target_logits"), (draft_logits, "draft_logits")):
+        if t.dtype != target_logits.dtype or tuple(t.shape) != (B, N1, V) or t.device != dev:
+            raise ValueError(f"{name} must be [B, N1, V] of one dtype and device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _need(parent, "parent", torch.int32, (B, N1), dev)
+    _need(node_token, "node_token", torch.int32, (B, N1), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, N1), dev)
+    _need(u_final, "u_final", torch.float32, (B,), dev)
+    D1 = max_depth + 1
+    if out is None:
+        out = TreeResult(
+            accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+            tokens=torch.empty((B, D1), dtype=torch.int32, device=dev),
+            path_nodes=torch.empty((B, D1), dtype=torch.int32, device=dev),
+            argmax=None,
+        )
+    s = _stream(stream, dev)
+    need = int(lib().spec_verify_tree_workspace_size(B, N1, V, code)) if B > 0 else 0
+    buf = workspace_buf if workspace_buf is not None else workspace(need, dev, s, "tree_sampled")
+    wp, wbytes = _aligned_ptr(buf)
+    args = (_ptr(target_logits), _ptr(draft_logits), code, _ptr(parent), _ptr(node_token), _ptr(temperature),
+            _ptr(u_accept), _ptr(u_final), B, N1, V, max_depth, _ptr(out.accept_len), _ptr(out.tokens),
+            _ptr(out.path_nodes), wp, wbytes, s)
+    return args, out, (target_logits, draft_logits, parent, node_token, temperature, u_accept, u_final, buf)
+
+
+def spec_verify_tree(target_logits: torch.Tensor, draft_logits: torch.Tensor, parent: torch.Tensor,
+                     node_token: torch.Tensor, temperature: torch.Tensor, u_accept: torch.Tensor,
+                     u_final: torch.Tensor, max_depth: int, *, out: Optional[TreeResult] = None,
+                     workspace_buf: Optional[torch.Tensor] = None, stream=None) -> TreeResult:
+    """Stochastic tree verification (spec_verify_tree).  target and draft [B, N1, V],
+    parent and node_token [B, N1] int32, temperature [B], u_accept [B, N1], u_final [B]."""
+    args, out, _ = _tree_sampled_call(target_logits, draft_logits, parent, node_token, temperature, u_accept,
+                                      u_final, max_depth, out, workspace_buf, stream)
+    _check("spec_verify_tree", lib().spec_verify_tree(*args))
+    return out
+
+
+def prepare_spec_verify_tree(target_logits: torch.Tensor, draft_logits: torch.Tensor, parent: torch.Tensor,
+                             node_token: torch.Tensor, temperature: torch.Tensor, u_accept: torch.Tensor,
+                             u_final: torch.Tensor, max_depth: int, *, out: Optional[TreeResult] = None,
+                             workspace_buf: Optional[torch.Tensor] = None, stream=None) -> PreparedCall:
+    """spec_verify_tree with every argument fixed (see PreparedCall)."""
+    args, out, keep = _tree_sampled_call(target_logits, draft_logits, parent, node_token, temperature, u_accept,
+                                         u_final, max_depth, out, workspace_buf, stream)
+    return PreparedCall("spec_verify_tree", lib().spec_verify_tree, _SIGNATURES["spec_verify_tree"][1], args,
+                        out, keep)
 
 
 @dataclass

@@ -1,0 +1,680 @@
+// Stochastic (temperature > 0) tree verification.
+//
+// "Speculative Decoding in Production: From Draft Models to EAGLE-3 Dynamic Trees ..."
+// (blog.llmgo.top): section I.1 gives the rule for one drafted token (accept with
+// min(1, p/q), else draw from max(0, p - q) normalised) and section III.2 verifies a tree
+// whose rejected branch B1 leaves its sibling B2 free to be accepted.  Reading (the
+// published multi-candidate form of the rule): the children of a node were drawn
+// independently from the draft distribution q at that node and are tried in node order
+// against a residual target r_j, r_1 = p and r_{j+1} = max(0, r_j - q) normalised; an
+// accepted child continues the walk, a node whose children are all rejected emits a draw
+// from the last residual, a leaf reached by acceptance emits a bonus draw from its p.
+//
+// The residual after j rejections has the closed form r_{j+1} = max(0, p - c q) / D with
+// c_1 = 0, D_1 = 1, c_{j+1} = c_j + D_j and D_{j+1} = sum_v max(0, p(v) - c_{j+1} q(v)), so
+// each rejection needs one sum over the vocabulary and nothing else.
+//
+// Only the rows on the walk are read: the accepted path's target rows and the draft rows
+// of its internal nodes.  The walk is sequential in depth, so it is spread over W
+// workgroups per sequence, each owning one slice of the vocabulary (256 lanes x 8 vectors
+// of 16 bytes).  A workgroup holds its slice of the current node's two rows in registers
+// for every test at that node; the per-slice sums (row maxima and exp2 sums, residual
+// masses) pass between the W workgroups through generation-tagged slots, and every
+// workgroup combines them in the same order, so all of them take the same decisions.  The
+// workgroup whose slice holds the final draw's point searches it and writes the outputs.
+//
+// ts_prep (one workgroup per sequence) validates the inputs and lists every node's
+// children in node order; ts_walk runs the walk.  Its workgroups wait for each other, so
+// a launch holds at most half of the workgroups that fit on the device at once, and every
+// wait is bounded.
+#include <atomic>
+
+#include "device_common.h"
+#include "host_runtime.h"
+#include "spec_verify.h"
+
+namespace specv {
+
+constexpr int kTsNV = 8;                          // 16-byte vectors per lane per row slice
+constexpr int kTsMaxSlices = 64;                  // workgroups per sequence
+constexpr int kTsWords = 8;                       // tagged 64-bit words per slot
+constexpr int kTsPollLimit = 1 << 18;             // polls before a wait gives up
+
+// Keeps the scheduler from interleaving the unpacked elements of several vectors, which
+// would hold all of them in registers at once.
+__device__ __forceinline__ void ts_vector_done() { __builtin_amdgcn_sched_barrier(0); }
+
+// Marks the packed slice registers as rewritten, so that each pass over them unpacks the
+// elements again instead of keeping every unpacked element alive from the first pass.
+__device__ __forceinline__ void ts_fresh(u32x4 (&r)[kTsNV]) {
+#pragma unroll
+  for (int j = 0; j < kTsNV; ++j) asm volatile("" : "+v"(r[j]));
+}
+
+struct TsArgs {
+  const void* target;
+  const void* draft;
+  const int32_t* parent;
+  const int32_t* token;
+  const float* temperature;
+  const float* u_accept;
+  const float* u_final;
+  int B, N1, V, max_depth, W;
+  int32_t* out_len;
+  int32_t* out_tokens;
+  int32_t* out_nodes;
+  uint32_t gen;     // the host's number for this call
+  uint32_t* runs;   // run counter, advanced by ts_prep on every run
+  int32_t* valid;   // [B]
+  int32_t* kstart;  // [B, N1 + 1] first child slot of each node
+  int32_t* klist;   // [B, N1] children, grouped by parent, in node order
+  uint64_t* slots;  // [B, 2, W, kTsWords]
+};
+
+// ---------------------------------------------------------------- hand-over words
+//
+// A slot word carries 32 payload bits and a 32-bit tag (the call's generation mixed with
+// the walk step), written by one agent-scope atomic store.  A reader takes a slot only
+// when every word carries the tag it expects, so stale words (earlier steps or calls, or
+// anything else) read as "not written yet".  Steps alternate between two slots per
+// workgroup: a workgroup publishes step s + 2 only after it has read every workgroup's
+// step s + 1, which each of them published only after reading step s, so no word is
+// overwritten before all readers have it.
+__device__ __forceinline__ uint32_t ts_tag(uint32_t gen, int step) {
+  const uint32_t t = gen ^ (static_cast<uint32_t>(step) * 0x9e3779b1u);
+  return t != 0u ? t : 0x2545f491u;
+}
+
+__device__ __forceinline__ uint64_t ts_word(uint32_t payload, uint32_t tag) {
+  return static_cast<uint64_t>(payload) | (static_cast<uint64_t>(tag) << 32);
+}
+
+__device__ __forceinline__ void ts_put_double(uint64_t* w, double v, uint32_t tag) {
+  const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(v));
+  store_agent(w, ts_word(static_cast<uint32_t>(bits), tag));
+  store_agent(w + 1, ts_word(static_cast<uint32_t>(bits >> 32), tag));
+}
+
+__device__ __forceinline__ bool ts_get_double(const uint64_t* w, uint32_t tag, double* v) {
+  const uint64_t lo = load_agent(w), hi = load_agent(w + 1);
+  *v = __longlong_as_double(static_cast<long long>((hi << 32) | (lo & 0xffffffffull)));
+  return static_cast<uint32_t>(lo >> 32) == tag && static_cast<uint32_t>(hi >> 32) == tag;
+}
+
+__device__ __forceinline__ bool ts_get_float(const uint64_t* w, uint32_t tag, float* v) {
+  const uint64_t x = load_agent(w);
+  *v = __uint_as_float(static_cast<uint32_t>(x));
+  return static_cast<uint32_t>(x >> 32) == tag;
+}
+
+// ---------------------------------------------------------------- prep
+__global__ __launch_bounds__(kThreads) void ts_prep_kernel(TsArgs a) {
+  __shared__ int s_par[SPEC_MAX_TREE_NODES];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int N1 = a.N1;
+  if (b == 0 && tid == 0) __hip_atomic_fetch_add(a.runs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int32_t* par = a.parent + static_cast<size_t>(b) * N1;
+  const int32_t* tok = a.token + static_cast<size_t>(b) * N1;
+  const float* ua = a.u_accept + static_cast<size_t>(b) * N1;
+  int bad = 0;
+  for (int i = tid; i < N1; i += kThreads) {
+    const int p = par[i];
+    s_par[i] = p;
+    if (i == 0) {
+      bad |= p != -1;
+    } else {
+      bad |= p < 0 || p >= i;
+      const int x = tok[i];
+      bad |= x < 0 || x >= a.V;
+      const float u = ua[i];
+      bad |= !(u > 0.f && u <= 1.f);
+    }
+  }
+  if (tid == 0) {
+    const float T = a.temperature[b];
+    const float uf = a.u_final[b];
+    bad |= !(T > 0.f && T <= 3.4e38f);
+    bad |= !(uf > 0.f && uf <= 1.f);
+  }
+  bad = __syncthreads_or(bad);
+  if (tid == 0) a.valid[b] = bad ? 0 : 1;
+  if (bad) return;
+  // Children grouped by parent in node order: node p's children start at the number of
+  // nodes whose parent precedes p, and node i sits after its siblings of lower index.
+  int32_t* ks = a.kstart + static_cast<size_t>(b) * (N1 + 1);
+  int32_t* kl = a.klist + static_cast<size_t>(b) * N1;
+  for (int p = tid; p <= N1; p += kThreads) {
+    int cnt = 0;
+    for (int i = 1; i < N1; ++i) cnt += s_par[i] < p;
+    ks[p] = cnt;
+  }
+  for (int i = 1 + tid; i < N1; i += kThreads) {
+    const int p = s_par[i];
+    int before = 0, rank = 0;
+    for (int j = 1; j < N1; ++j) {
+      const int q = s_par[j];
+      before += q < p;
+      rank += q == p && j < i;
+    }
+    kl[before + rank] = i;
+  }
+}
+
+// ---------------------------------------------------------------- walk
+__device__ __forceinline__ uint32_t ts_generation(const TsArgs& a) {
+  const uint32_t g = a.gen ^ (load_agent(a.runs) * 0x9e3779b1u);
+  return g != 0u ? g : 0x2545f491u;
+}
+
+__device__ __forceinline__ void ts_write_invalid(const TsArgs& a, int b) {
+  const int D1 = a.max_depth + 1;
+  for (int k = threadIdx.x; k < D1; k += kThreads) {
+    a.out_tokens[static_cast<size_t>(b) * D1 + k] = -1;
+    a.out_nodes[static_cast<size_t>(b) * D1 + k] = -1;
+  }
+  if (threadIdx.x == 0) a.out_len[b] = -1;
+}
+
+struct TsShared {
+  double mass[kTsMaxSlices];  // slice masses of the current final-draw candidate
+  float o[2][kTsMaxSlices];   // slice row maxima (target, draft) of the current step
+  double s[2][kTsMaxSlices];  // slice exp2 sums
+  double d[kWaves];
+  float f[kWaves];
+  int i[kWaves];
+  int missing, budget, y;
+  double base;
+  float lt[SPEC_MAX_TREE_NODES];  // logits of the current node's children tokens (target row)
+  float ld[SPEC_MAX_TREE_NODES];  // (draft row)
+  int path[SPEC_MAX_TREE_NODES + 1];
+};
+
+// Wait until every workgroup of the sequence has published `tag` in `slot_base[w]`, then
+// copy `nd` doubles (word pairs from word `dw`) and `nf` floats (from word `fw`) of each into
+// shared memory.  False if the wait gave up.
+__device__ __forceinline__ bool ts_gather(const uint64_t* slot_base, int W, uint32_t tag, int nd, int nf,
+                                          TsShared& sh, double* dst_d0, double* dst_d1, float* dst_f0,
+                                          float* dst_f1) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.budget = kTsPollLimit;
+  for (;;) {
+    int missing = 0;
+    if (tid < W) {
+      const uint64_t* sl = slot_base + static_cast<size_t>(tid) * kTsWords;
+      double v;
+      float f;
+      if (nd > 0) {
+        if (ts_get_double(sl + 0, tag, &v)) dst_d0[tid] = v; else missing = 1;
+      }
+      if (nd > 1) {
+        if (ts_get_double(sl + 2, tag, &v)) dst_d1[tid] = v; else missing = 1;
+      }
+      if (nf > 0) {
+        if (ts_get_float(sl + 4, tag, &f)) dst_f0[tid] = f; else missing = 1;
+      }
+      if (nf > 1) {
+        if (ts_get_float(sl + 5, tag, &f)) dst_f1[tid] = f; else missing = 1;
+      }
+    }
+    if (!__syncthreads_or(missing)) return true;
+    if (tid == 0) {
+      __builtin_amdgcn_s_sleep(2);
+      --sh.budget;
+    }
+    __syncthreads();
+    if (sh.budget <= 0) return false;
+  }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  constexpr int kSlice = kThreads * kTsNV * E;  // elements per slice
+  __shared__ TsShared sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int W = a.W;
+  const int b = b0 + static_cast<int>(blockIdx.x) / W;
+  const int w = static_cast<int>(blockIdx.x) % W;
+  const int N1 = a.N1, V = a.V;
+  if (!a.valid[b]) {
+    if (w == 0) ts_write_invalid(a, b);
+    return;
+  }
+  const uint32_t gen = ts_generation(a);
+  const float T = a.temperature[b];
+  const float scale = kLog2e / T;
+  const int32_t* ks = a.kstart + static_cast<size_t>(b) * (N1 + 1);
+  const int32_t* kl = a.klist + static_cast<size_t>(b) * N1;
+  const int32_t* tok = a.token + static_cast<size_t>(b) * N1;
+  const float* ua = a.u_accept + static_cast<size_t>(b) * N1;
+  uint64_t* slots = a.slots + static_cast<size_t>(b) * 2 * W * kTsWords;
+  const size_t rowb = static_cast<size_t>(V) * EL::kBytes;
+  const char* tbase = static_cast<const char*>(a.target) + static_cast<size_t>(b) * N1 * rowb;
+  const char* dbase = static_cast<const char*>(a.draft) + static_cast<size_t>(b) * N1 * rowb;
+  const int sl0 = w * kSlice;
+
+  int step = 0, cur = 0, plen = 0;
+  bool residual = false;            // final draw from the residual (else the bonus from p)
+  double c = 0.0, D = 1.0;          // residual max(0, p - c q) / D
+  float Op = 0.f, Oq = 0.f;
+  double Sp = 1.0, Sq = 1.0;
+  u32x4 rt[kTsNV], rd[kTsNV];
+#pragma unroll
+  for (int j = 0; j < kTsNV; ++j) rd[j] = u32x4{0u, 0u, 0u, 0u};
+
+  for (;;) {
+    __syncthreads();  // every lane is done with the previous node's shared values
+    const int k0 = uniform(ks[cur]);
+    const int m = uniform(ks[cur + 1]) - k0;
+    const char* row_t = tbase + static_cast<size_t>(cur) * rowb;
+    const char* row_d = dbase + static_cast<size_t>(cur) * rowb;
+#pragma unroll
+    for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(row_t, V, sl0 + (j * kThreads + tid) * E);
+    if (m > 0) {
+#pragma unroll
+      for (int j = 0; j < kTsNV; ++j) rd[j] = load_vector<DT, VEC>(row_d, V, sl0 + (j * kThreads + tid) * E);
+    }
+    for (int j = tid; j < m; j += kThreads) {
+      const int x = tok[kl[k0 + j]];
+      sh.lt[j] = EL::value(row_t, x);
+      sh.ld[j] = EL::value(row_d, x);
+    }
+    // ---- this slice's row maxima and exp2 sums (target, and draft when the node has children)
+    float mt = -INFINITY, md = -INFINITY;
+    ts_fresh(rt);
+    ts_fresh(rd);
+#pragma unroll
+    for (int j = 0; j < kTsNV; ++j) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        mt = fmaxf(mt, EL::get(rt[j], i));
+        if (m > 0) md = fmaxf(md, EL::get(rd[j], i));
+      }
+      ts_vector_done();
+    }
+    const float ot = block_max(mt, sh.f) * scale;
+    const float od = m > 0 ? block_max(md, sh.f) * scale : -INFINITY;
+    float st = 0.f, sd = 0.f;
+    ts_fresh(rt);
+    ts_fresh(rd);
+    if (ot > -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kTsNV; ++j) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) st += exp2_fast(fmaf(EL::get(rt[j], i), scale, -ot));
+        ts_vector_done();
+      }
+    }
+    if (m > 0 && od > -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kTsNV; ++j) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) sd += exp2_fast(fmaf(EL::get(rd[j], i), scale, -od));
+        ts_vector_done();
+      }
+    }
+    const double St = block_sum(static_cast<double>(st), sh.d);
+    const double Sd = m > 0 ? block_sum(static_cast<double>(sd), sh.d) : 0.0;
+    uint64_t* mine = slots + (static_cast<size_t>(step & 1) * W + w) * kTsWords;
+    uint32_t tag = ts_tag(gen, step);
+    if (tid == 0) {
+      ts_put_double(mine + 0, St, tag);
+      ts_put_double(mine + 2, Sd, tag);
+      store_agent(mine + 4, ts_word(__float_as_uint(ot), tag));
+      store_agent(mine + 5, ts_word(__float_as_uint(od), tag));
+    }
+    if (!ts_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, 2, 2, sh, sh.s[0], sh.s[1],
+                   sh.o[0], sh.o[1])) {
+      ts_write_invalid(a, b);
+      return;
+    }
+    ++step;
+    // ---- the node's p and q: combined in slice order, the same in every workgroup
+    Op = -INFINITY;
+    Oq = -INFINITY;
+    for (int q = 0; q < W; ++q) {
+      Op = fmaxf(Op, sh.o[0][q]);
+      Oq = fmaxf(Oq, sh.o[1][q]);
+    }
+    Sp = 0.0;
+    Sq = 0.0;
+    for (int q = 0; q < W; ++q) {
+      const double mp = sh.o[0][q] > -INFINITY ? sh.s[0][q] * static_cast<double>(exp2_fast(sh.o[0][q] - Op)) : 0.0;
+      Sp += mp;
+      if (tid == 0) sh.mass[q] = mp;  // bonus draw candidate: slice masses of p (scaled by Sp)
+      if (m > 0 && sh.o[1][q] > -INFINITY) Sq += sh.s[1][q] * static_cast<double>(exp2_fast(sh.o[1][q] - Oq));
+    }
+    // every lane holds the same values: keep them in scalar registers
+    Op = uniform(Op);
+    Oq = uniform(Oq);
+    Sp = uniform(Sp);
+    Sq = uniform(Sq);
+    __syncthreads();
+    if (m == 0) {
+      residual = false;
+      break;
+    }
+    // ---- the children in node order against the residual
+    c = 0.0;
+    D = 1.0;
+    bool moved = false;
+    for (int j = 0; j < m; ++j) {
+      const int kid = uniform(kl[k0 + j]);
+      const double px = static_cast<double>(exp2_fast(fmaf(uniform(sh.lt[j]), scale, -Op))) / Sp;
+      const double qx = static_cast<double>(exp2_fast(fmaf(uniform(sh.ld[j]), scale, -Oq))) / Sq;
+      const double rx = fmax(0.0, px - c * qx) / D;
+      const double alpha = uniform(qx > 0.0 ? fmin(1.0, rx / qx) : (rx > 0.0 ? 1.0 : 0.0));
+      if (static_cast<double>(ua[kid]) <= alpha) {
+        if (plen >= a.max_depth) {  // the path outgrows its output row
+          if (w == 0) ts_write_invalid(a, b);
+          return;
+        }
+        if (tid == 0) sh.path[plen] = kid;
+        ++plen;
+        cur = kid;
+        moved = true;
+        break;
+      }
+      // rejected: D' = sum over the vocabulary of max(0, p - c' q), c' = c + D
+      const double cn = c + D;
+      const float cf = static_cast<float>(cn);
+      const float ip = static_cast<float>(1.0 / Sp), iq = static_cast<float>(1.0 / Sq);
+      float acc = 0.f;
+      ts_fresh(rt);
+      ts_fresh(rd);
+#pragma unroll
+      for (int jj = 0; jj < kTsNV; ++jj) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const float pv = exp2_fast(fmaf(EL::get(rt[jj], i), scale, -Op)) * ip;
+          const float qv = exp2_fast(fmaf(EL::get(rd[jj], i), scale, -Oq)) * iq;
+          acc += fmaxf(0.f, pv - cf * qv);
+        }
+        ts_vector_done();
+      }
+      const double part = block_sum(static_cast<double>(acc), sh.d);
+      mine = slots + (static_cast<size_t>(step & 1) * W + w) * kTsWords;
+      tag = ts_tag(gen, step);
+      if (tid == 0) ts_put_double(mine, part, tag);
+      double* tmp = sh.s[0];  // reuse: the stats of this node are combined already
+      if (!ts_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, 1, 0, sh, tmp, nullptr,
+                     nullptr, nullptr)) {
+        ts_write_invalid(a, b);
+        return;
+      }
+      ++step;
+      double Dn = 0.0;
+      for (int q = 0; q < W; ++q) Dn += tmp[q];
+      Dn = uniform(Dn);
+      if (Dn > 0.0) {  // else no mass left after rounding: keep the previous residual (p at first)
+        c = cn;
+        D = Dn;
+        residual = true;
+        __syncthreads();
+        if (tid < W) sh.mass[tid] = tmp[tid];
+      }
+      __syncthreads();
+    }
+    if (!moved) break;
+    residual = false;
+  }
+  // After the loop: a leaf reached by acceptance (bonus from p; residual == false), or
+  // every child of `cur` rejected (draw from max(0, p - c q) / D; if no residual ever had
+  // mass, c = 0 and the draw is from p).
+  const bool use_q = residual;
+  const double total = [&] {
+    double t = 0.0;
+    for (int q = 0; q < W; ++q) t += sh.mass[q];
+    return t;
+  }();
+  const double tt = uniform(static_cast<double>(a.u_final[b]) * total);
+  int wsel = -1, wlast = -1;
+  {
+    double run = 0.0;
+    for (int q = 0; q < W; ++q) {
+      run += sh.mass[q];
+      if (sh.mass[q] > 0.0) {
+        wlast = q;
+        if (wsel < 0 && run >= tt) wsel = q;
+      }
+    }
+    if (wsel < 0) wsel = wlast >= 0 ? wlast : 0;
+  }
+  if (w != wsel) return;
+  double before = 0.0;
+  for (int q = 0; q < wsel; ++q) before += sh.mass[q];
+  const double t_loc = uniform(tt - before);
+  const float ip = static_cast<float>(1.0 / Sp), iq = static_cast<float>(1.0 / Sq);
+  const float cf = static_cast<float>(c);
+  // draw weights in the same scale as the slice masses: p's masses are sums of
+  // exp2(l * scale - Op); residual masses are sums of max(0, p - c q)
+  auto weight = [&](float l_t, float l_d) -> float {
+    const float et = exp2_fast(fmaf(l_t, scale, -Op));
+    if (!use_q) return et;
+    const float pv = et * ip;
+    const float qv = exp2_fast(fmaf(l_d, scale, -Oq)) * iq;
+    return fmaxf(0.f, pv - cf * qv);
+  };
+  // the vector round j holding t_loc (rounds are vocabulary-ordered inside the slice)
+  ts_fresh(rt);
+  ts_fresh(rd);
+  double rb = 0.0;
+  int jsel = -1, jlast = -1;
+  double jbase = 0.0;
+  for (int j = 0; j < kTsNV; ++j) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) s += weight(EL::get(rt[j], i), EL::get(rd[j], i));
+    const double tot = block_sum(static_cast<double>(s), sh.d);
+    if (tot > 0.0) {
+      jlast = j;
+      if (jsel < 0 && rb + tot >= t_loc) {
+        jsel = j;
+        jbase = rb;
+      }
+    }
+    rb += tot;
+  }
+  if (jsel < 0) {  // rounding left t_loc above the slice total: its last round with mass
+    jsel = jlast >= 0 ? jlast : 0;
+    jbase = 0.0;
+    for (int j = 0; j < jsel; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) s += weight(EL::get(rt[j], i), EL::get(rd[j], i));
+      jbase += block_sum(static_cast<double>(s), sh.d);
+    }
+  }
+  const double t_round = t_loc - jbase;
+  // the lane, then the element
+  u32x4 vt = rt[0], vd = rd[0];
+#pragma unroll
+  for (int j = 1; j < kTsNV; ++j)
+    if (j == jsel) {
+      vt = rt[j];
+      vd = rd[j];
+    }
+  const int e0 = sl0 + (jsel * kThreads + tid) * E;
+  float wl[E];
+  float lsum = 0.f;
+  int last_pos = -1;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    wl[i] = e0 + i < V ? weight(EL::get(vt, i), EL::get(vd, i)) : 0.f;
+    lsum += wl[i];
+    last_pos = wl[i] > 0.f ? e0 + i : last_pos;
+  }
+  const double lincl = wave_inclusive_scan(static_cast<double>(lsum));
+  __syncthreads();
+  if (lane == 63) sh.d[wv] = lincl;
+  __syncthreads();
+  double lbefore = lincl - static_cast<double>(lsum);
+  for (int i = 0; i < wv; ++i) lbefore += sh.d[i];
+  const int key = (lsum > 0.f && lbefore + static_cast<double>(lsum) >= t_round) ? tid : INT_MAX;
+  const int kmin = block_min_int(key, sh.i);
+  int y;
+  if (kmin == INT_MAX) {
+    y = block_max_int(last_pos, sh.i);
+    if (y < 0) y = sl0;
+  } else {
+    if (tid == kmin) {
+      double run = lbefore;
+      int pick = -1;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        run += wl[i];
+        if (pick < 0 && wl[i] > 0.f && run >= t_round) pick = e0 + i;
+      }
+      sh.y = pick >= 0 ? pick : last_pos;
+    }
+    __syncthreads();
+    y = sh.y;
+  }
+  const int D1 = a.max_depth + 1;
+  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * D1;
+  int32_t* on = a.out_nodes + static_cast<size_t>(b) * D1;
+  for (int k = tid; k < D1; k += kThreads) {
+    const int node = k < plen ? sh.path[k] : -1;
+    on[k] = node;
+    ot[k] = k < plen ? tok[node] : (k == plen ? y : -1);
+  }
+  if (tid == 0) a.out_len[b] = plen;
+}
+
+// ---------------------------------------------------------------- host
+struct TsLayout {
+  size_t off_valid, off_kstart, off_klist, off_slots, bytes;
+  int W;
+};
+
+static TsLayout ts_layout(int B, int N1, int V, spec_dtype_t dtype) {
+  TsLayout L{};
+  const int E = dtype == SPEC_BF16 ? 8 : 4;
+  const long long slice = static_cast<long long>(kThreads) * kTsNV * E;
+  L.W = static_cast<int>((V + slice - 1) / slice);
+  size_t off = 256;  // run counter
+  L.off_valid = off;
+  off = align_up(off + sizeof(int32_t) * B, 256);
+  L.off_kstart = off;
+  off = align_up(off + sizeof(int32_t) * static_cast<size_t>(B) * (N1 + 1), 256);
+  L.off_klist = off;
+  off = align_up(off + sizeof(int32_t) * static_cast<size_t>(B) * N1, 256);
+  L.off_slots = off;
+  off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * 2 * L.W * kTsWords, 256);
+  L.bytes = off;
+  return L;
+}
+
+template <int DT, bool VEC>
+static int ts_slots_per_device() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(ts_walk_kernel<DT, VEC>),
+                                                   kThreads, 0) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 1;
+  v = per_cu * cus;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+static uint32_t ts_next_generation() {
+  static std::atomic<uint32_t> counter{0x6a09e667u};
+  uint32_t g = counter.fetch_add(0x9e3779b9u, std::memory_order_relaxed);
+  return g != 0u ? g : 0x2545f491u;
+}
+
+template <int DT, bool VEC>
+static spec_status_t ts_launch(const TsArgs& a, hipStream_t s) {
+  const int slots = ts_slots_per_device<DT, VEC>();
+  const int per_launch = (slots / 2) / a.W;
+  if (per_launch < 1) return fail(SPEC_ERR_UNSUPPORTED, "V needs %d workgroups per sequence, more than fit", a.W);
+  {
+    LaunchScope scope("ts_prep", s);
+    scope.launch(ts_prep_kernel, dim3(static_cast<unsigned>(a.B)), dim3(kThreads), s, a);
+    const spec_status_t st = scope.finish();
+    if (st != SPEC_OK) return st;
+  }
+  for (int b0 = 0; b0 < a.B; b0 += per_launch) {
+    const int nb = a.B - b0 < per_launch ? a.B - b0 : per_launch;
+    LaunchScope scope("ts_walk", s);
+    scope.launch(ts_walk_kernel<DT, VEC>, dim3(static_cast<unsigned>(nb * a.W)), dim3(kThreads), s, a, b0);
+    const spec_status_t st = scope.finish();
+    if (st != SPEC_OK) return st;
+  }
+  return SPEC_OK;
+}
+
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" {
+
+size_t spec_verify_tree_workspace_size(int B, int N1, int V, spec_dtype_t dtype) {
+  if (B <= 0 || N1 < 1 || N1 > SPEC_MAX_TREE_NODES || V < 1 || (dtype != SPEC_F32 && dtype != SPEC_BF16)) return 0;
+  const TsLayout L = ts_layout(B, N1, V, dtype);
+  if (L.W > kTsMaxSlices) return 0;
+  return L.bytes;
+}
+
+spec_status_t spec_verify_tree(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                               const int32_t* parent, const int32_t* node_token, const float* temperature,
+                               const float* u_accept, const float* u_final, int B, int N1, int V, int max_depth,
+                               int32_t* out_accept_len, int32_t* out_tokens, int32_t* out_path_nodes,
+                               void* workspace, size_t workspace_bytes, spec_stream_t stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 0 || N1 < 1 || V < 1 || max_depth < 0)
+    return fail(SPEC_ERR_INVALID_ARG, "need B >= 0, N1 >= 1, V >= 1, max_depth >= 0");
+  if (N1 > SPEC_MAX_TREE_NODES) return fail(SPEC_ERR_UNSUPPORTED, "N1 = %d exceeds SPEC_MAX_TREE_NODES", N1);
+  if (max_depth > N1) return fail(SPEC_ERR_INVALID_ARG, "max_depth = %d exceeds N1 = %d", max_depth, N1);
+  const TsLayout L = ts_layout(B > 0 ? B : 1, N1, V, dtype);
+  if (L.W > kTsMaxSlices) return fail(SPEC_ERR_UNSUPPORTED, "V = %d needs more than %d slices", V, kTsMaxSlices);
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !draft_logits || !parent || !node_token || !temperature || !u_accept || !u_final ||
+      !out_accept_len || !out_tokens || !out_path_nodes)
+    return fail(SPEC_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (static_cast<double>(B) * N1 * V >= 140737488355328.0) return fail(SPEC_ERR_UNSUPPORTED, "B*N1*V too large");
+  if (!workspace) return fail(SPEC_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(SPEC_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (workspace_bytes < L.bytes)
+    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.bytes);
+  TsArgs a{};
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.parent = parent;
+  a.token = node_token;
+  a.temperature = temperature;
+  a.u_accept = u_accept;
+  a.u_final = u_final;
+  a.B = B;
+  a.N1 = N1;
+  a.V = V;
+  a.max_depth = max_depth;
+  a.W = L.W;
+  a.out_len = out_accept_len;
+  a.out_tokens = out_tokens;
+  a.out_nodes = out_path_nodes;
+  a.gen = ts_next_generation();
+  char* ws = static_cast<char*>(workspace);
+  a.runs = reinterpret_cast<uint32_t*>(ws);
+  a.valid = reinterpret_cast<int32_t*>(ws + L.off_valid);
+  a.kstart = reinterpret_cast<int32_t*>(ws + L.off_kstart);
+  a.klist = reinterpret_cast<int32_t*>(ws + L.off_klist);
+  a.slots = reinterpret_cast<uint64_t*>(ws + L.off_slots);
+  const int esize = dtype == SPEC_BF16 ? 2 : 4;
+  const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits) && aligned16(draft_logits);
+  if (dtype == SPEC_BF16) return vec ? ts_launch<kBF16, true>(a, s) : ts_launch<kBF16, false>(a, s);
+  return vec ? ts_launch<kF32, true>(a, s) : ts_launch<kF32, false>(a, s);
+}
+
+}  // extern "C"

@@ -8,6 +8,7 @@
  *
  *   spec_verify_chain        modified rejection sampling of a chain of drafts
  *   spec_verify_tree_greedy  greedy acceptance of the longest matching tree path
+ *   spec_verify_tree         stochastic (T > 0) tree verification against residuals
  *   ngram_propose            prompt n-gram lookup drafting (one-hot draft q)
  *   spec_tree_mask           2-D tree-attention mask and node depths of a draft tree
  *   spec_commit_path         copy the accepted path's cache entries into the KV cache
@@ -179,6 +180,47 @@ spec_status_t spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dt
                                       int32_t* out_accept_len, int32_t* out_tokens, int32_t* out_path_nodes,
                                       int32_t* out_argmax,
                                       void* workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Stochastic tree verification (temperature > 0).
+ *
+ * [Production] section I.1 (accept with min(1, p/q), else draw from the normalised
+ * residual max(0, p - q)) and section III.2 (a rejected branch B1 leaves its sibling
+ * B2 free to be accepted).  The pages give the rule for a single drafted token only;
+ * reading, from the published multi-candidate form of it: the children of a node
+ * were drawn independently from the draft distribution q at that node and are tried
+ * in node order against a residual r (r = p at first; after a rejection
+ * r <- max(0, r - q) normalised).  An accepted child continues the walk; when every
+ * child of a node is rejected a token is drawn from the last residual; a leaf reached
+ * by acceptance yields a bonus token from its own p.  A chain-shaped tree is exactly
+ * spec_verify_chain.  Temperature 0 (greedy) is spec_verify_tree_greedy.
+ *
+ * target_logits [B, N1, V] dtype: row i = target logits after node i (row 0 = root).
+ * draft_logits  [B, N1, V] dtype: row i = draft logits that node i's children were
+ *               drawn from (rows of leaves are never read).
+ * parent, node_token as for spec_verify_tree_greedy.
+ * temperature   [B] float32, > 0.
+ * u_accept      [B, N1] float32 in (0, 1]: the uniform of node i's accept test
+ *               (entry 0 unused).
+ * u_final       [B] float32 in (0, 1]: the uniform of the final draw.
+ * out_accept_len, out_tokens, out_path_nodes as for spec_verify_tree_greedy (the
+ *               last token is the residual draw or the bonus).
+ * workspace     >= spec_verify_tree_workspace_size() bytes, 256-byte aligned.
+ *
+ * Only the rows on the walk are read.  Invalid device data for sequence b (bad
+ * parent, token out of range, temperature not > 0 or not finite, a uniform outside
+ * (0, 1], accepted depth > max_depth) sets out_accept_len[b] = -1 and its outputs to
+ * -1.  Each used row needs a finite logit.
+ * Limits: 1 <= N1 <= SPEC_MAX_TREE_NODES, 0 <= max_depth <= N1, V at most 64 slices
+ * (1048576 bf16 or 524288 fp32 logits).
+ * ------------------------------------------------------------------------- */
+size_t spec_verify_tree_workspace_size(int B, int N1, int V, spec_dtype_t dtype);
+
+spec_status_t spec_verify_tree(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                               const int32_t* parent, const int32_t* node_token, const float* temperature,
+                               const float* u_accept, const float* u_final, int B, int N1, int V, int max_depth,
+                               int32_t* out_accept_len, int32_t* out_tokens, int32_t* out_path_nodes,
+                               void* workspace, size_t workspace_bytes, spec_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Prompt n-gram lookup drafting.

@@ -21,6 +21,9 @@ from .workloads import (  # noqa: F401
     tree_inputs,
     tree_config_eagle_bf16,
     tree_parents,
+    SampledTreeInputs,
+    tree_sampled_inputs,
+    tree_sampled_config_bf16,
     random_parents,
     kv_entries,
     commit_requests,

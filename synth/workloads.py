@@ -354,6 +354,95 @@ def tree_config_eagle_bf16(seed: int = 0, B: int = 32, n_nodes: int = 60, depth:
                        boost=10.0, p_boost=0.7, **kw)
 
 
+@dataclass
+class SampledTreeInputs:
+    """target, draft: [B, N1, V] (row i = logits after node i; draft row i is the
+    distribution node i's children were drawn from); parent, node_token [B, N1] int32;
+    temperature [B]; u_accept [B, N1]; u_final [B]."""
+
+    target: np.ndarray
+    draft: np.ndarray
+    dtype: str
+    parent: np.ndarray
+    node_token: np.ndarray
+    temperature: np.ndarray
+    u_accept: np.ndarray
+    u_final: np.ndarray
+    max_depth: int
+    name: str = ""
+
+    @property
+    def B(self) -> int:
+        return int(self.target.shape[0])
+
+    @property
+    def N1(self) -> int:
+        return int(self.target.shape[1])
+
+    @property
+    def V(self) -> int:
+        return int(self.target.shape[2])
+
+
+def tree_sampled_inputs(seed: int, *, B: int, n_nodes: int, depth: int, V: int, dtype: str = "bf16",
+                        target_sigma: float = 3.0, draft_sigma: float = 0.7, temperature: float = 0.8,
+                        peaks: int = 20, peak_shift: float = 8.0, max_branch: int = 4, parent=None,
+                        name: str = "", threads: Optional[int] = None) -> SampledTreeInputs:
+    """Random draft trees (the shapes of tree_inputs unless `parent` is given); target rows
+    N(0, target_sigma^2) with `peaks` tokens per row shifted by `peak_shift`; draft rows =
+    target + N(0, draft_sigma^2); the children of every node drawn independently from
+    softmax(draft row / T) of that node (Gumbel-max on the stored values)."""
+    store = np.uint16 if dtype == "bf16" else np.float32
+    if parent is None:
+        parent = np.stack([_tree_shape(philox(seed, "tree_shape", b), n_nodes, depth, max_branch) for b in range(B)])
+    parent = np.asarray(parent, dtype=np.int32)
+    N1 = parent.shape[1]
+    target = np.empty((B, N1, V), dtype=store)
+    draft = np.empty((B, N1, V), dtype=store)
+    node_token = np.zeros((B, N1), dtype=np.int32)
+    u_acc = np.empty((B, N1), dtype=np.float32)
+    u_fin = np.empty((B,), dtype=np.float32)
+
+    def one(b: int) -> None:
+        t = philox(seed, "target", b).standard_normal((N1, V), dtype=np.float32)
+        t *= np.float32(target_sigma)
+        if peaks:
+            rp = philox(seed, "peaks", b)
+            for r in range(N1):
+                idx = rp.choice(V, size=min(peaks, V), replace=False)
+                t[r, idx] += np.float32(peak_shift)
+        d = philox(seed, "draft_noise", b).standard_normal((N1, V), dtype=np.float32)
+        d *= np.float32(draft_sigma)
+        d += t
+        if dtype == "bf16":
+            target[b] = bf16_bits_from_f32(t)
+            draft[b] = bf16_bits_from_f32(d)
+            d_seen = f32_from_bf16_bits(draft[b])
+        else:
+            target[b] = t
+            draft[b] = d
+            d_seen = d
+        rs = philox(seed, "draft_sample", b)
+        for i in range(1, N1):
+            node_token[b, i] = _gumbel_argmax(rs, d_seen[parent[b, i]], temperature)
+        u_acc[b] = uniforms_open_closed(philox(seed, "u_accept", b), (N1,))
+        u_fin[b] = uniforms_open_closed(philox(seed, "u_final", b), (1,))[0]
+
+    _parallel(one, B, threads)
+    return SampledTreeInputs(target=target, draft=draft, dtype=dtype, parent=parent, node_token=node_token,
+                             temperature=np.full((B,), temperature, dtype=np.float32), u_accept=u_acc,
+                             u_final=u_fin, max_depth=depth,
+                             name=name or f"tree_sampled_{dtype}_B{B}_N{N1 - 1}_V{V}")
+
+
+def tree_sampled_config_bf16(seed: int = 0, B: int = 32, n_nodes: int = 60, depth: int = 6, V: int = 128256,
+                             **kw) -> SampledTreeInputs:
+    """Stochastic tree verify, bf16: the greedy workload's tree shapes (60 nodes, depth 6,
+    branching {1..4}) with the high-acceptance chain recipe per node (target N(0, 3^2) +
+    20 peaks at +8, draft = target + N(0, 0.7^2), T = 0.8); children drawn from q."""
+    return tree_sampled_inputs(seed, B=B, n_nodes=n_nodes, depth=depth, V=V, dtype="bf16", **kw)
+
+
 def tree_parents(seed: int = 0, *, B: int = 32, n_nodes: int = 60, depth: int = 6, max_branch: int = 4) -> np.ndarray:
     """The topologies of tree_inputs(seed, ...) alone: parent [B, n_nodes + 1] int32."""
     return np.stack([_tree_shape(philox(seed, "tree_shape", b), n_nodes, depth, max_branch) for b in range(B)])
