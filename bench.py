@@ -269,6 +269,9 @@ def other_workloads(warmup, steps, dev):
     out.append(_entry("tree_greedy_B32_N60_V128256_bf16", dict(ms=ms, bytes=tb, kernels=kms, steps=steps),
                       tr0.B * (tr0.N1 - 1)))
 
+    # stochastic tree verification, B=32 N=60 V=128256 bf16, T=0.8
+    out.append(tree_sampled_workload(warmup, steps, dev))
+
     # the steps on either side of tree verification, on the same workload's trees
     out += tree_io_workloads(warmup, steps, dev, tree_parents, tree_paths)
 
@@ -310,6 +313,54 @@ def other_workloads(warmup, steps, dev):
     out.append(_entry("ngram_propose_verify_B128_L4096_K5_V32000_bf16", dict(ms=ms, bytes=nb, kernels=kms, steps=steps),
                       128 * 5))
     return out
+
+
+def tree_sampled_workload(warmup, steps, dev):
+    """Stochastic tree verification on the greedy workload's tree shapes with the
+    high-acceptance chain recipe per node.  Algorithmic bytes: the rows the walk needs,
+    i.e. the target rows of the root and the accepted nodes and the draft rows of those
+    of them that have children."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_09_amd as sv
+    import synth
+
+    x0 = synth.tree_sampled_config_bf16(0)
+    per = x0.target.nbytes + x0.draft.nbytes
+    n_sets = sets_needed(per)
+    progress(f"tree_sampled: generating {n_sets} input sets")
+    prepared, moved = [], []
+    for s in range(n_sets):
+        x = x0 if s == 0 else synth.tree_sampled_config_bf16(s)
+        args = (to_dev(x.target, "bf16", dev), to_dev(x.draft, "bf16", dev), torch.from_numpy(x.parent).to(dev),
+                torch.from_numpy(x.node_token).to(dev), torch.from_numpy(x.temperature).to(dev),
+                torch.from_numpy(x.u_accept).to(dev), torch.from_numpy(x.u_final).to(dev))
+        pc = sv.prepare_spec_verify_tree(*args, x.max_depth)
+        r = pc()
+        torch.cuda.synchronize()
+        rows = 0
+        nodes = r.path_nodes.cpu().numpy()
+        acc = r.accept_len.cpu().numpy()
+        for b in range(x.B):
+            visited = [0] + [int(v) for v in nodes[b, : max(0, acc[b])]]
+            has_kids = set(int(p) for p in x.parent[b, 1:])
+            rows += len(visited) + sum(1 for v in visited if v in has_kids)
+        moved.append(rows * x.V * 2)
+        prepared.append(pc)
+        del x
+
+    def call(i):
+        prepared[i]()
+
+    ms, _ = time_calls(call, n_sets, warmup, steps, False)
+    _, kms = time_calls(call, n_sets, 2, steps, True)
+    r = _entry("tree_sampled_B32_N60_V128256_bf16", dict(ms=ms, bytes=int(np.mean(moved)), kernels=kms, steps=steps),
+               x0.B * (x0.N1 - 1))
+    r["rows_read_per_call"] = int(np.mean(moved)) // (x0.V * 2)
+    del prepared
+    torch.cuda.empty_cache()
+    return r
 
 
 def tree_io_workloads(warmup, steps, dev, parents, paths):
