@@ -107,6 +107,47 @@ __device__ __forceinline__ bool ts_get_float(const uint64_t* w, uint32_t tag, fl
   return static_cast<uint32_t>(x >> 32) == tag;
 }
 
+// Two workgroup reductions with one exchange through shared memory (lds: 2 * kWaves).
+__device__ __forceinline__ void ts_block_max2(float& x, float& y, float* lds) {
+  x = wave_max(x);
+  y = wave_max(y);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    lds[w] = x;
+    lds[kWaves + w] = y;
+  }
+  __syncthreads();
+  float rx = lds[0], ry = lds[kWaves];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) {
+    rx = fmaxf(rx, lds[i]);
+    ry = fmaxf(ry, lds[kWaves + i]);
+  }
+  x = rx;
+  y = ry;
+}
+
+__device__ __forceinline__ void ts_block_sum2(double& x, double& y, double* lds) {
+  x = wave_sum(x);
+  y = wave_sum(y);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    lds[w] = x;
+    lds[kWaves + w] = y;
+  }
+  __syncthreads();
+  double rx = 0.0, ry = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    rx += lds[i];
+    ry += lds[kWaves + i];
+  }
+  x = rx;
+  y = ry;
+}
+
 // ---------------------------------------------------------------- prep
 __global__ __launch_bounds__(kThreads) void ts_prep_kernel(TsArgs a) {
   __shared__ int s_par[SPEC_MAX_TREE_NODES];
@@ -180,14 +221,19 @@ struct TsShared {
   double mass[kTsMaxSlices];  // slice masses of the current final-draw candidate
   float o[2][kTsMaxSlices];   // slice row maxima (target, draft) of the current step
   double s[2][kTsMaxSlices];  // slice exp2 sums
-  double d[kWaves];
-  float f[kWaves];
+  double d[2 * kWaves];
+  float f[2 * kWaves];
   int i[kWaves];
   int missing, budget, y;
   double base;
   float lt[SPEC_MAX_TREE_NODES];  // logits of the current node's children tokens (target row)
   float ld[SPEC_MAX_TREE_NODES];  // (draft row)
   int path[SPEC_MAX_TREE_NODES + 1];
+  // the sequence's topology, tokens and uniforms, staged once
+  int ks[SPEC_MAX_TREE_NODES + 1];
+  int kl[SPEC_MAX_TREE_NODES];
+  int tok[SPEC_MAX_TREE_NODES];
+  float ua[SPEC_MAX_TREE_NODES];
 };
 
 // Wait until every workgroup of the sequence has published `tag` in `slot_base[w]`, then
@@ -247,10 +293,20 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
   const uint32_t gen = ts_generation(a);
   const float T = a.temperature[b];
   const float scale = kLog2e / T;
-  const int32_t* ks = a.kstart + static_cast<size_t>(b) * (N1 + 1);
-  const int32_t* kl = a.klist + static_cast<size_t>(b) * N1;
-  const int32_t* tok = a.token + static_cast<size_t>(b) * N1;
-  const float* ua = a.u_accept + static_cast<size_t>(b) * N1;
+  {
+    const int32_t* ks = a.kstart + static_cast<size_t>(b) * (N1 + 1);
+    const int32_t* kl = a.klist + static_cast<size_t>(b) * N1;
+    const int32_t* tok = a.token + static_cast<size_t>(b) * N1;
+    const float* ua = a.u_accept + static_cast<size_t>(b) * N1;
+    for (int i = tid; i <= N1; i += kThreads) {
+      sh.ks[i] = ks[i];
+      if (i < N1) {
+        sh.kl[i] = kl[i];
+        sh.tok[i] = tok[i];
+        sh.ua[i] = ua[i];
+      }
+    }
+  }
   uint64_t* slots = a.slots + static_cast<size_t>(b) * 2 * W * kTsWords;
   const size_t rowb = static_cast<size_t>(V) * EL::kBytes;
   const char* tbase = static_cast<const char*>(a.target) + static_cast<size_t>(b) * N1 * rowb;
@@ -268,8 +324,8 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
 
   for (;;) {
     __syncthreads();  // every lane is done with the previous node's shared values
-    const int k0 = uniform(ks[cur]);
-    const int m = uniform(ks[cur + 1]) - k0;
+    const int k0 = uniform(sh.ks[cur]);
+    const int m = uniform(sh.ks[cur + 1]) - k0;
     const char* row_t = tbase + static_cast<size_t>(cur) * rowb;
     const char* row_d = dbase + static_cast<size_t>(cur) * rowb;
 #pragma unroll
@@ -279,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
       for (int j = 0; j < kTsNV; ++j) rd[j] = load_vector<DT, VEC>(row_d, V, sl0 + (j * kThreads + tid) * E);
     }
     for (int j = tid; j < m; j += kThreads) {
-      const int x = tok[kl[k0 + j]];
+      const int x = sh.tok[sh.kl[k0 + j]];
       sh.lt[j] = EL::value(row_t, x);
       sh.ld[j] = EL::value(row_d, x);
     }
@@ -296,29 +352,36 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
       }
       ts_vector_done();
     }
-    const float ot = block_max(mt, sh.f) * scale;
-    const float od = m > 0 ? block_max(md, sh.f) * scale : -INFINITY;
+    ts_block_max2(mt, md, sh.f);
+    const float ot = mt * scale;
+    const float od = m > 0 ? md * scale : -INFINITY;
     float st = 0.f, sd = 0.f;
     ts_fresh(rt);
     ts_fresh(rd);
     if (ot > -INFINITY) {
+      float st2 = 0.f;
 #pragma unroll
-      for (int j = 0; j < kTsNV; ++j) {
+      for (int j = 0; j < kTsNV; ++j)
 #pragma unroll
-        for (int i = 0; i < E; ++i) st += exp2_fast(fmaf(EL::get(rt[j], i), scale, -ot));
-        ts_vector_done();
-      }
+        for (int i = 0; i < E; i += 2) {
+          st += exp2_fast(fmaf(EL::get(rt[j], i), scale, -ot));
+          st2 += exp2_fast(fmaf(EL::get(rt[j], i + 1), scale, -ot));
+        }
+      st += st2;
     }
     if (m > 0 && od > -INFINITY) {
+      float sd2 = 0.f;
 #pragma unroll
-      for (int j = 0; j < kTsNV; ++j) {
+      for (int j = 0; j < kTsNV; ++j)
 #pragma unroll
-        for (int i = 0; i < E; ++i) sd += exp2_fast(fmaf(EL::get(rd[j], i), scale, -od));
-        ts_vector_done();
-      }
+        for (int i = 0; i < E; i += 2) {
+          sd += exp2_fast(fmaf(EL::get(rd[j], i), scale, -od));
+          sd2 += exp2_fast(fmaf(EL::get(rd[j], i + 1), scale, -od));
+        }
+      sd += sd2;
     }
-    const double St = block_sum(static_cast<double>(st), sh.d);
-    const double Sd = m > 0 ? block_sum(static_cast<double>(sd), sh.d) : 0.0;
+    double St = static_cast<double>(st), Sd = static_cast<double>(sd);
+    ts_block_sum2(St, Sd, sh.d);
     uint64_t* mine = slots + (static_cast<size_t>(step & 1) * W + w) * kTsWords;
     uint32_t tag = ts_tag(gen, step);
     if (tid == 0) {
@@ -333,26 +396,20 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
       return;
     }
     ++step;
-    // ---- the node's p and q: combined in slice order, the same in every workgroup
-    Op = -INFINITY;
-    Oq = -INFINITY;
-    for (int q = 0; q < W; ++q) {
-      Op = fmaxf(Op, sh.o[0][q]);
-      Oq = fmaxf(Oq, sh.o[1][q]);
+    // ---- the node's p and q: lane q of every wave takes slice q, and the wave reductions
+    // (a fixed DPP order) give the same values in every wave of every workgroup
+    {
+      const float o0 = lane < W ? sh.o[0][lane] : -INFINITY;
+      const float o1 = lane < W && m > 0 ? sh.o[1][lane] : -INFINITY;
+      Op = uniform(wave_max(o0));
+      Oq = uniform(wave_max(o1));
+      const double mp = o0 > -INFINITY ? sh.s[0][lane] * static_cast<double>(exp2_fast(o0 - Op)) : 0.0;
+      const double mq = o1 > -INFINITY ? sh.s[1][lane] * static_cast<double>(exp2_fast(o1 - Oq)) : 0.0;
+      Sp = uniform(wave_sum(mp));
+      Sq = uniform(wave_sum(mq));
+      __syncthreads();
+      if (tid < W) sh.mass[tid] = mp;  // bonus draw candidate: slice masses of p (scaled by Sp)
     }
-    Sp = 0.0;
-    Sq = 0.0;
-    for (int q = 0; q < W; ++q) {
-      const double mp = sh.o[0][q] > -INFINITY ? sh.s[0][q] * static_cast<double>(exp2_fast(sh.o[0][q] - Op)) : 0.0;
-      Sp += mp;
-      if (tid == 0) sh.mass[q] = mp;  // bonus draw candidate: slice masses of p (scaled by Sp)
-      if (m > 0 && sh.o[1][q] > -INFINITY) Sq += sh.s[1][q] * static_cast<double>(exp2_fast(sh.o[1][q] - Oq));
-    }
-    // every lane holds the same values: keep them in scalar registers
-    Op = uniform(Op);
-    Oq = uniform(Oq);
-    Sp = uniform(Sp);
-    Sq = uniform(Sq);
     __syncthreads();
     if (m == 0) {
       residual = false;
@@ -363,12 +420,12 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
     D = 1.0;
     bool moved = false;
     for (int j = 0; j < m; ++j) {
-      const int kid = uniform(kl[k0 + j]);
+      const int kid = uniform(sh.kl[k0 + j]);
       const double px = static_cast<double>(exp2_fast(fmaf(uniform(sh.lt[j]), scale, -Op))) / Sp;
       const double qx = static_cast<double>(exp2_fast(fmaf(uniform(sh.ld[j]), scale, -Oq))) / Sq;
       const double rx = fmax(0.0, px - c * qx) / D;
       const double alpha = uniform(qx > 0.0 ? fmin(1.0, rx / qx) : (rx > 0.0 ? 1.0 : 0.0));
-      if (static_cast<double>(ua[kid]) <= alpha) {
+      if (static_cast<double>(sh.ua[kid]) <= alpha) {
         if (plen >= a.max_depth) {  // the path outgrows its output row
           if (w == 0) ts_write_invalid(a, b);
           return;
@@ -407,9 +464,7 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
         return;
       }
       ++step;
-      double Dn = 0.0;
-      for (int q = 0; q < W; ++q) Dn += tmp[q];
-      Dn = uniform(Dn);
+      const double Dn = uniform(wave_sum(lane < W ? tmp[lane] : 0.0));
       if (Dn > 0.0) {  // else no mass left after rounding: keep the previous residual (p at first)
         c = cn;
         D = Dn;
@@ -426,11 +481,7 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
   // every child of `cur` rejected (draw from max(0, p - c q) / D; if no residual ever had
   // mass, c = 0 and the draw is from p).
   const bool use_q = residual;
-  const double total = [&] {
-    double t = 0.0;
-    for (int q = 0; q < W; ++q) t += sh.mass[q];
-    return t;
-  }();
+  const double total = uniform(wave_sum(lane < W ? sh.mass[lane] : 0.0));
   const double tt = uniform(static_cast<double>(a.u_final[b]) * total);
   int wsel = -1, wlast = -1;
   {
@@ -540,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
   for (int k = tid; k < D1; k += kThreads) {
     const int node = k < plen ? sh.path[k] : -1;
     on[k] = node;
-    ot[k] = k < plen ? tok[node] : (k == plen ? y : -1);
+    ot[k] = k < plen ? sh.tok[node] : (k == plen ? y : -1);
   }
   if (tid == 0) a.out_len[b] = plen;
 }
