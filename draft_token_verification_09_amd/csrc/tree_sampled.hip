@@ -293,6 +293,16 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
   const uint32_t gen = ts_generation(a);
   const float T = a.temperature[b];
   const float scale = kLog2e / T;
+  const size_t rowb = static_cast<size_t>(V) * EL::kBytes;
+  const char* tbase = static_cast<const char*>(a.target) + static_cast<size_t>(b) * N1 * rowb;
+  const char* dbase = static_cast<const char*>(a.draft) + static_cast<size_t>(b) * N1 * rowb;
+  const int sl0 = w * kSlice;
+  u32x4 rt[kTsNV], rd[kTsNV];
+  // the root's slices first: they depend on nothing staged below
+#pragma unroll
+  for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(tbase, V, sl0 + (j * kThreads + tid) * E);
+#pragma unroll
+  for (int j = 0; j < kTsNV; ++j) rd[j] = load_vector<DT, VEC>(dbase, V, sl0 + (j * kThreads + tid) * E);
   {
     const int32_t* ks = a.kstart + static_cast<size_t>(b) * (N1 + 1);
     const int32_t* kl = a.klist + static_cast<size_t>(b) * N1;
@@ -308,19 +318,12 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
     }
   }
   uint64_t* slots = a.slots + static_cast<size_t>(b) * 2 * W * kTsWords;
-  const size_t rowb = static_cast<size_t>(V) * EL::kBytes;
-  const char* tbase = static_cast<const char*>(a.target) + static_cast<size_t>(b) * N1 * rowb;
-  const char* dbase = static_cast<const char*>(a.draft) + static_cast<size_t>(b) * N1 * rowb;
-  const int sl0 = w * kSlice;
 
   int step = 0, cur = 0, plen = 0;
   bool residual = false;            // final draw from the residual (else the bonus from p)
   double c = 0.0, D = 1.0;          // residual max(0, p - c q) / D
   float Op = 0.f, Oq = 0.f;
   double Sp = 1.0, Sq = 1.0;
-  u32x4 rt[kTsNV], rd[kTsNV];
-#pragma unroll
-  for (int j = 0; j < kTsNV; ++j) rd[j] = u32x4{0u, 0u, 0u, 0u};
 
   for (;;) {
     __syncthreads();  // every lane is done with the previous node's shared values
@@ -328,11 +331,13 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
     const int m = uniform(sh.ks[cur + 1]) - k0;
     const char* row_t = tbase + static_cast<size_t>(cur) * rowb;
     const char* row_d = dbase + static_cast<size_t>(cur) * rowb;
+    if (cur != 0) {  // the root's slices are loaded already
 #pragma unroll
-    for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(row_t, V, sl0 + (j * kThreads + tid) * E);
-    if (m > 0) {
+      for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(row_t, V, sl0 + (j * kThreads + tid) * E);
+      if (m > 0) {
 #pragma unroll
-      for (int j = 0; j < kTsNV; ++j) rd[j] = load_vector<DT, VEC>(row_d, V, sl0 + (j * kThreads + tid) * E);
+        for (int j = 0; j < kTsNV; ++j) rd[j] = load_vector<DT, VEC>(row_d, V, sl0 + (j * kThreads + tid) * E);
+      }
     }
     for (int j = tid; j < m; j += kThreads) {
       const int x = sh.tok[sh.kl[k0 + j]];
