@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_NAME = "libspecverify.so"
-SOURCES = ["host_runtime.hip", "chain.hip", "tree.hip", "ngram.hip", "tree_io.hip", "gate.hip", "tree_sampled.hip"]
+SOURCES = ["host_runtime.hip", "chain.hip", "tree.hip", "ngram.hip", "tree_io.hip", "gate.hip", "tree_walk.hip"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [

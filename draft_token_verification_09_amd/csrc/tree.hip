@@ -20,6 +20,7 @@
 #include "device_common.h"
 #include "host_runtime.h"
 #include "spec_verify.h"
+#include "tree_walk.h"
 
 namespace specv {
 
@@ -254,7 +255,9 @@ extern "C" {
 
 size_t spec_verify_tree_greedy_workspace_size(int B, int N1, int V, spec_dtype_t dtype) {
   if (B <= 0 || N1 < 1 || N1 > SPEC_MAX_TREE_NODES || V < 1) return 0;
-  return tree_layout(B, N1, V, dtype).bytes;
+  const size_t full = tree_layout(B, N1, V, dtype).bytes;
+  const size_t walk = tree_walk_workspace_bytes(B, N1, V, dtype);
+  return full > walk ? full : walk;
 }
 
 spec_status_t spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dtype,
@@ -278,6 +281,10 @@ spec_status_t spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dt
   if (L.C > kStageT) return fail(SPEC_ERR_UNSUPPORTED, "V = %d needs more than %d chunks", V, kStageT);
   if (!workspace) return fail(SPEC_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(SPEC_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  // Without per-node argmaxes only the accepted nodes' rows are needed: walk the tree.
+  if (!out_argmax && tree_walk_workspace_bytes(B, N1, V, dtype) > 0)
+    return tree_greedy_walk(target_logits, dtype, parent, node_token, B, N1, V, max_depth, out_accept_len, out_tokens,
+                            out_path_nodes, workspace, workspace_bytes, s);
   if (workspace_bytes < L.bytes)
     return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.bytes);
   TreeArgs a{};

@@ -23,8 +23,15 @@
 // workgroup combines them in the same order, so all of them take the same decisions.  The
 // workgroup whose slice holds the final draw's point searches it and writes the outputs.
 //
+// The greedy walk (tg_walk) serves spec_verify_tree_greedy when no per-node argmax is
+// asked for: node i is accepted iff its parent is accepted and its token is the argmax
+// of the parent's row, so only the accepted nodes' rows matter.  It keeps the frontier of
+// accepted nodes of the current depth (one node unless siblings repeat a token), finds
+// each frontier node's row argmax across the W slices, and moves to the children that
+// match; the deepest frontier's smallest node ends the path.
+//
 // ts_prep (one workgroup per sequence) validates the inputs and lists every node's
-// children in node order; ts_walk runs the walk.  Its workgroups wait for each other, so
+// children in node order; ts_walk and tg_walk run the walks.  Its workgroups wait for each other, so
 // a launch holds at most half of the workgroups that fit on the device at once, and every
 // wait is bounded.
 #include <atomic>
@@ -32,6 +39,7 @@
 #include "device_common.h"
 #include "host_runtime.h"
 #include "spec_verify.h"
+#include "tree_walk.h"
 
 namespace specv {
 
@@ -60,6 +68,7 @@ struct TsArgs {
   const float* u_accept;
   const float* u_final;
   int B, N1, V, max_depth, W;
+  int greedy;       // no temperature and uniforms (greedy walk)
   int32_t* out_len;
   int32_t* out_tokens;
   int32_t* out_nodes;
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void ts_prep_kernel(TsArgs a) {
   if (b == 0 && tid == 0) __hip_atomic_fetch_add(a.runs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int32_t* par = a.parent + static_cast<size_t>(b) * N1;
   const int32_t* tok = a.token + static_cast<size_t>(b) * N1;
-  const float* ua = a.u_accept + static_cast<size_t>(b) * N1;
+  const float* ua = a.greedy ? nullptr : a.u_accept + static_cast<size_t>(b) * N1;
   int bad = 0;
   for (int i = tid; i < N1; i += kThreads) {
     const int p = par[i];
@@ -168,11 +177,13 @@ __global__ __launch_bounds__(kThreads) void ts_prep_kernel(TsArgs a) {
       bad |= p < 0 || p >= i;
       const int x = tok[i];
       bad |= x < 0 || x >= a.V;
-      const float u = ua[i];
-      bad |= !(u > 0.f && u <= 1.f);
+      if (!a.greedy) {
+        const float u = ua[i];
+        bad |= !(u > 0.f && u <= 1.f);
+      }
     }
   }
-  if (tid == 0) {
+  if (tid == 0 && !a.greedy) {
     const float T = a.temperature[b];
     const float uf = a.u_final[b];
     bad |= !(T > 0.f && T <= 3.4e38f);
@@ -601,6 +612,201 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
   if (tid == 0) a.out_len[b] = plen;
 }
 
+// ---------------------------------------------------------------- greedy walk
+struct TgShared {
+  float v[kTsMaxSlices];  // slice maxima of the current node's row
+  float i[kTsMaxSlices];  // their first indices (int bits)
+  float wv[kWaves];
+  int wi[kWaves];
+  int budget;
+  int nf, nn;             // frontier and next-frontier sizes
+  int front[SPEC_MAX_TREE_NODES];
+  int nxt[SPEC_MAX_TREE_NODES];
+  int amax[SPEC_MAX_TREE_NODES];  // row argmax of each frontier node
+  int ks[SPEC_MAX_TREE_NODES + 1];
+  int kl[SPEC_MAX_TREE_NODES];
+  int tok[SPEC_MAX_TREE_NODES];
+  int par[SPEC_MAX_TREE_NODES];
+  double unused_d[kTsMaxSlices];  // gather targets that the greedy walk does not use
+};
+
+// Same hand-over as ts_gather, for the (max, first index) pair of each slice.
+__device__ __forceinline__ bool tg_gather(const uint64_t* slot_base, int W, uint32_t tag, TgShared& sh) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.budget = kTsPollLimit;
+  for (;;) {
+    int missing = 0;
+    if (tid < W) {
+      const uint64_t* sl = slot_base + static_cast<size_t>(tid) * kTsWords;
+      float f;
+      if (ts_get_float(sl + 4, tag, &f)) sh.v[tid] = f; else missing = 1;
+      if (ts_get_float(sl + 5, tag, &f)) sh.i[tid] = f; else missing = 1;
+    }
+    if (!__syncthreads_or(missing)) return true;
+    if (tid == 0) {
+      __builtin_amdgcn_s_sleep(2);
+      --sh.budget;
+    }
+    __syncthreads();
+    if (sh.budget <= 0) return false;
+  }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  constexpr int kSlice = kThreads * kTsNV * E;
+  __shared__ TgShared sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int W = a.W;
+  const int b = b0 + static_cast<int>(blockIdx.x) / W;
+  const int w = static_cast<int>(blockIdx.x) % W;
+  const int N1 = a.N1, V = a.V;
+  if (!a.valid[b]) {
+    if (w == 0) ts_write_invalid(a, b);
+    return;
+  }
+  const uint32_t gen = ts_generation(a);
+  const size_t rowb = static_cast<size_t>(V) * EL::kBytes;
+  const char* tbase = static_cast<const char*>(a.target) + static_cast<size_t>(b) * N1 * rowb;
+  const int sl0 = w * kSlice;
+  u32x4 rt[kTsNV];
+#pragma unroll
+  for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(tbase, V, sl0 + (j * kThreads + tid) * E);
+  {
+    const int32_t* ks = a.kstart + static_cast<size_t>(b) * (N1 + 1);
+    const int32_t* kl = a.klist + static_cast<size_t>(b) * N1;
+    const int32_t* tok = a.token + static_cast<size_t>(b) * N1;
+    const int32_t* par = a.parent + static_cast<size_t>(b) * N1;
+    for (int i = tid; i <= N1; i += kThreads) {
+      sh.ks[i] = ks[i];
+      if (i < N1) {
+        sh.kl[i] = kl[i];
+        sh.tok[i] = tok[i];
+        sh.par[i] = par[i];
+      }
+    }
+    if (tid == 0) {
+      sh.nf = 1;
+      sh.front[0] = 0;
+    }
+  }
+  uint64_t* slots = a.slots + static_cast<size_t>(b) * 2 * W * kTsWords;
+  int step = 0, depth = 0;
+  bool loaded = true;  // rt holds the root's slice
+  for (;;) {
+    __syncthreads();
+    const int F = uniform(sh.nf);
+    if (tid == 0) sh.nn = 0;
+    for (int fi = 0; fi < F; ++fi) {
+      const int f = uniform(sh.front[fi]);
+      if (!loaded) {
+        const char* row = tbase + static_cast<size_t>(f) * rowb;
+#pragma unroll
+        for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(row, V, sl0 + (j * kThreads + tid) * E);
+      }
+      loaded = false;
+      // (max, first index) over this lane's elements in vocabulary order, then the slice
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+#pragma unroll
+      for (int j = 0; j < kTsNV; ++j)
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const int e = sl0 + (j * kThreads + tid) * E + i;
+          const float x = EL::get(rt[j], i);
+          if (e < V && better(x, e, bv, bi)) {
+            bv = x;
+            bi = e;
+          }
+        }
+      wave_argmax(bv, bi);
+      __syncthreads();
+      if (lane == 0) {
+        sh.wv[wv] = bv;
+        sh.wi[wv] = bi;
+      }
+      __syncthreads();
+      float sv = sh.wv[0];
+      int si = sh.wi[0];
+      for (int k = 1; k < kWaves; ++k)
+        if (better(sh.wv[k], sh.wi[k], sv, si)) {
+          sv = sh.wv[k];
+          si = sh.wi[k];
+        }
+      const uint32_t tag = ts_tag(gen, step);
+      uint64_t* mine = slots + (static_cast<size_t>(step & 1) * W + w) * kTsWords;
+      if (tid == 0) {
+        store_agent(mine + 4, ts_word(__float_as_uint(sv), tag));
+        store_agent(mine + 5, ts_word(static_cast<uint32_t>(si), tag));
+      }
+      if (!tg_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, sh)) {
+        ts_write_invalid(a, b);
+        return;
+      }
+      ++step;
+      // every slice's pair, in slice order: the same argmax in every workgroup
+      float gv = -INFINITY;
+      int gi = INT_MAX;
+      for (int q = 0; q < W; ++q) {
+        const float qv = sh.v[q];
+        const int qi = __float_as_int(sh.i[q]);
+        if (better(qv, qi, gv, gi)) {
+          gv = qv;
+          gi = qi;
+        }
+      }
+      gi = uniform(gi);
+      if (tid == 0) {
+        sh.amax[fi] = gi;
+        const int k0 = sh.ks[f], k1 = sh.ks[f + 1];
+        for (int k = k0; k < k1; ++k) {
+          const int c = sh.kl[k];
+          if (sh.tok[c] == gi) sh.nxt[sh.nn++] = c;
+        }
+      }
+      __syncthreads();
+    }
+    const int nn = uniform(sh.nn);
+    if (nn == 0) break;
+    if (++depth > a.max_depth) {  // the accepted path outgrows its output row
+      if (w == 0) ts_write_invalid(a, b);
+      return;
+    }
+    if (tid == 0) {
+      for (int k = 0; k < nn; ++k) sh.front[k] = sh.nxt[k];
+      sh.nf = nn;
+    }
+  }
+  if (w != 0) return;
+  // the deepest accepted level is the frontier: its smallest node ends the path
+  const int F = uniform(sh.nf);
+  int best = INT_MAX, bonus = -1;
+  for (int fi = 0; fi < F; ++fi)
+    if (sh.front[fi] < best) {
+      best = sh.front[fi];
+      bonus = sh.amax[fi];
+    }
+  const int D1 = a.max_depth + 1;
+  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * D1;
+  int32_t* on = a.out_nodes + static_cast<size_t>(b) * D1;
+  if (tid == 0) {
+    int v = best;
+    for (int k = depth - 1; k >= 0; --k) {  // root-first: position k holds the node at depth k + 1
+      on[k] = v;
+      ot[k] = sh.tok[v];
+      v = sh.par[v];
+    }
+    ot[depth] = bonus;
+    a.out_len[b] = depth;
+  }
+  for (int k = depth + 1 + tid; k < D1; k += kThreads) ot[k] = -1;
+  for (int k = depth + tid; k < D1; k += kThreads) on[k] = -1;
+}
+
 // ---------------------------------------------------------------- host
 struct TsLayout {
   size_t off_valid, off_kstart, off_klist, off_slots, bytes;
@@ -667,6 +873,82 @@ static spec_status_t ts_launch(const TsArgs& a, hipStream_t s) {
     if (st != SPEC_OK) return st;
   }
   return SPEC_OK;
+}
+
+template <int DT, bool VEC>
+static int tg_slots_per_device() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(tg_walk_kernel<DT, VEC>),
+                                                   kThreads, 0) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 1;
+  v = per_cu * cus;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+template <int DT, bool VEC>
+static spec_status_t tg_launch(const TsArgs& a, hipStream_t s) {
+  const int per_launch = (tg_slots_per_device<DT, VEC>() / 2) / a.W;
+  if (per_launch < 1) return fail(SPEC_ERR_UNSUPPORTED, "V needs %d workgroups per sequence, more than fit", a.W);
+  {
+    LaunchScope scope("ts_prep", s);
+    scope.launch(ts_prep_kernel, dim3(static_cast<unsigned>(a.B)), dim3(kThreads), s, a);
+    const spec_status_t st = scope.finish();
+    if (st != SPEC_OK) return st;
+  }
+  for (int b0 = 0; b0 < a.B; b0 += per_launch) {
+    const int nb = a.B - b0 < per_launch ? a.B - b0 : per_launch;
+    LaunchScope scope("tg_walk", s);
+    scope.launch(tg_walk_kernel<DT, VEC>, dim3(static_cast<unsigned>(nb * a.W)), dim3(kThreads), s, a, b0);
+    const spec_status_t st = scope.finish();
+    if (st != SPEC_OK) return st;
+  }
+  return SPEC_OK;
+}
+
+size_t tree_walk_workspace_bytes(int B, int N1, int V, spec_dtype_t dtype) {
+  const TsLayout L = ts_layout(B, N1, V, dtype);
+  return L.W > kTsMaxSlices ? 0 : L.bytes;
+}
+
+spec_status_t tree_greedy_walk(const void* target_logits, spec_dtype_t dtype, const int32_t* parent,
+                               const int32_t* node_token, int B, int N1, int V, int max_depth,
+                               int32_t* out_accept_len, int32_t* out_tokens, int32_t* out_path_nodes,
+                               void* workspace, size_t workspace_bytes, hipStream_t s) {
+  const TsLayout L = ts_layout(B, N1, V, dtype);
+  if (L.W > kTsMaxSlices) return fail(SPEC_ERR_UNSUPPORTED, "V = %d needs more than %d slices", V, kTsMaxSlices);
+  if (workspace_bytes < L.bytes)
+    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.bytes);
+  TsArgs a{};
+  a.target = target_logits;
+  a.parent = parent;
+  a.token = node_token;
+  a.B = B;
+  a.N1 = N1;
+  a.V = V;
+  a.max_depth = max_depth;
+  a.W = L.W;
+  a.greedy = 1;
+  a.out_len = out_accept_len;
+  a.out_tokens = out_tokens;
+  a.out_nodes = out_path_nodes;
+  a.gen = ts_next_generation();
+  char* ws = static_cast<char*>(workspace);
+  a.runs = reinterpret_cast<uint32_t*>(ws);
+  a.valid = reinterpret_cast<int32_t*>(ws + L.off_valid);
+  a.kstart = reinterpret_cast<int32_t*>(ws + L.off_kstart);
+  a.klist = reinterpret_cast<int32_t*>(ws + L.off_klist);
+  a.slots = reinterpret_cast<uint64_t*>(ws + L.off_slots);
+  const int esize = dtype == SPEC_BF16 ? 2 : 4;
+  const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits);
+  if (dtype == SPEC_BF16) return vec ? tg_launch<kBF16, true>(a, s) : tg_launch<kBF16, false>(a, s);
+  return vec ? tg_launch<kF32, true>(a, s) : tg_launch<kF32, false>(a, s);
 }
 
 }  // namespace specv
