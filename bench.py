@@ -254,6 +254,7 @@ def other_workloads(warmup, steps, dev):
         sets.append((to_dev(tr.target, "bf16", dev), torch.from_numpy(tr.parent).to(dev),
                      torch.from_numpy(tr.node_token).to(dev)))
 
+    # every node's argmax asked for: every row is streamed once
     prepared = [sv.prepare_spec_verify_tree_greedy(t, p, k, 6) for t, p, k in sets]
 
     def tcall(i):
@@ -264,10 +265,22 @@ def other_workloads(warmup, steps, dev):
     torch.cuda.synchronize()
     tree_parents = [p for _, p, _ in sets]
     tree_paths = [(c.result.path_nodes.clone(), c.result.accept_len.clone()) for c in prepared]
-    del sets, prepared
+    accepted = [c.result.accept_len.cpu().numpy() for c in prepared]
+    del prepared
     tb = per + tr0.B * (7 * 3 + 1 + tr0.N1) * 4
-    out.append(_entry("tree_greedy_B32_N60_V128256_bf16", dict(ms=ms, bytes=tb, kernels=kms, steps=steps),
+    out.append(_entry("tree_greedy_all_argmax_B32_N60_V128256_bf16", dict(ms=ms, bytes=tb, kernels=kms, steps=steps),
                       tr0.B * (tr0.N1 - 1)))
+    # the path, its tokens and its nodes only (the workload's outputs): the walk reads the
+    # root's row and the accepted nodes' rows
+    prepared = [sv.prepare_spec_verify_tree_greedy(t, p, k, 6, want_argmax=False) for t, p, k in sets]
+    ms, _ = time_calls(tcall, n_sets, warmup, steps, False)
+    _, kms = time_calls(tcall, n_sets, 2, steps, True)
+    walked = int(np.mean([int((a + 1).sum()) for a in accepted])) * tr0.V * 2
+    r = _entry("tree_greedy_B32_N60_V128256_bf16", dict(ms=ms, bytes=walked, kernels=kms, steps=steps),
+               tr0.B * (tr0.N1 - 1))
+    r["rows_read_per_call"] = walked // (tr0.V * 2)
+    out.append(r)
+    del sets, prepared
 
     # stochastic tree verification, B=32 N=60 V=128256 bf16, T=0.8
     out.append(tree_sampled_workload(warmup, steps, dev))

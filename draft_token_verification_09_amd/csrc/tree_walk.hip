@@ -709,6 +709,7 @@ __global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
         for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(row, V, sl0 + (j * kThreads + tid) * E);
       }
       loaded = false;
+      const int k0 = uniform(sh.ks[f]), k1 = uniform(sh.ks[f + 1]);
       // (max, first index) over this lane's elements in vocabulary order, then the slice
       float bv = -INFINITY;
       int bi = INT_MAX;
@@ -748,24 +749,25 @@ __global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
         return;
       }
       ++step;
-      // every slice's pair, in slice order: the same argmax in every workgroup
-      float gv = -INFINITY;
-      int gi = INT_MAX;
-      for (int q = 0; q < W; ++q) {
-        const float qv = sh.v[q];
-        const int qi = __float_as_int(sh.i[q]);
-        if (better(qv, qi, gv, gi)) {
-          gv = qv;
-          gi = qi;
-        }
-      }
+      // every slice's pair: lane q takes slice q; (max, first index) does not depend on order
+      float gv = lane < W ? sh.v[lane] : -INFINITY;
+      int gi = lane < W ? __float_as_int(sh.i[lane]) : INT_MAX;
+      wave_argmax(gv, gi);
       gi = uniform(gi);
-      if (tid == 0) {
-        sh.amax[fi] = gi;
-        const int k0 = sh.ks[f], k1 = sh.ks[f + 1];
-        for (int k = k0; k < k1; ++k) {
-          const int c = sh.kl[k];
-          if (sh.tok[c] == gi) sh.nxt[sh.nn++] = c;
+      // the children whose token is the argmax join the next frontier, in node order
+      if (wv == 0) {
+        int base = sh.nn;
+        for (int k = k0; k < k1; k += 64) {
+          const int kk = k + lane;
+          const int c = kk < k1 ? sh.kl[kk] : 0;
+          const bool match = kk < k1 && sh.tok[c] == gi;
+          const unsigned long long mask = __ballot(match);
+          if (match) sh.nxt[base + __popcll(mask & ((1ull << lane) - 1ull))] = c;
+          base += __popcll(mask);
+        }
+        if (lane == 0) {
+          sh.nn = base;
+          sh.amax[fi] = gi;
         }
       }
       __syncthreads();
