@@ -193,3 +193,46 @@ def test_prepared_call_matches_plain_call():
     torch.cuda.synchronize()
     assert torch.equal(r1.accept_len, r2.accept_len) and torch.equal(r1.tokens, r2.tokens)
     assert torch.equal(r1.path_nodes, r2.path_nodes)
+
+
+def test_graph_replays_match_eager_calls():
+    # the walk's hand-over generation changes on every run, so a captured call replays
+    # correctly with new inputs each time
+    sv = _sv()
+    xs = [synth.tree_sampled_inputs(40 + s, B=6, n_nodes=20, depth=4, V=30000, dtype="bf16", name=f"g{s}")
+          for s in range(3)]
+
+    def dev_args(x):
+        return [logits_to_device(x.target, "bf16"), logits_to_device(x.draft, "bf16"), i32(x.parent),
+                i32(x.node_token), f32(x.temperature), f32(x.u_accept), f32(x.u_final)]
+
+    args = [dev_args(x) for x in xs]
+    static = [t.clone() for t in args[0]]
+    B, D1 = 6, xs[0].max_depth + 1
+    out = sv.TreeResult(torch.empty(B, dtype=torch.int32, device=dev()),
+                        torch.empty((B, D1), dtype=torch.int32, device=dev()),
+                        torch.empty((B, D1), dtype=torch.int32, device=dev()), None)
+    ws = torch.empty(int(sv.lib().spec_verify_tree_workspace_size(B, 21, 30000, 1)) + 256, dtype=torch.uint8,
+                     device=dev())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sv.spec_verify_tree(*static, xs[0].max_depth, out=out, workspace_buf=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.spec_verify_tree(*static, xs[0].max_depth, out=out, workspace_buf=ws)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        k = (rep + 1) % 3
+        for dst, src in zip(static, args[k]):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = sv.spec_verify_tree(*args[k], xs[k].max_depth)
+        torch.cuda.synchronize()
+        log(f"[tree_sampled] graph replay {rep}: input set {k}")
+        assert torch.equal(out.accept_len, eager.accept_len)
+        assert torch.equal(out.tokens, eager.tokens) and torch.equal(out.path_nodes, eager.path_nodes)

@@ -126,3 +126,37 @@ def test_walk_several_launches_dirty_workspace():
     ref = oracle.verify_tree_greedy(tr.target, tr.dtype, tr.parent, tr.node_token, tr.max_depth)
     assert np.array_equal(g.tokens.cpu().numpy(), ref.tokens)
     assert np.array_equal(g.path_nodes.cpu().numpy(), ref.path_nodes)
+
+
+def test_walk_graph_replays_match_eager_calls():
+    sv = _sv()
+    trs = [synth.tree_inputs(50 + s, B=6, n_nodes=20, depth=4, V=30000, dtype="bf16", p_boost=0.9) for s in range(3)]
+    args = [[logits_to_device(t.target, "bf16"), i32(t.parent), i32(t.node_token)] for t in trs]
+    static = [t.clone() for t in args[0]]
+    B, D1 = 6, trs[0].max_depth + 1
+    out = sv.TreeResult(torch.empty(B, dtype=torch.int32, device=dev()),
+                        torch.empty((B, D1), dtype=torch.int32, device=dev()),
+                        torch.empty((B, D1), dtype=torch.int32, device=dev()), None)
+    ws = torch.empty(int(sv.lib().spec_verify_tree_greedy_workspace_size(B, 21, 30000, 1)) + 256,
+                     dtype=torch.uint8, device=dev())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sv.spec_verify_tree_greedy(*static, trs[0].max_depth, want_argmax=False, out=out, workspace_buf=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.spec_verify_tree_greedy(*static, trs[0].max_depth, want_argmax=False, out=out, workspace_buf=ws)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        k = (rep + 1) % 3
+        for dst, src in zip(static, args[k]):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.verify_tree_greedy(trs[k].target, "bf16", trs[k].parent, trs[k].node_token, trs[k].max_depth)
+        log(f"[tree walk] graph replay {rep}: input set {k}")
+        assert np.array_equal(out.tokens.cpu().numpy(), ref.tokens)
+        assert np.array_equal(out.path_nodes.cpu().numpy(), ref.path_nodes)
