@@ -59,40 +59,22 @@ struct RowStat {
   double s;
 };
 
-// Segment masses pass between the tasks of one pool launch through slots of two 64-bit
-// words, each carrying 32 bits of the double in its low half and the call's generation
-// number in its high half, written by one atomic store.  A reader knows that a slot was
-// written during this call when both high halves equal the generation, so no clearing
-// pass is needed: whatever a slot held before (an earlier call's words, or anything else)
-// reads as "not written yet" unless 64 bits match by chance.  The generation mixes a
-// number the host draws for each call (a process-wide counter with a random start) with
-// a counter in the workspace that the stats kernel advances on every run, so that it
-// changes even when a captured graph replays the same launch arguments; it is never 0.
+// Segment masses pass between the tasks of one pool launch through slots of two tagged
+// 64-bit words (see the hand-over words in device_common.h), tagged with the call's
+// generation number.  The generation mixes a number the host draws for each call (a
+// process-wide counter with a random start) with a counter in the workspace that the
+// stats kernel advances on every run, so that it changes even when a captured graph
+// replays the same launch arguments; it is never 0.
 struct SlotDouble {
   uint64_t lo, hi;
 };
 
-__device__ __forceinline__ uint64_t tagged(uint32_t payload, uint32_t gen) {
-  return static_cast<uint64_t>(payload) | (static_cast<uint64_t>(gen) << 32);
-}
-
-__device__ __forceinline__ void put_slot(SlotDouble* p, double v, uint32_t gen) {
-  const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(v));
-  store_agent(&p->lo, tagged(static_cast<uint32_t>(bits), gen));
-  store_agent(&p->hi, tagged(static_cast<uint32_t>(bits >> 32), gen));
-}
+__device__ __forceinline__ void put_slot(SlotDouble* p, double v, uint32_t gen) { put_tagged_double(&p->lo, v, gen); }
 
 // Reads a slot; false if it has not been written during this call.
 __device__ __forceinline__ bool get_slot(const SlotDouble* p, uint32_t gen, double* v) {
-  const uint64_t lo = load_agent(&p->lo), hi = load_agent(&p->hi);
-  *v = __longlong_as_double(static_cast<long long>((hi << 32) | (lo & 0xffffffffull)));
-  return static_cast<uint32_t>(lo >> 32) == gen && static_cast<uint32_t>(hi >> 32) == gen;
+  return get_tagged_double(&p->lo, gen, v);
 }
-
-// Polls of a slot that has not been written yet before a wait gives up (each poll takes
-// at least a memory round trip, about a microsecond: a quarter of a second or more).
-constexpr int kPollLimit = 1 << 18;
-__device__ __forceinline__ void short_pause() { __builtin_amdgcn_s_sleep(2); }
 
 struct ChainDecision {
   int mode;

@@ -381,4 +381,41 @@ __device__ __forceinline__ T load_agent(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Hand-over words.  A 64-bit word carries 32 payload bits in its low half and a 32-bit tag
+// (the call's generation, possibly mixed with a step number) in its high half, written by
+// one agent-scope atomic store.  A reader takes a value only when every word of it
+// carries the tag it expects, so whatever a word held before (an earlier call's or step's
+// words, or anything else) reads as "not written yet" unless 32 bits match by chance, and
+// no clearing pass is needed.
+__device__ __forceinline__ uint64_t tagged(uint32_t payload, uint32_t tag) {
+  return static_cast<uint64_t>(payload) | (static_cast<uint64_t>(tag) << 32);
+}
+
+__device__ __forceinline__ void put_tagged_u32(uint64_t* w, uint32_t v, uint32_t tag) { store_agent(w, tagged(v, tag)); }
+
+__device__ __forceinline__ bool get_tagged_u32(const uint64_t* w, uint32_t tag, uint32_t* v) {
+  const uint64_t x = load_agent(w);
+  *v = static_cast<uint32_t>(x);
+  return static_cast<uint32_t>(x >> 32) == tag;
+}
+
+// A double as two tagged words (w[0] low half of its bits, w[1] high half).
+__device__ __forceinline__ void put_tagged_double(uint64_t* w, double v, uint32_t tag) {
+  const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(v));
+  store_agent(w, tagged(static_cast<uint32_t>(bits), tag));
+  store_agent(w + 1, tagged(static_cast<uint32_t>(bits >> 32), tag));
+}
+
+__device__ __forceinline__ bool get_tagged_double(const uint64_t* w, uint32_t tag, double* v) {
+  const uint64_t lo = load_agent(w), hi = load_agent(w + 1);
+  *v = __longlong_as_double(static_cast<long long>((hi << 32) | (lo & 0xffffffffull)));
+  return static_cast<uint32_t>(lo >> 32) == tag && static_cast<uint32_t>(hi >> 32) == tag;
+}
+
+// Polls of a hand-over word that has not been written yet before a wait gives up (each
+// poll takes at least a memory round trip, about a microsecond: a quarter of a second or
+// more), and the pause between polls.
+constexpr int kPollLimit = 1 << 18;
+__device__ __forceinline__ void short_pause() { __builtin_amdgcn_s_sleep(2); }
+
 }  // namespace specv

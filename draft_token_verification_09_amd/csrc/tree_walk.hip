@@ -46,7 +46,6 @@ namespace specv {
 constexpr int kTsNV = 8;                          // 16-byte vectors per lane per row slice
 constexpr int kTsMaxSlices = 64;                  // workgroups per sequence
 constexpr int kTsWords = 8;                       // tagged 64-bit words per slot
-constexpr int kTsPollLimit = 1 << 18;             // polls before a wait gives up
 
 // Keeps the scheduler from interleaving the unpacked elements of several vectors, which
 // would hold all of them in registers at once.
@@ -80,40 +79,23 @@ struct TsArgs {
   uint64_t* slots;  // [B, 2, W, kTsWords]
 };
 
-// ---------------------------------------------------------------- hand-over words
+// ---------------------------------------------------------------- hand-over tags
 //
-// A slot word carries 32 payload bits and a 32-bit tag (the call's generation mixed with
-// the walk step), written by one agent-scope atomic store.  A reader takes a slot only
-// when every word carries the tag it expects, so stale words (earlier steps or calls, or
-// anything else) read as "not written yet".  Steps alternate between two slots per
-// workgroup: a workgroup publishes step s + 2 only after it has read every workgroup's
-// step s + 1, which each of them published only after reading step s, so no word is
-// overwritten before all readers have it.
+// Slot words are the tagged words of device_common.h; the tag mixes the call's generation
+// with the walk step.  Steps alternate between two slots per workgroup: a workgroup
+// publishes step s + 2 only after it has read every workgroup's step s + 1, which each of
+// them published only after reading step s, so no word is overwritten before all readers
+// have it.
 __device__ __forceinline__ uint32_t ts_tag(uint32_t gen, int step) {
   const uint32_t t = gen ^ (static_cast<uint32_t>(step) * 0x9e3779b1u);
   return t != 0u ? t : 0x2545f491u;
 }
 
-__device__ __forceinline__ uint64_t ts_word(uint32_t payload, uint32_t tag) {
-  return static_cast<uint64_t>(payload) | (static_cast<uint64_t>(tag) << 32);
-}
-
-__device__ __forceinline__ void ts_put_double(uint64_t* w, double v, uint32_t tag) {
-  const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(v));
-  store_agent(w, ts_word(static_cast<uint32_t>(bits), tag));
-  store_agent(w + 1, ts_word(static_cast<uint32_t>(bits >> 32), tag));
-}
-
-__device__ __forceinline__ bool ts_get_double(const uint64_t* w, uint32_t tag, double* v) {
-  const uint64_t lo = load_agent(w), hi = load_agent(w + 1);
-  *v = __longlong_as_double(static_cast<long long>((hi << 32) | (lo & 0xffffffffull)));
-  return static_cast<uint32_t>(lo >> 32) == tag && static_cast<uint32_t>(hi >> 32) == tag;
-}
-
 __device__ __forceinline__ bool ts_get_float(const uint64_t* w, uint32_t tag, float* v) {
-  const uint64_t x = load_agent(w);
-  *v = __uint_as_float(static_cast<uint32_t>(x));
-  return static_cast<uint32_t>(x >> 32) == tag;
+  uint32_t x;
+  const bool ok = get_tagged_u32(w, tag, &x);
+  *v = __uint_as_float(x);
+  return ok;
 }
 
 // Two workgroup reductions with one exchange through shared memory (lds: 2 * kWaves).
@@ -254,7 +236,7 @@ __device__ __forceinline__ bool ts_gather(const uint64_t* slot_base, int W, uint
                                           TsShared& sh, double* dst_d0, double* dst_d1, float* dst_f0,
                                           float* dst_f1) {
   const int tid = threadIdx.x;
-  if (tid == 0) sh.budget = kTsPollLimit;
+  if (tid == 0) sh.budget = kPollLimit;
   for (;;) {
     int missing = 0;
     if (tid < W) {
@@ -262,10 +244,10 @@ __device__ __forceinline__ bool ts_gather(const uint64_t* slot_base, int W, uint
       double v;
       float f;
       if (nd > 0) {
-        if (ts_get_double(sl + 0, tag, &v)) dst_d0[tid] = v; else missing = 1;
+        if (get_tagged_double(sl + 0, tag, &v)) dst_d0[tid] = v; else missing = 1;
       }
       if (nd > 1) {
-        if (ts_get_double(sl + 2, tag, &v)) dst_d1[tid] = v; else missing = 1;
+        if (get_tagged_double(sl + 2, tag, &v)) dst_d1[tid] = v; else missing = 1;
       }
       if (nf > 0) {
         if (ts_get_float(sl + 4, tag, &f)) dst_f0[tid] = f; else missing = 1;
@@ -276,7 +258,7 @@ __device__ __forceinline__ bool ts_gather(const uint64_t* slot_base, int W, uint
     }
     if (!__syncthreads_or(missing)) return true;
     if (tid == 0) {
-      __builtin_amdgcn_s_sleep(2);
+      short_pause();
       --sh.budget;
     }
     __syncthreads();
@@ -401,10 +383,10 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
     uint64_t* mine = slots + (static_cast<size_t>(step & 1) * W + w) * kTsWords;
     uint32_t tag = ts_tag(gen, step);
     if (tid == 0) {
-      ts_put_double(mine + 0, St, tag);
-      ts_put_double(mine + 2, Sd, tag);
-      store_agent(mine + 4, ts_word(__float_as_uint(ot), tag));
-      store_agent(mine + 5, ts_word(__float_as_uint(od), tag));
+      put_tagged_double(mine + 0, St, tag);
+      put_tagged_double(mine + 2, Sd, tag);
+      store_agent(mine + 4, tagged(__float_as_uint(ot), tag));
+      store_agent(mine + 5, tagged(__float_as_uint(od), tag));
     }
     if (!ts_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, 2, 2, sh, sh.s[0], sh.s[1],
                    sh.o[0], sh.o[1])) {
@@ -472,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
       const double part = block_sum(static_cast<double>(acc), sh.d);
       mine = slots + (static_cast<size_t>(step & 1) * W + w) * kTsWords;
       tag = ts_tag(gen, step);
-      if (tid == 0) ts_put_double(mine, part, tag);
+      if (tid == 0) put_tagged_double(mine, part, tag);
       double* tmp = sh.s[0];  // reuse: the stats of this node are combined already
       if (!ts_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, 1, 0, sh, tmp, nullptr,
                      nullptr, nullptr)) {
@@ -633,7 +615,7 @@ struct TgShared {
 // Same hand-over as ts_gather, for the (max, first index) pair of each slice.
 __device__ __forceinline__ bool tg_gather(const uint64_t* slot_base, int W, uint32_t tag, TgShared& sh) {
   const int tid = threadIdx.x;
-  if (tid == 0) sh.budget = kTsPollLimit;
+  if (tid == 0) sh.budget = kPollLimit;
   for (;;) {
     int missing = 0;
     if (tid < W) {
@@ -644,7 +626,7 @@ __device__ __forceinline__ bool tg_gather(const uint64_t* slot_base, int W, uint
     }
     if (!__syncthreads_or(missing)) return true;
     if (tid == 0) {
-      __builtin_amdgcn_s_sleep(2);
+      short_pause();
       --sh.budget;
     }
     __syncthreads();
@@ -741,8 +723,8 @@ __global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
       const uint32_t tag = ts_tag(gen, step);
       uint64_t* mine = slots + (static_cast<size_t>(step & 1) * W + w) * kTsWords;
       if (tid == 0) {
-        store_agent(mine + 4, ts_word(__float_as_uint(sv), tag));
-        store_agent(mine + 5, ts_word(static_cast<uint32_t>(si), tag));
+        store_agent(mine + 4, tagged(__float_as_uint(sv), tag));
+        store_agent(mine + 5, tagged(static_cast<uint32_t>(si), tag));
       }
       if (!tg_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, sh)) {
         ts_write_invalid(a, b);
