@@ -16,8 +16,9 @@
 //
 // Only the rows on the walk are read: the accepted path's target rows and the draft rows
 // of its internal nodes.  The walk is sequential in depth, so it is spread over W
-// workgroups per sequence, each owning one slice of the vocabulary (256 lanes x 8 vectors
-// of 16 bytes).  A workgroup holds its slice of the current node's two rows in registers
+// workgroups per sequence, each owning one slice of the vocabulary (256 lanes x 4 vectors
+// of 16 bytes; smaller slices shorten each level, which is latency-bound, and 4 vectors
+// per lane measured best).  A workgroup holds its slice of the current node's two rows in registers
 // for every test at that node; the per-slice sums (row maxima and exp2 sums, residual
 // masses) pass between the W workgroups through generation-tagged slots, and every
 // workgroup combines them in the same order, so all of them take the same decisions.  The
@@ -43,7 +44,7 @@
 
 namespace specv {
 
-constexpr int kTsNV = 8;                          // 16-byte vectors per lane per row slice
+constexpr int kTsNV = 4;                          // 16-byte vectors per lane per row slice
 constexpr int kTsMaxSlices = 64;                  // workgroups per sequence
 constexpr int kTsWords = 8;                       // tagged 64-bit words per slot
 
@@ -217,8 +218,7 @@ struct TsShared {
   double d[2 * kWaves];
   float f[2 * kWaves];
   int i[kWaves];
-  int missing, budget, y;
-  double base;
+  int budget, y;
   float lt[SPEC_MAX_TREE_NODES];  // logits of the current node's children tokens (target row)
   float ld[SPEC_MAX_TREE_NODES];  // (draft row)
   int path[SPEC_MAX_TREE_NODES + 1];
@@ -230,7 +230,7 @@ struct TsShared {
 };
 
 // Wait until every workgroup of the sequence has published `tag` in `slot_base[w]`, then
-// copy `nd` doubles (word pairs from word `dw`) and `nf` floats (from word `fw`) of each into
+// copy its first `nd` doubles (words 0-1 and 2-3) and `nf` floats (words 4 and 5) into
 // shared memory.  False if the wait gave up.
 __device__ __forceinline__ bool ts_gather(const uint64_t* slot_base, int W, uint32_t tag, int nd, int nf,
                                           TsShared& sh, double* dst_d0, double* dst_d1, float* dst_f0,
@@ -609,7 +609,6 @@ struct TgShared {
   int kl[SPEC_MAX_TREE_NODES];
   int tok[SPEC_MAX_TREE_NODES];
   int par[SPEC_MAX_TREE_NODES];
-  double unused_d[kTsMaxSlices];  // gather targets that the greedy walk does not use
 };
 
 // Same hand-over as ts_gather, for the (max, first index) pair of each slice.

@@ -211,8 +211,8 @@ spec_status_t spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dt
  * parent, token out of range, temperature not > 0 or not finite, a uniform outside
  * (0, 1], accepted depth > max_depth) sets out_accept_len[b] = -1 and its outputs to
  * -1.  Each used row needs a finite logit.
- * Limits: 1 <= N1 <= SPEC_MAX_TREE_NODES, 0 <= max_depth <= N1, V at most 64 slices
- * (1048576 bf16 or 524288 fp32 logits).
+ * Limits: 1 <= N1 <= SPEC_MAX_TREE_NODES, 0 <= max_depth <= N1, V <= 524288 (bf16) or
+ * 262144 (fp32): at most 64 vocabulary slices of 8192 bf16 or 4096 fp32 logits.
  * ------------------------------------------------------------------------- */
 size_t spec_verify_tree_workspace_size(int B, int N1, int V, spec_dtype_t dtype);
 

@@ -82,7 +82,7 @@ def test_golden_b1_rejected_b2_accepted():
 
 
 def test_full_size_eagle_trees_bf16():
-    # B=32 trees of 60 nodes + root, depth 6, V=128256 bf16 (8 workgroups per sequence)
+    # B=32 trees of 60 nodes + root, depth 6, V=128256 bf16 (16 workgroups per sequence)
     compare(synth.tree_sampled_config_bf16(0))
 
 
@@ -92,7 +92,7 @@ def test_full_size_eagle_trees_bf16():
     (32001, "bf16", "mixed", 40),    # V * 2 not a multiple of 16: element-wise loads
     (50000, "bf16", "star", 30),     # many siblings: many residual passes
     (20000, "bf16", "chain", 24),    # a deep walk
-    (16384 * 3, "bf16", "random", 64),  # slices end exactly at V
+    (8192 * 5, "bf16", "random", 64),  # slices end exactly at V
 ])
 def test_shapes_and_topologies(V, dtype, kind, N1):
     B = 12
@@ -159,7 +159,7 @@ def test_path_longer_than_max_depth_is_flagged():
 
 
 def test_several_launches_and_dirty_workspace():
-    # B = 70 sequences of 8 workgroups each need two launches at the default occupancy;
+    # B = 70 sequences of 16 workgroups each need several launches at the default occupancy;
     # the workspace is filled with junk first and reused across shapes
     sv = _sv()
     x = synth.tree_sampled_inputs(7, B=70, n_nodes=7, depth=3, V=128256, dtype="bf16", name="B70")

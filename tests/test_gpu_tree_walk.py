@@ -48,7 +48,7 @@ def test_walk_eagle_full_size():
     compare(synth.tree_config_eagle_bf16(0))
 
 
-@pytest.mark.parametrize("V", [1000, 77777, 16384 * 2])
+@pytest.mark.parametrize("V", [1000, 77777, 8192 * 4])
 def test_walk_ragged_vocab(V):
     compare(synth.tree_inputs(4, B=8, n_nodes=30, depth=5, V=V, dtype="bf16", p_boost=0.9))
 
