@@ -31,8 +31,13 @@
 // each frontier node's row argmax across the W slices, and moves to the children that
 // match; the deepest frontier's smallest node ends the path.
 //
-// ts_prep (one workgroup per sequence) validates the inputs and lists every node's
-// children in node order; ts_walk and tg_walk run the walks.  Its workgroups wait for each other, so
+// ts_walk and tg_walk are the only kernels: every workgroup checks its sequence's inputs
+// and lists a node's children (node order) when it gets there.  A sequence's hand-over
+// generation mixes the host's number for the call with the sequence's epoch, a counter in
+// the workspace that every workgroup of the sequence reads when it starts and increments
+// once it has the first hand-over (by then all of them have read it), so every run, graph
+// replays included, tags its words anew without a kernel of its own.  The workgroups of a
+// sequence wait for each other, so
 // a launch holds at most half of the workgroups that fit on the device at once, and every
 // wait is bounded.
 #include <atomic>
@@ -73,10 +78,7 @@ struct TsArgs {
   int32_t* out_tokens;
   int32_t* out_nodes;
   uint32_t gen;     // the host's number for this call
-  uint32_t* runs;   // run counter, advanced by ts_prep on every run
-  int32_t* valid;   // [B]
-  int32_t* kstart;  // [B, N1 + 1] first child slot of each node
-  int32_t* klist;   // [B, N1] children, grouped by parent, in node order
+  uint32_t* epoch;  // [B] run counters
   uint64_t* slots;  // [B, 2, W, kTsWords]
 };
 
@@ -140,66 +142,18 @@ __device__ __forceinline__ void ts_block_sum2(double& x, double& y, double* lds)
   y = ry;
 }
 
-// ---------------------------------------------------------------- prep
-__global__ __launch_bounds__(kThreads) void ts_prep_kernel(TsArgs a) {
-  __shared__ int s_par[SPEC_MAX_TREE_NODES];
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int N1 = a.N1;
-  if (b == 0 && tid == 0) __hip_atomic_fetch_add(a.runs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int32_t* par = a.parent + static_cast<size_t>(b) * N1;
-  const int32_t* tok = a.token + static_cast<size_t>(b) * N1;
-  const float* ua = a.greedy ? nullptr : a.u_accept + static_cast<size_t>(b) * N1;
-  int bad = 0;
-  for (int i = tid; i < N1; i += kThreads) {
-    const int p = par[i];
-    s_par[i] = p;
-    if (i == 0) {
-      bad |= p != -1;
-    } else {
-      bad |= p < 0 || p >= i;
-      const int x = tok[i];
-      bad |= x < 0 || x >= a.V;
-      if (!a.greedy) {
-        const float u = ua[i];
-        bad |= !(u > 0.f && u <= 1.f);
-      }
-    }
-  }
-  if (tid == 0 && !a.greedy) {
-    const float T = a.temperature[b];
-    const float uf = a.u_final[b];
-    bad |= !(T > 0.f && T <= 3.4e38f);
-    bad |= !(uf > 0.f && uf <= 1.f);
-  }
-  bad = __syncthreads_or(bad);
-  if (tid == 0) a.valid[b] = bad ? 0 : 1;
-  if (bad) return;
-  // Children grouped by parent in node order: node p's children start at the number of
-  // nodes whose parent precedes p, and node i sits after its siblings of lower index.
-  int32_t* ks = a.kstart + static_cast<size_t>(b) * (N1 + 1);
-  int32_t* kl = a.klist + static_cast<size_t>(b) * N1;
-  for (int p = tid; p <= N1; p += kThreads) {
-    int cnt = 0;
-    for (int i = 1; i < N1; ++i) cnt += s_par[i] < p;
-    ks[p] = cnt;
-  }
-  for (int i = 1 + tid; i < N1; i += kThreads) {
-    const int p = s_par[i];
-    int before = 0, rank = 0;
-    for (int j = 1; j < N1; ++j) {
-      const int q = s_par[j];
-      before += q < p;
-      rank += q == p && j < i;
-    }
-    kl[before + rank] = i;
-  }
+// ---------------------------------------------------------------- walk
+// The sequence's generation.  Read before the sequence's first hand-over; ts_next_epoch
+// runs only after it, so all workgroups of a run read the same epoch.
+__device__ __forceinline__ uint32_t ts_generation(const TsArgs& a, int b) {
+  const uint32_t g = a.gen ^ (load_agent(a.epoch + b) * 0x9e3779b1u);
+  return g != 0u ? g : 0x2545f491u;
 }
 
-// ---------------------------------------------------------------- walk
-__device__ __forceinline__ uint32_t ts_generation(const TsArgs& a) {
-  const uint32_t g = a.gen ^ (load_agent(a.runs) * 0x9e3779b1u);
-  return g != 0u ? g : 0x2545f491u;
+// Every workgroup of a valid sequence adds 1 after its first completed hand-over, so the
+// next run of the sequence reads a new epoch.
+__device__ __forceinline__ void ts_next_epoch(const TsArgs& a, int b) {
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.epoch + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void ts_write_invalid(const TsArgs& a, int b) {
@@ -209,6 +163,64 @@ __device__ __forceinline__ void ts_write_invalid(const TsArgs& a, int b) {
     a.out_nodes[static_cast<size_t>(b) * D1 + k] = -1;
   }
   if (threadIdx.x == 0) a.out_len[b] = -1;
+}
+
+// Stage the sequence's parents and tokens (and uniforms) in shared memory and check them,
+// as every workgroup of the sequence does.  True if valid.
+__device__ __forceinline__ bool ts_stage(const TsArgs& a, int b, int* par, int* tok, float* ua) {
+  const int tid = threadIdx.x, N1 = a.N1;
+  const int32_t* gp = a.parent + static_cast<size_t>(b) * N1;
+  const int32_t* gt = a.token + static_cast<size_t>(b) * N1;
+  int bad = 0;
+  for (int i = tid; i < N1; i += kThreads) {
+    const int p = gp[i];
+    const int x = gt[i];
+    par[i] = p;
+    tok[i] = x;
+    if (i == 0) {
+      bad |= p != -1;
+    } else {
+      bad |= p < 0 || p >= i;
+      bad |= x < 0 || x >= a.V;
+    }
+    if (!a.greedy) {
+      const float u = a.u_accept[static_cast<size_t>(b) * N1 + i];
+      ua[i] = u;
+      if (i > 0) bad |= !(u > 0.f && u <= 1.f);
+    }
+  }
+  if (!a.greedy && tid == 0) {
+    const float T = a.temperature[b];
+    const float uf = a.u_final[b];
+    bad |= !(T > 0.f && T <= 3.4e38f);
+    bad |= !(uf > 0.f && uf <= 1.f);
+  }
+  return !__syncthreads_or(bad);
+}
+
+// The children of node u, in node order, into kids; returns their number (the same in
+// every lane).  Parents precede children, so a node's children follow it.
+__device__ __forceinline__ int ts_children(int u, int N1, const int* par, int* kids, int* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int total = 0;
+  for (int base = (u + 1) & ~(kThreads - 1); base < N1; base += kThreads) {
+    const int i = base + tid;
+    const bool is = i < N1 && i > u && par[i] == u;
+    const unsigned long long mask = __ballot(is);
+    __syncthreads();
+    if (lane == 0) red[wv] = __popcll(mask);
+    __syncthreads();
+    int before = total, add = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      before += k < wv ? red[k] : 0;
+      add += red[k];
+    }
+    if (is) kids[before + __popcll(mask & ((1ull << lane) - 1ull))] = i;
+    total += add;
+  }
+  __syncthreads();
+  return total;
 }
 
 struct TsShared {
@@ -223,10 +235,11 @@ struct TsShared {
   float ld[SPEC_MAX_TREE_NODES];  // (draft row)
   int path[SPEC_MAX_TREE_NODES + 1];
   // the sequence's topology, tokens and uniforms, staged once
-  int ks[SPEC_MAX_TREE_NODES + 1];
-  int kl[SPEC_MAX_TREE_NODES];
+  int par[SPEC_MAX_TREE_NODES];
+  int kids[SPEC_MAX_TREE_NODES];  // children of the current node
   int tok[SPEC_MAX_TREE_NODES];
   float ua[SPEC_MAX_TREE_NODES];
+  int ci[kWaves];
 };
 
 // Wait until every workgroup of the sequence has published `tag` in `slot_base[w]`, then
@@ -267,11 +280,10 @@ __device__ __forceinline__ bool ts_gather(const uint64_t* slot_base, int W, uint
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
+__device__ __forceinline__ void ts_walk_body(const TsArgs& a, int b0, uint32_t gen, TsShared& sh) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSlice = kThreads * kTsNV * E;  // elements per slice
-  __shared__ TsShared sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -279,11 +291,10 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
   const int b = b0 + static_cast<int>(blockIdx.x) / W;
   const int w = static_cast<int>(blockIdx.x) % W;
   const int N1 = a.N1, V = a.V;
-  if (!a.valid[b]) {
+  if (!ts_stage(a, b, sh.par, sh.tok, sh.ua)) {
     if (w == 0) ts_write_invalid(a, b);
     return;
   }
-  const uint32_t gen = ts_generation(a);
   const float T = a.temperature[b];
   const float scale = kLog2e / T;
   const size_t rowb = static_cast<size_t>(V) * EL::kBytes;
@@ -296,20 +307,6 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
   for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(tbase, V, sl0 + (j * kThreads + tid) * E);
 #pragma unroll
   for (int j = 0; j < kTsNV; ++j) rd[j] = load_vector<DT, VEC>(dbase, V, sl0 + (j * kThreads + tid) * E);
-  {
-    const int32_t* ks = a.kstart + static_cast<size_t>(b) * (N1 + 1);
-    const int32_t* kl = a.klist + static_cast<size_t>(b) * N1;
-    const int32_t* tok = a.token + static_cast<size_t>(b) * N1;
-    const float* ua = a.u_accept + static_cast<size_t>(b) * N1;
-    for (int i = tid; i <= N1; i += kThreads) {
-      sh.ks[i] = ks[i];
-      if (i < N1) {
-        sh.kl[i] = kl[i];
-        sh.tok[i] = tok[i];
-        sh.ua[i] = ua[i];
-      }
-    }
-  }
   uint64_t* slots = a.slots + static_cast<size_t>(b) * 2 * W * kTsWords;
 
   int step = 0, cur = 0, plen = 0;
@@ -319,9 +316,8 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
   double Sp = 1.0, Sq = 1.0;
 
   for (;;) {
-    __syncthreads();  // every lane is done with the previous node's shared values
-    const int k0 = uniform(sh.ks[cur]);
-    const int m = uniform(sh.ks[cur + 1]) - k0;
+    // (ts_children waits for every lane to be done with the previous node's shared values)
+    const int m = uniform(ts_children(cur, N1, sh.par, sh.kids, sh.ci));
     const char* row_t = tbase + static_cast<size_t>(cur) * rowb;
     const char* row_d = dbase + static_cast<size_t>(cur) * rowb;
     if (cur != 0) {  // the root's slices are loaded already
@@ -333,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
       }
     }
     for (int j = tid; j < m; j += kThreads) {
-      const int x = sh.tok[sh.kl[k0 + j]];
+      const int x = sh.tok[sh.kids[j]];
       sh.lt[j] = EL::value(row_t, x);
       sh.ld[j] = EL::value(row_d, x);
     }
@@ -393,6 +389,7 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
       ts_write_invalid(a, b);
       return;
     }
+    if (step == 0) ts_next_epoch(a, b);
     ++step;
     // ---- the node's p and q: lane q of every wave takes slice q, and the wave reductions
     // (a fixed DPP order) give the same values in every wave of every workgroup
@@ -418,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
     D = 1.0;
     bool moved = false;
     for (int j = 0; j < m; ++j) {
-      const int kid = uniform(sh.kl[k0 + j]);
+      const int kid = uniform(sh.kids[j]);
       const double px = static_cast<double>(exp2_fast(fmaf(uniform(sh.lt[j]), scale, -Op))) / Sp;
       const double qx = static_cast<double>(exp2_fast(fmaf(uniform(sh.ld[j]), scale, -Oq))) / Sq;
       const double rx = fmax(0.0, px - c * qx) / D;
@@ -594,6 +591,12 @@ __global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
   if (tid == 0) a.out_len[b] = plen;
 }
 
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void ts_walk_kernel(TsArgs a, int b0) {
+  __shared__ TsShared sh;
+  ts_walk_body<DT, VEC>(a, b0, ts_generation(a, b0 + static_cast<int>(blockIdx.x) / a.W), sh);
+}
+
 // ---------------------------------------------------------------- greedy walk
 struct TgShared {
   float v[kTsMaxSlices];  // slice maxima of the current node's row
@@ -605,8 +608,6 @@ struct TgShared {
   int front[SPEC_MAX_TREE_NODES];
   int nxt[SPEC_MAX_TREE_NODES];
   int amax[SPEC_MAX_TREE_NODES];  // row argmax of each frontier node
-  int ks[SPEC_MAX_TREE_NODES + 1];
-  int kl[SPEC_MAX_TREE_NODES];
   int tok[SPEC_MAX_TREE_NODES];
   int par[SPEC_MAX_TREE_NODES];
 };
@@ -634,11 +635,10 @@ __device__ __forceinline__ bool tg_gather(const uint64_t* slot_base, int W, uint
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
+__device__ __forceinline__ void tg_walk_body(const TsArgs& a, int b0, uint32_t gen, TgShared& sh) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSlice = kThreads * kTsNV * E;
-  __shared__ TgShared sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -646,34 +646,19 @@ __global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
   const int b = b0 + static_cast<int>(blockIdx.x) / W;
   const int w = static_cast<int>(blockIdx.x) % W;
   const int N1 = a.N1, V = a.V;
-  if (!a.valid[b]) {
-    if (w == 0) ts_write_invalid(a, b);
-    return;
-  }
-  const uint32_t gen = ts_generation(a);
   const size_t rowb = static_cast<size_t>(V) * EL::kBytes;
   const char* tbase = static_cast<const char*>(a.target) + static_cast<size_t>(b) * N1 * rowb;
   const int sl0 = w * kSlice;
   u32x4 rt[kTsNV];
 #pragma unroll
   for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(tbase, V, sl0 + (j * kThreads + tid) * E);
-  {
-    const int32_t* ks = a.kstart + static_cast<size_t>(b) * (N1 + 1);
-    const int32_t* kl = a.klist + static_cast<size_t>(b) * N1;
-    const int32_t* tok = a.token + static_cast<size_t>(b) * N1;
-    const int32_t* par = a.parent + static_cast<size_t>(b) * N1;
-    for (int i = tid; i <= N1; i += kThreads) {
-      sh.ks[i] = ks[i];
-      if (i < N1) {
-        sh.kl[i] = kl[i];
-        sh.tok[i] = tok[i];
-        sh.par[i] = par[i];
-      }
-    }
-    if (tid == 0) {
-      sh.nf = 1;
-      sh.front[0] = 0;
-    }
+  if (!ts_stage(a, b, sh.par, sh.tok, nullptr)) {
+    if (w == 0) ts_write_invalid(a, b);
+    return;
+  }
+  if (tid == 0) {
+    sh.nf = 1;
+    sh.front[0] = 0;
   }
   uint64_t* slots = a.slots + static_cast<size_t>(b) * 2 * W * kTsWords;
   int step = 0, depth = 0;
@@ -690,7 +675,6 @@ __global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
         for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(row, V, sl0 + (j * kThreads + tid) * E);
       }
       loaded = false;
-      const int k0 = uniform(sh.ks[f]), k1 = uniform(sh.ks[f + 1]);
       // (max, first index) over this lane's elements in vocabulary order, then the slice
       float bv = -INFINITY;
       int bi = INT_MAX;
@@ -729,6 +713,7 @@ __global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
         ts_write_invalid(a, b);
         return;
       }
+      if (step == 0) ts_next_epoch(a, b);
       ++step;
       // every slice's pair: lane q takes slice q; (max, first index) does not depend on order
       float gv = lane < W ? sh.v[lane] : -INFINITY;
@@ -736,12 +721,12 @@ __global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
       wave_argmax(gv, gi);
       gi = uniform(gi);
       // the children whose token is the argmax join the next frontier, in node order
+      // (children follow their parent)
       if (wv == 0) {
         int base = sh.nn;
-        for (int k = k0; k < k1; k += 64) {
-          const int kk = k + lane;
-          const int c = kk < k1 ? sh.kl[kk] : 0;
-          const bool match = kk < k1 && sh.tok[c] == gi;
+        for (int k = (f + 1) & ~63; k < N1; k += 64) {
+          const int c = k + lane;
+          const bool match = c > f && c < N1 && sh.par[c] == f && sh.tok[c] == gi;
           const unsigned long long mask = __ballot(match);
           if (match) sh.nxt[base + __popcll(mask & ((1ull << lane) - 1ull))] = c;
           base += __popcll(mask);
@@ -790,9 +775,15 @@ __global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
   for (int k = depth + tid; k < D1; k += kThreads) on[k] = -1;
 }
 
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void tg_walk_kernel(TsArgs a, int b0) {
+  __shared__ TgShared sh;
+  tg_walk_body<DT, VEC>(a, b0, ts_generation(a, b0 + static_cast<int>(blockIdx.x) / a.W), sh);
+}
+
 // ---------------------------------------------------------------- host
 struct TsLayout {
-  size_t off_valid, off_kstart, off_klist, off_slots, bytes;
+  size_t off_slots, bytes;
   int W;
 };
 
@@ -801,13 +792,8 @@ static TsLayout ts_layout(int B, int N1, int V, spec_dtype_t dtype) {
   const int E = dtype == SPEC_BF16 ? 8 : 4;
   const long long slice = static_cast<long long>(kThreads) * kTsNV * E;
   L.W = static_cast<int>((V + slice - 1) / slice);
-  size_t off = 256;  // run counter
-  L.off_valid = off;
-  off = align_up(off + sizeof(int32_t) * B, 256);
-  L.off_kstart = off;
-  off = align_up(off + sizeof(int32_t) * static_cast<size_t>(B) * (N1 + 1), 256);
-  L.off_klist = off;
-  off = align_up(off + sizeof(int32_t) * static_cast<size_t>(B) * N1, 256);
+  (void)N1;
+  size_t off = align_up(sizeof(uint32_t) * B, 256);  // epochs
   L.off_slots = off;
   off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * 2 * L.W * kTsWords, 256);
   L.bytes = off;
@@ -842,12 +828,6 @@ static spec_status_t ts_launch(const TsArgs& a, hipStream_t s) {
   const int slots = ts_slots_per_device<DT, VEC>();
   const int per_launch = (slots / 2) / a.W;
   if (per_launch < 1) return fail(SPEC_ERR_UNSUPPORTED, "V needs %d workgroups per sequence, more than fit", a.W);
-  {
-    LaunchScope scope("ts_prep", s);
-    scope.launch(ts_prep_kernel, dim3(static_cast<unsigned>(a.B)), dim3(kThreads), s, a);
-    const spec_status_t st = scope.finish();
-    if (st != SPEC_OK) return st;
-  }
   for (int b0 = 0; b0 < a.B; b0 += per_launch) {
     const int nb = a.B - b0 < per_launch ? a.B - b0 : per_launch;
     LaunchScope scope("ts_walk", s);
@@ -879,12 +859,6 @@ template <int DT, bool VEC>
 static spec_status_t tg_launch(const TsArgs& a, hipStream_t s) {
   const int per_launch = (tg_slots_per_device<DT, VEC>() / 2) / a.W;
   if (per_launch < 1) return fail(SPEC_ERR_UNSUPPORTED, "V needs %d workgroups per sequence, more than fit", a.W);
-  {
-    LaunchScope scope("ts_prep", s);
-    scope.launch(ts_prep_kernel, dim3(static_cast<unsigned>(a.B)), dim3(kThreads), s, a);
-    const spec_status_t st = scope.finish();
-    if (st != SPEC_OK) return st;
-  }
   for (int b0 = 0; b0 < a.B; b0 += per_launch) {
     const int nb = a.B - b0 < per_launch ? a.B - b0 : per_launch;
     LaunchScope scope("tg_walk", s);
@@ -923,10 +897,7 @@ spec_status_t tree_greedy_walk(const void* target_logits, spec_dtype_t dtype, co
   a.out_nodes = out_path_nodes;
   a.gen = ts_next_generation();
   char* ws = static_cast<char*>(workspace);
-  a.runs = reinterpret_cast<uint32_t*>(ws);
-  a.valid = reinterpret_cast<int32_t*>(ws + L.off_valid);
-  a.kstart = reinterpret_cast<int32_t*>(ws + L.off_kstart);
-  a.klist = reinterpret_cast<int32_t*>(ws + L.off_klist);
+  a.epoch = reinterpret_cast<uint32_t*>(ws);
   a.slots = reinterpret_cast<uint64_t*>(ws + L.off_slots);
   const int esize = dtype == SPEC_BF16 ? 2 : 4;
   const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits);
@@ -987,10 +958,7 @@ spec_status_t spec_verify_tree(const void* target_logits, const void* draft_logi
   a.out_nodes = out_path_nodes;
   a.gen = ts_next_generation();
   char* ws = static_cast<char*>(workspace);
-  a.runs = reinterpret_cast<uint32_t*>(ws);
-  a.valid = reinterpret_cast<int32_t*>(ws + L.off_valid);
-  a.kstart = reinterpret_cast<int32_t*>(ws + L.off_kstart);
-  a.klist = reinterpret_cast<int32_t*>(ws + L.off_klist);
+  a.epoch = reinterpret_cast<uint32_t*>(ws);
   a.slots = reinterpret_cast<uint64_t*>(ws + L.off_slots);
   const int esize = dtype == SPEC_BF16 ? 2 : 4;
   const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits) && aligned16(draft_logits);
