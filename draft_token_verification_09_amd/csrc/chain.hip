@@ -445,10 +445,10 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
     }
   }
 
-  // The lane's vectors in two halves, each with its own offset: the first half's sums run
-  // while the second half's loads are still in flight, and the halves combine at the end
-  // (measured: 2-4 % less kernel time than one offset for all vectors).
-  constexpr int kParts = NV >= 2 ? 2 : 1;
+  // The lane's vectors in parts of at most 4 (two parts for 8 vectors), each with its own
+  // offset: a part's sums run while the later parts' loads are still in flight, and the
+  // parts combine at the end (measured: 2-4 % less kernel time than one offset for all).
+  constexpr int kParts = NV >= 16 ? 4 : (NV >= 2 ? 2 : 1);
   constexpr int kPer = NV / kParts;
   float o = -INFINITY, s = 0.f;
   float po[kParts], ps[kParts];
@@ -773,23 +773,29 @@ struct ChainLayout {
   size_t off_gath, off_part, off_wseg, off_wsegp, bytes;
 };
 
-// Vectors per lane in one stats chunk: the largest of 8, 4, 2, 1 that gives at least 1024
-// workgroups (else 1), raised if needed until a row's partials fit the decision's staging.
-// (Smaller chunks shorten the stats pass's tail but lengthen the time between calls:
-// measured at B=64, K=5, V=128256, 8 is faster per call than 4.)  SPEC_NV in the
-// environment forces 1, 2, 4 or 8.
-static int chain_nv(long long rows, int V, int epv) {
+// Vectors per lane in one stats chunk: for bf16 rows read with 16-byte loads, 16 if that
+// gives at least 1024 workgroups; otherwise the largest of 8, 4, 2, 1 that does (else 1),
+// raised if needed until a row's partials fit the decision's staging.  (Measured per call
+// with bf16 rows: at B=64, K=5, V=128256, 16 vectors 50.6 us, 8 vectors 52.7, 4 vectors 58;
+// at B=256, K=8, V=152064, 16 vectors 246 us, 8 vectors 269.  Element-wise loads keep at most
+// 8, whose registers would not fit twice.)  SPEC_NV in the environment forces 1, 2, 4 or 8.
+static int chain_nv(long long rows, int V, int epv, bool vec) {
+  if (vec && epv == 8 && env_int("SPEC_NV", 0) == 0) {
+    const long long chunk = 16LL * kThreads * epv;
+    if (rows * ((V + chunk - 1) / chunk) >= 1024) return 16;
+  }
   int nv = choose_nv(rows, V, epv, 1024);
   while (nv < 8 && (V + static_cast<long long>(nv) * kThreads * epv - 1) / (static_cast<long long>(nv) * kThreads * epv) * kWaves > kStage)
     nv *= 2;
   return nv;
 }
 
-static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype) {
+// `vec`: the rows can be read with 16-byte loads (this sets the chunk size).
+static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool vec) {
   ChainLayout L{};
   const int epv = dtype == SPEC_BF16 ? 8 : 4;
   L.R = 2 * K + 1;
-  L.nv = chain_nv(static_cast<long long>(B) * L.R, V, epv);
+  L.nv = chain_nv(static_cast<long long>(B) * L.R, V, epv, vec);
   const long long chunk = static_cast<long long>(L.nv) * kThreads * epv;
   L.C = static_cast<int>((V + chunk - 1) / chunk);
   const long long seg = static_cast<long long>(kThreads) * epv;
@@ -872,6 +878,11 @@ static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
 template <int DT>
 static spec_status_t dispatch_chain(int nv, bool vec, const ChainArgs& a, hipStream_t s) {
   switch (nv) {
+    case 16:  // chosen only for bf16 rows with 16-byte loads
+      if constexpr (DT == kBF16) {
+        if (vec) return launch_chain<DT, 16, true>(a, s);
+      }
+      return fail(SPEC_ERR_UNSUPPORTED, "16-vector chunks need bf16 rows and 16-byte loads");
     case 8: return vec ? launch_chain<DT, 8, true>(a, s) : launch_chain<DT, 8, false>(a, s);
     case 4: return vec ? launch_chain<DT, 4, true>(a, s) : launch_chain<DT, 4, false>(a, s);
     case 2: return vec ? launch_chain<DT, 2, true>(a, s) : launch_chain<DT, 2, false>(a, s);
@@ -887,7 +898,10 @@ extern "C" {
 
 size_t spec_verify_chain_workspace_size(int B, int K, int V, spec_dtype_t dtype) {
   if (B <= 0 || K < 1 || K > SPEC_MAX_K || V < 1) return 0;
-  return chain_layout(B, K, V, dtype).bytes;
+  // either chunk size may be chosen at call time (it depends on the pointers' alignment)
+  const size_t with_vec = chain_layout(B, K, V, dtype, true).bytes;
+  const size_t without = chain_layout(B, K, V, dtype, false).bytes;
+  return with_vec > without ? with_vec : without;
 }
 
 spec_status_t spec_verify_chain(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
@@ -916,7 +930,9 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   const int esize = dtype == SPEC_BF16 ? 2 : 4;
   if (static_cast<double>(B) * (K + 1) * V >= 140737488355328.0)
     return fail(SPEC_ERR_UNSUPPORTED, "B*(K+1)*V too large");
-  const ChainLayout L = chain_layout(B, K, V, dtype);
+  const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits) &&
+                   (draft_logits == nullptr || aligned16(draft_logits));
+  const ChainLayout L = chain_layout(B, K, V, dtype, vec);
   const double groups = static_cast<double>(B) * L.R * L.C;
   if (groups > 2147483647.0) return fail(SPEC_ERR_UNSUPPORTED, "grid of %.0f workgroups too large", groups);
   if (L.S > 4 * kThreads || L.C * kWaves > kStage)
@@ -954,8 +970,6 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   a.wseg = reinterpret_cast<SlotDouble*>(ws + L.off_wseg);
   a.wsegp = reinterpret_cast<SlotDouble*>(ws + L.off_wsegp);
 
-  const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits) &&
-                   (draft_logits == nullptr || aligned16(draft_logits));
   if (dtype == SPEC_BF16) return dispatch_chain<kBF16>(L.nv, vec, a, s);
   return dispatch_chain<kF32>(L.nv, vec, a, s);
 }
