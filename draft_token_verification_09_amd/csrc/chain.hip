@@ -778,9 +778,12 @@ struct ChainLayout {
 // raised if needed until a row's partials fit the decision's staging.  (Measured per call
 // with bf16 rows: at B=64, K=5, V=128256, 16 vectors 50.6 us, 8 vectors 52.7, 4 vectors 58;
 // at B=256, K=8, V=152064, 16 vectors 246 us, 8 vectors 269.  Element-wise loads keep at most
-// 8, whose registers would not fit twice.)  SPEC_NV in the environment forces 1, 2, 4 or 8.
+// 8, whose registers would not fit twice.)  SPEC_NV in the environment forces 1, 2, 4 or 8,
+// or 16 where 16 may be chosen.
 static int chain_nv(long long rows, int V, int epv, bool vec) {
-  if (vec && epv == 8 && env_int("SPEC_NV", 0) == 0) {
+  const int forced = env_int("SPEC_NV", 0);
+  if (forced == 16 && vec && epv == 8) return 16;
+  if (vec && epv == 8 && forced == 0) {
     const long long chunk = 16LL * kThreads * epv;
     if (rows * ((V + chunk - 1) / chunk) >= 1024) return 16;
   }

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import chain_on_gpu, chain_oracle, check_packed, compare_chain, dev, f32, i32, log
+from gpu_helpers import chain_on_gpu, chain_oracle, check_packed, compare_chain, dev, f32, i32, log, logits_to_device
 from test_golden import load_fixtures, tree_rows
 
 pytestmark = pytest.mark.gpu
@@ -92,6 +92,32 @@ def test_unaligned_base_pointer_takes_scalar_path():
     g = sv().spec_verify_chain(t, d, i32(inp.tokens), f32(inp.temperature), f32(inp.u_accept), f32(inp.u_final))
     torch.cuda.synchronize()
     rep = compare_chain(g, chain_oracle(inp), inp)
+    assert rep.ok(), rep.failures[:5]
+
+
+def test_unaligned_bf16_rows_at_full_size_fit_the_queried_workspace():
+    # At B=64, K=5, V=128256 aligned bf16 rows take 16-vector chunks; rows one element off
+    # 16-byte alignment take the element-wise path with 8-vector chunks and more partials.
+    # The size query cannot see the pointers, so its answer must cover both layouts.
+    inp = synth.chain_config_high_accept_bf16(6)
+    B, K, V = inp.B, inp.K, inp.V
+    big_t = torch.zeros(B * (K + 1) * V + 1, dtype=torch.bfloat16, device=dev())
+    big_d = torch.zeros(B * K * V + 1, dtype=torch.bfloat16, device=dev())
+    t = big_t[1:].view(B, K + 1, V)
+    d = big_d[1:].view(B, K, V)
+    t.copy_(logits_to_device(inp.target, "bf16"))
+    d.copy_(logits_to_device(inp.draft, "bf16"))
+    assert t.data_ptr() % 16 != 0
+    need = int(sv().spec_verify_chain_workspace_size(B, K, V, 1))
+    raw = torch.empty(need + 256, dtype=torch.uint8, device=dev())
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + need]  # 256-byte aligned, exactly the queried size
+    log(f"[edge] unaligned bf16 rows B={B} K={K} V={V}, workspace {need} B")
+    g = sv().spec_verify_chain(t, d, i32(inp.tokens), f32(inp.temperature), f32(inp.u_accept), f32(inp.u_final),
+                               workspace_buf=ws)
+    torch.cuda.synchronize()
+    seqs = list(range(0, B, 8))
+    rep = compare_chain(g, chain_oracle(inp, seqs=seqs), inp, seqs=seqs)
     assert rep.ok(), rep.failures[:5]
 
 
