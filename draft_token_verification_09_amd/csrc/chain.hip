@@ -19,10 +19,12 @@
 //  chain_pool   grid = B x S/4 tasks (see chain_pool_kernel): every task of a sequence
 //               combines the partials into per-row (O, S) and evaluates p(x_k), q(x_k),
 //               alpha_k and the accept tests of all drafted positions at once (one lane
-//               per position), taking the first rejection n with a wave ballot; each task
-//               then sums the final draw's weights over its 4 segments of the row (a
-//               segment = one 16-byte vector per lane), and the token is drawn from those
-//               masses.
+//               per position), taking the first rejection n with a wave ballot.  After a
+//               rejection against draft rows, each task sums max(0, p - q) over its 4
+//               segments of the row pair (a segment = one 16-byte vector per lane), and the
+//               token is drawn from those masses.  A bonus or one-hot draw samples a target
+//               row whose chunk masses the stats pass already holds, so one task per
+//               sequence reads only the chunk that holds the draw.
 //  chain_pack   grid = 1, only for packed output: offsets and packed tokens.
 //
 // Softmax is evaluated in the exp2 domain: with scale = log2(e)/T,
@@ -118,6 +120,7 @@ struct ChainArgs {
   const float* u_accept;
   const float* u_final;
   int B, K, V, C, R;
+  int nv;               // vectors per lane in one stats chunk (a chunk = nv segments)
   int S;                // pool segment slots per row: ceil(V / segment) rounded up to whole tasks
   int32_t* out_tokens;
   int32_t* out_num;
@@ -381,14 +384,14 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
 }
 
 // grid = B x R x C: workgroup g reduces one chunk of one row, each of its waves to one
-// partial (the wave's lanes hold every 4th group of 64 vectors of the chunk).
+// partial of its quarter of the chunk (one contiguous span, see load_wave_span).
 template <int DT, int NV, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_fetch_add(a.runs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
-  constexpr int kSeg = ChunkShape<DT, NV>::kSegment;
   constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
+  constexpr int kSpan = kChunk / kWaves;  // elements of one wave's quarter
   const int g = blockIdx.x;
   const int c = g % a.C;
   const int rr = (g / a.C) % a.R;
@@ -400,12 +403,14 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   RowStat* out = a.part + ((static_cast<size_t>(b) * a.R + rr) * a.C + c) * kWaves + (threadIdx.x >> 6);
 
   u32x4 raw[NV];
-  load_chunk<DT, NV, VEC, true>(raw, row, a.V, c);
+  load_wave_span<DT, NV, VEC, true>(raw, row, a.V, c);
+  const int wv = static_cast<int>(threadIdx.x >> 6);
+  const int ln = static_cast<int>(threadIdx.x & 63);
 
   if (greedy) {  // (largest logit, smallest index) of the wave's share
     // The lane visits its elements in increasing vocabulary order, so a strict '>' keeps the
     // first maximum; elements past V read as -inf and never replace the lane's first one.
-    const int first = c * kChunk + static_cast<int>(threadIdx.x) * E;
+    const int first = c * kChunk + wv * kSpan + ln * E;
     float v = -INFINITY;
     int idx = first < a.V ? first : INT_MAX;
     // With vector loads, the packed registers count as rewritten here, so that no unpacked
@@ -421,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
         const float l = EL::get(raw[j], i);
         if (l > v) {
           v = l;
-          idx = c * kChunk + (j * kThreads + static_cast<int>(threadIdx.x)) * E + i;
+          idx = c * kChunk + wv * kSpan + (j * 64 + ln) * E + i;
         }
       }
     wave_argmax(v, idx);
@@ -435,8 +440,8 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   // The lane holding the drafted token's logit copies it out (bit-exact).
   if (x >= 0 && x < a.V && x / kChunk == c) {
     const int local = x - c * kChunk;
-    if (threadIdx.x == (local / E) % kThreads) {
-      const int j = local / kSeg;
+    if (wv == local / kSpan && ln == (local / E) % 64) {
+      const int j = (local % kSpan) / (64 * E);
       u32x4 v = raw[0];
 #pragma unroll
       for (int jj = 1; jj < NV; ++jj)
@@ -526,84 +531,208 @@ __device__ __forceinline__ void chain_pack(const ChainArgs& a) {
   if (tid == 0) a.out_offsets[a.B] = total;
 }
 
-// grid = Bs x CP pool tasks for the sequences b0 .. b0+Bs-1, CP = S/SPT per sequence:
-// task t = (sequence b, group c of SPT consecutive segments; a segment is one 16-byte vector
-// per lane, 256*E elements, and a row has S segment slots, the last ones past V weighing 0).
-//  1. Decides for b (identically in each of the sequence's tasks; the last task writes the
-//     count and probabilities), then loads its segments of the final draw's row(s) (two
-//     rows after a rejection) and sums, for each segment, the draw weights and p: per lane
-//     in fp32, across lanes in fp64.
-//  2. Hands the segment masses over and waits for those of the sequence's other tasks --
-//     every task when all_wait is set, else only the sequence's last task.
-//  3. Scans the S segment masses in vocabulary order -- the same way in every waiting
-//     task -- and takes the first segment whose inclusive prefix reaches u * W (W = the
-//     total).  With all_wait the task holding that segment (whose loads of it are still in
-//     the cache) finishes, else the last task: it narrows the segment to a lane
-//     and an element and writes the emitted row (x_0 .. x_{n-1}, the drawn token, then
-//     -1).  If rounding leaves no residual mass (W = 0 after a rejection) the draw uses
-//     the masses of p instead.
-// Tasks wait only for tasks of the same launch.  The host sets all_wait only when every
-// task of the launch fits on the device at once, and otherwise keeps the number of
-// sequences (hence of waiting tasks) to at most half of what fits, so the tasks waited
-// for always find room.  Every wait therefore ends (each is also bounded; on timeout the
-// sequence is flagged invalid).
-//
-// Vocabulary order inside a chunk is segment-major (a segment = one 16-byte vector per
-// lane), then lane, then element.
-template <int DT, int SPT, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0, int all_wait) {
-  constexpr int kRedBytes = 2 * SPT * kThreads * static_cast<int>(sizeof(float));
-  __shared__ __align__(16) unsigned char s_buf[kRedBytes > kStageBytes ? kRedBytes : kStageBytes];
-  __shared__ ChainDecision s_dec;
-  __shared__ double s_d[kWaves];
-  __shared__ int s_i[kWaves];
-  __shared__ double s_base;
-  __shared__ int s_budget, s_y;
+// Bonus and one-hot draws (and the fallback to p) sample target row d.row itself, minus the
+// drafted token after a one-hot rejection.  The stats pass already summed that row in
+// pieces: each wave partial (o, s) covers one contiguous quarter of a chunk, with mass
+// s * exp2(o - O) / S (the same terms whose total is the row's S).  So the draw needs no
+// pass over the whole row.  Units are pieces, or whole segments where a piece is smaller than
+// a segment; the unit whose inclusive prefix reaches u * W (W = the total) is picked from
+// these masses.  A unit of several segments is then read once and its segments' draw
+// weights summed to pick the segment.  Returns the segment and u * W minus the mass before
+// it; `mode` becomes kModeFallbackP if no mass is left after removing the drafted token.
+// Unit masses come from the stats partials and segment masses from the draw weights, so the
+// two agree to rounding; where u * W lies within that rounding of a boundary the last
+// segment (or element) with mass is taken, as for every other draw.  Called by every lane
+// of one task; `red` is shared memory of at least 4 * kThreads floats.
+template <int DT, bool VEC>
+__device__ __forceinline__ void direct_select(const ChainArgs& a, int b, const ChainDecision& d, int* mode,
+                                              const void* row, float* red, int* usel_out, double* tloc_out) {
+  __shared__ double s_tot[kWaves];
+  __shared__ double s_seg[4];
+  __shared__ int s_pick[kWaves];
+  __shared__ double s_before;
+  __shared__ int s_u;
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
-  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;  // elements per segment
+  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int CP = a.S / SPT;  // tasks per sequence
-  const int b = b0 + static_cast<int>(blockIdx.x) / CP;
-  const int c = static_cast<int>(blockIdx.x) % CP;  // this task's group of SPT segments
-  const bool last = c == CP - 1;
-  float* red = reinterpret_cast<float*>(s_buf);  // [2][SPT][kThreads] per-lane masses
+  const int piece = a.nv * (kSeg / kWaves);      // elements of one wave partial
+  const int pper = a.nv >= kWaves ? 1 : kWaves / a.nv;  // pieces per unit
+  const int segs = a.nv >= kWaves ? a.nv / kWaves : 1;  // segments per unit
+  const int unit = pper * piece;
+  const int units = (a.V + unit - 1) / unit;            // <= S <= 4 * kThreads
+  const int per = (units + kThreads - 1) / kThreads;    // <= 4
+  const int u0 = tid * per;
+  const int excl_unit = *mode == kModeOneHot ? d.excl_tok / unit : -1;
+  const RowStat* ps = a.part + (static_cast<size_t>(b) * a.R + d.row) * a.C * kWaves;
+
+  // unit masses in units of p (this lane: units u0 .. u0+per-1)
+  double m[4], mc[4];
+  double local = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    m[q] = 0.0;
+    const int u = u0 + q;
+    if (q < per && u < units) {
+      for (int k = 0; k < pper && u * pper + k < a.C * kWaves; ++k) {
+        const RowStat st = ps[u * pper + k];
+        if (st.o != -INFINITY) m[q] += st.s * static_cast<double>(exp2_fast(st.o - d.Ot));
+      }
+      m[q] /= d.St;
+    }
+    mc[q] = u0 + q == excl_unit ? fmax(0.0, m[q] - static_cast<double>(d.p_excl)) : m[q];
+    local += mc[q];
+  }
+  double W = block_sum(local, s_tot);
+  if (!(W > 0.0) && *mode == kModeOneHot) {  // all of the row's mass sat on the drafted token
+    *mode = kModeFallbackP;
+    local = 0.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      mc[q] = m[q];
+      local += m[q];
+    }
+    W = block_sum(local, s_tot);
+  }
+  const double tt = static_cast<double>(a.u_final[b]) * W;
+
+  // the unit whose inclusive prefix reaches u * W (lanes in unit order)
+  const double incl = wave_inclusive_scan(local);
+  __syncthreads();  // every wave has read block_sum's s_tot
+  if (lane == 63) s_tot[w] = incl;
+  __syncthreads();
+  double before = incl - local;
+  for (int i = 0; i < w; ++i) before += s_tot[i];
+  int cand = INT_MAX, lastu = -1;
+  {
+    double run = before;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      run += mc[q];
+      if (mc[q] > 0.0) {
+        lastu = u0 + q;
+        if (cand == INT_MAX && run >= tt) cand = u0 + q;
+      }
+    }
+  }
+  int usel = block_min_int(cand, s_pick);
+  if (usel == INT_MAX) {  // rounding left u * W above every prefix: last unit with mass
+    usel = block_max_int(lastu, s_pick);
+    if (usel < 0) usel = 0;
+  }
+  if (u0 <= usel && usel < u0 + per) {
+    double run = before;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (u0 + q < usel) run += mc[q];
+    s_before = run;
+  }
+  __syncthreads();
+  if (segs == 1) {  // the unit is one segment
+    *usel_out = usel;
+    *tloc_out = tt - s_before;
+    return;
+  }
+
+  // a unit of 2 or 4 segments: read it once and pick the segment
+  const int excl = *mode == kModeOneHot ? d.excl_tok : -1;
+  const int s_first = usel * segs;
+  u32x4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    v[q] = q < segs ? load_vector<DT, VEC>(row, a.V, ((s_first + q) * kThreads + tid) * E) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float ls = 0.f;
+    if (q < segs) {
+      const int e0 = ((s_first + q) * kThreads + tid) * E;
+#pragma unroll
+      for (int i = 0; i < E; ++i) ls += draw_weight(false, d, EL::get(v[q], i), 0.f, e0 + i, excl);
+    }
+    red[q * kThreads + tid] = ls;
+  }
+  __syncthreads();
+  {  // one 16-lane row of the workgroup sums one segment's 256 lane values
+    const int q = tid >> 4;
+    const int r = tid & 15;
+    double sv = 0.0;
+    if (q < segs) {
+      const float* src = red + q * kThreads + r * 16;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv += static_cast<double>(src[i]);
+    }
+    sv = row16_inclusive_sum(sv);
+    if (q < segs && r == 15) s_seg[q] = sv;
+  }
+  __syncthreads();
+  if (tid == 0) {  // the unit's segments in vocabulary order
+    double run = s_before;
+    int pick = -1, last_pos = -1;
+    double pick_base = 0.0, last_base = 0.0;
+    for (int q = 0; q < segs; ++q) {
+      const double sm = s_seg[q];
+      if (sm > 0.0) {
+        last_pos = q;
+        last_base = run;
+        if (pick < 0 && run + sm >= tt) {
+          pick = q;
+          pick_base = run;
+        }
+      }
+      run += sm;
+    }
+    if (pick < 0) {  // rounding, as above: last segment with mass (the unit's first if none)
+      pick = last_pos >= 0 ? last_pos : 0;
+      pick_base = last_pos >= 0 ? last_base : s_before;
+    }
+    s_u = s_first + pick;
+    s_before = tt - pick_base;
+  }
+  __syncthreads();
+  *usel_out = s_u;
+  *tloc_out = s_before;
+}
+
+// Residual draw after a rejection against draft rows (see chain_pool_kernel, steps 1-3):
+// this task's segment masses of max(0, p - q) and p go out through the slots; the task that
+// finishes the draw waits for the others' and returns true with the segment holding u * W
+// and u * W minus the mass before it.  Tasks that do not finish return false.  `red` is
+// shared memory of 2 * SPT * kThreads floats (per-lane masses).
+template <int DT, int SPT, bool VEC>
+__device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bool last, int all_wait,
+                                            const ChainDecision& d, int* mode, const void* row_t,
+                                            const void* row_d, float* red, int* usel_out, double* tloc_out) {
+  __shared__ double s_d[kWaves];
+  __shared__ int s_i[kWaves];
+  __shared__ double s_base;
+  __shared__ int s_budget;
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  // the slot generation is read after the decision, off its critical path (measured:
+  // 0.5 us less pool time at B=64, K=5, V=128256; 2.3 us at B=256, K=8, V=152064)
   const uint32_t gen = pool_generation(a);
 
-  chain_decide<DT>(a, b, clamped_len(a, b), last, &s_dec, s_buf);
-  const ChainDecision d = uniform_decision(s_dec);
-  if (d.mode == kModeInvalid || d.mode == kModeGreedy) return;  // the decision wrote the row
-  int mode = d.mode;
-  const void* row_t = target_row<DT>(a, b, d.row);
-  const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : row_t;
-
-  // ---- 1. per-lane masses of this task's segments: the draw weights, and p
+  // ---- 1. per-lane masses of this task's segments: max(0, p - q), and p
   {
-    const bool residual = mode == kModeResidual;
-    const int excl = mode == kModeOneHot ? d.excl_tok : -1;
     const int sbase = c * SPT * kSeg;  // first element of this task's segments
     u32x4 rt[SPT], rd[SPT];
 #pragma unroll
     for (int j = 0; j < SPT; ++j) rt[j] = load_vector<DT, VEC>(row_t, a.V, sbase + (j * kThreads + tid) * E);
-    if (residual) {
 #pragma unroll
-      for (int j = 0; j < SPT; ++j) rd[j] = load_vector<DT, VEC>(row_d, a.V, sbase + (j * kThreads + tid) * E);
-    } else {
-#pragma unroll
-      for (int j = 0; j < SPT; ++j) rd[j] = rt[j];
-    }
+    for (int j = 0; j < SPT; ++j) rd[j] = load_vector<DT, VEC>(row_d, a.V, sbase + (j * kThreads + tid) * E);
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
-      const int e0 = sbase + (j * kThreads + tid) * E;
       float aw = 0.f, ap = 0.f;
 #pragma unroll
       for (int i = 0; i < E; ++i) {
         const float pv = exp2_fast(fmaf(EL::get(rt[j], i), d.scale, -d.Ot)) * d.invSt;
-        float wv = pv;
-        if (residual) wv = fmaxf(0.f, pv - exp2_fast(fmaf(EL::get(rd[j], i), d.scale, -d.Od)) * d.invSd);
-        aw += e0 + i == excl ? 0.f : wv;
+        aw += fmaxf(0.f, pv - exp2_fast(fmaf(EL::get(rd[j], i), d.scale, -d.Od)) * d.invSd);
         ap += pv;
       }
       red[j * kThreads + tid] = aw;
@@ -627,7 +756,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
     v = row16_inclusive_sum(v);
     if (q < 2 * SPT && r == 15) put_slot((q < SPT ? mw : mp) + c * SPT + (q % SPT), v, gen);
   }
-  if (!all_wait && !last) return;
+  if (!all_wait && !last) return false;
 
   // ---- 3. every chunk's masses (this lane's share of the units)
   const int per = (units + kThreads - 1) / kThreads;  // <= 4
@@ -663,11 +792,11 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
         for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
         if (tid == 0) a.out_num[b] = -1;
       }
-      return;
+      return false;
     }
     W = block_sum(mass[0] + mass[1] + mass[2] + mass[3], s_d);
-    if (W > 0.0 || !(mode == kModeResidual || mode == kModeOneHot)) break;
-    mode = kModeFallbackP;  // no residual mass left after rounding: draw from p_n itself
+    if (W > 0.0) break;
+    *mode = kModeFallbackP;  // no residual mass left after rounding: draw from p_n itself
   }
 
   // ---- the segment holding u * W
@@ -696,7 +825,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
     usel = block_max_int(lastu, s_i);
     if (usel < 0) usel = 0;
   }
-  if (all_wait && usel / SPT != c) return;  // another task of the sequence holds the segment
+  if (all_wait && usel / SPT != c) return false;  // another task of the sequence holds the segment
   if (u0 <= usel && usel < u0 + per) {
     double run = before;
 #pragma unroll
@@ -705,7 +834,70 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
     s_base = run;
   }
   __syncthreads();
-  const double t_loc = tt - s_base;
+  *usel_out = usel;
+  *tloc_out = tt - s_base;
+  return true;
+}
+
+// grid = Bs x CP pool tasks for the sequences b0 .. b0+Bs-1, CP = S/SPT per sequence:
+// task t = (sequence b, group c of SPT consecutive segments; a segment is one 16-byte vector
+// per lane, 256*E elements, and a row has S segment slots, the last ones past V weighing 0).
+//  1. Decides for b (identically in each of the sequence's tasks; the last task writes the
+//     count and probabilities).  A bonus or one-hot draw is finished by the sequence's
+//     first task alone (direct_select); after a rejection against draft rows each task
+//     loads its segments of the row pair and sums, for each segment, max(0, p - q) and p:
+//     per lane in fp32, across lanes in fp64.
+//  2. Hands the segment masses over and waits for those of the sequence's other tasks --
+//     every task when all_wait is set, else only the sequence's last task.
+//  3. Scans the S segment masses in vocabulary order -- the same way in every waiting
+//     task -- and takes the first segment whose inclusive prefix reaches u * W (W = the
+//     total).  With all_wait the task holding that segment (whose loads of it are still in
+//     the cache) finishes, else the last task: it narrows the segment to a lane
+//     and an element and writes the emitted row (x_0 .. x_{n-1}, the drawn token, then
+//     -1).  If rounding leaves no residual mass (W = 0 after a rejection) the draw uses
+//     the masses of p instead.
+// Tasks wait only for tasks of the same launch.  The host sets all_wait only when every
+// task of the launch fits on the device at once, and otherwise keeps the number of
+// sequences (hence of waiting tasks) to at most half of what fits, so the tasks waited
+// for always find room.  Every wait therefore ends (each is also bounded; on timeout the
+// sequence is flagged invalid).
+//
+// Vocabulary order inside a chunk is segment-major (a segment = one 16-byte vector per
+// lane), then lane, then element.
+template <int DT, int SPT, bool VEC>
+__global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0, int all_wait) {
+  constexpr int kRedBytes = 2 * SPT * kThreads * static_cast<int>(sizeof(float));
+  __shared__ __align__(16) unsigned char s_buf[kRedBytes > kStageBytes ? kRedBytes : kStageBytes];
+  __shared__ ChainDecision s_dec;
+  __shared__ double s_d[kWaves];
+  __shared__ int s_i[kWaves];
+  __shared__ int s_y;
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;  // elements per segment
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int CP = a.S / SPT;  // tasks per sequence
+  const int b = b0 + static_cast<int>(blockIdx.x) / CP;
+  const int c = static_cast<int>(blockIdx.x) % CP;  // this task's group of SPT segments
+  const bool last = c == CP - 1;
+  float* red = reinterpret_cast<float*>(s_buf);  // [2][SPT][kThreads] per-lane masses
+
+  chain_decide<DT>(a, b, clamped_len(a, b), last, &s_dec, s_buf);
+  const ChainDecision d = uniform_decision(s_dec);
+  if (d.mode == kModeInvalid || d.mode == kModeGreedy) return;  // the decision wrote the row
+  int mode = d.mode;
+  const void* row_t = target_row<DT>(a, b, d.row);
+  const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : row_t;
+  int usel;
+  double t_loc;
+  if (mode != kModeResidual) {
+    if (c != 0) return;  // the sequence's first task draws alone
+    direct_select<DT, VEC>(a, b, d, &mode, row_t, red, &usel, &t_loc);
+  } else if (!slot_select<DT, SPT, VEC>(a, b, c, last, all_wait, d, &mode, row_t, row_d, red, &usel, &t_loc)) {
+    return;
+  }
   const int seg_start = usel * kSeg;  // segment u starts at element u * kSeg
 
   // ---- the lane and the element inside that segment
@@ -736,7 +928,9 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   int y;
   if (kmin == INT_MAX) {  // rounding left t_loc above the segment total: last positive weight
     y = block_max_int(last_pos, s_i);
-    if (y < 0) y = seg_start;  // unreachable: the selected segment has positive mass
+    // no positive weight at all: only when a direct draw's chunk mass (from the stats
+    // partials) is positive while every draw weight of the chunk underflows to 0
+    if (y < 0) y = seg_start;
   } else {
     if (tid == kmin) {
       double run = lbefore;
@@ -958,6 +1152,7 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   a.K = K;
   a.V = V;
   a.C = L.C;
+  a.nv = L.nv;
   a.S = L.S;
   a.R = draft_logits ? L.R : K + 1;  // the workspace is laid out for 2K+1 rows; fewer fit
   a.out_tokens = out_tokens;

@@ -136,6 +136,44 @@ __device__ __forceinline__ u32x4 load_vector(const void* row, int V, int e0) {
   return v;
 }
 
+// Load chunk `c` of a row so that wave w of the workgroup holds the w-th quarter of it as
+// one contiguous span: vector j of lane l of wave w is element ((w*NV + j)*64 + l)*E of the
+// chunk.  Each wave instruction still reads 1 KiB of contiguous memory.  Elements past V
+// read as -inf; VEC as for load_chunk.
+template <int DT, int NV, bool VEC, bool NT = false>
+__device__ __forceinline__ void load_wave_span(u32x4 (&raw)[NV], const void* row, int V, int c) {
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  constexpr uint32_t kNegInf2 = EL::kNegInfBits | (E == 8 ? (EL::kNegInfBits << 16) : 0u);
+  const int base = c * ChunkShape<DT, NV>::kChunk;
+  const int first = (static_cast<int>(threadIdx.x >> 6) * NV * 64 + static_cast<int>(threadIdx.x & 63));  // vector index
+  if (VEC) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
+                                                    static_cast<size_t>(base) * EL::kBytes) + first;
+    if (base + ChunkShape<DT, NV>::kChunk <= V) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) raw[j] = load16<NT>(p + j * 64);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        raw[j] = base + (first + j * 64) * E < V ? load16<NT>(p + j * 64)
+                                                 : u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int e0 = base + (first + j * 64) * E;
+    u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int e = e0 + i;
+      EL::put(v, i, e < V ? EL::bits(row, e) : EL::kNegInfBits);
+    }
+    raw[j] = v;
+  }
+}
+
 // ---------------------------------------------------------------- wave64 scans and reductions
 //
 // Cross-lane steps use DPP (data-parallel primitives: operands read from another lane

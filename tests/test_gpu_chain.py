@@ -1,5 +1,6 @@
 """GPU parity of spec_verify_chain against the oracle on the seeded workload recipes."""
 
+import dataclasses
 import os
 
 import numpy as np
@@ -66,6 +67,19 @@ def test_chunk_sizes_give_identical_decisions(nv, monkeypatch):
     monkeypatch.setenv("SPEC_NV", nv)
     _run(synth.chain_config_high_accept_bf16(5, B=6, K=4, V=40000))
     _run(synth.chain_config_small_f32(5, B=6, K=4, V=9000))
+
+
+@pytest.mark.parametrize("nv", ["1", "2", "4", "8", "16"])
+def test_chunk_sizes_one_hot_and_bonus_draws(nv, monkeypatch):
+    # one-hot drafts (no draft rows) and bonus draws sample a target row from the stats
+    # pass's piece masses, reading only the piece that holds the draw: every chunk size,
+    # ragged tails (V = 40000, 9000) and a batch where most sequences take the bonus
+    monkeypatch.setenv("SPEC_NV", nv)
+    _run(dataclasses.replace(synth.chain_config_high_accept_bf16(6, B=12, K=4, V=40000), draft=None))
+    _run(dataclasses.replace(synth.chain_config_small_f32(6, B=12, K=4, V=9000), draft=None))
+    inp = synth.chain_config_high_accept_bf16(7, B=12, K=2, V=40000)
+    _, rep = _run(dataclasses.replace(inp, u_accept=np.full_like(inp.u_accept, 2.0 ** -24)))
+    assert rep.sequences == 12
 
 
 def test_repeat_calls_are_bit_identical():
