@@ -1005,12 +1005,14 @@ static int chain_nv(long long rows, int V, int epv, bool vec) {
   return nv;
 }
 
-// `vec`: the rows can be read with 16-byte loads (this sets the chunk size).
-static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool vec) {
+// `vec`: the rows can be read with 16-byte loads; `one_hot`: no draft rows (K+1 rows per
+// sequence are streamed instead of 2K+1).  Both set the chunk size; the workspace regions keep
+// room for 2K+1 rows either way.
+static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool vec, bool one_hot) {
   ChainLayout L{};
   const int epv = dtype == SPEC_BF16 ? 8 : 4;
   L.R = 2 * K + 1;
-  L.nv = chain_nv(static_cast<long long>(B) * L.R, V, epv, vec);
+  L.nv = chain_nv(static_cast<long long>(B) * (one_hot ? K + 1 : L.R), V, epv, vec);
   const long long chunk = static_cast<long long>(L.nv) * kThreads * epv;
   L.C = static_cast<int>((V + chunk - 1) / chunk);
   const long long seg = static_cast<long long>(kThreads) * epv;
@@ -1114,10 +1116,15 @@ extern "C" {
 
 size_t spec_verify_chain_workspace_size(int B, int K, int V, spec_dtype_t dtype) {
   if (B <= 0 || K < 1 || K > SPEC_MAX_K || V < 1) return 0;
-  // either chunk size may be chosen at call time (it depends on the pointers' alignment)
-  const size_t with_vec = chain_layout(B, K, V, dtype, true).bytes;
-  const size_t without = chain_layout(B, K, V, dtype, false).bytes;
-  return with_vec > without ? with_vec : without;
+  // any of the chunk sizes may be chosen at call time (they depend on the pointers' alignment
+  // and on whether draft rows are given)
+  size_t bytes = 0;
+  for (int vec = 0; vec < 2; ++vec)
+    for (int one_hot = 0; one_hot < 2; ++one_hot) {
+      const size_t b = chain_layout(B, K, V, dtype, vec != 0, one_hot != 0).bytes;
+      bytes = b > bytes ? b : bytes;
+    }
+  return bytes;
 }
 
 spec_status_t spec_verify_chain(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
@@ -1148,7 +1155,7 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
     return fail(SPEC_ERR_UNSUPPORTED, "B*(K+1)*V too large");
   const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits) &&
                    (draft_logits == nullptr || aligned16(draft_logits));
-  const ChainLayout L = chain_layout(B, K, V, dtype, vec);
+  const ChainLayout L = chain_layout(B, K, V, dtype, vec, draft_logits == nullptr);
   const double groups = static_cast<double>(B) * L.R * L.C;
   if (groups > 2147483647.0) return fail(SPEC_ERR_UNSUPPORTED, "grid of %.0f workgroups too large", groups);
   if (L.S > 4 * kThreads || L.C * kWaves > kStage)

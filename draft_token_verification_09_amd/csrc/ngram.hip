@@ -16,6 +16,9 @@
 // combine them, and the largest n with an occurrence wins.  The context goes
 // through shared memory in tiles of kTile tokens (plus the n_max - 1 before each
 // tile), loaded with independent reads, so the comparisons never wait on memory.
+// The first tile is read before the context length arrives (it does not depend on it);
+// when the whole context fits in it, the suffix and the proposed tokens come from shared
+// memory too, so the kernel waits on global memory once before its stores.
 #include "device_common.h"
 #include "host_runtime.h"
 #include "spec_verify.h"
@@ -37,6 +40,8 @@ __global__ __launch_bounds__(kNgramThreads) void ngram_propose_kernel(const int3
   const int32_t* c = context + static_cast<size_t>(b) * L_max;
   int32_t* od = out_draft + static_cast<size_t>(b) * K;
   const int L = context_len[b];
+  const int pre = min(kTile, L_max);  // the first tile: tokens [0, pre), in bounds whatever L is
+  for (int i = tid; i < pre; i += kNgramThreads) s_ctx[i] = c[i];
   if (L < 1 || L > L_max) {
     for (int k = tid; k < K; k += kNgramThreads) od[k] = -1;
     if (tid == 0) {
@@ -45,8 +50,10 @@ __global__ __launch_bounds__(kNgramThreads) void ngram_propose_kernel(const int3
     }
     return;
   }
-  if (tid < n_max) s_suffix[tid] = tid < L ? c[L - 1 - tid] : 0;
+  const bool one_tile = L <= pre;  // the whole context is in the first tile, and stays there
   if (tid <= n_max) s_first[tid] = INT_MAX;
+  __syncthreads();  // the first tile is in shared memory
+  if (tid < n_max) s_suffix[tid] = tid < L ? (one_tile ? s_ctx[L - 1 - tid] : c[L - 1 - tid]) : 0;
   // This lane's earliest end position per n.  A lane visits end positions in increasing
   // order, so first[n] is set once, when the lane's longest match so far first reaches n.
   int first[SPEC_MAX_NGRAM_N + 1];
@@ -57,8 +64,9 @@ __global__ __launch_bounds__(kNgramThreads) void ngram_propose_kernel(const int3
     // end positions e in [t0, t1) need tokens [lo, t1)
     const int t1 = min(t0 + kTile, L - 1);
     const int lo = max(0, t0 - (n_max - 1));
-    __syncthreads();  // the previous tile's comparisons are done
-    for (int i = tid; i < t1 - lo; i += kNgramThreads) s_ctx[i] = c[lo + i];
+    __syncthreads();  // the previous tile's comparisons (and the suffix) are done
+    if (t0 > 0)       // the first tile, [0, t1) within [0, pre), is already loaded
+      for (int i = tid; i < t1 - lo; i += kNgramThreads) s_ctx[i] = c[lo + i];
     __syncthreads();
     for (int e = t0 + tid; e < t1; e += kNgramThreads) {
       int ml = 0;
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(kNgramThreads) void ngram_propose_kernel(const int3
   }
   const int start = best_e + 1;  // first continuation token
   const int len = best_n ? min(K, L - start) : 0;
-  for (int k = tid; k < K; k += kNgramThreads) od[k] = k < len ? c[start + k] : -1;
+  for (int k = tid; k < K; k += kNgramThreads) od[k] = k < len ? (one_tile ? s_ctx[start + k] : c[start + k]) : -1;
   if (tid == 0) {
     out_len[b] = len;
     if (out_match_n) out_match_n[b] = best_n;

@@ -100,6 +100,25 @@ def test_ngram_variable_lengths_zipf():
     _ngram_compare(pr.context, pr.context_len, 1, 4, 5)
 
 
+def test_ngram_multi_tile_contexts():
+    # contexts longer than one 4096-token shared-memory tile: lengths around the tile ends,
+    # Zipf prompts, and unique-token contexts whose only earlier copy of the suffix is planted
+    # across a tile boundary
+    lens = np.array([1, 2, 5, 4095, 4096, 4097, 4098, 5000, 8191, 8192, 8193, 8194, 9000, 9999, 10000, 7000],
+                    np.int32)
+    pr = synth.ngram_prompts(4, B=16, L=10000, V=32000, lengths=lens)
+    _ngram_compare(pr.context, pr.context_len, 1, 4, 5)
+    starts = [4090, 4092, 4093, 4094, 4095, 4096, 8186, 8189, 8190, 8191, 8192, 100]
+    B, L_max = len(starts), 10000
+    ctx = np.tile(np.arange(L_max, dtype=np.int32) + 7, (B, 1))
+    lens = np.full(B, L_max, np.int32)
+    for i, p in enumerate(starts):
+        n = 2 + i % 3  # planted copy of the last n tokens, straddling the boundary
+        ctx[i, p:p + n] = ctx[i, L_max - n:]
+    g, ref = _ngram_compare(ctx, lens, 1, 4, 5)
+    assert (ref.match_n >= 2).all()
+
+
 def test_ngram_invalid_length_flagged():
     ctx = np.zeros((3, 8), np.int32)
     # lengths 0 and 9 (> L_max) are flagged; [0, 0, 0, 0] matches n = 3 at j = 0, leaving one token
