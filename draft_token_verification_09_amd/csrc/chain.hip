@@ -985,24 +985,37 @@ struct ChainLayout {
   size_t off_gath, off_part, off_wseg, off_wsegp, bytes;
 };
 
-// Vectors per lane in one stats chunk: for bf16 rows read with 16-byte loads, 16 if that
-// gives at least 1024 workgroups; otherwise the largest of 8, 4, 2, 1 that does (else 1),
-// raised if needed until a row's partials fit the decision's staging.  (Measured per call
-// with bf16 rows: at B=64, K=5, V=128256, 16 vectors 50.6 us, 8 vectors 52.7, 4 vectors 58;
-// at B=256, K=8, V=152064, 16 vectors 246 us, 8 vectors 269.  Element-wise loads keep at most
-// 8, whose registers would not fit twice.)  SPEC_NV in the environment forces 1, 2, 4 or 8,
-// or 16 where 16 may be chosen.
+// Vectors per lane in one stats chunk.  The largest chunk (16 vectors for bf16 rows read with
+// 16-byte loads, else 8) that gives at least 1024 workgroups with at most kMaxChunks chunks a
+// row; if none reaches 1024 workgroups within that bound (small batches), the smallest chunk
+// within it; if even the largest chunk leaves more than kMaxChunks a row, the largest chunk.
+// Bounding the chunks a row bounds the partials every pool task combines before it can
+// decide, which sets the latency of small batches.  Measured per call: at B=64, K=5,
+// V=128256 bf16, 16 vectors 50.6 us, 8 vectors 52.7, 4 vectors 58; at B=256, K=8, V=152064,
+// 16 vectors 246 us, 8 vectors 269; at K=5, V=128256 bf16, B=1: 4 vectors (16 chunks) 13.1 us
+// against 23.1 with 1 vector (63 chunks, the 1024-workgroup target alone), B=4: 15.9 against
+// 19.0 with 2 vectors, B=16: 8 vectors 22.3 either way; at B=1, K=5, V=32000 fp32: 2 vectors
+// 12.8 us, 4 vectors 12.1, against 15.9 with 1 vector.  Element-wise loads keep at most 8,
+// whose registers would not fit twice.  SPEC_NV in the environment forces 1, 2, 4 or 8, or
+// 16 where 16 may be chosen.
+constexpr int kMaxChunks = 16;
+
 static int chain_nv(long long rows, int V, int epv, bool vec) {
   const int forced = env_int("SPEC_NV", 0);
-  if (forced == 16 && vec && epv == 8) return 16;
-  if (vec && epv == 8 && forced == 0) {
-    const long long chunk = 16LL * kThreads * epv;
-    if (rows * ((V + chunk - 1) / chunk) >= 1024) return 16;
+  const int top = vec && epv == 8 ? 16 : 8;
+  if (forced == 16 && top == 16) return 16;
+  if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
+  const auto chunks = [&](int nv) {
+    const long long chunk = static_cast<long long>(nv) * kThreads * epv;
+    return (V + chunk - 1) / chunk;
+  };
+  int pick = 0;
+  for (int nv = top; nv >= 1; nv >>= 1) {
+    if (chunks(nv) > kMaxChunks) break;  // smaller chunks only give more
+    pick = nv;
+    if (rows * chunks(nv) >= 1024) return nv;
   }
-  int nv = choose_nv(rows, V, epv, 1024);
-  while (nv < 8 && (V + static_cast<long long>(nv) * kThreads * epv - 1) / (static_cast<long long>(nv) * kThreads * epv) * kWaves > kStage)
-    nv *= 2;
-  return nv;
+  return pick ? pick : top;
 }
 
 // `vec`: the rows can be read with 16-byte loads; `one_hot`: no draft rows (K+1 rows per
