@@ -988,14 +988,15 @@ struct ChainLayout {
 // Vectors per lane in one stats chunk.  The largest chunk (16 vectors for bf16 rows read with
 // 16-byte loads, else 8) that gives at least 1024 workgroups with at most kMaxChunks chunks a
 // row; if none reaches 1024 workgroups within that bound (small batches), the smallest chunk
-// within it; if even the largest chunk leaves more than kMaxChunks a row, the largest chunk.
+// within it but no smaller than 4 vectors (16 KiB); if even the largest chunk leaves more
+// than kMaxChunks a row, the largest chunk.
 // Bounding the chunks a row bounds the partials every pool task combines before it can
 // decide, which sets the latency of small batches.  Measured per call: at B=64, K=5,
 // V=128256 bf16, 16 vectors 50.6 us, 8 vectors 52.7, 4 vectors 58; at B=256, K=8, V=152064,
 // 16 vectors 246 us, 8 vectors 269; at K=5, V=128256 bf16, B=1: 4 vectors (16 chunks) 13.1 us
 // against 23.1 with 1 vector (63 chunks, the 1024-workgroup target alone), B=4: 15.9 against
-// 19.0 with 2 vectors, B=16: 8 vectors 22.3 either way; at B=1, K=5, V=32000 fp32: 2 vectors
-// 12.8 us, 4 vectors 12.1, against 15.9 with 1 vector.  Element-wise loads keep at most 8,
+// 19.0 with 2 vectors, B=16: 8 vectors 22.3 either way; at B=1, K=5, V=32000 fp32: 4 vectors
+// 12.1 us, 2 vectors 12.8, 8 vectors 13.0, against 15.9 with 1 vector.  Element-wise loads keep at most 8,
 // whose registers would not fit twice.  SPEC_NV in the environment forces 1, 2, 4 or 8, or
 // 16 where 16 may be chosen.
 constexpr int kMaxChunks = 16;
@@ -1015,7 +1016,7 @@ static int chain_nv(long long rows, int V, int epv, bool vec) {
     pick = nv;
     if (rows * chunks(nv) >= 1024) return nv;
   }
-  return pick ? pick : top;
+  return pick ? (pick < 4 ? 4 : pick) : top;
 }
 
 // `vec`: the rows can be read with 16-byte loads; `one_hot`: no draft rows (K+1 rows per
