@@ -11,11 +11,11 @@
 // Two kernels (three with packed output), ordered by the stream:
 //
 //  chain_stats  grid = B x R x C: R = K+1 target rows (+ K draft rows when draft logits
-//               are given), C chunks per row.  Each workgroup reduces one chunk
-//               (non-temporal 16-byte loads) to (o, s) = (max(l) * log2(e)/T,
-//               sum exp2(l * log2(e)/T - o)) and, if the chunk holds the row's drafted
-//               token x_k, copies l(x_k) out of its registers.  This is the pass that
-//               reads every logit, once.
+//               are given), C chunks per row.  Each wave of a workgroup reduces one
+//               contiguous quarter of a chunk (non-temporal 16-byte loads) to
+//               (o, s) = (max(l) * log2(e)/T, sum exp2(l * log2(e)/T - o)), and the lane
+//               holding the row's drafted token x_k copies l(x_k) out of its registers.
+//               This is the pass that reads every logit, once.
 //  chain_pool   grid = B x S/4 tasks (see chain_pool_kernel): every task of a sequence
 //               combines the partials into per-row (O, S) and evaluates p(x_k), q(x_k),
 //               alpha_k and the accept tests of all drafted positions at once (one lane
@@ -23,8 +23,8 @@
 //               rejection against draft rows, each task sums max(0, p - q) over its 4
 //               segments of the row pair (a segment = one 16-byte vector per lane), and the
 //               token is drawn from those masses.  A bonus or one-hot draw samples a target
-//               row whose chunk masses the stats pass already holds, so one task per
-//               sequence reads only the chunk that holds the draw.
+//               row whose piece masses (one per wave partial) the stats pass already holds,
+//               so one task per sequence reads only the piece that holds the draw.
 //  chain_pack   grid = 1, only for packed output: offsets and packed tokens.
 //
 // Softmax is evaluated in the exp2 domain: with scale = log2(e)/T,
