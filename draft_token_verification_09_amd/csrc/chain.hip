@@ -391,8 +391,9 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   __syncthreads();
 }
 
-// grid = B x R x C: workgroup g reduces one chunk of one row, each of its waves to one
-// partial of its quarter of the chunk (one contiguous span, see load_wave_span).
+// grid = B x R x C: each workgroup reduces one chunk g of one row (g in XCD-blocked order, see
+// xcd_blocked_index), each of its waves to one partial of its quarter of the chunk (one
+// contiguous span, see load_wave_span).
 template <int DT, int NV, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_fetch_add(a.runs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   constexpr int E = EL::kPerVec;
   constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
   constexpr int kSpan = kChunk / kWaves;  // elements of one wave's quarter
-  const int g = blockIdx.x;
+  const int g = xcd_blocked_index();
   const int c = g % a.C;
   const int rr = (g / a.C) % a.R;
   const int b = g / (a.C * a.R);

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void tree_argmax_kernel(TreeArgs a) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
-  const int g = blockIdx.x;
+  const int g = xcd_blocked_index();  // chunk of this workgroup
   const int c = g % a.C;
   const int r = (g / a.C) % a.N1;
   const int b = g / (a.C * a.N1);
