@@ -82,6 +82,15 @@ def test_chunk_sizes_one_hot_and_bonus_draws(nv, monkeypatch):
     assert rep.sequences == 12
 
 
+@pytest.mark.parametrize("B, V", [(160, 128256), (1000, 16385)])
+def test_one_hot_batches_beyond_one_resident_launch(B, V):
+    # one-hot drafts put each sequence's first pool task first; at B=160, V=128256 the 2560 pool
+    # tasks do not all fit at once, and at B=1000, V=16385 the pool runs in two launches
+    inp = dataclasses.replace(synth.chain_config_high_accept_bf16(21, B=B, K=5, V=V), draft=None)
+    seqs = sorted(set(list(range(0, B, max(1, B // 24))) + [B - 1]))
+    _run(inp, seqs=seqs)
+
+
 def test_repeat_calls_are_bit_identical():
     inp = synth.chain_config_high_accept_bf16(2, B=16, V=60000)
     a = chain_on_gpu(inp)
