@@ -12,11 +12,13 @@ every step streams its logits from HBM.
 Prints ONE JSON line (rank 0).  `value` is verified draft positions per second
 (B*K per step); `roofline` reports the dominant kernel (chain_stats, the pass that
 reads every logit once) against the MI355X HBM peak, with its duration from HIP events
-stamped at its own dispatch and completion on its stream (hipExtLaunchKernelGGL);
-`cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.  Secondary workloads (greedy
-tree verify, low-acceptance chain, n-gram propose + one-hot verify, the small
-fp32 chain) are reported under "other_workloads" unless --quick is given.
+stamped at its own dispatch and completion on its stream (hipExtLaunchKernelGGL), and
+against the achievable read rate (pure reads of the same bytes in the same access
+shape, timed the same way); `roofline.call` gives the whole call's algorithmic rate.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload, on all
+the cores of this process's share (worker processes) and on one core.  Secondary
+workloads (greedy tree verify, low-acceptance chain, n-gram propose + one-hot verify,
+the small fp32 chain) are reported under "other_workloads" unless --quick is given.
 """
 
 from __future__ import annotations
@@ -211,22 +213,81 @@ def bench_chain_workload(make, name, warmup, steps, dev, kernel_timing=True, pas
                 steps=steps)
 
 
-def cpu_baseline(host_inp, budget_s=15.0):
-    """The oracle, as it stands, on a bounded sample of sequences of the same workload."""
+# ---------------------------------------------------------------- CPU baseline (the oracle)
+#
+# The oracle verifies one sequence at a time.  It is timed in two settings on the host: one
+# process on one core, and a pool of worker processes (one per core of this process's CPU
+# share, at most CPU_POOL_MAX) that each verify their own sequences of the same input set.
+# The pool is forked before the GPU is initialised, with the input set already in memory, so
+# the workers share it and never touch the GPU.
+
+CPU_POOL_MAX = 16
+_CPU_INPUT = None  # the headline's input set 0, set before the pool forks
+
+
+def cpu_pool_size() -> int:
+    try:
+        share = len(os.sched_getaffinity(0))
+    except AttributeError:
+        share = os.cpu_count() or 1
+    return max(1, min(share, CPU_POOL_MAX, int(os.environ.get("OMP_NUM_THREADS", CPU_POOL_MAX))))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_loop(first: int, step: int, budget_s: float):
+    """Verify sequences first, first + step, ... of the input set (cycling) for budget_s seconds."""
     import oracle
 
+    inp = _CPU_INPUT
     t0 = time.perf_counter()
     done = 0
-    while time.perf_counter() - t0 < budget_s and done < 64 * host_inp.B:
-        oracle.verify_chain(host_inp.target, host_inp.draft, host_inp.dtype, host_inp.tokens, host_inp.temperature,
-                            host_inp.u_accept, host_inp.u_final, draft_len=host_inp.draft_len,
-                            seqs=[done % host_inp.B])
+    while time.perf_counter() - t0 < budget_s:
+        oracle.verify_chain(inp.target, inp.draft, inp.dtype, inp.tokens, inp.temperature, inp.u_accept, inp.u_final,
+                            draft_len=inp.draft_len, seqs=[(first + done * step) % inp.B])
         done += 1
-    dt = time.perf_counter() - t0
-    return dict(value=done * host_inp.K / dt, unit="positions/s", cores=1, kind="oracle",
-                sample=f"{done} sequence verifications cycling over the {host_inp.B} sequences (K={host_inp.K}, "
-                       f"V={host_inp.V}, {host_inp.dtype}) of input set 0, one after another, {dt:.1f} s; "
-                       f"float64 NumPy on one thread")
+    return done, time.perf_counter() - t0
+
+
+def _oracle_worker(args):
+    return _oracle_loop(*args)
+
+
+def start_cpu_pool(host_inp):
+    """Fork the worker pool (before any GPU work) with the input set in memory."""
+    import multiprocessing as mp
+
+    global _CPU_INPUT
+    _CPU_INPUT = host_inp
+    n = cpu_pool_size()
+    return mp.get_context("fork").Pool(n), n
+
+
+def cpu_baseline(pool, workers: int, one_core_s=12.0, pool_s=8.0):
+    """The oracle, as it stands, on a bounded sample of sequences of the headline workload."""
+    inp = _CPU_INPUT
+    done1, dt1 = _oracle_loop(0, 1, one_core_s)
+    res = pool.map(_oracle_worker, [(w, workers, pool_s) for w in range(workers)])
+    done_all = sum(d for d, _ in res)
+    dt_all = max(t for _, t in res)
+    shape = f"K={inp.K}, V={inp.V}, {inp.dtype}"
+    return dict(
+        value=done_all * inp.K / dt_all, unit="positions/s", cores=workers, kind="oracle",
+        sample=f"{done_all} sequence verifications in {dt_all:.1f} s by {workers} worker processes, each cycling "
+               f"over its own sequences of the {inp.B} of input set 0 ({shape}); float64 NumPy, one thread each",
+        cpu_model=cpu_model(), host_cpus=os.cpu_count(),
+        one_core=dict(value=done1 * inp.K / dt1, cores=1,
+                      sample=f"{done1} sequence verifications cycling over the {inp.B} sequences in {dt1:.1f} s, "
+                             f"one process on one thread"))
 
 
 def other_workloads(warmup, steps, dev):
@@ -488,6 +549,33 @@ def kernels_per_call(kernels, steps):
     return {k: round(v[1] / steps * 1e3, 3) for k, v in kernels.items()}
 
 
+def achievable_read(dev, nbytes, warmup, steps):
+    """The achievable read rate the streaming pass is compared with: pure reads of the same bytes
+    in its access shape (one workgroup per chunk, XCD-blocked, non-temporal 16-byte loads), for
+    chunks of 16, 32 and 64 KiB, back to back over rotating buffers that exceed the last-level
+    cache, each launch timed by events stamped at its own dispatch and completion (as the
+    stats kernel is).  Returns (best GB/s, {chunk KiB: GB/s}, bytes per launch)."""
+    import torch
+
+    import draft_token_verification_09_amd as sv
+
+    per = nbytes // 65536 * 65536
+    n_sets = sets_needed(per)
+    bufs = [torch.empty(per, dtype=torch.uint8, device=dev).random_(0, 255) for _ in range(n_sets)]
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    rates = {}
+    for chunk in (16384, 32768, 65536):
+        def call(i, chunk=chunk):
+            sv.spec_probe_read(bufs[i], out, chunk)
+
+        _, k = time_calls(call, n_sets, warmup, steps, kernel_timing=True)
+        launches, ms = k["probe_read"]
+        rates[chunk // 1024] = round(per / (ms / launches * 1e-3) / 1e9, 1)
+    del bufs
+    torch.cuda.empty_cache()
+    return max(rates.values()), rates, per
+
+
 def probe(dev, nbytes=1 << 30):
     """Streaming read and copy probes over `nbytes` (calibration for counters and roofline)."""
     import torch
@@ -498,7 +586,7 @@ def probe(dev, nbytes=1 << 30):
     dst = torch.empty_like(src)
     out = torch.zeros(1, dtype=torch.int32, device=dev)
     res = {}
-    for name, fn in (("probe_read", lambda: sv.spec_probe_read(src, out)),
+    for name, fn in (("probe_read", lambda: sv.spec_probe_read(src, out, 65536)),
                      ("probe_copy", lambda: sv.spec_probe_copy(src, dst))):
         for _ in range(3):
             fn()
@@ -534,10 +622,19 @@ def main():
               f"without communication, so run one process per GPU.", file=sys.stderr)
         sys.exit(2)
 
+    import synth
+
+    # the headline's input set 0, generated before any GPU work so that the CPU baseline's
+    # worker pool can be forked with it in memory (forking after the GPU is initialised is not)
+    progress("generating input set 0 of the headline workload")
+    host0 = synth.chain_config_high_accept_bf16(0)
+    pool = None
+    if not args.no_cpu_baseline:
+        pool, workers = start_cpu_pool(host0)
+
     import torch
 
     import draft_token_verification_09_amd as sv
-    import synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -547,7 +644,7 @@ def main():
     progress(f"device {torch.cuda.get_device_name(dev)}")
 
     workload = "chain_verify_B64_K5_V128256_bf16_high_accept"
-    head = bench_chain_workload(lambda s: synth.chain_config_high_accept_bf16(s), workload,
+    head = bench_chain_workload(lambda s: host0 if s == 0 else synth.chain_config_high_accept_bf16(s), workload,
                                 args.warmup, args.steps, dev)
     ms = head["ms"]
     B, K, V = 64, 5, 128256
@@ -558,6 +655,9 @@ def main():
     achieved = logits_bytes / stats_avg_s / 1e9
     digest = source_digest(STATS_SOURCES)
     traffic = read_traffic(ROOF_KERNEL, "B64_K5_V128256_bf16", digest)
+    progress("achievable read rate (pure reads in the stats pass's access shape)")
+    achievable, by_chunk, probe_bytes = achievable_read(dev, logits_bytes, args.warmup, args.steps)
+    call_bytes = head["bytes"]
 
     result = {
         "metric": "verified draft positions/sec and achieved HBM GB/s (% of peak), 1 MI355X",
@@ -587,11 +687,20 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": logits_bytes,
+            "achievable": achievable,
+            "frac_of_achievable": round(achieved / achievable, 4),
+            "achievable_probe": {"kernel": "probe_read", "bytes_per_launch": probe_bytes, "GBps_by_chunk_KiB": by_chunk},
+            "call": {"achieved": round(call_bytes / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(call_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "frac_of_achievable": round(call_bytes / (ms * 1e-3) / 1e9 / achievable, 4),
+                     "algorithmic_bytes_per_call": call_bytes},
         },
     }
-    if not args.no_cpu_baseline:
-        progress("cpu baseline (oracle on a bounded sample)")
-        result["cpu_baseline"] = cpu_baseline(head["host"])
+    if pool is not None:
+        progress(f"cpu baseline (oracle on a bounded sample, 1 and {workers} cores)")
+        result["cpu_baseline"] = cpu_baseline(pool, workers)
+        pool.close()
+        pool.join()
     if not args.quick:
         result["other_workloads"] = other_workloads(args.warmup, max(20, args.steps // 2), dev)
     if args.probe:

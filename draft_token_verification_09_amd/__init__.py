@@ -6,6 +6,10 @@ ctypes binding (binding.py) whose functions carry the C entry points' names.
 """
 
 from .binding import (  # noqa: F401
+    FLAG_INVALID,
+    FLAG_TIMED_OUT,
+    SPEC_KNOB_CHUNK_VECTORS,
+    SPEC_KNOB_POLL_LIMIT,
     ChainResult,
     GATE_CLOSED,
     GATE_HALF_OPEN,
@@ -16,6 +20,7 @@ from .binding import (  # noqa: F401
     SpecGate,
     TreeMaskResult,
     TreeResult,
+    knob,
     lib,
     loaded_library_path,
     ngram_propose,
@@ -26,6 +31,8 @@ from .binding import (  # noqa: F401
     prepare_spec_verify_tree,
     prepare_spec_verify_tree_greedy,
     spec_commit_path,
+    spec_get_knob,
+    spec_set_knob,
     spec_probe_copy,
     spec_probe_read,
     spec_timing_collect,

@@ -8,6 +8,7 @@ raises -- there is no fallback path.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -23,6 +24,10 @@ SPEC_BF16 = 1
 SPEC_MAX_K = 64
 SPEC_MAX_TREE_NODES = 1024
 SPEC_MAX_NGRAM_N = 16
+SPEC_KNOB_CHUNK_VECTORS = 0
+SPEC_KNOB_POLL_LIMIT = 1
+FLAG_INVALID = -1    # count output of a sequence with invalid device data
+FLAG_TIMED_OUT = -2  # count output of a sequence whose hand-over wait gave up
 
 
 class SpecError(RuntimeError):
@@ -70,7 +75,9 @@ _SIGNATURES = {
     "spec_timing_collect": (_i32, []),
     "spec_timing_entry": (_i32, [_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_longlong),
                                  ctypes.POINTER(ctypes.c_double)]),
-    "spec_probe_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "spec_set_knob": (_i32, [_i32, _i32]),
+    "spec_get_knob": (_i32, [_i32]),
+    "spec_probe_read": (_i32, [_vp, _sz, _sz, _vp, _vp]),
     "spec_probe_copy": (_i32, [_vp, _vp, _sz, _vp]),
 }
 
@@ -645,9 +652,31 @@ def spec_timing_collect() -> List[Tuple[str, int, float]]:
     return out
 
 
-def spec_probe_read(src: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+def spec_set_knob(knob_id: int, value: int) -> None:
+    """Process-wide override of a library choice (include/spec_measure.h); value < 0 restores
+    the default."""
+    _check("spec_set_knob", lib().spec_set_knob(knob_id, value))
+
+
+def spec_get_knob(knob_id: int) -> int:
+    return int(lib().spec_get_knob(knob_id))
+
+
+@contextlib.contextmanager
+def knob(knob_id: int, value: int):
+    """Set a knob for the duration of a block, then restore its previous value."""
+    old = spec_get_knob(knob_id)
+    spec_set_knob(knob_id, value)
+    try:
+        yield
+    finally:
+        spec_set_knob(knob_id, old)
+
+
+def spec_probe_read(src: torch.Tensor, out: torch.Tensor, chunk_bytes: int = 65536, stream=None) -> None:
     s = _stream(stream, src.device)
-    _check("spec_probe_read", lib().spec_probe_read(src.data_ptr(), src.numel() * src.element_size(), out.data_ptr(), s))
+    _check("spec_probe_read", lib().spec_probe_read(src.data_ptr(), src.numel() * src.element_size(), chunk_bytes,
+                                                    out.data_ptr(), s))
 
 
 def spec_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

@@ -136,6 +136,7 @@ struct ChainArgs {
   int32_t* out_packed;
   int32_t* out_offsets;
   uint32_t gen;         // the host's number for this call (see pool_generation)
+  int poll_limit;       // polls of a missing hand-over word before the wait gives up
   uint32_t* runs;       // workspace counter advanced by every stats kernel run
   RowStat* part;        // [B, R, C, 4] partials, one per wave of each chunk
   float* gath;          // [B, R] logit of the drafted token in each scoring row
@@ -705,18 +706,18 @@ __device__ __forceinline__ void direct_select(const ChainArgs& a, int b, const C
 }
 
 // Residual draw after a rejection against draft rows (see chain_pool_kernel, steps 1-3):
-// this task's segment masses of max(0, p - q) and p go out through the slots; the task that
-// finishes the draw waits for the others' and returns true with the segment holding u * W
-// and u * W minus the mass before it.  Tasks that do not finish return false.  `red` is
-// shared memory of 2 * SPT * kThreads floats (per-lane masses).
+// this task's segment masses of max(0, p - q) and p go out through the slots; the sequence's
+// last task waits for the others' and returns true with the segment holding u * W and u * W
+// minus the mass before it.  Other tasks return false, and so does a last task whose wait
+// gave up (it flags the sequence).  `red` is shared memory of 2 * SPT * kThreads floats
+// (per-lane masses).
 template <int DT, int SPT, bool VEC>
-__device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bool last, int all_wait,
-                                            const ChainDecision& d, int* mode, const void* row_t,
-                                            const void* row_d, float* red, int* usel_out, double* tloc_out) {
+__device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bool last, const ChainDecision& d,
+                                            int* mode, const void* row_t, const void* row_d, float* red,
+                                            int* usel_out, double* tloc_out) {
   __shared__ double s_d[kWaves];
   __shared__ int s_i[kWaves];
   __shared__ double s_base;
-  __shared__ int s_budget;
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
@@ -765,7 +766,7 @@ __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bo
     v = row16_inclusive_sum(v);
     if (q < 2 * SPT && r == 15) put_slot((q < SPT ? mw : mp) + c * SPT + (q % SPT), v, gen);
   }
-  if (!all_wait && !last) return false;
+  if (!last) return false;
 
   // ---- 3. every chunk's masses (this lane's share of the units)
   const int per = (units + kThreads - 1) / kThreads;  // <= 4
@@ -774,9 +775,8 @@ __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bo
   double W = 0.0;
   for (int attempt = 0; attempt < 2; ++attempt) {
     const SlotDouble* slots = attempt == 0 ? mw : mp;
-    if (tid == 0) s_budget = kPollLimit;
-    bool arrived = true;
-    for (;;) {
+    bool arrived = false;
+    for (int polls = 0; polls < a.poll_limit; ++polls) {
       int missing = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -784,23 +784,18 @@ __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bo
         mass[q] = 0.0;
         if (q < per && u < units && !get_slot(slots + u, gen, &mass[q])) missing = 1;
       }
-      if (!__syncthreads_or(missing)) break;
-      if (tid == 0) {
-        short_pause();
-        --s_budget;
-      }
-      __syncthreads();
-      if (s_budget <= 0) {
-        arrived = false;
+      if (!__syncthreads_or(missing)) {
+        arrived = true;
         break;
       }
+      short_pause();
     }
-    if (!arrived) {  // flag the sequence rather than wait on
-      if (last) {
-        int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-        for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
-        if (tid == 0) a.out_num[b] = -1;
-      }
+    if (!arrived) {  // flag the sequence rather than wait on (this task alone writes its row)
+      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+      for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
+      if (tid == 0) a.out_num[b] = kFlagTimedOut;
+      if (a.out_probs)
+        for (int i = tid; i < a.K * 3; i += kThreads) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
       return false;
     }
     W = block_sum(mass[0] + mass[1] + mass[2] + mass[3], s_d);
@@ -834,7 +829,6 @@ __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bo
     usel = block_max_int(lastu, s_i);
     if (usel < 0) usel = 0;
   }
-  if (all_wait && usel / SPT != c) return false;  // another task of the sequence holds the segment
   if (u0 <= usel && usel < u0 + per) {
     double run = before;
 #pragma unroll
@@ -856,20 +850,22 @@ __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bo
 //     first task alone (direct_select); after a rejection against draft rows each task
 //     loads its segments of the row pair and sums, for each segment, max(0, p - q) and p:
 //     per lane in fp32, across lanes in fp64.
-//  2. Hands the segment masses over and waits for those of the sequence's other tasks --
-//     every task when all_wait is set, else only the sequence's last task.
-//  3. Scans the S segment masses in vocabulary order -- the same way in every waiting
-//     task -- and takes the first segment whose inclusive prefix reaches u * W (W = the
-//     total).  With all_wait the task holding that segment (whose loads of it are still in
-//     the cache) finishes, else the last task: it narrows the segment to a lane
+//  2. Hands the segment masses over; the sequence's last task waits for those of its
+//     siblings.
+//  3. The last task scans the S segment masses in vocabulary order and takes the first
+//     segment whose inclusive prefix reaches u * W (W = the total), narrows it to a lane
 //     and an element and writes the emitted row (x_0 .. x_{n-1}, the drawn token, then
 //     -1).  If rounding leaves no residual mass (W = 0 after a rejection) the draw uses
 //     the masses of p instead.
-// Tasks wait only for tasks of the same launch.  The host sets all_wait only when every
-// task of the launch fits on the device at once, and otherwise keeps the number of
-// sequences (hence of waiting tasks) to at most half of what fits, so the tasks waited
-// for always find room.  Every wait therefore ends (each is also bounded; on timeout the
-// sequence is flagged invalid).
+// Only a sequence's last task waits, and only for tasks of the same launch that come before
+// it in dispatch order and never wait themselves, so every wait ends even when other
+// kernels share the device.  The host also keeps a launch to at most half as many sequences
+// (hence waiting tasks) as pool workgroups fit at once, so the tasks waited for find room
+// quickly.  Each wait is bounded besides: after the poll limit the last task flags the
+// sequence -2 (it alone writes the sequence's count, probabilities and row, so the flag
+// never mixes with a result).  (Measured at B=64, K=5, V=128256 bf16: letting every task
+// wait, so that the task holding the drawn segment finishes with it still in cache, gave the
+// same pool time, 14.5 us per call.)
 //
 // Task order: with first_tasks_first (set by the host when there are no draft rows, so every
 // sampled draw is a bonus or one-hot draw finished by task 0) the launch's first Bs
@@ -883,8 +879,7 @@ __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bo
 // Vocabulary order inside a chunk is segment-major (a segment = one 16-byte vector per
 // lane), then lane, then element.
 template <int DT, int SPT, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0, int all_wait,
-                                                               int first_tasks_first) {
+__global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0, int first_tasks_first) {
   constexpr int kRedBytes = 2 * SPT * kThreads * static_cast<int>(sizeof(float));
   __shared__ __align__(16) unsigned char s_buf[kRedBytes > kStageBytes ? kRedBytes : kStageBytes];
   __shared__ ChainDecision s_dec;
@@ -922,7 +917,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   if (mode != kModeResidual) {
     if (c != 0) return;  // the sequence's first task draws alone
     direct_select<DT, VEC>(a, b, d, &mode, row_t, red, &usel, &t_loc);
-  } else if (!slot_select<DT, SPT, VEC>(a, b, c, last, all_wait, d, &mode, row_t, row_d, red, &usel, &t_loc)) {
+  } else if (!slot_select<DT, SPT, VEC>(a, b, c, last, d, &mode, row_t, row_d, red, &usel, &t_loc)) {
     return;
   }
   const int seg_start = usel * kSeg;  // segment u starts at element u * kSeg
@@ -1006,12 +1001,12 @@ struct ChainLayout {
 // against 23.1 with 1 vector (63 chunks, the 1024-workgroup target alone), B=4: 15.9 against
 // 19.0 with 2 vectors, B=16: 8 vectors 22.3 either way; at B=1, K=5, V=32000 fp32: 4 vectors
 // 12.1 us, 2 vectors 12.8, 8 vectors 13.0, against 15.9 with 1 vector.  Element-wise loads keep at most 8,
-// whose registers would not fit twice.  SPEC_NV in the environment forces 1, 2, 4 or 8, or
-// 16 where 16 may be chosen.
+// whose registers would not fit twice.  SPEC_KNOB_CHUNK_VECTORS forces 1, 2, 4 or 8, or 16
+// where 16 may be chosen.
 constexpr int kMaxChunks = 16;
 
 static int chain_nv(long long rows, int V, int epv, bool vec) {
-  const int forced = env_int("SPEC_NV", 0);
+  const int forced = knob(SPEC_KNOB_CHUNK_VECTORS);
   const int top = vec && epv == 8 ? 16 : 8;
   if (forced == 16 && top == 16) return 16;
   if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
@@ -1096,15 +1091,12 @@ static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
   {
     const auto kernel = chain_pool_kernel<DT, kPoolSegments, VEC>;
     const int CP = a.S / kPoolSegments;
-    const int slots = pool_slots(reinterpret_cast<const void*>(kernel), slots_cache);
-    // every task waits when the whole launch fits at once; else only last tasks wait,
-    // at most half of what fits per launch
-    const int all_wait = static_cast<long long>(a.B) * CP <= slots && env_int("SPEC_POOL_ALL_WAIT", 1) != 0 ? 1 : 0;
-    const int per_launch = all_wait ? a.B : max(1, slots / 2);
+    // one waiting task per sequence: at most half as many sequences per launch as fit at once
+    const int per_launch = max(1, pool_slots(reinterpret_cast<const void*>(kernel), slots_cache) / 2);
     for (int b0 = 0; b0 < a.B; b0 += per_launch) {
       const int bs = min(per_launch, a.B - b0);
       LaunchScope scope("chain_pool", stream);
-      scope.launch(kernel, dim3(static_cast<unsigned>(static_cast<long long>(bs) * CP)), dim3(kThreads), stream, a, b0, all_wait,
+      scope.launch(kernel, dim3(static_cast<unsigned>(static_cast<long long>(bs) * CP)), dim3(kThreads), stream, a, b0,
                    a.draft == nullptr ? 1 : 0);
       const spec_status_t st = scope.finish();
       if (st != SPEC_OK) return st;
@@ -1211,6 +1203,7 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   a.out_offsets = out_offsets;
   char* ws = static_cast<char*>(workspace);
   a.gen = next_generation();
+  a.poll_limit = knob(SPEC_KNOB_POLL_LIMIT);
   a.runs = static_cast<uint32_t*>(workspace);
   a.gath = reinterpret_cast<float*>(ws + L.off_gath);
   a.part = reinterpret_cast<RowStat*>(ws + L.off_part);

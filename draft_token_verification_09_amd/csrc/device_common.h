@@ -467,8 +467,10 @@ __device__ __forceinline__ bool get_tagged_double(const uint64_t* w, uint32_t ta
 
 // Polls of a hand-over word that has not been written yet before a wait gives up (each
 // poll takes at least a memory round trip, about a microsecond: a quarter of a second or
-// more), and the pause between polls.
+// more; the default of a host-side knob), and the pause between polls.  A sequence whose
+// wait gave up is flagged with kFlagTimedOut in its count output (invalid input gives -1).
 constexpr int kPollLimit = 1 << 18;
+constexpr int kFlagTimedOut = -2;
 __device__ __forceinline__ void short_pause() { __builtin_amdgcn_s_sleep(2); }
 
 }  // namespace specv

@@ -7,6 +7,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "spec_measure.h"
 #include "spec_verify.h"
 
 namespace specv {
@@ -50,12 +51,12 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Integer tuning knob from the environment (read on every call; absent -> dflt).
-int env_int(const char* name, int dflt);
+// Current value of a knob of spec_measure.h (its default unless a caller set it).
+int knob(spec_knob_t k);
 
 // Vectors (16 B each) per lane in one chunk: the largest of 8, 4, 2, 1 that still
 // gives at least `min_groups` workgroups over `rows` rows of V elements, else 1.
-// SPEC_NV in the environment forces a value (1, 2, 4 or 8).
+// SPEC_KNOB_CHUNK_VECTORS forces 1, 2, 4 or 8.
 int choose_nv(long long rows, int V, int elems_per_vec, long long min_groups);
 
 }  // namespace specv

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -26,14 +27,23 @@ spec_status_t fail(spec_status_t status, const char* fmt, ...) {
   return status;
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  return atoi(v);
+// ---------------------------------------------------------------- knobs
+
+namespace {
+
+constexpr int kKnobs = 2;
+constexpr int kKnobDefault[kKnobs] = {0, kPollLimit};
+std::atomic<int> g_knobs[kKnobs] = {{kKnobDefault[0]}, {kKnobDefault[1]}};
+
+}  // namespace
+
+int knob(spec_knob_t k) {
+  const int i = static_cast<int>(k);
+  return i >= 0 && i < kKnobs ? g_knobs[i].load(std::memory_order_relaxed) : 0;
 }
 
 int choose_nv(long long rows, int V, int elems_per_vec, long long min_groups) {
-  const int forced = env_int("SPEC_NV", 0);
+  const int forced = knob(SPEC_KNOB_CHUNK_VECTORS);
   if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
   for (int nv = 8; nv >= 1; nv >>= 1) {
     const long long chunk = static_cast<long long>(nv) * kThreads * elems_per_vec;
@@ -110,21 +120,21 @@ LaunchScope::~LaunchScope() {
 
 // ---------------------------------------------------------------- small kernels
 
-__global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4* src, size_t n16, uint32_t* out) {
-  const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+// Pure read in the streaming passes' access shape: one workgroup per chunk of NV * 4 KiB,
+// chunks in XCD-blocked order, each wave one contiguous quarter of its chunk, every
+// non-temporal 16-byte load issued before any is used.  The words are folded with XOR and
+// a never-true test on the result keeps the loads alive.
+template <int NV>
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4* src, uint32_t* out) {
+  const int g = xcd_blocked_index();
+  const u32x4* p = src + static_cast<size_t>(g) * NV * kThreads + (threadIdx.x >> 6) * NV * 64 + (threadIdx.x & 63);
+  u32x4 v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = __builtin_nontemporal_load(p + j * 64);
   uint32_t acc = 0;
-  size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc += a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 a = src[i];
-    acc += a.x ^ a.y ^ a.z ^ a.w;
-  }
-  __shared__ int s_i[kWaves];
-  const int r = block_max_int(static_cast<int>(acc & 0x7fffffff), s_i);
-  if (threadIdx.x == 0 && r == -1) *out = 1u;  // never true: keeps the loads alive
+#pragma unroll
+  for (int j = 0; j < NV; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  if (wave_max_int(static_cast<int>(acc & 0x7fffffff)) == -1 && threadIdx.x == 0) *out = 1u;
 }
 
 __global__ __launch_bounds__(kThreads) void probe_copy_kernel(const u32x4* src, u32x4* dst, size_t n16) {
@@ -157,6 +167,22 @@ const char* spec_status_string(spec_status_t status) {
 }
 
 const char* spec_last_error(void) { return g_last_error; }
+
+spec_status_t spec_set_knob(spec_knob_t k, int value) {
+  const int i = static_cast<int>(k);
+  if (i < 0 || i >= kKnobs) return fail(SPEC_ERR_INVALID_ARG, "unknown knob %d", i);
+  if (value < 0) value = kKnobDefault[i];
+  const bool ok = k != SPEC_KNOB_CHUNK_VECTORS ||
+                  (value == 0 || value == 1 || value == 2 || value == 4 || value == 8 || value == 16);
+  if (!ok) return fail(SPEC_ERR_INVALID_ARG, "value %d is not allowed for knob %d", value, i);
+  g_knobs[i].store(value, std::memory_order_relaxed);
+  return SPEC_OK;
+}
+
+int spec_get_knob(spec_knob_t k) {
+  const int i = static_cast<int>(k);
+  return i >= 0 && i < kKnobs ? g_knobs[i].load(std::memory_order_relaxed) : -1;
+}
 
 spec_status_t spec_timing_enable(int enable) {
   TimingState& t = timing();
@@ -213,12 +239,20 @@ spec_status_t spec_timing_entry(int index, const char** name, long long* launche
   return SPEC_OK;
 }
 
-spec_status_t spec_probe_read(const void* src, size_t bytes, uint32_t* out, spec_stream_t stream) {
-  if (!src || !out || bytes == 0 || bytes % 16 || !aligned16(src))
-    return fail(SPEC_ERR_INVALID_ARG, "probe_read needs a 16-byte aligned source and size");
-  const unsigned grid = static_cast<unsigned>(device_cu_count() * 8);
-  LaunchScope scope("probe_read", static_cast<hipStream_t>(stream));
-  scope.launch(probe_read_kernel, dim3(grid), dim3(kThreads), static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), bytes / 16, out);
+spec_status_t spec_probe_read(const void* src, size_t bytes, size_t chunk_bytes, uint32_t* out,
+                              spec_stream_t stream) {
+  if (chunk_bytes != 16384 && chunk_bytes != 32768 && chunk_bytes != 65536)
+    return fail(SPEC_ERR_INVALID_ARG, "probe_read chunk must be 16, 32 or 64 KiB");
+  if (!src || !out || bytes == 0 || bytes % chunk_bytes || !aligned16(src))
+    return fail(SPEC_ERR_INVALID_ARG, "probe_read needs a 16-byte aligned source of whole chunks");
+  if (bytes / chunk_bytes > 2147483647u) return fail(SPEC_ERR_UNSUPPORTED, "probe_read grid too large");
+  const dim3 grid(static_cast<unsigned>(bytes / chunk_bytes));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const u32x4* p = static_cast<const u32x4*>(src);
+  LaunchScope scope("probe_read", s);
+  if (chunk_bytes == 16384) scope.launch(probe_read_kernel<4>, grid, dim3(kThreads), s, p, out);
+  else if (chunk_bytes == 32768) scope.launch(probe_read_kernel<8>, grid, dim3(kThreads), s, p, out);
+  else scope.launch(probe_read_kernel<16>, grid, dim3(kThreads), s, p, out);
   return scope.finish();
 }
 

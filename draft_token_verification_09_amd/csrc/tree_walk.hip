@@ -78,6 +78,7 @@ struct TsArgs {
   int32_t* out_tokens;
   int32_t* out_nodes;
   uint32_t gen;     // the host's number for this call
+  int poll_limit;   // polls of a missing hand-over word before a wait gives up
   uint32_t* epoch;  // [B] run counters
   uint64_t* slots;  // [B, 2, W, kTsWords]
 };
@@ -156,13 +157,18 @@ __device__ __forceinline__ void ts_next_epoch(const TsArgs& a, int b) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(a.epoch + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void ts_write_invalid(const TsArgs& a, int b) {
+// Flags sequence b: out_len = code (-1 invalid input, -2 a hand-over wait gave up), path
+// outputs -1.  Only workgroup 0 of a sequence writes its outputs, in every case, so that a
+// flag never mixes with a result.
+constexpr int kFlagInvalid = -1;
+
+__device__ __forceinline__ void ts_write_flag(const TsArgs& a, int b, int code) {
   const int D1 = a.max_depth + 1;
   for (int k = threadIdx.x; k < D1; k += kThreads) {
     a.out_tokens[static_cast<size_t>(b) * D1 + k] = -1;
     a.out_nodes[static_cast<size_t>(b) * D1 + k] = -1;
   }
-  if (threadIdx.x == 0) a.out_len[b] = -1;
+  if (threadIdx.x == 0) a.out_len[b] = code;
 }
 
 // Stage the sequence's parents and tokens (and uniforms) in shared memory and check them,
@@ -230,7 +236,7 @@ struct TsShared {
   double d[2 * kWaves];
   float f[2 * kWaves];
   int i[kWaves];
-  int budget, y;
+  int y;
   float lt[SPEC_MAX_TREE_NODES];  // logits of the current node's children tokens (target row)
   float ld[SPEC_MAX_TREE_NODES];  // (draft row)
   int path[SPEC_MAX_TREE_NODES + 1];
@@ -244,13 +250,14 @@ struct TsShared {
 
 // Wait until every workgroup of the sequence has published `tag` in `slot_base[w]`, then
 // copy its first `nd` doubles (words 0-1 and 2-3) and `nf` floats (words 4 and 5) into
-// shared memory.  False if the wait gave up.
+// shared memory.  False if the wait gave up (after `limit` polls that found a word missing;
+// at once when limit is 0).
 __device__ __forceinline__ bool ts_gather(const uint64_t* slot_base, int W, uint32_t tag, int nd, int nf,
-                                          TsShared& sh, double* dst_d0, double* dst_d1, float* dst_f0,
+                                          int limit, double* dst_d0, double* dst_d1, float* dst_f0,
                                           float* dst_f1) {
   const int tid = threadIdx.x;
-  if (tid == 0) sh.budget = kPollLimit;
-  for (;;) {
+  for (int polls = 0;; ++polls) {
+    if (polls >= limit) return false;
     int missing = 0;
     if (tid < W) {
       const uint64_t* sl = slot_base + static_cast<size_t>(tid) * kTsWords;
@@ -270,13 +277,31 @@ __device__ __forceinline__ bool ts_gather(const uint64_t* slot_base, int W, uint
       }
     }
     if (!__syncthreads_or(missing)) return true;
-    if (tid == 0) {
-      short_pause();
-      --sh.budget;
-    }
-    __syncthreads();
-    if (sh.budget <= 0) return false;
+    short_pause();
   }
+}
+
+// Wait for one tagged 32-bit word (the drawn token that the drawing workgroup hands to
+// workgroup 0); false if the wait gave up, as for ts_gather.
+__device__ __forceinline__ bool ts_wait_word(const uint64_t* word, uint32_t tag, int limit, uint32_t* v) {
+  for (int polls = 0;; ++polls) {
+    if (polls >= limit) return false;
+    if (!__syncthreads_or(get_tagged_u32(word, tag, v) ? 0 : 1)) return true;
+    short_pause();
+  }
+}
+
+// The accepted path (sh.path[0 .. plen-1]), its tokens, then y, then -1.
+__device__ __forceinline__ void ts_write_path(const TsArgs& a, int b, const TsShared& sh, int plen, int y) {
+  const int D1 = a.max_depth + 1;
+  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * D1;
+  int32_t* on = a.out_nodes + static_cast<size_t>(b) * D1;
+  for (int k = threadIdx.x; k < D1; k += kThreads) {
+    const int node = k < plen ? sh.path[k] : -1;
+    on[k] = node;
+    ot[k] = k < plen ? sh.tok[node] : (k == plen ? y : -1);
+  }
+  if (threadIdx.x == 0) a.out_len[b] = plen;
 }
 
 template <int DT, bool VEC>
@@ -292,7 +317,7 @@ __device__ __forceinline__ void ts_walk_body(const TsArgs& a, int b0, uint32_t g
   const int w = static_cast<int>(blockIdx.x) % W;
   const int N1 = a.N1, V = a.V;
   if (!ts_stage(a, b, sh.par, sh.tok, sh.ua)) {
-    if (w == 0) ts_write_invalid(a, b);
+    if (w == 0) ts_write_flag(a, b, kFlagInvalid);
     return;
   }
   const float T = a.temperature[b];
@@ -384,9 +409,9 @@ __device__ __forceinline__ void ts_walk_body(const TsArgs& a, int b0, uint32_t g
       store_agent(mine + 4, tagged(__float_as_uint(ot), tag));
       store_agent(mine + 5, tagged(__float_as_uint(od), tag));
     }
-    if (!ts_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, 2, 2, sh, sh.s[0], sh.s[1],
-                   sh.o[0], sh.o[1])) {
-      ts_write_invalid(a, b);
+    if (!ts_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, 2, 2, a.poll_limit, sh.s[0],
+                   sh.s[1], sh.o[0], sh.o[1])) {
+      if (w == 0) ts_write_flag(a, b, kFlagTimedOut);
       return;
     }
     if (step == 0) ts_next_epoch(a, b);
@@ -422,7 +447,7 @@ __device__ __forceinline__ void ts_walk_body(const TsArgs& a, int b0, uint32_t g
       const double alpha = uniform(qx > 0.0 ? fmin(1.0, rx / qx) : (rx > 0.0 ? 1.0 : 0.0));
       if (static_cast<double>(sh.ua[kid]) <= alpha) {
         if (plen >= a.max_depth) {  // the path outgrows its output row
-          if (w == 0) ts_write_invalid(a, b);
+          if (w == 0) ts_write_flag(a, b, kFlagInvalid);
           return;
         }
         if (tid == 0) sh.path[plen] = kid;
@@ -453,9 +478,9 @@ __device__ __forceinline__ void ts_walk_body(const TsArgs& a, int b0, uint32_t g
       tag = ts_tag(gen, step);
       if (tid == 0) put_tagged_double(mine, part, tag);
       double* tmp = sh.s[0];  // reuse: the stats of this node are combined already
-      if (!ts_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, 1, 0, sh, tmp, nullptr,
-                     nullptr, nullptr)) {
-        ts_write_invalid(a, b);
+      if (!ts_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, 1, 0, a.poll_limit, tmp,
+                     nullptr, nullptr, nullptr)) {
+        if (w == 0) ts_write_flag(a, b, kFlagTimedOut);
         return;
       }
       ++step;
@@ -490,7 +515,19 @@ __device__ __forceinline__ void ts_walk_body(const TsArgs& a, int b0, uint32_t g
     }
     if (wsel < 0) wsel = wlast >= 0 ? wlast : 0;
   }
-  if (w != wsel) return;
+  const int D1 = a.max_depth + 1;
+  if (w != wsel) {
+    if (w != 0) return;
+    // workgroup 0 writes the row once the drawing workgroup has handed the token over
+    uint32_t yv = 0;
+    if (!ts_wait_word(slots + (static_cast<size_t>(step & 1) * W + wsel) * kTsWords + 4, ts_tag(gen, step),
+                      a.poll_limit, &yv)) {
+      ts_write_flag(a, b, kFlagTimedOut);
+      return;
+    }
+    ts_write_path(a, b, sh, plen, static_cast<int>(yv));
+    return;
+  }
   double before = 0.0;
   for (int q = 0; q < wsel; ++q) before += sh.mass[q];
   const double t_loc = uniform(tt - before);
@@ -580,15 +617,15 @@ __device__ __forceinline__ void ts_walk_body(const TsArgs& a, int b0, uint32_t g
     __syncthreads();
     y = sh.y;
   }
-  const int D1 = a.max_depth + 1;
-  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * D1;
-  int32_t* on = a.out_nodes + static_cast<size_t>(b) * D1;
-  for (int k = tid; k < D1; k += kThreads) {
-    const int node = k < plen ? sh.path[k] : -1;
-    on[k] = node;
-    ot[k] = k < plen ? sh.tok[node] : (k == plen ? y : -1);
+  if (w != 0) {  // hand the token to workgroup 0, which writes the row
+    // (this workgroup's slot of parity `step` held its word of step - 2, which every
+    // workgroup had read before publishing step - 1, read here in the last gather)
+    if (tid == 0)
+      store_agent(slots + (static_cast<size_t>(step & 1) * W + w) * kTsWords + 4,
+                  tagged(static_cast<uint32_t>(y), ts_tag(gen, step)));
+    return;
   }
-  if (tid == 0) a.out_len[b] = plen;
+  ts_write_path(a, b, sh, plen, y);
 }
 
 template <int DT, bool VEC>
@@ -603,7 +640,6 @@ struct TgShared {
   float i[kTsMaxSlices];  // their first indices (int bits)
   float wv[kWaves];
   int wi[kWaves];
-  int budget;
   int nf, nn;             // frontier and next-frontier sizes
   int front[SPEC_MAX_TREE_NODES];
   int nxt[SPEC_MAX_TREE_NODES];
@@ -613,10 +649,10 @@ struct TgShared {
 };
 
 // Same hand-over as ts_gather, for the (max, first index) pair of each slice.
-__device__ __forceinline__ bool tg_gather(const uint64_t* slot_base, int W, uint32_t tag, TgShared& sh) {
+__device__ __forceinline__ bool tg_gather(const uint64_t* slot_base, int W, uint32_t tag, int limit, TgShared& sh) {
   const int tid = threadIdx.x;
-  if (tid == 0) sh.budget = kPollLimit;
-  for (;;) {
+  for (int polls = 0;; ++polls) {
+    if (polls >= limit) return false;
     int missing = 0;
     if (tid < W) {
       const uint64_t* sl = slot_base + static_cast<size_t>(tid) * kTsWords;
@@ -625,12 +661,7 @@ __device__ __forceinline__ bool tg_gather(const uint64_t* slot_base, int W, uint
       if (ts_get_float(sl + 5, tag, &f)) sh.i[tid] = f; else missing = 1;
     }
     if (!__syncthreads_or(missing)) return true;
-    if (tid == 0) {
-      short_pause();
-      --sh.budget;
-    }
-    __syncthreads();
-    if (sh.budget <= 0) return false;
+    short_pause();
   }
 }
 
@@ -653,7 +684,7 @@ __device__ __forceinline__ void tg_walk_body(const TsArgs& a, int b0, uint32_t g
 #pragma unroll
   for (int j = 0; j < kTsNV; ++j) rt[j] = load_vector<DT, VEC>(tbase, V, sl0 + (j * kThreads + tid) * E);
   if (!ts_stage(a, b, sh.par, sh.tok, nullptr)) {
-    if (w == 0) ts_write_invalid(a, b);
+    if (w == 0) ts_write_flag(a, b, kFlagInvalid);
     return;
   }
   if (tid == 0) {
@@ -709,8 +740,8 @@ __device__ __forceinline__ void tg_walk_body(const TsArgs& a, int b0, uint32_t g
         store_agent(mine + 4, tagged(__float_as_uint(sv), tag));
         store_agent(mine + 5, tagged(static_cast<uint32_t>(si), tag));
       }
-      if (!tg_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, sh)) {
-        ts_write_invalid(a, b);
+      if (!tg_gather(slots + static_cast<size_t>(step & 1) * W * kTsWords, W, tag, a.poll_limit, sh)) {
+        if (w == 0) ts_write_flag(a, b, kFlagTimedOut);
         return;
       }
       if (step == 0) ts_next_epoch(a, b);
@@ -741,7 +772,7 @@ __device__ __forceinline__ void tg_walk_body(const TsArgs& a, int b0, uint32_t g
     const int nn = uniform(sh.nn);
     if (nn == 0) break;
     if (++depth > a.max_depth) {  // the accepted path outgrows its output row
-      if (w == 0) ts_write_invalid(a, b);
+      if (w == 0) ts_write_flag(a, b, kFlagInvalid);
       return;
     }
     if (tid == 0) {
@@ -896,6 +927,7 @@ spec_status_t tree_greedy_walk(const void* target_logits, spec_dtype_t dtype, co
   a.out_tokens = out_tokens;
   a.out_nodes = out_path_nodes;
   a.gen = ts_next_generation();
+  a.poll_limit = knob(SPEC_KNOB_POLL_LIMIT);
   char* ws = static_cast<char*>(workspace);
   a.epoch = reinterpret_cast<uint32_t*>(ws);
   a.slots = reinterpret_cast<uint64_t*>(ws + L.off_slots);
@@ -957,6 +989,7 @@ spec_status_t spec_verify_tree(const void* target_logits, const void* draft_logi
   a.out_tokens = out_tokens;
   a.out_nodes = out_path_nodes;
   a.gen = ts_next_generation();
+  a.poll_limit = knob(SPEC_KNOB_POLL_LIMIT);
   char* ws = static_cast<char*>(workspace);
   a.epoch = reinterpret_cast<uint32_t*>(ws);
   a.slots = reinterpret_cast<uint64_t*>(ws + L.off_slots);

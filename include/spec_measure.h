@@ -33,9 +33,40 @@ int spec_timing_collect(void);
  * kernel name (static storage), number of launches, summed milliseconds. */
 spec_status_t spec_timing_entry(int index, const char** name, long long* launches, double* total_ms);
 
-/* Read-only streaming probe: sums `bytes` (a multiple of 16, 16-byte aligned)
- * of device memory at `src` as 32-bit words into *out (device uint32). */
-spec_status_t spec_probe_read(const void* src, size_t bytes, uint32_t* out, spec_stream_t stream);
+/* Process-wide overrides of choices the library otherwise makes itself, for tests
+ * and measurements.  Each knob starts at its default; spec_set_knob with a negative
+ * value restores it.  Set knobs only while no call of the library is being issued on
+ * another thread; a call reads every knob once, when it is issued.
+ *
+ *   SPEC_KNOB_CHUNK_VECTORS  16-byte vectors per lane in one chunk of the streaming
+ *                            passes (chain row statistics, tree row argmax): 1, 2, 4,
+ *                            8 or 16 (16 only for bf16 chain rows with 16-byte loads);
+ *                            0 (default) = the library's choice.
+ *   SPEC_KNOB_POLL_LIMIT     polls of a hand-over word that has not arrived before a
+ *                            cross-workgroup wait gives up and flags its sequence -2
+ *                            (default 262144, at least a quarter of a second); 0 = give
+ *                            up before the first poll, so that every sequence that needs
+ *                            a wait is flagged (a test of the flag path).
+ */
+typedef enum spec_knob {
+  SPEC_KNOB_CHUNK_VECTORS = 0,
+  SPEC_KNOB_POLL_LIMIT = 1
+} spec_knob_t;
+
+spec_status_t spec_set_knob(spec_knob_t knob, int value);
+
+/* Current value of a knob (its default unless set), or -1 for an unknown knob. */
+int spec_get_knob(spec_knob_t knob);
+
+/* Read-only streaming probe in the access shape of the library's streaming passes: one
+ * workgroup per `chunk_bytes` chunk (16384, 32768 or 65536), chunks dealt to the XCDs in
+ * contiguous blocks, each wave reading one contiguous quarter of its chunk with
+ * non-temporal 16-byte loads.  `bytes` is a whole number of chunks at a 16-byte aligned
+ * `src`; *out (device uint32) is written only in a case that never occurs (it keeps the
+ * loads alive).  The figure it gives is the achievable read rate the streaming passes are
+ * compared with. */
+spec_status_t spec_probe_read(const void* src, size_t bytes, size_t chunk_bytes, uint32_t* out,
+                              spec_stream_t stream);
 
 /* Plain copy of `bytes` (a multiple of 16, 16-byte aligned) from src to dst. */
 spec_status_t spec_probe_copy(const void* src, void* dst, size_t bytes, spec_stream_t stream);

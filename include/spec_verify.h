@@ -79,6 +79,26 @@ const char* spec_status_string(spec_status_t status);
 /* Detail message of the last non-OK status returned on the calling thread. */
 const char* spec_last_error(void);
 
+/* Count output (out_num_accepted, out_accept_len) of a sequence whose device data is
+ * invalid, and of one whose cross-workgroup hand-over wait gave up (see below). */
+#define SPEC_FLAG_INVALID (-1)
+#define SPEC_FLAG_TIMED_OUT (-2)
+
+/* Hand-over waits.  spec_verify_chain (after a rejection against draft rows),
+ * spec_verify_tree and spec_verify_tree_greedy (without out_argmax) split each
+ * sequence over several workgroups that hand partial sums to each other inside one
+ * kernel and wait for them.  spec_verify_chain's waiting workgroup only waits for
+ * workgroups dispatched before it, which never wait, so its waits end whatever else
+ * runs on the device.  The tree walks' workgroups of one sequence wait for each other:
+ * a launch holds at most half the workgroups the device runs at once, so one or two
+ * such calls in flight together always fit, but more (on other streams, or next to
+ * other kernels that wait on their own workgroups) can keep a sequence's workgroups
+ * from all running at once.  Every wait is bounded (SPEC_KNOB_POLL_LIMIT in
+ * spec_measure.h, at least a quarter of a second by default): a sequence whose wait
+ * gives up gets count SPEC_FLAG_TIMED_OUT and -1 in its other outputs, written by the
+ * one workgroup that writes the sequence's outputs, so a flag never mixes with a
+ * result.  Issue the call again for such sequences. */
+
 /* ---------------------------------------------------------------------------
  * Chain verification by modified rejection sampling.
  *
@@ -128,7 +148,9 @@ const char* spec_last_error(void);
  *
  * Invalid device data for sequence b (token out of range, k_b outside [0, K],
  * T negative or not finite, a uniform outside (0, 1] when T > 0) sets out_num_accepted[b]
- * = -1, out_tokens[b, :] = -1, out_probs[b] = 0 and gives it no packed tokens.
+ * = -1, out_tokens[b, :] = -1, out_probs[b] = 0 and gives it no packed tokens.  A
+ * sequence whose hand-over wait gave up (see "Hand-over waits") gets the same outputs
+ * with out_num_accepted[b] = SPEC_FLAG_TIMED_OUT (-2).
  * Limits: 1 <= K <= SPEC_MAX_K, V >= 1, B >= 0, B*(K+1)*V < 2^47.
  * Logits may be -inf (probability 0); +inf and NaN are not supported; each
  * used row needs at least one finite logit.
@@ -169,7 +191,10 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
  * workspace     >= spec_verify_tree_greedy_workspace_size() bytes, as for the chain.
  *
  * Invalid device data for sequence b (bad parent, token out of range, accepted
- * depth > max_depth) sets out_accept_len[b] = -1 and its path outputs to -1.
+ * depth > max_depth) sets out_accept_len[b] = -1 and its path outputs to -1.  Without
+ * out_argmax the rows are read by a walk that hands partial results between
+ * workgroups: a sequence whose wait gave up gets out_accept_len[b] = -2 and -1 path
+ * outputs (see "Hand-over waits").
  * Limits: 1 <= N1 <= SPEC_MAX_TREE_NODES, V >= 1, 0 <= max_depth < N1 + 1.
  * ------------------------------------------------------------------------- */
 size_t spec_verify_tree_greedy_workspace_size(int B, int N1, int V, spec_dtype_t dtype);
@@ -210,7 +235,8 @@ spec_status_t spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dt
  * Only the rows on the walk are read.  Invalid device data for sequence b (bad
  * parent, token out of range, temperature not > 0 or not finite, a uniform outside
  * (0, 1], accepted depth > max_depth) sets out_accept_len[b] = -1 and its outputs to
- * -1.  Each used row needs a finite logit.
+ * -1; a sequence whose hand-over wait gave up gets out_accept_len[b] = -2 and -1
+ * outputs (see "Hand-over waits").  Each used row needs a finite logit.
  * Limits: 1 <= N1 <= SPEC_MAX_TREE_NODES, 0 <= max_depth <= N1, V <= 524288 (bf16) or
  * 262144 (fp32): at most 64 vocabulary slices of 8192 bf16 or 4096 fp32 logits.
  * ------------------------------------------------------------------------- */

@@ -15,6 +15,7 @@ from .workloads import (  # noqa: F401
     philox,
     uniforms_open_closed,
     chain_inputs,
+    chain_shared_rows,
     chain_config_small_f32,
     chain_config_high_accept_bf16,
     chain_config_low_accept_bf16,

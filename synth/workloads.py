@@ -214,6 +214,39 @@ def chain_inputs(
     )
 
 
+def chain_shared_rows(seed: int, index: int, *, target: np.ndarray, draft: Optional[np.ndarray], dtype: str, B: int,
+                      temperature: float, tokens: Optional[np.ndarray] = None, name: str = "") -> ChainInputs:
+    """B sequences that all score the same rows (target [K+1, V] and draft [K, V], stored as
+    `dtype`: float32 values or uint16 bf16 bits), each with its own fresh draws: draft
+    tokens x_k ~ softmax(draft_k / T) by Gumbel-max over [B, K, V] at once (or, with
+    draft None, the given one-hot tokens [K]) and fresh uniforms.  `index` selects an
+    independent batch of draws, for statistics over many calls."""
+    store = np.uint16 if dtype == "bf16" else np.float32
+    target = np.asarray(target, dtype=store)
+    K1, V = target.shape
+    K = K1 - 1
+    if draft is None:
+        toks = np.broadcast_to(np.asarray(tokens, dtype=np.int32), (B, K)).copy()
+    else:
+        draft = np.asarray(draft, dtype=store)
+        seen = f32_from_bf16_bits(draft) if dtype == "bf16" else draft
+        u = philox(seed, "draft_sample", index).random((B, K, V))
+        with np.errstate(divide="ignore"):
+            g = -np.log(-np.log(u))
+        toks = np.argmax(seen.astype(np.float64)[None] / temperature + g, axis=-1).astype(np.int32)
+    return ChainInputs(
+        target=np.broadcast_to(target, (B, K1, V)).copy(),
+        draft=None if draft is None else np.broadcast_to(draft, (B, K, V)).copy(),
+        dtype=dtype,
+        tokens=toks,
+        draft_len=None,
+        temperature=np.full((B,), temperature, dtype=np.float32),
+        u_accept=uniforms_open_closed(philox(seed, "u_accept", index), (B, K)),
+        u_final=uniforms_open_closed(philox(seed, "u_final", index), (B,)),
+        name=name,
+    )
+
+
 def chain_config_small_f32(seed: int = 0, B: int = 1, K: int = 5, V: int = 32000, **kw) -> ChainInputs:
     """Chain verify, fp32: target N(0, 2^2) per position, draft = target + N(0, 1), T = 1.0."""
     return chain_inputs(seed, B=B, K=K, V=V, dtype="f32", target_sigma=2.0, draft_sigma=1.0,

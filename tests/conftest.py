@@ -27,3 +27,13 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    # parity totals of the GPU comparisons run in this session (see gpu_helpers.TOTALS)
+    helpers = sys.modules.get("gpu_helpers")
+    totals = getattr(helpers, "TOTALS", None)
+    if totals and totals["comparisons"]:
+        terminalreporter.write_line(
+            "parity totals: {comparisons} comparisons, {sequences} sequences, {exact} exact, {flips} near-tie flips, "
+            "{failures} failures, largest relative probability error {max_prob_rel_err:.3e}".format(**totals))

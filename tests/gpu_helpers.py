@@ -4,8 +4,16 @@ A GPU/oracle difference in an accept decision or a drawn token counts as a
 "flip" (reported, not a failure) only when the oracle's own margin at the first
 differing decision is below 1e-5: |u - alpha| for an accept test, or the
 normalised distance of u*W to the nearer inverse-CDF boundary for a draw.
-Every other difference is a failure.  Probabilities must agree within 1e-5
-relative for float32 logits and 2e-3 for bf16 logits (absolute floor 1e-30).
+Every other difference is a failure, and so is a comparison with more than
+FLIP_LIMIT flips: with uniforms on the 2^-24 grid a decision falls within 1e-5
+of its boundary with probability about 2e-5, so a handful of flips in a few
+thousand decisions already points at a systematic error near the boundaries.
+Probabilities must agree within 1e-5 relative for float32 logits and 2e-3 for
+bf16 logits (absolute floor 1e-30).  Beside that bar, PROB_GUARD bounds the
+largest relative error of either dtype: both sides read the same logit bits, so
+the difference is only the GPU's fp32 exponent arithmetic (a few 1e-6 at the
+benchmark's logit ranges), and a lost or doubled partial sum would show far
+above it.
 """
 
 from __future__ import annotations
@@ -21,6 +29,20 @@ import oracle
 DECISION_MARGIN = 1e-5
 PROB_RTOL = {"f32": 1e-5, "bf16": 2e-3}
 PROB_ATOL = 1e-30
+PROB_GUARD = 1e-5
+FLIP_LIMIT = 2
+
+# running totals over the session, printed by conftest at the end of the run
+TOTALS = {"comparisons": 0, "sequences": 0, "exact": 0, "flips": 0, "failures": 0, "max_prob_rel_err": 0.0}
+
+
+def _tally(rep) -> None:
+    TOTALS["comparisons"] += 1
+    TOTALS["sequences"] += rep.sequences
+    TOTALS["exact"] += rep.exact
+    TOTALS["flips"] += rep.flips
+    TOTALS["failures"] += len(rep.failures)
+    TOTALS["max_prob_rel_err"] = max(TOTALS["max_prob_rel_err"], rep.max_prob_rel_err)
 
 
 def log(msg: str) -> None:
@@ -79,7 +101,7 @@ class ParityReport:
                 f"max_prob_rel_err={self.max_prob_rel_err:.3e} mean_accepted={self.accept_rate:.3f}")
 
 
-def compare_chain(gpu, ref, inp, seqs=None) -> ParityReport:
+def compare_chain(gpu, ref, inp, seqs=None, flip_limit=FLIP_LIMIT) -> ParityReport:
     """Element-by-element comparison of the GPU outputs with the oracle's, with flip accounting."""
     rep = ParityReport()
     g_tok = gpu.tokens.cpu().numpy()
@@ -125,6 +147,86 @@ def compare_chain(gpu, ref, inp, seqs=None) -> ParityReport:
             rep.failures.append((b, f"drawn token gpu={int(g_tok[b, n])} oracle={int(ref_tok[n])} "
                                     f"gap={r.cdf_gap:.3e} mode={r.mode}"))
     rep.accept_rate = float(np.mean(acc)) if acc else 0.0
+    _bound(rep, flip_limit)
+    return rep
+
+
+def _bound(rep, flip_limit) -> None:
+    if rep.flips > flip_limit:
+        rep.failures.append(("*", f"{rep.flips} near-tie flips exceed the bound {flip_limit}"))
+    if rep.max_prob_rel_err > PROB_GUARD:
+        rep.failures.append(("*", f"largest relative probability error {rep.max_prob_rel_err:.3e} above {PROB_GUARD}"))
+    _tally(rep)
+
+
+def _children(parent_row):
+    kids = [[] for _ in range(len(parent_row))]
+    for i in range(1, len(parent_row)):
+        kids[int(parent_row[i])].append(i)
+    return kids
+
+
+def _walk_of_path(kids, accept_len, path_nodes_row):
+    """The accept tests a walk that ends on this path made, in order: at each node its
+    children are tried in node order up to the accepted one; at the last node every child is
+    rejected.  [(node, accepted)], or None if the path is not a root path of the tree."""
+    tests, cur = [], 0
+    for d in range(accept_len):
+        nxt = int(path_nodes_row[d])
+        if nxt not in kids[cur]:
+            return None
+        for c in kids[cur]:
+            tests.append((c, c == nxt))
+            if c == nxt:
+                break
+        cur = nxt
+    tests += [(c, False) for c in kids[cur]]
+    return tests
+
+
+def compare_tree_sampled(gpu, ref, x, seqs=None, flip_limit=FLIP_LIMIT) -> ParityReport:
+    """GPU stochastic tree verification against the oracle.  A sequence that differs is a flip
+    only if the oracle's margin at the first decision where the two walks differ is below
+    1e-5 (an accept test: |u - alpha|; when every accept test agrees, the final draw's
+    normalised inverse-CDF gap); a GPU flag (-1 or -2) against a valid oracle result, or a path
+    that is not a path of the tree, is a failure."""
+    rep = ParityReport()
+    ga, gt, gn = gpu.accept_len.cpu().numpy(), gpu.tokens.cpu().numpy(), gpu.path_nodes.cpu().numpy()
+    acc = []
+    for b in (range(x.B) if seqs is None else seqs):
+        rep.sequences += 1
+        r = ref.sequences[b]
+        acc.append(r.accept_len)
+        if ga[b] == ref.accept_len[b] and (gt[b] == ref.tokens[b]).all() and (gn[b] == ref.path_nodes[b]).all():
+            rep.exact += 1
+            continue
+        n = int(ga[b])
+        if n < 0 or r.accept_len < 0:
+            rep.failures.append((b, f"accept_len gpu={n} oracle={r.accept_len}"))
+            continue
+        kids = _children(x.parent[b])
+        walk = _walk_of_path(kids, n, gn[b])
+        path = [int(v) for v in gn[b, :n]]
+        if (walk is None or (gn[b, n:] != -1).any() or (gt[b, n + 1:] != -1).any()
+                or [int(v) for v in gt[b, :n]] != [int(x.node_token[b, v]) for v in path]):
+            rep.failures.append((b, f"not a valid walk: accept_len={n} path={gn[b].tolist()} tokens={gt[b].tolist()}"))
+            continue
+        first = next((i for i, (g, o) in enumerate(zip(walk, r.tests)) if g[0] != o[0] or g[1] != o[2]), None)
+        if first is None and len(walk) != len(r.tests):
+            rep.failures.append((b, f"walks of different length with equal decisions: {walk} vs {r.tests}"))
+        elif first is not None:
+            if r.accept_margins[first] < DECISION_MARGIN:
+                rep.flips += 1
+            else:
+                rep.failures.append((b, f"decision {first} (node {r.tests[first][0]}): gpu accepted={walk[first][1]} "
+                                        f"oracle alpha={r.tests[first][1]!r} margin={r.accept_margins[first]:.3e}"))
+        elif r.cdf_gap < DECISION_MARGIN:
+            rep.flips += 1
+        else:
+            rep.failures.append((b, f"drawn token gpu={int(gt[b, n])} oracle={int(ref.tokens[b, n])} "
+                                    f"gap={r.cdf_gap:.3e} mode={r.mode}"))
+    rep.accept_rate = float(np.mean(acc)) if acc else 0.0
+    _bound(rep, flip_limit)
     return rep
 
 

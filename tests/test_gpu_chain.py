@@ -48,38 +48,45 @@ def test_high_accept_bf16_full_size():
     assert rep.sequences == 64
 
 
-def test_low_accept_bf16_full_size_sampled():
-    # B=256, K=8, V=152064, bf16: the GPU runs the whole batch, the oracle checks 48 sequences
-    inp = synth.chain_config_low_accept_bf16(0)
-    seqs = list(range(0, 256, 16)) + list(range(1, 256, 8))
-    _run(inp, seqs=sorted(set(seqs)))
+@pytest.mark.parametrize("seed", [0, 1])
+def test_low_accept_bf16_full_size(seed):
+    # B=256, K=8, V=152064, bf16, low acceptance: most sequences end in a residual draw;
+    # every sequence checked
+    _, rep = _run(synth.chain_config_low_accept_bf16(seed))
+    assert rep.sequences == 256
 
 
 def test_low_accept_bf16_reduced():
     _run(synth.chain_config_low_accept_bf16(3, B=12, K=8, V=20000))
 
 
-@pytest.mark.parametrize("nv", ["1", "2", "4", "8", "16"])
-def test_chunk_sizes_give_identical_decisions(nv, monkeypatch):
+def _chunk_vectors(nv):
+    import draft_token_verification_09_amd as sv
+
+    return sv.knob(sv.SPEC_KNOB_CHUNK_VECTORS, nv)
+
+
+@pytest.mark.parametrize("nv", [1, 2, 4, 8, 16])
+def test_chunk_sizes_give_identical_decisions(nv):
     # every chunk size the library may pick agrees with the oracle (and hence with each other);
     # 16 applies to the bf16 rows only (V = 40000 leaves a ragged second chunk), the fp32 call
     # then takes the default
-    monkeypatch.setenv("SPEC_NV", nv)
-    _run(synth.chain_config_high_accept_bf16(5, B=6, K=4, V=40000))
-    _run(synth.chain_config_small_f32(5, B=6, K=4, V=9000))
+    with _chunk_vectors(nv):
+        _run(synth.chain_config_high_accept_bf16(5, B=6, K=4, V=40000))
+        _run(synth.chain_config_small_f32(5, B=6, K=4, V=9000))
 
 
-@pytest.mark.parametrize("nv", ["1", "2", "4", "8", "16"])
-def test_chunk_sizes_one_hot_and_bonus_draws(nv, monkeypatch):
+@pytest.mark.parametrize("nv", [1, 2, 4, 8, 16])
+def test_chunk_sizes_one_hot_and_bonus_draws(nv):
     # one-hot drafts (no draft rows) and bonus draws sample a target row from the stats
     # pass's piece masses, reading only the piece that holds the draw: every chunk size,
     # ragged tails (V = 40000, 9000) and a batch where most sequences take the bonus
-    monkeypatch.setenv("SPEC_NV", nv)
-    _run(dataclasses.replace(synth.chain_config_high_accept_bf16(6, B=12, K=4, V=40000), draft=None))
-    _run(dataclasses.replace(synth.chain_config_small_f32(6, B=12, K=4, V=9000), draft=None))
-    inp = synth.chain_config_high_accept_bf16(7, B=12, K=2, V=40000)
-    _, rep = _run(dataclasses.replace(inp, u_accept=np.full_like(inp.u_accept, 2.0 ** -24)))
-    assert rep.sequences == 12
+    with _chunk_vectors(nv):
+        _run(dataclasses.replace(synth.chain_config_high_accept_bf16(6, B=12, K=4, V=40000), draft=None))
+        _run(dataclasses.replace(synth.chain_config_small_f32(6, B=12, K=4, V=9000), draft=None))
+        inp = synth.chain_config_high_accept_bf16(7, B=12, K=2, V=40000)
+        _, rep = _run(dataclasses.replace(inp, u_accept=np.full_like(inp.u_accept, 2.0 ** -24)))
+        assert rep.sequences == 12
 
 
 @pytest.mark.parametrize("B, V", [(160, 128256), (1000, 16385)])
@@ -146,24 +153,39 @@ def test_dirty_workspace_reused_across_shapes():
 
 
 @pytest.mark.parametrize("recipe", ["high", "low"])
-def test_pool_wait_modes_agree(recipe, monkeypatch):
-    # the pool kernel finishes the draw either in the task owning the chosen segment (every
-    # task waits) or in each sequence's last task (only last tasks wait); same results
+def test_wait_that_gives_up_flags_the_sequence(recipe):
+    # With a poll limit of 0 every hand-over wait gives up before its first poll (the
+    # kernel's own bounded wait, forced from the host; every workgroup still exits).  A
+    # sequence whose draw needs the hand-over (a rejection against draft rows) is then
+    # flagged -2 with -1 tokens, zero probabilities and no packed tokens; bonus draws need
+    # no wait and match the oracle.  With the default limit restored, the same inputs give
+    # the oracle's results.
     import draft_token_verification_09_amd as sv
 
     inp = (synth.chain_config_high_accept_bf16(6, B=20, V=70000) if recipe == "high"
            else synth.chain_config_low_accept_bf16(6, B=20, K=8, V=70000))
+    ref = chain_oracle(inp)
     args = _device_args(inp)
-    monkeypatch.setenv("SPEC_POOL_ALL_WAIT", "1")
-    a = sv.spec_verify_chain(*args)
-    monkeypatch.setenv("SPEC_POOL_ALL_WAIT", "0")
-    b = sv.spec_verify_chain(*args)
-    torch.cuda.synchronize()
-    assert torch.equal(a.tokens, b.tokens)
-    assert torch.equal(a.num_accepted, b.num_accepted)
-    assert torch.equal(a.probs, b.probs)
-    rep = compare_chain(b, chain_oracle(inp), inp)
+    with sv.knob(sv.SPEC_KNOB_POLL_LIMIT, 0):
+        g = sv.spec_verify_chain(*args, want_packed=True)
+        torch.cuda.synchronize()
+    n = g.num_accepted.cpu().numpy()
+    residual = [b for b in range(inp.B) if ref.sequences[b].num_accepted < inp.K]
+    log(f"[chain] poll limit 0, {recipe}: {len(residual)} residual draws flagged, "
+        f"{inp.B - len(residual)} bonus draws")
+    assert residual, "the recipe gives no residual draw"
+    for b in range(inp.B):
+        if b in residual:
+            assert n[b] == sv.FLAG_TIMED_OUT, (b, n[b])
+            assert (g.tokens[b].cpu().numpy() == -1).all() and (g.probs[b].cpu().numpy() == 0).all()
+    rep = compare_chain(g, ref, inp, seqs=[b for b in range(inp.B) if b not in residual])
     assert rep.ok(), rep.failures[:5]
+    check_packed(g, inp.B)
+    again = sv.spec_verify_chain(*args, want_packed=True)
+    torch.cuda.synchronize()
+    rep = compare_chain(again, ref, inp)
+    assert rep.ok(), rep.failures[:5]
+    check_packed(again, inp.B)
 
 
 def test_graph_replays_match_eager_calls():

@@ -166,19 +166,18 @@ def test_whole_chunks_of_neg_inf():
     _parity(inp)
 
 
-@pytest.mark.parametrize("nv", [None, "8", "16"])
-def test_whole_chunks_of_neg_inf_one_hot(nv, monkeypatch):
+@pytest.mark.parametrize("nv", [0, 8, 16])
+def test_whole_chunks_of_neg_inf_one_hot(nv):
     # one-hot drafts draw from the stats pass's piece masses: pieces of -inf have no mass and
     # are never chosen, and the draw still lands on the piece holding u * W (one, two or four
     # segments a piece)
-    if nv:
-        monkeypatch.setenv("SPEC_NV", nv)
     inp = synth.chain_config_high_accept_bf16(13, B=6, K=3, V=70000)
     neg_inf_bits = np.uint16(0xFF80)
     inp.target[:, :, 20000:60000] = neg_inf_bits
     inp.draft = None
     inp.u_accept[:] = np.float32(1.0)  # reject at position 0 unless p(x_0) = 1
-    _parity(inp)
+    with sv().knob(sv().SPEC_KNOB_CHUNK_VECTORS, nv):
+        _parity(inp)
 
 
 def test_empty_batch():

@@ -1,9 +1,10 @@
 """GPU parity of spec_verify_tree (stochastic tree verification) against the oracle.
 
 Accepted lengths, path nodes and tokens must match the oracle exactly.  The one
-exception, as for chains, is a sequence whose oracle result contains a decision within
-1e-5 of its boundary (|u - alpha| for an accept test, the normalised inverse-CDF gap for
-the final draw): a difference there is counted as a flip, not a failure.
+exception, as for chains, is a sequence whose walk first differs from the oracle's at a
+decision within 1e-5 of its boundary (|u - alpha| for an accept test, the normalised
+inverse-CDF gap for the final draw when every accept test agrees): that difference is
+counted as a flip, not a failure, and a comparison allows at most a couple of them.
 """
 
 import json
@@ -15,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import DECISION_MARGIN, dev, f32, i32, log, logits_to_device
+from gpu_helpers import compare_tree_sampled, dev, f32, i32, log, logits_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -38,28 +39,23 @@ def run_gpu(x, max_depth=None, workspace_buf=None):
     return r
 
 
-def compare(x, max_depth=None, seqs=None):
+def oracle_of(x, max_depth=None, seqs=None):
     md = x.max_depth if max_depth is None else max_depth
-    g = run_gpu(x, md)
-    ref = oracle.verify_tree_sampled(x.target, x.draft, x.dtype, x.parent, x.node_token, x.temperature, x.u_accept,
-                                     x.u_final, md, seqs=seqs)
-    ga, gt, gn = g.accept_len.cpu().numpy(), g.tokens.cpu().numpy(), g.path_nodes.cpu().numpy()
-    exact = flips = 0
-    bad = []
-    for b in (range(x.B) if seqs is None else seqs):
-        same = ga[b] == ref.accept_len[b] and (gt[b] == ref.tokens[b]).all() and (gn[b] == ref.path_nodes[b]).all()
-        if same:
-            exact += 1
-            continue
-        r = ref.sequences[b]
-        near = r.accept_len >= 0 and min(r.accept_margins + [r.cdf_gap]) < DECISION_MARGIN
-        if near:
-            flips += 1
-        else:
-            bad.append((b, int(ga[b]), int(ref.accept_len[b]), gt[b].tolist(), ref.tokens[b].tolist()))
-    log(f"[tree_sampled] {x.name}: B={x.B} N1={x.N1} V={x.V}: exact {exact}, flips {flips}, failures {len(bad)}; "
-        f"mean accept_len {np.mean([ref.accept_len[b] for b in (range(x.B) if seqs is None else seqs)]):.3f}")
-    assert not bad, bad[:4]
+    return oracle.verify_tree_sampled(x.target, x.draft, x.dtype, x.parent, x.node_token, x.temperature, x.u_accept,
+                                      x.u_final, md, seqs=seqs)
+
+
+def check(g, ref, x, seqs=None, what=""):
+    rep = compare_tree_sampled(g, ref, x, seqs=seqs)
+    log(f"[tree_sampled] {x.name}{what}: B={x.B} N1={x.N1} V={x.V}: {rep}")
+    assert rep.ok(), rep.failures[:4]
+    return rep
+
+
+def compare(x, max_depth=None, seqs=None):
+    g = run_gpu(x, max_depth)
+    ref = oracle_of(x, max_depth, seqs)
+    check(g, ref, x, seqs)
     return g, ref
 
 
@@ -127,7 +123,7 @@ def test_chain_shaped_trees_match_chain_verification():
                              f32(ch.temperature), f32(ch.u_accept), f32(ch.u_final))
     torch.cuda.synchronize()
     same = (c.num_accepted.cpu().numpy() == g.accept_len.cpu().numpy())
-    assert same.mean() >= 0.9  # identical except for near-boundary flips of either path
+    assert (~same).sum() <= 2  # identical except for near-boundary flips of either path
     for b in np.flatnonzero(same):
         n = int(c.num_accepted[b])
         assert c.tokens[b, : n + 1].cpu().tolist() == g.tokens[b, : n + 1].cpu().tolist()
@@ -160,25 +156,17 @@ def test_path_longer_than_max_depth_is_flagged():
 
 def test_several_launches_and_dirty_workspace():
     # B = 70 sequences of 16 workgroups each need several launches at the default occupancy;
-    # the workspace is filled with junk first and reused across shapes
+    # the workspace is filled with junk first, then reused by a call of another shape and by
+    # a second call of the first: every result is checked against the oracle
     sv = _sv()
     x = synth.tree_sampled_inputs(7, B=70, n_nodes=7, depth=3, V=128256, dtype="bf16", name="B70")
     need = int(sv.lib().spec_verify_tree_workspace_size(70, 8, 128256, 1))
     buf = torch.randint(0, 255, (need + 512,), dtype=torch.uint8, device=dev())
-    g = run_gpu(x, workspace_buf=buf)
-    ref = oracle.verify_tree_sampled(x.target, x.draft, x.dtype, x.parent, x.node_token, x.temperature, x.u_accept,
-                                     x.u_final, x.max_depth)
-    agree = (g.accept_len.cpu().numpy() == ref.accept_len).mean()
-    log(f"[tree_sampled] B=70 dirty workspace: accept_len agreement {agree:.3f}")
-    compare(x)
+    ref = oracle_of(x)
+    check(run_gpu(x, workspace_buf=buf), ref, x, what=" (junk-filled workspace)")
     y = synth.tree_sampled_inputs(8, B=9, n_nodes=20, depth=4, V=9000, dtype="f32", name="reuse")
-    g2 = run_gpu(y, workspace_buf=buf)
-    r2 = oracle.verify_tree_sampled(y.target, y.draft, y.dtype, y.parent, y.node_token, y.temperature, y.u_accept,
-                                    y.u_final, y.max_depth)
-    near = [min(s.accept_margins + [s.cdf_gap]) < DECISION_MARGIN for s in r2.sequences]
-    for b in range(9):
-        if not near[b]:
-            assert int(g2.accept_len[b]) == int(r2.accept_len[b]) and g2.tokens[b].cpu().tolist() == r2.tokens[b].tolist()
+    check(run_gpu(y, workspace_buf=buf), oracle_of(y), y, what=" (workspace reused)")
+    check(run_gpu(x, workspace_buf=buf), ref, x, what=" (workspace reused again)")
 
 
 def test_prepared_call_matches_plain_call():
@@ -236,3 +224,17 @@ def test_graph_replays_match_eager_calls():
         log(f"[tree_sampled] graph replay {rep}: input set {k}")
         assert torch.equal(out.accept_len, eager.accept_len)
         assert torch.equal(out.tokens, eager.tokens) and torch.equal(out.path_nodes, eager.path_nodes)
+
+
+def test_wait_that_gives_up_flags_every_walk():
+    # With a poll limit of 0 every hand-over wait gives up before its first poll (forced
+    # from the host; every workgroup still exits): each sequence is flagged -2 with -1
+    # outputs, written by the sequence's workgroup 0 alone.  Then, with the default limit,
+    # the same inputs match the oracle, so a flagged call leaves nothing behind.
+    sv = _sv()
+    x = synth.tree_sampled_inputs(12, B=10, n_nodes=20, depth=4, V=40000, dtype="bf16", name="poll0")
+    with sv.knob(sv.SPEC_KNOB_POLL_LIMIT, 0):
+        g = run_gpu(x)
+    assert (g.accept_len.cpu().numpy() == sv.FLAG_TIMED_OUT).all()
+    assert (g.tokens.cpu().numpy() == -1).all() and (g.path_nodes.cpu().numpy() == -1).all()
+    compare(x)

@@ -160,3 +160,22 @@ def test_walk_graph_replays_match_eager_calls():
         log(f"[tree walk] graph replay {rep}: input set {k}")
         assert np.array_equal(out.tokens.cpu().numpy(), ref.tokens)
         assert np.array_equal(out.path_nodes.cpu().numpy(), ref.path_nodes)
+
+
+def test_wait_that_gives_up_flags_every_walk():
+    # With a poll limit of 0 every hand-over wait of the walk gives up before its first poll
+    # (forced from the host; every workgroup still exits): each sequence is flagged -2 by
+    # the one workgroup that writes its outputs, with -1 tokens and path nodes.  The design
+    # that computes every row's argmax does not hand anything over and is unaffected; with
+    # the default limit restored the walk matches the oracle again.
+    sv = _sv()
+    tr = synth.tree_inputs(11, B=10, n_nodes=20, depth=4, V=40000, dtype="bf16", p_boost=0.9)
+    with sv.knob(sv.SPEC_KNOB_POLL_LIMIT, 0):
+        g = walk(tr)
+        full = walk(tr, want_argmax=True)
+    assert (g.accept_len.cpu().numpy() == sv.FLAG_TIMED_OUT).all()
+    assert (g.tokens.cpu().numpy() == -1).all() and (g.path_nodes.cpu().numpy() == -1).all()
+    ref = oracle.verify_tree_greedy(tr.target, tr.dtype, tr.parent, tr.node_token, tr.max_depth)
+    assert np.array_equal(full.accept_len.cpu().numpy(), ref.accept_len)
+    assert np.array_equal(full.tokens.cpu().numpy(), ref.tokens)
+    compare(tr)
