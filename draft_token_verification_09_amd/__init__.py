@@ -40,6 +40,7 @@ from .binding import (  # noqa: F401
     spec_timing_reset,
     spec_tree_mask,
     spec_verify_chain,
+    spec_verify_chain_noalloc,
     spec_verify_chain_workspace_size,
     spec_verify_tree,
     spec_verify_tree_greedy,

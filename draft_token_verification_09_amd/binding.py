@@ -53,6 +53,8 @@ _SIGNATURES = {
     "spec_verify_chain_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "spec_verify_chain": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_chain_noalloc": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                         _vp, _vp, _vp, _vp, _vp, _vp]),
     "spec_verify_tree_greedy_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "spec_verify_tree_greedy": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                        _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -186,9 +188,10 @@ def spec_verify_chain_workspace_size(B: int, K: int, V: int, dtype_code: int) ->
 def _chain_call(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor], draft_tokens: torch.Tensor,
                 temperature: torch.Tensor, u_accept: torch.Tensor, u_final: torch.Tensor,
                 draft_len: Optional[torch.Tensor], want_probs: bool, want_packed: bool,
-                out: Optional[ChainResult], workspace_buf: Optional[torch.Tensor], stream):
+                out: Optional[ChainResult], workspace_buf: Optional[torch.Tensor], stream, use_workspace=True):
     """Checks the tensors and returns (argument tuple of spec_verify_chain, result, buffers
-    the call uses)."""
+    the call uses).  Without use_workspace the tuple has no workspace arguments (the
+    allocation-free entry point)."""
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [B, K+1, V]")
     B, K1, V = target_logits.shape
@@ -214,13 +217,17 @@ def _chain_call(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor
             offsets=torch.empty((B + 1,), dtype=torch.int32, device=dev) if want_packed else None,
         )
     s = _stream(stream, dev)
-    need = int(lib().spec_verify_chain_workspace_size(B, K, V, code)) if B > 0 else 0
-    buf = workspace_buf if workspace_buf is not None else workspace(need, dev, s, "chain")
-    wp, wbytes = _aligned_ptr(buf)
     args = (_ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(draft_len),
             _ptr(temperature), _ptr(u_accept), _ptr(u_final), B, K, V,
             _ptr(out.tokens), _ptr(out.num_accepted), _ptr(out.probs),
-            _ptr(out.packed), _ptr(out.offsets), wp, wbytes, s)
+            _ptr(out.packed), _ptr(out.offsets))
+    buf = None
+    if use_workspace:
+        need = int(lib().spec_verify_chain_workspace_size(B, K, V, code)) if B > 0 else 0
+        buf = workspace_buf if workspace_buf is not None else workspace(need, dev, s, "chain")
+        wp, wbytes = _aligned_ptr(buf)
+        args += (wp, wbytes)
+    args += (s,)
     keep = (target_logits, draft_logits, draft_tokens, temperature, u_accept, u_final, draft_len, buf)
     return args, out, keep
 
@@ -237,6 +244,20 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.
     args, out, _ = _chain_call(target_logits, draft_logits, draft_tokens, temperature, u_accept, u_final,
                                draft_len, want_probs, want_packed, out, workspace_buf, stream)
     _check("spec_verify_chain", lib().spec_verify_chain(*args))
+    return out
+
+
+def spec_verify_chain_noalloc(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                              draft_tokens: torch.Tensor, temperature: torch.Tensor, u_accept: torch.Tensor,
+                              u_final: torch.Tensor, draft_len: Optional[torch.Tensor] = None, *,
+                              out: ChainResult, stream=None) -> ChainResult:
+    """spec_verify_chain_noalloc: as spec_verify_chain, with the library's own device scratch
+    instead of a workspace.  `out` is required (the library allocates nothing, and neither
+    does this wrapper)."""
+    args, out, _ = _chain_call(target_logits, draft_logits, draft_tokens, temperature, u_accept, u_final,
+                               draft_len, out.probs is not None, out.packed is not None, out, None, stream,
+                               use_workspace=False)
+    _check("spec_verify_chain_noalloc", lib().spec_verify_chain_noalloc(*args))
     return out
 
 

@@ -1123,6 +1123,37 @@ static spec_status_t dispatch_chain(int nv, bool vec, const ChainArgs& a, hipStr
   }
 }
 
+// ---------------------------------------------------------------- allocation-free variant
+//
+// spec_verify_chain_noalloc runs spec_verify_chain on this file-scope device array instead of
+// a caller's workspace.  Each device the library runs on holds its own copy until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it only stands in
+// for the symbol): the device address comes from hipGetSymbolAddress, taken once per device
+// on that device's first call and kept.  Nothing in the array needs to start at zero: the
+// values the kernels hand each other carry the call's generation number, and the run
+// counter at its start may hold anything.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+static spec_status_t scratch_address(void** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPEC_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SPEC_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g != hipSuccess || !p)
+      return fail(SPEC_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(g));
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SPEC_OK;
+}
+
 }  // namespace specv
 
 using namespace specv;
@@ -1212,6 +1243,25 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
 
   if (dtype == SPEC_BF16) return dispatch_chain<kBF16>(L.nv, vec, a, s);
   return dispatch_chain<kF32>(L.nv, vec, a, s);
+}
+
+spec_status_t spec_verify_chain_noalloc(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                        const int32_t* draft_tokens, const int32_t* draft_len,
+                                        const float* temperature, const float* u_accept, const float* u_final,
+                                        int B, int K, int V,
+                                        int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                        int32_t* out_packed, int32_t* out_offsets, spec_stream_t stream) {
+  const size_t need = B > 0 ? spec_verify_chain_workspace_size(B, K, V, dtype) : 0;
+  if (need > kScratchBytes)
+    return fail(SPEC_ERR_UNSUPPORTED,
+                "B = %d, K = %d, V = %d needs %zu bytes of scratch; the allocation-free call holds %zu", B, K, V, need,
+                kScratchBytes);
+  void* ws = nullptr;
+  const spec_status_t st = scratch_address(&ws);
+  if (st != SPEC_OK) return st;
+  return spec_verify_chain(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature, u_accept,
+                           u_final, B, K, V, out_tokens, out_num_accepted, out_probs, out_packed, out_offsets, ws,
+                           kScratchBytes, stream);
 }
 
 }  // extern "C"

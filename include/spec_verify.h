@@ -166,6 +166,25 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
                                 void* workspace, size_t workspace_bytes, spec_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * spec_verify_chain without a workspace, for callers that cannot allocate device
+ * memory (code recorded into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors as spec_verify_chain; the scratch
+ * space is a 16 MiB array that the library holds on each device it runs on, for the
+ * life of the process (enough for B = 1024, K = 8, V = 152064 bf16).  A shape that
+ * needs more returns SPEC_ERR_UNSUPPORTED and launches nothing.  The call allocates
+ * nothing (the array's device address is looked up on the device's first call).
+ * Every call on one device shares that device's array, so calls that overlap in
+ * time on one device (different streams, host threads) race: issue them one after
+ * another, or use spec_verify_chain with a workspace per stream.
+ * ------------------------------------------------------------------------- */
+spec_status_t spec_verify_chain_noalloc(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                        const int32_t* draft_tokens, const int32_t* draft_len,
+                                        const float* temperature, const float* u_accept, const float* u_final,
+                                        int B, int K, int V,
+                                        int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                        int32_t* out_packed, int32_t* out_offsets, spec_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Greedy tree verification.
  *
  * [Production] section III.2 "The Tree Attention Verification Mechanism": all

@@ -155,3 +155,13 @@ def test_knobs_set_get_and_restore(lib):
     bd.spec_set_knob(bd.SPEC_KNOB_POLL_LIMIT, 5)
     bd.spec_set_knob(bd.SPEC_KNOB_POLL_LIMIT, -1)  # negative: back to the default
     assert bd.spec_get_knob(bd.SPEC_KNOB_POLL_LIMIT) == 1 << 18
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
+    # host-side: the allocation-free chain call checks the scratch its shape needs against the
+    # library's 16 MiB array before it looks at any pointer or launches anything
+    B, K, V = 4096, 8, 152064
+    assert lib.spec_verify_chain_workspace_size(B, K, V, 1) > 16 << 20
+    st = lib.spec_verify_chain_noalloc(1, 1, 1, 1, None, 1, 1, 1, B, K, V, 1, 1, None, None, None, None)
+    assert st == 2  # SPEC_ERR_UNSUPPORTED
+    assert b"allocation-free" in lib.spec_last_error()
