@@ -549,6 +549,85 @@ def kernels_per_call(kernels, steps):
     return {k: round(v[1] / steps * 1e3, 3) for k, v in kernels.items()}
 
 
+MODE_NAMES = {1: "residual", 2: "bonus", 3: "one-hot", 4: "fallback-p", 5: "greedy", 0: "invalid"}
+
+
+def chain_phases(make, name, warmup, calls, dev, chunk_vectors, pool_segments):
+    """Per-phase timeline of chain calls from the library's phase timestamps (device clock,
+    100 MHz): for each of `calls` calls (after `warmup`), the stats pass's span and the pool
+    kernel's phases, relative to the first stats workgroup's start.  Returns a text summary."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_09_amd as sv
+
+    probe = make(0)
+    per_set = chain_bytes(probe)
+    n_sets = sets_needed(per_set)
+    sets, _ = chain_device_sets(make, n_sets, dev)
+    B, K, V = probe.B, probe.K, probe.V
+    code = 1 if probe.dtype == "bf16" else 0
+    ws = torch.empty(sv.spec_verify_chain_workspace_size(B, K, V, code) + 256, dtype=torch.uint8, device=dev)
+    prepared = [sv.prepare_spec_verify_chain(s["t"], s["d"], s["tok"], s["T"], s["ua"], s["uf"], s["dl"],
+                                             workspace_buf=ws) for s in sets]
+    epv = 8 if probe.dtype == "bf16" else 4
+    C = -(-V // (chunk_vectors * 256 * epv))
+    R = 2 * K + 1 if probe.draft is not None else K + 1
+    S = -(-(-(-V // (256 * epv))) // pool_segments) * pool_segments
+    G, P = B * R * C, B * (S // pool_segments)
+    buf = torch.zeros(2 * G + 6 * P, dtype=torch.int64, device=dev)
+    for i in range(warmup):
+        prepared[i % n_sets]()
+    torch.cuda.synchronize()
+    rows = []
+    us = 0.01  # microseconds per clock tick
+    for i in range(calls):
+        buf.fill_(-1)
+        torch.cuda.synchronize()
+        sv.spec_chain_phase_stamps(buf)
+        prepared[(warmup + i) % n_sets]()
+        torch.cuda.synchronize()
+        sv.spec_chain_phase_stamps(None)
+        st = buf.cpu().numpy()
+        stats = st[: 2 * G].reshape(G, 2)
+        pool = st[2 * G:].reshape(P, 6)
+        # every stats workgroup and pool task stamps its start and end (else the layout is not the call's)
+        assert (stats != -1).all() and (pool[:, [0, 1, 4, 5]] != -1).all(), "stamp layout does not match the call"
+        t0 = stats[:, 0].min()
+        r = dict(stats_end=(stats[:, 1].max() - t0) * us, pool_start=(pool[:, 0].min() - t0) * us,
+                 decide=np.median(pool[:, 1] - pool[:, 0]) * us,
+                 call_end=(pool[:, 4].max() - t0) * us)
+        mode = pool[:, 5] & 0xFF
+        c = (pool[:, 5] >> 8) & 0xFFFFFF
+        res = mode == 1
+        last = res & (c == S // pool_segments - 1)
+        if res.any():
+            r["residual_sequences"] = int(last.sum())
+            r["published"] = np.median(pool[res, 2] - pool[res, 1]) * us
+            r["wait"] = np.median(pool[last, 3] - pool[last, 2]) * us
+            r["wait_after_last_published"] = np.median(
+                [(pool[last][j, 3] - pool[res & ((pool[:, 5] >> 32) == (pool[last][j, 5] >> 32)), 2].max()) * us
+                 for j in range(int(last.sum()))])
+            r["narrow"] = np.median(pool[last, 4] - pool[last, 3]) * us
+        direct = (mode == 2) | (mode == 3) | (mode == 4)
+        first = direct & (c == 0)
+        if first.any():
+            r["direct_sequences"] = int(first.sum())
+            r["direct_select"] = np.median(pool[first, 2] - pool[first, 1]) * us
+            r["direct_narrow"] = np.median(pool[first, 4] - pool[first, 2]) * us
+        rows.append(r)
+    del prepared, sets
+    torch.cuda.empty_cache()
+    keys = ["stats_end", "pool_start", "decide", "published", "wait", "wait_after_last_published", "narrow",
+            "direct_select", "direct_narrow", "call_end", "residual_sequences", "direct_sequences"]
+    lines = [f"{name}: {calls} calls after {warmup}, medians over the calls (each call: median over its tasks)"]
+    for k in keys:
+        vals = [r[k] for r in rows if k in r]
+        if vals:
+            lines.append(f"  {k:28s} {np.median(vals):8.2f}   (min {np.min(vals):.2f}, max {np.max(vals):.2f})")
+    return "\n".join(lines)
+
+
 def achievable_read(dev, nbytes, warmup, steps):
     """The achievable read rate the streaming pass is compared with: pure reads of the same bytes
     in its access shape (one workgroup per chunk, XCD-blocked, non-temporal 16-byte loads), for
@@ -614,6 +693,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", action="store_true", help="also run the streaming read/copy probes")
+    ap.add_argument("--phases", metavar="FILE", help="write a per-phase timeline of chain calls (the library's "
+                    "phase timestamps) for the headline and the low-acceptance workloads to FILE")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -705,6 +786,14 @@ def main():
         result["other_workloads"] = other_workloads(args.warmup, max(20, args.steps // 2), dev)
     if args.probe:
         result["probes"] = probe(dev)
+    if args.phases:
+        progress("phase timestamps")
+        text = [chain_phases(lambda s: host0 if s == 0 else synth.chain_config_high_accept_bf16(s), workload,
+                             args.warmup, 20, dev, 16, 4),
+                chain_phases(lambda s: synth.chain_config_low_accept_bf16(s), "chain_verify_B256_K8_V152064_bf16",
+                             args.warmup, 20, dev, 16, 4)]
+        with open(args.phases, "w") as f:
+            f.write("\n\n".join(text) + "\n")
     print(json.dumps(result), flush=True)
 
 

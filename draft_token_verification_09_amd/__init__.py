@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     prepare_spec_tree_mask,
     prepare_spec_verify_tree,
     prepare_spec_verify_tree_greedy,
+    spec_chain_phase_stamps,
     spec_commit_path,
     spec_get_knob,
     spec_set_knob,

@@ -78,6 +78,7 @@ _SIGNATURES = {
     "spec_timing_entry": (_i32, [_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_longlong),
                                  ctypes.POINTER(ctypes.c_double)]),
     "spec_set_knob": (_i32, [_i32, _i32]),
+    "spec_chain_phase_stamps": (_i32, [_vp, _sz]),
     "spec_get_knob": (_i32, [_i32]),
     "spec_probe_read": (_i32, [_vp, _sz, _sz, _vp, _vp]),
     "spec_probe_copy": (_i32, [_vp, _vp, _sz, _vp]),
@@ -692,6 +693,16 @@ def knob(knob_id: int, value: int):
         yield
     finally:
         spec_set_knob(knob_id, old)
+
+
+def spec_chain_phase_stamps(buffer: Optional[torch.Tensor]) -> None:
+    """Start (a device int64 tensor) or stop (None) the phase timestamps of chain calls."""
+    if buffer is None:
+        _check("spec_chain_phase_stamps", lib().spec_chain_phase_stamps(None, 0))
+    else:
+        if buffer.dtype != torch.int64 or not buffer.is_cuda or not buffer.is_contiguous():
+            raise ValueError("the stamp buffer must be a contiguous int64 CUDA tensor")
+        _check("spec_chain_phase_stamps", lib().spec_chain_phase_stamps(buffer.data_ptr(), buffer.numel()))
 
 
 def spec_probe_read(src: torch.Tensor, out: torch.Tensor, chunk_bytes: int = 65536, stream=None) -> None:

@@ -142,7 +142,20 @@ struct ChainArgs {
   float* gath;          // [B, R] logit of the drafted token in each scoring row
   SlotDouble* wseg;     // [B, S] slots: mass of the final draw's weights per segment
   SlotDouble* wsegp;    // [B, S] slots: mass of p of the same row per segment (fallback)
+  unsigned long long* stamps;  // phase timestamps (measurement only; see spec_chain_phase_stamps), or null
+  size_t stamps_pool;          // index of the pool tasks' first stamp
 };
+
+// Phase timestamps (the device's constant 100 MHz clock), written by thread 0 when the
+// caller asked for them.  Stats workgroup g: stamps[2g] start, [2g+1] end.  Pool task t
+// (t = launch offset + workgroup index): stamps[stamps_pool + kStampsPerTask * t + i] for
+// the phases of kPoolPhase, the last word holding (b << 32) | (c << 8) | mode.
+constexpr int kStampsPerTask = 6;
+enum PoolPhase : int { kPhStart = 0, kPhDecided = 1, kPhPublished = 2, kPhGathered = 3, kPhEnd = 4, kPhInfo = 5 };
+
+__device__ __forceinline__ void stamp(const ChainArgs& a, size_t i) {
+  if (a.stamps && threadIdx.x == 0) a.stamps[i] = __builtin_amdgcn_s_memrealtime();
+}
 
 // Generation of the slot words of this pool launch (see SlotDouble): the host's number
 // mixed with the workspace counter as the stats kernel of this call left it.
@@ -188,22 +201,17 @@ __device__ __forceinline__ int row_position(const ChainArgs& a, int rr, int kb) 
 
 // ---------------------------------------------------------------- decision
 
-constexpr int kStage = 1024;  // chunk partials staged in shared memory per batch of rows
-constexpr int kStageBytes = kStage * (sizeof(double) + sizeof(float));
 
 // Called by every lane of every pool task of sequence b: combines the sequence's chunk
 // partials, decides and leaves the decision in *out (shared memory) -- identically in
 // every task: same data, same arithmetic, same order.  With write_outputs it also writes
-// the count and the probabilities (and a -1 row for invalid input).  `stage` is shared
-// memory of at least kStageBytes (reused by the caller afterwards).  The loads of a batch
+// the count and the probabilities (and a -1 row for invalid input).  The loads of a batch
 // of rows are all issued before any is used.
 template <int DT>
 __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, bool write_outputs,
-                                             ChainDecision* out, unsigned char* stage) {
+                                             ChainDecision* out) {
   __shared__ float sO[2 * SPEC_MAX_K + 1];
   __shared__ double sS[2 * SPEC_MAX_K + 1];
-  double* st_s = reinterpret_cast<double*>(stage);
-  float* st_o = reinterpret_cast<float*>(stage + kStage * sizeof(double));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -227,66 +235,67 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   const bool greedy = T == 0.f;
 
   // Per-row (O, S) from the partials -- for a greedy sequence the row argmax instead:
-  // each 16-lane row of the workgroup combines one row of logits (16 at a time), lane r
-  // taking partials r, r+16, ...
-  __shared__ float s_om[kThreads / 16];
+  // each 16-lane group of the workgroup combines one row of logits (16 rows at a time), lane
+  // r taking partials r, r+16, ... straight from memory (the first kRegPer of them in
+  // registers, all loads issued before any is used); the group's lane 15 leaves the row's
+  // result in shared memory.
   __shared__ int sA[2 * SPEC_MAX_K + 1];  // greedy: argmax of each target row
   const int grp = tid >> 4;  // 16-lane group
   const int r = tid & 15;
-  const int rows_per_batch = max(1, kStage / C);
-  for (int r0 = 0; r0 < R; r0 += rows_per_batch) {
-    const int r1 = min(R, r0 + rows_per_batch);
-    const int items = (r1 - r0) * C;
-    const RowStat* ps = a.part + (static_cast<size_t>(b) * R + r0) * C;
-    for (int i = tid; i < items; i += kThreads) {
-      const RowStat st = ps[i];
-      st_o[i] = st.o;
-      st_s[i] = st.s;
+  const int row_lane15 = (lane & ~15) | 15;
+  constexpr int kRegPer = 4;
+  for (int r0 = 0; r0 < R; r0 += kThreads / 16) {
+    const int rr = r0 + grp;
+    const bool live = rr < R && row_needed(a, rr, kb, greedy);
+    const RowStat* ps = a.part + (static_cast<size_t>(b) * R + (live ? rr : 0)) * C;
+    RowStat st[kRegPer];
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) {
+      const int c = r + 16 * j;
+      st[j] = live && c < C ? ps[c] : RowStat{-INFINITY, 0.f, static_cast<double>(INT_MAX)};
     }
-    __syncthreads();
-    for (int g0 = r0; g0 < r1 && greedy; g0 += kThreads / 16) {
-      const int rr = g0 + grp;
-      const bool live = rr < r1 && row_needed(a, rr, kb, true);
-      const int base = (rr - r0) * C;
+    if (greedy) {
       float v = -INFINITY;
       int idx = INT_MAX;
-      if (live)
-        for (int c = r; c < C; c += 16) {
-          const int ci = static_cast<int>(st_s[base + c]);
-          if (better(st_o[base + c], ci, v, idx)) {
-            v = st_o[base + c];
-            idx = ci;
-          }
+      for (int j = 0; j < kRegPer; ++j) {
+        const int ci = static_cast<int>(st[j].s);
+        if (better(st[j].o, ci, v, idx)) {
+          v = st[j].o;
+          idx = ci;
         }
+      }
+      for (int c = r + 16 * kRegPer; live && c < C; c += 16) {
+        const RowStat s2 = ps[c];
+        const int ci = static_cast<int>(s2.s);
+        if (better(s2.o, ci, v, idx)) {
+          v = s2.o;
+          idx = ci;
+        }
+      }
       row16_argmax(v, idx);
       if (live && r == 15) sA[rr] = idx;
-    }
-    __syncthreads();
-    for (int g0 = r0; g0 < r1 && !greedy; g0 += kThreads / 16) {
-      const int rr = g0 + grp;
-      const bool live = rr < r1 && row_needed(a, rr, kb, false);
-      const int base = (rr - r0) * C;
+    } else {
       float om = -INFINITY;
-      if (live)
-        for (int c = r; c < C; c += 16) om = fmaxf(om, st_o[base + c]);
-      om = row16_inclusive_max(om);
-      if (r == 15) s_om[grp] = om;
-      __syncthreads();
-      om = s_om[grp];
+#pragma unroll
+      for (int j = 0; j < kRegPer; ++j) om = fmaxf(om, st[j].o);
+      for (int c = r + 16 * kRegPer; live && c < C; c += 16) om = fmaxf(om, ps[c].o);
+      om = __shfl(row16_inclusive_max(om), row_lane15);
       double sum = 0.0;
-      if (live)
-        for (int c = r; c < C; c += 16) {
-          const float o = st_o[base + c];
-          if (o != -INFINITY) sum += st_s[base + c] * static_cast<double>(exp2_fast(o - om));
-        }
+#pragma unroll
+      for (int j = 0; j < kRegPer; ++j)
+        if (st[j].o != -INFINITY) sum += st[j].s * static_cast<double>(exp2_fast(st[j].o - om));
+      for (int c = r + 16 * kRegPer; live && c < C; c += 16) {
+        const RowStat s2 = ps[c];
+        if (s2.o != -INFINITY) sum += s2.s * static_cast<double>(exp2_fast(s2.o - om));
+      }
       sum = row16_inclusive_sum(sum);
       if (live && r == 15) {
         sO[rr] = om;
         sS[rr] = sum;
       }
-      __syncthreads();
     }
   }
+  __syncthreads();
 
   if (w == 0 && greedy) {
     // One lane per drafted position: accepted iff the draft is its target row's argmax;
@@ -398,6 +407,7 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
 template <int DT, int NV, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_fetch_add(a.runs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  stamp(a, 2 * static_cast<size_t>(blockIdx.x));
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
@@ -408,7 +418,10 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   const int b = g / (a.C * a.R);
   const int kb = clamped_len(a, b);
   const bool greedy = is_greedy(a, b);
-  if (!row_needed(a, rr, kb, greedy)) return;
+  if (!row_needed(a, rr, kb, greedy)) {
+    stamp(a, 2 * static_cast<size_t>(blockIdx.x) + 1);
+    return;
+  }
   const void* row = rr <= a.K ? target_row<DT>(a, b, rr) : draft_row<DT>(a, b, rr - (a.K + 1));
   RowStat* out = a.part + ((static_cast<size_t>(b) * a.R + rr) * a.C + c) * kWaves + (threadIdx.x >> 6);
 
@@ -441,6 +454,7 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
       }
     wave_argmax(v, idx);
     if ((threadIdx.x & 63) == 0) *out = RowStat{v, 0.f, static_cast<double>(idx)};
+    stamp(a, 2 * static_cast<size_t>(blockIdx.x) + 1);
     return;
   }
   const float scale = kLog2e / a.temperature[b];
@@ -501,6 +515,7 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   const double contrib = (o == -INFINITY) ? 0.0 : static_cast<double>(s) * static_cast<double>(exp2_fast(o - ow));
   const double sw = wave_sum(contrib);
   if ((threadIdx.x & 63) == 0) *out = RowStat{ow, 0.f, sw};
+  stamp(a, 2 * static_cast<size_t>(blockIdx.x) + 1);
 }
 
 // ---------------------------------------------------------------- final draw
@@ -705,6 +720,89 @@ __device__ __forceinline__ void direct_select(const ChainArgs& a, int b, const C
   *tloc_out = s_before;
 }
 
+// Wave 0 of a sequence's last pool task, alone (the other waves wait at a barrier): lane l
+// takes segments l, l + 64, ... (round r holds segments 64 r .. 64 r + 63), waits for their
+// masses, and the rounds' inclusive scans in vocabulary order give the total W and the
+// segment whose prefix first reaches u * W.  The masses stay in shared memory (s_m, room for
+// S doubles); the scans are recomputed for the search.  Leaves the segment and u * W minus
+// the mass before it in *usel_out and *tloc_out (lane 0 writes them) and returns true; if a
+// wait gives up, flags the sequence and returns false.
+__device__ __forceinline__ bool gather_and_locate(const ChainArgs& a, int b, uint32_t gen, const SlotDouble* mw,
+                                                  const SlotDouble* mp, int units, double* s_m, int* mode,
+                                                  int* usel_out, double* tloc_out, size_t sb) {
+  const int lane = threadIdx.x & 63;
+  const int rounds = (units + 63) / 64;  // units = S <= 4 * kThreads
+  double W = 0.0;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const SlotDouble* slots = attempt == 0 ? mw : mp;
+    unsigned have = 0;  // rounds whose slot this lane has read
+    for (int r = 0; r < rounds; ++r)
+      if (64 * r + lane >= units) {
+        have |= 1u << r;
+        s_m[64 * r + lane] = 0.0;
+      }
+    const unsigned all = rounds >= 32 ? ~0u : (1u << rounds) - 1u;
+    bool arrived = false;
+    for (int polls = 0; polls < a.poll_limit; ++polls) {
+      for (int r = 0; r < rounds; ++r) {
+        double v;
+        if (!(have >> r & 1u) && get_slot(slots + 64 * r + lane, gen, &v)) {
+          have |= 1u << r;
+          s_m[64 * r + lane] = v;
+        }
+      }
+      if (__ballot(have != all) == 0ull) {
+        arrived = true;
+        break;
+      }
+      short_pause();
+    }
+    if (!arrived) {  // flag the sequence rather than wait on (this task alone writes its row)
+      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+      for (int kk = lane; kk <= a.K; kk += 64) ot[kk] = -1;
+      if (lane == 0) a.out_num[b] = kFlagTimedOut;
+      if (a.out_probs)
+        for (int i = lane; i < a.K * 3; i += 64) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
+      return false;
+    }
+    double carry = 0.0;
+    for (int r = 0; r < rounds; ++r) carry = lane_broadcast(wave_inclusive_scan(s_m[64 * r + lane]) + carry, 63);
+    W = carry;
+    if (W > 0.0) break;
+    *mode = kModeFallbackP;  // no residual mass left after rounding: draw from p_n itself
+  }
+  stamp(a, sb + kPhGathered);
+  const double tt = static_cast<double>(a.u_final[b]) * W;
+  int usel = -1, lastu = -1;
+  double before = 0.0, last_before = 0.0, carry = 0.0;
+  for (int r = 0; r < rounds && usel < 0; ++r) {
+    const double mr = s_m[64 * r + lane];
+    const double ir = wave_inclusive_scan(mr) + carry;  // as in the total above
+    carry = lane_broadcast(ir, 63);
+    const unsigned long long hit = __ballot(mr > 0.0 && ir >= tt);
+    if (hit) {
+      const int l = __ffsll(static_cast<long long>(hit)) - 1;
+      usel = 64 * r + l;
+      before = lane_broadcast(ir - mr, l);
+    }
+    const unsigned long long pos = __ballot(mr > 0.0);
+    if (pos) {  // the last segment with mass so far
+      const int l = 63 - __clzll(static_cast<long long>(pos));
+      lastu = 64 * r + l;
+      last_before = lane_broadcast(ir - mr, l);
+    }
+  }
+  if (usel < 0) {  // rounding left u * W above every prefix: the last segment with mass
+    usel = lastu >= 0 ? lastu : 0;
+    before = lastu >= 0 ? last_before : 0.0;
+  }
+  if (lane == 0) {
+    *usel_out = usel;
+    *tloc_out = tt - before;
+  }
+  return true;
+}
+
 // Residual draw after a rejection against draft rows (see chain_pool_kernel, steps 1-3):
 // this task's segment masses of max(0, p - q) and p go out through the slots; the sequence's
 // last task waits for the others' and returns true with the segment holding u * W and u * W
@@ -714,10 +812,7 @@ __device__ __forceinline__ void direct_select(const ChainArgs& a, int b, const C
 template <int DT, int SPT, bool VEC>
 __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bool last, const ChainDecision& d,
                                             int* mode, const void* row_t, const void* row_d, float* red,
-                                            int* usel_out, double* tloc_out) {
-  __shared__ double s_d[kWaves];
-  __shared__ int s_i[kWaves];
-  __shared__ double s_base;
+                                            int* usel_out, double* tloc_out, size_t sb) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
@@ -766,80 +861,87 @@ __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bo
     v = row16_inclusive_sum(v);
     if (q < 2 * SPT && r == 15) put_slot((q < SPT ? mw : mp) + c * SPT + (q % SPT), v, gen);
   }
+  stamp(a, sb + kPhPublished);
   if (!last) return false;
+  __shared__ int s_usel, s_mode;
+  __shared__ double s_tloc;
+  __syncthreads();  // every wave is done with `red`, which holds the gathered masses next
+  if (w == 0 && !gather_and_locate(a, b, gen, mw, mp, units, reinterpret_cast<double*>(red), mode, &s_usel,
+                                   &s_tloc, sb)) {
+    if (lane == 0) s_usel = -1;
+  }
+  if (w == 0 && lane == 0) s_mode = *mode;
+  __syncthreads();
+  *mode = s_mode;
+  *usel_out = s_usel;
+  *tloc_out = s_tloc;
+  return s_usel >= 0;
+}
 
-  // ---- 3. every chunk's masses (this lane's share of the units)
-  const int per = (units + kThreads - 1) / kThreads;  // <= 4
-  const int u0 = tid * per;
-  double mass[4];
-  double W = 0.0;
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    const SlotDouble* slots = attempt == 0 ? mw : mp;
-    bool arrived = false;
-    for (int polls = 0; polls < a.poll_limit; ++polls) {
-      int missing = 0;
+// Narrows a draw to one element of segment `usel` and writes the emitted row (x_0 .. x_{n-1},
+// the drawn token, then -1); called by every lane.  Lane t takes the segment's vector t, sums
+// its draw weights in fp32 exactly as the segment masses were summed and scans the sums in
+// fp64; the first lane whose prefix reaches t_loc picks the element, walking its weights in
+// order, and writes it.  If rounding leaves t_loc above the segment's total, the last
+// positive weight is taken; with no positive weight at all (a direct draw whose piece mass
+// came from the stats partials while every weight underflows) the segment's first element.
+template <int DT, bool VEC>
+__device__ __forceinline__ void narrow_and_emit(const ChainArgs& a, int b, const ChainDecision& d, int mode,
+                                                int usel, double t_loc, const void* row_t, const void* row_d) {
+  __shared__ double s_wt[kWaves];
+  __shared__ int s_first[kWaves];
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const bool residual = mode == kModeResidual;
+  const int excl = mode == kModeOneHot ? d.excl_tok : -1;
+  const int e0 = usel * kSeg + tid * E;
+  const u32x4 vt = load_vector<DT, VEC>(row_t, a.V, e0);
+  const u32x4 vd = residual ? load_vector<DT, VEC>(row_d, a.V, e0) : vt;
+  float wl[E];
+  float lsum = 0.f;
+  int last_pos = -1;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int u = u0 + q;
-        mass[q] = 0.0;
-        if (q < per && u < units && !get_slot(slots + u, gen, &mass[q])) missing = 1;
-      }
-      if (!__syncthreads_or(missing)) {
-        arrived = true;
-        break;
-      }
-      short_pause();
-    }
-    if (!arrived) {  // flag the sequence rather than wait on (this task alone writes its row)
-      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-      for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
-      if (tid == 0) a.out_num[b] = kFlagTimedOut;
-      if (a.out_probs)
-        for (int i = tid; i < a.K * 3; i += kThreads) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
-      return false;
-    }
-    W = block_sum(mass[0] + mass[1] + mass[2] + mass[3], s_d);
-    if (W > 0.0) break;
-    *mode = kModeFallbackP;  // no residual mass left after rounding: draw from p_n itself
+  for (int i = 0; i < E; ++i) {
+    wl[i] = draw_weight(residual, d, EL::get(vt, i), EL::get(vd, i), e0 + i, excl);
+    lsum += wl[i];
+    last_pos = wl[i] > 0.f ? e0 + i : last_pos;
   }
-
-  // ---- the segment holding u * W
-  const double local = mass[0] + mass[1] + mass[2] + mass[3];
-  const double tt = static_cast<double>(a.u_final[b]) * W;
-  const double incl = wave_inclusive_scan(local);
+  const double incl = wave_inclusive_scan(static_cast<double>(lsum));
+  if (lane == 63) s_wt[w] = incl;
   __syncthreads();
-  if (lane == 63) s_d[w] = incl;
+  double lbefore = incl - static_cast<double>(lsum);
+  for (int i = 0; i < w; ++i) lbefore += s_wt[i];
+  const unsigned long long hit = __ballot(lsum > 0.f && lbefore + static_cast<double>(lsum) >= t_loc);
+  if (lane == 0) s_first[w] = hit ? w * 64 + __ffsll(static_cast<long long>(hit)) - 1 : INT_MAX;
   __syncthreads();
-  double before = incl - local;
-  for (int i = 0; i < w; ++i) before += s_d[i];
-  int cand = INT_MAX, lastu = -1;
-  {
-    double run = before;
+  int kmin = s_first[0];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      run += mass[q];
-      if (mass[q] > 0.0) {
-        lastu = u0 + q;
-        if (cand == INT_MAX && run >= tt) cand = u0 + q;
-      }
-    }
+  for (int i = 1; i < kWaves; ++i) kmin = min(kmin, s_first[i]);
+  const int n = d.n;
+  const int32_t* xs = a.tokens + static_cast<size_t>(b) * a.K;
+  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+  if (kmin == INT_MAX) {  // rounding left t_loc above the segment total: last positive weight
+    int y = block_max_int(last_pos, s_first);
+    if (y < 0) y = usel * kSeg;
+    for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = kk < n ? xs[kk] : (kk == n ? y : -1);
+    return;
   }
-  int usel = block_min_int(cand, s_i);
-  if (usel == INT_MAX) {  // rounding left u * W above every prefix: last segment with mass
-    usel = block_max_int(lastu, s_i);
-    if (usel < 0) usel = 0;
-  }
-  if (u0 <= usel && usel < u0 + per) {
-    double run = before;
+  for (int kk = tid; kk <= a.K; kk += kThreads)
+    if (kk != n) ot[kk] = kk < n ? xs[kk] : -1;
+  if (tid == kmin) {
+    double run = lbefore;
+    int pick = -1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (u0 + q < usel) run += mass[q];
-    s_base = run;
+    for (int i = 0; i < E; ++i) {
+      run += wl[i];
+      if (pick < 0 && wl[i] > 0.f && run >= t_loc) pick = e0 + i;
+    }
+    ot[n] = pick >= 0 ? pick : last_pos;
   }
-  __syncthreads();
-  *usel_out = usel;
-  *tloc_out = tt - s_base;
-  return true;
 }
 
 // grid = Bs x CP pool tasks for the sequences b0 .. b0+Bs-1, CP = S/SPT per sequence:
@@ -881,14 +983,8 @@ __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bo
 template <int DT, int SPT, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0, int first_tasks_first) {
   constexpr int kRedBytes = 2 * SPT * kThreads * static_cast<int>(sizeof(float));
-  __shared__ __align__(16) unsigned char s_buf[kRedBytes > kStageBytes ? kRedBytes : kStageBytes];
+  __shared__ __align__(16) unsigned char s_buf[kRedBytes];
   __shared__ ChainDecision s_dec;
-  __shared__ double s_d[kWaves];
-  __shared__ int s_i[kWaves];
-  __shared__ int s_y;
-  using EL = Elem<DT>;
-  constexpr int E = EL::kPerVec;
-  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;  // elements per segment
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -905,72 +1001,37 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   }
   const bool last = c == CP - 1;
   float* red = reinterpret_cast<float*>(s_buf);  // [2][SPT][kThreads] per-lane masses
+  const size_t sb = a.stamps_pool + kStampsPerTask * (static_cast<size_t>(b0) * CP + gi);
+  stamp(a, sb + kPhStart);
 
-  chain_decide<DT>(a, b, clamped_len(a, b), last, &s_dec, s_buf);
+  chain_decide<DT>(a, b, clamped_len(a, b), last, &s_dec);
   const ChainDecision d = uniform_decision(s_dec);
-  if (d.mode == kModeInvalid || d.mode == kModeGreedy) return;  // the decision wrote the row
+  stamp(a, sb + kPhDecided);
+  if (a.stamps && tid == 0)
+    a.stamps[sb + kPhInfo] = (static_cast<unsigned long long>(b) << 32) | (static_cast<unsigned>(c) << 8) |
+                             static_cast<unsigned>(d.mode);
+  if (d.mode == kModeInvalid || d.mode == kModeGreedy) {  // the decision wrote the row
+    stamp(a, sb + kPhEnd);
+    return;
+  }
   int mode = d.mode;
   const void* row_t = target_row<DT>(a, b, d.row);
   const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : row_t;
   int usel;
   double t_loc;
   if (mode != kModeResidual) {
-    if (c != 0) return;  // the sequence's first task draws alone
+    if (c != 0) {  // the sequence's first task draws alone
+      stamp(a, sb + kPhEnd);
+      return;
+    }
     direct_select<DT, VEC>(a, b, d, &mode, row_t, red, &usel, &t_loc);
-  } else if (!slot_select<DT, SPT, VEC>(a, b, c, last, d, &mode, row_t, row_d, red, &usel, &t_loc)) {
+    stamp(a, sb + kPhPublished);
+  } else if (!slot_select<DT, SPT, VEC>(a, b, c, last, d, &mode, row_t, row_d, red, &usel, &t_loc, sb)) {
+    stamp(a, sb + kPhEnd);
     return;
   }
-  const int seg_start = usel * kSeg;  // segment u starts at element u * kSeg
-
-  // ---- the lane and the element inside that segment
-  const int e0 = seg_start + tid * E;
-  const u32x4 vt = load_vector<DT, VEC>(row_t, a.V, e0);
-  const u32x4 vd = mode == kModeResidual ? load_vector<DT, VEC>(row_d, a.V, e0) : vt;
-  float wl[E];
-  float lsum = 0.f;
-  int last_pos = -1;
-  {
-    const bool residual = mode == kModeResidual;
-    const int excl = mode == kModeOneHot ? d.excl_tok : -1;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      wl[i] = draw_weight(residual, d, EL::get(vt, i), EL::get(vd, i), e0 + i, excl);
-      lsum += wl[i];
-      last_pos = wl[i] > 0.f ? e0 + i : last_pos;
-    }
-  }
-  const double lincl = wave_inclusive_scan(static_cast<double>(lsum));
-  __syncthreads();
-  if (lane == 63) s_d[w] = lincl;
-  __syncthreads();
-  double lbefore = lincl - static_cast<double>(lsum);
-  for (int i = 0; i < w; ++i) lbefore += s_d[i];
-  const int key = (lsum > 0.f && lbefore + static_cast<double>(lsum) >= t_loc) ? tid : INT_MAX;
-  const int kmin = block_min_int(key, s_i);
-  int y;
-  if (kmin == INT_MAX) {  // rounding left t_loc above the segment total: last positive weight
-    y = block_max_int(last_pos, s_i);
-    // no positive weight at all: only when a direct draw's chunk mass (from the stats
-    // partials) is positive while every draw weight of the chunk underflows to 0
-    if (y < 0) y = seg_start;
-  } else {
-    if (tid == kmin) {
-      double run = lbefore;
-      int pick = -1;
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        run += wl[i];
-        if (pick < 0 && wl[i] > 0.f && run >= t_loc) pick = e0 + i;
-      }
-      s_y = pick >= 0 ? pick : last_pos;
-    }
-    __syncthreads();
-    y = s_y;
-  }
-  const int n = d.n;
-  const int32_t* xs = a.tokens + static_cast<size_t>(b) * a.K;
-  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-  for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = kk < n ? xs[kk] : (kk == n ? y : -1);
+  narrow_and_emit<DT, VEC>(a, b, d, mode, usel, t_loc, row_t, row_d);
+  stamp(a, sb + kPhEnd);
 }
 
 // grid = 1: offsets and packed tokens of the batch (only when packed output is asked for).
@@ -1078,8 +1139,21 @@ static uint32_t next_generation() {
   return g;
 }
 
+// Phase timestamp buffer set by spec_chain_phase_stamps (null: none).
+static std::atomic<unsigned long long*> g_stamps{nullptr};
+static std::atomic<size_t> g_stamp_words{0};
+
 template <int DT, int NV, bool VEC>
-static spec_status_t launch_chain(const ChainArgs& a, hipStream_t stream) {
+static spec_status_t launch_chain(ChainArgs a, hipStream_t stream) {
+  a.stamps = nullptr;
+  if (unsigned long long* buf = g_stamps.load(std::memory_order_acquire)) {
+    const size_t g1 = static_cast<size_t>(a.B) * a.R * a.C;
+    const size_t need = 2 * g1 + kStampsPerTask * static_cast<size_t>(a.B) * (a.S / kPoolSegments);
+    if (need <= g_stamp_words.load(std::memory_order_acquire)) {
+      a.stamps = buf;
+      a.stamps_pool = 2 * g1;
+    }
+  }
   static std::atomic<int> slots_cache[kMaxDevices];
   {
     const long long g1 = static_cast<long long>(a.B) * a.R * a.C;
@@ -1204,7 +1278,7 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   const ChainLayout L = chain_layout(B, K, V, dtype, vec, draft_logits == nullptr);
   const double groups = static_cast<double>(B) * L.R * L.C;
   if (groups > 2147483647.0) return fail(SPEC_ERR_UNSUPPORTED, "grid of %.0f workgroups too large", groups);
-  if (L.S > 4 * kThreads || L.C * kWaves > kStage)
+  if (L.S > 4 * kThreads)
     return fail(SPEC_ERR_UNSUPPORTED, "V = %d is too large (at most %d segments of %d elements)", V, 4 * kThreads,
                 kThreads * (dtype == SPEC_BF16 ? 8 : 4));
   if (!workspace) return fail(SPEC_ERR_WORKSPACE, "workspace is NULL");
@@ -1243,6 +1317,12 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
 
   if (dtype == SPEC_BF16) return dispatch_chain<kBF16>(L.nv, vec, a, s);
   return dispatch_chain<kF32>(L.nv, vec, a, s);
+}
+
+spec_status_t spec_chain_phase_stamps(unsigned long long* buffer, size_t words) {
+  g_stamp_words.store(buffer ? words : 0, std::memory_order_release);
+  g_stamps.store(buffer, std::memory_order_release);
+  return SPEC_OK;
 }
 
 spec_status_t spec_verify_chain_noalloc(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,

@@ -58,6 +58,18 @@ spec_status_t spec_set_knob(spec_knob_t knob, int value);
 /* Current value of a knob (its default unless set), or -1 for an unknown knob. */
 int spec_get_knob(spec_knob_t knob);
 
+/* Phase timestamps of spec_verify_chain's kernels.  While `buffer` (device memory of
+ * `words` unsigned 64-bit words) is set, every following call whose stamps fit writes
+ * the device's constant 100 MHz clock at its phase boundaries into it (a call that needs
+ * more words writes none): with G = B * R * C stats workgroups (R rows and C chunks per
+ * row as the call chose them) and P pool tasks, words [2g, 2g+1] are the start and end of
+ * stats workgroup g and words [2G + 6t, 2G + 6t + 5] those of pool task t: start,
+ * decision made, own segment masses published (or the piece chosen, for a draw from a
+ * target row), siblings' masses gathered (the waiting task), end, and
+ * (b << 32) | (c << 8) | mode.  Words of phases a task does not reach are left as they
+ * were.  NULL stops the stamping.  Measurement only; the same thread rule as the knobs. */
+spec_status_t spec_chain_phase_stamps(unsigned long long* buffer, size_t words);
+
 /* Read-only streaming probe in the access shape of the library's streaming passes: one
  * workgroup per `chunk_bytes` chunk (16384, 32768 or 65536), chunks dealt to the XCDs in
  * contiguous blocks, each wave reading one contiguous quarter of its chunk with
