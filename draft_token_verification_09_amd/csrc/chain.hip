@@ -141,7 +141,6 @@ struct ChainArgs {
   RowStat* part;        // [B, R, C, 4] partials, one per wave of each chunk
   float* gath;          // [B, R] logit of the drafted token in each scoring row
   SlotDouble* wseg;     // [B, S] slots: mass of the final draw's weights per segment
-  SlotDouble* wsegp;    // [B, S] slots: mass of p of the same row per segment (fallback)
   unsigned long long* stamps;  // phase timestamps (measurement only; see spec_chain_phase_stamps), or null
   size_t stamps_pool;          // index of the pool tasks' first stamp
 };
@@ -557,184 +556,223 @@ __device__ __forceinline__ void chain_pack(const ChainArgs& a) {
 }
 
 // Bonus and one-hot draws (and the fallback to p) sample target row d.row itself, minus the
-// drafted token after a one-hot rejection.  The stats pass already summed that row in
-// pieces: each wave partial (o, s) covers one contiguous quarter of a chunk, with mass
-// s * exp2(o - O) / S (the same terms whose total is the row's S).  So the draw needs no
-// pass over the whole row.  Units are pieces, or whole segments where a piece is smaller than
-// a segment; the unit whose inclusive prefix reaches u * W (W = the total) is picked from
-// these masses.  A unit of several segments is then read once and its segments' draw
-// weights summed to pick the segment.  Returns the segment and u * W minus the mass before
-// it; `mode` becomes kModeFallbackP if no mass is left after removing the drafted token.
+// drafted token after a one-hot rejection, and write the emitted row; called by every lane
+// of one task.  The stats pass already summed that row in pieces: each wave partial (o, s)
+// covers one contiguous quarter of a chunk, with mass s * exp2(o - O) / S (the same terms
+// whose total is the row's S).  So the draw needs no pass over the whole row:
+//  1. wave 0 alone takes the units (pieces, or whole segments where a piece is smaller than
+//     a segment), 64 per round, forms their masses from the partials, and scans them in
+//     vocabulary order for the unit whose inclusive prefix reaches u * W (W = the total);
+//  2. wave q reads segment q of that unit (lane l: the segment's vectors l, l + 64, l + 128,
+//     l + 192, so that each load is 1 KiB of contiguous memory), sums each vector's draw
+//     weights in fp32 and scans the sums in vocabulary order in fp64, one round of 64
+//     vectors at a time; the final prefix is the segment's mass;
+//  3. every lane picks the segment from the masses, and the wave holding it narrows from its
+//     registers to the vector, then the element, and writes the row.
 // Unit masses come from the stats partials and segment masses from the draw weights, so the
 // two agree to rounding; where u * W lies within that rounding of a boundary the last
-// segment (or element) with mass is taken, as for every other draw.  Called by every lane
-// of one task; `red` is shared memory of at least 4 * kThreads floats.
+// segment (or element) with mass is taken, as for every other draw.  With no mass left
+// after removing the drafted token (all of the row on it), the draw falls back to p.
 template <int DT, bool VEC>
-__device__ __forceinline__ void direct_select(const ChainArgs& a, int b, const ChainDecision& d, int* mode,
-                                              const void* row, float* red, int* usel_out, double* tloc_out) {
-  __shared__ double s_tot[kWaves];
-  __shared__ double s_seg[4];
-  __shared__ int s_pick[kWaves];
-  __shared__ double s_before;
-  __shared__ int s_u;
+__device__ __forceinline__ void direct_draw(const ChainArgs& a, int b, const ChainDecision& d, int mode,
+                                            const void* row, size_t sb) {
+  __shared__ int s_unit, s_mode;
+  __shared__ double s_tu;
+  __shared__ double s_segm[kWaves];
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
+  constexpr int kVPL = kThreads / 64;  // vectors of a segment per lane of a wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int piece = a.nv * (kSeg / kWaves);      // elements of one wave partial
+  const int piece = a.nv * (kSeg / kWaves);             // elements of one wave partial
   const int pper = a.nv >= kWaves ? 1 : kWaves / a.nv;  // pieces per unit
   const int segs = a.nv >= kWaves ? a.nv / kWaves : 1;  // segments per unit
   const int unit = pper * piece;
   const int units = (a.V + unit - 1) / unit;            // <= S <= 4 * kThreads
-  const int per = (units + kThreads - 1) / kThreads;    // <= 4
-  const int u0 = tid * per;
-  const int excl_unit = *mode == kModeOneHot ? d.excl_tok / unit : -1;
-  const RowStat* ps = a.part + (static_cast<size_t>(b) * a.R + d.row) * a.C * kWaves;
+  const int nparts = a.C * kWaves;
+  const RowStat* ps = a.part + (static_cast<size_t>(b) * a.R + d.row) * nparts;
 
-  // unit masses in units of p (this lane: units u0 .. u0+per-1)
-  double m[4], mc[4];
-  double local = 0.0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    m[q] = 0.0;
-    const int u = u0 + q;
-    if (q < per && u < units) {
-      for (int k = 0; k < pper && u * pper + k < a.C * kWaves; ++k) {
-        const RowStat st = ps[u * pper + k];
-        if (st.o != -INFINITY) m[q] += st.s * static_cast<double>(exp2_fast(st.o - d.Ot));
+  // ---- 1. wave 0: the unit holding u * W
+  if (w == 0) {
+    const int rounds = (units + 63) / 64;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+      const int excl_unit = mode == kModeOneHot ? d.excl_tok / unit : -1;
+      auto mass = [&](int u) -> double {  // unit u's mass in units of p
+        double m = 0.0;
+        if (u < units) {
+          for (int k = 0; k < pper && u * pper + k < nparts; ++k) {
+            const RowStat st = ps[u * pper + k];
+            if (st.o != -INFINITY) m += st.s * static_cast<double>(exp2_fast(st.o - d.Ot));
+          }
+          m /= d.St;
+          if (u == excl_unit) m = fmax(0.0, m - static_cast<double>(d.p_excl));
+        }
+        return m;
+      };
+      double carry = 0.0;
+      for (int r = 0; r < rounds; ++r) carry = lane_broadcast(wave_inclusive_scan(mass(64 * r + lane)) + carry, 63);
+      const double W = carry;
+      if (!(W > 0.0) && mode == kModeOneHot) {  // all of the row's mass sat on the drafted token
+        mode = kModeFallbackP;
+        continue;
       }
-      m[q] /= d.St;
+      const double tt = static_cast<double>(a.u_final[b]) * W;
+      int usel = -1, lastu = -1;
+      double before = 0.0, last_before = 0.0;
+      carry = 0.0;
+      for (int r = 0; r < rounds && usel < 0; ++r) {
+        const double m = mass(64 * r + lane);
+        const double incl = wave_inclusive_scan(m) + carry;  // as for the total above
+        carry = lane_broadcast(incl, 63);
+        const unsigned long long hit = __ballot(m > 0.0 && incl >= tt);
+        if (hit) {
+          const int l = __ffsll(static_cast<long long>(hit)) - 1;
+          usel = 64 * r + l;
+          before = lane_broadcast(incl - m, l);
+        }
+        const unsigned long long pos = __ballot(m > 0.0);
+        if (pos) {
+          const int l = 63 - __clzll(static_cast<long long>(pos));
+          lastu = 64 * r + l;
+          last_before = lane_broadcast(incl - m, l);
+        }
+      }
+      if (usel < 0) {  // rounding left u * W above every prefix: the last unit with mass
+        usel = lastu >= 0 ? lastu : 0;
+        before = lastu >= 0 ? last_before : 0.0;
+      }
+      if (lane == 0) {
+        s_unit = usel;
+        s_tu = tt - before;
+        s_mode = mode;
+      }
+      break;
     }
-    mc[q] = u0 + q == excl_unit ? fmax(0.0, m[q] - static_cast<double>(d.p_excl)) : m[q];
-    local += mc[q];
   }
-  double W = block_sum(local, s_tot);
-  if (!(W > 0.0) && *mode == kModeOneHot) {  // all of the row's mass sat on the drafted token
-    *mode = kModeFallbackP;
-    local = 0.0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      mc[q] = m[q];
-      local += m[q];
-    }
-    W = block_sum(local, s_tot);
-  }
-  const double tt = static_cast<double>(a.u_final[b]) * W;
-
-  // the unit whose inclusive prefix reaches u * W (lanes in unit order)
-  const double incl = wave_inclusive_scan(local);
-  __syncthreads();  // every wave has read block_sum's s_tot
-  if (lane == 63) s_tot[w] = incl;
   __syncthreads();
-  double before = incl - local;
-  for (int i = 0; i < w; ++i) before += s_tot[i];
-  int cand = INT_MAX, lastu = -1;
+  stamp(a, sb + kPhPublished);
+  const int usel = s_unit;
+  const double t_unit = s_tu;
+  mode = s_mode;
+  const int excl = mode == kModeOneHot ? d.excl_tok : -1;
+
+  // ---- 2. wave q: segment q of the unit, scanned in vocabulary order
+  const int seg = usel * segs + w;  // this wave's segment
+  const int e0 = seg * kSeg + lane * E;
+  u32x4 v[kVPL];
+  float vs[kVPL];
+  double incl[kVPL];
+  double carry = 0.0;
+  if (w < segs) {
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) v[j] = load_vector<DT, VEC>(row, a.V, e0 + j * 64 * E);
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) s += draw_weight(false, d, EL::get(v[j], i), 0.f, e0 + j * 64 * E + i, excl);
+      vs[j] = s;
+      incl[j] = wave_inclusive_scan(static_cast<double>(s)) + carry;
+      carry = lane_broadcast(incl[j], 63);
+    }
+    if (lane == 0) s_segm[w] = carry;
+  }
+  __syncthreads();
+
+  // ---- 3. the segment (the same choice in every lane), then the wave holding it narrows
+  int q = -1, lastq = -1;
+  double qbase = 0.0, lastbase = 0.0;
   {
-    double run = before;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      run += mc[q];
-      if (mc[q] > 0.0) {
-        lastu = u0 + q;
-        if (cand == INT_MAX && run >= tt) cand = u0 + q;
-      }
-    }
-  }
-  int usel = block_min_int(cand, s_pick);
-  if (usel == INT_MAX) {  // rounding left u * W above every prefix: last unit with mass
-    usel = block_max_int(lastu, s_pick);
-    if (usel < 0) usel = 0;
-  }
-  if (u0 <= usel && usel < u0 + per) {
-    double run = before;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (u0 + q < usel) run += mc[q];
-    s_before = run;
-  }
-  __syncthreads();
-  if (segs == 1) {  // the unit is one segment
-    *usel_out = usel;
-    *tloc_out = tt - s_before;
-    return;
-  }
-
-  // a unit of 2 or 4 segments: read it once and pick the segment
-  const int excl = *mode == kModeOneHot ? d.excl_tok : -1;
-  const int s_first = usel * segs;
-  u32x4 v[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    v[q] = q < segs ? load_vector<DT, VEC>(row, a.V, ((s_first + q) * kThreads + tid) * E) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float ls = 0.f;
-    if (q < segs) {
-      const int e0 = ((s_first + q) * kThreads + tid) * E;
-#pragma unroll
-      for (int i = 0; i < E; ++i) ls += draw_weight(false, d, EL::get(v[q], i), 0.f, e0 + i, excl);
-    }
-    red[q * kThreads + tid] = ls;
-  }
-  __syncthreads();
-  {  // one 16-lane row of the workgroup sums one segment's 256 lane values
-    const int q = tid >> 4;
-    const int r = tid & 15;
-    double sv = 0.0;
-    if (q < segs) {
-      const float* src = red + q * kThreads + r * 16;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sv += static_cast<double>(src[i]);
-    }
-    sv = row16_inclusive_sum(sv);
-    if (q < segs && r == 15) s_seg[q] = sv;
-  }
-  __syncthreads();
-  if (tid == 0) {  // the unit's segments in vocabulary order
-    double run = s_before;
-    int pick = -1, last_pos = -1;
-    double pick_base = 0.0, last_base = 0.0;
-    for (int q = 0; q < segs; ++q) {
-      const double sm = s_seg[q];
+    double run = 0.0;
+    for (int k = 0; k < segs; ++k) {
+      const double sm = s_segm[k];
       if (sm > 0.0) {
-        last_pos = q;
-        last_base = run;
-        if (pick < 0 && run + sm >= tt) {
-          pick = q;
-          pick_base = run;
+        lastq = k;
+        lastbase = run;
+        if (q < 0 && run + sm >= t_unit) {
+          q = k;
+          qbase = run;
         }
       }
       run += sm;
     }
-    if (pick < 0) {  // rounding, as above: last segment with mass (the unit's first if none)
-      pick = last_pos >= 0 ? last_pos : 0;
-      pick_base = last_pos >= 0 ? last_base : s_before;
+    if (q < 0) {  // rounding, as above: the unit's last segment with mass (its first if none)
+      q = lastq >= 0 ? lastq : 0;
+      qbase = lastq >= 0 ? lastbase : 0.0;
     }
-    s_u = s_first + pick;
-    s_before = tt - pick_base;
   }
-  __syncthreads();
-  *usel_out = s_u;
-  *tloc_out = s_before;
+  if (w != q) return;
+  const double t_seg = t_unit - qbase;
+  int jsel = -1, lsel = -1;
+#pragma unroll
+  for (int j = 0; j < kVPL; ++j) {
+    const unsigned long long hit = __ballot(vs[j] > 0.f && incl[j] >= t_seg);
+    if (jsel < 0 && hit) {
+      jsel = j;
+      lsel = __ffsll(static_cast<long long>(hit)) - 1;
+    }
+  }
+  int y;
+  if (jsel < 0) {  // rounding left t_seg above the segment's total: its last positive weight
+    int last_pos = -1;
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j)
+#pragma unroll
+      for (int i = 0; i < E; ++i)
+        if (draw_weight(false, d, EL::get(v[j], i), 0.f, e0 + j * 64 * E + i, excl) > 0.f)
+          last_pos = max(last_pos, e0 + j * 64 * E + i);
+    y = wave_max_int(last_pos);
+    if (y < 0) y = seg * kSeg;
+  } else {
+    int pick = -1;
+    if (lane == lsel) {
+      u32x4 vv = v[0];
+      double run = incl[0] - static_cast<double>(vs[0]);
+#pragma unroll
+      for (int j = 1; j < kVPL; ++j)
+        if (j == jsel) {
+          vv = v[j];
+          run = incl[j] - static_cast<double>(vs[j]);
+        }
+      const int ev = e0 + jsel * 64 * E;
+      int lastw = -1;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const float wv = draw_weight(false, d, EL::get(vv, i), 0.f, ev + i, excl);
+        run += static_cast<double>(wv);
+        if (wv > 0.f) lastw = ev + i;
+        if (pick < 0 && wv > 0.f && run >= t_seg) pick = ev + i;
+      }
+      if (pick < 0) pick = lastw;
+    }
+    y = lane_broadcast(pick, lsel);
+  }
+  const int n = d.n;
+  const int32_t* xs = a.tokens + static_cast<size_t>(b) * a.K;
+  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+  for (int kk = lane; kk <= a.K; kk += 64) ot[kk] = kk < n ? xs[kk] : (kk == n ? y : -1);
 }
+
+// Outcomes of a residual draw's hand-over (slot_select, gather_and_locate).
+enum SlotOutcome : int { kSlotDone = 0, kSlotLocated = 1, kSlotNoMass = 2 };
 
 // Wave 0 of a sequence's last pool task, alone (the other waves wait at a barrier): lane l
 // takes segments l, l + 64, ... (round r holds segments 64 r .. 64 r + 63), waits for their
 // masses, and the rounds' inclusive scans in vocabulary order give the total W and the
 // segment whose prefix first reaches u * W.  The masses stay in shared memory (s_m, room for
-// S doubles); the scans are recomputed for the search.  Leaves the segment and u * W minus
-// the mass before it in *usel_out and *tloc_out (lane 0 writes them) and returns true; if a
-// wait gives up, flags the sequence and returns false.
-__device__ __forceinline__ bool gather_and_locate(const ChainArgs& a, int b, uint32_t gen, const SlotDouble* mw,
-                                                  const SlotDouble* mp, int units, double* s_m, int* mode,
-                                                  int* usel_out, double* tloc_out, size_t sb) {
+// S doubles); the scans are recomputed for the search.  Returns kSlotLocated with the segment
+// and u * W minus the mass before it in *usel_out and *tloc_out (lane 0 writes them);
+// kSlotNoMass if rounding left no residual mass (W = 0); kSlotDone if a wait gave up (the
+// sequence is then flagged).
+__device__ __forceinline__ int gather_and_locate(const ChainArgs& a, int b, uint32_t gen, const SlotDouble* mw,
+                                                 int units, double* s_m, int* usel_out, double* tloc_out,
+                                                 size_t sb) {
   const int lane = threadIdx.x & 63;
   const int rounds = (units + 63) / 64;  // units = S <= 4 * kThreads
-  double W = 0.0;
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    const SlotDouble* slots = attempt == 0 ? mw : mp;
+  {
+    const SlotDouble* slots = mw;
     unsigned have = 0;  // rounds whose slot this lane has read
     for (int r = 0; r < rounds; ++r)
       if (64 * r + lane >= units) {
@@ -763,15 +801,13 @@ __device__ __forceinline__ bool gather_and_locate(const ChainArgs& a, int b, uin
       if (lane == 0) a.out_num[b] = kFlagTimedOut;
       if (a.out_probs)
         for (int i = lane; i < a.K * 3; i += 64) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
-      return false;
+      return kSlotDone;
     }
-    double carry = 0.0;
-    for (int r = 0; r < rounds; ++r) carry = lane_broadcast(wave_inclusive_scan(s_m[64 * r + lane]) + carry, 63);
-    W = carry;
-    if (W > 0.0) break;
-    *mode = kModeFallbackP;  // no residual mass left after rounding: draw from p_n itself
   }
+  double W = 0.0;
+  for (int r = 0; r < rounds; ++r) W = lane_broadcast(wave_inclusive_scan(s_m[64 * r + lane]) + W, 63);
   stamp(a, sb + kPhGathered);
+  if (!(W > 0.0)) return kSlotNoMass;  // no residual mass left after rounding: draw from p_n itself
   const double tt = static_cast<double>(a.u_final[b]) * W;
   int usel = -1, lastu = -1;
   double before = 0.0, last_before = 0.0, carry = 0.0;
@@ -800,19 +836,19 @@ __device__ __forceinline__ bool gather_and_locate(const ChainArgs& a, int b, uin
     *usel_out = usel;
     *tloc_out = tt - before;
   }
-  return true;
+  return kSlotLocated;
 }
 
 // Residual draw after a rejection against draft rows (see chain_pool_kernel, steps 1-3):
-// this task's segment masses of max(0, p - q) and p go out through the slots; the sequence's
-// last task waits for the others' and returns true with the segment holding u * W and u * W
-// minus the mass before it.  Other tasks return false, and so does a last task whose wait
-// gave up (it flags the sequence).  `red` is shared memory of 2 * SPT * kThreads floats
-// (per-lane masses).
+// this task's segment masses of max(0, p - q) go out through the slots; the sequence's last
+// task waits for the others' and returns kSlotLocated with the segment holding u * W and
+// u * W minus the mass before it, or kSlotNoMass if rounding left no residual mass.  Other
+// tasks return kSlotDone, and so does a last task whose wait gave up (it flags the
+// sequence).  `red` is shared memory of 2 * SPT * kThreads floats.
 template <int DT, int SPT, bool VEC>
-__device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bool last, const ChainDecision& d,
-                                            int* mode, const void* row_t, const void* row_d, float* red,
-                                            int* usel_out, double* tloc_out, size_t sb) {
+__device__ __forceinline__ int slot_select(const ChainArgs& a, int b, int c, bool last, const ChainDecision& d,
+                                           const void* row_t, const void* row_d, float* red, int* usel_out,
+                                           double* tloc_out, size_t sb) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
@@ -823,7 +859,7 @@ __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bo
   // 0.5 us less pool time at B=64, K=5, V=128256; 2.3 us at B=256, K=8, V=152064)
   const uint32_t gen = pool_generation(a);
 
-  // ---- 1. per-lane masses of this task's segments: max(0, p - q), and p
+  // ---- 1. per-lane masses of this task's segments: max(0, p - q), one vector per lane
   {
     const int sbase = c * SPT * kSeg;  // first element of this task's segments
     u32x4 rt[SPT], rd[SPT];
@@ -833,49 +869,44 @@ __device__ __forceinline__ bool slot_select(const ChainArgs& a, int b, int c, bo
     for (int j = 0; j < SPT; ++j) rd[j] = load_vector<DT, VEC>(row_d, a.V, sbase + (j * kThreads + tid) * E);
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
-      float aw = 0.f, ap = 0.f;
+      float aw = 0.f;
 #pragma unroll
       for (int i = 0; i < E; ++i) {
         const float pv = exp2_fast(fmaf(EL::get(rt[j], i), d.scale, -d.Ot)) * d.invSt;
         aw += fmaxf(0.f, pv - exp2_fast(fmaf(EL::get(rd[j], i), d.scale, -d.Od)) * d.invSd);
-        ap += pv;
       }
       red[j * kThreads + tid] = aw;
-      red[(SPT + j) * kThreads + tid] = ap;
     }
   }
   __syncthreads();
   // ---- 2. segment totals in fp64 (one 16-lane row sums one segment's 256 lane values)
   const int units = a.S;  // segment slots per row
   SlotDouble* mw = a.wseg + static_cast<size_t>(b) * units;
-  SlotDouble* mp = a.wsegp + static_cast<size_t>(b) * units;
   {
-    const int q = tid >> 4;  // q < SPT: draw-weight mass of segment q; SPT <= q < 2 SPT: p mass
+    const int q = tid >> 4;  // q < SPT: segment q
     const int r = tid & 15;
     double v = 0.0;
-    if (q < 2 * SPT) {
+    if (q < SPT) {
       const float* src = red + q * kThreads + r * 16;
 #pragma unroll
       for (int i = 0; i < 16; ++i) v += static_cast<double>(src[i]);
     }
     v = row16_inclusive_sum(v);
-    if (q < 2 * SPT && r == 15) put_slot((q < SPT ? mw : mp) + c * SPT + (q % SPT), v, gen);
+    if (q < SPT && r == 15) put_slot(mw + c * SPT + q, v, gen);
   }
   stamp(a, sb + kPhPublished);
-  if (!last) return false;
-  __shared__ int s_usel, s_mode;
+  if (!last) return kSlotDone;
+  __shared__ int s_outcome, s_usel;
   __shared__ double s_tloc;
   __syncthreads();  // every wave is done with `red`, which holds the gathered masses next
-  if (w == 0 && !gather_and_locate(a, b, gen, mw, mp, units, reinterpret_cast<double*>(red), mode, &s_usel,
-                                   &s_tloc, sb)) {
-    if (lane == 0) s_usel = -1;
+  if (w == 0) {
+    const int o = gather_and_locate(a, b, gen, mw, units, reinterpret_cast<double*>(red), &s_usel, &s_tloc, sb);
+    if (lane == 0) s_outcome = o;
   }
-  if (w == 0 && lane == 0) s_mode = *mode;
   __syncthreads();
-  *mode = s_mode;
   *usel_out = s_usel;
   *tloc_out = s_tloc;
-  return s_usel >= 0;
+  return s_outcome;
 }
 
 // Narrows a draw to one element of segment `usel` and writes the emitted row (x_0 .. x_{n-1},
@@ -1016,21 +1047,21 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   }
   int mode = d.mode;
   const void* row_t = target_row<DT>(a, b, d.row);
-  const void* row_d = mode == kModeResidual ? draft_row<DT>(a, b, d.row) : row_t;
-  int usel;
-  double t_loc;
-  if (mode != kModeResidual) {
-    if (c != 0) {  // the sequence's first task draws alone
+  if (mode == kModeResidual) {
+    int usel;
+    double t_loc;
+    const int o = slot_select<DT, SPT, VEC>(a, b, c, last, d, row_t, draft_row<DT>(a, b, d.row), red, &usel, &t_loc, sb);
+    if (o == kSlotLocated) narrow_and_emit<DT, VEC>(a, b, d, mode, usel, t_loc, row_t, draft_row<DT>(a, b, d.row));
+    if (o != kSlotNoMass) {
       stamp(a, sb + kPhEnd);
       return;
     }
-    direct_select<DT, VEC>(a, b, d, &mode, row_t, red, &usel, &t_loc);
-    stamp(a, sb + kPhPublished);
-  } else if (!slot_select<DT, SPT, VEC>(a, b, c, last, d, &mode, row_t, row_d, red, &usel, &t_loc, sb)) {
+    mode = kModeFallbackP;  // no residual mass left after rounding: the last task draws from p_n
+  } else if (c != 0) {      // a bonus or one-hot draw: the sequence's first task draws alone
     stamp(a, sb + kPhEnd);
     return;
   }
-  narrow_and_emit<DT, VEC>(a, b, d, mode, usel, t_loc, row_t, row_d);
+  direct_draw<DT, VEC>(a, b, d, mode, row_t, sb);
   stamp(a, sb + kPhEnd);
 }
 
@@ -1047,7 +1078,7 @@ constexpr int kPoolSegments = 4;  // segments per pool task
 
 struct ChainLayout {
   int nv, C, R, S;
-  size_t off_gath, off_part, off_wseg, off_wsegp, bytes;
+  size_t off_gath, off_part, off_wseg, bytes;
 };
 
 // Vectors per lane in one stats chunk.  The largest chunk (16 vectors for bf16 rows read with
@@ -1104,8 +1135,6 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool ve
   L.off_part = off;
   off = align_up(off + sizeof(RowStat) * static_cast<size_t>(B) * L.R * L.C * kWaves, 256);
   L.off_wseg = off;
-  off = align_up(off + sizeof(SlotDouble) * segs, 256);
-  L.off_wsegp = off;
   off = align_up(off + sizeof(SlotDouble) * segs, 256);
   L.bytes = off;
   return L;
@@ -1313,7 +1342,6 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   a.gath = reinterpret_cast<float*>(ws + L.off_gath);
   a.part = reinterpret_cast<RowStat*>(ws + L.off_part);
   a.wseg = reinterpret_cast<SlotDouble*>(ws + L.off_wseg);
-  a.wsegp = reinterpret_cast<SlotDouble*>(ws + L.off_wsegp);
 
   if (dtype == SPEC_BF16) return dispatch_chain<kBF16>(L.nv, vec, a, s);
   return dispatch_chain<kF32>(L.nv, vec, a, s);

@@ -251,3 +251,32 @@ def test_host_errors_raise():
     with pytest.raises(m.SpecError):
         m.ngram_propose(torch.zeros((1, 4), dtype=torch.int32, device=dev()),
                         torch.ones(1, dtype=torch.int32, device=dev()), 1, 17, 5)
+
+
+def _rounding_residual_case(B=8, K=2, V=4100, seed=14):
+    # The residual max(0, p - q) is zero in both the oracle's float64 and the GPU's float32
+    # arithmetic although a draft was rejected: 4096 logits of 0 and four of -50 in each row,
+    # so every row sum is exactly 2^12 and every p (and q) of a 0 logit is exactly 2^-12.  At
+    # position 0 the drafted token x is one of the -50s in the target and -49 in the draft:
+    # alpha = 1/e, u = 1 rejects it, and q(x) moves no row sum, so p = q everywhere but at x.
+    # Both sides then draw from p_0 (the fallback of the oracle's step 3), with u_final kept
+    # half a token away from every boundary of p_0's cumulative sum.
+    rng = np.random.default_rng(seed)
+    target = np.zeros((B, K + 1, V), np.float32)
+    tokens = np.zeros((B, K), np.int32)
+    for b in range(B):
+        neg = rng.choice(V, size=4, replace=False)
+        target[b, :, neg] = np.float32(-50.0)
+        tokens[b] = [int(neg[0]), int(rng.integers(0, V))]
+    draft = target[:, :K].copy()
+    for b in range(B):
+        draft[b, 0, tokens[b, 0]] = np.float32(-49.0)
+    u_fin = ((rng.integers(0, 4096, B) + 0.5) / 4096.0).astype(np.float32)
+    return _inputs_from_arrays(target, draft, tokens, np.ones((B, K)), u_fin)
+
+
+def test_residual_mass_lost_to_rounding_draws_from_p():
+    inp = _rounding_residual_case()
+    ref = chain_oracle(inp)
+    assert all(s.mode == "residual_zero_fallback" and s.num_accepted == 0 for s in ref.sequences)
+    _parity(inp)
