@@ -379,7 +379,24 @@ def other_workloads(warmup, steps, dev):
                          ua=torch.from_numpy(inp.u_accept).to(dev), uf=torch.from_numpy(inp.u_final).to(dev),
                          bytes=chain_bytes(inp) + pr.context.nbytes + pr.context_len.nbytes))
 
-    # propose, then verify the proposals in place (the verify reads the propose's outputs)
+    nb = int(np.mean([s["bytes"] for s in sets]))
+    # one call: the lookup runs beside the row statistics of every target row (all K+1 rows are
+    # read, since the draft lengths are not known when the streaming starts)
+    fused = [sv.prepare_spec_ngram_verify(s["ctx"], s["cl"], 1, 4, s["t"], s["T"], s["ua"], s["uf"]) for s in sets]
+
+    def fcall(i):
+        fused[i]()
+
+    ms = time_calls_median(fcall, n_sets, warmup, steps)
+    _, kms = time_calls(fcall, n_sets, 2, steps, True)
+    r = _entry("ngram_propose_verify_B128_L4096_K5_V32000_bf16", dict(ms=ms, bytes=nb, kernels=kms, steps=steps),
+               128 * 5)
+    r["call"] = "spec_ngram_verify"
+    r["rows_streamed_per_call"] = 128 * 6
+    out.append(r)
+    del fused
+    # the same work as two calls: propose, then verify the proposals in place (the verify reads
+    # the propose's outputs and streams only the rows up to each draft length)
     pairs = []
     for s in sets:
         pp = sv.prepare_ngram_propose(s["ctx"], s["cl"], 1, 4, 5)
@@ -394,10 +411,11 @@ def other_workloads(warmup, steps, dev):
 
     ms = time_calls_median(ncall, n_sets, warmup, steps)
     _, kms = time_calls(ncall, n_sets, 2, steps, True)
-    nb = int(np.mean([s["bytes"] for s in sets]))
     del sets
-    out.append(_entry("ngram_propose_verify_B128_L4096_K5_V32000_bf16", dict(ms=ms, bytes=nb, kernels=kms, steps=steps),
-                      128 * 5))
+    r = _entry("ngram_propose_then_verify_B128_L4096_K5_V32000_bf16", dict(ms=ms, bytes=nb, kernels=kms, steps=steps),
+               128 * 5)
+    r["call"] = "ngram_propose + spec_verify_chain"
+    out.append(r)
     return out
 
 
@@ -566,6 +584,11 @@ def chain_phases(make, name, warmup, calls, dev, chunk_vectors, pool_segments):
     n_sets = sets_needed(per_set)
     sets, _ = chain_device_sets(make, n_sets, dev)
     B, K, V = probe.B, probe.K, probe.V
+    if chunk_vectors is None:  # the library's own choice, read back from its chunk rule's inputs
+        epv = 8 if probe.dtype == "bf16" else 4
+        vec = (V * (2 if probe.dtype == "bf16" else 4)) % 16 == 0
+        rows = B * (2 * K + 1 if probe.draft is not None else K + 1)
+        chunk_vectors = library_chunk_vectors(rows, V, epv, vec)
     code = 1 if probe.dtype == "bf16" else 0
     ws = torch.empty(sv.spec_verify_chain_workspace_size(B, K, V, code) + 256, dtype=torch.uint8, device=dev)
     prepared = [sv.prepare_spec_verify_chain(s["t"], s["d"], s["tok"], s["T"], s["ua"], s["uf"], s["dl"],
@@ -574,7 +597,7 @@ def chain_phases(make, name, warmup, calls, dev, chunk_vectors, pool_segments):
     C = -(-V // (chunk_vectors * 256 * epv))
     R = 2 * K + 1 if probe.draft is not None else K + 1
     S = -(-(-(-V // (256 * epv))) // pool_segments) * pool_segments
-    G, P = B * R * C, B * (S // pool_segments)
+    G, P = B * R * C, B * (S // pool_segments if probe.draft is not None else 1)
     buf = torch.zeros(2 * G + 6 * P, dtype=torch.int64, device=dev)
     for i in range(warmup):
         prepared[i % n_sets]()
@@ -600,7 +623,7 @@ def chain_phases(make, name, warmup, calls, dev, chunk_vectors, pool_segments):
         mode = pool[:, 5] & 0xFF
         c = (pool[:, 5] >> 8) & 0xFFFFFF
         res = mode == 1
-        last = res & (c == S // pool_segments - 1)
+        last = res & (c == (S // pool_segments if probe.draft is not None else 1) - 1)
         if res.any():
             r["residual_sequences"] = int(last.sum())
             r["published"] = np.median(pool[res, 2] - pool[res, 1]) * us
@@ -626,6 +649,24 @@ def chain_phases(make, name, warmup, calls, dev, chunk_vectors, pool_segments):
         if vals:
             lines.append(f"  {k:28s} {np.median(vals):8.2f}   (min {np.min(vals):.2f}, max {np.max(vals):.2f})")
     return "\n".join(lines)
+
+
+def library_chunk_vectors(rows, V, epv, vec, max_chunks=16):
+    """The chain stats pass's chunk rule (vectors per lane in one chunk), restated for laying out
+    the phase timestamps: the largest chunk giving at least 1024 workgroups with at most
+    max_chunks chunks a row, else the smallest within that bound but not under 4 vectors."""
+    top = 16 if vec and epv == 8 else 8
+    pick = 0
+    nv = top
+    while nv >= 1:
+        chunks = -(-V // (nv * 256 * epv))
+        if chunks > max_chunks:
+            break
+        pick = nv
+        if rows * chunks >= 1024:
+            return nv
+        nv //= 2
+    return (4 if pick < 4 else pick) if pick else top
 
 
 def achievable_read(dev, nbytes, warmup, steps):
@@ -788,10 +829,18 @@ def main():
         result["probes"] = probe(dev)
     if args.phases:
         progress("phase timestamps")
+        def one_hot(s):
+            inp = synth.chain_config_high_accept_bf16(s, B=128, V=32000)
+            inp.draft = None
+            return inp
+
         text = [chain_phases(lambda s: host0 if s == 0 else synth.chain_config_high_accept_bf16(s), workload,
-                             args.warmup, 20, dev, 16, 4),
+                             args.warmup, 20, dev, None, 4),
                 chain_phases(lambda s: synth.chain_config_low_accept_bf16(s), "chain_verify_B256_K8_V152064_bf16",
-                             args.warmup, 20, dev, 16, 4)]
+                             args.warmup, 20, dev, None, 4),
+                chain_phases(lambda s: synth.chain_config_small_f32(s), "chain_verify_B1_K5_V32000_f32",
+                             args.warmup, 20, dev, None, 4),
+                chain_phases(one_hot, "chain_verify_one_hot_B128_K5_V32000_bf16", args.warmup, 20, dev, None, 4)]
         with open(args.phases, "w") as f:
             f.write("\n\n".join(text) + "\n")
     print(json.dumps(result), flush=True)

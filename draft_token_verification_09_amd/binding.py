@@ -59,6 +59,8 @@ _SIGNATURES = {
     "spec_verify_tree_greedy": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                        _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ngram_propose": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "spec_ngram_verify": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_tree_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "spec_verify_tree": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                 _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -443,6 +445,78 @@ def ngram_propose(context: torch.Tensor, context_len: torch.Tensor, n_min: int, 
     args, out, _ = _ngram_call(context, context_len, n_min, n_max, K, want_match_n, out, stream)
     _check("ngram_propose", lib().ngram_propose(*args))
     return out
+
+
+@dataclass
+class NgramVerifyResult:
+    proposal: NgramResult
+    verify: ChainResult
+
+
+def _ngram_verify_call(context, context_len, n_min, n_max, target_logits, temperature, u_accept, u_final,
+                       want_probs, want_packed, out, workspace_buf, stream):
+    if context.dim() != 2 or target_logits.dim() != 3:
+        raise ValueError("context must be [B, L_max] and target_logits [B, K+1, V]")
+    B, L_max = context.shape
+    B2, K1, V = target_logits.shape
+    if B2 != B:
+        raise ValueError("context and target_logits must have the same batch")
+    K = K1 - 1
+    dev = target_logits.device
+    code = _dtype_code(target_logits)
+    if not target_logits.is_contiguous():
+        raise ValueError("target_logits must be contiguous")
+    _need(context, "context", torch.int32, (B, L_max), dev)
+    _need(context_len, "context_len", torch.int32, (B,), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, K), dev)
+    _need(u_final, "u_final", torch.float32, (B,), dev)
+    if out is None:
+        out = NgramVerifyResult(
+            proposal=NgramResult(draft_tokens=torch.empty((B, K), dtype=torch.int32, device=dev),
+                                 draft_len=torch.empty((B,), dtype=torch.int32, device=dev),
+                                 match_n=torch.empty((B,), dtype=torch.int32, device=dev)),
+            verify=ChainResult(
+                tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                num_accepted=torch.empty((B,), dtype=torch.int32, device=dev),
+                probs=torch.empty((B, K, 3), dtype=torch.float32, device=dev) if want_probs else None,
+                packed=torch.empty((max(1, B * (K + 1)),), dtype=torch.int32, device=dev) if want_packed else None,
+                offsets=torch.empty((B + 1,), dtype=torch.int32, device=dev) if want_packed else None))
+    s = _stream(stream, dev)
+    need = int(lib().spec_verify_chain_workspace_size(B, K, V, code)) if B > 0 else 0
+    buf = workspace_buf if workspace_buf is not None else workspace(need, dev, s, "chain")
+    wp, wbytes = _aligned_ptr(buf)
+    p, v = out.proposal, out.verify
+    args = (_ptr(context), _ptr(context_len), L_max, n_min, n_max, _ptr(target_logits), code, _ptr(temperature),
+            _ptr(u_accept), _ptr(u_final), B, K, V, _ptr(p.draft_tokens), _ptr(p.draft_len), _ptr(p.match_n),
+            _ptr(v.tokens), _ptr(v.num_accepted), _ptr(v.probs), _ptr(v.packed), _ptr(v.offsets), wp, wbytes, s)
+    return args, out, (context, context_len, target_logits, temperature, u_accept, u_final, buf)
+
+
+def spec_ngram_verify(context: torch.Tensor, context_len: torch.Tensor, n_min: int, n_max: int,
+                      target_logits: torch.Tensor, temperature: torch.Tensor, u_accept: torch.Tensor,
+                      u_final: torch.Tensor, *, want_probs: bool = True, want_packed: bool = False,
+                      out: Optional[NgramVerifyResult] = None, workspace_buf: Optional[torch.Tensor] = None,
+                      stream=None) -> NgramVerifyResult:
+    """Prompt n-gram lookup and the verification of its drafts in one call (spec_ngram_verify).
+    context [B, L_max] int32, context_len [B] int32, target_logits [B, K+1, V], temperature [B],
+    u_accept [B, K], u_final [B]."""
+    args, out, _ = _ngram_verify_call(context, context_len, n_min, n_max, target_logits, temperature, u_accept,
+                                      u_final, want_probs, want_packed, out, workspace_buf, stream)
+    _check("spec_ngram_verify", lib().spec_ngram_verify(*args))
+    return out
+
+
+def prepare_spec_ngram_verify(context: torch.Tensor, context_len: torch.Tensor, n_min: int, n_max: int,
+                              target_logits: torch.Tensor, temperature: torch.Tensor, u_accept: torch.Tensor,
+                              u_final: torch.Tensor, *, want_probs: bool = True, want_packed: bool = False,
+                              out: Optional[NgramVerifyResult] = None, workspace_buf: Optional[torch.Tensor] = None,
+                              stream=None) -> PreparedCall:
+    """spec_ngram_verify with every argument fixed (see PreparedCall)."""
+    args, out, keep = _ngram_verify_call(context, context_len, n_min, n_max, target_logits, temperature, u_accept,
+                                         u_final, want_probs, want_packed, out, workspace_buf, stream)
+    return PreparedCall("spec_ngram_verify", lib().spec_ngram_verify, _SIGNATURES["spec_ngram_verify"][1], args,
+                        out, keep)
 
 
 def prepare_ngram_propose(context: torch.Tensor, context_len: torch.Tensor, n_min: int, n_max: int, K: int, *,

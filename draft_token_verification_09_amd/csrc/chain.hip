@@ -39,6 +39,7 @@
 
 #include "device_common.h"
 #include "host_runtime.h"
+#include "ngram_body.h"
 #include "spec_verify.h"
 
 namespace specv {
@@ -141,6 +142,7 @@ struct ChainArgs {
   RowStat* part;        // [B, R, C, 4] partials, one per wave of each chunk
   float* gath;          // [B, R] logit of the drafted token in each scoring row
   SlotDouble* wseg;     // [B, S] slots: mass of the final draw's weights per segment
+  int stats_copy;              // the stats pass copies the drafted tokens' logits out (else the lookup does)
   unsigned long long* stamps;  // phase timestamps (measurement only; see spec_chain_phase_stamps), or null
   size_t stamps_pool;          // index of the pool tasks' first stamp
 };
@@ -400,25 +402,25 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   __syncthreads();
 }
 
-// grid = B x R x C: each workgroup reduces one chunk g of one row (g in XCD-blocked order, see
-// xcd_blocked_index), each of its waves to one partial of its quarter of the chunk (one
-// contiguous span, see load_wave_span).
-template <int DT, int NV, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_fetch_add(a.runs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  stamp(a, 2 * static_cast<size_t>(blockIdx.x));
+// One chunk g (in (sequence, row, chunk) order) of one row, reduced by one workgroup: each of
+// its waves makes one partial of its quarter of the chunk (one contiguous span, see
+// load_wave_span).  ALL_ROWS: every target row is read and no drafted logit is copied out (the
+// draft lengths and tokens are being written by the same launch; see ngram_chain_stats_kernel).
+// si: this workgroup's stamp pair.
+template <int DT, int NV, bool VEC, bool ALL_ROWS>
+__device__ __forceinline__ void chain_stats_body(const ChainArgs& a, int g, size_t si) {
+  stamp(a, si);
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
   constexpr int kSpan = kChunk / kWaves;  // elements of one wave's quarter
-  const int g = xcd_blocked_index();
   const int c = g % a.C;
   const int rr = (g / a.C) % a.R;
   const int b = g / (a.C * a.R);
-  const int kb = clamped_len(a, b);
+  const int kb = ALL_ROWS ? a.K : clamped_len(a, b);
   const bool greedy = is_greedy(a, b);
   if (!row_needed(a, rr, kb, greedy)) {
-    stamp(a, 2 * static_cast<size_t>(blockIdx.x) + 1);
+    stamp(a, si + 1);
     return;
   }
   const void* row = rr <= a.K ? target_row<DT>(a, b, rr) : draft_row<DT>(a, b, rr - (a.K + 1));
@@ -453,11 +455,13 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
       }
     wave_argmax(v, idx);
     if ((threadIdx.x & 63) == 0) *out = RowStat{v, 0.f, static_cast<double>(idx)};
-    stamp(a, 2 * static_cast<size_t>(blockIdx.x) + 1);
+    stamp(a, si + 1);
     return;
   }
   const float scale = kLog2e / a.temperature[b];
-  const int pos = row_position(a, rr, kb);
+  // (a run-time test rather than ALL_ROWS: with the copy compiled out, the compiler schedules the
+  // pass with 74 instead of 63 VGPRs, 6 instead of 8 waves per SIMD)
+  const int pos = a.stats_copy ? row_position(a, rr, kb) : -1;
   const int x = pos >= 0 ? a.tokens[static_cast<size_t>(b) * a.K + pos] : -1;
 
   // The lane holding the drafted token's logit copies it out (bit-exact).
@@ -514,7 +518,47 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
   const double contrib = (o == -INFINITY) ? 0.0 : static_cast<double>(s) * static_cast<double>(exp2_fast(o - ow));
   const double sw = wave_sum(contrib);
   if ((threadIdx.x & 63) == 0) *out = RowStat{ow, 0.f, sw};
-  stamp(a, 2 * static_cast<size_t>(blockIdx.x) + 1);
+  stamp(a, si + 1);
+}
+
+// grid = B x R x C: workgroup i reduces chunk g = xcd_blocked(i, G) of one row.
+template <int DT, int NV, bool VEC>
+__global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_fetch_add(a.runs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  chain_stats_body<DT, NV, VEC, false>(a, xcd_blocked_index(), 2 * static_cast<size_t>(blockIdx.x));
+}
+
+// Where the prompt n-gram lookup drafts: the lookup of ngram_body.h and the row statistics of
+// every target row run in one launch.  grid = B + B x (K+1) x C: workgroup i < B proposes for
+// sequence i (draft tokens, lengths and matched n into the chain call's tokens, draft lengths
+// and `match_n`) and copies the drafted tokens' logits out of their target rows (a token that
+// is no vocabulary index is left for the decision to flag); the others reduce chunks as
+// chain_stats_kernel does, over all K+1 target rows, since the draft lengths are not known when
+// they start.
+struct NgramArgs {
+  const int32_t* context;
+  const int32_t* context_len;
+  int L_max, n_min, n_max;
+  int32_t* match_n;
+};
+
+template <int DT, int NV, bool VEC>
+__global__ __launch_bounds__(kThreads) void ngram_chain_stats_kernel(ChainArgs a, NgramArgs ng) {
+  const int i = static_cast<int>(blockIdx.x);
+  if (i < a.B) {
+    if (i == 0 && threadIdx.x == 0) __hip_atomic_fetch_add(a.runs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int32_t* tokens = const_cast<int32_t*>(a.tokens);
+    const int len = ngram_propose_body<kThreads>(i, ng.context, ng.context_len, ng.L_max, ng.n_min, ng.n_max, a.K,
+                                                 tokens, const_cast<int32_t*>(a.draft_len), ng.match_n);
+    // lane k wrote token k of the draft above and reads it back
+    for (int k = threadIdx.x; k < len; k += kThreads) {
+      const int x = tokens[static_cast<size_t>(i) * a.K + k];
+      if (x >= 0 && x < a.V) a.gath[static_cast<size_t>(i) * a.R + k] = Elem<DT>::value(target_row<DT>(a, i, k), x);
+    }
+    return;
+  }
+  const int G = static_cast<int>(gridDim.x) - a.B;
+  chain_stats_body<DT, NV, VEC, true>(a, xcd_blocked(i - a.B, G), 0);
 }
 
 // ---------------------------------------------------------------- final draw
@@ -975,21 +1019,21 @@ __device__ __forceinline__ void narrow_and_emit(const ChainArgs& a, int b, const
   }
 }
 
-// grid = Bs x CP pool tasks for the sequences b0 .. b0+Bs-1, CP = S/SPT per sequence:
+// grid = Bs x CP pool tasks for the sequences b0 .. b0+Bs-1 (CP per sequence, below):
 // task t = (sequence b, group c of SPT consecutive segments; a segment is one 16-byte vector
 // per lane, 256*E elements, and a row has S segment slots, the last ones past V weighing 0).
 //  1. Decides for b (identically in each of the sequence's tasks; the last task writes the
 //     count and probabilities).  A bonus or one-hot draw is finished by the sequence's
-//     first task alone (direct_select); after a rejection against draft rows each task
-//     loads its segments of the row pair and sums, for each segment, max(0, p - q) and p:
-//     per lane in fp32, across lanes in fp64.
+//     first task alone (direct_draw); after a rejection against draft rows each task loads
+//     its segments of the row pair and sums, for each segment, max(0, p - q): per lane in
+//     fp32, across lanes in fp64.
 //  2. Hands the segment masses over; the sequence's last task waits for those of its
 //     siblings.
 //  3. The last task scans the S segment masses in vocabulary order and takes the first
 //     segment whose inclusive prefix reaches u * W (W = the total), narrows it to a lane
 //     and an element and writes the emitted row (x_0 .. x_{n-1}, the drawn token, then
-//     -1).  If rounding leaves no residual mass (W = 0 after a rejection) the draw uses
-//     the masses of p instead.
+//     -1).  If rounding leaves no residual mass (W = 0 after a rejection) the last task
+//     draws from p (the target row) as a bonus draw does.
 // Only a sequence's last task waits, and only for tasks of the same launch that come before
 // it in dispatch order and never wait themselves, so every wait ends even when other
 // kernels share the device.  The host also keeps a launch to at most half as many sequences
@@ -1000,36 +1044,24 @@ __device__ __forceinline__ void narrow_and_emit(const ChainArgs& a, int b, const
 // wait, so that the task holding the drawn segment finishes with it still in cache, gave the
 // same pool time, 14.5 us per call.)
 //
-// Task order: with first_tasks_first (set by the host when there are no draft rows, so every
-// sampled draw is a bonus or one-hot draw finished by task 0) the launch's first Bs
-// workgroups are the sequences' first tasks and the rest follow sequence by sequence;
-// otherwise workgroups go sequence by sequence.  A waiting task (a last task) still comes
-// after every task it waits for.  (Measured, B=128, K=5, V=128256 bf16 without draft rows:
-// pool 18.0 -> 8.0 us, since the 2048 tasks do not all fit and the drawing tasks no longer
-// queue behind the others; with draft rows the order made no difference at B=64 and cost
-// 1 us at B=256, K=8, V=152064.)
+// Tasks per sequence: CP = S / SPT when draft rows are given, else 1 (without draft rows every
+// sampled draw is a bonus or one-hot draw from a target row's piece masses, which the first
+// task finishes alone).  Workgroups go sequence by sequence, so a waiting task (a last task)
+// comes after every task it waits for.
 //
 // Vocabulary order inside a chunk is segment-major (a segment = one 16-byte vector per
 // lane), then lane, then element.
 template <int DT, int SPT, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0, int first_tasks_first) {
+__global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b0, int CP) {
   constexpr int kRedBytes = 2 * SPT * kThreads * static_cast<int>(sizeof(float));
   __shared__ __align__(16) unsigned char s_buf[kRedBytes];
   __shared__ ChainDecision s_dec;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int CP = a.S / SPT;  // tasks per sequence
   const int gi = static_cast<int>(blockIdx.x);
-  const int Bs = static_cast<int>(gridDim.x) / CP;  // sequences of this launch
-  int b, c;  // sequence, and this task's group of SPT segments
-  if (!first_tasks_first || CP == 1) {
-    b = b0 + gi / CP;
-    c = gi % CP;
-  } else {
-    b = b0 + (gi < Bs ? gi : (gi - Bs) / (CP - 1));
-    c = gi < Bs ? 0 : 1 + (gi - Bs) % (CP - 1);
-  }
+  const int b = b0 + gi / CP;  // sequence
+  const int c = gi % CP;       // this task's group of SPT segments
   const bool last = c == CP - 1;
   float* red = reinterpret_cast<float*>(s_buf);  // [2][SPT][kThreads] per-lane masses
   const size_t sb = a.stamps_pool + kStampsPerTask * (static_cast<size_t>(b0) * CP + gi);
@@ -1172,12 +1204,14 @@ static uint32_t next_generation() {
 static std::atomic<unsigned long long*> g_stamps{nullptr};
 static std::atomic<size_t> g_stamp_words{0};
 
+// The stats pass (with the n-gram lookup in the same launch when `ng` is given), then the pool
+// kernel and, when asked for, the packed output.
 template <int DT, int NV, bool VEC>
-static spec_status_t launch_chain(ChainArgs a, hipStream_t stream) {
+static spec_status_t launch_chain(ChainArgs a, const NgramArgs* ng, hipStream_t stream) {
   a.stamps = nullptr;
-  if (unsigned long long* buf = g_stamps.load(std::memory_order_acquire)) {
+  if (unsigned long long* buf = ng ? nullptr : g_stamps.load(std::memory_order_acquire)) {
     const size_t g1 = static_cast<size_t>(a.B) * a.R * a.C;
-    const size_t need = 2 * g1 + kStampsPerTask * static_cast<size_t>(a.B) * (a.S / kPoolSegments);
+    const size_t need = 2 * g1 + kStampsPerTask * static_cast<size_t>(a.B) * (a.draft ? a.S / kPoolSegments : 1);
     if (need <= g_stamp_words.load(std::memory_order_acquire)) {
       a.stamps = buf;
       a.stamps_pool = 2 * g1;
@@ -1186,21 +1220,29 @@ static spec_status_t launch_chain(ChainArgs a, hipStream_t stream) {
   static std::atomic<int> slots_cache[kMaxDevices];
   {
     const long long g1 = static_cast<long long>(a.B) * a.R * a.C;
-    LaunchScope scope("chain_stats", stream);
-    scope.launch((chain_stats_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), stream, a);
-    const spec_status_t st = scope.finish();
-    if (st != SPEC_OK) return st;
+    if (ng) {
+      LaunchScope scope("ngram_chain_stats", stream);
+      scope.launch((ngram_chain_stats_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(a.B + g1)), dim3(kThreads),
+                   stream, a, *ng);
+      const spec_status_t st = scope.finish();
+      if (st != SPEC_OK) return st;
+    } else {
+      LaunchScope scope("chain_stats", stream);
+      scope.launch((chain_stats_kernel<DT, NV, VEC>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), stream, a);
+      const spec_status_t st = scope.finish();
+      if (st != SPEC_OK) return st;
+    }
   }
   {
     const auto kernel = chain_pool_kernel<DT, kPoolSegments, VEC>;
-    const int CP = a.S / kPoolSegments;
+    const int CP = a.draft ? a.S / kPoolSegments : 1;  // tasks per sequence
     // one waiting task per sequence: at most half as many sequences per launch as fit at once
     const int per_launch = max(1, pool_slots(reinterpret_cast<const void*>(kernel), slots_cache) / 2);
     for (int b0 = 0; b0 < a.B; b0 += per_launch) {
       const int bs = min(per_launch, a.B - b0);
       LaunchScope scope("chain_pool", stream);
       scope.launch(kernel, dim3(static_cast<unsigned>(static_cast<long long>(bs) * CP)), dim3(kThreads), stream, a, b0,
-                   a.draft == nullptr ? 1 : 0);
+                   CP);
       const spec_status_t st = scope.finish();
       if (st != SPEC_OK) return st;
     }
@@ -1212,17 +1254,17 @@ static spec_status_t launch_chain(ChainArgs a, hipStream_t stream) {
 }
 
 template <int DT>
-static spec_status_t dispatch_chain(int nv, bool vec, const ChainArgs& a, hipStream_t s) {
+static spec_status_t dispatch_chain(int nv, bool vec, const ChainArgs& a, const NgramArgs* ng, hipStream_t s) {
   switch (nv) {
     case 16:  // chosen only for bf16 rows with 16-byte loads
       if constexpr (DT == kBF16) {
-        if (vec) return launch_chain<DT, 16, true>(a, s);
+        if (vec) return launch_chain<DT, 16, true>(a, ng, s);
       }
       return fail(SPEC_ERR_UNSUPPORTED, "16-vector chunks need bf16 rows and 16-byte loads");
-    case 8: return vec ? launch_chain<DT, 8, true>(a, s) : launch_chain<DT, 8, false>(a, s);
-    case 4: return vec ? launch_chain<DT, 4, true>(a, s) : launch_chain<DT, 4, false>(a, s);
-    case 2: return vec ? launch_chain<DT, 2, true>(a, s) : launch_chain<DT, 2, false>(a, s);
-    default: return vec ? launch_chain<DT, 1, true>(a, s) : launch_chain<DT, 1, false>(a, s);
+    case 8: return vec ? launch_chain<DT, 8, true>(a, ng, s) : launch_chain<DT, 8, false>(a, ng, s);
+    case 4: return vec ? launch_chain<DT, 4, true>(a, ng, s) : launch_chain<DT, 4, false>(a, ng, s);
+    case 2: return vec ? launch_chain<DT, 2, true>(a, ng, s) : launch_chain<DT, 2, false>(a, ng, s);
+    default: return vec ? launch_chain<DT, 1, true>(a, ng, s) : launch_chain<DT, 1, false>(a, ng, s);
   }
 }
 
@@ -1276,13 +1318,18 @@ size_t spec_verify_chain_workspace_size(int B, int K, int V, spec_dtype_t dtype)
   return bytes;
 }
 
-spec_status_t spec_verify_chain(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
-                                const int32_t* draft_tokens, const int32_t* draft_len,
-                                const float* temperature, const float* u_accept, const float* u_final,
-                                int B, int K, int V,
-                                int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
-                                int32_t* out_packed, int32_t* out_offsets,
-                                void* workspace, size_t workspace_bytes, spec_stream_t stream) {
+}  // extern "C"
+
+// spec_verify_chain, and (with ng) the n-gram lookup's fused form: draft_tokens and draft_len
+// are then the lookup's outputs, written by the first launch.
+static spec_status_t verify_chain_impl(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                       const int32_t* draft_tokens, const int32_t* draft_len,
+                                       const float* temperature, const float* u_accept, const float* u_final,
+                                       int B, int K, int V,
+                                       int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                       int32_t* out_packed, int32_t* out_offsets,
+                                       void* workspace, size_t workspace_bytes, const NgramArgs* ng,
+                                       spec_stream_t stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (B < 0 || K < 1 || V < 1) return fail(SPEC_ERR_INVALID_ARG, "need B >= 0, K >= 1, V >= 1 (got %d, %d, %d)", B, K, V);
@@ -1338,13 +1385,46 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
   char* ws = static_cast<char*>(workspace);
   a.gen = next_generation();
   a.poll_limit = knob(SPEC_KNOB_POLL_LIMIT);
+  a.stats_copy = ng ? 0 : 1;
   a.runs = static_cast<uint32_t*>(workspace);
   a.gath = reinterpret_cast<float*>(ws + L.off_gath);
   a.part = reinterpret_cast<RowStat*>(ws + L.off_part);
   a.wseg = reinterpret_cast<SlotDouble*>(ws + L.off_wseg);
 
-  if (dtype == SPEC_BF16) return dispatch_chain<kBF16>(L.nv, vec, a, s);
-  return dispatch_chain<kF32>(L.nv, vec, a, s);
+  if (dtype == SPEC_BF16) return dispatch_chain<kBF16>(L.nv, vec, a, ng, s);
+  return dispatch_chain<kF32>(L.nv, vec, a, ng, s);
+}
+
+extern "C" {
+
+spec_status_t spec_verify_chain(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                const int32_t* draft_tokens, const int32_t* draft_len,
+                                const float* temperature, const float* u_accept, const float* u_final,
+                                int B, int K, int V,
+                                int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                int32_t* out_packed, int32_t* out_offsets,
+                                void* workspace, size_t workspace_bytes, spec_stream_t stream) {
+  return verify_chain_impl(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature, u_accept,
+                           u_final, B, K, V, out_tokens, out_num_accepted, out_probs, out_packed, out_offsets,
+                           workspace, workspace_bytes, nullptr, stream);
+}
+
+spec_status_t spec_ngram_verify(const int32_t* context, const int32_t* context_len, int L_max, int n_min, int n_max,
+                                const void* target_logits, spec_dtype_t dtype, const float* temperature,
+                                const float* u_accept, const float* u_final, int B, int K, int V,
+                                int32_t* out_draft_tokens, int32_t* out_draft_len, int32_t* out_match_n,
+                                int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                int32_t* out_packed, int32_t* out_offsets,
+                                void* workspace, size_t workspace_bytes, spec_stream_t stream) {
+  if (L_max < 1 || n_min < 1 || n_max < n_min)
+    return fail(SPEC_ERR_INVALID_ARG, "need L_max >= 1, 1 <= n_min <= n_max");
+  if (n_max > SPEC_MAX_NGRAM_N) return fail(SPEC_ERR_UNSUPPORTED, "n_max = %d exceeds SPEC_MAX_NGRAM_N", n_max);
+  if (B > 0 && (!context || !context_len || !out_draft_tokens || !out_draft_len))
+    return fail(SPEC_ERR_INVALID_ARG, "a required pointer is NULL");
+  const NgramArgs ng{context, context_len, L_max, n_min, n_max, out_match_n};
+  return verify_chain_impl(target_logits, nullptr, dtype, out_draft_tokens, out_draft_len, temperature, u_accept,
+                           u_final, B, K, V, out_tokens, out_num_accepted, out_probs, out_packed, out_offsets,
+                           workspace, workspace_bytes, &ng, stream);
 }
 
 spec_status_t spec_chain_phase_stamps(unsigned long long* buffer, size_t words) {

@@ -183,10 +183,14 @@ __device__ __forceinline__ void load_wave_span(u32x4 (&raw)[NV], const void* row
 // pass 74.9 -> 71.8 us at B=32, 61 rows, V=128256 bf16.)
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int xcd_blocked_index() {
-  const int G = static_cast<int>(gridDim.x);
-  const int i = static_cast<int>(blockIdx.x);
+// The same order for workgroup i of a range of G workgroups within a launch (where the range
+// starts at a multiple of 8, its workgroup i sits on XCD i % 8 as well).
+__device__ __forceinline__ int xcd_blocked(int i, int G) {
   return G % kXcds == 0 ? (i % kXcds) * (G / kXcds) + i / kXcds : i;
+}
+
+__device__ __forceinline__ int xcd_blocked_index() {
+  return xcd_blocked(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
 }
 
 // ---------------------------------------------------------------- wave64 scans and reductions

@@ -10,6 +10,7 @@
  *   spec_verify_tree_greedy  greedy acceptance of the longest matching tree path
  *   spec_verify_tree         stochastic (T > 0) tree verification against residuals
  *   ngram_propose            prompt n-gram lookup drafting (one-hot draft q)
+ *   spec_ngram_verify        the lookup and the verification of its drafts in one call
  *   spec_tree_mask           2-D tree-attention mask and node depths of a draft tree
  *   spec_commit_path         copy the accepted path's cache entries into the KV cache
  *
@@ -293,6 +294,37 @@ spec_status_t ngram_propose(const int32_t* context, const int32_t* context_len,
                             int B, int L_max, int n_min, int n_max, int K,
                             int32_t* out_draft_tokens, int32_t* out_draft_len, int32_t* out_match_n,
                             spec_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Prompt n-gram lookup drafting and its verification in one call.
+ *
+ * [Accelerating] (prompt lookup drafts K tokens with q one-hot) and [Production]
+ * section I.1 (the verification): the same results as ngram_propose followed by
+ * spec_verify_chain(draft_logits = NULL, draft_tokens = out_draft_tokens,
+ * draft_len = out_draft_len) on the same inputs, bit for bit, in one call whose
+ * first kernel runs the lookup and the row statistics of all K+1 target rows of
+ * every sequence side by side (every target row is read, also past a sequence's
+ * draft length, since the lengths are not known until the lookup ends).
+ *
+ * context, context_len, L_max, n_min, n_max, out_draft_tokens, out_draft_len,
+ * out_match_n: as for ngram_propose (K drafted tokens at most).
+ * target_logits, dtype, temperature, u_accept, u_final, B, K, V, out_tokens,
+ * out_num_accepted, out_probs, out_packed, out_offsets, workspace: as for
+ * spec_verify_chain with draft_logits = NULL; the workspace is
+ * spec_verify_chain_workspace_size(B, K, V, dtype) bytes.
+ *
+ * A sequence whose context length is invalid proposes nothing (draft length 0,
+ * match_n -1) and is verified like any other with no draft: a token drawn from
+ * p_0.  A proposed token outside [0, V) flags the sequence as spec_verify_chain does.
+ * Limits: those of both calls.
+ * ------------------------------------------------------------------------- */
+spec_status_t spec_ngram_verify(const int32_t* context, const int32_t* context_len, int L_max, int n_min, int n_max,
+                                const void* target_logits, spec_dtype_t dtype, const float* temperature,
+                                const float* u_accept, const float* u_final, int B, int K, int V,
+                                int32_t* out_draft_tokens, int32_t* out_draft_len, int32_t* out_match_n,
+                                int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                int32_t* out_packed, int32_t* out_offsets,
+                                void* workspace, size_t workspace_bytes, spec_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Tree-attention mask.
