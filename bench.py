@@ -573,12 +573,15 @@ MODE_NAMES = {1: "residual", 2: "bonus", 3: "one-hot", 4: "fallback-p", 5: "gree
 def chain_phases(make, name, warmup, calls, dev, chunk_vectors, pool_segments):
     """Per-phase timeline of chain calls from the library's phase timestamps (device clock,
     100 MHz): for each of `calls` calls (after `warmup`), the stats pass's span and the pool
-    kernel's phases, relative to the first stats workgroup's start.  Returns a text summary."""
+    kernel's phases, relative to the first stats workgroup's start.  The calls run as separate
+    launches (whose stamp layout this reads).  Returns a text summary."""
     import numpy as np
     import torch
 
     import draft_token_verification_09_amd as sv
 
+    single = sv.spec_get_knob(sv.SPEC_KNOB_SINGLE_LAUNCH)
+    sv.spec_set_knob(sv.SPEC_KNOB_SINGLE_LAUNCH, 1)
     probe = make(0)
     per_set = chain_bytes(probe)
     n_sets = sets_needed(per_set)
@@ -639,6 +642,7 @@ def chain_phases(make, name, warmup, calls, dev, chunk_vectors, pool_segments):
             r["direct_select"] = np.median(pool[first, 2] - pool[first, 1]) * us
             r["direct_narrow"] = np.median(pool[first, 4] - pool[first, 2]) * us
         rows.append(r)
+    sv.spec_set_knob(sv.SPEC_KNOB_SINGLE_LAUNCH, single)
     del prepared, sets
     torch.cuda.empty_cache()
     keys = ["stats_end", "pool_start", "decide", "published", "wait", "wait_after_last_published", "narrow",

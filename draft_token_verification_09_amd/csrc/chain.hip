@@ -97,6 +97,7 @@ struct ChainDecision {
   float Ot, Od;  // row offsets (target, draft)
   float invSt, invSd;
   float p_excl;  // one-hot mode: p_n(x_n)
+  float uf;      // the final draw's uniform
   double St, Sd;
 };
 
@@ -114,6 +115,7 @@ __device__ __forceinline__ ChainDecision uniform_decision(const ChainDecision& s
   d.invSt = uniform(s.invSt);
   d.invSd = uniform(s.invSd);
   d.p_excl = uniform(s.p_excl);
+  d.uf = uniform(s.uf);
   d.St = uniform(s.St);
   d.Sd = uniform(s.Sd);
   return d;
@@ -143,6 +145,12 @@ struct ChainArgs {
   float* gath;          // [B, R] logit of the drafted token in each scoring row
   SlotDouble* wseg;     // [B, S] slots: mass of the final draw's weights per segment
   int stats_copy;              // the stats pass copies the drafted tokens' logits out (else the lookup does)
+  // single-launch path (see chain_single_kernel): hand-over words tagged with seq_tag
+  uint32_t* epoch;             // [B] per-sequence run counters
+  uint64_t* tpart;             // [B, kSingleMaxParts, 3] partials ([R, C, kWaves]): o, then s as a tagged double
+  uint64_t* tprop;             // [B, 2K+1] lookup results: draft length, tokens [K], their logits [K]
+  uint64_t* status;            // [B, kSingleMaxParts / kWaves] one word per workgroup (see SeqStatus)
+  SlotDouble* tmass;           // [B, K, S] slots: residual mass of each segment, should position k reject
   unsigned long long* stamps;  // phase timestamps (measurement only; see spec_chain_phase_stamps), or null
   size_t stamps_pool;          // index of the pool tasks' first stamp
 };
@@ -153,6 +161,9 @@ struct ChainArgs {
 // the phases of kPoolPhase, the last word holding (b << 32) | (c << 8) | mode.
 constexpr int kStampsPerTask = 6;
 enum PoolPhase : int { kPhStart = 0, kPhDecided = 1, kPhPublished = 2, kPhGathered = 3, kPhEnd = 4, kPhInfo = 5 };
+// Phases of a single-launch workgroup (stamps[kStampsPerTask * w + i] for workgroup w of the
+// sequences' workgroups, in grid order after the lookup's).
+enum SinglePhase : int { kSgStart = 0, kSgPublished = 1, kSgGathered = 2, kSgDecided = 3, kSgDrawn = 4, kSgEnd = 5 };
 
 __device__ __forceinline__ void stamp(const ChainArgs& a, size_t i) {
   if (a.stamps && threadIdx.x == 0) a.stamps[i] = __builtin_amdgcn_s_memrealtime();
@@ -162,6 +173,19 @@ __device__ __forceinline__ void stamp(const ChainArgs& a, size_t i) {
 // mixed with the workspace counter as the stats kernel of this call left it.
 __device__ __forceinline__ uint32_t pool_generation(const ChainArgs& a) {
   const uint32_t g = a.gen ^ (load_agent(a.runs) * 0x9e3779b1u);
+  return g != 0u ? g : 0x2545f491u;
+}
+
+// Tag of sequence b's hand-over words on the single-launch path: the host's number for the call
+// mixed with the sequence's run counter, which its last pool task advances once every
+// workgroup of the sequence has read it (so that a captured graph replaying the same launch
+// arguments still gets new tags; kernels of a stream run one after another, so no word of a
+// run is written during the next), and with the address of the launch's dispatch packet in
+// the queue: after a wait gave up, workgroups of the run that start late may read the advanced
+// counter, and the packet address keeps their words apart from those of the next launch.
+__device__ __forceinline__ uint32_t seq_tag(const ChainArgs& a, int b) {
+  const uint64_t packet = reinterpret_cast<uint64_t>(__builtin_amdgcn_dispatch_ptr()) >> 6;  // 64-byte packets
+  const uint32_t g = a.gen ^ (static_cast<uint32_t>(packet) * 0x85ebca6bu) ^ (load_agent(a.epoch + b) * 0x9e3779b1u);
   return g != 0u ? g : 0x2545f491u;
 }
 
@@ -203,14 +227,46 @@ __device__ __forceinline__ int row_position(const ChainArgs& a, int rr, int kb) 
 // ---------------------------------------------------------------- decision
 
 
+// A sequence's inputs to the decision: its chunk partials ([R][C * kWaves]), drafted tokens
+// ([K]), copied logits of the drafted tokens ([R], target row k at k, draft row k at K+1+k),
+// accept-test uniforms ([K]), temperature, final uniform and raw draft length -- in the
+// workspace and the caller's arrays, or staged in shared memory by a workgroup of the
+// single-launch path.
+struct SeqInputs {
+  const RowStat* part;
+  const int32_t* tokens;
+  const float* gath;
+  const float* u_accept;
+  float T, uf;
+  int kb_raw;
+};
+
+__device__ __forceinline__ SeqInputs seq_inputs(const ChainArgs& a, int b) {
+  return SeqInputs{a.part + static_cast<size_t>(b) * a.R * a.C * kWaves,
+                   a.tokens + static_cast<size_t>(b) * a.K,
+                   a.gath + static_cast<size_t>(b) * a.R,
+                   a.u_accept + static_cast<size_t>(b) * a.K,
+                   a.temperature[b],
+                   a.u_final[b],
+                   a.draft_len ? a.draft_len[b] : a.K};
+}
+
+// No work between the decision's combining of the partials and the decision itself.
+struct NoMidStep {
+  __device__ void operator()(const float*, const double*) const {}
+};
+
 // Called by every lane of every pool task of sequence b: combines the sequence's chunk
 // partials, decides and leaves the decision in *out (shared memory) -- identically in
 // every task: same data, same arithmetic, same order.  With write_outputs it also writes
 // the count and the probabilities (and a -1 row for invalid input).  The loads of a batch
-// of rows are all issued before any is used.
-template <int DT>
-__device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, bool write_outputs,
-                                             ChainDecision* out) {
+// of rows are all issued before any is used.  kb = the draft length clamped to [0, K].
+// mid(sO, sS), called by every lane once the rows' offsets and sums are in shared memory
+// (sampled sequences: sO[r], sS[r] of row r as indexed by the partials), may use them before
+// the decision is taken.
+template <int DT, class Mid = NoMidStep>
+__device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, const SeqInputs& in,
+                                             bool write_outputs, ChainDecision* out, Mid mid = Mid()) {
   __shared__ float sO[2 * SPEC_MAX_K + 1];
   __shared__ double sS[2 * SPEC_MAX_K + 1];
   const int tid = threadIdx.x;
@@ -224,15 +280,14 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   int x = 0;
   float u = 1.f, gt = 0.f, gd = 0.f;
   if (active) {
-    x = a.tokens[static_cast<size_t>(b) * a.K + k];
-    u = a.u_accept[static_cast<size_t>(b) * a.K + k];
-    const float* g = a.gath + static_cast<size_t>(b) * R;
-    gt = g[k];
-    if (a.draft) gd = g[a.K + 1 + k];
+    x = in.tokens[k];
+    u = in.u_accept[k];
+    gt = in.gath[k];
+    if (a.draft) gd = in.gath[a.K + 1 + k];
   }
-  const float T = a.temperature[b];
-  const float uf = a.u_final[b];
-  const int kb_raw = a.draft_len ? a.draft_len[b] : a.K;
+  const float T = in.T;
+  const float uf = in.uf;
+  const int kb_raw = in.kb_raw;
   const bool greedy = T == 0.f;
 
   // Per-row (O, S) from the partials -- for a greedy sequence the row argmax instead:
@@ -248,7 +303,7 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   for (int r0 = 0; r0 < R; r0 += kThreads / 16) {
     const int rr = r0 + grp;
     const bool live = rr < R && row_needed(a, rr, kb, greedy);
-    const RowStat* ps = a.part + (static_cast<size_t>(b) * R + (live ? rr : 0)) * C;
+    const RowStat* ps = in.part + static_cast<size_t>(live ? rr : 0) * C;
     RowStat st[kRegPer];
 #pragma unroll
     for (int j = 0; j < kRegPer; ++j) {
@@ -297,6 +352,7 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
     }
   }
   __syncthreads();
+  mid(sO, sS);
 
   if (w == 0 && greedy) {
     // One lane per drafted position: accepted iff the draft is its target row's argmax;
@@ -373,6 +429,7 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
       d.n = n;
       d.kb = kb;
       d.scale = scale;
+      d.uf = uf;
       d.excl_tok = -1;
       if (invalid) {
         d.mode = kModeInvalid;
@@ -402,81 +459,49 @@ __device__ __forceinline__ void chain_decide(const ChainArgs& a, int b, int kb, 
   __syncthreads();
 }
 
-// One chunk g (in (sequence, row, chunk) order) of one row, reduced by one workgroup: each of
-// its waves makes one partial of its quarter of the chunk (one contiguous span, see
-// load_wave_span).  ALL_ROWS: every target row is read and no drafted logit is copied out (the
-// draft lengths and tokens are being written by the same launch; see ngram_chain_stats_kernel).
-// si: this workgroup's stamp pair.
-template <int DT, int NV, bool VEC, bool ALL_ROWS>
-__device__ __forceinline__ void chain_stats_body(const ChainArgs& a, int g, size_t si) {
-  stamp(a, si);
+// A wave's (largest logit, smallest index) over its share of chunk c (raw as load_wave_span
+// leaves it).  The lane visits its elements in increasing vocabulary order, so a strict '>'
+// keeps the first maximum; elements past V read as -inf and never replace the lane's first one.
+template <int DT, int NV, bool VEC>
+__device__ __forceinline__ void wave_argmax_partial(u32x4 (&raw)[NV], int c, int V, float* v_out, int* idx_out) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
   constexpr int kSpan = kChunk / kWaves;  // elements of one wave's quarter
-  const int c = g % a.C;
-  const int rr = (g / a.C) % a.R;
-  const int b = g / (a.C * a.R);
-  const int kb = ALL_ROWS ? a.K : clamped_len(a, b);
-  const bool greedy = is_greedy(a, b);
-  if (!row_needed(a, rr, kb, greedy)) {
-    stamp(a, si + 1);
-    return;
-  }
-  const void* row = rr <= a.K ? target_row<DT>(a, b, rr) : draft_row<DT>(a, b, rr - (a.K + 1));
-  RowStat* out = a.part + ((static_cast<size_t>(b) * a.R + rr) * a.C + c) * kWaves + (threadIdx.x >> 6);
-
-  u32x4 raw[NV];
-  load_wave_span<DT, NV, VEC, true>(raw, row, a.V, c);
   const int wv = static_cast<int>(threadIdx.x >> 6);
   const int ln = static_cast<int>(threadIdx.x & 63);
-
-  if (greedy) {  // (largest logit, smallest index) of the wave's share
-    // The lane visits its elements in increasing vocabulary order, so a strict '>' keeps the
-    // first maximum; elements past V read as -inf and never replace the lane's first one.
-    const int first = c * kChunk + wv * kSpan + ln * E;
-    float v = -INFINITY;
-    int idx = first < a.V ? first : INT_MAX;
-    // With vector loads, the packed registers count as rewritten here, so that no unpacked
-    // element is shared with (and kept alive for) the sampling path below.
-    if constexpr (VEC) {
+  const int first = c * kChunk + wv * kSpan + ln * E;
+  float v = -INFINITY;
+  int idx = first < V ? first : INT_MAX;
+  // With vector loads, the packed registers count as rewritten here, so that no unpacked
+  // element is shared with (and kept alive for) the sampling path.
+  if constexpr (VEC) {
 #pragma unroll
-      for (int j = 0; j < NV; ++j) asm volatile("" : "+v"(raw[j]));
-    }
+    for (int j = 0; j < NV; ++j) asm volatile("" : "+v"(raw[j]));
+  }
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
+  for (int j = 0; j < NV; ++j)
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const float l = EL::get(raw[j], i);
-        if (l > v) {
-          v = l;
-          idx = c * kChunk + wv * kSpan + (j * 64 + ln) * E + i;
-        }
+    for (int i = 0; i < E; ++i) {
+      const float l = EL::get(raw[j], i);
+      if (l > v) {
+        v = l;
+        idx = c * kChunk + wv * kSpan + (j * 64 + ln) * E + i;
       }
-    wave_argmax(v, idx);
-    if ((threadIdx.x & 63) == 0) *out = RowStat{v, 0.f, static_cast<double>(idx)};
-    stamp(a, si + 1);
-    return;
-  }
-  const float scale = kLog2e / a.temperature[b];
-  // (a run-time test rather than ALL_ROWS: with the copy compiled out, the compiler schedules the
-  // pass with 74 instead of 63 VGPRs, 6 instead of 8 waves per SIMD)
-  const int pos = a.stats_copy ? row_position(a, rr, kb) : -1;
-  const int x = pos >= 0 ? a.tokens[static_cast<size_t>(b) * a.K + pos] : -1;
-
-  // The lane holding the drafted token's logit copies it out (bit-exact).
-  if (x >= 0 && x < a.V && x / kChunk == c) {
-    const int local = x - c * kChunk;
-    if (wv == local / kSpan && ln == (local / E) % 64) {
-      const int j = (local % kSpan) / (64 * E);
-      u32x4 v = raw[0];
-#pragma unroll
-      for (int jj = 1; jj < NV; ++jj)
-        if (jj == j) v = raw[jj];
-      a.gath[static_cast<size_t>(b) * a.R + rr] = EL::get(v, local % E);
     }
-  }
+  wave_argmax(v, idx);
+  *v_out = v;
+  *idx_out = idx;
+}
 
+// A wave's softmax partial of its share of a chunk: o = its largest logit times `scale`
+// (log2(e) / T, so that o is in the exp2 domain) and s = the sum of exp2(l * scale - o) over
+// its elements, in fp64 across lanes; (-inf, 0) when every element is -inf.
+template <int DT, int NV>
+__device__ __forceinline__ void wave_softmax_partial(const u32x4 (&raw)[NV], float scale, float* o_out,
+                                                     double* s_out) {
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
   // The lane's vectors in parts of at most 4 (two parts for 8 vectors), each with its own
   // offset: a part's sums run while the later parts' loads are still in flight, and the
   // parts combine at the end (measured: 2-4 % less kernel time than one offset for all).
@@ -513,11 +538,73 @@ __device__ __forceinline__ void chain_stats_body(const ChainArgs& a, int g, size
     for (int q = 0; q < kParts; ++q)
       if (po[q] != -INFINITY) s += ps[q] * exp2_fast(po[q] - o);
   }
-  // One partial per wave: no workgroup barrier in this kernel.
   const float ow = wave_max(o);
   const double contrib = (o == -INFINITY) ? 0.0 : static_cast<double>(s) * static_cast<double>(exp2_fast(o - ow));
-  const double sw = wave_sum(contrib);
-  if ((threadIdx.x & 63) == 0) *out = RowStat{ow, 0.f, sw};
+  *o_out = ow;
+  *s_out = wave_sum(contrib);
+}
+
+// One chunk g (in (sequence, row, chunk) order) of one row, reduced by one workgroup: each of
+// its waves makes one partial of its quarter of the chunk (one contiguous span, see
+// load_wave_span).  ALL_ROWS: every target row is read and no drafted logit is copied out (the
+// draft lengths and tokens are being written by the same launch; see ngram_chain_stats_kernel).
+// si: this workgroup's stamp pair.
+template <int DT, int NV, bool VEC, bool ALL_ROWS>
+__device__ __forceinline__ void chain_stats_body(const ChainArgs& a, int g, size_t si) {
+  stamp(a, si);
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  constexpr int kChunk = ChunkShape<DT, NV>::kChunk;
+  constexpr int kSpan = kChunk / kWaves;  // elements of one wave's quarter
+  const int c = g % a.C;
+  const int rr = (g / a.C) % a.R;
+  const int b = g / (a.C * a.R);
+  const int kb = ALL_ROWS ? a.K : clamped_len(a, b);
+  const bool greedy = is_greedy(a, b);
+  if (!row_needed(a, rr, kb, greedy)) {
+    stamp(a, si + 1);
+    return;
+  }
+  const void* row = rr <= a.K ? target_row<DT>(a, b, rr) : draft_row<DT>(a, b, rr - (a.K + 1));
+  RowStat* out = a.part + ((static_cast<size_t>(b) * a.R + rr) * a.C + c) * kWaves + (threadIdx.x >> 6);
+
+  u32x4 raw[NV];
+  load_wave_span<DT, NV, VEC, true>(raw, row, a.V, c);
+  const int wv = static_cast<int>(threadIdx.x >> 6);
+  const int ln = static_cast<int>(threadIdx.x & 63);
+
+  if (greedy) {  // (largest logit, smallest index) of the wave's share
+    float v;
+    int idx;
+    wave_argmax_partial<DT, NV, VEC>(raw, c, a.V, &v, &idx);
+    if (ln == 0) *out = RowStat{v, 0.f, static_cast<double>(idx)};
+    stamp(a, si + 1);
+    return;
+  }
+  const float scale = kLog2e / a.temperature[b];
+  // (a run-time test rather than ALL_ROWS: with the copy compiled out, the compiler schedules the
+  // pass with 74 instead of 63 VGPRs, 6 instead of 8 waves per SIMD)
+  const int pos = a.stats_copy ? row_position(a, rr, kb) : -1;
+  const int x = pos >= 0 ? a.tokens[static_cast<size_t>(b) * a.K + pos] : -1;
+
+  // The lane holding the drafted token's logit copies it out (bit-exact).
+  if (x >= 0 && x < a.V && x / kChunk == c) {
+    const int local = x - c * kChunk;
+    if (wv == local / kSpan && ln == (local / E) % 64) {
+      const int j = (local % kSpan) / (64 * E);
+      u32x4 v = raw[0];
+#pragma unroll
+      for (int jj = 1; jj < NV; ++jj)
+        if (jj == j) v = raw[jj];
+      a.gath[static_cast<size_t>(b) * a.R + rr] = EL::get(v, local % E);
+    }
+  }
+
+  float ow;
+  double sw;
+  wave_softmax_partial<DT, NV>(raw, scale, &ow, &sw);
+  // One partial per wave: no workgroup barrier in this kernel.
+  if (ln == 0) *out = RowStat{ow, 0.f, sw};
   stamp(a, si + 1);
 }
 
@@ -600,54 +687,67 @@ __device__ __forceinline__ void chain_pack(const ChainArgs& a) {
 }
 
 // Bonus and one-hot draws (and the fallback to p) sample target row d.row itself, minus the
-// drafted token after a one-hot rejection, and write the emitted row; called by every lane
-// of one task.  The stats pass already summed that row in pieces: each wave partial (o, s)
-// covers one contiguous quarter of a chunk, with mass s * exp2(o - O) / S (the same terms
-// whose total is the row's S).  So the draw needs no pass over the whole row:
-//  1. wave 0 alone takes the units (pieces, or whole segments where a piece is smaller than
-//     a segment), 64 per round, forms their masses from the partials, and scans them in
-//     vocabulary order for the unit whose inclusive prefix reaches u * W (W = the total);
-//  2. wave q reads segment q of that unit (lane l: the segment's vectors l, l + 64, l + 128,
-//     l + 192, so that each load is 1 KiB of contiguous memory), sums each vector's draw
-//     weights in fp32 and scans the sums in vocabulary order in fp64, one round of 64
-//     vectors at a time; the final prefix is the segment's mass;
-//  3. every lane picks the segment from the masses, and the wave holding it narrows from its
-//     registers to the vector, then the element, and writes the row.
+// drafted token after a one-hot rejection, and write the emitted row.  The stats pass already
+// summed that row in pieces: each wave partial (o, s) covers one contiguous quarter of a chunk,
+// with mass s * exp2(o - O) / S (the same terms whose total is the row's S).  So the draw
+// needs no pass over the whole row:
+//  1. (direct_locate) wave 0 alone takes the units (pieces, or whole segments where a piece is
+//     smaller than a segment), 64 per round, forms their masses from the partials, and scans
+//     them in vocabulary order for the unit whose inclusive prefix reaches u * W (W = the
+//     total);
+//  2. (wave_segment_scan) each segment of that unit is held by one wave, lane l holding the
+//     segment's vectors l, l + 64, l + 128, l + 192 (each load 1 KiB of contiguous memory):
+//     the wave sums each vector's draw weights in fp32 and scans the sums in vocabulary order
+//     in fp64, one round of 64 vectors at a time; the final prefix is the segment's mass;
+//  3. (pick_segment, wave_segment_pick) the segment is picked from those masses, and the wave
+//     holding it narrows from its registers to the vector, then the element.
 // Unit masses come from the stats partials and segment masses from the draw weights, so the
 // two agree to rounding; where u * W lies within that rounding of a boundary the last
 // segment (or element) with mass is taken, as for every other draw.  With no mass left
 // after removing the drafted token (all of the row on it), the draw falls back to p.
-template <int DT, bool VEC>
-__device__ __forceinline__ void direct_draw(const ChainArgs& a, int b, const ChainDecision& d, int mode,
-                                            const void* row, size_t sb) {
+
+// Units of a direct draw on rows split into chunks of nv vectors a lane.
+struct DirectUnits {
+  int piece;  // elements of one wave partial
+  int pper;   // pieces per unit
+  int segs;   // segments per unit
+  int unit;   // elements per unit
+  int units;  // units in a row
+};
+
+template <int DT>
+__device__ __forceinline__ DirectUnits direct_units(int nv, int V) {
+  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
+  DirectUnits u;
+  u.piece = nv * (kSeg / kWaves);
+  u.pper = nv >= kWaves ? 1 : kWaves / nv;
+  u.segs = nv >= kWaves ? nv / kWaves : 1;
+  u.unit = u.pper * u.piece;
+  u.units = (V + u.unit - 1) / u.unit;  // <= S <= 4 * kThreads
+  return u;
+}
+
+// Step 1, every lane calls it: wave 0 finds the unit holding u * W from the partials of row
+// d.row (ps, C * kWaves of them) and the result is shared through shared memory.  *mode_io may
+// turn from one-hot into the fallback to p.
+template <int DT>
+__device__ __forceinline__ void direct_locate(const ChainArgs& a, int b, const ChainDecision& d, int* mode_io,
+                                              const RowStat* ps, int* usel_out, double* tunit_out) {
   __shared__ int s_unit, s_mode;
   __shared__ double s_tu;
-  __shared__ double s_segm[kWaves];
-  using EL = Elem<DT>;
-  constexpr int E = EL::kPerVec;
-  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
-  constexpr int kVPL = kThreads / 64;  // vectors of a segment per lane of a wave
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int piece = a.nv * (kSeg / kWaves);             // elements of one wave partial
-  const int pper = a.nv >= kWaves ? 1 : kWaves / a.nv;  // pieces per unit
-  const int segs = a.nv >= kWaves ? a.nv / kWaves : 1;  // segments per unit
-  const int unit = pper * piece;
-  const int units = (a.V + unit - 1) / unit;            // <= S <= 4 * kThreads
+  const int lane = threadIdx.x & 63;
+  const DirectUnits U = direct_units<DT>(a.nv, a.V);
   const int nparts = a.C * kWaves;
-  const RowStat* ps = a.part + (static_cast<size_t>(b) * a.R + d.row) * nparts;
-
-  // ---- 1. wave 0: the unit holding u * W
-  if (w == 0) {
-    const int rounds = (units + 63) / 64;
+  int mode = *mode_io;
+  if ((threadIdx.x >> 6) == 0) {
+    const int rounds = (U.units + 63) / 64;
     for (int attempt = 0; attempt < 2; ++attempt) {
-      const int excl_unit = mode == kModeOneHot ? d.excl_tok / unit : -1;
+      const int excl_unit = mode == kModeOneHot ? d.excl_tok / U.unit : -1;
       auto mass = [&](int u) -> double {  // unit u's mass in units of p
         double m = 0.0;
-        if (u < units) {
-          for (int k = 0; k < pper && u * pper + k < nparts; ++k) {
-            const RowStat st = ps[u * pper + k];
+        if (u < U.units) {
+          for (int k = 0; k < U.pper && u * U.pper + k < nparts; ++k) {
+            const RowStat st = ps[u * U.pper + k];
             if (st.o != -INFINITY) m += st.s * static_cast<double>(exp2_fast(st.o - d.Ot));
           }
           m /= d.St;
@@ -662,7 +762,7 @@ __device__ __forceinline__ void direct_draw(const ChainArgs& a, int b, const Cha
         mode = kModeFallbackP;
         continue;
       }
-      const double tt = static_cast<double>(a.u_final[b]) * W;
+      const double tt = static_cast<double>(d.uf) * W;
       int usel = -1, lastu = -1;
       double before = 0.0, last_before = 0.0;
       carry = 0.0;
@@ -696,59 +796,72 @@ __device__ __forceinline__ void direct_draw(const ChainArgs& a, int b, const Cha
     }
   }
   __syncthreads();
-  stamp(a, sb + kPhPublished);
-  const int usel = s_unit;
-  const double t_unit = s_tu;
-  mode = s_mode;
-  const int excl = mode == kModeOneHot ? d.excl_tok : -1;
+  *usel_out = s_unit;
+  *tunit_out = s_tu;
+  *mode_io = s_mode;
+}
 
-  // ---- 2. wave q: segment q of the unit, scanned in vocabulary order
-  const int seg = usel * segs + w;  // this wave's segment
-  const int e0 = seg * kSeg + lane * E;
-  u32x4 v[kVPL];
-  float vs[kVPL];
-  double incl[kVPL];
+// Step 2 for one segment held by the calling wave (v[j], lane l: the segment's vector
+// l + 64 j; e0 = the segment's first element + l * E): per-vector fp32 sums of the draw
+// weights (vs) and their inclusive fp64 prefixes in vocabulary order (incl); returns the
+// segment's mass.
+template <int DT>
+__device__ __forceinline__ double wave_segment_scan(const ChainDecision& d, const u32x4 (&v)[kThreads / 64], int e0,
+                                                    int excl, float (&vs)[kThreads / 64],
+                                                    double (&incl)[kThreads / 64]) {
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
   double carry = 0.0;
-  if (w < segs) {
 #pragma unroll
-    for (int j = 0; j < kVPL; ++j) v[j] = load_vector<DT, VEC>(row, a.V, e0 + j * 64 * E);
+  for (int j = 0; j < kThreads / 64; ++j) {
+    float sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < kVPL; ++j) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) s += draw_weight(false, d, EL::get(v[j], i), 0.f, e0 + j * 64 * E + i, excl);
-      vs[j] = s;
-      incl[j] = wave_inclusive_scan(static_cast<double>(s)) + carry;
-      carry = lane_broadcast(incl[j], 63);
-    }
-    if (lane == 0) s_segm[w] = carry;
+    for (int i = 0; i < E; ++i) sum += draw_weight(false, d, EL::get(v[j], i), 0.f, e0 + j * 64 * E + i, excl);
+    vs[j] = sum;
+    incl[j] = wave_inclusive_scan(static_cast<double>(sum)) + carry;
+    carry = lane_broadcast(incl[j], 63);
   }
-  __syncthreads();
+  return carry;
+}
 
-  // ---- 3. the segment (the same choice in every lane), then the wave holding it narrows
+// Step 3's choice of segment among a unit's `segs` segment masses m[0..segs) (t_unit: u * W
+// minus the mass before the unit): the first whose prefix reaches t_unit, else (rounding) the
+// last with mass, else the first.  *qbase: the mass before it.
+template <class Masses>
+__device__ __forceinline__ int pick_segment(const Masses& m, int segs, double t_unit, double* qbase) {
   int q = -1, lastq = -1;
-  double qbase = 0.0, lastbase = 0.0;
-  {
-    double run = 0.0;
-    for (int k = 0; k < segs; ++k) {
-      const double sm = s_segm[k];
-      if (sm > 0.0) {
-        lastq = k;
-        lastbase = run;
-        if (q < 0 && run + sm >= t_unit) {
-          q = k;
-          qbase = run;
-        }
+  double base = 0.0, lastbase = 0.0, run = 0.0;
+  for (int k = 0; k < segs; ++k) {
+    const double sm = m(k);
+    if (sm > 0.0) {
+      lastq = k;
+      lastbase = run;
+      if (q < 0 && run + sm >= t_unit) {
+        q = k;
+        base = run;
       }
-      run += sm;
     }
-    if (q < 0) {  // rounding, as above: the unit's last segment with mass (its first if none)
-      q = lastq >= 0 ? lastq : 0;
-      qbase = lastq >= 0 ? lastbase : 0.0;
-    }
+    run += sm;
   }
-  if (w != q) return;
-  const double t_seg = t_unit - qbase;
+  if (q < 0) {
+    q = lastq >= 0 ? lastq : 0;
+    base = lastq >= 0 ? lastbase : 0.0;
+  }
+  *qbase = base;
+  return q;
+}
+
+// Step 3's narrowing by the wave holding the segment (its scan from wave_segment_scan; t_seg:
+// u * W minus the mass before the segment); returns the drawn element in every lane.
+template <int DT>
+__device__ __forceinline__ int wave_segment_pick(const ChainDecision& d, const u32x4 (&v)[kThreads / 64], int e0,
+                                                 int excl, const float (&vs)[kThreads / 64],
+                                                 const double (&incl)[kThreads / 64], double t_seg, int seg) {
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
+  constexpr int kVPL = kThreads / 64;
+  const int lane = threadIdx.x & 63;
   int jsel = -1, lsel = -1;
 #pragma unroll
   for (int j = 0; j < kVPL; ++j) {
@@ -758,7 +871,6 @@ __device__ __forceinline__ void direct_draw(const ChainArgs& a, int b, const Cha
       lsel = __ffsll(static_cast<long long>(hit)) - 1;
     }
   }
-  int y;
   if (jsel < 0) {  // rounding left t_seg above the segment's total: its last positive weight
     int last_pos = -1;
 #pragma unroll
@@ -767,52 +879,96 @@ __device__ __forceinline__ void direct_draw(const ChainArgs& a, int b, const Cha
       for (int i = 0; i < E; ++i)
         if (draw_weight(false, d, EL::get(v[j], i), 0.f, e0 + j * 64 * E + i, excl) > 0.f)
           last_pos = max(last_pos, e0 + j * 64 * E + i);
-    y = wave_max_int(last_pos);
-    if (y < 0) y = seg * kSeg;
-  } else {
-    int pick = -1;
-    if (lane == lsel) {
-      u32x4 vv = v[0];
-      double run = incl[0] - static_cast<double>(vs[0]);
-#pragma unroll
-      for (int j = 1; j < kVPL; ++j)
-        if (j == jsel) {
-          vv = v[j];
-          run = incl[j] - static_cast<double>(vs[j]);
-        }
-      const int ev = e0 + jsel * 64 * E;
-      int lastw = -1;
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const float wv = draw_weight(false, d, EL::get(vv, i), 0.f, ev + i, excl);
-        run += static_cast<double>(wv);
-        if (wv > 0.f) lastw = ev + i;
-        if (pick < 0 && wv > 0.f && run >= t_seg) pick = ev + i;
-      }
-      if (pick < 0) pick = lastw;
-    }
-    y = lane_broadcast(pick, lsel);
+    const int y = wave_max_int(last_pos);
+    return y < 0 ? seg * kSeg : y;
   }
-  const int n = d.n;
-  const int32_t* xs = a.tokens + static_cast<size_t>(b) * a.K;
+  int pick = -1;
+  if (lane == lsel) {
+    // (each vector walked under its own test, so that no vector is selected by a run-time
+    // index, which would put the wave's vectors in scratch memory)
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j)
+      if (j == jsel) {
+        double run = incl[j] - static_cast<double>(vs[j]);
+        const int ev = e0 + j * 64 * E;
+        int lastw = -1;
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const float wv = draw_weight(false, d, EL::get(v[j], i), 0.f, ev + i, excl);
+          run += static_cast<double>(wv);
+          if (wv > 0.f) lastw = ev + i;
+          if (pick < 0 && wv > 0.f && run >= t_seg) pick = ev + i;
+        }
+        if (pick < 0) pick = lastw;
+      }
+  }
+  return lane_broadcast(pick, lsel);
+}
+
+// The emitted row of sequence b after n accepted drafts xs[0..n) and the drawn token y
+// (then -1), written by the lanes of one wave.
+__device__ __forceinline__ void write_row_wave(const ChainArgs& a, int b, int n, const int32_t* xs, int y) {
   int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-  for (int kk = lane; kk <= a.K; kk += 64) ot[kk] = kk < n ? xs[kk] : (kk == n ? y : -1);
+  for (int kk = static_cast<int>(threadIdx.x & 63); kk <= a.K; kk += 64) ot[kk] = kk < n ? xs[kk] : (kk == n ? y : -1);
+}
+
+// The whole direct draw by one workgroup, reading the unit's segments from memory; every lane
+// calls it.  ps: the partials of row d.row; xs: the sequence's drafted tokens.
+template <int DT, bool VEC>
+__device__ __forceinline__ void direct_draw(const ChainArgs& a, int b, const ChainDecision& d, int mode,
+                                            const void* row, const RowStat* ps, const int32_t* xs, size_t sb) {
+  __shared__ double s_segm[kWaves];
+  using EL = Elem<DT>;
+  constexpr int E = EL::kPerVec;
+  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
+  constexpr int kVPL = kThreads / 64;  // vectors of a segment per lane of a wave
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int usel;
+  double t_unit;
+  direct_locate<DT>(a, b, d, &mode, ps, &usel, &t_unit);
+  stamp(a, sb + kPhPublished);
+  const int excl = mode == kModeOneHot ? d.excl_tok : -1;
+  const int segs = direct_units<DT>(a.nv, a.V).segs;
+
+  // ---- 2. wave q: segment q of the unit, scanned in vocabulary order
+  const int seg = usel * segs + w;  // this wave's segment
+  const int e0 = seg * kSeg + lane * E;
+  u32x4 v[kVPL];
+  float vs[kVPL];
+  double incl[kVPL];
+  if (w < segs) {
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) v[j] = load_vector<DT, VEC>(row, a.V, e0 + j * 64 * E);
+    const double m = wave_segment_scan<DT>(d, v, e0, excl, vs, incl);
+    if (lane == 0) s_segm[w] = m;
+  }
+  __syncthreads();
+
+  // ---- 3. the segment (the same choice in every lane), then the wave holding it narrows
+  double qbase;
+  const int q = pick_segment([&](int k) { return s_segm[k]; }, segs, t_unit, &qbase);
+  if (w != q) return;
+  const int y = wave_segment_pick<DT>(d, v, e0, excl, vs, incl, t_unit - qbase, seg);
+  write_row_wave(a, b, d.n, xs, y);
 }
 
 // Outcomes of a residual draw's hand-over (slot_select, gather_and_locate).
 enum SlotOutcome : int { kSlotDone = 0, kSlotLocated = 1, kSlotNoMass = 2 };
 
-// Wave 0 of a sequence's last pool task, alone (the other waves wait at a barrier): lane l
-// takes segments l, l + 64, ... (round r holds segments 64 r .. 64 r + 63), waits for their
-// masses, and the rounds' inclusive scans in vocabulary order give the total W and the
-// segment whose prefix first reaches u * W.  The masses stay in shared memory (s_m, room for
-// S doubles); the scans are recomputed for the search.  Returns kSlotLocated with the segment
-// and u * W minus the mass before it in *usel_out and *tloc_out (lane 0 writes them);
-// kSlotNoMass if rounding left no residual mass (W = 0); kSlotDone if a wait gave up (the
-// sequence is then flagged).
+// One wave alone (the other waves of its workgroup wait at a barrier): lane l takes segments
+// l, l + 64, ... (round r holds segments 64 r .. 64 r + 63), waits for their masses, and the
+// rounds' inclusive scans in vocabulary order give the total W and the segment whose prefix
+// first reaches uf * W.  The masses stay in shared memory (s_m, room for S doubles); the scans
+// are recomputed for the search.  Returns kSlotLocated with the segment and u * W minus the
+// mass before it in *usel_out and *tloc_out (lane 0 writes them); kSlotNoMass if rounding
+// left no residual mass (W = 0); kSlotDone if a wait gave up (the sequence is then flagged)
+// or if abort() (wave-uniform, asked between polls) said that another workgroup finishes the
+// draw.
+template <class Abort>
 __device__ __forceinline__ int gather_and_locate(const ChainArgs& a, int b, uint32_t gen, const SlotDouble* mw,
-                                                 int units, double* s_m, int* usel_out, double* tloc_out,
-                                                 size_t sb) {
+                                                 int units, float uf, double* s_m, int* usel_out, double* tloc_out,
+                                                 size_t sb, Abort abort) {
   const int lane = threadIdx.x & 63;
   const int rounds = (units + 63) / 64;  // units = S <= 4 * kThreads
   {
@@ -837,6 +993,7 @@ __device__ __forceinline__ int gather_and_locate(const ChainArgs& a, int b, uint
         arrived = true;
         break;
       }
+      if (abort()) return kSlotDone;  // another workgroup finishes the draw
       short_pause();
     }
     if (!arrived) {  // flag the sequence rather than wait on (this task alone writes its row)
@@ -852,7 +1009,7 @@ __device__ __forceinline__ int gather_and_locate(const ChainArgs& a, int b, uint
   for (int r = 0; r < rounds; ++r) W = lane_broadcast(wave_inclusive_scan(s_m[64 * r + lane]) + W, 63);
   stamp(a, sb + kPhGathered);
   if (!(W > 0.0)) return kSlotNoMass;  // no residual mass left after rounding: draw from p_n itself
-  const double tt = static_cast<double>(a.u_final[b]) * W;
+  const double tt = static_cast<double>(uf) * W;
   int usel = -1, lastu = -1;
   double before = 0.0, last_before = 0.0, carry = 0.0;
   for (int r = 0; r < rounds && usel < 0; ++r) {
@@ -883,6 +1040,37 @@ __device__ __forceinline__ int gather_and_locate(const ChainArgs& a, int b, uint
   return kSlotLocated;
 }
 
+// Residual mass of one vector of a row pair: the sum over its E elements, in order, of
+// max(0, p - q) in fp32.
+template <int DT>
+__device__ __forceinline__ float residual_vector_mass(const ChainDecision& d, const u32x4& vt, const u32x4& vd) {
+  using EL = Elem<DT>;
+  float aw = 0.f;
+#pragma unroll
+  for (int i = 0; i < EL::kPerVec; ++i) {
+    const float pv = exp2_fast(fmaf(EL::get(vt, i), d.scale, -d.Ot)) * d.invSt;
+    aw += fmaxf(0.f, pv - exp2_fast(fmaf(EL::get(vd, i), d.scale, -d.Od)) * d.invSd);
+  }
+  return aw;
+}
+
+// Masses of `nseg` consecutive segments from the per-vector masses red[q * kThreads + t] of
+// segment q's vector t, in fp64 (one 16-lane row of the workgroup sums one segment: lane r
+// adds vectors 16 r .. 16 r + 15 in order, then the row's inclusive sum), published in slots
+// mw[0 .. nseg) with tag `gen`.  Every lane calls it; nseg <= kThreads / 16.
+__device__ __forceinline__ void publish_segment_masses(const float* red, int nseg, SlotDouble* mw, uint32_t gen) {
+  const int q = threadIdx.x >> 4;  // q < nseg: segment q
+  const int r = threadIdx.x & 15;
+  double v = 0.0;
+  if (q < nseg) {
+    const float* src = red + q * kThreads + r * 16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v += static_cast<double>(src[i]);
+  }
+  v = row16_inclusive_sum(v);
+  if (q < nseg && r == 15) put_slot(mw + q, v, gen);
+}
+
 // Residual draw after a rejection against draft rows (see chain_pool_kernel, steps 1-3):
 // this task's segment masses of max(0, p - q) go out through the slots; the sequence's last
 // task waits for the others' and returns kSlotLocated with the segment holding u * W and
@@ -892,16 +1080,13 @@ __device__ __forceinline__ int gather_and_locate(const ChainArgs& a, int b, uint
 template <int DT, int SPT, bool VEC>
 __device__ __forceinline__ int slot_select(const ChainArgs& a, int b, int c, bool last, const ChainDecision& d,
                                            const void* row_t, const void* row_d, float* red, int* usel_out,
-                                           double* tloc_out, size_t sb) {
+                                           double* tloc_out, size_t sb, uint32_t gen) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  // the slot generation is read after the decision, off its critical path (measured:
-  // 0.5 us less pool time at B=64, K=5, V=128256; 2.3 us at B=256, K=8, V=152064)
-  const uint32_t gen = pool_generation(a);
 
   // ---- 1. per-lane masses of this task's segments: max(0, p - q), one vector per lane
   {
@@ -912,39 +1097,21 @@ __device__ __forceinline__ int slot_select(const ChainArgs& a, int b, int c, boo
 #pragma unroll
     for (int j = 0; j < SPT; ++j) rd[j] = load_vector<DT, VEC>(row_d, a.V, sbase + (j * kThreads + tid) * E);
 #pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-      float aw = 0.f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const float pv = exp2_fast(fmaf(EL::get(rt[j], i), d.scale, -d.Ot)) * d.invSt;
-        aw += fmaxf(0.f, pv - exp2_fast(fmaf(EL::get(rd[j], i), d.scale, -d.Od)) * d.invSd);
-      }
-      red[j * kThreads + tid] = aw;
-    }
+    for (int j = 0; j < SPT; ++j) red[j * kThreads + tid] = residual_vector_mass<DT>(d, rt[j], rd[j]);
   }
   __syncthreads();
-  // ---- 2. segment totals in fp64 (one 16-lane row sums one segment's 256 lane values)
+  // ---- 2. segment totals in fp64
   const int units = a.S;  // segment slots per row
   SlotDouble* mw = a.wseg + static_cast<size_t>(b) * units;
-  {
-    const int q = tid >> 4;  // q < SPT: segment q
-    const int r = tid & 15;
-    double v = 0.0;
-    if (q < SPT) {
-      const float* src = red + q * kThreads + r * 16;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v += static_cast<double>(src[i]);
-    }
-    v = row16_inclusive_sum(v);
-    if (q < SPT && r == 15) put_slot(mw + c * SPT + q, v, gen);
-  }
+  publish_segment_masses(red, SPT, mw + c * SPT, gen);
   stamp(a, sb + kPhPublished);
   if (!last) return kSlotDone;
   __shared__ int s_outcome, s_usel;
   __shared__ double s_tloc;
   __syncthreads();  // every wave is done with `red`, which holds the gathered masses next
   if (w == 0) {
-    const int o = gather_and_locate(a, b, gen, mw, units, reinterpret_cast<double*>(red), &s_usel, &s_tloc, sb);
+    const int o = gather_and_locate(a, b, gen, mw, units, d.uf, reinterpret_cast<double*>(red), &s_usel, &s_tloc,
+                                    sb, [] { return false; });
     if (lane == 0) s_outcome = o;
   }
   __syncthreads();
@@ -960,9 +1127,13 @@ __device__ __forceinline__ int slot_select(const ChainArgs& a, int b, int c, boo
 // order, and writes it.  If rounding leaves t_loc above the segment's total, the last
 // positive weight is taken; with no positive weight at all (a direct draw whose piece mass
 // came from the stats partials while every weight underflows) the segment's first element.
+// xs: the sequence's drafted tokens.  The segment's vectors come from memory, or from shared
+// memory (st, sd: vector t at index t) where a caller holds them already.
 template <int DT, bool VEC>
 __device__ __forceinline__ void narrow_and_emit(const ChainArgs& a, int b, const ChainDecision& d, int mode,
-                                                int usel, double t_loc, const void* row_t, const void* row_d) {
+                                                int usel, double t_loc, const void* row_t, const void* row_d,
+                                                const int32_t* xs, const u32x4* st = nullptr,
+                                                const u32x4* sd = nullptr) {
   __shared__ double s_wt[kWaves];
   __shared__ int s_first[kWaves];
   using EL = Elem<DT>;
@@ -974,8 +1145,8 @@ __device__ __forceinline__ void narrow_and_emit(const ChainArgs& a, int b, const
   const bool residual = mode == kModeResidual;
   const int excl = mode == kModeOneHot ? d.excl_tok : -1;
   const int e0 = usel * kSeg + tid * E;
-  const u32x4 vt = load_vector<DT, VEC>(row_t, a.V, e0);
-  const u32x4 vd = residual ? load_vector<DT, VEC>(row_d, a.V, e0) : vt;
+  const u32x4 vt = st ? st[tid] : load_vector<DT, VEC>(row_t, a.V, e0);
+  const u32x4 vd = !residual ? vt : (sd ? sd[tid] : load_vector<DT, VEC>(row_d, a.V, e0));
   float wl[E];
   float lsum = 0.f;
   int last_pos = -1;
@@ -997,7 +1168,6 @@ __device__ __forceinline__ void narrow_and_emit(const ChainArgs& a, int b, const
 #pragma unroll
   for (int i = 1; i < kWaves; ++i) kmin = min(kmin, s_first[i]);
   const int n = d.n;
-  const int32_t* xs = a.tokens + static_cast<size_t>(b) * a.K;
   int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
   if (kmin == INT_MAX) {  // rounding left t_loc above the segment total: last positive weight
     int y = block_max_int(last_pos, s_first);
@@ -1067,7 +1237,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   const size_t sb = a.stamps_pool + kStampsPerTask * (static_cast<size_t>(b0) * CP + gi);
   stamp(a, sb + kPhStart);
 
-  chain_decide<DT>(a, b, clamped_len(a, b), last, &s_dec);
+  chain_decide<DT>(a, b, clamped_len(a, b), seq_inputs(a, b), last, &s_dec);
   const ChainDecision d = uniform_decision(s_dec);
   stamp(a, sb + kPhDecided);
   if (a.stamps && tid == 0)
@@ -1082,8 +1252,13 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   if (mode == kModeResidual) {
     int usel;
     double t_loc;
-    const int o = slot_select<DT, SPT, VEC>(a, b, c, last, d, row_t, draft_row<DT>(a, b, d.row), red, &usel, &t_loc, sb);
-    if (o == kSlotLocated) narrow_and_emit<DT, VEC>(a, b, d, mode, usel, t_loc, row_t, draft_row<DT>(a, b, d.row));
+    // the slot generation is read after the decision, off its critical path (measured: 0.5 us
+    // less pool time at B=64, K=5, V=128256; 2.3 us at B=256, K=8, V=152064)
+    const int o = slot_select<DT, SPT, VEC>(a, b, c, last, d, row_t, draft_row<DT>(a, b, d.row), red, &usel, &t_loc,
+                                            sb, pool_generation(a));
+    if (o == kSlotLocated)
+      narrow_and_emit<DT, VEC>(a, b, d, mode, usel, t_loc, row_t, draft_row<DT>(a, b, d.row),
+                               a.tokens + static_cast<size_t>(b) * a.K);
     if (o != kSlotNoMass) {
       stamp(a, sb + kPhEnd);
       return;
@@ -1093,8 +1268,482 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
     stamp(a, sb + kPhEnd);
     return;
   }
-  direct_draw<DT, VEC>(a, b, d, mode, row_t, sb);
+  direct_draw<DT, VEC>(a, b, d, mode, row_t, a.part + (static_cast<size_t>(b) * a.R + d.row) * a.C * kWaves,
+                       a.tokens + static_cast<size_t>(b) * a.K, sb);
   stamp(a, sb + kPhEnd);
+}
+
+// ---------------------------------------------------------------- single-launch path
+//
+// For batches whose whole grid fits on the device at once, one launch holds (in dispatch
+// order) the n-gram lookup's workgroups (when it drafts) and then, sequence by sequence, one
+// workgroup per position k = 0..K and chunk c.  That workgroup reads chunk c of target row k
+// and, where a draft row scores position k, of draft row k, keeps both in registers, and
+// publishes their wave partials (o, s) as words tagged with seq_tag.  It then gathers every
+// partial its sequence's decision reads into shared memory and decides (every workgroup of the
+// sequence reaches the same decision from the same data in the same order), and the
+// workgroups of the draw's position finish the draw from their registers:
+//  - a bonus or one-hot draw: the unit holding u * W is found from the partials
+//    (direct_locate); the one wave holding that unit narrows it (wave_segment_scan,
+//    pick_segment, wave_segment_pick);
+//  - a residual draw: each workgroup of position n sums max(0, p - q) over its segments and
+//    publishes the masses; each then gathers all of the row's masses and locates the segment
+//    holding u * W (gather_and_locate), and the workgroup holding that segment stages it in
+//    shared memory and narrows it (narrow_and_emit).
+// The reads and the arithmetic are those of the separate launches (chain_stats_kernel, then
+// chain_pool_kernel) with the same chunk size, so the two give the same outputs bit for bit.
+//
+// Waits.  The sequence's last workgroup (the anchor: position K, last chunk) waits only for
+// workgroups dispatched before it, with the long poll limit; it writes the count and the
+// probabilities.  The others wait for the partials with a short limit (kShortPolls) and
+// publish a status word once they hold every partial (kStPassed) or gave up (kStLeft); one
+// that passed never gives up afterwards.  The anchor checks the statuses of the workgroups
+// the draw needs (the owner of a direct draw's unit; every workgroup of a residual draw's
+// position): if any left, it finishes the draw itself from memory, as chain_pool_kernel does,
+// and the workgroups of that position that passed see the departure and stand down.  So
+// every wait ends (the long ones wait only for earlier workgroups, whose own waits are
+// bounded), and exactly one workgroup writes each sequence's emitted row.  The anchor
+// advances the sequence's run counter once every workgroup of the sequence has published
+// its status (and so has read the counter).  If the anchor's own wait gives up and no
+// workgroup passed, it flags the sequence -2.
+
+constexpr int kPoolSegments = 4;       // segments per pool task (chain_pool_kernel)
+constexpr int kSingleVectors = 4;      // vectors a lane in a chunk of the single launch
+constexpr int kSingleMaxParts = 512;   // partials one sequence's decision reads (R * C * kWaves)
+constexpr int kSingleMaxGroups = 1024; // workgroups of a single launch (about four per compute unit)
+constexpr int kSmallTile = 1024;       // the lookup's context tile inside a shared launch (4 KiB)
+constexpr int kShortPolls = 2048;      // polls of a non-anchor workgroup's wait for the partials
+constexpr uint32_t kFallbackTagMix = 0x27d4eb2fu;  // slot tag of the anchor's own residual draw
+enum SeqStatus : uint32_t { kStPassed = 1, kStLeft = 2 };
+
+// Gather sequence b's decision inputs into shared memory; every lane calls it.  With the
+// lookup (NGRAM) its draft length, tokens and their logits come as tagged words; otherwise
+// the caller left them in s_kb, s_tok and s_gath before the call.  False if the wait gave up
+// after `limit` polls.
+__device__ __forceinline__ bool single_gather(const ChainArgs& a, int b, uint32_t tag, bool greedy, bool NGRAM,
+                                              int limit, RowStat* s_part, int32_t* s_tok, float* s_gath,
+                                              int* s_kb) {
+  const int tid = threadIdx.x;
+  const int C4 = a.C * kWaves;
+  if (NGRAM) {
+    const uint64_t* w = a.tprop + static_cast<size_t>(b) * (2 * a.K + 1);
+    bool ok = false;
+    for (int polls = 0; polls < limit; ++polls) {
+      uint32_t v = 0;
+      const bool got = tid != 0 || get_tagged_u32(w, tag, &v);
+      if (tid == 0 && got) *s_kb = static_cast<int>(v);
+      if (!__syncthreads_or(!got)) {
+        ok = true;
+        break;
+      }
+      short_pause();
+    }
+    if (!ok) return false;
+    const int len = *s_kb;
+    ok = false;
+    for (int polls = 0; polls < limit; ++polls) {
+      bool missing = false;
+      if (tid < len) {
+        uint32_t x = 0, g = 0;
+        if (get_tagged_u32(w + 1 + tid, tag, &x) && get_tagged_u32(w + 1 + a.K + tid, tag, &g)) {
+          s_tok[tid] = static_cast<int32_t>(x);
+          s_gath[tid] = __uint_as_float(g);
+        } else {
+          missing = true;
+        }
+      }
+      if (!__syncthreads_or(missing)) {
+        ok = true;
+        break;
+      }
+      short_pause();
+    }
+    if (!ok) return false;
+  } else {
+    __syncthreads();
+  }
+  const int kb_raw = *s_kb;
+  const int kb = kb_raw < 0 ? 0 : (kb_raw > a.K ? a.K : kb_raw);
+  // partials of the rows the decision reads (the lookup's case: every target row)
+  const uint64_t* tp = a.tpart + static_cast<size_t>(b) * (3 * kSingleMaxParts);
+  const int items = a.R * C4;
+  unsigned have = 0;  // items tid, tid + kThreads (items <= kSingleMaxParts = 2 * kThreads)
+  for (int polls = 0; polls < limit; ++polls) {
+    bool missing = false;
+#pragma unroll
+    for (int j = 0; j < kSingleMaxParts / kThreads; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < items && !(have >> j & 1u)) {
+        if (!(NGRAM || row_needed(a, i / C4, kb, greedy))) {
+          have |= 1u << j;
+          continue;
+        }
+        uint32_t o;
+        double sv;
+        if (get_tagged_u32(tp + 3 * i, tag, &o) && get_tagged_double(tp + 3 * i + 1, tag, &sv)) {
+          s_part[i] = RowStat{__uint_as_float(o), 0.f, sv};
+          have |= 1u << j;
+        } else {
+          missing = true;
+        }
+      }
+    }
+    if (!__syncthreads_or(missing)) return true;
+    short_pause();
+  }
+  return false;
+}
+
+// Copies row `row`'s partials (published, so read without waiting) back into shared memory.
+__device__ __forceinline__ void single_restage_row(const ChainArgs& a, int b, uint32_t tag, int row, RowStat* s_part) {
+  const int C4 = a.C * kWaves;
+  const uint64_t* tp = a.tpart + static_cast<size_t>(b) * (3 * kSingleMaxParts) + 3 * static_cast<size_t>(row) * C4;
+  for (int i = threadIdx.x; i < C4; i += kThreads) {
+    uint32_t o = 0;
+    double sv = 0.0;
+    get_tagged_u32(tp + 3 * i, tag, &o);
+    get_tagged_double(tp + 3 * i + 1, tag, &sv);
+    s_part[static_cast<size_t>(row) * C4 + i] = RowStat{__uint_as_float(o), 0.f, sv};
+  }
+  __syncthreads();
+}
+
+// The wave holding unit `usel` of a direct draw in registers (raw: this wave's share of the
+// chunk, NV >= kWaves vectors a lane, so a unit is one wave's share) narrows it and writes the
+// row; called by that wave alone.
+template <int DT, int NV>
+__device__ __forceinline__ void single_direct_finish(const ChainArgs& a, int b, const ChainDecision& d, int mode,
+                                                     int usel, double t_unit, const u32x4 (&raw)[NV],
+                                                     const int32_t* xs) {
+  static_assert(NV >= kWaves, "a unit is one wave's share of a chunk");
+  constexpr int E = Elem<DT>::kPerVec;
+  constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
+  constexpr int kVPL = kThreads / 64;
+  constexpr int kSegs = NV / kWaves;  // segments of the unit
+  const int lane = threadIdx.x & 63;
+  const int excl = mode == kModeOneHot ? d.excl_tok : -1;
+  double m[kSegs];
+#pragma unroll
+  for (int q = 0; q < kSegs; ++q) {  // segment q: this wave's vectors 4q .. 4q + 3
+    u32x4 v[kVPL];
+    float vs[kVPL];
+    double incl[kVPL];
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) v[j] = raw[q * kVPL + j];
+    m[q] = wave_segment_scan<DT>(d, v, (usel * kSegs + q) * kSeg + lane * E, excl, vs, incl);
+  }
+  double qbase;
+  const int q = pick_segment(
+      [&](int k) {
+        double r = m[0];
+#pragma unroll
+        for (int t = 1; t < kSegs; ++t)
+          if (t == k) r = m[t];
+        return r;
+      },
+      kSegs, t_unit, &qbase);
+  u32x4 v[kVPL];
+#pragma unroll
+  for (int j = 0; j < kVPL; ++j) {
+    v[j] = raw[j];
+#pragma unroll
+    for (int t = 1; t < kSegs; ++t)
+      if (t == q) v[j] = raw[t * kVPL + j];
+  }
+  const int seg = usel * kSegs + q;
+  const int e0 = seg * kSeg + lane * E;
+  float vs[kVPL];
+  double incl[kVPL];
+  wave_segment_scan<DT>(d, v, e0, excl, vs, incl);
+  const int y = wave_segment_pick<DT>(d, v, e0, excl, vs, incl, t_unit - qbase, seg);
+  write_row_wave(a, b, d.n, xs, y);
+}
+
+// One workgroup of a single launch: sequence b, position k, chunk c (see above).
+template <int DT, int NV, bool VEC, bool DRAFT>
+__device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, int c, bool ngram) {
+  using EL = Elem<DT>;
+  constexpr size_t kBufBytes = kSingleMaxParts * sizeof(RowStat);
+  constexpr int kMaxGroups = kSingleMaxParts / kWaves;  // workgroups of one sequence
+  static_assert(2 * kThreads * sizeof(u32x4) <= kBufBytes, "a staged segment pair");
+  static_assert(!DRAFT || NV * kThreads * sizeof(float) <= kBufBytes, "per-vector residual masses");
+  static_assert(kMaxGroups <= kThreads, "one status a lane");
+  __shared__ __align__(16) unsigned char s_buf[kBufBytes];  // partials; then masses or a staged segment
+  __shared__ int32_t s_tok[SPEC_MAX_K];
+  __shared__ float s_gath[2 * SPEC_MAX_K + 1];
+  __shared__ float s_u[SPEC_MAX_K];
+  __shared__ int s_kb;
+  __shared__ ChainDecision s_dec;
+  __shared__ int s_outcome, s_usel;
+  __shared__ double s_tloc;
+  __shared__ uint32_t s_stv[kMaxGroups];
+  RowStat* s_part = reinterpret_cast<RowStat*>(s_buf);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int C = a.C;
+  const int nw = (a.K + 1) * C;  // workgroups of the sequence
+  const int j = k * C + c;
+  const bool anchor = j == nw - 1;
+  const int kb0 = ngram ? a.K : clamped_len(a, b);  // positions read: 0 .. kb0
+  const bool greedy = is_greedy(a, b);
+  const bool has_t = k <= kb0;
+  if (!has_t && !anchor) return;  // reads nothing and takes no part
+  const bool has_d = DRAFT && has_t && !greedy && k < kb0;
+  const size_t sb = kStampsPerTask * (static_cast<size_t>(b) * nw + j);  // this workgroup's stamps
+  stamp(a, sb + kSgStart);
+  const uint32_t tag = seq_tag(a, b);
+  uint64_t* tp = a.tpart + static_cast<size_t>(b) * (3 * kSingleMaxParts);
+  uint64_t* st = a.status + static_cast<size_t>(b) * kMaxGroups;
+  const int S = a.S;
+
+  // the decision's scalar inputs and (wave 0, lane l) drafted token l and its uniform first,
+  // then the chunks, then the tokens' logits
+  const float T = a.temperature[b];
+  const float uf = a.u_final[b];
+  int x = -1;
+  float ul = 1.f;
+  if (w == 0 && lane < a.K) {
+    if (!ngram) x = a.tokens[static_cast<size_t>(b) * a.K + lane];
+    ul = a.u_accept[static_cast<size_t>(b) * a.K + lane];
+  }
+  u32x4 rt[NV], rd[NV];
+  if (has_t) load_wave_span<DT, NV, VEC, true>(rt, target_row<DT>(a, b, k), a.V, c);
+  if (has_d) load_wave_span<DT, NV, VEC, true>(rd, draft_row<DT>(a, b, k), a.V, c);
+  float gt = 0.f, gd = 0.f;
+  if (!ngram && !greedy && w == 0 && lane < kb0 && x >= 0 && x < a.V) {
+    gt = EL::value(target_row<DT>(a, b, lane), x);
+    if (DRAFT) gd = EL::value(draft_row<DT>(a, b, lane), x);
+  }
+
+  // this workgroup's partials
+  const float scale = kLog2e / T;
+  if (has_t) {
+    float o;
+    double sv;
+    if (greedy) {
+      int idx;
+      wave_argmax_partial<DT, NV, VEC>(rt, c, a.V, &o, &idx);
+      sv = static_cast<double>(idx);
+    } else {
+      wave_softmax_partial<DT, NV>(rt, scale, &o, &sv);
+    }
+    const size_t i = (static_cast<size_t>(k) * C + c) * kWaves + w;
+    if (lane == 0) {
+      put_tagged_u32(tp + 3 * i, __float_as_uint(o), tag);
+      put_tagged_double(tp + 3 * i + 1, sv, tag);
+    }
+  }
+  if (has_d) {
+    float o;
+    double sv;
+    wave_softmax_partial<DT, NV>(rd, scale, &o, &sv);
+    const size_t i = (static_cast<size_t>(a.K + 1 + k) * C + c) * kWaves + w;
+    if (lane == 0) {
+      put_tagged_u32(tp + 3 * i, __float_as_uint(o), tag);
+      put_tagged_double(tp + 3 * i + 1, sv, tag);
+    }
+  }
+  stamp(a, sb + kSgPublished);
+
+  // the decision's inputs
+  if (w == 0) {
+    if (lane < a.K) s_u[lane] = ul;
+    if (!ngram) {
+      if (lane < a.K) s_tok[lane] = x;
+      if (lane < kb0) {
+        s_gath[lane] = gt;
+        if (DRAFT) s_gath[a.K + 1 + lane] = gd;
+      }
+      if (lane == 0) s_kb = a.draft_len ? a.draft_len[b] : a.K;
+    }
+  }
+  const int limit = anchor ? a.poll_limit : min(a.poll_limit, kShortPolls);
+  bool ok = single_gather(a, b, tag, greedy, ngram, limit, s_part, s_tok, s_gath, &s_kb);
+  stamp(a, sb + kSgGathered);
+  if (!anchor) {
+    if (tid == 0) put_tagged_u32(st + j, ok ? kStPassed : kStLeft, tag);
+    if (!ok) return;
+  }
+  // the anchor's view of the others: the sequence's other workgroups that read rows (its own
+  // position, K, is among them only when it reads rows itself)
+  const int others = min((kb0 + 1) * C, nw - 1);
+  auto read_statuses = [&] {  // every lane; true once all are out (s_stv: the values, 0 = none)
+    bool got = tid >= others;
+    for (int polls = 0; polls < a.poll_limit; ++polls) {
+      if (!got) {
+        uint32_t v = 0;
+        got = get_tagged_u32(st + tid, tag, &v);
+        s_stv[tid] = got ? v : 0u;
+      }
+      if (!__syncthreads_or(!got)) return true;
+      short_pause();
+    }
+    __syncthreads();
+    return false;
+  };
+  if (!ok) {  // the anchor's wait gave up: go on if another workgroup holds every partial
+    read_statuses();
+    bool passed = false;
+    for (int i = tid; i < others; i += kThreads) passed |= s_stv[i] == kStPassed;
+    if (__syncthreads_or(passed)) ok = single_gather(a, b, tag, greedy, ngram, a.poll_limit, s_part, s_tok, s_gath, &s_kb);
+    if (!ok) {
+      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+      for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
+      if (a.out_probs)
+        for (int i = tid; i < a.K * 3; i += kThreads) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
+      if (tid == 0) {
+        a.out_num[b] = kFlagTimedOut;
+        __hip_atomic_fetch_add(a.epoch + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
+    }
+  }
+
+  const int kb_raw = s_kb;
+  const int kb = kb_raw < 0 ? 0 : (kb_raw > a.K ? a.K : kb_raw);
+  SlotDouble* tm = a.tmass + static_cast<size_t>(b) * a.K * S;  // [K][S]
+  // Before deciding, a workgroup whose position has draft rows publishes its segments' residual
+  // masses for a rejection at its position (they need only that position's row offsets and
+  // sums, with the arithmetic the decision would give them), so that they are out by the time
+  // the decision is.
+  auto speculate = [&](const float* sO, const double* sS) {
+    if (!(has_d && k < kb)) return;
+    ChainDecision dk{};
+    dk.scale = scale;
+    dk.Ot = sO[k];
+    dk.invSt = static_cast<float>(inv_row_sum(sS[k]));
+    dk.Od = sO[a.K + 1 + k];
+    dk.invSd = static_cast<float>(inv_row_sum(sS[a.K + 1 + k]));
+    float* red = reinterpret_cast<float*>(s_buf);  // the partials are combined: free
+#pragma unroll
+    for (int jv = 0; jv < NV; ++jv) red[(w * NV + jv) * 64 + lane] = residual_vector_mass<DT>(dk, rt[jv], rd[jv]);
+    __syncthreads();
+    // this chunk holds segments c * NV .. c * NV + NV - 1 (those from S on lie past V)
+    publish_segment_masses(red, min(NV, S - c * NV), tm + static_cast<size_t>(k) * S + c * NV, tag);
+  };
+  chain_decide<DT>(a, b, kb, SeqInputs{s_part, s_tok, s_gath, s_u, T, uf, kb_raw}, anchor, &s_dec, speculate);
+  const ChainDecision d = uniform_decision(s_dec);
+  stamp(a, sb + kSgDecided);
+  const int mode = d.mode;
+  const int row = d.row;
+  const bool direct = mode == kModeBonus || mode == kModeOneHot;
+  int owner_c = -1;  // a direct draw: the chunk holding its unit
+  if (mode == kModeResidual && DRAFT && k == row) {
+    // every workgroup of position n has published its masses: gather them, locate the draw
+    if (w == 0) {
+      const int o = gather_and_locate(a, b, tag, tm + static_cast<size_t>(row) * S, S, d.uf,
+                                      reinterpret_cast<double*>(s_buf), &s_usel, &s_tloc, 0, [&] {
+                                        bool gone = false;
+                                        if (lane < C) {
+                                          uint32_t v = 0;
+                                          gone = get_tagged_u32(st + row * C + lane, tag, &v) && v == kStLeft;
+                                        }
+                                        return __ballot(gone) != 0ull;
+                                      });
+      if (lane == 0) s_outcome = o;
+    }
+    __syncthreads();
+    stamp(a, sb + kSgDrawn);
+    const int o = s_outcome;
+    if (o == kSlotLocated) {
+      const int usel = s_usel;
+      if (usel / NV != c) return;
+      // stage the segment pair (vector t of the segment at index t) and narrow it
+      u32x4* stt = reinterpret_cast<u32x4*>(s_buf);
+      u32x4* sdd = stt + kThreads;
+      const int sq = usel % NV;
+#pragma unroll
+      for (int jv = 0; jv < NV; ++jv) {
+        const int tc = (w * NV + jv) * 64 + lane;  // vector index within the chunk
+        if (tc / kThreads == sq) {
+          stt[tc % kThreads] = rt[jv];
+          sdd[tc % kThreads] = rd[jv];
+        }
+      }
+      __syncthreads();
+      narrow_and_emit<DT, VEC>(a, b, d, mode, usel, s_tloc, nullptr, nullptr, s_tok, stt, sdd);
+      stamp(a, sb + kSgEnd);
+      return;
+    }
+    if (o != kSlotNoMass) return;
+    // no residual mass after rounding: the draw takes p_n itself, as a bonus draw would
+    single_restage_row(a, b, tag, row, s_part);
+    int m2 = kModeFallbackP, usel;
+    double t_unit;
+    direct_locate<DT>(a, b, d, &m2, s_part + static_cast<size_t>(row) * C * kWaves, &usel, &t_unit);
+    if (usel / kWaves == c && w == usel % kWaves) single_direct_finish<DT, NV>(a, b, d, m2, usel, t_unit, rt, s_tok);
+    return;
+  }
+  if (direct && (k == row || anchor)) {
+    int m2 = mode, usel;
+    double t_unit;
+    direct_locate<DT>(a, b, d, &m2, s_part + static_cast<size_t>(row) * C * kWaves, &usel, &t_unit);
+    stamp(a, sb + kSgDrawn);
+    owner_c = usel / kWaves;  // a unit is one wave's share: four to a chunk
+    if (k == row && c == owner_c && w == usel % kWaves) {
+      single_direct_finish<DT, NV>(a, b, d, m2, usel, t_unit, rt, s_tok);
+      if (a.stamps && lane == 0) a.stamps[sb + kSgEnd] = __builtin_amdgcn_s_memrealtime();
+    }
+  }
+  if (!anchor) return;
+  // The anchor: every status (also the one every workgroup's use of the run counter ends with);
+  // a draw whose workgroups did not all pass is finished here from memory
+  const bool all = read_statuses();
+  if (direct && !(k == row && c == owner_c) && s_stv[row * C + owner_c] != kStPassed)
+    direct_draw<DT, VEC>(a, b, d, mode, target_row<DT>(a, b, row), s_part + static_cast<size_t>(row) * C * kWaves,
+                         s_tok, 0);
+  if (mode == kModeResidual && DRAFT) {
+    bool gone = false;
+    for (int i = tid; i < C; i += kThreads) gone |= s_stv[row * C + i] != kStPassed;
+    if (__syncthreads_or(gone)) {
+      const void* row_t = target_row<DT>(a, b, row);
+      const void* row_d = draft_row<DT>(a, b, row);
+      const uint32_t g2 = tag ^ kFallbackTagMix;
+      float* red = reinterpret_cast<float*>(s_buf);
+      int usel = 0, o = kSlotDone;
+      double t_loc = 0.0;
+      for (int cg = 0; cg < S / kPoolSegments; ++cg)
+        o = slot_select<DT, kPoolSegments, VEC>(a, b, cg, cg == S / kPoolSegments - 1, d, row_t, row_d, red, &usel,
+                                                &t_loc, 0, g2);
+      if (o == kSlotLocated) narrow_and_emit<DT, VEC>(a, b, d, mode, usel, t_loc, row_t, row_d, s_tok);
+      if (o == kSlotNoMass) {
+        single_restage_row(a, b, tag, row, s_part);
+        direct_draw<DT, VEC>(a, b, d, kModeFallbackP, row_t, s_part + static_cast<size_t>(row) * C * kWaves, s_tok,
+                             0);
+      }
+    }
+  }
+  (void)all;
+  if (tid == 0) __hip_atomic_fetch_add(a.epoch + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  stamp(a, sb + kSgEnd);
+}
+
+// grid = P + B x (K+1) x C: P = B lookup workgroups when the lookup drafts (else 0), then the
+// sequences' workgroups (position k, chunk c).
+template <int DT, int NV, bool VEC, bool DRAFT>
+__global__ __launch_bounds__(kThreads) void chain_single_kernel(ChainArgs a, NgramArgs ng, int P) {
+  int i = static_cast<int>(blockIdx.x);
+  if (i < P) {  // the lookup for sequence i, and its results as tagged words
+    int32_t* tokens = const_cast<int32_t*>(a.tokens);
+    const int len = ngram_propose_body<kThreads, kSmallTile>(i, ng.context, ng.context_len, ng.L_max, ng.n_min,
+                                                            ng.n_max, a.K, tokens, const_cast<int32_t*>(a.draft_len),
+                                                            ng.match_n);
+    const uint32_t tag = seq_tag(a, i);
+    uint64_t* w = a.tprop + static_cast<size_t>(i) * (2 * a.K + 1);
+    for (int k = threadIdx.x; k < len; k += kThreads) {  // lane k wrote token k above and reads it back
+      const int x = tokens[static_cast<size_t>(i) * a.K + k];
+      const float g = x >= 0 && x < a.V ? Elem<DT>::value(target_row<DT>(a, i, k), x) : 0.f;
+      put_tagged_u32(w + 1 + k, static_cast<uint32_t>(x), tag);
+      put_tagged_u32(w + 1 + a.K + k, __float_as_uint(g), tag);
+    }
+    if (threadIdx.x == 0) put_tagged_u32(w, static_cast<uint32_t>(len), tag);
+    return;
+  }
+  i -= P;
+  const int per = (a.K + 1) * a.C;
+  const int j = i % per;
+  single_task<DT, NV, VEC, DRAFT>(a, i / per, j / a.C, j % a.C, P > 0);
 }
 
 // grid = 1: offsets and packed tokens of the batch (only when packed output is asked for).
@@ -1106,11 +1755,10 @@ __global__ void write_zero_offset_kernel(int32_t* offsets) {
 
 // ---------------------------------------------------------------- host side
 
-constexpr int kPoolSegments = 4;  // segments per pool task
-
 struct ChainLayout {
   int nv, C, R, S;
-  size_t off_gath, off_part, off_wseg, bytes;
+  bool single;  // the shape may take the single-launch path (its regions are laid out)
+  size_t off_gath, off_part, off_wseg, off_epoch, off_tpart, off_tprop, off_status, off_tmass, bytes;
 };
 
 // Vectors per lane in one stats chunk.  The largest chunk (16 vectors for bf16 rows read with
@@ -1150,16 +1798,32 @@ static int chain_nv(long long rows, int V, int epv, bool vec) {
 // `vec`: the rows can be read with 16-byte loads; `one_hot`: no draft rows (K+1 rows per
 // sequence are streamed instead of 2K+1).  Both set the chunk size; the workspace regions keep
 // room for 2K+1 rows either way.
-static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool vec, bool one_hot) {
+static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool vec, bool one_hot, bool prefer_single) {
   ChainLayout L{};
   const int epv = dtype == SPEC_BF16 ? 8 : 4;
   L.R = 2 * K + 1;
-  L.nv = chain_nv(static_cast<long long>(B) * (one_hot ? K + 1 : L.R), V, epv, vec);
-  const long long chunk = static_cast<long long>(L.nv) * kThreads * epv;
-  L.C = static_cast<int>((V + chunk - 1) / chunk);
+  const int rows = one_hot ? K + 1 : L.R;  // rows a sequence streams
   const long long seg = static_cast<long long>(kThreads) * epv;
   const long long used = (V + seg - 1) / seg;
   L.S = static_cast<int>((used + kPoolSegments - 1) / kPoolSegments * kPoolSegments);
+  const auto chunks = [&](int nv) {
+    const long long chunk = static_cast<long long>(nv) * kThreads * epv;
+    return static_cast<int>((V + chunk - 1) / chunk);
+  };
+  // the single launch: chunks of kSingleVectors vectors a lane, the whole grid (lookup and
+  // (K+1) x C workgroups a sequence) within kSingleMaxGroups and a sequence's partials within
+  // kSingleMaxParts
+  const auto fits_single = [&](int nv) {
+    const long long groups = static_cast<long long>(B) * ((K + 1) * static_cast<long long>(chunks(nv)) + 1);
+    return nv == kSingleVectors && groups <= kSingleMaxGroups &&
+           static_cast<long long>(rows) * chunks(nv) * kWaves <= kSingleMaxParts;
+  };
+  L.nv = chain_nv(static_cast<long long>(B) * rows, V, epv, vec);
+  // a small batch whose chunk choice is smaller takes the single launch's chunk when that fits
+  // (unless a knob forces the chunk or the separate launches)
+  if (prefer_single && L.nv < kSingleVectors && knob(SPEC_KNOB_CHUNK_VECTORS) == 0 && fits_single(kSingleVectors))
+    L.nv = kSingleVectors;
+  L.C = chunks(L.nv);
   const size_t segs = static_cast<size_t>(B) * L.S;
   size_t off = 256;  // bytes 0..3: the run counter
   L.off_gath = off;
@@ -1168,6 +1832,20 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool ve
   off = align_up(off + sizeof(RowStat) * static_cast<size_t>(B) * L.R * L.C * kWaves, 256);
   L.off_wseg = off;
   off = align_up(off + sizeof(SlotDouble) * segs, 256);
+  // the single-launch path's words, for shapes it may take (the device decides at call time)
+  L.single = prefer_single && fits_single(L.nv);
+  if (L.single) {
+    L.off_epoch = off;
+    off = align_up(off + sizeof(uint32_t) * B, 256);
+    L.off_tpart = off;
+    off = align_up(off + 3 * sizeof(uint64_t) * static_cast<size_t>(B) * kSingleMaxParts, 256);
+    L.off_tprop = off;
+    off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * (2 * K + 1), 256);
+    L.off_status = off;
+    off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * (kSingleMaxParts / kWaves), 256);
+    L.off_tmass = off;
+    off = align_up(off + sizeof(SlotDouble) * static_cast<size_t>(B) * K * L.S, 256);
+  }
   L.bytes = off;
   return L;
 }
@@ -1218,6 +1896,32 @@ static spec_status_t launch_chain(ChainArgs a, const NgramArgs* ng, hipStream_t 
     }
   }
   static std::atomic<int> slots_cache[kMaxDevices];
+  static std::atomic<int> single_cache[2][kMaxDevices];
+  if constexpr (NV == kSingleVectors) {
+    if (a.epoch && knob(SPEC_KNOB_SINGLE_LAUNCH) == 0) {
+      // one launch when the whole grid fits on the device at once (with its own stamp layout)
+      ChainArgs as = a;
+      as.stamps = nullptr;
+      as.stamps_pool = 0;
+      if (unsigned long long* buf = g_stamps.load(std::memory_order_acquire))
+        if (kStampsPerTask * static_cast<size_t>(a.B) * (a.K + 1) * a.C <= g_stamp_words.load(std::memory_order_acquire))
+          as.stamps = buf;
+      using Kernel = void (*)(ChainArgs, NgramArgs, int);
+      const Kernel kernel = a.draft ? chain_single_kernel<DT, NV, VEC, true> : chain_single_kernel<DT, NV, VEC, false>;
+      const int P = ng ? a.B : 0;
+      const long long total = P + static_cast<long long>(a.B) * (a.K + 1) * a.C;
+      if (total <= pool_slots(reinterpret_cast<const void*>(kernel), single_cache[a.draft ? 1 : 0])) {
+        const NgramArgs none{};
+        LaunchScope scope("chain_single", stream);
+        scope.launch(kernel, dim3(static_cast<unsigned>(total)), dim3(kThreads), stream, as, ng ? *ng : none, P);
+        const spec_status_t st = scope.finish();
+        if (st != SPEC_OK || !a.out_packed) return st;
+        LaunchScope pack("chain_pack", stream);
+        pack.launch(chain_pack_kernel, dim3(1), dim3(kThreads), stream, a);
+        return pack.finish();
+      }
+    }
+  }
   {
     const long long g1 = static_cast<long long>(a.B) * a.R * a.C;
     if (ng) {
@@ -1307,14 +2011,15 @@ extern "C" {
 
 size_t spec_verify_chain_workspace_size(int B, int K, int V, spec_dtype_t dtype) {
   if (B <= 0 || K < 1 || K > SPEC_MAX_K || V < 1) return 0;
-  // any of the chunk sizes may be chosen at call time (they depend on the pointers' alignment
-  // and on whether draft rows are given)
+  // any of the chunk sizes may be chosen at call time (they depend on the pointers' alignment,
+  // on whether draft rows are given and on whether the single launch is allowed)
   size_t bytes = 0;
   for (int vec = 0; vec < 2; ++vec)
-    for (int one_hot = 0; one_hot < 2; ++one_hot) {
-      const size_t b = chain_layout(B, K, V, dtype, vec != 0, one_hot != 0).bytes;
-      bytes = b > bytes ? b : bytes;
-    }
+    for (int one_hot = 0; one_hot < 2; ++one_hot)
+      for (int single = 0; single < 2; ++single) {
+        const size_t b = chain_layout(B, K, V, dtype, vec != 0, one_hot != 0, single != 0).bytes;
+        bytes = b > bytes ? b : bytes;
+      }
   return bytes;
 }
 
@@ -1351,7 +2056,7 @@ static spec_status_t verify_chain_impl(const void* target_logits, const void* dr
     return fail(SPEC_ERR_UNSUPPORTED, "B*(K+1)*V too large");
   const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits) &&
                    (draft_logits == nullptr || aligned16(draft_logits));
-  const ChainLayout L = chain_layout(B, K, V, dtype, vec, draft_logits == nullptr);
+  const ChainLayout L = chain_layout(B, K, V, dtype, vec, draft_logits == nullptr, knob(SPEC_KNOB_SINGLE_LAUNCH) == 0);
   const double groups = static_cast<double>(B) * L.R * L.C;
   if (groups > 2147483647.0) return fail(SPEC_ERR_UNSUPPORTED, "grid of %.0f workgroups too large", groups);
   if (L.S > 4 * kThreads)
@@ -1390,6 +2095,13 @@ static spec_status_t verify_chain_impl(const void* target_logits, const void* dr
   a.gath = reinterpret_cast<float*>(ws + L.off_gath);
   a.part = reinterpret_cast<RowStat*>(ws + L.off_part);
   a.wseg = reinterpret_cast<SlotDouble*>(ws + L.off_wseg);
+  if (L.single) {
+    a.epoch = reinterpret_cast<uint32_t*>(ws + L.off_epoch);
+    a.tpart = reinterpret_cast<uint64_t*>(ws + L.off_tpart);
+    a.tprop = reinterpret_cast<uint64_t*>(ws + L.off_tprop);
+    a.status = reinterpret_cast<uint64_t*>(ws + L.off_status);
+    a.tmass = reinterpret_cast<SlotDouble*>(ws + L.off_tmass);
+  }
 
   if (dtype == SPEC_BF16) return dispatch_chain<kBF16>(L.nv, vec, a, ng, s);
   return dispatch_chain<kF32>(L.nv, vec, a, ng, s);

@@ -31,9 +31,9 @@ spec_status_t fail(spec_status_t status, const char* fmt, ...) {
 
 namespace {
 
-constexpr int kKnobs = 2;
-constexpr int kKnobDefault[kKnobs] = {0, kPollLimit};
-std::atomic<int> g_knobs[kKnobs] = {{kKnobDefault[0]}, {kKnobDefault[1]}};
+constexpr int kKnobs = 3;
+constexpr int kKnobDefault[kKnobs] = {0, kPollLimit, 0};
+std::atomic<int> g_knobs[kKnobs] = {{kKnobDefault[0]}, {kKnobDefault[1]}, {kKnobDefault[2]}};
 
 }  // namespace
 
@@ -172,8 +172,9 @@ spec_status_t spec_set_knob(spec_knob_t k, int value) {
   const int i = static_cast<int>(k);
   if (i < 0 || i >= kKnobs) return fail(SPEC_ERR_INVALID_ARG, "unknown knob %d", i);
   if (value < 0) value = kKnobDefault[i];
-  const bool ok = k != SPEC_KNOB_CHUNK_VECTORS ||
-                  (value == 0 || value == 1 || value == 2 || value == 4 || value == 8 || value == 16);
+  const bool ok = k == SPEC_KNOB_CHUNK_VECTORS
+                      ? (value == 0 || value == 1 || value == 2 || value == 4 || value == 8 || value == 16)
+                      : (k != SPEC_KNOB_SINGLE_LAUNCH || value == 0 || value == 1);
   if (!ok) return fail(SPEC_ERR_INVALID_ARG, "value %d is not allowed for knob %d", value, i);
   g_knobs[i].store(value, std::memory_order_relaxed);
   return SPEC_OK;

@@ -51,20 +51,21 @@ __device__ __forceinline__ void stage_tokens(int* s, const int32_t* c, int lo, i
   }
 }
 
-// Proposal of sequence b by a workgroup of NT lanes.  Returns the draft length (0 with no
-// match or an invalid context length) in every lane, and leaves the draft in out_draft[b].
-template <int NT>
+// Proposal of sequence b by a workgroup of NT lanes, through context tiles of TILE tokens.
+// Returns the draft length (0 with no match or an invalid context length) in every lane, and
+// leaves the draft in out_draft[b].
+template <int NT, int TILE = kTile>
 __device__ __forceinline__ int ngram_propose_body(int b, const int32_t* context, const int32_t* context_len,
                                                   int L_max, int n_min, int n_max, int K, int32_t* out_draft,
                                                   int32_t* out_len, int32_t* out_match_n) {
   __shared__ int s_suffix[SPEC_MAX_NGRAM_N];
   __shared__ int s_first[SPEC_MAX_NGRAM_N + 1];
-  __shared__ int s_ctx[kTile + SPEC_MAX_NGRAM_N];
+  __shared__ int s_ctx[TILE + SPEC_MAX_NGRAM_N];
   const int tid = threadIdx.x;
   const int32_t* c = context + static_cast<size_t>(b) * L_max;
   int32_t* od = out_draft + static_cast<size_t>(b) * K;
   const int L = context_len[b];
-  const int pre = min(kTile, L_max);  // the first tile: tokens [0, pre), in bounds whatever L is
+  const int pre = min(TILE, L_max);  // the first tile: tokens [0, pre), in bounds whatever L is
   stage_tokens<NT>(s_ctx, c, 0, pre);
   if (L < 1 || L > L_max) {
     for (int k = tid; k < K; k += NT) od[k] = -1;
@@ -79,9 +80,9 @@ __device__ __forceinline__ int ngram_propose_body(int b, const int32_t* context,
   __syncthreads();  // the first tile is in shared memory
   if (tid < n_max) s_suffix[tid] = tid < L ? (one_tile ? s_ctx[L - 1 - tid] : c[L - 1 - tid]) : 0;
   int reached = 0;  // this lane's longest match so far
-  for (int t0 = 0; t0 <= L - 2; t0 += kTile) {
+  for (int t0 = 0; t0 <= L - 2; t0 += TILE) {
     // end positions e in [t0, t1) need tokens [lo, t1)
-    const int t1 = min(t0 + kTile, L - 1);
+    const int t1 = min(t0 + TILE, L - 1);
     const int lo = max(0, t0 - (n_max - 1));
     __syncthreads();  // the previous tile's comparisons (and the suffix) are done
     if (t0 > 0)  // the first tile, [0, t1) within [0, pre), is already loaded

@@ -47,10 +47,15 @@ spec_status_t spec_timing_entry(int index, const char** name, long long* launche
  *                            (default 262144, at least a quarter of a second); 0 = give
  *                            up before the first poll, so that every sequence that needs
  *                            a wait is flagged (a test of the flag path).
+ *   SPEC_KNOB_SINGLE_LAUNCH  0 (default): spec_verify_chain and spec_ngram_verify run as one
+ *                            launch (plus the packed output's) when the whole grid fits on
+ *                            the device at once; 1: always as separate statistics and
+ *                            draw launches.
  */
 typedef enum spec_knob {
   SPEC_KNOB_CHUNK_VECTORS = 0,
-  SPEC_KNOB_POLL_LIMIT = 1
+  SPEC_KNOB_POLL_LIMIT = 1,
+  SPEC_KNOB_SINGLE_LAUNCH = 2
 } spec_knob_t;
 
 spec_status_t spec_set_knob(spec_knob_t knob, int value);
@@ -66,8 +71,12 @@ int spec_get_knob(spec_knob_t knob);
  * stats workgroup g and words [2G + 6t, 2G + 6t + 5] those of pool task t: start,
  * decision made, own segment masses published (or the piece chosen, for a draw from a
  * target row), siblings' masses gathered (the waiting task), end, and
- * (b << 32) | (c << 8) | mode.  Words of phases a task does not reach are left as they
- * were.  NULL stops the stamping.  Measurement only; the same thread rule as the knobs. */
+ * (b << 32) | (c << 8) | mode.  A call that runs as one launch (SPEC_KNOB_SINGLE_LAUNCH)
+ * stamps its B * (K+1) * C workgroups of sequences instead (w = (b * (K+1) + k) * C + c,
+ * the lookup's workgroups unstamped): words [6w, 6w + 5] are its start, its partials
+ * published, every partial gathered, decision made, draw located (or own segment masses
+ * published) and end.  Words of phases a task does not reach are left as they were.
+ * NULL stops the stamping.  Measurement only; the same thread rule as the knobs. */
 spec_status_t spec_chain_phase_stamps(unsigned long long* buffer, size_t words);
 
 /* Read-only streaming probe in the access shape of the library's streaming passes: one

@@ -90,15 +90,21 @@ const char* spec_last_error(void);
  * sequence over several workgroups that hand partial sums to each other inside one
  * kernel and wait for them.  spec_verify_chain's waiting workgroup only waits for
  * workgroups dispatched before it, which never wait, so its waits end whatever else
- * runs on the device.  The tree walks' workgroups of one sequence wait for each other:
- * a launch holds at most half the workgroups the device runs at once, so one or two
- * such calls in flight together always fit, but more (on other streams, or next to
- * other kernels that wait on their own workgroups) can keep a sequence's workgroups
- * from all running at once.  Every wait is bounded (SPEC_KNOB_POLL_LIMIT in
- * spec_measure.h, at least a quarter of a second by default): a sequence whose wait
- * gives up gets count SPEC_FLAG_TIMED_OUT and -1 in its other outputs, written by the
- * one workgroup that writes the sequence's outputs, so a flag never mixes with a
- * result.  Issue the call again for such sequences. */
+ * runs on the device.  spec_verify_chain and spec_ngram_verify run a small batch (chunks
+ * of 4 vectors a lane, at most 1024 workgroups, and the whole grid resident on the
+ * device at once) as a single launch whose workgroups keep their rows in registers and
+ * each wait for every partial sum of their sequence: there every workgroup but the
+ * sequence's last gives up after a short wait (about 2048 polls) and says so, and the
+ * last one, which waits only for workgroups dispatched before it, then finishes the
+ * sequence from memory; so those waits end as well, only later.  The tree walks'
+ * workgroups of one sequence wait for each other: a launch holds at most half the
+ * workgroups the device runs at once, so one or two such calls in flight together always
+ * fit, but more (on other streams, or next to other kernels that wait on their own
+ * workgroups) can keep a sequence's workgroups from all running at once.  Every wait is
+ * bounded (SPEC_KNOB_POLL_LIMIT in spec_measure.h, at least a quarter of a second by
+ * default): a sequence whose wait gives up gets count SPEC_FLAG_TIMED_OUT and -1 in its
+ * other outputs, written by the one workgroup that writes the sequence's outputs, so a
+ * flag never mixes with a result.  Issue the call again for such sequences. */
 
 /* ---------------------------------------------------------------------------
  * Chain verification by modified rejection sampling.

@@ -155,6 +155,25 @@ def test_knobs_set_get_and_restore(lib):
     bd.spec_set_knob(bd.SPEC_KNOB_POLL_LIMIT, 5)
     bd.spec_set_knob(bd.SPEC_KNOB_POLL_LIMIT, -1)  # negative: back to the default
     assert bd.spec_get_knob(bd.SPEC_KNOB_POLL_LIMIT) == 1 << 18
+    assert bd.spec_get_knob(bd.SPEC_KNOB_SINGLE_LAUNCH) == 0
+    with bd.knob(bd.SPEC_KNOB_SINGLE_LAUNCH, 1):
+        assert bd.spec_get_knob(bd.SPEC_KNOB_SINGLE_LAUNCH) == 1
+    assert bd.spec_get_knob(bd.SPEC_KNOB_SINGLE_LAUNCH) == 0
+    with pytest.raises(bd.SpecError):
+        bd.spec_set_knob(bd.SPEC_KNOB_SINGLE_LAUNCH, 2)  # only 0 and 1
+
+
+def test_workspace_size_covers_the_single_launch_layout(lib):
+    # a shape that may run as one launch needs room for its hand-over words on top of the
+    # separate launches' regions; the size must not depend on whether the single launch is
+    # allowed when it is asked, since a call may be made with the other setting
+    from draft_token_verification_09_amd import binding as bd
+
+    small = bd.spec_verify_chain_workspace_size(1, 5, 32000, 0)
+    with bd.knob(bd.SPEC_KNOB_SINGLE_LAUNCH, 1):
+        assert bd.spec_verify_chain_workspace_size(1, 5, 32000, 0) == small
+    # per sequence at least the partial words (3 words x 512) of the single launch
+    assert small >= 3 * 8 * 512
 
 
 def test_noalloc_refuses_shapes_beyond_its_scratch(lib):

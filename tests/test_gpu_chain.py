@@ -159,14 +159,15 @@ def test_wait_that_gives_up_flags_the_sequence(recipe):
     # sequence whose draw needs the hand-over (a rejection against draft rows) is then
     # flagged -2 with -1 tokens, zero probabilities and no packed tokens; bonus draws need
     # no wait and match the oracle.  With the default limit restored, the same inputs give
-    # the oracle's results.
+    # the oracle's results.  (The separate launches, where only the residual draw waits; in
+    # the single launch every sequence waits for its row statistics, tested on its own.)
     import draft_token_verification_09_amd as sv
 
     inp = (synth.chain_config_high_accept_bf16(6, B=20, V=70000) if recipe == "high"
            else synth.chain_config_low_accept_bf16(6, B=20, K=8, V=70000))
     ref = chain_oracle(inp)
     args = _device_args(inp)
-    with sv.knob(sv.SPEC_KNOB_POLL_LIMIT, 0):
+    with sv.knob(sv.SPEC_KNOB_POLL_LIMIT, 0), sv.knob(sv.SPEC_KNOB_SINGLE_LAUNCH, 1):
         g = sv.spec_verify_chain(*args, want_packed=True)
         torch.cuda.synchronize()
     n = g.num_accepted.cpu().numpy()
