@@ -151,6 +151,7 @@ struct ChainArgs {
   uint64_t* tprop;             // [B, 2K+1] lookup results: draft length, tokens [K], their logits [K]
   uint64_t* status;            // [B, kSingleMaxParts / kWaves] one word per workgroup (see SeqStatus)
   SlotDouble* tmass;           // [B, K, S] slots: residual mass of each segment, should position k reject
+  uint64_t* tdec;              // [B, kFusedDecisionWords] the fused path's decisions
   unsigned long long* stamps;  // phase timestamps (measurement only; see spec_chain_phase_stamps), or null
   size_t stamps_pool;          // index of the pool tasks' first stamp
 };
@@ -1746,6 +1747,281 @@ __global__ __launch_bounds__(kThreads) void chain_single_kernel(ChainArgs a, Ngr
   single_task<DT, NV, VEC, DRAFT>(a, i / per, j / a.C, j % a.C, P > 0);
 }
 
+// ---------------------------------------------------------------- fused path
+//
+// Batches that do not run as a single launch run the statistics and the draw in one launch
+// when each sequence's partials fit in kSingleMaxParts and its pool tasks in the status words:
+// grid = G stats workgroups (in xcd_blocked chunk order, as chain_stats_kernel) and then CP
+// helper workgroups per sequence (as chain_pool_kernel's tasks).  A stats workgroup publishes
+// its wave partials as tagged words (seq_tag).  The sequence's stats workgroup dispatched
+// last (its finisher) then gathers the sequence's partials, waiting only for workgroups
+// dispatched before it, decides (writing the count and the probabilities), publishes the
+// decision as tagged words and finishes a bonus or one-hot draw itself (direct_draw).  The
+// helpers wait for the decision; after a rejection against draft rows they sum, hand over
+// and narrow the residual masses as chain_pool_kernel's tasks do, the last helper waiting for
+// the others.  Every wait is on workgroups dispatched earlier whose own waits end, so every
+// wait ends; the last helper advances the sequence's run counter once every helper has
+// published that it read it (the finisher having read it before deciding, and every stats
+// workgroup whose partials it gathered before publishing them).  A sequence is decided as
+// soon as its own rows are summed, so the draws of the sequences finished early overlap the
+// rest of the pass, and no launch boundary separates the pass from the draws.  The reads and
+// arithmetic are those of the separate launches, whose outputs it gives bit for bit.
+
+constexpr int kFusedDecisionWords = 9;
+// Helpers of one fused launch at most (beyond, the separate launches: measured at B=256, K=8,
+// V=152064 bf16 with 4864 helpers, 234.7 us per call fused against 229.1 separate; at B=64,
+// K=5, V=128256 with 1024, 43.9 against 44.5).
+constexpr long long kFusedMaxHelpers = 2048;
+
+// Dispatch index of chunk g in xcd_blocked order over G workgroups (its inverse).
+__device__ __forceinline__ int xcd_blocked_inverse(int g, int G) {
+  if (G % kXcds != 0) return g;
+  const int blk = G / kXcds;
+  return (g % blk) * kXcds + g / blk;
+}
+
+// Whether chunk g is the last dispatched of its sequence's chunks [g0, g1).
+__device__ __forceinline__ bool last_dispatched(int g, int g0, int g1, int G) {
+  if (G % kXcds != 0) return g == g1 - 1;
+  const int blk = G / kXcds;
+  int best = -1;
+  for (int x = g0 / blk; x <= (g1 - 1) / blk; ++x)  // the sequence's last chunk in each XCD's block
+    best = max(best, xcd_blocked_inverse(min(g1, (x + 1) * blk) - 1, G));
+  return xcd_blocked_inverse(g, G) == best;
+}
+
+// The finisher of sequence b (every lane): gathers, decides, publishes the decision and
+// finishes a direct draw.
+template <int DT, bool VEC>
+__device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t tag) {
+  using EL = Elem<DT>;
+  __shared__ __align__(16) RowStat s_part[kSingleMaxParts];
+  __shared__ int32_t s_tok[SPEC_MAX_K];
+  __shared__ float s_gath[2 * SPEC_MAX_K + 1];
+  __shared__ float s_u[SPEC_MAX_K];
+  __shared__ int s_kb;
+  __shared__ ChainDecision s_dec;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int kb0 = clamped_len(a, b);
+  const bool greedy = is_greedy(a, b);
+  const float T = a.temperature[b];
+  const float uf = a.u_final[b];
+  if (tid < 64) {  // wave 0, lane l: drafted token l, its uniform and its logits
+    int x = -1;
+    float ul = 1.f, gt = 0.f, gd = 0.f;
+    if (lane < a.K) {
+      x = a.tokens[static_cast<size_t>(b) * a.K + lane];
+      ul = a.u_accept[static_cast<size_t>(b) * a.K + lane];
+    }
+    if (!greedy && lane < kb0 && x >= 0 && x < a.V) {
+      gt = EL::value(target_row<DT>(a, b, lane), x);
+      if (a.draft) gd = EL::value(draft_row<DT>(a, b, lane), x);
+    }
+    if (lane < a.K) {
+      s_tok[lane] = x;
+      s_u[lane] = ul;
+    }
+    if (lane < kb0) {
+      s_gath[lane] = gt;
+      if (a.draft) s_gath[a.K + 1 + lane] = gd;
+    }
+    if (lane == 0) s_kb = a.draft_len ? a.draft_len[b] : a.K;
+  }
+  uint64_t* dw = a.tdec + static_cast<size_t>(b) * kFusedDecisionWords;
+  if (!single_gather(a, b, tag, greedy, false, a.poll_limit, s_part, s_tok, s_gath, &s_kb)) {
+    // the wait gave up: flag the sequence (this workgroup alone writes its outputs) and let
+    // the helpers stand down
+    int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+    for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
+    if (a.out_probs)
+      for (int i = tid; i < a.K * 3; i += kThreads) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
+    if (tid == 0) a.out_num[b] = kFlagTimedOut;
+    if (tid < kFusedDecisionWords) put_tagged_u32(dw + tid, tid == 0 ? static_cast<uint32_t>(kModeInvalid) : 0u, tag);
+    return;
+  }
+  const int kb_raw = s_kb;
+  const int kb = kb_raw < 0 ? 0 : (kb_raw > a.K ? a.K : kb_raw);
+  chain_decide<DT>(a, b, kb, SeqInputs{s_part, s_tok, s_gath, s_u, T, uf, kb_raw}, true, &s_dec);
+  const ChainDecision d = uniform_decision(s_dec);
+  if (tid < kFusedDecisionWords) {  // what a residual draw needs
+    const uint64_t st_bits = static_cast<uint64_t>(__double_as_longlong(d.St));
+    const uint32_t v[kFusedDecisionWords] = {
+        static_cast<uint32_t>(d.mode) | (static_cast<uint32_t>(d.n) << 8) | (static_cast<uint32_t>(d.row) << 16),
+        __float_as_uint(d.scale), __float_as_uint(d.Ot), __float_as_uint(d.invSt), __float_as_uint(d.Od),
+        __float_as_uint(d.invSd), __float_as_uint(d.uf), static_cast<uint32_t>(st_bits),
+        static_cast<uint32_t>(st_bits >> 32)};
+    uint32_t mine = v[0];
+#pragma unroll
+    for (int i = 1; i < kFusedDecisionWords; ++i)
+      if (i == tid) mine = v[i];
+    put_tagged_u32(dw + tid, mine, tag);
+  }
+  if (d.mode == kModeBonus || d.mode == kModeOneHot)
+    direct_draw<DT, VEC>(a, b, d, d.mode, target_row<DT>(a, b, d.row), s_part + static_cast<size_t>(d.row) * a.C * kWaves,
+                         s_tok, 0);
+}
+
+// Stats workgroup for chunk g of a fused launch of G stats workgroups.
+template <int DT, int NV, bool VEC>
+__device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G) {
+  const int c = g % a.C;
+  const int rr = (g / a.C) % a.R;
+  const int b = g / (a.C * a.R);
+  const int kb = clamped_len(a, b);
+  const bool greedy = is_greedy(a, b);
+  const bool needed = row_needed(a, rr, kb, greedy);
+  const int g0 = b * a.R * a.C;
+  const bool finisher = last_dispatched(g, g0, g0 + a.R * a.C, G);
+  if (!needed && !finisher) return;
+  const uint32_t tag = seq_tag(a, b);
+  if (needed) {
+    const void* row = rr <= a.K ? target_row<DT>(a, b, rr) : draft_row<DT>(a, b, rr - (a.K + 1));
+    u32x4 raw[NV];
+    load_wave_span<DT, NV, VEC, true>(raw, row, a.V, c);
+    float o;
+    double sv;
+    if (greedy) {
+      int idx;
+      wave_argmax_partial<DT, NV, VEC>(raw, c, a.V, &o, &idx);
+      sv = static_cast<double>(idx);
+    } else {
+      wave_softmax_partial<DT, NV>(raw, kLog2e / a.temperature[b], &o, &sv);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      uint64_t* tp = a.tpart + static_cast<size_t>(b) * (3 * kSingleMaxParts) +
+                     3 * ((static_cast<size_t>(rr) * a.C + c) * kWaves + (threadIdx.x >> 6));
+      put_tagged_u32(tp, __float_as_uint(o), tag);
+      put_tagged_double(tp + 1, sv, tag);
+    }
+  }
+  if (finisher) fused_finish<DT, VEC>(a, b, tag);
+}
+
+// Helper c of CP for sequence b (every lane).
+template <int DT, int SPT, bool VEC>
+__device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, int CP) {
+  constexpr size_t kBufBytes = 2 * SPT * kThreads * sizeof(float) > kSingleMaxParts * sizeof(RowStat)
+                                   ? 2 * SPT * kThreads * sizeof(float)
+                                   : kSingleMaxParts * sizeof(RowStat);
+  __shared__ __align__(16) unsigned char s_buf[kBufBytes];  // per-lane masses, or row n's partials
+  __shared__ uint32_t s_w[kFusedDecisionWords];
+  const int tid = threadIdx.x;
+  const bool last = c == CP - 1;
+  const uint32_t tag = seq_tag(a, b);
+  uint64_t* st = a.status + static_cast<size_t>(b) * (kSingleMaxParts / kWaves);
+  if (!last && tid == 0) put_tagged_u32(st + c, 1u, tag);  // this helper has read the run counter
+  const uint64_t* dw = a.tdec + static_cast<size_t>(b) * kFusedDecisionWords;
+  bool ok = false;
+  for (int polls = 0; polls < a.poll_limit; ++polls) {
+    bool missing = false;
+    if (tid < kFusedDecisionWords) {
+      uint32_t v = 0;
+      if (get_tagged_u32(dw + tid, tag, &v))
+        s_w[tid] = v;
+      else
+        missing = true;
+    }
+    if (!__syncthreads_or(missing)) {
+      ok = true;
+      break;
+    }
+    short_pause();
+  }
+  if (ok && (uniform(static_cast<int>(s_w[0] & 0xff)) == kModeResidual)) {
+    ChainDecision d{};
+    d.mode = kModeResidual;
+    d.n = uniform(static_cast<int>((s_w[0] >> 8) & 0xff));
+    d.row = uniform(static_cast<int>((s_w[0] >> 16) & 0xff));
+    d.excl_tok = -1;
+    d.scale = uniform(__uint_as_float(s_w[1]));
+    d.Ot = uniform(__uint_as_float(s_w[2]));
+    d.invSt = uniform(__uint_as_float(s_w[3]));
+    d.Od = uniform(__uint_as_float(s_w[4]));
+    d.invSd = uniform(__uint_as_float(s_w[5]));
+    d.uf = uniform(__uint_as_float(s_w[6]));
+    d.St = uniform(__longlong_as_double(static_cast<long long>(
+        (static_cast<uint64_t>(s_w[8]) << 32) | static_cast<uint64_t>(s_w[7]))));
+    using EL = Elem<DT>;
+    const void* row_t = target_row<DT>(a, b, d.row);
+    const void* row_d = draft_row<DT>(a, b, d.row);
+    const int32_t* xs = a.tokens + static_cast<size_t>(b) * a.K;
+    // this helper's segments c * SPT .. c * SPT + SPT - 1 (lane t: vector t of each), their
+    // masses as chain_pool_kernel's tasks sum them
+    constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
+    float* red = reinterpret_cast<float*>(s_buf);
+    u32x4 rt[SPT], rd[SPT];
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) rt[j] = load_vector<DT, VEC>(row_t, a.V, (c * SPT + j) * kSeg + tid * EL::kPerVec);
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) rd[j] = load_vector<DT, VEC>(row_d, a.V, (c * SPT + j) * kSeg + tid * EL::kPerVec);
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) red[j * kThreads + tid] = residual_vector_mass<DT>(d, rt[j], rd[j]);
+    __syncthreads();
+    SlotDouble* mw = a.wseg + static_cast<size_t>(b) * a.S;
+    publish_segment_masses(red, SPT, mw + c * SPT, tag);
+    __syncthreads();  // `red` holds the gathered masses next
+    // every helper gathers the masses and locates the draw; the one holding the segment
+    // narrows it from its registers
+    __shared__ int s_outcome, s_usel;
+    __shared__ double s_tloc;
+    if (tid < 64) {
+      const int o = gather_and_locate(a, b, tag, mw, a.S, d.uf, reinterpret_cast<double*>(s_buf), &s_usel, &s_tloc, 0,
+                                      [] { return false; });
+      if (tid == 0) s_outcome = o;
+    }
+    __syncthreads();
+    const int o = s_outcome;
+    if (o == kSlotLocated && s_usel / SPT == c) {
+      const int q = s_usel % SPT;
+      u32x4* stt = reinterpret_cast<u32x4*>(s_buf);
+      u32x4* sdd = stt + kThreads;
+      u32x4 vt = rt[0], vd = rd[0];
+#pragma unroll
+      for (int j = 1; j < SPT; ++j)
+        if (j == q) {
+          vt = rt[j];
+          vd = rd[j];
+        }
+      stt[tid] = vt;
+      sdd[tid] = vd;
+      __syncthreads();
+      narrow_and_emit<DT, VEC>(a, b, d, d.mode, s_usel, s_tloc, row_t, row_d, xs, stt, sdd);
+    }
+    if (o == kSlotNoMass && last) {  // no residual mass after rounding: the last helper draws from p_n
+      RowStat* s_part = reinterpret_cast<RowStat*>(s_buf);
+      single_restage_row(a, b, tag, d.row, s_part);
+      direct_draw<DT, VEC>(a, b, d, kModeFallbackP, row_t, s_part + static_cast<size_t>(d.row) * a.C * kWaves, xs, 0);
+    }
+  } else if (!ok && last) {  // the wait gave up: flag the sequence
+    int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+    for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
+    if (a.out_probs)
+      for (int i = tid; i < a.K * 3; i += kThreads) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
+    if (tid == 0) a.out_num[b] = kFlagTimedOut;
+  }
+  // the last helper advances the sequence's run counter once the other helpers have read it
+  // (lane 0 alone: the other waves may have left)
+  if (last && tid == 0) {
+    for (int t2 = 0; t2 + 1 < CP; ++t2) {
+      uint32_t v;
+      for (int polls = 0; polls < a.poll_limit && !get_tagged_u32(st + t2, tag, &v); ++polls) short_pause();
+    }
+    __hip_atomic_fetch_add(a.epoch + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// grid = G stats workgroups, then B x CP helpers.
+template <int DT, int NV, bool VEC>
+__global__ __launch_bounds__(kThreads) void chain_fused_kernel(ChainArgs a, int G, int CP) {
+  const int i = static_cast<int>(blockIdx.x);
+  if (i < G) {
+    fused_stats<DT, NV, VEC>(a, xcd_blocked(i, G), G);
+    return;
+  }
+  fused_helper<DT, kPoolSegments, VEC>(a, (i - G) / CP, (i - G) % CP, CP);
+}
+
 // grid = 1: offsets and packed tokens of the batch (only when packed output is asked for).
 __global__ __launch_bounds__(kThreads) void chain_pack_kernel(ChainArgs a) { chain_pack(a); }
 
@@ -1758,7 +2034,8 @@ __global__ void write_zero_offset_kernel(int32_t* offsets) {
 struct ChainLayout {
   int nv, C, R, S;
   bool single;  // the shape may take the single-launch path (its regions are laid out)
-  size_t off_gath, off_part, off_wseg, off_epoch, off_tpart, off_tprop, off_status, off_tmass, bytes;
+  bool fused;   // the shape may take the fused path (its regions are laid out)
+  size_t off_gath, off_part, off_wseg, off_epoch, off_tpart, off_tprop, off_status, off_tmass, off_tdec, bytes;
 };
 
 // Vectors per lane in one stats chunk.  The largest chunk (16 vectors for bf16 rows read with
@@ -1834,17 +2111,29 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool ve
   off = align_up(off + sizeof(SlotDouble) * segs, 256);
   // the single-launch path's words, for shapes it may take (the device decides at call time)
   L.single = prefer_single && fits_single(L.nv);
-  if (L.single) {
+  // the fused path: a sequence's partials within kSingleMaxParts and its pool tasks within the
+  // status words
+  const long long cp = one_hot ? 1 : L.S / kPoolSegments;
+  L.fused = prefer_single && static_cast<long long>(rows) * L.C * kWaves <= kSingleMaxParts &&
+            cp <= kSingleMaxParts / kWaves &&
+            static_cast<long long>(B) * (static_cast<long long>(rows) * L.C + cp) <= 2147483647LL;
+  if (L.single || L.fused) {
     L.off_epoch = off;
     off = align_up(off + sizeof(uint32_t) * B, 256);
     L.off_tpart = off;
     off = align_up(off + 3 * sizeof(uint64_t) * static_cast<size_t>(B) * kSingleMaxParts, 256);
-    L.off_tprop = off;
-    off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * (2 * K + 1), 256);
     L.off_status = off;
     off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * (kSingleMaxParts / kWaves), 256);
+  }
+  if (L.single) {
+    L.off_tprop = off;
+    off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * (2 * K + 1), 256);
     L.off_tmass = off;
     off = align_up(off + sizeof(SlotDouble) * static_cast<size_t>(B) * K * L.S, 256);
+  }
+  if (L.fused) {
+    L.off_tdec = off;
+    off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * kFusedDecisionWords, 256);
   }
   L.bytes = off;
   return L;
@@ -1898,7 +2187,7 @@ static spec_status_t launch_chain(ChainArgs a, const NgramArgs* ng, hipStream_t 
   static std::atomic<int> slots_cache[kMaxDevices];
   static std::atomic<int> single_cache[2][kMaxDevices];
   if constexpr (NV == kSingleVectors) {
-    if (a.epoch && knob(SPEC_KNOB_SINGLE_LAUNCH) == 0) {
+    if (a.tmass && knob(SPEC_KNOB_SINGLE_LAUNCH) == 0) {
       // one launch when the whole grid fits on the device at once (with its own stamp layout)
       ChainArgs as = a;
       as.stamps = nullptr;
@@ -1921,6 +2210,20 @@ static spec_status_t launch_chain(ChainArgs a, const NgramArgs* ng, hipStream_t 
         return pack.finish();
       }
     }
+  }
+  if (a.tdec && !ng && !a.stamps && knob(SPEC_KNOB_SINGLE_LAUNCH) == 0 &&
+      static_cast<long long>(a.B) * (a.draft ? a.S / kPoolSegments : 1) <= kFusedMaxHelpers) {
+    // the pass and the draws in one launch: G stats workgroups, then CP helpers a sequence
+    const int G = a.B * a.R * a.C;
+    const int CP = a.draft ? a.S / kPoolSegments : 1;
+    LaunchScope scope("chain_fused", stream);
+    scope.launch(chain_fused_kernel<DT, NV, VEC>, dim3(static_cast<unsigned>(G + a.B * CP)), dim3(kThreads), stream, a,
+                 G, CP);
+    const spec_status_t st = scope.finish();
+    if (st != SPEC_OK || !a.out_packed) return st;
+    LaunchScope pack("chain_pack", stream);
+    pack.launch(chain_pack_kernel, dim3(1), dim3(kThreads), stream, a);
+    return pack.finish();
   }
   {
     const long long g1 = static_cast<long long>(a.B) * a.R * a.C;
@@ -2095,13 +2398,16 @@ static spec_status_t verify_chain_impl(const void* target_logits, const void* dr
   a.gath = reinterpret_cast<float*>(ws + L.off_gath);
   a.part = reinterpret_cast<RowStat*>(ws + L.off_part);
   a.wseg = reinterpret_cast<SlotDouble*>(ws + L.off_wseg);
-  if (L.single) {
+  if (L.single || L.fused) {
     a.epoch = reinterpret_cast<uint32_t*>(ws + L.off_epoch);
     a.tpart = reinterpret_cast<uint64_t*>(ws + L.off_tpart);
-    a.tprop = reinterpret_cast<uint64_t*>(ws + L.off_tprop);
     a.status = reinterpret_cast<uint64_t*>(ws + L.off_status);
+  }
+  if (L.single) {
+    a.tprop = reinterpret_cast<uint64_t*>(ws + L.off_tprop);
     a.tmass = reinterpret_cast<SlotDouble*>(ws + L.off_tmass);
   }
+  if (L.fused) a.tdec = reinterpret_cast<uint64_t*>(ws + L.off_tdec);
 
   if (dtype == SPEC_BF16) return dispatch_chain<kBF16>(L.nv, vec, a, ng, s);
   return dispatch_chain<kF32>(L.nv, vec, a, ng, s);

@@ -1,0 +1,171 @@
+"""The fused path of chain verification (the row statistics and the draws in one launch: each
+sequence decided by its last-dispatched stats workgroup, residual draws finished by helper
+workgroups at the end of the grid, for batches of at most 2048 helpers) against the separate
+launches: bit-identical outputs on the
+same inputs, at full benchmark sizes and on ragged, greedy, invalid and one-hot batches, on a
+dirty workspace reused across shapes and in graph replays; and the flag of a wait that gives
+up."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import chain_oracle, check_packed, compare_chain, f32, i32, log, logits_to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _sv():
+    import draft_token_verification_09_amd as sv
+
+    return sv
+
+
+def _args(inp):
+    return (logits_to_device(inp.target, inp.dtype), None if inp.draft is None else logits_to_device(inp.draft, inp.dtype),
+            i32(inp.tokens), f32(inp.temperature), f32(inp.u_accept), f32(inp.u_final),
+            None if inp.draft_len is None else i32(inp.draft_len))
+
+
+def _kernels_of(call):
+    sv = _sv()
+    sv.spec_timing_reset()
+    sv.spec_timing_enable(True)
+    res = call()
+    torch.cuda.synchronize()
+    sv.spec_timing_enable(False)
+    names = [name for name, _, _ in sv.spec_timing_collect()]
+    sv.spec_timing_reset()
+    return res, names
+
+
+def _fused_vs_separate(inp, ws=None):
+    """The default call (which must take the fused launch) and the separate launches, checked
+    equal bit for bit; returns the fused result."""
+    sv = _sv()
+    args = _args(inp)
+    one, names = _kernels_of(lambda: sv.spec_verify_chain(*args, want_packed=True, workspace_buf=ws))
+    assert names[0] == "chain_fused", names
+    with sv.knob(sv.SPEC_KNOB_SINGLE_LAUNCH, 1):
+        two, names = _kernels_of(lambda: sv.spec_verify_chain(*args, want_packed=True, workspace_buf=ws))
+    assert "chain_stats" in names and "chain_pool" in names, names
+    for name in ("tokens", "num_accepted", "probs", "offsets"):
+        assert torch.equal(getattr(one, name), getattr(two, name)), name
+    total = int(two.offsets[-1])
+    assert torch.equal(one.packed[:total], two.packed[:total])
+    check_packed(one, inp.B)
+    return one
+
+
+CASES = {
+    "headline_B64_K5_V128256": lambda: synth.chain_config_high_accept_bf16(0),
+    "low_accept_B96_K8_V152064": lambda: synth.chain_config_low_accept_bf16(1, B=96),
+    "ragged_B24_K5_V50000": lambda: synth.chain_config_high_accept_bf16(2, B=24, V=50000),
+    "f32_B48_K5_V32000": lambda: synth.chain_config_small_f32(7, B=48),
+    "one_hot_B160_K5_V128256": lambda: dataclasses.replace(
+        synth.chain_config_high_accept_bf16(21, B=160, V=128256), draft=None),
+    "unaligned_B120_K3_V30001": lambda: synth.chain_inputs(9, B=120, K=3, V=30001, dtype="bf16", target_sigma=2.0,
+                                                           draft_sigma=1.5, temperature=0.9),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fused_matches_separate_launches(name):
+    inp = CASES[name]()
+    log(f"[fused] {name}: B={inp.B} K={inp.K} V={inp.V} {inp.dtype}")
+    g = _fused_vs_separate(inp)
+    n = g.num_accepted.cpu().numpy()
+    assert (n >= 0).all()
+    # a sample of sequences against the oracle as well
+    seqs = sorted(set(range(0, inp.B, max(1, inp.B // 6))) | {inp.B - 1})
+    rep = compare_chain(g, chain_oracle(inp, seqs=seqs), inp, seqs=seqs)
+    log(f"[fused]   {rep}")
+    assert rep.ok(), rep.failures[:5]
+
+
+def test_greedy_variable_length_and_invalid_sequences():
+    inp = synth.chain_config_high_accept_bf16(10, B=40, K=5, V=60000)
+    inp.temperature[[1, 4, 30]] = 0.0
+    inp.draft_len = (np.arange(40) % 6).astype(np.int32)
+    inp.draft_len[[3, 17]] = [7, -1]                   # out of range: flagged
+    inp.tokens[5, 0] = 60000                           # out of range (sequence 5 drafts 5 tokens)
+    inp.u_final[7] = 0.0                               # outside (0, 1]
+    g = _fused_vs_separate(inp)
+    n = g.num_accepted.cpu().numpy()
+    for b in (3, 17, 5, 7):
+        assert n[b] == -1, (b, n[b])
+    keep = [b for b in range(40) if b not in (3, 17, 5, 7)]
+    rep = compare_chain(g, chain_oracle(inp, seqs=keep), inp, seqs=keep)
+    assert rep.ok(), rep.failures[:5]
+
+
+def test_dirty_workspace_reused_across_shapes():
+    sv = _sv()
+    shapes = [synth.chain_config_high_accept_bf16(11, B=32, V=128256),
+              synth.chain_config_low_accept_bf16(12, B=20, K=8, V=100000),
+              dataclasses.replace(synth.chain_config_high_accept_bf16(13, B=64, V=64000), draft=None)]
+    need = max(sv.spec_verify_chain_workspace_size(i.B, i.K, i.V, 1) for i in shapes)
+    ws = torch.randint(0, 255, (need + 512,), dtype=torch.uint8, device="cuda:0")
+    for rnd in range(2):
+        for inp in shapes:
+            log(f"[fused] dirty workspace round {rnd}: B={inp.B} K={inp.K} V={inp.V}")
+            _fused_vs_separate(inp, ws)
+
+
+def test_graph_replays_get_new_tags():
+    sv = _sv()
+    inps = [synth.chain_config_low_accept_bf16(40 + s, B=24, K=6, V=90000) for s in range(3)]
+    dev_args = [_args(inp) for inp in inps]
+    static = [x.clone() if x is not None else None for x in dev_args[0]]
+    B, K1, V = static[0].shape
+    out = sv.ChainResult(tokens=torch.empty((B, K1), dtype=torch.int32, device="cuda:0"),
+                         num_accepted=torch.empty((B,), dtype=torch.int32, device="cuda:0"),
+                         probs=torch.empty((B, K1 - 1, 3), dtype=torch.float32, device="cuda:0"),
+                         packed=None, offsets=None)
+    ws = torch.empty(sv.spec_verify_chain_workspace_size(B, K1 - 1, V, 1) + 256, dtype=torch.uint8, device="cuda:0")
+    refs = []
+    for args in dev_args:  # the separate launches' outputs for every input set
+        with sv.knob(sv.SPEC_KNOB_SINGLE_LAUNCH, 1):
+            r = sv.spec_verify_chain(*args)
+        torch.cuda.synchronize()
+        refs.append(r)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sv.spec_verify_chain(*static, out=out, workspace_buf=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.spec_verify_chain(*static, out=out, workspace_buf=ws)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        k = (rep + 1) % 3
+        for dst, src in zip(static, dev_args[k]):
+            if dst is not None:
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        log(f"[fused] graph replay {rep}: input set {k}")
+        for name in ("tokens", "num_accepted", "probs"):
+            assert torch.equal(getattr(out, name), getattr(refs[k], name)), (rep, name)
+
+
+def test_wait_that_gives_up_flags_every_sequence():
+    # poll limit 0 (forced from the host; every workgroup still exits): each finisher's wait for
+    # its sequence's partials gives up at once, so every sequence is flagged -2 with -1 tokens
+    # and zero probabilities; then the default limit gives the separate launches' outputs
+    sv = _sv()
+    inp = synth.chain_config_high_accept_bf16(15, B=32, V=100000)
+    args = _args(inp)
+    with sv.knob(sv.SPEC_KNOB_POLL_LIMIT, 0):
+        g, names = _kernels_of(lambda: sv.spec_verify_chain(*args, want_packed=True))
+    assert names[0] == "chain_fused", names
+    assert (g.num_accepted.cpu().numpy() == sv.FLAG_TIMED_OUT).all()
+    assert (g.tokens.cpu().numpy() == -1).all() and (g.probs.cpu().numpy() == 0).all()
+    assert int(g.offsets[-1]) == 0
+    _fused_vs_separate(inp)
