@@ -10,11 +10,13 @@ distinct input sets whose total exceeds twice the 256 MB last-level cache, so
 every step streams its logits from HBM.
 
 Prints ONE JSON line (rank 0).  `value` is verified draft positions per second
-(B*K per step); `roofline` reports the dominant kernel (chain_stats, the pass that
-reads every logit once) against the MI355X HBM peak, with its duration from HIP events
+(B*K per step); `roofline` reports the dominant kernel (chain_fused: the pass that reads
+every logit once and the draws, in one launch) against the MI355X HBM peak, with its duration from HIP events
 stamped at its own dispatch and completion on its stream (hipExtLaunchKernelGGL), and
 against the achievable read rate (pure reads of the same bytes in the same access
-shape, timed the same way); `roofline.call` gives the whole call's algorithmic rate.
+shape, timed the same way); `roofline.call` gives the whole call's algorithmic rate, and
+`roofline.separate_launches` the same calls with the pass and the draws as separate launches
+(the pass alone against the peak: `stats_pass`).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload, on all
 the cores of this process's share (worker processes) and on one core.  Secondary
 workloads (greedy tree verify, low-acceptance chain, n-gram propose + one-hot verify,
@@ -35,7 +37,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-ROOF_KERNEL = "chain_stats"  # the dominant kernel of a chain call: the pass over every logit
+# the dominant kernel of a chain call: the fused launch (the pass over every logit and the draws)
+# where the call takes it, else the separate statistics pass
+ROOF_KERNELS = ("chain_fused", "chain_stats")
 LLC_BYTES = 256 * 1024 * 1024
 
 
@@ -58,9 +62,14 @@ def source_digest(parts) -> str:
     return h.hexdigest()[:16]
 
 
-# the chain_stats kernel: chain.hip up to its draw section, and the shared device helpers
-STATS_SOURCES = (("draft_token_verification_09_amd/csrc/chain.hip", STATS_END_MARKER),
-                 ("draft_token_verification_09_amd/csrc/device_common.h", None))
+# the chain_stats kernel: chain.hip up to its draw section, and the shared device helpers; the
+# fused kernel: all of chain.hip (it holds the draws too) and the same helpers
+KERNEL_SOURCES = {
+    "chain_stats": (("draft_token_verification_09_amd/csrc/chain.hip", STATS_END_MARKER),
+                    ("draft_token_verification_09_amd/csrc/device_common.h", None)),
+    "chain_fused": (("draft_token_verification_09_amd/csrc/chain.hip", None),
+                    ("draft_token_verification_09_amd/csrc/device_common.h", None)),
+}
 
 
 def read_traffic(kernel: str, workload: str, digest: str):
@@ -174,7 +183,10 @@ def time_calls_median(call, n_sets, warmup, steps, passes=3):
     return sorted(runs)[len(runs) // 2]
 
 
-def bench_chain_workload(make, name, warmup, steps, dev, kernel_timing=True, passes=1):
+def bench_chain_workload(make, name, warmup, steps, dev, kernel_timing=True, passes=1, separate=False):
+    """Times `steps` calls of one chain workload (after `warmup`), rotating input sets.  With
+    `separate`, the same calls are timed again with the statistics and the draws forced into
+    separate launches (SPEC_KNOB_SINGLE_LAUNCH), reported under "separate"."""
     import torch
 
     import draft_token_verification_09_amd as sv
@@ -208,9 +220,16 @@ def bench_chain_workload(make, name, warmup, steps, dev, kernel_timing=True, pas
     kms = {}
     if kernel_timing:
         _, kms = time_calls(call, n_sets, 2, steps, kernel_timing=True)
+    sep = None
+    if separate:
+        progress(f"{name}: timing {steps} calls as separate launches")
+        with sv.knob(sv.SPEC_KNOB_SINGLE_LAUNCH, 1):
+            ms_sep, _ = time_calls(call, n_sets, warmup, steps, kernel_timing=False)
+            _, kms_sep = time_calls(call, n_sets, 2, steps, kernel_timing=True)
+        sep = dict(ms=ms_sep, kernels=kms_sep)
     del sets
     return dict(ms=ms, bytes=per_set, kernels=kms, host=host0, positions=probe.B * probe.K, host_us=host_us,
-                steps=steps)
+                steps=steps, separate=sep)
 
 
 # ---------------------------------------------------------------- CPU baseline (the oracle)
@@ -771,19 +790,21 @@ def main():
 
     workload = "chain_verify_B64_K5_V128256_bf16_high_accept"
     head = bench_chain_workload(lambda s: host0 if s == 0 else synth.chain_config_high_accept_bf16(s), workload,
-                                args.warmup, args.steps, dev)
+                                args.warmup, args.steps, dev, separate=True)
     ms = head["ms"]
     B, K, V = 64, 5, 128256
     positions = B * K
     logits_bytes = B * (2 * K + 1) * V * 2
-    stats_launches, stats_ms = head["kernels"].get(ROOF_KERNEL, (1, float("nan")))
-    stats_avg_s = stats_ms / stats_launches * 1e-3
-    achieved = logits_bytes / stats_avg_s / 1e9
-    digest = source_digest(STATS_SOURCES)
-    traffic = read_traffic(ROOF_KERNEL, "B64_K5_V128256_bf16", digest)
+    roof_kernel = next((k for k in ROOF_KERNELS if k in head["kernels"]), ROOF_KERNELS[-1])
+    launches, kernel_ms = head["kernels"].get(roof_kernel, (1, float("nan")))
+    achieved = logits_bytes / (kernel_ms / launches * 1e-3) / 1e9
+    traffic = read_traffic(roof_kernel, "B64_K5_V128256_bf16", source_digest(KERNEL_SOURCES[roof_kernel]))
     progress("achievable read rate (pure reads in the stats pass's access shape)")
     achievable, by_chunk, probe_bytes = achievable_read(dev, logits_bytes, args.warmup, args.steps)
     call_bytes = head["bytes"]
+    sep = head["separate"]
+    s_launches, s_ms = sep["kernels"].get("chain_stats", (1, float("nan")))
+    s_achieved = logits_bytes / (s_ms / s_launches * 1e-3) / 1e9
 
     result = {
         "metric": "verified draft positions/sec and achieved HBM GB/s (% of peak), 1 MI355X",
@@ -806,7 +827,7 @@ def main():
         "host_issue_us_per_step": round(head["host_us"], 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": ROOF_KERNEL,
+            "kernel": roof_kernel,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -820,6 +841,15 @@ def main():
                      "frac": round(call_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "frac_of_achievable": round(call_bytes / (ms * 1e-3) / 1e9 / achievable, 4),
                      "algorithmic_bytes_per_call": call_bytes},
+            # the same calls with the statistics pass and the draws as separate launches: the
+            # pass over every logit on its own, and the call it makes
+            "separate_launches": {
+                "ms_per_step": round(sep["ms"], 5),
+                "kernels_us_per_call": kernels_per_call(sep["kernels"], args.steps),
+                "stats_pass": {"kernel": "chain_stats", "achieved": round(s_achieved, 1),
+                               "frac": round(s_achieved / HBM_PEAK_GBPS, 4),
+                               "frac_of_achievable": round(s_achieved / achievable, 4)},
+            },
         },
     }
     if pool is not None:

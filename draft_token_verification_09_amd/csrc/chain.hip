@@ -1720,25 +1720,33 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
   stamp(a, sb + kSgEnd);
 }
 
+// The n-gram lookup for sequence i inside a chain launch, through context tiles of TILE tokens
+// in s_ctx (kTileInts<TILE> ints of shared memory): its draft length, tokens and their target
+// logits go out as words tagged with seq_tag (and the lookup's outputs to the caller).
+template <int DT, int TILE>
+__device__ __forceinline__ void lookup_workgroup(const ChainArgs& a, const NgramArgs& ng, int i, int* s_ctx) {
+  int32_t* tokens = const_cast<int32_t*>(a.tokens);
+  const int len = ngram_propose_in<kThreads, TILE>(s_ctx, i, ng.context, ng.context_len, ng.L_max, ng.n_min, ng.n_max,
+                                                   a.K, tokens, const_cast<int32_t*>(a.draft_len), ng.match_n);
+  const uint32_t tag = seq_tag(a, i);
+  uint64_t* w = a.tprop + static_cast<size_t>(i) * (2 * a.K + 1);
+  for (int k = threadIdx.x; k < len; k += kThreads) {  // lane k wrote token k above and reads it back
+    const int x = tokens[static_cast<size_t>(i) * a.K + k];
+    const float g = x >= 0 && x < a.V ? Elem<DT>::value(target_row<DT>(a, i, k), x) : 0.f;
+    put_tagged_u32(w + 1 + k, static_cast<uint32_t>(x), tag);
+    put_tagged_u32(w + 1 + a.K + k, __float_as_uint(g), tag);
+  }
+  if (threadIdx.x == 0) put_tagged_u32(w, static_cast<uint32_t>(len), tag);
+}
+
 // grid = P + B x (K+1) x C: P = B lookup workgroups when the lookup drafts (else 0), then the
 // sequences' workgroups (position k, chunk c).
 template <int DT, int NV, bool VEC, bool DRAFT>
 __global__ __launch_bounds__(kThreads) void chain_single_kernel(ChainArgs a, NgramArgs ng, int P) {
   int i = static_cast<int>(blockIdx.x);
-  if (i < P) {  // the lookup for sequence i, and its results as tagged words
-    int32_t* tokens = const_cast<int32_t*>(a.tokens);
-    const int len = ngram_propose_body<kThreads, kSmallTile>(i, ng.context, ng.context_len, ng.L_max, ng.n_min,
-                                                            ng.n_max, a.K, tokens, const_cast<int32_t*>(a.draft_len),
-                                                            ng.match_n);
-    const uint32_t tag = seq_tag(a, i);
-    uint64_t* w = a.tprop + static_cast<size_t>(i) * (2 * a.K + 1);
-    for (int k = threadIdx.x; k < len; k += kThreads) {  // lane k wrote token k above and reads it back
-      const int x = tokens[static_cast<size_t>(i) * a.K + k];
-      const float g = x >= 0 && x < a.V ? Elem<DT>::value(target_row<DT>(a, i, k), x) : 0.f;
-      put_tagged_u32(w + 1 + k, static_cast<uint32_t>(x), tag);
-      put_tagged_u32(w + 1 + a.K + k, __float_as_uint(g), tag);
-    }
-    if (threadIdx.x == 0) put_tagged_u32(w, static_cast<uint32_t>(len), tag);
+  if (i < P) {
+    __shared__ int s_ctx[kTileInts<kSmallTile>];
+    lookup_workgroup<DT, kSmallTile>(a, ng, i, s_ctx);
     return;
   }
   i -= P;
@@ -1794,11 +1802,10 @@ __device__ __forceinline__ bool last_dispatched(int g, int g0, int g1, int G) {
 }
 
 // The finisher of sequence b (every lane): gathers, decides, publishes the decision and
-// finishes a direct draw.
+// finishes a direct draw.  s_part: shared memory for kSingleMaxParts partials.
 template <int DT, bool VEC>
-__device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t tag) {
+__device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t tag, RowStat* s_part) {
   using EL = Elem<DT>;
-  __shared__ __align__(16) RowStat s_part[kSingleMaxParts];
   __shared__ int32_t s_tok[SPEC_MAX_K];
   __shared__ float s_gath[2 * SPEC_MAX_K + 1];
   __shared__ float s_u[SPEC_MAX_K];
@@ -1865,9 +1872,10 @@ __device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t
                          s_tok, 0);
 }
 
-// Stats workgroup for chunk g of a fused launch of G stats workgroups.
+// Stats workgroup for chunk g of a fused launch of G stats workgroups.  s_mem: the launch's
+// shared buffer.
 template <int DT, int NV, bool VEC>
-__device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G) {
+__device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G, unsigned char* s_mem) {
   const int c = g % a.C;
   const int rr = (g / a.C) % a.R;
   const int b = g / (a.C * a.R);
@@ -1898,16 +1906,15 @@ __device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G) {
       put_tagged_double(tp + 1, sv, tag);
     }
   }
-  if (finisher) fused_finish<DT, VEC>(a, b, tag);
+  if (finisher) fused_finish<DT, VEC>(a, b, tag, reinterpret_cast<RowStat*>(s_mem));
 }
 
 // Helper c of CP for sequence b (every lane).
+// s_buf: the launch's shared buffer (per-lane masses, then a staged segment pair, or row n's
+// partials).
 template <int DT, int SPT, bool VEC>
-__device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, int CP) {
-  constexpr size_t kBufBytes = 2 * SPT * kThreads * sizeof(float) > kSingleMaxParts * sizeof(RowStat)
-                                   ? 2 * SPT * kThreads * sizeof(float)
-                                   : kSingleMaxParts * sizeof(RowStat);
-  __shared__ __align__(16) unsigned char s_buf[kBufBytes];  // per-lane masses, or row n's partials
+__device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, int CP, unsigned char* s_buf) {
+  static_assert(2 * SPT * kThreads * sizeof(float) <= kSingleMaxParts * sizeof(RowStat), "buffer");
   __shared__ uint32_t s_w[kFusedDecisionWords];
   const int tid = threadIdx.x;
   const bool last = c == CP - 1;
@@ -2014,15 +2021,20 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
   }
 }
 
-// grid = G stats workgroups, then B x CP helpers.
+// grid = G stats workgroups, then B x CP helpers.  (With the n-gram lookup's workgroups ahead of
+// them, the finishers taking the drafts from the lookup's tagged words, the prompt-lookup
+// workload ran 22.0 us per call against 20.4 for the lookup beside the separate stats pass:
+// calls that draft by lookup take the separate launches.)
 template <int DT, int NV, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_fused_kernel(ChainArgs a, int G, int CP) {
+  // one buffer for the finisher's partials and the helpers' masses
+  __shared__ __align__(16) unsigned char s_mem[kSingleMaxParts * sizeof(RowStat)];
   const int i = static_cast<int>(blockIdx.x);
   if (i < G) {
-    fused_stats<DT, NV, VEC>(a, xcd_blocked(i, G), G);
+    fused_stats<DT, NV, VEC>(a, xcd_blocked(i, G), G, s_mem);
     return;
   }
-  fused_helper<DT, kPoolSegments, VEC>(a, (i - G) / CP, (i - G) % CP, CP);
+  fused_helper<DT, kPoolSegments, VEC>(a, (i - G) / CP, (i - G) % CP, CP, s_mem);
 }
 
 // grid = 1: offsets and packed tokens of the batch (only when packed output is asked for).

@@ -51,16 +51,19 @@ __device__ __forceinline__ void stage_tokens(int* s, const int32_t* c, int lo, i
   }
 }
 
-// Proposal of sequence b by a workgroup of NT lanes, through context tiles of TILE tokens.
-// Returns the draft length (0 with no match or an invalid context length) in every lane, and
-// leaves the draft in out_draft[b].
-template <int NT, int TILE = kTile>
-__device__ __forceinline__ int ngram_propose_body(int b, const int32_t* context, const int32_t* context_len,
-                                                  int L_max, int n_min, int n_max, int K, int32_t* out_draft,
-                                                  int32_t* out_len, int32_t* out_match_n) {
+// Shared-memory ints a context tile of TILE tokens takes (with the n-gram overlap).
+template <int TILE>
+constexpr int kTileInts = TILE + SPEC_MAX_NGRAM_N;
+
+// Proposal of sequence b by a workgroup of NT lanes, through context tiles of TILE tokens held
+// in s_ctx (shared memory of kTileInts<TILE> ints).  Returns the draft length (0 with no match
+// or an invalid context length) in every lane, and leaves the draft in out_draft[b].
+template <int NT, int TILE>
+__device__ __forceinline__ int ngram_propose_in(int* s_ctx, int b, const int32_t* context, const int32_t* context_len,
+                                                int L_max, int n_min, int n_max, int K, int32_t* out_draft,
+                                                int32_t* out_len, int32_t* out_match_n) {
   __shared__ int s_suffix[SPEC_MAX_NGRAM_N];
   __shared__ int s_first[SPEC_MAX_NGRAM_N + 1];
-  __shared__ int s_ctx[TILE + SPEC_MAX_NGRAM_N];
   const int tid = threadIdx.x;
   const int32_t* c = context + static_cast<size_t>(b) * L_max;
   int32_t* od = out_draft + static_cast<size_t>(b) * K;
@@ -112,6 +115,16 @@ __device__ __forceinline__ int ngram_propose_body(int b, const int32_t* context,
     if (out_match_n) out_match_n[b] = best_n;
   }
   return len;
+}
+
+// The same with the tile in a shared array of its own.
+template <int NT, int TILE = kTile>
+__device__ __forceinline__ int ngram_propose_body(int b, const int32_t* context, const int32_t* context_len,
+                                                  int L_max, int n_min, int n_max, int K, int32_t* out_draft,
+                                                  int32_t* out_len, int32_t* out_match_n) {
+  __shared__ int s_ctx[kTileInts<TILE>];
+  return ngram_propose_in<NT, TILE>(s_ctx, b, context, context_len, L_max, n_min, n_max, K, out_draft, out_len,
+                                    out_match_n);
 }
 
 }  // namespace specv

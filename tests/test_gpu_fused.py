@@ -169,3 +169,4 @@ def test_wait_that_gives_up_flags_every_sequence():
     assert (g.tokens.cpu().numpy() == -1).all() and (g.probs.cpu().numpy() == 0).all()
     assert int(g.offsets[-1]) == 0
     _fused_vs_separate(inp)
+
