@@ -674,6 +674,67 @@ def chain_phases(make, name, warmup, calls, dev, chunk_vectors, pool_segments):
     return "\n".join(lines)
 
 
+def chain_phases_single(make, name, warmup, calls, dev):
+    """Per-phase timeline of chain calls that run as one launch (the single-launch stamp layout:
+    six words per workgroup of the sequences, B x (K+1) x C of them, C from 4-vector chunks):
+    medians over the calls of the latest partials published, the median and latest gather, the
+    median decision, draw located and end, relative to the first workgroup's start, and the last
+    workgroup's end (the call's device time).  Returns a text summary."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_09_amd as sv
+
+    sets = []
+    probe = make(0)
+    for s in range(6):
+        inp = probe if s == 0 else make(s)
+        t = to_dev(inp.target, inp.dtype, dev)
+        d = None if inp.draft is None else to_dev(inp.draft, inp.dtype, dev)
+        f = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        sets.append(sv.prepare_spec_verify_chain(t, d, f(inp.tokens), f(inp.temperature), f(inp.u_accept),
+                                                 f(inp.u_final)))
+    epv = 8 if probe.dtype == "bf16" else 4
+    C = -(-probe.V // (4 * 256 * epv))
+    nw = probe.B * (probe.K + 1) * C
+    buf = torch.full((6 * nw,), -1, dtype=torch.int64, device=dev)
+    for i in range(warmup):
+        sets[i % len(sets)]()
+    torch.cuda.synchronize()
+    keys = ["published_last", "gathered_median", "gathered_last", "decided_median", "located_median", "end_last"]
+    vals = {k: [] for k in keys}
+    for i in range(calls):
+        buf.fill_(-1)
+        torch.cuda.synchronize()
+        sv.spec_chain_phase_stamps(buf)
+        sv.spec_timing_reset()
+        sv.spec_timing_enable(True)
+        sets[(warmup + i) % len(sets)]()
+        torch.cuda.synchronize()
+        sv.spec_timing_enable(False)
+        sv.spec_chain_phase_stamps(None)
+        assert "chain_single" in [k for k, _, _ in sv.spec_timing_collect()], "the call did not run as one launch"
+        st = buf.cpu().numpy().reshape(nw, 6).astype(np.float64)
+        live = st[:, 0] >= 0
+        r = (st - st[live, 0].min()) * 0.01  # 100 MHz ticks -> us
+        r[st < 0] = np.nan
+        vals["published_last"].append(np.nanmax(r[:, 1]))
+        vals["gathered_median"].append(np.nanmedian(r[:, 2]))
+        vals["gathered_last"].append(np.nanmax(r[:, 2]))
+        vals["decided_median"].append(np.nanmedian(r[:, 3]))
+        if np.isfinite(r[:, 4]).any():
+            vals["located_median"].append(np.nanmedian(r[:, 4]))
+        vals["end_last"].append(np.nanmax(r[:, 5]))
+    sv.spec_timing_reset()
+    lines = [f"{name}: one launch, {nw} workgroups (4-vector chunks, C = {C}); {calls} calls after {warmup}; "
+             "us from the first workgroup's start, medians over the calls"]
+    for k in keys:
+        v = vals[k]
+        if v:
+            lines.append(f"  {k:28s} {np.median(v):8.2f}   (min {np.min(v):.2f}, max {np.max(v):.2f})")
+    return "\n".join(lines)
+
+
 def library_chunk_vectors(rows, V, epv, vec, max_chunks=16):
     """The chain stats pass's chunk rule (vectors per lane in one chunk), restated for laying out
     the phase timestamps: the largest chunk giving at least 1024 workgroups with at most
@@ -758,7 +819,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", action="store_true", help="also run the streaming read/copy probes")
     ap.add_argument("--phases", metavar="FILE", help="write a per-phase timeline of chain calls (the library's "
-                    "phase timestamps) for the headline and the low-acceptance workloads to FILE")
+                    "phase timestamps) to FILE: the headline, low-acceptance, B=1 fp32 and one-hot workloads as "
+                    "separate launches, and small batches as single launches")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -875,6 +937,18 @@ def main():
                 chain_phases(lambda s: synth.chain_config_small_f32(s), "chain_verify_B1_K5_V32000_f32",
                              args.warmup, 20, dev, None, 4),
                 chain_phases(one_hot, "chain_verify_one_hot_B128_K5_V32000_bf16", args.warmup, 20, dev, None, 4)]
+
+        def one_hot16(s):
+            inp = synth.chain_config_high_accept_bf16(s, B=16, V=32000)
+            inp.draft = None
+            return inp
+
+        text += ["single launches (the calls' default path at these shapes):",
+                 chain_phases_single(lambda s: synth.chain_config_small_f32(s), "chain_verify_B1_K5_V32000_f32",
+                                     args.warmup, 20, dev),
+                 chain_phases_single(lambda s: synth.chain_config_high_accept_bf16(s, B=8, V=32000),
+                                     "chain_verify_B8_K5_V32000_bf16", args.warmup, 20, dev),
+                 chain_phases_single(one_hot16, "chain_verify_one_hot_B16_K5_V32000_bf16", args.warmup, 20, dev)]
         with open(args.phases, "w") as f:
             f.write("\n\n".join(text) + "\n")
     print(json.dumps(result), flush=True)
