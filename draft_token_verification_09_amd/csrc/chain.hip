@@ -147,9 +147,10 @@ struct ChainArgs {
   int stats_copy;              // the stats pass copies the drafted tokens' logits out (else the lookup does)
   // single-launch path (see chain_single_kernel): hand-over words tagged with seq_tag
   uint32_t* epoch;             // [B] per-sequence run counters
-  uint64_t* tpart;             // [B, kSingleMaxParts, 3] partials ([R, C, kWaves]): o, then s as a tagged double
+  uint64_t* tpart;             // [B, tstride] partials ([R, C, kWaves] of 3 words): o, then s as a tagged double
   uint64_t* tprop;             // [B, 2K+1] lookup results: draft length, tokens [K], their logits [K]
-  uint64_t* status;            // [B, kSingleMaxParts / kWaves] one word per workgroup (see SeqStatus)
+  uint64_t* status;            // [B, sstride] one word per workgroup (see SeqStatus) or helper
+  int tstride, sstride;        // words per sequence in tpart and status
   SlotDouble* tmass;           // [B, K, S] slots: residual mass of each segment, should position k reject
   uint64_t* tdec;              // [B, kFusedDecisionWords] the fused path's decisions
   unsigned long long* stamps;  // phase timestamps (measurement only; see spec_chain_phase_stamps), or null
@@ -1366,7 +1367,7 @@ __device__ __forceinline__ bool single_gather(const ChainArgs& a, int b, uint32_
   const int kb_raw = *s_kb;
   const int kb = kb_raw < 0 ? 0 : (kb_raw > a.K ? a.K : kb_raw);
   // partials of the rows the decision reads (the lookup's case: every target row)
-  const uint64_t* tp = a.tpart + static_cast<size_t>(b) * (3 * kSingleMaxParts);
+  const uint64_t* tp = a.tpart + static_cast<size_t>(b) * a.tstride;
   const int items = a.R * C4;
   unsigned have = 0;  // items tid, tid + kThreads (items <= kSingleMaxParts = 2 * kThreads)
   for (int polls = 0; polls < limit; ++polls) {
@@ -1398,7 +1399,7 @@ __device__ __forceinline__ bool single_gather(const ChainArgs& a, int b, uint32_
 // Copies row `row`'s partials (published, so read without waiting) back into shared memory.
 __device__ __forceinline__ void single_restage_row(const ChainArgs& a, int b, uint32_t tag, int row, RowStat* s_part) {
   const int C4 = a.C * kWaves;
-  const uint64_t* tp = a.tpart + static_cast<size_t>(b) * (3 * kSingleMaxParts) + 3 * static_cast<size_t>(row) * C4;
+  const uint64_t* tp = a.tpart + static_cast<size_t>(b) * a.tstride + 3 * static_cast<size_t>(row) * C4;
   for (int i = threadIdx.x; i < C4; i += kThreads) {
     uint32_t o = 0;
     double sv = 0.0;
@@ -1494,8 +1495,8 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
   const size_t sb = kStampsPerTask * (static_cast<size_t>(b) * nw + j);  // this workgroup's stamps
   stamp(a, sb + kSgStart);
   const uint32_t tag = seq_tag(a, b);
-  uint64_t* tp = a.tpart + static_cast<size_t>(b) * (3 * kSingleMaxParts);
-  uint64_t* st = a.status + static_cast<size_t>(b) * kMaxGroups;
+  uint64_t* tp = a.tpart + static_cast<size_t>(b) * a.tstride;
+  uint64_t* st = a.status + static_cast<size_t>(b) * a.sstride;
   const int S = a.S;
 
   // the decision's scalar inputs and (wave 0, lane l) drafted token l and its uniform first,
@@ -1900,7 +1901,7 @@ __device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G, un
       wave_softmax_partial<DT, NV>(raw, kLog2e / a.temperature[b], &o, &sv);
     }
     if ((threadIdx.x & 63) == 0) {
-      uint64_t* tp = a.tpart + static_cast<size_t>(b) * (3 * kSingleMaxParts) +
+      uint64_t* tp = a.tpart + static_cast<size_t>(b) * a.tstride +
                      3 * ((static_cast<size_t>(rr) * a.C + c) * kWaves + (threadIdx.x >> 6));
       put_tagged_u32(tp, __float_as_uint(o), tag);
       put_tagged_double(tp + 1, sv, tag);
@@ -1919,7 +1920,7 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
   const int tid = threadIdx.x;
   const bool last = c == CP - 1;
   const uint32_t tag = seq_tag(a, b);
-  uint64_t* st = a.status + static_cast<size_t>(b) * (kSingleMaxParts / kWaves);
+  uint64_t* st = a.status + static_cast<size_t>(b) * a.sstride;
   if (!last && tid == 0) put_tagged_u32(st + c, 1u, tag);  // this helper has read the run counter
   const uint64_t* dw = a.tdec + static_cast<size_t>(b) * kFusedDecisionWords;
   bool ok = false;
@@ -2050,6 +2051,7 @@ struct ChainLayout {
   int nv, C, R, S;
   bool single;  // the shape may take the single-launch path (its regions are laid out)
   bool fused;   // the shape may take the fused path (its regions are laid out)
+  int tstride, sstride;  // words per sequence of the tagged partials and of the status words
   size_t off_gath, off_part, off_wseg, off_epoch, off_tpart, off_tprop, off_status, off_tmass, off_tdec, bytes;
 };
 
@@ -2130,15 +2132,18 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool ve
   // status words
   const long long cp = one_hot ? 1 : L.S / kPoolSegments;
   L.fused = prefer_single && static_cast<long long>(rows) * L.C * kWaves <= kSingleMaxParts &&
-            cp <= kSingleMaxParts / kWaves &&
             static_cast<long long>(B) * (static_cast<long long>(rows) * L.C + cp) <= 2147483647LL;
   if (L.single || L.fused) {
+    // a sequence's tagged partials (rows x C chunks x kWaves, 3 words each) and its status words
+    // (one per workgroup of a single launch, one per helper of a fused one)
+    L.tstride = 3 * rows * L.C * kWaves;
+    L.sstride = max((K + 1) * L.C, L.S / kPoolSegments);
     L.off_epoch = off;
     off = align_up(off + sizeof(uint32_t) * B, 256);
     L.off_tpart = off;
-    off = align_up(off + 3 * sizeof(uint64_t) * static_cast<size_t>(B) * kSingleMaxParts, 256);
+    off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * L.tstride, 256);
     L.off_status = off;
-    off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * (kSingleMaxParts / kWaves), 256);
+    off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(B) * L.sstride, 256);
   }
   if (L.single) {
     L.off_tprop = off;
@@ -2152,6 +2157,21 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool ve
   }
   L.bytes = off;
   return L;
+}
+
+// Workspace bytes a chain call of this shape may need: the largest of the layouts it may take
+// (the chunk size depends on the pointers' alignment, on whether draft rows are given and on
+// whether a one-launch path is allowed; one_launch = false leaves the last out).
+static size_t chain_workspace_bytes(int B, int K, int V, spec_dtype_t dtype, bool one_launch) {
+  if (B <= 0 || K < 1 || K > SPEC_MAX_K || V < 1) return 0;
+  size_t bytes = 0;
+  for (int vec = 0; vec < 2; ++vec)
+    for (int one_hot = 0; one_hot < 2; ++one_hot)
+      for (int single = 0; single < (one_launch ? 2 : 1); ++single) {
+        const size_t b = chain_layout(B, K, V, dtype, vec != 0, one_hot != 0, single != 0).bytes;
+        bytes = b > bytes ? b : bytes;
+      }
+  return bytes;
 }
 
 // Pool workgroups the current device holds at once (cached per device).
@@ -2328,17 +2348,7 @@ using namespace specv;
 extern "C" {
 
 size_t spec_verify_chain_workspace_size(int B, int K, int V, spec_dtype_t dtype) {
-  if (B <= 0 || K < 1 || K > SPEC_MAX_K || V < 1) return 0;
-  // any of the chunk sizes may be chosen at call time (they depend on the pointers' alignment,
-  // on whether draft rows are given and on whether the single launch is allowed)
-  size_t bytes = 0;
-  for (int vec = 0; vec < 2; ++vec)
-    for (int one_hot = 0; one_hot < 2; ++one_hot)
-      for (int single = 0; single < 2; ++single) {
-        const size_t b = chain_layout(B, K, V, dtype, vec != 0, one_hot != 0, single != 0).bytes;
-        bytes = b > bytes ? b : bytes;
-      }
-  return bytes;
+  return chain_workspace_bytes(B, K, V, dtype, true);
 }
 
 }  // extern "C"
@@ -2352,7 +2362,7 @@ static spec_status_t verify_chain_impl(const void* target_logits, const void* dr
                                        int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
                                        int32_t* out_packed, int32_t* out_offsets,
                                        void* workspace, size_t workspace_bytes, const NgramArgs* ng,
-                                       spec_stream_t stream) {
+                                       bool one_launch, spec_stream_t stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (B < 0 || K < 1 || V < 1) return fail(SPEC_ERR_INVALID_ARG, "need B >= 0, K >= 1, V >= 1 (got %d, %d, %d)", B, K, V);
@@ -2374,7 +2384,8 @@ static spec_status_t verify_chain_impl(const void* target_logits, const void* dr
     return fail(SPEC_ERR_UNSUPPORTED, "B*(K+1)*V too large");
   const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits) &&
                    (draft_logits == nullptr || aligned16(draft_logits));
-  const ChainLayout L = chain_layout(B, K, V, dtype, vec, draft_logits == nullptr, knob(SPEC_KNOB_SINGLE_LAUNCH) == 0);
+  const ChainLayout L =
+      chain_layout(B, K, V, dtype, vec, draft_logits == nullptr, one_launch && knob(SPEC_KNOB_SINGLE_LAUNCH) == 0);
   const double groups = static_cast<double>(B) * L.R * L.C;
   if (groups > 2147483647.0) return fail(SPEC_ERR_UNSUPPORTED, "grid of %.0f workgroups too large", groups);
   if (L.S > 4 * kThreads)
@@ -2417,6 +2428,8 @@ static spec_status_t verify_chain_impl(const void* target_logits, const void* dr
     a.epoch = reinterpret_cast<uint32_t*>(ws + L.off_epoch);
     a.tpart = reinterpret_cast<uint64_t*>(ws + L.off_tpart);
     a.status = reinterpret_cast<uint64_t*>(ws + L.off_status);
+    a.tstride = L.tstride;
+    a.sstride = L.sstride;
   }
   if (L.single) {
     a.tprop = reinterpret_cast<uint64_t*>(ws + L.off_tprop);
@@ -2439,7 +2452,7 @@ spec_status_t spec_verify_chain(const void* target_logits, const void* draft_log
                                 void* workspace, size_t workspace_bytes, spec_stream_t stream) {
   return verify_chain_impl(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature, u_accept,
                            u_final, B, K, V, out_tokens, out_num_accepted, out_probs, out_packed, out_offsets,
-                           workspace, workspace_bytes, nullptr, stream);
+                           workspace, workspace_bytes, nullptr, true, stream);
 }
 
 spec_status_t spec_ngram_verify(const int32_t* context, const int32_t* context_len, int L_max, int n_min, int n_max,
@@ -2457,7 +2470,7 @@ spec_status_t spec_ngram_verify(const int32_t* context, const int32_t* context_l
   const NgramArgs ng{context, context_len, L_max, n_min, n_max, out_match_n};
   return verify_chain_impl(target_logits, nullptr, dtype, out_draft_tokens, out_draft_len, temperature, u_accept,
                            u_final, B, K, V, out_tokens, out_num_accepted, out_probs, out_packed, out_offsets,
-                           workspace, workspace_bytes, &ng, stream);
+                           workspace, workspace_bytes, &ng, true, stream);
 }
 
 spec_status_t spec_chain_phase_stamps(unsigned long long* buffer, size_t words) {
@@ -2472,7 +2485,9 @@ spec_status_t spec_verify_chain_noalloc(const void* target_logits, const void* d
                                         int B, int K, int V,
                                         int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
                                         int32_t* out_packed, int32_t* out_offsets, spec_stream_t stream) {
-  const size_t need = B > 0 ? spec_verify_chain_workspace_size(B, K, V, dtype) : 0;
+  // the one-launch paths where their hand-over words fit the scratch too, else the separate launches
+  const bool one_launch = chain_workspace_bytes(B, K, V, dtype, true) <= kScratchBytes;
+  const size_t need = chain_workspace_bytes(B, K, V, dtype, false);
   if (need > kScratchBytes)
     return fail(SPEC_ERR_UNSUPPORTED,
                 "B = %d, K = %d, V = %d needs %zu bytes of scratch; the allocation-free call holds %zu", B, K, V, need,
@@ -2480,9 +2495,9 @@ spec_status_t spec_verify_chain_noalloc(const void* target_logits, const void* d
   void* ws = nullptr;
   const spec_status_t st = scratch_address(&ws);
   if (st != SPEC_OK) return st;
-  return spec_verify_chain(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature, u_accept,
+  return verify_chain_impl(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature, u_accept,
                            u_final, B, K, V, out_tokens, out_num_accepted, out_probs, out_packed, out_offsets, ws,
-                           kScratchBytes, stream);
+                           kScratchBytes, nullptr, one_launch, stream);
 }
 
 }  // extern "C"

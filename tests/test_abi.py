@@ -172,8 +172,8 @@ def test_workspace_size_covers_the_single_launch_layout(lib):
     small = bd.spec_verify_chain_workspace_size(1, 5, 32000, 0)
     with bd.knob(bd.SPEC_KNOB_SINGLE_LAUNCH, 1):
         assert bd.spec_verify_chain_workspace_size(1, 5, 32000, 0) == small
-    # per sequence at least the partial words (3 words x 512) of the single launch
-    assert small >= 3 * 8 * 512
+    # at least the single launch's tagged partial words: 3 words for each of 11 rows x 8 chunks x 4 waves
+    assert small >= 3 * 8 * 11 * 8 * 4
 
 
 def test_noalloc_refuses_shapes_beyond_its_scratch(lib):

@@ -53,3 +53,33 @@ def test_noalloc_matches_the_workspace_entry_point_on_two_calls():
         assert rep.ok(), rep.failures[:5]
         check_packed(got, inp.B)
 
+
+
+def test_noalloc_falls_back_to_separate_launches_when_one_launch_words_do_not_fit():
+    # B=2000, K=32, V=2048 bf16: with the one-launch paths' hand-over words the workspace exceeds
+    # the 16 MiB scratch array, without them it fits, so the allocation-free call runs the
+    # separate launches while spec_verify_chain (with its own workspace) takes the fused launch;
+    # the two give the same outputs bit for bit
+    sv = _sv()
+    B, K, V = 2000, 32, 2048
+    assert sv.spec_verify_chain_workspace_size(B, K, V, 1) > 16 << 20
+    inp = synth.chain_inputs(33, B=B, K=K, V=V, dtype="bf16", target_sigma=2.0, draft_sigma=1.0, temperature=1.0)
+    log(f"[noalloc] fallback B={B} K={K} V={V}")
+    args = _args(inp)
+    got = sv.spec_verify_chain_noalloc(*args, out=_out(B, K))
+    sv.spec_timing_reset()
+    sv.spec_timing_enable(True)
+    want = sv.spec_verify_chain(*args, want_packed=True)
+    torch.cuda.synchronize()
+    sv.spec_timing_enable(False)
+    names = [n for n, _, _ in sv.spec_timing_collect()]
+    sv.spec_timing_reset()
+    assert names[0] == "chain_fused", names
+    for name in ("tokens", "num_accepted", "probs", "offsets"):
+        assert torch.equal(getattr(got, name), getattr(want, name)), name
+    total = int(want.offsets[-1])
+    assert torch.equal(got.packed[:total], want.packed[:total])
+    seqs = list(range(0, B, 97)) + [B - 1]
+    rep = compare_chain(got, chain_oracle(inp, seqs=seqs), inp, seqs=seqs)
+    log(f"[noalloc]   {rep}")
+    assert rep.ok(), rep.failures[:5]
