@@ -185,11 +185,15 @@ __device__ __forceinline__ uint32_t pool_generation(const ChainArgs& a) {
 // run is written during the next), and with the address of the launch's dispatch packet in
 // the queue: after a wait gave up, workgroups of the run that start late may read the advanced
 // counter, and the packet address keeps their words apart from those of the next launch.
-__device__ __forceinline__ uint32_t seq_tag(const ChainArgs& a, int b) {
+// (seq_tag_from: the same from a counter value read beforehand, so that the read can go out
+// with a workgroup's streaming loads and be used once they are consumed.)
+__device__ __forceinline__ uint32_t seq_tag_from(const ChainArgs& a, uint32_t run) {
   const uint64_t packet = reinterpret_cast<uint64_t>(__builtin_amdgcn_dispatch_ptr()) >> 6;  // 64-byte packets
-  const uint32_t g = a.gen ^ (static_cast<uint32_t>(packet) * 0x85ebca6bu) ^ (load_agent(a.epoch + b) * 0x9e3779b1u);
+  const uint32_t g = a.gen ^ (static_cast<uint32_t>(packet) * 0x85ebca6bu) ^ (run * 0x9e3779b1u);
   return g != 0u ? g : 0x2545f491u;
 }
+
+__device__ __forceinline__ uint32_t seq_tag(const ChainArgs& a, int b) { return seq_tag_from(a, load_agent(a.epoch + b)); }
 
 template <int DT>
 __device__ __forceinline__ const void* target_row(const ChainArgs& a, int b, int k) {
@@ -203,15 +207,36 @@ __device__ __forceinline__ const void* draft_row(const ChainArgs& a, int b, int 
          (static_cast<size_t>(b) * a.K + k) * static_cast<size_t>(a.V) * Elem<DT>::kBytes;
 }
 
+// An element of a caller's input array.  SCALAR: read through the scalar cache, for an array
+// that no workgroup of the launch writes (not the draft lengths and tokens of a launch whose
+// lookup writes them): with a workgroup-uniform index it is one scalar load, which the
+// sequence's first workgroup brings into the cache for the rest, and which does not queue
+// behind the streaming vector loads in flight on its compute unit.  The fused launch's stats
+// workgroups read their sequence's length and temperature so before their chunk's loads can
+// go out (measured at B=64, K=5, V=128256 bf16: greedy calls 27.5 -> 26.4 us, sampled calls
+// unchanged); the separate stats pass and the single launch keep vector loads, which measured
+// faster there (B=256, K=8, V=152064: 185.8 against 190.7 us for the pass; B=1, K=5,
+// V=32000 fp32: 9.2 against 9.6 us per call).
+template <bool SCALAR = false, class T>
+__device__ __forceinline__ T input_load(const T* p, size_t i) {
+  if (!SCALAR) return p[i];
+  using CT = const __attribute__((address_space(4))) T;
+  return reinterpret_cast<CT*>(reinterpret_cast<uintptr_t>(p))[i];
+}
+
 // Draft length of sequence b clamped to [0, K] (an out-of-range value is flagged later).
+template <bool SCALAR = false>
 __device__ __forceinline__ int clamped_len(const ChainArgs& a, int b) {
   if (!a.draft_len) return a.K;
-  const int v = a.draft_len[b];
+  const int v = input_load<SCALAR>(a.draft_len, b);
   return v < 0 ? 0 : (v > a.K ? a.K : v);
 }
 
 // Temperature 0 selects greedy verification for a sequence.
-__device__ __forceinline__ bool is_greedy(const ChainArgs& a, int b) { return a.temperature[b] == 0.f; }
+template <bool SCALAR = false>
+__device__ __forceinline__ bool is_greedy(const ChainArgs& a, int b) {
+  return input_load<SCALAR>(a.temperature, b) == 0.f;
+}
 
 // Row rr of the stats grid: rr <= K is target row rr, otherwise draft row rr-K-1
 // (draft rows exist only when draft logits are given; then R = 2K+1, else R = K+1; a
@@ -248,9 +273,9 @@ __device__ __forceinline__ SeqInputs seq_inputs(const ChainArgs& a, int b) {
                    a.tokens + static_cast<size_t>(b) * a.K,
                    a.gath + static_cast<size_t>(b) * a.R,
                    a.u_accept + static_cast<size_t>(b) * a.K,
-                   a.temperature[b],
-                   a.u_final[b],
-                   a.draft_len ? a.draft_len[b] : a.K};
+                   input_load(a.temperature, b),
+                   input_load(a.u_final, b),
+                   a.draft_len ? input_load(a.draft_len, b) : a.K};
 }
 
 // No work between the decision's combining of the partials and the decision itself.
@@ -583,7 +608,7 @@ __device__ __forceinline__ void chain_stats_body(const ChainArgs& a, int g, size
     stamp(a, si + 1);
     return;
   }
-  const float scale = kLog2e / a.temperature[b];
+  const float scale = kLog2e / input_load(a.temperature, b);
   // (a run-time test rather than ALL_ROWS: with the copy compiled out, the compiler schedules the
   // pass with 74 instead of 63 VGPRs, 6 instead of 8 waves per SIMD)
   const int pos = a.stats_copy ? row_position(a, rr, kb) : -1;
@@ -1494,15 +1519,14 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
   const bool has_d = DRAFT && has_t && !greedy && k < kb0;
   const size_t sb = kStampsPerTask * (static_cast<size_t>(b) * nw + j);  // this workgroup's stamps
   stamp(a, sb + kSgStart);
-  const uint32_t tag = seq_tag(a, b);
   uint64_t* tp = a.tpart + static_cast<size_t>(b) * a.tstride;
   uint64_t* st = a.status + static_cast<size_t>(b) * a.sstride;
   const int S = a.S;
 
   // the decision's scalar inputs and (wave 0, lane l) drafted token l and its uniform first,
   // then the chunks, then the tokens' logits
-  const float T = a.temperature[b];
-  const float uf = a.u_final[b];
+  const float T = input_load(a.temperature, b);
+  const float uf = input_load(a.u_final, b);
   int x = -1;
   float ul = 1.f;
   if (w == 0 && lane < a.K) {
@@ -1512,11 +1536,14 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
   u32x4 rt[NV], rd[NV];
   if (has_t) load_wave_span<DT, NV, VEC, true>(rt, target_row<DT>(a, b, k), a.V, c);
   if (has_d) load_wave_span<DT, NV, VEC, true>(rd, draft_row<DT>(a, b, k), a.V, c);
-  float gt = 0.f, gd = 0.f;
+  uint32_t gt = 0u, gd = 0u;  // bits, converted when used
   if (!ngram && !greedy && w == 0 && lane < kb0 && x >= 0 && x < a.V) {
-    gt = EL::value(target_row<DT>(a, b, lane), x);
-    if (DRAFT) gd = EL::value(draft_row<DT>(a, b, lane), x);
+    gt = EL::bits(target_row<DT>(a, b, lane), x);
+    if (DRAFT) gd = EL::bits(draft_row<DT>(a, b, lane), x);
   }
+  // the tag's counter read goes out behind the chunks' loads (no load waits for it) and is
+  // used once the partials are made
+  const uint32_t run = load_agent(a.epoch + b);
 
   // this workgroup's partials
   const float scale = kLog2e / T;
@@ -1530,22 +1557,25 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
     } else {
       wave_softmax_partial<DT, NV>(rt, scale, &o, &sv);
     }
+    const uint32_t tg = seq_tag_from(a, run);
     const size_t i = (static_cast<size_t>(k) * C + c) * kWaves + w;
     if (lane == 0) {
-      put_tagged_u32(tp + 3 * i, __float_as_uint(o), tag);
-      put_tagged_double(tp + 3 * i + 1, sv, tag);
+      put_tagged_u32(tp + 3 * i, __float_as_uint(o), tg);
+      put_tagged_double(tp + 3 * i + 1, sv, tg);
     }
   }
   if (has_d) {
     float o;
     double sv;
     wave_softmax_partial<DT, NV>(rd, scale, &o, &sv);
+    const uint32_t tg = seq_tag_from(a, run);
     const size_t i = (static_cast<size_t>(a.K + 1 + k) * C + c) * kWaves + w;
     if (lane == 0) {
-      put_tagged_u32(tp + 3 * i, __float_as_uint(o), tag);
-      put_tagged_double(tp + 3 * i + 1, sv, tag);
+      put_tagged_u32(tp + 3 * i, __float_as_uint(o), tg);
+      put_tagged_double(tp + 3 * i + 1, sv, tg);
     }
   }
+  const uint32_t tag = seq_tag_from(a, run);
   stamp(a, sb + kSgPublished);
 
   // the decision's inputs
@@ -1554,10 +1584,10 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
     if (!ngram) {
       if (lane < a.K) s_tok[lane] = x;
       if (lane < kb0) {
-        s_gath[lane] = gt;
-        if (DRAFT) s_gath[a.K + 1 + lane] = gd;
+        s_gath[lane] = EL::from_bits(gt);
+        if (DRAFT) s_gath[a.K + 1 + lane] = EL::from_bits(gd);
       }
-      if (lane == 0) s_kb = a.draft_len ? a.draft_len[b] : a.K;
+      if (lane == 0) s_kb = a.draft_len ? input_load(a.draft_len, b) : a.K;
     }
   }
   const int limit = anchor ? a.poll_limit : min(a.poll_limit, kShortPolls);
@@ -1802,11 +1832,46 @@ __device__ __forceinline__ bool last_dispatched(int g, int g0, int g1, int G) {
   return xcd_blocked_inverse(g, G) == best;
 }
 
-// The finisher of sequence b (every lane): gathers, decides, publishes the decision and
-// finishes a direct draw.  s_part: shared memory for kSingleMaxParts partials.
-template <int DT, bool VEC>
-__device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t tag, RowStat* s_part) {
+// A finisher's own decision inputs (wave 0, lane l: drafted token l, its accept uniform and
+// the bits of its target and draft logits), fetched in two steps around the loads of its
+// chunk so that the fetches overlap the chunk's streaming: first the tokens and scalars, then
+// (once the chunk's loads are out) the logits at the tokens, converted only when used.
+struct FinisherInputs {
+  int x = -1;
+  float ul = 1.f;
+  uint32_t gt = 0u, gd = 0u;
+  float T = 0.f, uf = 0.f;
+  int kb_raw = 0;
+};
+
+__device__ __forceinline__ void finisher_fetch_tokens(const ChainArgs& a, int b, FinisherInputs* f) {
+  const int lane = threadIdx.x & 63;
+  f->T = input_load(a.temperature, b);
+  f->uf = input_load(a.u_final, b);
+  f->kb_raw = a.draft_len ? input_load(a.draft_len, b) : a.K;
+  if (threadIdx.x < 64 && lane < a.K) {
+    f->x = a.tokens[static_cast<size_t>(b) * a.K + lane];
+    f->ul = a.u_accept[static_cast<size_t>(b) * a.K + lane];
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void finisher_fetch_logits(const ChainArgs& a, int b, int kb0, bool greedy,
+                                                      FinisherInputs* f) {
   using EL = Elem<DT>;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64 && !greedy && lane < kb0 && f->x >= 0 && f->x < a.V) {
+    f->gt = EL::bits(target_row<DT>(a, b, lane), f->x);
+    if (a.draft) f->gd = EL::bits(draft_row<DT>(a, b, lane), f->x);
+  }
+}
+
+// The finisher of sequence b (every lane): gathers, decides, publishes the decision and
+// finishes a direct draw.  s_part: shared memory for kSingleMaxParts partials; f: its inputs
+// as finisher_fetch_tokens and finisher_fetch_logits left them.
+template <int DT, bool VEC>
+__device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t tag, RowStat* s_part,
+                                             const FinisherInputs& f) {
   __shared__ int32_t s_tok[SPEC_MAX_K];
   __shared__ float s_gath[2 * SPEC_MAX_K + 1];
   __shared__ float s_u[SPEC_MAX_K];
@@ -1815,29 +1880,19 @@ __device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int kb0 = clamped_len(a, b);
-  const bool greedy = is_greedy(a, b);
-  const float T = a.temperature[b];
-  const float uf = a.u_final[b];
-  if (tid < 64) {  // wave 0, lane l: drafted token l, its uniform and its logits
-    int x = -1;
-    float ul = 1.f, gt = 0.f, gd = 0.f;
+  const bool greedy = f.T == 0.f;
+  const float T = f.T;
+  const float uf = f.uf;
+  if (tid < 64) {
     if (lane < a.K) {
-      x = a.tokens[static_cast<size_t>(b) * a.K + lane];
-      ul = a.u_accept[static_cast<size_t>(b) * a.K + lane];
-    }
-    if (!greedy && lane < kb0 && x >= 0 && x < a.V) {
-      gt = EL::value(target_row<DT>(a, b, lane), x);
-      if (a.draft) gd = EL::value(draft_row<DT>(a, b, lane), x);
-    }
-    if (lane < a.K) {
-      s_tok[lane] = x;
-      s_u[lane] = ul;
+      s_tok[lane] = f.x;
+      s_u[lane] = f.ul;
     }
     if (lane < kb0) {
-      s_gath[lane] = gt;
-      if (a.draft) s_gath[a.K + 1 + lane] = gd;
+      s_gath[lane] = Elem<DT>::from_bits(f.gt);
+      if (a.draft) s_gath[a.K + 1 + lane] = Elem<DT>::from_bits(f.gd);
     }
-    if (lane == 0) s_kb = a.draft_len ? a.draft_len[b] : a.K;
+    if (lane == 0) s_kb = f.kb_raw;
   }
   uint64_t* dw = a.tdec + static_cast<size_t>(b) * kFusedDecisionWords;
   if (!single_gather(a, b, tag, greedy, false, a.poll_limit, s_part, s_tok, s_gath, &s_kb)) {
@@ -1880,17 +1935,25 @@ __device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G, un
   const int c = g % a.C;
   const int rr = (g / a.C) % a.R;
   const int b = g / (a.C * a.R);
-  const int kb = clamped_len(a, b);
-  const bool greedy = is_greedy(a, b);
+  const int kb = clamped_len<true>(a, b);
+  const bool greedy = is_greedy<true>(a, b);
   const bool needed = row_needed(a, rr, kb, greedy);
   const int g0 = b * a.R * a.C;
   const bool finisher = last_dispatched(g, g0, g0 + a.R * a.C, G);
   if (!needed && !finisher) return;
-  const uint32_t tag = seq_tag(a, b);
+  FinisherInputs f;
+  if (finisher) finisher_fetch_tokens(a, b, &f);
+  u32x4 raw[NV];
   if (needed) {
     const void* row = rr <= a.K ? target_row<DT>(a, b, rr) : draft_row<DT>(a, b, rr - (a.K + 1));
-    u32x4 raw[NV];
     load_wave_span<DT, NV, VEC, true>(raw, row, a.V, c);
+  }
+  if (finisher) finisher_fetch_logits<DT>(a, b, kb, greedy, &f);
+  // the tag's counter read goes out behind the chunk's loads (no load waits for it) and is
+  // used once the partials are made (the sums need not wait for it either)
+  const uint32_t run = load_agent(a.epoch + b);
+  uint32_t tag = 0u;
+  if (needed) {
     float o;
     double sv;
     if (greedy) {
@@ -1898,8 +1961,9 @@ __device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G, un
       wave_argmax_partial<DT, NV, VEC>(raw, c, a.V, &o, &idx);
       sv = static_cast<double>(idx);
     } else {
-      wave_softmax_partial<DT, NV>(raw, kLog2e / a.temperature[b], &o, &sv);
+      wave_softmax_partial<DT, NV>(raw, kLog2e / input_load<true>(a.temperature, b), &o, &sv);
     }
+    tag = seq_tag_from(a, run);
     if ((threadIdx.x & 63) == 0) {
       uint64_t* tp = a.tpart + static_cast<size_t>(b) * a.tstride +
                      3 * ((static_cast<size_t>(rr) * a.C + c) * kWaves + (threadIdx.x >> 6));
@@ -1907,7 +1971,8 @@ __device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G, un
       put_tagged_double(tp + 1, sv, tag);
     }
   }
-  if (finisher) fused_finish<DT, VEC>(a, b, tag, reinterpret_cast<RowStat*>(s_mem));
+  if (!finisher) return;
+  fused_finish<DT, VEC>(a, b, seq_tag_from(a, run), reinterpret_cast<RowStat*>(s_mem), f);
 }
 
 // Helper c of CP for sequence b (every lane).

@@ -41,6 +41,7 @@ struct Elem<kF32> {
   __device__ static __forceinline__ float value(const void* base, size_t idx) {
     return reinterpret_cast<const float*>(base)[idx];
   }
+  __device__ static __forceinline__ float from_bits(uint32_t b) { return __uint_as_float(b); }
   // pack E element bit patterns (already in the low bits) into a vector
   __device__ static __forceinline__ void put(u32x4& v, int i, uint32_t b) { v[i] = b; }
 };
@@ -60,6 +61,7 @@ struct Elem<kBF16> {
   __device__ static __forceinline__ float value(const void* base, size_t idx) {
     return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(base)[idx]) << 16);
   }
+  __device__ static __forceinline__ float from_bits(uint32_t b) { return __uint_as_float(b << 16); }
   __device__ static __forceinline__ void put(u32x4& v, int i, uint32_t b) {
     uint32_t w = v[i >> 1];
     w = (i & 1) ? ((w & 0x0000ffffu) | (b << 16)) : ((w & 0xffff0000u) | b);
@@ -136,6 +138,19 @@ __device__ __forceinline__ u32x4 load_vector(const void* row, int V, int e0) {
   return v;
 }
 
+// Raw buffer descriptor over `bytes` bytes from p (the word-3 value of raw buffer access on
+// this architecture family); loads through it past `bytes` return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), bytes, 0x00020000);
+}
+
+// 16-byte load at byte offset `off` through a buffer descriptor; NT as for load16 (the
+// cache-policy operand's non-temporal bit).
+template <bool NT>
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, NT ? 2 : 0);
+}
+
 // Load chunk `c` of a row so that wave w of the workgroup holds the w-th quarter of it as
 // one contiguous span: vector j of lane l of wave w is element ((w*NV + j)*64 + l)*E of the
 // chunk.  Each wave instruction still reads 1 KiB of contiguous memory.  Elements past V
@@ -148,16 +163,20 @@ __device__ __forceinline__ void load_wave_span(u32x4 (&raw)[NV], const void* row
   const int base = c * ChunkShape<DT, NV>::kChunk;
   const int first = (static_cast<int>(threadIdx.x >> 6) * NV * 64 + static_cast<int>(threadIdx.x & 63));  // vector index
   if (VEC) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
-                                                    static_cast<size_t>(base) * EL::kBytes) + first;
-    if (base + ChunkShape<DT, NV>::kChunk <= V) {
+    // A buffer descriptor spans the chunk's bytes of the row (fewer in a ragged last chunk):
+    // the hardware's range check reads vectors past the row's end as zeros, so every load
+    // issues unconditionally from one 32-bit offset, and those vectors become -inf afterwards.
+    constexpr int kChunkBytes = ChunkShape<DT, NV>::kChunk * EL::kBytes;
+    const long long rem = static_cast<long long>(V - base) * EL::kBytes;
+    const int nrec = rem < kChunkBytes ? static_cast<int>(rem) : kChunkBytes;
+    const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(static_cast<const char*>(row) + static_cast<size_t>(base) * EL::kBytes,
+                                                 nrec);
 #pragma unroll
-      for (int j = 0; j < NV; ++j) raw[j] = load16<NT>(p + j * 64);
-    } else {
+    for (int j = 0; j < NV; ++j) raw[j] = buffer_load16<NT>(rs, (first + j * 64) * 16);
+    if (nrec < kChunkBytes) {
 #pragma unroll
       for (int j = 0; j < NV; ++j)
-        raw[j] = base + (first + j * 64) * E < V ? load16<NT>(p + j * 64)
-                                                 : u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
+        if (base + (first + j * 64) * E >= V) raw[j] = u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
     }
     return;
   }
