@@ -735,6 +735,107 @@ def chain_phases_single(make, name, warmup, calls, dev):
     return "\n".join(lines)
 
 
+def chain_phases_fused(make, name, warmup, calls, dev):
+    """Per-phase timeline of chain calls that run as the fused launch (its stamp layout: two words
+    per stats chunk in sequence/row/chunk order, four per sequence's finisher, seven per helper):
+    per call, the pass's end (the last chunk's partials published) and, for the sequence that
+    ends last, its own last chunk, its finisher's gather and decision, the last of its helpers to
+    see the decision, to publish its masses and to locate the draw, and the draw's end; then the
+    medians over the call's residual draws of each step's duration, and the spread of the eight
+    XCDs' pass ends, and the last workgroup's exit.  us from the first stats workgroup's start,
+    medians over the calls.  Returns
+    a text summary."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_09_amd as sv
+
+    probe = make(0)
+    per_set = chain_bytes(probe)
+    n_sets = sets_needed(per_set)
+    sets, _ = chain_device_sets(make, n_sets, dev)
+    B, K, V = probe.B, probe.K, probe.V
+    epv = 8 if probe.dtype == "bf16" else 4
+    vec = (V * (2 if probe.dtype == "bf16" else 4)) % 16 == 0
+    has_d = probe.draft is not None
+    R = 2 * K + 1 if has_d else K + 1  # rows of a sequence in the stats grid
+    C = -(-V // (library_chunk_vectors(B * R, V, epv, vec) * 256 * epv))
+    S = -(-(-(-V // (256 * epv))) // 4) * 4
+    CP = S // 4 if has_d else 1
+    G = B * R * C
+    code = 1 if probe.dtype == "bf16" else 0
+    ws = torch.empty(sv.spec_verify_chain_workspace_size(B, K, V, code) + 256, dtype=torch.uint8, device=dev)
+    prepared = [sv.prepare_spec_verify_chain(s["t"], s["d"], s["tok"], s["T"], s["ua"], s["uf"], s["dl"],
+                                             workspace_buf=ws) for s in sets]
+    buf = torch.zeros(2 * G + 4 * B + 7 * B * CP, dtype=torch.int64, device=dev)
+    for i in range(warmup):
+        prepared[i % n_sets]()
+    torch.cuda.synchronize()
+    us = 0.01
+    rows = []
+    for i in range(calls):
+        buf.fill_(-1)
+        torch.cuda.synchronize()
+        sv.spec_chain_phase_stamps(buf)
+        sv.spec_timing_reset()
+        sv.spec_timing_enable(True)
+        prepared[(warmup + i) % n_sets]()
+        torch.cuda.synchronize()
+        sv.spec_timing_enable(False)
+        sv.spec_chain_phase_stamps(None)
+        assert "chain_fused" in [k for k, _, _ in sv.spec_timing_collect()], "the call did not run as the fused launch"
+        st = buf.cpu().numpy().astype(np.float64)
+        stats = st[: 2 * G].reshape(G, 2)
+        fin = st[2 * G: 2 * G + 4 * B].reshape(B, 4)
+        hlp = st[2 * G + 4 * B:].reshape(B, CP, 7)
+        t0 = stats[stats[:, 0] >= 0, 0].min()
+        rel = lambda x: np.where(x >= 0, (x - t0) * us, np.nan)
+        s_end = rel(stats[:, 1]).reshape(B, R * C)
+        seq_stats_end = np.nanmax(s_end, axis=1)
+        f_g, f_d, f_e = rel(fin[:, 0]), rel(fin[:, 1]), rel(fin[:, 2])
+        mode = fin[:, 3]
+        seen, pub, loc, nar, ext = (rel(hlp[:, :, j]) for j in (1, 2, 3, 4, 5))
+        res = mode == 1
+        with np.errstate(all="ignore"):
+            import warnings
+            warnings.simplefilter("ignore", RuntimeWarning)
+            seq_end = np.where(res, np.nanmax(nar, axis=1), f_e)
+            crit = int(np.nanargmax(seq_end))
+            r = dict(pass_end=np.nanmax(s_end), call_end=np.nanmax(seq_end), crit_stats_end=seq_stats_end[crit],
+                     crit_gathered=f_g[crit], crit_decided=f_d[crit])
+            if res[crit]:
+                r.update(crit_seen_last=np.nanmax(seen[crit]), crit_published_last=np.nanmax(pub[crit]),
+                         crit_located_last=np.nanmax(loc[crit]))
+            r["crit_end"] = seq_end[crit]
+            r["last_exit"] = max(np.nanmax(ext), np.nanmax(f_e))
+            r["gather"] = np.nanmedian(f_g - seq_stats_end)
+            r["decide"] = np.nanmedian(f_d - f_g)
+            if res.any():
+                sl, pl, ll = np.nanmax(seen[res], axis=1), np.nanmax(pub[res], axis=1), np.nanmax(loc[res], axis=1)
+                r["hand_over"] = np.nanmedian(sl - f_d[res])
+                r["masses"] = np.nanmedian(pl - sl)
+                r["locate"] = np.nanmedian(ll - pl)
+                r["narrow"] = np.nanmedian(np.nanmax(nar[res], axis=1) - ll)
+                r["residual_sequences"] = int(res.sum())
+            if G % 8 == 0:
+                xe = [np.nanmax(s_end.reshape(-1)[x * (G // 8):(x + 1) * (G // 8)]) for x in range(8)]
+                r["xcd_pass_end_spread"] = max(xe) - min(xe)
+        rows.append(r)
+    sv.spec_timing_reset()
+    del prepared, sets
+    torch.cuda.empty_cache()
+    keys = ["pass_end", "crit_stats_end", "crit_gathered", "crit_decided", "crit_seen_last", "crit_published_last",
+            "crit_located_last", "crit_end", "call_end", "last_exit", "gather", "decide", "hand_over", "masses", "locate", "narrow",
+            "residual_sequences", "xcd_pass_end_spread"]
+    lines = [f"{name}: fused launch, {G} stats workgroups ({C} chunks a row), {B * CP} helpers; {calls} calls after "
+             f"{warmup}; us from the first stats workgroup's start, medians over the calls"]
+    for k in keys:
+        vals = [r[k] for r in rows if k in r and np.isfinite(r[k])]
+        if vals:
+            lines.append(f"  {k:28s} {np.median(vals):8.2f}   (min {np.min(vals):.2f}, max {np.max(vals):.2f})")
+    return "\n".join(lines)
+
+
 def library_chunk_vectors(rows, V, epv, vec, max_chunks=16):
     """The chain stats pass's chunk rule (vectors per lane in one chunk), restated for laying out
     the phase timestamps: the largest chunk giving at least 1024 workgroups with at most
@@ -930,7 +1031,11 @@ def main():
             inp.draft = None
             return inp
 
-        text = [chain_phases(lambda s: host0 if s == 0 else synth.chain_config_high_accept_bf16(s), workload,
+        text = ["the default path at the benchmarked shape (one fused launch):",
+                chain_phases_fused(lambda s: host0 if s == 0 else synth.chain_config_high_accept_bf16(s), workload,
+                                   args.warmup, 20, dev),
+                "separate launches (stats pass, then pool kernel):",
+                chain_phases(lambda s: host0 if s == 0 else synth.chain_config_high_accept_bf16(s), workload,
                              args.warmup, 20, dev, None, 4),
                 chain_phases(lambda s: synth.chain_config_low_accept_bf16(s), "chain_verify_B256_K8_V152064_bf16",
                              args.warmup, 20, dev, None, 4),

@@ -166,9 +166,23 @@ enum PoolPhase : int { kPhStart = 0, kPhDecided = 1, kPhPublished = 2, kPhGather
 // Phases of a single-launch workgroup (stamps[kStampsPerTask * w + i] for workgroup w of the
 // sequences' workgroups, in grid order after the lookup's).
 enum SinglePhase : int { kSgStart = 0, kSgPublished = 1, kSgGathered = 2, kSgDecided = 3, kSgDrawn = 4, kSgEnd = 5 };
+// Phases of a fused launch (G stats workgroups, B finishers, B x CP helpers): stats chunk g
+// (sequence, row, chunk order) at stamps[2g] (start) and [2g+1] (partials published); the
+// finisher of sequence b at stamps[2G + kFinisherStamps * b + i]; helper h = b * CP + c at
+// stamps[2G + kFinisherStamps * B + kHelperStamps * h + i].
+constexpr int kFinisherStamps = 4;
+constexpr int kHelperStamps = 7;
+enum FinisherPhase : int { kFnGathered = 0, kFnDecided = 1, kFnEnd = 2, kFnMode = 3 };
+enum HelperPhase : int {
+  kHpStart = 0, kHpSeen = 1, kHpPublished = 2, kHpLocated = 3, kHpNarrowed = 4, kHpExit = 5, kHpInfo = 6
+};
+
+// A stamp base from kNoStamp on writes nothing (callers whose layout has no word for a helper's
+// phase pass it).
+constexpr size_t kNoStamp = ~size_t{0} >> 1;
 
 __device__ __forceinline__ void stamp(const ChainArgs& a, size_t i) {
-  if (a.stamps && threadIdx.x == 0) a.stamps[i] = __builtin_amdgcn_s_memrealtime();
+  if (a.stamps && i < kNoStamp && threadIdx.x == 0) a.stamps[i] = __builtin_amdgcn_s_memrealtime();
 }
 
 // Generation of the slot words of this pool launch (see SlotDouble): the host's number
@@ -1665,7 +1679,7 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
     // every workgroup of position n has published its masses: gather them, locate the draw
     if (w == 0) {
       const int o = gather_and_locate(a, b, tag, tm + static_cast<size_t>(row) * S, S, d.uf,
-                                      reinterpret_cast<double*>(s_buf), &s_usel, &s_tloc, 0, [&] {
+                                      reinterpret_cast<double*>(s_buf), &s_usel, &s_tloc, kNoStamp, [&] {
                                         bool gone = false;
                                         if (lane < C) {
                                           uint32_t v = 0;
@@ -1724,7 +1738,7 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
   const bool all = read_statuses();
   if (direct && !(k == row && c == owner_c) && s_stv[row * C + owner_c] != kStPassed)
     direct_draw<DT, VEC>(a, b, d, mode, target_row<DT>(a, b, row), s_part + static_cast<size_t>(row) * C * kWaves,
-                         s_tok, 0);
+                         s_tok, kNoStamp);
   if (mode == kModeResidual && DRAFT) {
     bool gone = false;
     for (int i = tid; i < C; i += kThreads) gone |= s_stv[row * C + i] != kStPassed;
@@ -1737,12 +1751,12 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
       double t_loc = 0.0;
       for (int cg = 0; cg < S / kPoolSegments; ++cg)
         o = slot_select<DT, kPoolSegments, VEC>(a, b, cg, cg == S / kPoolSegments - 1, d, row_t, row_d, red, &usel,
-                                                &t_loc, 0, g2);
+                                                &t_loc, kNoStamp, g2);
       if (o == kSlotLocated) narrow_and_emit<DT, VEC>(a, b, d, mode, usel, t_loc, row_t, row_d, s_tok);
       if (o == kSlotNoMass) {
         single_restage_row(a, b, tag, row, s_part);
         direct_draw<DT, VEC>(a, b, d, kModeFallbackP, row_t, s_part + static_cast<size_t>(row) * C * kWaves, s_tok,
-                             0);
+                             kNoStamp);
       }
     }
   }
@@ -1895,6 +1909,7 @@ __device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t
     if (lane == 0) s_kb = f.kb_raw;
   }
   uint64_t* dw = a.tdec + static_cast<size_t>(b) * kFusedDecisionWords;
+  const size_t fb = 2 * static_cast<size_t>(a.B) * a.R * a.C + kFinisherStamps * static_cast<size_t>(b);
   if (!single_gather(a, b, tag, greedy, false, a.poll_limit, s_part, s_tok, s_gath, &s_kb)) {
     // the wait gave up: flag the sequence (this workgroup alone writes its outputs) and let
     // the helpers stand down
@@ -1906,6 +1921,7 @@ __device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t
     if (tid < kFusedDecisionWords) put_tagged_u32(dw + tid, tid == 0 ? static_cast<uint32_t>(kModeInvalid) : 0u, tag);
     return;
   }
+  stamp(a, fb + kFnGathered);
   const int kb_raw = s_kb;
   const int kb = kb_raw < 0 ? 0 : (kb_raw > a.K ? a.K : kb_raw);
   chain_decide<DT>(a, b, kb, SeqInputs{s_part, s_tok, s_gath, s_u, T, uf, kb_raw}, true, &s_dec);
@@ -1923,9 +1939,12 @@ __device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t
       if (i == tid) mine = v[i];
     put_tagged_u32(dw + tid, mine, tag);
   }
+  stamp(a, fb + kFnDecided);
   if (d.mode == kModeBonus || d.mode == kModeOneHot)
     direct_draw<DT, VEC>(a, b, d, d.mode, target_row<DT>(a, b, d.row), s_part + static_cast<size_t>(d.row) * a.C * kWaves,
-                         s_tok, 0);
+                         s_tok, kNoStamp);
+  stamp(a, fb + kFnEnd);
+  if (a.stamps && tid == 0) a.stamps[fb + kFnMode] = static_cast<unsigned long long>(d.mode);
 }
 
 // Stats workgroup for chunk g of a fused launch of G stats workgroups.  s_mem: the launch's
@@ -1941,6 +1960,7 @@ __device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G, un
   const int g0 = b * a.R * a.C;
   const bool finisher = last_dispatched(g, g0, g0 + a.R * a.C, G);
   if (!needed && !finisher) return;
+  stamp(a, 2 * static_cast<size_t>(g));
   FinisherInputs f;
   if (finisher) finisher_fetch_tokens(a, b, &f);
   u32x4 raw[NV];
@@ -1971,6 +1991,7 @@ __device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G, un
       put_tagged_double(tp + 1, sv, tag);
     }
   }
+  stamp(a, 2 * static_cast<size_t>(g) + 1);
   if (!finisher) return;
   fused_finish<DT, VEC>(a, b, seq_tag_from(a, run), reinterpret_cast<RowStat*>(s_mem), f);
 }
@@ -1984,10 +2005,22 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
   __shared__ uint32_t s_w[kFusedDecisionWords];
   const int tid = threadIdx.x;
   const bool last = c == CP - 1;
+  const size_t hb = 2 * static_cast<size_t>(a.B) * a.R * a.C + kFinisherStamps * static_cast<size_t>(a.B) +
+                    kHelperStamps * (static_cast<size_t>(b) * CP + c);
+  stamp(a, hb + kHpStart);
   const uint32_t tag = seq_tag(a, b);
   uint64_t* st = a.status + static_cast<size_t>(b) * a.sstride;
   if (!last && tid == 0) put_tagged_u32(st + c, 1u, tag);  // this helper has read the run counter
   const uint64_t* dw = a.tdec + static_cast<size_t>(b) * kFusedDecisionWords;
+  // The last helper's waves 1-3 watch the other helpers' status words while wave 0 waits for
+  // the decision, so that advancing the run counter at the end rarely needs another poll.
+  constexpr int kSeenPer = (kFusedMaxHelpers - 2) / (kThreads - 64) + 1;  // status words a thread watches
+  __shared__ int s_nseen;
+  uint32_t seen = 0u;
+  if (last) {
+    if (tid == 0) s_nseen = 0;
+    __syncthreads();
+  }
   bool ok = false;
   for (int polls = 0; polls < a.poll_limit; ++polls) {
     bool missing = false;
@@ -1998,12 +2031,23 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
       else
         missing = true;
     }
+    if (last && tid >= 64) {
+      for (int j = 0; j < kSeenPer; ++j) {
+        const int i = tid - 64 + j * (kThreads - 64);
+        uint32_t v;
+        if (i < CP - 1 && !(seen >> j & 1u) && get_tagged_u32(st + i, tag, &v)) {
+          seen |= 1u << j;
+          atomicAdd(&s_nseen, 1);
+        }
+      }
+    }
     if (!__syncthreads_or(missing)) {
       ok = true;
       break;
     }
     short_pause();
   }
+  stamp(a, hb + kHpSeen);
   if (ok && (uniform(static_cast<int>(s_w[0] & 0xff)) == kModeResidual)) {
     ChainDecision d{};
     d.mode = kModeResidual;
@@ -2036,18 +2080,23 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
     __syncthreads();
     SlotDouble* mw = a.wseg + static_cast<size_t>(b) * a.S;
     publish_segment_masses(red, SPT, mw + c * SPT, tag);
+    stamp(a, hb + kHpPublished);
     __syncthreads();  // `red` holds the gathered masses next
     // every helper gathers the masses and locates the draw; the one holding the segment
     // narrows it from its registers
     __shared__ int s_outcome, s_usel;
     __shared__ double s_tloc;
     if (tid < 64) {
-      const int o = gather_and_locate(a, b, tag, mw, a.S, d.uf, reinterpret_cast<double*>(s_buf), &s_usel, &s_tloc, 0,
+      const int o = gather_and_locate(a, b, tag, mw, a.S, d.uf, reinterpret_cast<double*>(s_buf), &s_usel, &s_tloc, kNoStamp,
                                       [] { return false; });
       if (tid == 0) s_outcome = o;
     }
     __syncthreads();
+    stamp(a, hb + kHpLocated);
     const int o = s_outcome;
+    if (a.stamps && tid == 0)
+      a.stamps[hb + kHpInfo] = (static_cast<unsigned long long>(b) << 32) | (static_cast<unsigned>(c) << 8) |
+                               static_cast<unsigned>(o == kSlotLocated && s_usel / SPT == c ? 1 : 0);
     if (o == kSlotLocated && s_usel / SPT == c) {
       const int q = s_usel % SPT;
       u32x4* stt = reinterpret_cast<u32x4*>(s_buf);
@@ -2063,11 +2112,13 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
       sdd[tid] = vd;
       __syncthreads();
       narrow_and_emit<DT, VEC>(a, b, d, d.mode, s_usel, s_tloc, row_t, row_d, xs, stt, sdd);
+      stamp(a, hb + kHpNarrowed);
     }
     if (o == kSlotNoMass && last) {  // no residual mass after rounding: the last helper draws from p_n
       RowStat* s_part = reinterpret_cast<RowStat*>(s_buf);
       single_restage_row(a, b, tag, d.row, s_part);
-      direct_draw<DT, VEC>(a, b, d, kModeFallbackP, row_t, s_part + static_cast<size_t>(d.row) * a.C * kWaves, xs, 0);
+      direct_draw<DT, VEC>(a, b, d, kModeFallbackP, row_t, s_part + static_cast<size_t>(d.row) * a.C * kWaves, xs,
+                           kNoStamp);
     }
   } else if (!ok && last) {  // the wait gave up: flag the sequence
     int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
@@ -2077,14 +2128,17 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
     if (tid == 0) a.out_num[b] = kFlagTimedOut;
   }
   // the last helper advances the sequence's run counter once the other helpers have read it
-  // (lane 0 alone: the other waves may have left)
+  // (lane 0 alone: the other waves may have left); the words not seen while it waited (s_nseen
+  // counts those seen, as of the wait's last barrier) are polled now
   if (last && tid == 0) {
-    for (int t2 = 0; t2 + 1 < CP; ++t2) {
-      uint32_t v;
-      for (int polls = 0; polls < a.poll_limit && !get_tagged_u32(st + t2, tag, &v); ++polls) short_pause();
-    }
+    if (s_nseen < CP - 1)
+      for (int t2 = 0; t2 + 1 < CP; ++t2) {
+        uint32_t v;
+        for (int polls = 0; polls < a.poll_limit && !get_tagged_u32(st + t2, tag, &v); ++polls) short_pause();
+      }
     __hip_atomic_fetch_add(a.epoch + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  stamp(a, hb + kHpExit);
 }
 
 // grid = G stats workgroups, then B x CP helpers.  (With the n-gram lookup's workgroups ahead of
@@ -2311,13 +2365,20 @@ static spec_status_t launch_chain(ChainArgs a, const NgramArgs* ng, hipStream_t 
       }
     }
   }
-  if (a.tdec && !ng && !a.stamps && knob(SPEC_KNOB_SINGLE_LAUNCH) == 0 &&
+  if (a.tdec && !ng && knob(SPEC_KNOB_SINGLE_LAUNCH) == 0 &&
       static_cast<long long>(a.B) * (a.draft ? a.S / kPoolSegments : 1) <= kFusedMaxHelpers) {
     // the pass and the draws in one launch: G stats workgroups, then CP helpers a sequence
     const int G = a.B * a.R * a.C;
     const int CP = a.draft ? a.S / kPoolSegments : 1;
+    ChainArgs af = a;  // with the fused launch's own stamp layout
+    af.stamps = nullptr;
+    af.stamps_pool = 0;
+    if (unsigned long long* buf = g_stamps.load(std::memory_order_acquire))
+      if (2 * static_cast<size_t>(G) + kFinisherStamps * static_cast<size_t>(a.B) +
+              kHelperStamps * static_cast<size_t>(a.B) * CP <= g_stamp_words.load(std::memory_order_acquire))
+        af.stamps = buf;
     LaunchScope scope("chain_fused", stream);
-    scope.launch(chain_fused_kernel<DT, NV, VEC>, dim3(static_cast<unsigned>(G + a.B * CP)), dim3(kThreads), stream, a,
+    scope.launch(chain_fused_kernel<DT, NV, VEC>, dim3(static_cast<unsigned>(G + a.B * CP)), dim3(kThreads), stream, af,
                  G, CP);
     const spec_status_t st = scope.finish();
     if (st != SPEC_OK || !a.out_packed) return st;

@@ -75,8 +75,16 @@ int spec_get_knob(spec_knob_t knob);
  * stamps its B * (K+1) * C workgroups of sequences instead (w = (b * (K+1) + k) * C + c,
  * the lookup's workgroups unstamped): words [6w, 6w + 5] are its start, its partials
  * published, every partial gathered, decision made, draw located (or own segment masses
- * published) and end.  Words of phases a task does not reach are left as they were.
- * NULL stops the stamping.  Measurement only; the same thread rule as the knobs. */
+ * published) and end.  A call that runs as the fused launch (statistics and draws in one
+ * launch, with CP helper workgroups a sequence) stamps words [2g, 2g+1] for stats chunk g in
+ * (sequence, row, chunk) order (start, partials published), then four words per sequence b
+ * from 2G + 4b (its finisher's partials gathered, decision published, end, and the decision's
+ * mode), then seven words per helper h = b * CP + c from 2G + 4B + 7h (start, decision seen,
+ * own segment masses published, draw located, drawn segment narrowed and the row written,
+ * exit, and, in a residual draw, (b << 32) | (c << 8) | n with n = 1 for the helper that
+ * narrowed, 0 for the others).  Words of phases a task
+ * does not reach are left as they were.  NULL stops the stamping.  Measurement only; the same
+ * thread rule as the knobs. */
 spec_status_t spec_chain_phase_stamps(unsigned long long* buffer, size_t words);
 
 /* Read-only streaming probe in the access shape of the library's streaming passes: one
