@@ -1824,6 +1824,11 @@ __global__ __launch_bounds__(kThreads) void chain_single_kernel(ChainArgs a, Ngr
 // arithmetic are those of the separate launches, whose outputs it gives bit for bit.
 
 constexpr int kFusedDecisionWords = 9;
+// Reads of a hand-over word kept in flight by a pipelined wait (a wait may make up to that many
+// reads beyond its poll limit), and the pause between starting them (s_sleep 8: 512 clocks,
+// about a quarter of a memory round trip at the end of the pass).
+constexpr int kPollsInFlight = 4;
+__device__ __forceinline__ void stagger_pause() { __builtin_amdgcn_s_sleep(8); }
 // Helpers of one fused launch at most (beyond, the separate launches: measured at B=256, K=8,
 // V=152064 bf16 with 4864 helpers, 234.7 us per call fused against 229.1 separate; at B=64,
 // K=5, V=128256 with 1024, 43.9 against 44.5).
@@ -2012,41 +2017,52 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
   uint64_t* st = a.status + static_cast<size_t>(b) * a.sstride;
   if (!last && tid == 0) put_tagged_u32(st + c, 1u, tag);  // this helper has read the run counter
   const uint64_t* dw = a.tdec + static_cast<size_t>(b) * kFusedDecisionWords;
-  // The last helper's waves 1-3 watch the other helpers' status words while wave 0 waits for
-  // the decision, so that advancing the run counter at the end rarely needs another poll.
-  constexpr int kSeenPer = (kFusedMaxHelpers - 2) / (kThreads - 64) + 1;  // status words a thread watches
-  __shared__ int s_nseen;
-  uint32_t seen = 0u;
-  if (last) {
-    if (tid == 0) s_nseen = 0;
-    __syncthreads();
-  }
-  bool ok = false;
-  for (int polls = 0; polls < a.poll_limit; ++polls) {
-    bool missing = false;
-    if (tid < kFusedDecisionWords) {
-      uint32_t v = 0;
-      if (get_tagged_u32(dw + tid, tag, &v))
-        s_w[tid] = v;
-      else
-        missing = true;
-    }
-    if (last && tid >= 64) {
-      for (int j = 0; j < kSeenPer; ++j) {
-        const int i = tid - 64 + j * (kThreads - 64);
-        uint32_t v;
-        if (i < CP - 1 && !(seen >> j & 1u) && get_tagged_u32(st + i, tag, &v)) {
-          seen |= 1u << j;
-          atomicAdd(&s_nseen, 1);
-        }
+  // Wave 0 waits for the decision words (lanes 0-8) with kPollsInFlight reads of each in flight,
+  // started a quarter of a round trip apart and each reissued as soon as it returns, so that
+  // the words are sampled four times a round trip rather than once; in the last helper, lanes
+  // 9-63 watch the other helpers' status words meanwhile, so that advancing the run counter at
+  // the end rarely needs another poll.  Each read counts as a poll.
+  __shared__ int s_ok, s_nseen;
+  if (tid < 64) {
+    const bool dec_lane = tid < kFusedDecisionWords;
+    const int si = tid - kFusedDecisionWords;  // status word this lane watches
+    const bool st_lane = last && si >= 0 && si < CP - 1;
+    const uint64_t* src = dec_lane ? dw + tid : (st_lane ? st + si : dw);
+    bool got = false, st_seen = false;
+    uint64_t took = 0;
+    if (a.poll_limit > 0) {
+      // (each read is reissued as soon as it is checked, even by the check that ends the wait,
+      // and the limit is checked once a round: so the reads in flight stay in issue order and
+      // each check waits for its own read alone)
+      uint64_t r0 = load_agent(src);
+      stagger_pause();
+      uint64_t r1 = load_agent(src);
+      stagger_pause();
+      uint64_t r2 = load_agent(src);
+      stagger_pause();
+      uint64_t r3 = load_agent(src);
+      auto step = [&](uint64_t& r) {
+        const bool valid = static_cast<uint32_t>(r >> 32) == tag;
+        st_seen |= st_lane && valid;
+        const bool all = __ballot(dec_lane && !valid) == 0ull;
+        if (all) took = r;
+        got |= all;
+        r = load_agent(src);
+        return all;
+      };
+      for (int polls = kPollsInFlight; !(step(r0) || step(r1) || step(r2) || step(r3)) && polls < a.poll_limit;
+           polls += kPollsInFlight) {
       }
     }
-    if (!__syncthreads_or(missing)) {
-      ok = true;
-      break;
+    if (got && dec_lane) s_w[tid] = static_cast<uint32_t>(took);
+    const int nseen = __popcll(__ballot(st_seen));
+    if (tid == 0) {
+      s_ok = got ? 1 : 0;
+      s_nseen = nseen;
     }
-    short_pause();
   }
+  __syncthreads();
+  const bool ok = s_ok != 0;
   stamp(a, hb + kHpSeen);
   if (ok && (uniform(static_cast<int>(s_w[0] & 0xff)) == kModeResidual)) {
     ChainDecision d{};
