@@ -1386,7 +1386,9 @@ __device__ __forceinline__ bool single_gather(const ChainArgs& a, int b, uint32_
       bool missing = false;
       if (tid < len) {
         uint32_t x = 0, g = 0;
-        if (get_tagged_u32(w + 1 + tid, tag, &x) && get_tagged_u32(w + 1 + a.K + tid, tag, &g)) {
+        const bool hx = get_tagged_u32(w + 1 + tid, tag, &x);  // both reads go out before either is checked
+        const bool hg = get_tagged_u32(w + 1 + a.K + tid, tag, &g);
+        if (hx && hg) {
           s_tok[tid] = static_cast<int32_t>(x);
           s_gath[tid] = __uint_as_float(g);
         } else {
@@ -1421,7 +1423,9 @@ __device__ __forceinline__ bool single_gather(const ChainArgs& a, int b, uint32_
         }
         uint32_t o;
         double sv;
-        if (get_tagged_u32(tp + 3 * i, tag, &o) && get_tagged_double(tp + 3 * i + 1, tag, &sv)) {
+        const bool ho = get_tagged_u32(tp + 3 * i, tag, &o);  // all three reads go out before any is checked
+        const bool hs = get_tagged_double(tp + 3 * i + 1, tag, &sv);
+        if (ho && hs) {
           s_part[i] = RowStat{__uint_as_float(o), 0.f, sv};
           have |= 1u << j;
         } else {
