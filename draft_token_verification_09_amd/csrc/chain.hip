@@ -144,6 +144,8 @@ struct ChainArgs {
   RowStat* part;        // [B, R, C, 4] partials, one per wave of each chunk
   float* gath;          // [B, R] logit of the drafted token in each scoring row
   SlotDouble* wseg;     // [B, S] slots: mass of the final draw's weights per segment
+  ChainDecision* decs;  // [B] decisions of chain_decide_kernel for the pool kernel
+  int decided;          // the pool reads its decisions from decs (else it decides itself)
   int stats_copy;              // the stats pass copies the drafted tokens' logits out (else the lookup does)
   // single-launch path (see chain_single_kernel): hand-over words tagged with seq_tag
   uint32_t* epoch;             // [B] per-sequence run counters
@@ -1278,7 +1280,12 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   const size_t sb = a.stamps_pool + kStampsPerTask * (static_cast<size_t>(b0) * CP + gi);
   stamp(a, sb + kPhStart);
 
-  chain_decide<DT>(a, b, clamped_len(a, b), seq_inputs(a, b), last, &s_dec);
+  if (a.decided) {  // decided by chain_decide_kernel, which also wrote the count and probabilities
+    if (tid == 0) s_dec = a.decs[b];
+    __syncthreads();
+  } else {
+    chain_decide<DT>(a, b, clamped_len(a, b), seq_inputs(a, b), last, &s_dec);
+  }
   const ChainDecision d = uniform_decision(s_dec);
   stamp(a, sb + kPhDecided);
   if (a.stamps && tid == 0)
@@ -1312,6 +1319,19 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   direct_draw<DT, VEC>(a, b, d, mode, row_t, a.part + (static_cast<size_t>(b) * a.R + d.row) * a.C * kWaves,
                        a.tokens + static_cast<size_t>(b) * a.K, sb);
   stamp(a, sb + kPhEnd);
+}
+
+// grid = B: sequence b's decision, as chain_pool_kernel's tasks would each take it, once, for the
+// pool kernel that follows (which then only reads it): count, probabilities and a -1 row for
+// invalid input written here.  Used where a sequence has several pool tasks (draft rows given):
+// at B=256, K=8, V=152064 the 4864 tasks, 1792 of them resident at a time, each combined the
+// sequence's 340 partials before it could start its draw.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainArgs a) {
+  __shared__ ChainDecision s_dec;
+  const int b = static_cast<int>(blockIdx.x);
+  chain_decide<DT>(a, b, clamped_len(a, b), seq_inputs(a, b), true, &s_dec);
+  if (threadIdx.x == 0) a.decs[b] = s_dec;
 }
 
 // ---------------------------------------------------------------- single-launch path
@@ -2191,7 +2211,8 @@ struct ChainLayout {
   bool single;  // the shape may take the single-launch path (its regions are laid out)
   bool fused;   // the shape may take the fused path (its regions are laid out)
   int tstride, sstride;  // words per sequence of the tagged partials and of the status words
-  size_t off_gath, off_part, off_wseg, off_epoch, off_tpart, off_tprop, off_status, off_tmass, off_tdec, bytes;
+  size_t off_gath, off_part, off_wseg, off_decs, off_epoch, off_tpart, off_tprop, off_status, off_tmass, off_tdec,
+      bytes;
 };
 
 // Vectors per lane in one stats chunk.  The largest chunk (16 vectors for bf16 rows read with
@@ -2265,6 +2286,8 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool ve
   off = align_up(off + sizeof(RowStat) * static_cast<size_t>(B) * L.R * L.C * kWaves, 256);
   L.off_wseg = off;
   off = align_up(off + sizeof(SlotDouble) * segs, 256);
+  L.off_decs = off;
+  off = align_up(off + sizeof(ChainDecision) * static_cast<size_t>(B), 256);
   // the single-launch path's words, for shapes it may take (the device decides at call time)
   L.single = prefer_single && fits_single(L.nv);
   // the fused path: a sequence's partials within kSingleMaxParts and its pool tasks within the
@@ -2424,6 +2447,17 @@ static spec_status_t launch_chain(ChainArgs a, const NgramArgs* ng, hipStream_t 
   {
     const auto kernel = chain_pool_kernel<DT, kPoolSegments, VEC>;
     const int CP = a.draft ? a.S / kPoolSegments : 1;  // tasks per sequence
+    // More pool tasks than fit at once: one decision a sequence beforehand, which the tasks read
+    // (measured at B=256, K=8, V=152064: pool 43.1 -> 33.7 us plus 4.2 for the decisions, 230.0 ->
+    // 225.3 us per call; at B=64, K=5, V=128256, whose 1024 tasks all fit, 12.8 -> 11.7 plus 4.2)
+    if (a.draft && a.decs &&
+        static_cast<long long>(a.B) * CP > pool_slots(reinterpret_cast<const void*>(kernel), slots_cache)) {
+      LaunchScope scope("chain_decide", stream);
+      scope.launch(chain_decide_kernel<DT>, dim3(static_cast<unsigned>(a.B)), dim3(kThreads), stream, a);
+      const spec_status_t st = scope.finish();
+      if (st != SPEC_OK) return st;
+      a.decided = 1;
+    }
     // one waiting task per sequence: at most half as many sequences per launch as fit at once
     const int per_launch = max(1, pool_slots(reinterpret_cast<const void*>(kernel), slots_cache) / 2);
     for (int b0 = 0; b0 < a.B; b0 += per_launch) {
@@ -2570,6 +2604,8 @@ static spec_status_t verify_chain_impl(const void* target_logits, const void* dr
   a.gath = reinterpret_cast<float*>(ws + L.off_gath);
   a.part = reinterpret_cast<RowStat*>(ws + L.off_part);
   a.wseg = reinterpret_cast<SlotDouble*>(ws + L.off_wseg);
+  a.decs = reinterpret_cast<ChainDecision*>(ws + L.off_decs);
+  a.decided = 0;
   if (L.single || L.fused) {
     a.epoch = reinterpret_cast<uint32_t*>(ws + L.off_epoch);
     a.tpart = reinterpret_cast<uint64_t*>(ws + L.off_tpart);
