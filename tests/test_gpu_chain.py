@@ -228,3 +228,27 @@ def test_graph_replays_match_eager_calls():
         assert torch.equal(out.probs, eager.probs)
         rep_ = compare_chain(out, chain_oracle(inps[k]), inps[k])
         assert rep_.ok(), rep_.failures[:5]
+
+
+def test_oversubscribed_pool_decides_once():
+    # separate launches whose pool tasks outnumber the pool kernel's resident slots take each
+    # sequence's decision once (chain_decide) before the pool: B=250, K=8, V=80000 gives 2500
+    # tasks (10 a sequence), more than fit at once and more helpers than the fused launch takes
+    import draft_token_verification_09_amd as sv
+
+    inp = synth.chain_config_low_accept_bf16(8, B=250, K=8, V=80000)
+    args = _device_args(inp)
+    sv.spec_timing_reset()
+    sv.spec_timing_enable(True)
+    g = sv.spec_verify_chain(*args, want_packed=True)
+    torch.cuda.synchronize()
+    sv.spec_timing_enable(False)
+    names = [name for name, _, _ in sv.spec_timing_collect()]
+    sv.spec_timing_reset()
+    log(f"[chain] B=250 K=8 V=80000 launches: {names}")
+    assert names[:3] == ["chain_stats", "chain_decide", "chain_pool"], names
+    seqs = sorted(set(list(range(0, inp.B, 9)) + [inp.B - 1]))
+    rep = compare_chain(g, chain_oracle(inp, seqs=seqs), inp, seqs=seqs)
+    log(f"[chain]   {rep}")
+    assert rep.ok(), rep.failures[:5]
+    check_packed(g, inp.B)

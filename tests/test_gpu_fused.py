@@ -170,3 +170,48 @@ def test_wait_that_gives_up_flags_every_sequence():
     assert int(g.offsets[-1]) == 0
     _fused_vs_separate(inp)
 
+
+
+def test_phase_stamps_of_the_fused_launch():
+    # the fused launch's stamp layout (spec_chain_phase_stamps): 2 words per stats chunk in
+    # (sequence, row, chunk) order, 4 per finisher, 7 per helper; with 16-vector chunks forced,
+    # C = ceil(V / 32768) and CP = S / 4 helpers a sequence.  Every stamped phase is ordered
+    # (start <= end), every finisher records its decision's mode (1 for a residual draw, 2 for a
+    # bonus draw) and every helper its start and exit; the outputs are those of an unstamped call
+    sv = _sv()
+    inp = synth.chain_config_high_accept_bf16(31, B=40, K=5, V=50000)
+    args = _args(inp)
+    B, K, V = inp.B, inp.K, inp.V
+    R, C = 2 * K + 1, -(-V // 32768)
+    S = -(-(-(-V // 2048)) // 4) * 4
+    CP = S // 4
+    G = B * R * C
+    buf = torch.full((2 * G + 4 * B + 7 * B * CP,), -1, dtype=torch.int64, device="cuda:0")
+    with sv.knob(sv.SPEC_KNOB_CHUNK_VECTORS, 16):
+        plain, _ = _kernels_of(lambda: sv.spec_verify_chain(*args))
+        sv.spec_chain_phase_stamps(buf)
+        try:
+            g, names = _kernels_of(lambda: sv.spec_verify_chain(*args))
+        finally:
+            sv.spec_chain_phase_stamps(None)
+    assert names[0] == "chain_fused", names
+    for name in ("tokens", "num_accepted", "probs"):
+        assert torch.equal(getattr(g, name), getattr(plain, name)), name
+    st = buf.cpu().numpy()
+    stats = st[: 2 * G].reshape(B, R * C, 2)
+    fin = st[2 * G: 2 * G + 4 * B].reshape(B, 4)
+    hlp = st[2 * G + 4 * B:].reshape(B, CP, 7)
+    n = g.num_accepted.cpu().numpy()
+    for b in range(B):
+        live = stats[b, :, 0] >= 0
+        assert live.sum() >= (K + 1) * C, b  # every target row's chunks at least (draft rows: kb of them)
+        assert (stats[b, live, 1] >= stats[b, live, 0]).all(), b
+        assert 0 <= fin[b, 0] <= fin[b, 1] <= fin[b, 2], (b, fin[b])
+        assert fin[b, 3] == (1 if n[b] < K else 2), (b, fin[b, 3], n[b])
+        assert (hlp[b, :, 0] >= 0).all() and (hlp[b, :, 5] >= hlp[b, :, 0]).all(), b
+        if n[b] < K:  # a residual draw: every helper located it, one narrowed it
+            assert (hlp[b, :, 3] >= hlp[b, :, 1]).all(), b
+            owners = (hlp[b, :, 6] & 0xFF) == 1
+            assert owners.sum() == 1 and hlp[b, owners, 4][0] >= hlp[b, owners, 3][0], b
+            assert ((hlp[b, :, 6] >> 32) == b).all() and (((hlp[b, :, 6] >> 8) & 0xFFFFFF) == np.arange(CP)).all(), b
+    log(f"[fused] stamps: {int((n < K).sum())} residual draws, {int((n == K).sum())} bonus draws")
