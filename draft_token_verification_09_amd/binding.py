@@ -27,6 +27,7 @@ SPEC_MAX_NGRAM_N = 16
 SPEC_KNOB_CHUNK_VECTORS = 0
 SPEC_KNOB_POLL_LIMIT = 1
 SPEC_KNOB_SINGLE_LAUNCH = 2
+SPEC_KNOB_XCD_LOCAL = 3
 FLAG_INVALID = -1    # count output of a sequence with invalid device data
 FLAG_TIMED_OUT = -2  # count output of a sequence whose hand-over wait gave up
 

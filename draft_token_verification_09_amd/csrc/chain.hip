@@ -72,7 +72,9 @@ struct SlotDouble {
   uint64_t lo, hi;
 };
 
-__device__ __forceinline__ void put_slot(SlotDouble* p, double v, uint32_t gen) { put_tagged_double(&p->lo, v, gen); }
+__device__ __forceinline__ void put_slot(SlotDouble* p, double v, uint32_t gen, bool local = false) {
+  put_tagged_double(&p->lo, v, gen, local);
+}
 
 // Reads a slot; false if it has not been written during this call.
 __device__ __forceinline__ bool get_slot(const SlotDouble* p, uint32_t gen, double* v) {
@@ -146,6 +148,7 @@ struct ChainArgs {
   SlotDouble* wseg;     // [B, S] slots: mass of the final draw's weights per segment
   ChainDecision* decs;  // [B] decisions of chain_decide_kernel for the pool kernel
   int decided;          // the pool reads its decisions from decs (else it decides itself)
+  int xcd_local;        // fused launch: each sequence's workgroups share an XCD, hand-overs stay in its L2
   int stats_copy;              // the stats pass copies the drafted tokens' logits out (else the lookup does)
   // single-launch path (see chain_single_kernel): hand-over words tagged with seq_tag
   uint32_t* epoch;             // [B] per-sequence run counters
@@ -1101,7 +1104,8 @@ __device__ __forceinline__ float residual_vector_mass(const ChainDecision& d, co
 // segment q's vector t, in fp64 (one 16-lane row of the workgroup sums one segment: lane r
 // adds vectors 16 r .. 16 r + 15 in order, then the row's inclusive sum), published in slots
 // mw[0 .. nseg) with tag `gen`.  Every lane calls it; nseg <= kThreads / 16.
-__device__ __forceinline__ void publish_segment_masses(const float* red, int nseg, SlotDouble* mw, uint32_t gen) {
+__device__ __forceinline__ void publish_segment_masses(const float* red, int nseg, SlotDouble* mw, uint32_t gen,
+                                                       bool local = false) {
   const int q = threadIdx.x >> 4;  // q < nseg: segment q
   const int r = threadIdx.x & 15;
   double v = 0.0;
@@ -1111,7 +1115,7 @@ __device__ __forceinline__ void publish_segment_masses(const float* red, int nse
     for (int i = 0; i < 16; ++i) v += static_cast<double>(src[i]);
   }
   v = row16_inclusive_sum(v);
-  if (q < nseg && r == 15) put_slot(mw + q, v, gen);
+  if (q < nseg && r == 15) put_slot(mw + q, v, gen, local);
 }
 
 // Residual draw after a rejection against draft rows (see chain_pool_kernel, steps 1-3):
@@ -1913,7 +1917,7 @@ __device__ __forceinline__ void finisher_fetch_logits(const ChainArgs& a, int b,
 // finishes a direct draw.  s_part: shared memory for kSingleMaxParts partials; f: its inputs
 // as finisher_fetch_tokens and finisher_fetch_logits left them.
 template <int DT, bool VEC>
-__device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t tag, RowStat* s_part,
+__device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t tag, bool local, RowStat* s_part,
                                              const FinisherInputs& f) {
   __shared__ int32_t s_tok[SPEC_MAX_K];
   __shared__ float s_gath[2 * SPEC_MAX_K + 1];
@@ -1947,7 +1951,8 @@ __device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t
     if (a.out_probs)
       for (int i = tid; i < a.K * 3; i += kThreads) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
     if (tid == 0) a.out_num[b] = kFlagTimedOut;
-    if (tid < kFusedDecisionWords) put_tagged_u32(dw + tid, tid == 0 ? static_cast<uint32_t>(kModeInvalid) : 0u, tag);
+    if (tid < kFusedDecisionWords)
+      put_tagged_u32(dw + tid, tid == 0 ? static_cast<uint32_t>(kModeInvalid) : 0u, tag, local);
     return;
   }
   stamp(a, fb + kFnGathered);
@@ -1966,7 +1971,7 @@ __device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t
 #pragma unroll
     for (int i = 1; i < kFusedDecisionWords; ++i)
       if (i == tid) mine = v[i];
-    put_tagged_u32(dw + tid, mine, tag);
+    put_tagged_u32(dw + tid, mine, tag, local);
   }
   stamp(a, fb + kFnDecided);
   if (d.mode == kModeBonus || d.mode == kModeOneHot)
@@ -1990,6 +1995,8 @@ __device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G, un
   const bool finisher = last_dispatched(g, g0, g0 + a.R * a.C, G);
   if (!needed && !finisher) return;
   stamp(a, 2 * static_cast<size_t>(g));
+  // the partials' readers (the finisher) and the decision's (the helpers) share this XCD
+  const bool local = a.xcd_local && on_indexed_xcd();
   FinisherInputs f;
   if (finisher) finisher_fetch_tokens(a, b, &f);
   u32x4 raw[NV];
@@ -2016,13 +2023,13 @@ __device__ __forceinline__ void fused_stats(const ChainArgs& a, int g, int G, un
     if ((threadIdx.x & 63) == 0) {
       uint64_t* tp = a.tpart + static_cast<size_t>(b) * a.tstride +
                      3 * ((static_cast<size_t>(rr) * a.C + c) * kWaves + (threadIdx.x >> 6));
-      put_tagged_u32(tp, __float_as_uint(o), tag);
-      put_tagged_double(tp + 1, sv, tag);
+      put_tagged_u32(tp, __float_as_uint(o), tag, local);
+      put_tagged_double(tp + 1, sv, tag, local);
     }
   }
   stamp(a, 2 * static_cast<size_t>(g) + 1);
   if (!finisher) return;
-  fused_finish<DT, VEC>(a, b, seq_tag_from(a, run), reinterpret_cast<RowStat*>(s_mem), f);
+  fused_finish<DT, VEC>(a, b, seq_tag_from(a, run), local, reinterpret_cast<RowStat*>(s_mem), f);
 }
 
 // Helper c of CP for sequence b (every lane).
@@ -2038,8 +2045,9 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
                     kHelperStamps * (static_cast<size_t>(b) * CP + c);
   stamp(a, hb + kHpStart);
   const uint32_t tag = seq_tag(a, b);
+  const bool local = a.xcd_local && on_indexed_xcd();  // the sequence's other helpers share this XCD
   uint64_t* st = a.status + static_cast<size_t>(b) * a.sstride;
-  if (!last && tid == 0) put_tagged_u32(st + c, 1u, tag);  // this helper has read the run counter
+  if (!last && tid == 0) put_tagged_u32(st + c, 1u, tag, local);  // this helper has read the run counter
   const uint64_t* dw = a.tdec + static_cast<size_t>(b) * kFusedDecisionWords;
   // Wave 0 waits for the decision words (lanes 0-8) with kPollsInFlight reads of each in flight,
   // started a quarter of a round trip apart and each reissued as soon as it returns, so that
@@ -2119,7 +2127,7 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
     for (int j = 0; j < SPT; ++j) red[j * kThreads + tid] = residual_vector_mass<DT>(d, rt[j], rd[j]);
     __syncthreads();
     SlotDouble* mw = a.wseg + static_cast<size_t>(b) * a.S;
-    publish_segment_masses(red, SPT, mw + c * SPT, tag);
+    publish_segment_masses(red, SPT, mw + c * SPT, tag, local);
     stamp(a, hb + kHpPublished);
     __syncthreads();  // `red` holds the gathered masses next
     // every helper gathers the masses and locates the draw; the one holding the segment
@@ -2181,10 +2189,14 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
   stamp(a, hb + kHpExit);
 }
 
-// grid = G stats workgroups, then B x CP helpers.  (With the n-gram lookup's workgroups ahead of
-// them, the finishers taking the drafts from the lookup's tagged words, the prompt-lookup
-// workload ran 22.0 us per call against 20.4 for the lookup beside the separate stats pass:
-// calls that draft by lookup take the separate launches.)
+// grid = G stats workgroups, then B x CP helpers.  When B is a multiple of 8, the stats
+// workgroups of XCD x (in xcd_blocked order) stream sequences [x B/8, (x+1) B/8) whole, and the
+// helpers are placed so that XCD x also holds those sequences' helpers: helper slot h = 8 m + x
+// serves sequence x B/8 + m / CP.  Every hand-over of a sequence then stays on one XCD, and
+// with xcd_local its words go through that XCD's L2 (store_xcd).  (With the n-gram lookup's
+// workgroups ahead of them, the finishers taking the drafts from the lookup's tagged words, the
+// prompt-lookup workload ran 22.0 us per call against 20.4 for the lookup beside the separate
+// stats pass: calls that draft by lookup take the separate launches.)
 template <int DT, int NV, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_fused_kernel(ChainArgs a, int G, int CP) {
   // one buffer for the finisher's partials and the helpers' masses
@@ -2194,7 +2206,13 @@ __global__ __launch_bounds__(kThreads) void chain_fused_kernel(ChainArgs a, int 
     fused_stats<DT, NV, VEC>(a, xcd_blocked(i, G), G, s_mem);
     return;
   }
-  fused_helper<DT, kPoolSegments, VEC>(a, (i - G) / CP, (i - G) % CP, CP, s_mem);
+  const int h = i - G;
+  if (a.B % kXcds == 0) {
+    const int m = h / kXcds;
+    fused_helper<DT, kPoolSegments, VEC>(a, (h % kXcds) * (a.B / kXcds) + m / CP, m % CP, CP, s_mem);
+  } else {
+    fused_helper<DT, kPoolSegments, VEC>(a, h / CP, h % CP, CP, s_mem);
+  }
 }
 
 // grid = 1: offsets and packed tokens of the batch (only when packed output is asked for).
@@ -2420,6 +2438,9 @@ static spec_status_t launch_chain(ChainArgs a, const NgramArgs* ng, hipStream_t 
       if (2 * static_cast<size_t>(G) + kFinisherStamps * static_cast<size_t>(a.B) +
               kHelperStamps * static_cast<size_t>(a.B) * CP <= g_stamp_words.load(std::memory_order_acquire))
         af.stamps = buf;
+    // each sequence's workgroups on one XCD (see chain_fused_kernel): its hand-overs through that
+    // XCD's L2, unless switched off
+    af.xcd_local = a.B % kXcds == 0 && knob(SPEC_KNOB_XCD_LOCAL) != 0;
     LaunchScope scope("chain_fused", stream);
     scope.launch(chain_fused_kernel<DT, NV, VEC>, dim3(static_cast<unsigned>(G + a.B * CP)), dim3(kThreads), stream, af,
                  G, CP);
@@ -2606,6 +2627,7 @@ static spec_status_t verify_chain_impl(const void* target_logits, const void* dr
   a.wseg = reinterpret_cast<SlotDouble*>(ws + L.off_wseg);
   a.decs = reinterpret_cast<ChainDecision*>(ws + L.off_decs);
   a.decided = 0;
+  a.xcd_local = 0;
   if (L.single || L.fused) {
     a.epoch = reinterpret_cast<uint32_t*>(ws + L.off_epoch);
     a.tpart = reinterpret_cast<uint64_t*>(ws + L.off_tpart);

@@ -31,9 +31,9 @@ spec_status_t fail(spec_status_t status, const char* fmt, ...) {
 
 namespace {
 
-constexpr int kKnobs = 3;
-constexpr int kKnobDefault[kKnobs] = {0, kPollLimit, 0};
-std::atomic<int> g_knobs[kKnobs] = {{kKnobDefault[0]}, {kKnobDefault[1]}, {kKnobDefault[2]}};
+constexpr int kKnobs = 4;
+constexpr int kKnobDefault[kKnobs] = {0, kPollLimit, 0, 1};
+std::atomic<int> g_knobs[kKnobs] = {{kKnobDefault[0]}, {kKnobDefault[1]}, {kKnobDefault[2]}, {kKnobDefault[3]}};
 
 }  // namespace
 
@@ -174,7 +174,7 @@ spec_status_t spec_set_knob(spec_knob_t k, int value) {
   if (value < 0) value = kKnobDefault[i];
   const bool ok = k == SPEC_KNOB_CHUNK_VECTORS
                       ? (value == 0 || value == 1 || value == 2 || value == 4 || value == 8 || value == 16)
-                      : (k != SPEC_KNOB_SINGLE_LAUNCH || value == 0 || value == 1);
+                      : ((k != SPEC_KNOB_SINGLE_LAUNCH && k != SPEC_KNOB_XCD_LOCAL) || value == 0 || value == 1);
   if (!ok) return fail(SPEC_ERR_INVALID_ARG, "value %d is not allowed for knob %d", value, i);
   g_knobs[i].store(value, std::memory_order_relaxed);
   return SPEC_OK;

@@ -51,11 +51,17 @@ spec_status_t spec_timing_entry(int index, const char** name, long long* launche
  *                            launch (plus the packed output's) when the whole grid fits on
  *                            the device at once; 1: always as separate statistics and
  *                            draw launches.
+ *   SPEC_KNOB_XCD_LOCAL      1 (default): where all workgroups of a sequence run on one XCD
+ *                            (the fused chain launch of a batch whose size is a multiple of
+ *                            8), the values they hand each other go through that XCD's L2;
+ *                            0: every hand-over through agent-scope stores.  The results are
+ *                            the same either way.
  */
 typedef enum spec_knob {
   SPEC_KNOB_CHUNK_VECTORS = 0,
   SPEC_KNOB_POLL_LIMIT = 1,
-  SPEC_KNOB_SINGLE_LAUNCH = 2
+  SPEC_KNOB_SINGLE_LAUNCH = 2,
+  SPEC_KNOB_XCD_LOCAL = 3
 } spec_knob_t;
 
 spec_status_t spec_set_knob(spec_knob_t knob, int value);

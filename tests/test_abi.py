@@ -161,6 +161,12 @@ def test_knobs_set_get_and_restore(lib):
     assert bd.spec_get_knob(bd.SPEC_KNOB_SINGLE_LAUNCH) == 0
     with pytest.raises(bd.SpecError):
         bd.spec_set_knob(bd.SPEC_KNOB_SINGLE_LAUNCH, 2)  # only 0 and 1
+    assert bd.spec_get_knob(bd.SPEC_KNOB_XCD_LOCAL) == 1
+    with bd.knob(bd.SPEC_KNOB_XCD_LOCAL, 0):
+        assert bd.spec_get_knob(bd.SPEC_KNOB_XCD_LOCAL) == 0
+    assert bd.spec_get_knob(bd.SPEC_KNOB_XCD_LOCAL) == 1
+    with pytest.raises(bd.SpecError):
+        bd.spec_set_knob(bd.SPEC_KNOB_XCD_LOCAL, 2)  # only 0 and 1
 
 
 def test_workspace_size_covers_the_single_launch_layout(lib):

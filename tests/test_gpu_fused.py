@@ -3,8 +3,8 @@ sequence decided by its last-dispatched stats workgroup, residual draws finished
 workgroups at the end of the grid, for batches of at most 2048 helpers) against the separate
 launches: bit-identical outputs on the
 same inputs, at full benchmark sizes and on ragged, greedy, invalid and one-hot batches, on a
-dirty workspace reused across shapes and in graph replays; and the flag of a wait that gives
-up."""
+dirty workspace reused across shapes and in graph replays; with hand-overs through one XCD's L2
+and through agent-scope stores alike; and the flag of a wait that gives up."""
 
 import dataclasses
 
@@ -69,6 +69,9 @@ CASES = {
         synth.chain_config_high_accept_bf16(21, B=160, V=128256), draft=None),
     "unaligned_B120_K3_V30001": lambda: synth.chain_inputs(9, B=120, K=3, V=30001, dtype="bf16", target_sigma=2.0,
                                                            draft_sigma=1.5, temperature=0.9),
+    # a batch that is not a multiple of 8: sequences straddle XCDs, every hand-over at agent scope
+    "odd_B37_K4_V64000": lambda: synth.chain_inputs(16, B=37, K=4, V=64000, dtype="bf16", target_sigma=2.0,
+                                                    draft_sigma=1.5, temperature=0.8),
 }
 
 
@@ -83,6 +86,28 @@ def test_fused_matches_separate_launches(name):
     seqs = sorted(set(range(0, inp.B, max(1, inp.B // 6))) | {inp.B - 1})
     rep = compare_chain(g, chain_oracle(inp, seqs=seqs), inp, seqs=seqs)
     log(f"[fused]   {rep}")
+    assert rep.ok(), rep.failures[:5]
+
+
+@pytest.mark.parametrize("B", [64, 40, 37, 24])
+def test_xcd_local_hand_overs_change_nothing(B):
+    # batches whose size is a multiple of 8 keep each sequence's workgroups on one XCD and hand
+    # over through its L2; the outputs must equal those of agent-scope hand-overs bit for bit
+    sv = _sv()
+    inp = synth.chain_config_high_accept_bf16(30 + B, B=B, V=128256 if B == 64 else 70000)
+    args = _args(inp)
+    assert sv.spec_get_knob(sv.SPEC_KNOB_XCD_LOCAL) == 1
+    local, names = _kernels_of(lambda: sv.spec_verify_chain(*args, want_packed=True))
+    assert names[0] == "chain_fused", names
+    with sv.knob(sv.SPEC_KNOB_XCD_LOCAL, 0):
+        agent, names = _kernels_of(lambda: sv.spec_verify_chain(*args, want_packed=True))
+    assert names[0] == "chain_fused", names
+    log(f"[fused] XCD-local hand-overs B={B}: mean accepted {local.num_accepted.float().mean().item():.3f}")
+    for name in ("tokens", "num_accepted", "probs", "offsets"):
+        assert torch.equal(getattr(local, name), getattr(agent, name)), name
+    assert (local.num_accepted.cpu().numpy() >= 0).all()
+    seqs = [0, B // 3, B - 1]
+    rep = compare_chain(local, chain_oracle(inp, seqs=seqs), inp, seqs=seqs)
     assert rep.ok(), rep.failures[:5]
 
 
