@@ -238,3 +238,20 @@ def test_wait_that_gives_up_flags_every_walk():
     assert (g.accept_len.cpu().numpy() == sv.FLAG_TIMED_OUT).all()
     assert (g.tokens.cpu().numpy() == -1).all() and (g.path_nodes.cpu().numpy() == -1).all()
     compare(x)
+
+
+@pytest.mark.parametrize("B", [32, 13])
+def test_xcd_local_hand_overs_change_nothing(B):
+    # as for the greedy walk: slice exchanges through one XCD's L2 (a launch of a multiple of
+    # 8 sequences) and through agent-scope stores give the same walks, which match the oracle
+    sv = _sv()
+    x = synth.tree_sampled_config_bf16(60 + B) if B == 32 else synth.tree_sampled_inputs(
+        61, B=B, n_nodes=30, depth=5, V=128256, dtype="bf16", name="B13")
+    assert sv.spec_get_knob(sv.SPEC_KNOB_XCD_LOCAL) == 1
+    g = run_gpu(x)
+    with sv.knob(sv.SPEC_KNOB_XCD_LOCAL, 0):
+        h = run_gpu(x)
+    for name in ("accept_len", "tokens", "path_nodes"):
+        assert torch.equal(getattr(g, name), getattr(h, name)), name
+    seqs = [0, B // 2, B - 1]
+    check(g, oracle_of(x, seqs=seqs), x, seqs=seqs, what=" (XCD-local)")

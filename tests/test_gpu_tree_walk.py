@@ -179,3 +179,23 @@ def test_wait_that_gives_up_flags_every_walk():
     assert np.array_equal(full.accept_len.cpu().numpy(), ref.accept_len)
     assert np.array_equal(full.tokens.cpu().numpy(), ref.tokens)
     compare(tr)
+
+
+@pytest.mark.parametrize("B", [32, 13])
+def test_xcd_local_hand_overs_change_nothing(B):
+    # a launch of a multiple of 8 sequences keeps each sequence's workgroups on one XCD and
+    # exchanges the slices through its L2; the results must equal those of agent-scope
+    # exchanges and the oracle's
+    sv = _sv()
+    tr = synth.tree_config_eagle_bf16(50 + B) if B == 32 else synth.tree_inputs(
+        51, B=B, n_nodes=30, depth=5, V=128256, dtype="bf16", p_boost=0.9)
+    assert sv.spec_get_knob(sv.SPEC_KNOB_XCD_LOCAL) == 1
+    g = walk(tr)
+    with sv.knob(sv.SPEC_KNOB_XCD_LOCAL, 0):
+        h = walk(tr)
+    for name in ("accept_len", "tokens", "path_nodes"):
+        assert torch.equal(getattr(g, name), getattr(h, name)), name
+    ref = oracle.verify_tree_greedy(tr.target, tr.dtype, tr.parent, tr.node_token, tr.max_depth)
+    assert np.array_equal(g.tokens.cpu().numpy(), ref.tokens)
+    assert np.array_equal(g.path_nodes.cpu().numpy(), ref.path_nodes)
+    log(f"[tree walk] XCD-local B={B}: exact; mean accept_len {ref.accept_len.mean():.3f}")
