@@ -164,7 +164,7 @@ struct ChainArgs {
 
 // Phase timestamps (the device's constant 100 MHz clock), written by thread 0 when the
 // caller asked for them.  Stats workgroup g: stamps[2g] start, [2g+1] end.  Pool task t
-// (t = launch offset + workgroup index): stamps[stamps_pool + kStampsPerTask * t + i] for
+// (t = b * CP + c for task c of sequence b): stamps[stamps_pool + kStampsPerTask * t + i] for
 // the phases of kPoolPhase, the last word holding (b << 32) | (c << 8) | mode.
 constexpr int kStampsPerTask = 6;
 enum PoolPhase : int { kPhStart = 0, kPhDecided = 1, kPhPublished = 2, kPhGathered = 3, kPhEnd = 4, kPhInfo = 5 };
@@ -1123,11 +1123,12 @@ __device__ __forceinline__ void publish_segment_masses(const float* red, int nse
 // task waits for the others' and returns kSlotLocated with the segment holding u * W and
 // u * W minus the mass before it, or kSlotNoMass if rounding left no residual mass.  Other
 // tasks return kSlotDone, and so does a last task whose wait gave up (it flags the
-// sequence).  `red` is shared memory of 2 * SPT * kThreads floats.
+// sequence).  `red` is shared memory of 2 * SPT * kThreads floats.  local: the sequence's tasks
+// share this XCD, the masses go through its L2.
 template <int DT, int SPT, bool VEC>
 __device__ __forceinline__ int slot_select(const ChainArgs& a, int b, int c, bool last, const ChainDecision& d,
                                            const void* row_t, const void* row_d, float* red, int* usel_out,
-                                           double* tloc_out, size_t sb, uint32_t gen) {
+                                           double* tloc_out, size_t sb, uint32_t gen, bool local) {
   using EL = Elem<DT>;
   constexpr int E = EL::kPerVec;
   constexpr int kSeg = ChunkShape<DT, 1>::kSegment;
@@ -1150,7 +1151,7 @@ __device__ __forceinline__ int slot_select(const ChainArgs& a, int b, int c, boo
   // ---- 2. segment totals in fp64
   const int units = a.S;  // segment slots per row
   SlotDouble* mw = a.wseg + static_cast<size_t>(b) * units;
-  publish_segment_masses(red, SPT, mw + c * SPT, gen);
+  publish_segment_masses(red, SPT, mw + c * SPT, gen, local);
   stamp(a, sb + kPhPublished);
   if (!last) return kSlotDone;
   __shared__ int s_outcome, s_usel;
@@ -1277,11 +1278,18 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int gi = static_cast<int>(blockIdx.x);
-  const int b = b0 + gi / CP;  // sequence
-  const int c = gi % CP;       // this task's group of SPT segments
+  // Task ti of the launch, sequence-major.  With xcd_local and a multiple of 8 sequences in the
+  // launch, XCD x (grid index mod 8) runs the tasks of sequences [x nb/8, (x+1) nb/8) of its nb,
+  // each sequence's in task order, and their masses go through its L2.
+  const int nb = static_cast<int>(gridDim.x) / CP;
+  const bool place = a.xcd_local && nb % kXcds == 0;
+  const int ti = place ? (gi % kXcds) * (nb / kXcds) * CP + gi / kXcds : gi;
+  const bool local = place && on_indexed_xcd();
+  const int b = b0 + ti / CP;  // sequence
+  const int c = ti % CP;       // this task's group of SPT segments
   const bool last = c == CP - 1;
   float* red = reinterpret_cast<float*>(s_buf);  // [2][SPT][kThreads] per-lane masses
-  const size_t sb = a.stamps_pool + kStampsPerTask * (static_cast<size_t>(b0) * CP + gi);
+  const size_t sb = a.stamps_pool + kStampsPerTask * (static_cast<size_t>(b0) * CP + ti);
   stamp(a, sb + kPhStart);
 
   if (a.decided) {  // decided by chain_decide_kernel, which also wrote the count and probabilities
@@ -1307,7 +1315,7 @@ __global__ __launch_bounds__(kThreads) void chain_pool_kernel(ChainArgs a, int b
     // the slot generation is read after the decision, off its critical path (measured: 0.5 us
     // less pool time at B=64, K=5, V=128256; 2.3 us at B=256, K=8, V=152064)
     const int o = slot_select<DT, SPT, VEC>(a, b, c, last, d, row_t, draft_row<DT>(a, b, d.row), red, &usel, &t_loc,
-                                            sb, pool_generation(a));
+                                            sb, pool_generation(a), local);
     if (o == kSlotLocated)
       narrow_and_emit<DT, VEC>(a, b, d, mode, usel, t_loc, row_t, draft_row<DT>(a, b, d.row),
                                a.tokens + static_cast<size_t>(b) * a.K);
@@ -1779,7 +1787,7 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
       double t_loc = 0.0;
       for (int cg = 0; cg < S / kPoolSegments; ++cg)
         o = slot_select<DT, kPoolSegments, VEC>(a, b, cg, cg == S / kPoolSegments - 1, d, row_t, row_d, red, &usel,
-                                                &t_loc, kNoStamp, g2);
+                                                &t_loc, kNoStamp, g2, false);
       if (o == kSlotLocated) narrow_and_emit<DT, VEC>(a, b, d, mode, usel, t_loc, row_t, row_d, s_tok);
       if (o == kSlotNoMass) {
         single_restage_row(a, b, tag, row, s_part);
@@ -2482,6 +2490,7 @@ static spec_status_t launch_chain(ChainArgs a, const NgramArgs* ng, hipStream_t 
     }
     // one waiting task per sequence: at most half as many sequences per launch as fit at once
     const int per_launch = max(1, pool_slots(reinterpret_cast<const void*>(kernel), slots_cache) / 2);
+    a.xcd_local = knob(SPEC_KNOB_XCD_LOCAL) != 0;  // (used by launches of a multiple of 8 sequences)
     for (int b0 = 0; b0 < a.B; b0 += per_launch) {
       const int bs = min(per_launch, a.B - b0);
       LaunchScope scope("chain_pool", stream);

@@ -74,7 +74,8 @@ int spec_get_knob(spec_knob_t knob);
  * `words` unsigned 64-bit words) is set, every following call whose stamps fit writes
  * the device's constant 100 MHz clock at its phase boundaries into it (a call that needs
  * more words writes none): with G = B * R * C stats workgroups (R rows and C chunks per
- * row as the call chose them) and P pool tasks, words [2g, 2g+1] are the start and end of
+ * row as the call chose them) and P pool tasks (task t = b * CP + c is task c of the CP
+ * of sequence b), words [2g, 2g+1] are the start and end of
  * stats workgroup g and words [2G + 6t, 2G + 6t + 5] those of pool task t: start,
  * decision made, own segment masses published (or the piece chosen, for a draw from a
  * target row), siblings' masses gathered (the waiting task), end, and

@@ -252,3 +252,28 @@ def test_oversubscribed_pool_decides_once():
     log(f"[chain]   {rep}")
     assert rep.ok(), rep.failures[:5]
     check_packed(g, inp.B)
+
+
+@pytest.mark.parametrize("B", [256, 250])
+def test_pool_xcd_local_hand_overs_change_nothing(B):
+    # the separate launches (forced for B = 256, whose helpers would exceed one fused launch):
+    # a pool launch of a multiple of 8 sequences keeps each sequence's tasks on one XCD and
+    # hands the segment masses over through its L2; the outputs must equal those of
+    # agent-scope hand-overs bit for bit
+    import draft_token_verification_09_amd as sv
+
+    inp = synth.chain_config_low_accept_bf16(70 + B, B=B, K=8, V=80000)
+    args = (logits_to_device(inp.target, inp.dtype), logits_to_device(inp.draft, inp.dtype), i32(inp.tokens),
+            f32(inp.temperature), f32(inp.u_accept), f32(inp.u_final))
+    with sv.knob(sv.SPEC_KNOB_SINGLE_LAUNCH, 1):
+        local = sv.spec_verify_chain(*args)
+        with sv.knob(sv.SPEC_KNOB_XCD_LOCAL, 0):
+            agent = sv.spec_verify_chain(*args)
+    torch.cuda.synchronize()
+    for name in ("tokens", "num_accepted", "probs"):
+        assert torch.equal(getattr(local, name), getattr(agent, name)), name
+    assert (local.num_accepted.cpu().numpy() >= 0).all()
+    seqs = [0, B // 2, B - 1]
+    rep = compare_chain(local, chain_oracle(inp, seqs=seqs), inp, seqs=seqs)
+    log(f"[chain] pool XCD-local B={B}: {rep}")
+    assert rep.ok(), rep.failures[:5]
