@@ -1002,6 +1002,17 @@ __device__ __forceinline__ void direct_draw(const ChainArgs& a, int b, const Cha
 // Outcomes of a residual draw's hand-over (slot_select, gather_and_locate).
 enum SlotOutcome : int { kSlotDone = 0, kSlotLocated = 1, kSlotNoMass = 2 };
 
+// Flags sequence b after a wait that gave up: -1 tokens, zero probabilities and the count
+// kFlagTimedOut, written by threads first, first + step, ... (a whole workgroup or one wave; the
+// one with first = 0 writes the count).
+__device__ __forceinline__ void write_timed_out(const ChainArgs& a, int b, int first, int step) {
+  int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
+  for (int kk = first; kk <= a.K; kk += step) ot[kk] = -1;
+  if (a.out_probs)
+    for (int i = first; i < a.K * 3; i += step) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
+  if (first == 0) a.out_num[b] = kFlagTimedOut;
+}
+
 // One wave alone (the other waves of its workgroup wait at a barrier): lane l takes segments
 // l, l + 64, ... (round r holds segments 64 r .. 64 r + 63), waits for their masses, and the
 // rounds' inclusive scans in vocabulary order give the total W and the segment whose prefix
@@ -1043,11 +1054,7 @@ __device__ __forceinline__ int gather_and_locate(const ChainArgs& a, int b, uint
       short_pause();
     }
     if (!arrived) {  // flag the sequence rather than wait on (this task alone writes its row)
-      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-      for (int kk = lane; kk <= a.K; kk += 64) ot[kk] = -1;
-      if (lane == 0) a.out_num[b] = kFlagTimedOut;
-      if (a.out_probs)
-        for (int i = lane; i < a.K * 3; i += 64) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
+      write_timed_out(a, b, lane, 64);
       return kSlotDone;
     }
   }
@@ -1471,18 +1478,26 @@ __device__ __forceinline__ bool single_gather(const ChainArgs& a, int b, uint32_
   return false;
 }
 
-// Copies row `row`'s partials (published, so read without waiting) back into shared memory.
-__device__ __forceinline__ void single_restage_row(const ChainArgs& a, int b, uint32_t tag, int row, RowStat* s_part) {
+// Copies row `row`'s partials (published before the decision that led here) back into shared
+// memory, every word checked against the tag (a bounded wait, for a reader that did not gather
+// them itself); false if a wait gave up.  Every lane.
+__device__ __forceinline__ bool single_restage_row(const ChainArgs& a, int b, uint32_t tag, int row, RowStat* s_part) {
   const int C4 = a.C * kWaves;
   const uint64_t* tp = a.tpart + static_cast<size_t>(b) * a.tstride + 3 * static_cast<size_t>(row) * C4;
-  for (int i = threadIdx.x; i < C4; i += kThreads) {
-    uint32_t o = 0;
-    double sv = 0.0;
-    get_tagged_u32(tp + 3 * i, tag, &o);
-    get_tagged_double(tp + 3 * i + 1, tag, &sv);
-    s_part[static_cast<size_t>(row) * C4 + i] = RowStat{__uint_as_float(o), 0.f, sv};
+  for (int polls = 0; polls < a.poll_limit; ++polls) {
+    bool missing = false;
+    for (int i = threadIdx.x; i < C4; i += kThreads) {
+      uint32_t o = 0;
+      double sv = 0.0;
+      const bool ho = get_tagged_u32(tp + 3 * i, tag, &o);  // both reads go out before either is checked
+      const bool hs = get_tagged_double(tp + 3 * i + 1, tag, &sv);
+      missing |= !(ho && hs);
+      s_part[static_cast<size_t>(row) * C4 + i] = RowStat{__uint_as_float(o), 0.f, sv};
+    }
+    if (!__syncthreads_or(missing)) return true;
+    short_pause();
   }
-  __syncthreads();
+  return false;
 }
 
 // The wave holding unit `usel` of a direct draw in registers (raw: this wave's share of the
@@ -1670,14 +1685,8 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
     for (int i = tid; i < others; i += kThreads) passed |= s_stv[i] == kStPassed;
     if (__syncthreads_or(passed)) ok = single_gather(a, b, tag, greedy, ngram, a.poll_limit, s_part, s_tok, s_gath, &s_kb);
     if (!ok) {
-      int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-      for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
-      if (a.out_probs)
-        for (int i = tid; i < a.K * 3; i += kThreads) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
-      if (tid == 0) {
-        a.out_num[b] = kFlagTimedOut;
-        __hip_atomic_fetch_add(a.epoch + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      write_timed_out(a, b, tid, kThreads);
+      if (tid == 0) __hip_atomic_fetch_add(a.epoch + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
   }
@@ -1750,7 +1759,8 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
     }
     if (o != kSlotNoMass) return;
     // no residual mass after rounding: the draw takes p_n itself, as a bonus draw would
-    single_restage_row(a, b, tag, row, s_part);
+    // (this workgroup gathered and checked these words itself, so the re-read finds them)
+    (void)single_restage_row(a, b, tag, row, s_part);
     int m2 = kModeFallbackP, usel;
     double t_unit;
     direct_locate<DT>(a, b, d, &m2, s_part + static_cast<size_t>(row) * C * kWaves, &usel, &t_unit);
@@ -1790,7 +1800,7 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
                                                 &t_loc, kNoStamp, g2, false);
       if (o == kSlotLocated) narrow_and_emit<DT, VEC>(a, b, d, mode, usel, t_loc, row_t, row_d, s_tok);
       if (o == kSlotNoMass) {
-        single_restage_row(a, b, tag, row, s_part);
+        (void)single_restage_row(a, b, tag, row, s_part);  // gathered and checked here before
         direct_draw<DT, VEC>(a, b, d, kModeFallbackP, row_t, s_part + static_cast<size_t>(row) * C * kWaves, s_tok,
                              kNoStamp);
       }
@@ -1954,11 +1964,7 @@ __device__ __forceinline__ void fused_finish(const ChainArgs& a, int b, uint32_t
   if (!single_gather(a, b, tag, greedy, false, a.poll_limit, s_part, s_tok, s_gath, &s_kb)) {
     // the wait gave up: flag the sequence (this workgroup alone writes its outputs) and let
     // the helpers stand down
-    int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-    for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
-    if (a.out_probs)
-      for (int i = tid; i < a.K * 3; i += kThreads) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
-    if (tid == 0) a.out_num[b] = kFlagTimedOut;
+    write_timed_out(a, b, tid, kThreads);
     if (tid < kFusedDecisionWords)
       put_tagged_u32(dw + tid, tid == 0 ? static_cast<uint32_t>(kModeInvalid) : 0u, tag, local);
     return;
@@ -2172,16 +2178,14 @@ __device__ __forceinline__ void fused_helper(const ChainArgs& a, int b, int c, i
     }
     if (o == kSlotNoMass && last) {  // no residual mass after rounding: the last helper draws from p_n
       RowStat* s_part = reinterpret_cast<RowStat*>(s_buf);
-      single_restage_row(a, b, tag, d.row, s_part);
-      direct_draw<DT, VEC>(a, b, d, kModeFallbackP, row_t, s_part + static_cast<size_t>(d.row) * a.C * kWaves, xs,
-                           kNoStamp);
+      if (single_restage_row(a, b, tag, d.row, s_part))
+        direct_draw<DT, VEC>(a, b, d, kModeFallbackP, row_t, s_part + static_cast<size_t>(d.row) * a.C * kWaves, xs,
+                             kNoStamp);
+      else
+        write_timed_out(a, b, tid, kThreads);
     }
   } else if (!ok && last) {  // the wait gave up: flag the sequence
-    int32_t* ot = a.out_tokens + static_cast<size_t>(b) * (a.K + 1);
-    for (int kk = tid; kk <= a.K; kk += kThreads) ot[kk] = -1;
-    if (a.out_probs)
-      for (int i = tid; i < a.K * 3; i += kThreads) a.out_probs[static_cast<size_t>(b) * a.K * 3 + i] = 0.f;
-    if (tid == 0) a.out_num[b] = kFlagTimedOut;
+    write_timed_out(a, b, tid, kThreads);
   }
   // the last helper advances the sequence's run counter once the other helpers have read it
   // (lane 0 alone: the other waves may have left); the words not seen while it waited (s_nseen

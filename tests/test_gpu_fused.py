@@ -240,3 +240,41 @@ def test_phase_stamps_of_the_fused_launch():
             assert owners.sum() == 1 and hlp[b, owners, 4][0] >= hlp[b, owners, 3][0], b
             assert ((hlp[b, :, 6] >> 32) == b).all() and (((hlp[b, :, 6] >> 8) & 0xFFFFFF) == np.arange(CP)).all(), b
     log(f"[fused] stamps: {int((n < K).sum())} residual draws, {int((n == K).sum())} bonus draws")
+
+
+def test_residual_mass_lost_to_rounding_in_the_fused_launch():
+    # A rejected draft whose residual max(0, p - q) is zero in both arithmetics, at a batch that
+    # runs as the fused launch (hand-overs in one XCD's L2): the last helper finds no mass,
+    # re-reads row 0's partials (checking every word's tag) and draws from p_0.  Each row holds
+    # 2^17 logits of 0 and four of -50, so every row sum is exactly 2^17 and every p (and q) of a
+    # 0 logit exactly 2^-17; the drafted token is a -50 in the target and -49 in the draft, so
+    # alpha = 1/e, u = 1 rejects it and q(x) moves no row sum.  u_final stays half a token away
+    # from every boundary of p_0's cumulative sum.
+    sv = _sv()
+    B, K, V = 56, 2, (1 << 17) + 4  # 56 x 33 helpers: one fused launch
+    rng = np.random.default_rng(17)
+    target = np.zeros((B, K + 1, V), np.float32)
+    tokens = np.zeros((B, K), np.int32)
+    for b in range(B):
+        neg = rng.choice(V, size=4, replace=False)
+        target[b, :, neg] = np.float32(-50.0)
+        tokens[b] = [int(neg[0]), int(rng.integers(0, V))]
+    draft = target[:, :K].copy()
+    draft[np.arange(B), 0, tokens[:, 0]] = np.float32(-49.0)
+    u_fin = ((rng.integers(0, 1 << 17, B) + 0.5) / float(1 << 17)).astype(np.float32)
+    inp = synth.ChainInputs(target=target, draft=draft, dtype="f32", tokens=tokens, draft_len=None,
+                            temperature=np.ones((B,), np.float32), u_accept=np.ones((B, K), np.float32),
+                            u_final=u_fin, name="lost_residual")
+    ref = chain_oracle(inp)
+    assert all(s.mode == "residual_zero_fallback" and s.num_accepted == 0 for s in ref.sequences)
+    args = _args(inp)
+    g, names = _kernels_of(lambda: sv.spec_verify_chain(*args, want_packed=True))
+    assert names[0] == "chain_fused", names
+    rep = compare_chain(g, ref, inp)
+    log(f"[fused] lost residual mass B={B} V={V}: {rep}")
+    assert rep.ok(), rep.failures[:5]
+    with sv.knob(sv.SPEC_KNOB_XCD_LOCAL, 0):
+        h = sv.spec_verify_chain(*args)
+    torch.cuda.synchronize()
+    for name in ("tokens", "num_accepted", "probs"):
+        assert torch.equal(getattr(g, name), getattr(h, name)), name
