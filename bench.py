@@ -759,9 +759,12 @@ def chain_phases_fused(make, name, warmup, calls, dev):
     vec = (V * (2 if probe.dtype == "bf16" else 4)) % 16 == 0
     has_d = probe.draft is not None
     R = 2 * K + 1 if has_d else K + 1  # rows of a sequence in the stats grid
-    C = -(-V // (library_chunk_vectors(B * R, V, epv, vec) * 256 * epv))
     S = -(-(-(-V // (256 * epv))) // 4) * 4
     CP = S // 4 if has_d else 1
+    nv = library_chunk_vectors(B * R, V, epv, vec)
+    if nv == 16 and R * -(-V // (8 * 256 * epv)) * 4 <= 512 and B * CP <= 2048:
+        nv = 8  # the fused launch streams 32 KiB chunks where its partials fit
+    C = -(-V // (nv * 256 * epv))
     G = B * R * C
     code = 1 if probe.dtype == "bf16" else 0
     ws = torch.empty(sv.spec_verify_chain_workspace_size(B, K, V, code) + 256, dtype=torch.uint8, device=dev)

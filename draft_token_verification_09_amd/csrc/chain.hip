@@ -2281,9 +2281,11 @@ static int chain_nv(long long rows, int V, int epv, bool vec) {
 }
 
 // `vec`: the rows can be read with 16-byte loads; `one_hot`: no draft rows (K+1 rows per
-// sequence are streamed instead of 2K+1).  Both set the chunk size; the workspace regions keep
+// sequence are streamed instead of 2K+1); `lookup`: the drafts come from the n-gram lookup
+// (which never takes the fused launch).  They set the chunk size; the workspace regions keep
 // room for 2K+1 rows either way.
-static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool vec, bool one_hot, bool prefer_single) {
+static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool vec, bool one_hot, bool prefer_single,
+                                bool lookup) {
   ChainLayout L{};
   const int epv = dtype == SPEC_BF16 ? 8 : 4;
   L.R = 2 * K + 1;
@@ -2308,6 +2310,16 @@ static ChainLayout chain_layout(int B, int K, int V, spec_dtype_t dtype, bool ve
   // (unless a knob forces the chunk or the separate launches)
   if (prefer_single && L.nv < kSingleVectors && knob(SPEC_KNOB_CHUNK_VECTORS) == 0 && fits_single(kSingleVectors))
     L.nv = kSingleVectors;
+  // A call that takes the fused launch streams 32 KiB chunks where the rule gives 64 KiB, when
+  // its partials still fit: the pass is faster with them, and with the hand-overs in one XCD's
+  // L2 the doubled partials cost the finisher less than that (measured per call at B=64, K=5,
+  // V=128256 bf16: 39.5 -> 38.9 us, greedy 22.4 -> 22.2 us, one-hot B=160 47.9 -> 46.0 us; the
+  // separate launches keep 64 KiB chunks, B=256, K=8, V=152064: 222.8 against 225.0 us with 32 KiB)
+  const long long fused_cp = one_hot ? 1 : L.S / kPoolSegments;
+  if (prefer_single && !lookup && L.nv == 16 && knob(SPEC_KNOB_CHUNK_VECTORS) == 0 &&
+      static_cast<long long>(rows) * chunks(8) * kWaves <= kSingleMaxParts &&
+      static_cast<long long>(B) * fused_cp <= kFusedMaxHelpers)
+    L.nv = 8;
   L.C = chunks(L.nv);
   const size_t segs = static_cast<size_t>(B) * L.S;
   size_t off = 256;  // bytes 0..3: the run counter
@@ -2360,10 +2372,11 @@ static size_t chain_workspace_bytes(int B, int K, int V, spec_dtype_t dtype, boo
   size_t bytes = 0;
   for (int vec = 0; vec < 2; ++vec)
     for (int one_hot = 0; one_hot < 2; ++one_hot)
-      for (int single = 0; single < (one_launch ? 2 : 1); ++single) {
-        const size_t b = chain_layout(B, K, V, dtype, vec != 0, one_hot != 0, single != 0).bytes;
-        bytes = b > bytes ? b : bytes;
-      }
+      for (int single = 0; single < (one_launch ? 2 : 1); ++single)
+        for (int lookup = 0; lookup < 2; ++lookup) {
+          const size_t b = chain_layout(B, K, V, dtype, vec != 0, one_hot != 0, single != 0, lookup != 0).bytes;
+          bytes = b > bytes ? b : bytes;
+        }
   return bytes;
 }
 
@@ -2600,7 +2613,8 @@ static spec_status_t verify_chain_impl(const void* target_logits, const void* dr
   const bool vec = (static_cast<size_t>(V) * esize) % 16 == 0 && aligned16(target_logits) &&
                    (draft_logits == nullptr || aligned16(draft_logits));
   const ChainLayout L =
-      chain_layout(B, K, V, dtype, vec, draft_logits == nullptr, one_launch && knob(SPEC_KNOB_SINGLE_LAUNCH) == 0);
+      chain_layout(B, K, V, dtype, vec, draft_logits == nullptr, one_launch && knob(SPEC_KNOB_SINGLE_LAUNCH) == 0,
+                   ng != nullptr);
   const double groups = static_cast<double>(B) * L.R * L.C;
   if (groups > 2147483647.0) return fail(SPEC_ERR_UNSUPPORTED, "grid of %.0f workgroups too large", groups);
   if (L.S > 4 * kThreads)

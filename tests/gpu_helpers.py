@@ -68,6 +68,36 @@ def f32(x) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float32))).to(dev())
 
 
+def fused_chunk_vectors(B: int, K: int, V: int, dtype: str, one_hot: bool = False) -> int:
+    """Vectors a lane in one stats chunk of a chain call that takes the fused launch, so that
+    the separate launches can be forced to the same chunk size for a bit-for-bit comparison.
+    Restates the library's rule: the largest chunk (16 vectors for bf16 rows read 16 bytes at a
+    time, else 8) giving at least 1024 workgroups with at most 16 chunks a row (else the
+    smallest within that bound, at least 4); 16 becomes 8 where the sequence's partials still
+    fit 512 and its helpers the launch's 2048."""
+    epv = 8 if dtype == "bf16" else 4
+    vec = V * (2 if dtype == "bf16" else 4) % 16 == 0  # rows on 16-byte boundaries (aligned bases)
+    rows = K + 1 if one_hot else 2 * K + 1
+    top = 16 if vec and epv == 8 else 8
+    chunks = lambda nv: -(-V // (nv * 256 * epv))
+    pick, nv, choice = 0, top, None
+    while nv >= 1:
+        if chunks(nv) > 16:
+            break
+        pick = nv
+        if B * rows * chunks(nv) >= 1024:
+            choice = nv
+            break
+        nv //= 2
+    if choice is None:
+        choice = (4 if pick < 4 else pick) if pick else top
+    S = -(-(-(-V // (256 * epv))) // 4) * 4
+    cp = 1 if one_hot else S // 4
+    if choice == 16 and rows * chunks(8) * 4 <= 512 and B * cp <= 2048:
+        choice = 8
+    return choice
+
+
 def chain_on_gpu(inp, want_packed=True):
     import draft_token_verification_09_amd as sv
 

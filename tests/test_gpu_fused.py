@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import chain_oracle, check_packed, compare_chain, f32, i32, log, logits_to_device
+from gpu_helpers import chain_oracle, check_packed, compare_chain, f32, fused_chunk_vectors, i32, log, logits_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -43,13 +43,14 @@ def _kernels_of(call):
 
 
 def _fused_vs_separate(inp, ws=None):
-    """The default call (which must take the fused launch) and the separate launches, checked
-    equal bit for bit; returns the fused result."""
+    """The default call (which must take the fused launch) and the separate launches at the same
+    chunk size, checked equal bit for bit; returns the fused result."""
     sv = _sv()
     args = _args(inp)
     one, names = _kernels_of(lambda: sv.spec_verify_chain(*args, want_packed=True, workspace_buf=ws))
     assert names[0] == "chain_fused", names
-    with sv.knob(sv.SPEC_KNOB_SINGLE_LAUNCH, 1):
+    nv = fused_chunk_vectors(inp.B, inp.K, inp.V, inp.dtype, one_hot=inp.draft is None)
+    with sv.knob(sv.SPEC_KNOB_SINGLE_LAUNCH, 1), sv.knob(sv.SPEC_KNOB_CHUNK_VECTORS, nv):
         two, names = _kernels_of(lambda: sv.spec_verify_chain(*args, want_packed=True, workspace_buf=ws))
     assert "chain_stats" in names and "chain_pool" in names, names
     for name in ("tokens", "num_accepted", "probs", "offsets"):
@@ -152,8 +153,9 @@ def test_graph_replays_get_new_tags():
                          packed=None, offsets=None)
     ws = torch.empty(sv.spec_verify_chain_workspace_size(B, K1 - 1, V, 1) + 256, dtype=torch.uint8, device="cuda:0")
     refs = []
-    for args in dev_args:  # the separate launches' outputs for every input set
-        with sv.knob(sv.SPEC_KNOB_SINGLE_LAUNCH, 1):
+    nv = fused_chunk_vectors(B, K1 - 1, V, inps[0].dtype)
+    for args in dev_args:  # the separate launches' outputs (same chunk size) for every input set
+        with sv.knob(sv.SPEC_KNOB_SINGLE_LAUNCH, 1), sv.knob(sv.SPEC_KNOB_CHUNK_VECTORS, nv):
             r = sv.spec_verify_chain(*args)
         torch.cuda.synchronize()
         refs.append(r)
