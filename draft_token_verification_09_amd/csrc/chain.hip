@@ -1587,6 +1587,7 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
   uint64_t* tp = a.tpart + static_cast<size_t>(b) * a.tstride;
   uint64_t* st = a.status + static_cast<size_t>(b) * a.sstride;
   const int S = a.S;
+  const bool local = a.xcd_local && on_indexed_xcd();  // the sequence's workgroups share this XCD
 
   // the decision's scalar inputs and (wave 0, lane l) drafted token l and its uniform first,
   // then the chunks, then the tokens' logits
@@ -1625,8 +1626,8 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
     const uint32_t tg = seq_tag_from(a, run);
     const size_t i = (static_cast<size_t>(k) * C + c) * kWaves + w;
     if (lane == 0) {
-      put_tagged_u32(tp + 3 * i, __float_as_uint(o), tg);
-      put_tagged_double(tp + 3 * i + 1, sv, tg);
+      put_tagged_u32(tp + 3 * i, __float_as_uint(o), tg, local);
+      put_tagged_double(tp + 3 * i + 1, sv, tg, local);
     }
   }
   if (has_d) {
@@ -1636,8 +1637,8 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
     const uint32_t tg = seq_tag_from(a, run);
     const size_t i = (static_cast<size_t>(a.K + 1 + k) * C + c) * kWaves + w;
     if (lane == 0) {
-      put_tagged_u32(tp + 3 * i, __float_as_uint(o), tg);
-      put_tagged_double(tp + 3 * i + 1, sv, tg);
+      put_tagged_u32(tp + 3 * i, __float_as_uint(o), tg, local);
+      put_tagged_double(tp + 3 * i + 1, sv, tg, local);
     }
   }
   const uint32_t tag = seq_tag_from(a, run);
@@ -1659,7 +1660,7 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
   bool ok = single_gather(a, b, tag, greedy, ngram, limit, s_part, s_tok, s_gath, &s_kb);
   stamp(a, sb + kSgGathered);
   if (!anchor) {
-    if (tid == 0) put_tagged_u32(st + j, ok ? kStPassed : kStLeft, tag);
+    if (tid == 0) put_tagged_u32(st + j, ok ? kStPassed : kStLeft, tag, local);
     if (!ok) return;
   }
   // the anchor's view of the others: the sequence's other workgroups that read rows (its own
@@ -1711,7 +1712,7 @@ __device__ __forceinline__ void single_task(const ChainArgs& a, int b, int k, in
     for (int jv = 0; jv < NV; ++jv) red[(w * NV + jv) * 64 + lane] = residual_vector_mass<DT>(dk, rt[jv], rd[jv]);
     __syncthreads();
     // this chunk holds segments c * NV .. c * NV + NV - 1 (those from S on lie past V)
-    publish_segment_masses(red, min(NV, S - c * NV), tm + static_cast<size_t>(k) * S + c * NV, tag);
+    publish_segment_masses(red, min(NV, S - c * NV), tm + static_cast<size_t>(k) * S + c * NV, tag, local);
   };
   chain_decide<DT>(a, b, kb, SeqInputs{s_part, s_tok, s_gath, s_u, T, uf, kb_raw}, anchor, &s_dec, speculate);
   const ChainDecision d = uniform_decision(s_dec);
@@ -1820,28 +1821,48 @@ __device__ __forceinline__ void lookup_workgroup(const ChainArgs& a, const Ngram
   const int len = ngram_propose_in<kThreads, TILE>(s_ctx, i, ng.context, ng.context_len, ng.L_max, ng.n_min, ng.n_max,
                                                    a.K, tokens, const_cast<int32_t*>(a.draft_len), ng.match_n);
   const uint32_t tag = seq_tag(a, i);
+  const bool local = a.xcd_local && on_indexed_xcd();  // the sequence's workgroups share this XCD
   uint64_t* w = a.tprop + static_cast<size_t>(i) * (2 * a.K + 1);
   for (int k = threadIdx.x; k < len; k += kThreads) {  // lane k wrote token k above and reads it back
     const int x = tokens[static_cast<size_t>(i) * a.K + k];
     const float g = x >= 0 && x < a.V ? Elem<DT>::value(target_row<DT>(a, i, k), x) : 0.f;
-    put_tagged_u32(w + 1 + k, static_cast<uint32_t>(x), tag);
-    put_tagged_u32(w + 1 + a.K + k, __float_as_uint(g), tag);
+    put_tagged_u32(w + 1 + k, static_cast<uint32_t>(x), tag, local);
+    put_tagged_u32(w + 1 + a.K + k, __float_as_uint(g), tag, local);
   }
-  if (threadIdx.x == 0) put_tagged_u32(w, static_cast<uint32_t>(len), tag);
+  if (threadIdx.x == 0) put_tagged_u32(w, static_cast<uint32_t>(len), tag, local);
 }
 
 // grid = P + B x (K+1) x C: P = B lookup workgroups when the lookup drafts (else 0), then the
-// sequences' workgroups (position k, chunk c).
+// sequences' workgroups (position k, chunk c).  With xcd_local (batches of 8 or more),
+// grid = 8 x ceil(B/8) x (L + (K+1) C) (L = 1 when the lookup drafts, else 0): XCD x (grid index
+// mod 8) runs sequences x, x + 8, ..., first their lookups, then each sequence's workgroups in
+// order, and the rest of its share idles, so that every hand-over of a sequence stays in one
+// XCD's L2 (store_xcd).
 template <int DT, int NV, bool VEC, bool DRAFT>
 __global__ __launch_bounds__(kThreads) void chain_single_kernel(ChainArgs a, NgramArgs ng, int P) {
+  __shared__ int s_ctx[kTileInts<kSmallTile>];
+  const int per = (a.K + 1) * a.C;
   int i = static_cast<int>(blockIdx.x);
+  if (a.xcd_local) {
+    const int x = i % kXcds;
+    int m = i / kXcds;
+    const int nb = x < a.B ? (a.B - x + kXcds - 1) / kXcds : 0;  // sequences of XCD x
+    if (P > 0) {
+      if (m < nb) {
+        lookup_workgroup<DT, kSmallTile>(a, ng, x + kXcds * m, s_ctx);
+        return;
+      }
+      m -= nb;
+    }
+    if (m >= nb * per) return;  // beyond this XCD's share
+    single_task<DT, NV, VEC, DRAFT>(a, x + kXcds * (m / per), (m % per) / a.C, m % a.C, P > 0);
+    return;
+  }
   if (i < P) {
-    __shared__ int s_ctx[kTileInts<kSmallTile>];
     lookup_workgroup<DT, kSmallTile>(a, ng, i, s_ctx);
     return;
   }
   i -= P;
-  const int per = (a.K + 1) * a.C;
   const int j = i % per;
   single_task<DT, NV, VEC, DRAFT>(a, i / per, j / a.C, j % a.C, P > 0);
 }
@@ -2440,10 +2461,18 @@ static spec_status_t launch_chain(ChainArgs a, const NgramArgs* ng, hipStream_t 
       const Kernel kernel = a.draft ? chain_single_kernel<DT, NV, VEC, true> : chain_single_kernel<DT, NV, VEC, false>;
       const int P = ng ? a.B : 0;
       const long long total = P + static_cast<long long>(a.B) * (a.K + 1) * a.C;
-      if (total <= pool_slots(reinterpret_cast<const void*>(kernel), single_cache[a.draft ? 1 : 0])) {
+      // each sequence on one XCD (see chain_single_kernel) once every XCD has a sequence: an eighth
+      // of the slots for each XCD's share.  (Fewer sequences would leave XCDs idle and stream each
+      // sequence's rows through one: B=1, K=5, V=32000 fp32 9.7 -> 10.7 us per call; with 8 or more,
+      // B=16 one-hot, V=32000 bf16 10.5 -> 9.6 us, B=8 11.9 -> 11.7 us.)
+      const long long share = static_cast<long long>((a.B + kXcds - 1) / kXcds) * ((ng ? 1 : 0) + (a.K + 1) * a.C);
+      const int slots = pool_slots(reinterpret_cast<const void*>(kernel), single_cache[a.draft ? 1 : 0]);
+      as.xcd_local = knob(SPEC_KNOB_XCD_LOCAL) != 0 && a.B >= kXcds && share <= slots / kXcds;
+      if (total <= slots) {
         const NgramArgs none{};
+        const long long grid = as.xcd_local ? kXcds * share : total;
         LaunchScope scope("chain_single", stream);
-        scope.launch(kernel, dim3(static_cast<unsigned>(total)), dim3(kThreads), stream, as, ng ? *ng : none, P);
+        scope.launch(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), stream, as, ng ? *ng : none, P);
         const spec_status_t st = scope.finish();
         if (st != SPEC_OK || !a.out_packed) return st;
         LaunchScope pack("chain_pack", stream);

@@ -52,11 +52,12 @@ spec_status_t spec_timing_entry(int index, const char** name, long long* launche
  *                            the device at once; 1: always as separate statistics and
  *                            draw launches.
  *   SPEC_KNOB_XCD_LOCAL      1 (default): where all workgroups of a sequence run on one XCD
- *                            (the fused chain launch and the tree walks of a batch, or of a
- *                            launch's share of it, whose size is a multiple of 8), the values
+ *                            (the fused chain launch, the pool kernel and the tree walks of a
+ *                            batch, or of a launch's share of it, whose size is a multiple of
+ *                            8; the single chain launch of 8 sequences or more), the values
  *                            they hand each other go through that XCD's L2; 0: every
- *                            hand-over through agent-scope stores.  The results are the same
- *                            either way.
+ *                            hand-over through agent-scope stores, in the spread placement.
+ *                            The results are the same either way.
  */
 typedef enum spec_knob {
   SPEC_KNOB_CHUNK_VECTORS = 0,

@@ -195,3 +195,24 @@ def test_wait_that_gives_up_flags_every_sequence():
     torch.cuda.synchronize()
     rep = compare_chain(g, chain_oracle(inp), inp)
     assert rep.ok(), rep.failures[:5]
+
+
+@pytest.mark.parametrize("name", ["B8_bf16_high", "B12_bf16_bonus", "B16_one_hot", "B1_fp32"])
+def test_xcd_local_hand_overs_change_nothing(name):
+    # batches of 8 or more: each sequence's workgroups on one XCD (sequence b on XCD b mod 8, the
+    # rest of each XCD's share idle) with its hand-overs through that XCD's L2, against
+    # agent-scope hand-overs (a smaller batch keeps the spread placement either way)
+    sv = _sv()
+    inp = CASES[name]()
+    args = _args(inp)
+    assert sv.spec_get_knob(sv.SPEC_KNOB_XCD_LOCAL) == 1
+    local, names = _kernels_of(lambda: sv.spec_verify_chain(*args, want_packed=True))
+    assert names[0] == "chain_single", names
+    with sv.knob(sv.SPEC_KNOB_XCD_LOCAL, 0):
+        agent, names = _kernels_of(lambda: sv.spec_verify_chain(*args, want_packed=True))
+    assert names[0] == "chain_single", names
+    for field in ("tokens", "num_accepted", "probs", "offsets"):
+        assert torch.equal(getattr(local, field), getattr(agent, field)), field
+    rep = compare_chain(local, chain_oracle(inp), inp)
+    log(f"[single] XCD-local {name}: {rep}")
+    assert rep.ok(), rep.failures[:5]
