@@ -57,3 +57,38 @@ def test_random_shape(i):
     assert rep.ok(), rep.failures[:5]
     assert rep.sequences == inp.B
     check_packed(g, inp.B)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_batch_of_a_multiple_of_8(i):
+    # batches of 8 to 64 sequences: the launch shapes that keep each sequence's workgroups on
+    # one XCD (single launch, fused launch, pool kernel) and hand over through its L2; every
+    # sequence against the oracle, and the same outputs with agent-scope hand-overs
+    import draft_token_verification_09_amd as sv
+    import torch
+
+    base = _case(100 + i)
+    rng = np.random.default_rng(7100 + i)
+    B = 8 * int(rng.integers(1, 9))
+    V = int(rng.choice([2049, 8193, 16385, 40000, 65537, 128256]))
+    inp = synth.chain_inputs(9100 + i, B=B, K=base.K, V=V, dtype=base.dtype, target_sigma=2.0,
+                             draft_sigma=float(rng.choice([0.3, 1.0, 3.0])), temperature=float(base.temperature.max()),
+                             name=f"random8x{i}")
+    if rng.random() < 0.4:
+        inp.draft_len = rng.integers(0, base.K + 1, B).astype(np.int32)
+    if rng.random() < 0.3:
+        inp.draft = None
+    log(f"[random] batch case {i}: B={B} K={inp.K} V={V} {inp.dtype} one-hot={inp.draft is None}")
+    g = chain_on_gpu(inp)
+    rep = compare_chain(g, chain_oracle(inp), inp)
+    log(f"[random]   {rep}")
+    assert rep.ok(), rep.failures[:5]
+    assert rep.sequences == B
+    check_packed(g, B)
+    with sv.knob(sv.SPEC_KNOB_XCD_LOCAL, 0):
+        h = chain_on_gpu(inp)
+    torch.cuda.synchronize()
+    for name in ("tokens", "num_accepted", "probs", "offsets"):
+        assert torch.equal(getattr(g, name), getattr(h, name)), name
+    total = int(g.offsets[-1])
+    assert torch.equal(g.packed[:total], h.packed[:total])
