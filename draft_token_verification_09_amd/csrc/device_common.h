@@ -8,7 +8,8 @@
 //   waves of a workgroup.
 // * Partial results pass between kernels through the workspace (the stream orders the
 //   kernels); inside a kernel, workgroups hand values over through agent-scope atomic
-//   stores and loads (see "cross-workgroup hand-off" below).
+//   loads and agent-scope or, within one XCD, workgroup-scope atomic stores (see
+//   "cross-workgroup hand-off" below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -492,7 +493,7 @@ __device__ __forceinline__ bool on_indexed_xcd() {
 
 // Hand-over words.  A 64-bit word carries 32 payload bits in its low half and a 32-bit tag
 // (the call's generation, possibly mixed with a step number) in its high half, written by
-// one agent-scope atomic store.  A reader takes a value only when every word of it
+// one atomic store (agent scope, or XCD-local; see above).  A reader takes a value only when every word of it
 // carries the tag it expects, so whatever a word held before (an earlier call's or step's
 // words, or anything else) reads as "not written yet" unless 32 bits match by chance, and
 // no clearing pass is needed.
